@@ -1,0 +1,248 @@
+"""CPU oracle for log-linear attention (forward and O(log T) decode step).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP library.
+
+Plain, slow, fp64 NumPy.  It materialises the full lower-triangular mask and
+multiplies densely (O(T^2)); the chunkwise / hierarchical algorithm that the GPU
+runs is an exact rearrangement of this definition and is deliberately NOT
+reproduced here.
+
+Sources (the web pages this follows; cited by title and section):
+
+* [P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制"
+  (paper-reading blog).  Sections used: 前缀的层次化分解 (Fenwick partition of the
+  prefix, the t=7 example), 层级判定算法 (level of s as seen from t),
+  循环形式与输出计算 (per-level states and lambda-weighted readout),
+  并行形式 (O = (QK^T ⊙ M^H) V and its 8x8 pattern table),
+  解码：基于 lssb 的状态更新 (decode rule), 与已有模型的组合 (M^S ⊙ M^H).
+* [P2] "算力终结者来了！华人天团「降维打击」注意力瓶颈，AI狂飙进对数时代" (news
+  write-up).  Sections: 对数线性注意力 (O = (A ⊙ M) V), 特殊结构：Fenwick树划分.
+* [P4] "动态线性注意力 — HF Daily Papers".  Section 前置知识 / 多状态线性注意力
+  (bucket count ceil(log2(t+1)) + 1, state S = sum over bucket of v k^T).
+* [P5] "論文紹介：Log Linear Attention" (journal-club slides), slides 19-21
+  (t=7 walk-through, decode update rule).
+
+Readings of points the pages leave open (each is listed in the design doc):
+
+* M^S is the Mamba-2 scalar-decay mask M^S[t,s] = exp(cum[t] - cum[s]) with
+  cum the inclusive prefix sum of log_a ([P1] 与已有模型的组合 names "the
+  original model's semiseparable mask"; its formula is stripped).
+* lambda is indexed by the query position t and the level ([P1] 并行形式 table).
+* No softmax and no 1/sqrt(dk) scale: the operator is exactly (QK^T ⊙ M) V.
+* States are stored k-major, S = sum k v^T (dk x dv), the transpose of the
+  pages' v k^T; the readout is o = q^T S.
+* lssb(t) is the 0-based index of the lowest set bit.  The decode rule zeroes
+  levels 1..lssb(t) (inclusive) and writes the merge to level lssb(t)+1; the
+  slide's "0 < l < lssb(t)" is read as a typo because only the inclusive range
+  reproduces the parallel form (pinned by the recurrent == parallel test).
+* Every kept or merged state is multiplied by a_t = exp(log_a[t]) on the step
+  to t; the new level-0 state k_t v_t^T is not decayed (M^S[t,t] = 1).
+* At t = 0 all levels are cleared before level 0 receives k_0 v_0^T.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Index structure: the Fenwick partition of the prefix [0, t]
+# --------------------------------------------------------------------------
+
+def fenwick_buckets(t: int) -> list[tuple[int, int, int]]:
+    """Partition of the prefix [0, t] into Fenwick buckets.
+
+    Returns a list of (level, lo, hi) with hi exclusive.  Level 0 is the
+    size-one sentinel {t}.  The rest of the prefix, [0, t), is cut by starting
+    at t and repeatedly removing the lowest set bit: each removal of a low bit
+    of value 2^(l-1) cuts off a bucket of that size at level l
+    ([P1] 前缀的层次化分解; [P2] 特殊结构：Fenwick树划分).
+    """
+    if t < 0:
+        raise ValueError("t must be >= 0")
+    out = [(0, t, t + 1)]
+    end = t
+    while end:
+        low = end & -end              # value of the lowest set bit
+        level = low.bit_length()      # 2^(level-1) == low
+        out.append((level, end - low, end))
+        end -= low
+    return out
+
+
+def level_of(t: int, s: int) -> int:
+    """Level of key position s as seen from query position t (s <= t):
+    the level of the Fenwick bucket of [0, t] that contains s ([P1] 层级判定算法)."""
+    if not 0 <= s <= t:
+        raise ValueError("need 0 <= s <= t")
+    for level, lo, hi in fenwick_buckets(t):
+        if lo <= s < hi:
+            return level
+    raise AssertionError("buckets do not cover the prefix")
+
+
+def level_rows(t0: int, t1: int, T: int) -> np.ndarray:
+    """Levels for query rows t0..t1-1 against keys 0..T-1, -1 where s > t.
+
+    Filled bucket by bucket from fenwick_buckets, so it is the same rule as
+    level_of applied to every pair.
+    """
+    out = np.full((t1 - t0, T), -1, dtype=np.int16)
+    for r, t in enumerate(range(t0, t1)):
+        for level, lo, hi in fenwick_buckets(t):
+            out[r, lo:hi] = level
+    return out
+
+
+def level_matrix(T: int) -> np.ndarray:
+    """Full T x T level matrix (row t = query, column s = key), -1 above the diagonal."""
+    return level_rows(0, T, T)
+
+
+# --------------------------------------------------------------------------
+# Forward: O = ((Q K^T) ⊙ M^S ⊙ M^H) V
+# --------------------------------------------------------------------------
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor (bf16 values are exact in fp32)
+        x = x.detach().cpu().float().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def mask_rows(log_a: np.ndarray, lam: np.ndarray, t0: int, t1: int) -> np.ndarray:
+    """Rows t0..t1-1 of M = M^S ⊙ M^H for one (batch, head).
+
+    M^H[t, s] = lam[t, level(t, s)]  ([P1] 并行形式)
+    M^S[t, s] = exp(cum[t] - cum[s]), cum = inclusive prefix sum of log_a
+                ([P1] 与已有模型的组合; Mamba-2 reading, see module docstring)
+    Both are zero above the diagonal (s > t).
+    """
+    log_a = _f64(log_a)
+    lam = _f64(lam)
+    T = log_a.shape[0]
+    cum = np.cumsum(log_a)
+    lev = level_rows(t0, t1, T)
+    causal = lev >= 0
+    rows = np.arange(t0, t1)[:, None]
+    mh = np.where(causal, lam[rows, np.maximum(lev, 0)], 0.0)
+    diff = np.where(causal, cum[t0:t1, None] - cum[None, :], -np.inf)
+    return mh * np.exp(diff)
+
+
+def forward(q, k, v, log_a, lam, row_block: int = 1024) -> np.ndarray:
+    """Dense fp64 forward for all (b, h).
+
+    q, k: [B, H, T, dk]; v: [B, H, T, dv]; log_a: [B, H, T]; lam: [B, H, T, L]
+    with L = bit_length(T-1) + 1.  Returns out [B, H, T, dv] float64.
+    """
+    q, k, v, log_a, lam = (_f64(x) for x in (q, k, v, log_a, lam))
+    B, H, T, _ = q.shape
+    dv = v.shape[-1]
+    L = int(T - 1).bit_length() + 1
+    if lam.shape[-1] != L:
+        raise ValueError(f"lambda has {lam.shape[-1]} levels, expected {L}")
+    out = np.zeros((B, H, T, dv))
+    for b in range(B):
+        for h in range(H):
+            for t0 in range(0, T, row_block):
+                t1 = min(T, t0 + row_block)
+                m = mask_rows(log_a[b, h], lam[b, h], t0, t1)
+                a = q[b, h, t0:t1] @ k[b, h].T          # (QK^T) rows
+                out[b, h, t0:t1] = (a * m) @ v[b, h]
+    return out
+
+
+def forward_rows(q, k, v, log_a, lam, bh: tuple[int, int], rows) -> np.ndarray:
+    """Selected output rows of one (b, h): o_t = sum_{s<=t} M[t,s] (q_t . k_s) v_s.
+
+    Same definition as ``forward`` evaluated one query row at a time, for
+    spot checks at sizes where the full O(T^2) product is too slow.
+    """
+    b, h = bh
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+    la, lm = _f64(log_a[b, h]), _f64(lam[b, h])
+    cum = np.cumsum(la)
+    res = []
+    for t in rows:
+        t = int(t)
+        lev = np.empty(t + 1, dtype=np.int64)
+        for level, lo, hi in fenwick_buckets(t):
+            lev[lo:hi] = level
+        m = lm[t, lev] * np.exp(cum[t] - cum[: t + 1])
+        res.append((m * (kh[: t + 1] @ qh[t])) @ vh[: t + 1])
+    return np.stack(res) if res else np.zeros((0, vh.shape[-1]))
+
+
+# --------------------------------------------------------------------------
+# Decode: per-level states with the lssb merge / promote rule
+# --------------------------------------------------------------------------
+
+def lssb(t: int) -> int:
+    """0-based index of the lowest set bit of t > 0 ([P1] 解码；[P5] slide 21)."""
+    if t <= 0:
+        raise ValueError("lssb needs t > 0")
+    return (t & -t).bit_length() - 1
+
+
+def decode_step(states, q, k, v, log_a, lam, t):
+    """One decode step for every (sequence, head), in fp64.
+
+    states: [N, H, L, dk, dv] holding S_{t-1} (k-major, S = sum k v^T);
+    q, k: [N, H, dk]; v: [N, H, dv]; log_a: [N, H]; lam: [N, H, L];
+    t: [N] positions of the incoming tokens.
+    Returns (out [N, H, dv], new_states) and leaves ``states`` untouched.
+
+    Update at position t with m = lssb(t)  ([P1] 解码：基于 lssb 的状态更新;
+    [P5] slide 21):
+      level m+1  <- a_t * (S^0 + S^1 + ... + S^m)   (lower levels promoted)
+      levels 1..m <- 0
+      levels > m+1 <- a_t * S^l                     (kept, decayed)
+      level 0    <- k_t v_t^T                       (the new token)
+    At t = 0 every level is cleared first.  Readout ([P1] 循环形式与输出计算):
+      o_t = sum_l lam[t, l] * q_t^T S_t^l.
+    Positions outside [0, 2^(L-1)) give a NaN output row and unchanged states.
+    """
+    S = _f64(states).copy()
+    q, k, v, log_a, lam = (_f64(x) for x in (q, k, v, log_a, lam))
+    t = np.asarray(t.detach().cpu().numpy() if hasattr(t, "detach") else t, dtype=np.int64)
+    N, H, L, dk, dv = S.shape
+    out = np.zeros((N, H, dv))
+    for i in range(N):
+        ti = int(t[i])
+        if ti < 0 or ti >= (1 << (L - 1)):
+            out[i] = np.nan
+            continue
+        for h in range(H):
+            lev = S[i, h]
+            a = np.exp(log_a[i, h])
+            if ti == 0:
+                lev[:] = 0.0
+            else:
+                m = lssb(ti)
+                merged = a * lev[: m + 1].sum(axis=0)
+                lev[m + 2:] *= a
+                lev[1: m + 1] = 0.0
+                lev[m + 1] = merged
+            lev[0] = np.outer(k[i, h], v[i, h])
+            out[i, h] = np.einsum("l,d,lde->e", lam[i, h], q[i, h], lev)
+    return out, S
+
+
+def recurrent_forward(q, k, v, log_a, lam) -> np.ndarray:
+    """Run decode_step over t = 0..T-1 from empty states for every (b, h).
+
+    Same inputs and output as ``forward``; used to pin the parallel form to
+    the recurrent form ([P1] 解码 and 并行形式 describe the same operator).
+    """
+    q, k, v, log_a, lam = (_f64(x) for x in (q, k, v, log_a, lam))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    out = np.zeros((B, H, T, dv))
+    states = np.zeros((B, H, L, dk, dv))
+    for t in range(T):
+        o, states = decode_step(states, q[:, :, t], k[:, :, t], v[:, :, t],
+                                log_a[:, :, t], lam[:, :, t], np.full(B, t))
+        out[:, :, t] = o
+    return out

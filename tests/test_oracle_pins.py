@@ -1,0 +1,311 @@
+"""Pins of the CPU oracle to facts the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print (fixtures under tests/golden/, each with its source), closed
+forms, special cases that reduce to textbook recurrences, invariants, and
+brute force over explicit bucket sets.  Page abbreviations:
+
+[P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制"
+[P4] "动态线性注意力 — HF Daily Papers"
+[P5] "論文紹介：Log Linear Attention" (journal-club slides)
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import loglinear_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_inputs(rng, B, H, T, dk, dv, decay=0.3, lam_scale=1.0):
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    log_a = -decay * rng.random((B, H, T))
+    L = int(T - 1).bit_length() + 1
+    lam = lam_scale * (0.25 + rng.random((B, H, T, L)))
+    return q, k, v, log_a, lam
+
+
+# ---------------------------------------------------------------- indexing
+
+def test_level_table_8x8_matches_page():
+    """[P1] 并行形式: the printed 8x8 lambda-exponent pattern."""
+    rows = []
+    with open(os.path.join(GOLDEN, "level_table_8x8.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            rows.append([-1 if x == "-" else int(x) for x in line.split()])
+    assert np.array_equal(oracle.level_matrix(8), np.array(rows))
+
+
+def test_t7_partition_matches_pages():
+    """[P1] 前缀的层次化分解 and [P5] slides 19-20: t = 7 -> {7},{6},{4,5},{0..3}."""
+    with open(os.path.join(GOLDEN, "t7_partition.json")) as f:
+        g = json.load(f)
+    got = {str(lev): list(range(lo, hi)) for lev, lo, hi in oracle.fenwick_buckets(g["t"])}
+    assert got == g["buckets"]
+
+
+def test_partition_properties_all_t():
+    """[P1] 前缀的层次化分解 / [P4] 多状态线性注意力: for every t < 4096 the buckets are
+    disjoint and cover [0, t]; one non-empty bucket per set bit of t plus the
+    sentinel; bucket l has size 2^(l-1); at most ceil(log2(t+1)) + 1 buckets."""
+    for t in range(4096):
+        bk = oracle.fenwick_buckets(t)
+        covered = np.zeros(t + 1, dtype=int)
+        for lev, lo, hi in bk:
+            covered[lo:hi] += 1
+            assert hi - lo == (1 if lev == 0 else 2 ** (lev - 1))
+            if lev > 0:
+                assert (t >> (lev - 1)) & 1, "bucket level must match a set bit of t"
+        assert np.all(covered == 1)
+        assert len(bk) == bin(t).count("1") + 1
+        assert len(bk) <= math.ceil(math.log2(t + 1)) + 1
+
+
+def test_power_of_two_history_is_one_bucket():
+    """[P1] 前缀的层次化分解 (t = 8 example): at t = 2^k the whole history [0, t)
+    is a single bucket, at level k+1."""
+    for kk in range(12):
+        t = 1 << kk
+        assert sorted(oracle.fenwick_buckets(t)) == [(0, t, t + 1), (kk + 1, 0, t)]
+
+
+def test_level_closed_form():
+    """Closed form level(t,s) = bit_length(t xor s) for s < t (0 at s == t)
+    against the bucket walk, every pair up to T = 512."""
+    lv = oracle.level_matrix(512)
+    t, s = np.tril_indices(512)
+    closed = np.array([0 if a == b else int(a ^ b).bit_length() for a, b in zip(t, s)])
+    assert np.array_equal(lv[t, s], closed)
+
+
+def test_chunk_level_example():
+    """[P1] 两阶段计算 example (T=8, C=2): levels <= log2(C) stay inside a chunk;
+    level 2 links chunk 0->1 and 2->3, level 3 links {0,1} -> {2,3}."""
+    with open(os.path.join(GOLDEN, "chunk_levels_T8_C2.json")) as f:
+        g = json.load(f)
+    T, C = g["T"], g["C"]
+    lv = oracle.level_matrix(T)
+    inter = {}
+    for t in range(T):
+        for s in range(t + 1):
+            if t // C == s // C:
+                assert lv[t, s] <= g["intra_max_level"]
+            else:
+                inter.setdefault(str(lv[t, s]), set()).add((s // C, t // C))
+    assert {k: sorted(map(list, v)) for k, v in inter.items()} == {
+        k: sorted(v) for k, v in g["inter"].items()}
+
+
+# ---------------------------------------------------------------- forward
+
+def test_no_decay_unit_lambda_is_causal_linear_attention():
+    """lambda == 1 and log_a == 0: o_t = q_t^T sum_{s<=t} k_s v_s^T (prefix sums
+    of outer products, [P1] 循环形式 degenerate case)."""
+    rng = np.random.default_rng(1)
+    q, k, v, _, _ = _rand_inputs(rng, 1, 2, 37, 5, 3)
+    L = int(36).bit_length() + 1
+    got = oracle.forward(q, k, v, np.zeros((1, 2, 37)), np.ones((1, 2, 37, L)))
+    kv = np.cumsum(np.einsum("bhtd,bhte->bhtde", k, v), axis=2)
+    want = np.einsum("bhtd,bhtde->bhte", q, kv)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_level_independent_lambda_is_gated_linear_attention():
+    """[P1] 循环形式 退化条件: lambda_t^l = c_t for all l reduces to gated linear
+    attention S_t = a_t S_{t-1} + k_t v_t^T, o_t = c_t q_t^T S_t."""
+    rng = np.random.default_rng(2)
+    B, H, T, dk, dv = 1, 2, 45, 4, 3
+    q, k, v, log_a, _ = _rand_inputs(rng, B, H, T, dk, dv, decay=0.5)
+    c = 0.5 + rng.random((B, H, T))
+    L = int(T - 1).bit_length() + 1
+    lam = np.repeat(c[..., None], L, axis=-1)
+    got = oracle.forward(q, k, v, log_a, lam)
+    want = np.zeros_like(got)
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv))
+            for t in range(T):
+                S = np.exp(log_a[b, h, t]) * S + np.outer(k[b, h, t], v[b, h, t])
+                want[b, h, t] = c[b, h, t] * (q[b, h, t] @ S)
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+
+
+def test_forward_equals_bucket_brute_force():
+    """[P1] 循环形式与输出计算: o_t = sum_l lam_t^l q_t^T S_t^l with
+    S_t^l = sum_{s in bucket l} M^S[t,s] k_s v_s^T, by explicit loops."""
+    rng = np.random.default_rng(3)
+    B, H, T, dk, dv = 1, 1, 23, 3, 2
+    q, k, v, log_a, lam = _rand_inputs(rng, B, H, T, dk, dv, decay=0.7)
+    got = oracle.forward(q, k, v, log_a, lam)[0, 0]
+    for t in range(T):
+        o = np.zeros(dv)
+        for lev, lo, hi in oracle.fenwick_buckets(t):
+            S = np.zeros((dk, dv))
+            for s in range(lo, hi):
+                decay = math.exp(sum(log_a[0, 0, r] for r in range(s + 1, t + 1)))
+                S += decay * np.outer(k[0, 0, s], v[0, 0, s])
+            o += lam[0, 0, t, lev] * (q[0, 0, t] @ S)
+        np.testing.assert_allclose(got[t], o, rtol=1e-11, atol=1e-12)
+
+
+def test_one_hot_lambda_selects_one_bucket():
+    """With lambda one-hot at level l0 the output is the decayed attention over
+    exactly the level-l0 bucket; any bucket-membership error is O(1)."""
+    rng = np.random.default_rng(4)
+    T, dk, dv = 40, 4, 4
+    q, k, v, log_a, _ = _rand_inputs(rng, 1, 1, T, dk, dv, decay=0.1)
+    L = int(T - 1).bit_length() + 1
+    for l0 in range(L):
+        lam = np.zeros((1, 1, T, L))
+        lam[..., l0] = 1.0
+        got = oracle.forward(q, k, v, log_a, lam)[0, 0]
+        cum = np.cumsum(log_a[0, 0])
+        for t in range(T):
+            want = np.zeros(dv)
+            for lev, lo, hi in oracle.fenwick_buckets(t):
+                if lev == l0:
+                    for s in range(lo, hi):
+                        want += math.exp(cum[t] - cum[s]) * (q[0, 0, t] @ k[0, 0, s]) * v[0, 0, s]
+            np.testing.assert_allclose(got[t], want, rtol=1e-11, atol=1e-12)
+
+
+def test_offdiagonal_blocks_rank_one():
+    """[P1] HODLR 结构与低秩性: every off-diagonal block of the recursive bisection
+    of M = M^S ⊙ M^H has rank 1 (also with the decay mask, [P1] 与已有模型的组合)."""
+    rng = np.random.default_rng(5)
+    T = 64
+    log_a = -0.2 * rng.random(T)
+    L = int(T - 1).bit_length() + 1
+    lam = 0.5 + rng.random((T, L))
+    M = O.mask_rows(log_a, lam, 0, T)
+    checked = 0
+    size = T
+    while size >= 2:
+        half = size // 2
+        for start in range(0, T, size):
+            blk = M[start + half:start + size, start:start + half]
+            sv = np.linalg.svd(blk, compute_uv=False)
+            assert sv[0] > 0
+            assert sv[1] / sv[0] < 1e-12 if len(sv) > 1 else True
+            checked += 1
+        size = half
+    assert checked == T - 1
+
+
+def test_forward_rows_matches_forward():
+    rng = np.random.default_rng(6)
+    q, k, v, log_a, lam = _rand_inputs(rng, 2, 2, 50, 4, 3)
+    full = oracle.forward(q, k, v, log_a, lam)
+    rows = [0, 1, 17, 31, 32, 49]
+    got = oracle.forward_rows(q, k, v, log_a, lam, (1, 0), rows)
+    np.testing.assert_allclose(got, full[1, 0, rows], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- decode
+
+def test_recurrent_equals_parallel():
+    """[P1] 解码：基于 lssb 的状态更新 vs [P1] 并行形式: running the lssb decode rule
+    from t = 0 reproduces the dense forward (to rounding)."""
+    rng = np.random.default_rng(7)
+    q, k, v, log_a, lam = _rand_inputs(rng, 2, 2, 70, 4, 3, decay=0.3)
+    dense = oracle.forward(q, k, v, log_a, lam)
+    rec = oracle.recurrent_forward(q, k, v, log_a, lam)
+    np.testing.assert_allclose(rec, dense, rtol=1e-11, atol=1e-12)
+
+
+def test_decode_zero_pattern():
+    """After the step to t: levels 1..lssb(t) are zero, level lssb(t)+1 holds the
+    promoted merge, levels of unset higher bits stay zero."""
+    rng = np.random.default_rng(8)
+    N, H, L, dk, dv = 6, 1, 8, 3, 2
+    ts = np.array([1, 2, 3, 8, 12, 127])
+    states = np.zeros((N, H, L, dk, dv))
+    for i, t in enumerate(ts):
+        prev = t - 1
+        states[i, :, 0] = rng.standard_normal((H, dk, dv))
+        for b in range(L - 1):
+            if (prev >> b) & 1:
+                states[i, :, b + 1] = rng.standard_normal((H, dk, dv))
+    q = rng.standard_normal((N, H, dk)); k = rng.standard_normal((N, H, dk))
+    v = rng.standard_normal((N, H, dv)); log_a = -rng.random((N, H)); lam = rng.random((N, H, L))
+    _, new = oracle.decode_step(states, q, k, v, log_a, lam, ts)
+    for i, t in enumerate(ts):
+        m = oracle.lssb(int(t))
+        nz = [bool(np.any(new[i, 0, lev] != 0)) for lev in range(L)]
+        want = [True] + [False] * L
+        for lev in range(1, L):
+            want[lev] = (lev == m + 1) or (lev > m + 1 and (t >> (lev - 1)) & 1 == 1)
+        assert nz == want[:L], (t, nz)
+
+
+def test_decode_out_of_range_t_gives_nan_and_keeps_states():
+    rng = np.random.default_rng(9)
+    states = rng.standard_normal((3, 1, 4, 2, 2))
+    q = rng.standard_normal((3, 1, 2)); v = rng.standard_normal((3, 1, 2))
+    out, new = oracle.decode_step(states, q, q, v, np.zeros((3, 1)), np.ones((3, 1, 4)),
+                                  np.array([-1, 8, 3]))
+    assert np.all(np.isnan(out[:2])) and np.all(np.isfinite(out[2]))
+    np.testing.assert_array_equal(new[:2], states[:2])
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _strict_decode_rule(states, q, k, v, log_a, lam, t):
+    """The slide's literal 'clear 0 < l < lssb(t)' (exclusive) variant."""
+    S = np.array(states, dtype=np.float64).copy()
+    N, H, L, dk, dv = S.shape
+    out = np.zeros((N, H, dv))
+    for i in range(N):
+        ti = int(t[i])
+        for h in range(H):
+            lev = S[i, h]
+            a = math.exp(log_a[i, h])
+            if ti == 0:
+                lev[:] = 0
+            else:
+                m = O.lssb(ti)
+                merged = a * lev[: m + 1].sum(axis=0)
+                lev[m + 2:] *= a
+                lev[1:m] = 0.0           # exclusive upper end: level m survives
+                lev[m + 1] = merged
+            lev[0] = np.outer(k[i, h], v[i, h])
+            out[i, h] = np.einsum("l,d,lde->e", lam[i, h], q[i, h], lev)
+    return out, S
+
+
+@pytest.mark.parametrize("mistake", ["strict_decode", "decay_sign", "lambda_by_key", "transposed_qk"])
+def test_planted_mistakes_are_caught(monkeypatch, mistake):
+    """Plant a plausible mistake in the oracle (CPU only) and check that the
+    recurrent == parallel pin or the gated-linear-attention pin rejects it."""
+    rng = np.random.default_rng(10)
+    q, k, v, log_a, lam = _rand_inputs(rng, 1, 1, 24, 3, 3, decay=0.4)
+    if mistake == "strict_decode":
+        monkeypatch.setattr(O, "decode_step", _strict_decode_rule)
+    elif mistake == "decay_sign":
+        real = O.mask_rows
+        monkeypatch.setattr(O, "mask_rows", lambda la, lm, t0, t1: real(-np.asarray(la), lm, t0, t1))
+    elif mistake == "lambda_by_key":
+        def by_key(la, lm, t0, t1):
+            la, lm = np.asarray(la, float), np.asarray(lm, float)
+            T = la.shape[0]
+            cum = np.cumsum(la)
+            lev = O.level_rows(t0, t1, T)
+            cols = np.arange(T)[None, :].repeat(t1 - t0, 0)
+            mh = np.where(lev >= 0, lm[cols, np.maximum(lev, 0)], 0.0)
+            return mh * np.exp(np.where(lev >= 0, cum[t0:t1, None] - cum[None, :], -np.inf))
+        monkeypatch.setattr(O, "mask_rows", by_key)
+    elif mistake == "transposed_qk":
+        real_fwd = O.forward
+        monkeypatch.setattr(O, "forward", lambda q_, k_, *a, **kw: real_fwd(k_, q_, *a, **kw))
+    dense = O.forward(q, k, v, log_a, lam)
+    rec = O.recurrent_forward(q, k, v, log_a, lam)
+    assert not np.allclose(dense, rec, rtol=1e-6, atol=1e-8)
