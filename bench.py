@@ -1,0 +1,201 @@
+"""Benchmark of the log-linear attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--no-cpu-baseline]
+
+A step is one loglinear_fwd call (segment-state, node and sweep kernels) over
+one batch of synthetic inputs already resident in HBM.  Prints ONE JSON line.
+Default workload: log-linear Mamba-2 forward, B=2, H=16, T=16384, dk=dv=128,
+bf16 q/k/v, fp32 log_a / lambda / out, L=15, C=64.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd tokens/sec + TFLOP/s vs bf16 MFMA peak, log-linear Mamba-2 at T=16K"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def algorithmic_flops(B, H, T, dk, dv, C):
+    """Multiply-adds x2 the method must do (not the dense work it avoids):
+    causal intra-chunk pairs, chunk states, popcount-weighted inter-chunk reads."""
+    N = -(-T // C)
+    intra = 0
+    for n in range(N):
+        c = min(C, T - n * C)
+        intra += c * (c + 1) // 2 * 2 * (dk + dv)
+    states = (N - 1) * 2 * C * dk * dv
+    inter = sum(bin(n).count("1") for n in range(N)) * 2 * C * dk * dv
+    return B * H * (intra + states + inter)
+
+
+def algorithmic_bytes(B, H, T, dk, dv, L, in_bytes=2):
+    """Minimal HBM traffic: q, k, v, log_a, lambda read once, fp32 out written once."""
+    per = (2 * dk + dv) * in_bytes + 4 + 4 * L + 4 * dv
+    return B * H * T * per
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("loglinear_fwd.hip", "ll_device.h", "ll_internal.h", "loglinear_api.cpp"):
+        with open(os.path.join(ROOT, "log_linear_attention_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per sweep launch from committed rocprofv3 --pmc summaries,
+    or None when they are missing or were taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"fwd_sweep_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The CPU oracle (fp64 NumPy, dense O(T^2)) on whole (b, h) head-sequences
+    of the same workload until ~budget_s of work; rate in the metric's unit."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0])
+    except Exception:
+        threads = 0
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        b, h = divmod(done, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.forward(q[sl], k[sl], v[sl], la[sl], lam[sl])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= w.B * w.H:
+            break
+    tokens = done * w.T / w.H   # one token = one position of one batch row, all H heads
+    return {
+        "value": tokens / el, "unit": "tokens/s", "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"oracle.forward (fp64 NumPy, dense masked QK^T V) on {done} of {w.B * w.H} (b,h) "
+                  f"head-sequences of T={w.T}, {el:.1f} s; rate = {done}*T/H tokens / time",
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lm_B2H16_T16384_dk128_dv128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seg-log2", type=int, default=-1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import log_linear_attention_attn_amd as ll
+    import workloads as W
+
+    w = W.FWD_WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    base = W.make_fwd_inputs(w)
+    sets = [[t.to(dev) for t in base]]
+    # a second input set (same values, other buffers) so consecutive steps do not
+    # find their inputs in the 256 MB infinity cache
+    sets.append([t.clone() for t in sets[0]])
+    out = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.float32, device=dev)
+    K, Wm = args.steps, args.warmup
+
+    def step(i, ev=None):
+        q, k, v, la, lam = sets[i % len(sets)]
+        ll.fwd_ex(q, k, v, la, lam, C=w.C, out=out, seg_log2=args.seg_log2, phase_events=ev)
+
+    for i in range(Wm):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for s in evs:
+        for e in s:
+            e.record()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / K
+    phases = [[s[j].elapsed_time(s[j + 1]) for j in range(3)] for s in evs]
+    seg_ms, node_ms, sweep_ms = (sum(p[j] for p in phases) / K for j in range(3))
+
+    flops = algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv, w.C)
+    in_bytes = 2 if w.dtype == "bf16" else 4
+    abytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv, w.L, in_bytes)
+    tokens = w.B * w.T
+    tflops = flops / (ms * 1e-3) / 1e12
+    sweep_gbs = abytes / (sweep_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name)
+    rec = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "C": w.C, "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_a/lambda/out",
+                   "decay": w.decay, "seed": w.seed},
+        "head_tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+        "tflops": tflops,
+        "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "algorithmic_flops": flops,
+        "algorithmic_bytes": abytes,
+        "frac_roofline_step": max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBS * 1e9)) / (ms * 1e-3),
+        "kernels_ms": {"seg_state": seg_ms, "seg_node": node_ms, "fwd_sweep": sweep_ms},
+        "wall_ms_per_step": wall / K * 1e3,
+        "roofline": {
+            "kernel": "fwd_sweep_kernel",
+            "bound": "hbm",
+            "achieved": sweep_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": sweep_gbs / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "mfma_tflops": flops / (sweep_ms * 1e-3) / 1e12,
+        },
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * loglinear.h — C ABI of the MI355X (gfx950) log-linear attention library.
+ *
+ * The operator (page "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性
+ * 复杂度注意力机制", sections 并行形式 and 与已有模型的组合):
+ *
+ *     O = (Q K^T ⊙ M^S ⊙ M^H) V,
+ *     M^H[t,s] = lambda[t, level(t,s)],   M^S[t,s] = exp(cum[t] - cum[s]),  s <= t,
+ *
+ * where level(t,s) is the Fenwick-bucket level of key s seen from query t
+ * (section 层级判定算法; 0 for s == t) and cum is the inclusive prefix sum of
+ * log_a (the Mamba-2 scalar decay).  No softmax and no 1/sqrt(dk) scale.
+ *
+ * Common conventions
+ *   - Every tensor pointer is a DEVICE pointer to row-major, contiguous memory
+ *     owned by the caller.  Nothing is retained after a call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = the null stream)
+ *     and return once the work is enqueued.  No host/device synchronisation.
+ *   - Return value: LL_OK (0) or a negative status; loglinear_strerror() gives
+ *     its text.  Argument errors are detected on the host before any HIP call,
+ *     leave all buffers untouched, and need no GPU.
+ *   - Results are deterministic: no atomics, fixed reduction order.
+ *   - `out` must not alias any input.
+ *   - L = loglinear_num_levels(T) = bit_length(T-1) + 1 lambda levels.
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16_t storage).
+ */
+#ifndef LOGLINEAR_H
+#define LOGLINEAR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum loglinear_status {
+  LL_OK = 0,
+  LL_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  LL_ERR_SHAPE = -2,       /* a size is negative, inconsistent or out of range */
+  LL_ERR_UNSUPPORTED = -3, /* valid sizes that this build has no kernel for    */
+  LL_ERR_HIP = -4,         /* a HIP runtime call (launch / allocation) failed  */
+  LL_ERR_WORKSPACE = -5    /* caller workspace too small                       */
+};
+
+enum loglinear_dtype { LL_BF16 = 0, LL_F32 = 1 };
+
+/* Number of lambda levels for sequence length T >= 1: bit_length(T-1) + 1
+ * (T = 64 -> 7, 2048 -> 12, 16384 -> 15, 65536 -> 17).  Returns 0 for T < 1. */
+int loglinear_num_levels(int T);
+
+/*
+ * Forward, bf16 inputs (the performance path).
+ *   q, k   : [B, H, T, dk]  bf16
+ *   v      : [B, H, T, dv]  bf16
+ *   log_a  : [B, H, T]      fp32, per-token log decay (0 = no decay)
+ *   lambda : [B, H, T, L]   fp32, level weights lambda[t, l]
+ *   out    : [B, H, T, dv]  fp32, written completely
+ *   C      : chunk size of the chunkwise algorithm (page above, section
+ *            训练：分块并行扫描算法): pairs inside one C-token chunk (levels
+ *            <= log2 C) are computed densely, all other levels through
+ *            chunk states.  C in {16, 32, 64}.
+ * Sizes: B, H, T >= 0 (any zero -> nothing to do, LL_OK, pointers unchecked);
+ * T need not be a multiple of C (the last chunk is ragged);
+ * dk a multiple of 16 in [16, 128]; dv a multiple of 16 in [16, 1024].
+ * Scratch: allocated stream-ordered (hipMallocAsync) on `stream` and freed
+ * the same way; allocation failure returns LL_ERR_HIP.
+ */
+int loglinear_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                  const float* lambda, float* out, int B, int H, int T, int dk, int dv,
+                  int C, void* stream);
+
+/* Forward with fp32 q, k, v (fp32 matrix-core arithmetic throughout).  Same
+ * contract as loglinear_fwd otherwise. */
+int loglinear_fwd_f32(const float* q, const float* k, const float* v, const float* log_a,
+                      const float* lambda, float* out, int B, int H, int T, int dk, int dv,
+                      int C, void* stream);
+
+/*
+ * Options for loglinear_fwd_ex.
+ *   dtype        : LL_BF16 or LL_F32 (type of q, k, v).
+ *   seg_log2     : -1 = automatic.  Otherwise the sequence is processed in
+ *                  segments of 2^seg_log2 chunks (0..12); states of levels that
+ *                  span whole segments are built by a separate segment pass.
+ *                  Changes only the rounding order, never the result's
+ *                  definition; exposed so every path can be exercised at small T.
+ *   workspace    : NULL = allocate stream-ordered on `stream`; otherwise a
+ *                  device buffer of at least loglinear_fwd_workspace_size()
+ *                  bytes, 256-byte aligned, owned by the caller, not used by
+ *                  any concurrent call.
+ *   workspace_bytes : size of `workspace`.
+ *   phase_events : NULL, or 4 caller-created hipEvent_t recorded on `stream`
+ *                  before the segment-state kernel, before the node kernel,
+ *                  before the sweep kernel and after it (kernels that a plan
+ *                  does not need are skipped, their events still recorded), so
+ *                  a caller can time each kernel of one call.
+ */
+typedef struct {
+  int dtype;
+  int seg_log2;
+  void* workspace;
+  size_t workspace_bytes;
+  void* const* phase_events;
+} loglinear_fwd_opts;
+
+int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* log_a,
+                     const float* lambda, float* out, int B, int H, int T, int dk, int dv,
+                     int C, const loglinear_fwd_opts* opts, void* stream);
+
+/* Workspace bytes loglinear_fwd_ex needs for these sizes (0 if none); seg_log2
+ * as in loglinear_fwd_opts.  Returns (size_t)-1 for invalid sizes. */
+size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2);
+
+/*
+ * Decode states: a HOST struct describing a caller-owned DEVICE buffer
+ *   data : [N, H, L, dk, dv] fp32, row-major (dv fastest).
+ * Slot l holds the level-l state S^(l) = sum over the level-l bucket of
+ * decay * k v^T, stored k-major (dk x dv) — the transpose of the pages' v k^T.
+ */
+typedef struct {
+  float* data;
+  int N, H, L, dk, dv;
+} loglinear_states;
+
+/*
+ * One O(log T) decode step for N sequences x H heads (page above, section
+ * 解码：基于 lssb 的状态更新; slide 21 of "論文紹介：Log Linear Attention").
+ *   states : on entry S_{t-1} of every (sequence, head), levels dead at t-1
+ *            equal to 0; on return S_t, updated in place.  With m = lssb(t)
+ *            (index of the lowest set bit): level m+1 <- a_t * sum_{l<=m} S^l,
+ *            levels 1..m <- 0, levels > m+1 that are live <- a_t * S^l, level
+ *            0 <- k_t v_t^T; a_t = exp(log_a).  At t = 0 all levels are
+ *            cleared before level 0 is written.  Levels above m+1 that are
+ *            dead at t are neither read nor written.
+ *   q, k   : [N, H, dk] bf16;  v : [N, H, dv] bf16
+ *   log_a  : [N, H] fp32;  lambda : [N, H, L] fp32
+ *   t      : [N] int32 DEVICE array, position of the incoming token
+ *   out    : [N, H, dv] fp32, o = sum_l lambda[l] q^T S_t^l
+ * Valid t: 0 <= t < 2^(L-1).  A t outside that range cannot be checked on the
+ * host: that sequence's out rows are set to NaN and its states left unchanged.
+ * Sizes: dk, dv multiples of 4 in [4, 1024]; 1 <= L <= 31; N, H >= 0.
+ */
+int loglinear_decode_step(const loglinear_states* states, const void* q, const void* k,
+                          const void* v, const float* log_a, const float* lambda,
+                          const int* t, float* out, void* stream);
+
+/* Same as loglinear_decode_step with fp32 q, k, v. */
+int loglinear_decode_step_f32(const loglinear_states* states, const float* q,
+                              const float* k, const float* v, const float* log_a,
+                              const float* lambda, const int* t, float* out, void* stream);
+
+/*
+ * Test export: lev[t*T + s] = level(t, s) for s <= t and -1 for s > t (int8,
+ * DEVICE buffer of T*T bytes), computed on the GPU with the same device
+ * helper the kernels use (section 层级判定算法).  1 <= T <= 8192.
+ */
+int loglinear_level_table(signed char* lev, int T, void* stream);
+
+/* Static text for a status code. */
+const char* loglinear_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGLINEAR_H */

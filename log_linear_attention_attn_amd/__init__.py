@@ -1,0 +1,242 @@
+"""Log-linear attention on MI355X (gfx950): thin ctypes binding of libloglinear.so.
+
+Every step of the computation runs in the HIP kernels of libloglinear.so; this
+module only checks tensor metadata, passes device pointers and the current HIP
+stream, and turns status codes into exceptions.  There is no CPU fallback: if
+the library is not built, every call raises.
+
+Entry points (same names as the C ABI in include/loglinear.h):
+    fwd(q, k, v, log_a, lam, C=64, out=None)            bf16 or fp32 q/k/v
+    fwd_ex(..., seg_log2=-1, workspace=None)            explicit options
+    fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1)
+    decode_step(states, q, k, v, log_a, lam, t, out=None)
+    level_table(T, device=None)                          int8 [T, T]
+    num_levels(T)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LogLinearError", "lib", "library_path", "num_levels", "fwd", "fwd_ex",
+    "fwd_workspace_size", "decode_step", "level_table", "strerror",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libloglinear.so")
+_lib = None
+
+LL_BF16, LL_F32 = 0, 1
+EXPORTED_SYMBOLS = (
+    "loglinear_num_levels", "loglinear_fwd", "loglinear_fwd_f32", "loglinear_fwd_ex",
+    "loglinear_fwd_workspace_size", "loglinear_decode_step", "loglinear_decode_step_f32",
+    "loglinear_level_table", "loglinear_strerror",
+)
+
+
+class LogLinearError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({strerror(status)})")
+        self.status = status
+
+
+class _FwdOpts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("seg_log2", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("phase_events", ctypes.c_void_p)]
+
+
+class _States(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("N", ctypes.c_int), ("H", ctypes.c_int),
+                ("L", ctypes.c_int), ("dk", ctypes.c_int), ("dv", ctypes.c_int)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libloglinear.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m log_linear_attention_attn_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    fwd_args = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i]
+    L.loglinear_num_levels.argtypes = [i]
+    L.loglinear_num_levels.restype = i
+    L.loglinear_fwd.argtypes = fwd_args + [vp]
+    L.loglinear_fwd.restype = i
+    L.loglinear_fwd_f32.argtypes = fwd_args + [vp]
+    L.loglinear_fwd_f32.restype = i
+    L.loglinear_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(_FwdOpts), vp]
+    L.loglinear_fwd_ex.restype = i
+    L.loglinear_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    L.loglinear_fwd_workspace_size.restype = sz
+    dec_args = [ctypes.POINTER(_States), vp, vp, vp, vp, vp, vp, vp, vp]
+    L.loglinear_decode_step.argtypes = dec_args
+    L.loglinear_decode_step.restype = i
+    L.loglinear_decode_step_f32.argtypes = dec_args
+    L.loglinear_decode_step_f32.restype = i
+    L.loglinear_level_table.argtypes = [vp, i, vp]
+    L.loglinear_level_table.restype = i
+    L.loglinear_strerror.argtypes = [i]
+    L.loglinear_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    try:
+        return lib().loglinear_strerror(int(status)).decode()
+    except Exception:  # library missing: still report the number
+        return "unknown"
+
+
+def num_levels(T: int) -> int:
+    return int(lib().loglinear_num_levels(int(T)))
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_dev(name: str, t: torch.Tensor, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _raise(status: int, what: str):
+    if status != 0:
+        raise LogLinearError(status, what)
+
+
+def fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1) -> int:
+    n = lib().loglinear_fwd_workspace_size(B, H, T, dk, dv, C, seg_log2)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, workspace=None,
+           phase_events=None):
+    """Log-linear attention forward through loglinear_fwd_ex.
+
+    q, k: [B, H, T, dk]; v: [B, H, T, dv] (all bf16 or all fp32);
+    log_a: [B, H, T] fp32; lam: [B, H, T, L] fp32 with L = num_levels(T).
+    phase_events: None or 4 recorded torch.cuda.Event(enable_timing=True)
+    objects, re-recorded before / between / after the library's kernels.
+    Returns out [B, H, T, dv] fp32 (allocated unless given).
+    """
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T) if T > 0 else 0
+    _check_dev("q", q, q.dtype, (B, H, T, dk), dev)
+    _check_dev("k", k, q.dtype, (B, H, T, dk), dev)
+    _check_dev("v", v, q.dtype, (B, H, T, dv), dev)
+    _check_dev("log_a", log_a, torch.float32, (B, H, T), dev)
+    _check_dev("lam", lam, torch.float32, (B, H, T, L), dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (B, H, T, dv), dev)
+    ev = None
+    if phase_events is not None:
+        if len(phase_events) != 4:
+            raise ValueError("phase_events needs 4 events")
+        ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in phase_events])
+        if not all(ev):
+            raise ValueError("record each phase event once before passing it")
+    opts = _FwdOpts(LL_BF16 if q.dtype == torch.bfloat16 else LL_F32, int(seg_log2),
+                    _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                    ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
+    st = lib().loglinear_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out),
+                                B, H, T, dk, dv, int(C), ctypes.byref(opts), _stream(dev))
+    _raise(st, "loglinear_fwd_ex")
+    return out
+
+
+def fwd(q, k, v, log_a, lam, C: int = 64, out=None):
+    """Log-linear attention forward (loglinear_fwd for bf16, loglinear_fwd_f32 for fp32)."""
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T) if T > 0 else 0
+    _check_dev("q", q, q.dtype, (B, H, T, dk), dev)
+    _check_dev("k", k, q.dtype, (B, H, T, dk), dev)
+    _check_dev("v", v, q.dtype, (B, H, T, dv), dev)
+    _check_dev("log_a", log_a, torch.float32, (B, H, T), dev)
+    _check_dev("lam", lam, torch.float32, (B, H, T, L), dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (B, H, T, dv), dev)
+    f = lib().loglinear_fwd if q.dtype == torch.bfloat16 else lib().loglinear_fwd_f32
+    st = f(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out), B, H, T, dk, dv, int(C),
+           _stream(dev))
+    _raise(st, "loglinear_fwd")
+    return out
+
+
+def decode_step(states, q, k, v, log_a, lam, t, out=None):
+    """One decode step; updates ``states`` [N, H, L, dk, dv] fp32 in place.
+
+    q, k: [N, H, dk]; v: [N, H, dv] (bf16 or fp32); log_a: [N, H] fp32;
+    lam: [N, H, L] fp32; t: [N] int32.  Returns out [N, H, dv] fp32.
+    """
+    dev = states.device
+    if dev.type != "cuda":
+        raise ValueError("states must be on a GPU device")
+    N, H, L, dk, dv = states.shape
+    _check_dev("states", states, torch.float32, (N, H, L, dk, dv), dev)
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    _check_dev("q", q, q.dtype, (N, H, dk), dev)
+    _check_dev("k", k, q.dtype, (N, H, dk), dev)
+    _check_dev("v", v, q.dtype, (N, H, dv), dev)
+    _check_dev("log_a", log_a, torch.float32, (N, H), dev)
+    _check_dev("lam", lam, torch.float32, (N, H, L), dev)
+    _check_dev("t", t, torch.int32, (N,), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (N, H, dv), dev)
+    desc = _States(states.data_ptr(), N, H, L, dk, dv)
+    f = lib().loglinear_decode_step if q.dtype == torch.bfloat16 else lib().loglinear_decode_step_f32
+    st = f(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(t), _ptr(out),
+           _stream(dev))
+    _raise(st, "loglinear_decode_step")
+    return out
+
+
+def level_table(T: int, device=None):
+    """GPU-computed level table (int8 [T, T], -1 above the diagonal)."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    lev = torch.empty((T, T), dtype=torch.int8, device=dev)
+    _raise(lib().loglinear_level_table(_ptr(lev), int(T), _stream(dev)), "loglinear_level_table")
+    return lev

@@ -1,0 +1,65 @@
+// Internal interfaces between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "loglinear.h"
+
+namespace ll {
+
+// Largest dynamic LDS allocation of one workgroup on gfx950 (160 KiB per CU).
+constexpr int kMaxLds = 160 * 1024;
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_a;
+  const float* lam;
+  float* out;
+  const float* nodes;      // [BH][nseg][dv][DKP] bucket states starting at each segment
+  const float* seg_decay;  // [BH][nseg] total log decay of each segment
+  int BH, T, dk, dv, L;
+  int seg_log2;  // chunks per segment = 2^seg_log2
+  int nseg;
+  int nslot;  // chunk-level Fenwick bits = bit_length(N - 1)
+};
+
+struct SegArgs {
+  const void* k;
+  const void* v;
+  const float* log_a;
+  float* seg_state;  // [BH][nseg][dv][DKP]
+  float* seg_decay;  // [BH][nseg]
+  int BH, T, dk, dv, C, seg_log2, nseg;
+};
+
+struct NodeArgs {
+  const float* seg_state;
+  const float* seg_decay;
+  float* nodes;
+  int nseg;
+  int E;  // elements per state = dv * DKP
+};
+
+struct DecArgs {
+  float* S;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_a;
+  const float* lam;
+  const int* t;
+  float* out;
+  int N, H, L, dk, dv;
+};
+
+int sweep_lds_bytes(int dtype, int C, int DKP, int L, int nslot);
+int launch_sweep(int dtype, int C, int DKP, const FwdArgs& a, int nblocks, hipStream_t s);
+int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStream_t s);
+int launch_seg_nodes(const NodeArgs& a, int BH, hipStream_t s);
+int launch_level_table(signed char* lev, int T, hipStream_t s);
+int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
+
+}  // namespace ll

@@ -1,0 +1,209 @@
+// C ABI of the log-linear attention library: argument validation (host only,
+// before any HIP call), planning of the segmented sweep, workspace handling
+// and kernel dispatch.  Semantics of every entry point: include/loglinear.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ll_internal.h"
+#include "loglinear.h"
+
+namespace {
+
+int bit_length(long long x) {
+  int n = 0;
+  while (x > 0) {
+    ++n;
+    x >>= 1;
+  }
+  return n;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct FwdPlan {
+  int BH, N, L, DKP, seg_log2, nseg, nslot;
+  size_t ws_state, ws_nodes, ws_decay, ws_total;
+};
+
+// Chunks per segment: as large as possible (fewer segment states, less
+// prologue traffic) while still giving the sweep at least ~2048 workgroups
+// (8 per CU on 256 CUs), capped at 16 chunks.
+int auto_seg_log2(long long BH, int D, int N) {
+  int s = 4;
+  while (s > 0) {
+    const long long nseg = (N + (1LL << s) - 1) >> s;
+    if (BH * D * nseg >= 2048) break;
+    --s;
+  }
+  return s;
+}
+
+int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* p) {
+  if (B < 0 || H < 0 || T < 0) return LL_ERR_SHAPE;
+  if (C <= 0 || (C & (C - 1)) != 0) return LL_ERR_SHAPE;
+  if (C != 16 && C != 32 && C != 64) return LL_ERR_UNSUPPORTED;
+  if (dk < 16 || dk % 16 != 0 || dv < 16 || dv % 16 != 0) return LL_ERR_SHAPE;
+  if (dk > 128 || dv > 1024) return LL_ERR_UNSUPPORTED;
+  if (T > (1 << 28)) return LL_ERR_UNSUPPORTED;
+  if (seg_log2 < -1 || seg_log2 > 12) return LL_ERR_SHAPE;
+  if ((long long)B * H > (1LL << 24)) return LL_ERR_UNSUPPORTED;
+  p->BH = B * H;
+  p->N = T > 0 ? (T + C - 1) / C : 0;
+  p->L = T > 0 ? bit_length(T - 1) + 1 : 0;
+  p->DKP = dk <= 32 ? 32 : (dk <= 64 ? 64 : 128);
+  p->nslot = p->N > 1 ? bit_length(p->N - 1) : 0;
+  p->seg_log2 = seg_log2 >= 0 ? seg_log2 : auto_seg_log2(p->BH, dv / 16, p->N);
+  p->nseg = p->N > 0 ? (p->N + (1 << p->seg_log2) - 1) >> p->seg_log2 : 0;
+  if (p->nseg > 1) {
+    const size_t elems = (size_t)p->BH * p->nseg * dv * p->DKP;
+    p->ws_state = align256(elems * sizeof(float));
+    p->ws_nodes = align256(elems * sizeof(float));
+    p->ws_decay = align256((size_t)p->BH * p->nseg * sizeof(float));
+  } else {
+    p->ws_state = p->ws_nodes = p->ws_decay = 0;
+  }
+  p->ws_total = p->ws_state + p->ws_nodes + p->ws_decay;
+  return LL_OK;
+}
+
+int run_fwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
+            const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
+            int seg_log2, void* workspace, size_t workspace_bytes, void* const* events,
+            hipStream_t stream) {
+  FwdPlan p;
+  int st = plan_fwd(B, H, T, dk, dv, C, seg_log2, &p);
+  if (st != LL_OK) return st;
+  if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
+  if (B == 0 || H == 0 || T == 0) return LL_OK;
+  if (!q || !k || !v || !log_a || !lambda || !out) return LL_ERR_NULL;
+  const int lds = ll::sweep_lds_bytes(dtype, C, p.DKP, p.L, p.nslot);
+  if (lds < 0 || lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
+  if (workspace && workspace_bytes < p.ws_total) return LL_ERR_WORKSPACE;
+
+  void* ws = workspace;
+  bool owned = false;
+  if (p.ws_total > 0 && !ws) {
+    if (hipMallocAsync(&ws, p.ws_total, stream) != hipSuccess) return LL_ERR_HIP;
+    owned = true;
+  }
+  float* seg_state = static_cast<float*>(ws);
+  float* nodes = p.ws_total ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_state) : nullptr;
+  float* seg_decay =
+      p.ws_total ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_state + p.ws_nodes) : nullptr;
+
+  auto mark = [&](int i) {
+    if (events && st == LL_OK && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess)
+      st = LL_ERR_HIP;
+  };
+  mark(0);
+  if (p.nseg > 1) {
+    ll::SegArgs sa{k, v, log_a, seg_state, seg_decay, p.BH, T, dk, dv, C, p.seg_log2, p.nseg};
+    const int ndvg = (dv + 127) / 128;
+    st = ll::launch_seg_state(dtype, p.DKP, sa, p.BH * (p.nseg - 1) * ndvg, stream);
+    mark(1);
+    if (st == LL_OK) {
+      ll::NodeArgs na{seg_state, seg_decay, nodes, p.nseg, dv * p.DKP};
+      st = ll::launch_seg_nodes(na, p.BH, stream);
+    }
+  } else {
+    mark(1);
+  }
+  mark(2);
+  if (st == LL_OK) {
+    ll::FwdArgs fa{q, k, v, log_a, lambda, out, nodes, seg_decay, p.BH, T, dk, dv, p.L,
+                   p.seg_log2, p.nseg, p.nslot};
+    const long long pairs = (long long)p.BH * p.nseg;
+    const long long nblocks = ((pairs + 7) / 8) * 8 * (dv / 16);
+    if (nblocks > 0x7fffffffLL) st = LL_ERR_UNSUPPORTED;
+    else st = ll::launch_sweep(dtype, C, p.DKP, fa, static_cast<int>(nblocks), stream);
+  }
+  mark(3);
+  if (owned) {
+    if (hipFreeAsync(ws, stream) != hipSuccess && st == LL_OK) st = LL_ERR_HIP;
+  }
+  return st;
+}
+
+int run_decode(int dtype, const loglinear_states* s, const void* q, const void* k, const void* v,
+               const float* log_a, const float* lambda, const int* t, float* out,
+               hipStream_t stream) {
+  if (!s) return LL_ERR_NULL;
+  if (s->N < 0 || s->H < 0) return LL_ERR_SHAPE;
+  if (s->L < 1 || s->L > 31) return LL_ERR_SHAPE;
+  if (s->dk < 4 || s->dk % 4 != 0 || s->dv < 4 || s->dv % 4 != 0) return LL_ERR_SHAPE;
+  if (s->dk > 1024 || s->dv > 1024) return LL_ERR_UNSUPPORTED;
+  if ((long long)s->N * s->H > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
+  if (s->N == 0 || s->H == 0) return LL_OK;
+  if (!s->data || !q || !k || !v || !log_a || !lambda || !t || !out) return LL_ERR_NULL;
+  ll::DecArgs a{s->data, q, k, v, log_a, lambda, t, out, s->N, s->H, s->L, s->dk, s->dv};
+  return ll::launch_decode(dtype, a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int loglinear_num_levels(int T) { return T >= 1 ? bit_length(T - 1) + 1 : 0; }
+
+int loglinear_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                  const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
+                  void* stream) {
+  return run_fwd(LL_BF16, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, nullptr, 0, nullptr,
+                 static_cast<hipStream_t>(stream));
+}
+
+int loglinear_fwd_f32(const float* q, const float* k, const float* v, const float* log_a,
+                      const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
+                      void* stream) {
+  return run_fwd(LL_F32, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, nullptr, 0, nullptr,
+                 static_cast<hipStream_t>(stream));
+}
+
+int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* log_a,
+                     const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
+                     const loglinear_fwd_opts* opts, void* stream) {
+  if (!opts) return LL_ERR_NULL;
+  return run_fwd(opts->dtype, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, opts->seg_log2,
+                 opts->workspace, opts->workspace_bytes, opts->phase_events,
+                 static_cast<hipStream_t>(stream));
+}
+
+size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2) {
+  FwdPlan p;
+  if (plan_fwd(B, H, T, dk, dv, C, seg_log2, &p) != LL_OK) return static_cast<size_t>(-1);
+  return p.ws_total;
+}
+
+int loglinear_decode_step(const loglinear_states* states, const void* q, const void* k,
+                          const void* v, const float* log_a, const float* lambda, const int* t,
+                          float* out, void* stream) {
+  return run_decode(LL_BF16, states, q, k, v, log_a, lambda, t, out,
+                    static_cast<hipStream_t>(stream));
+}
+
+int loglinear_decode_step_f32(const loglinear_states* states, const float* q, const float* k,
+                              const float* v, const float* log_a, const float* lambda,
+                              const int* t, float* out, void* stream) {
+  return run_decode(LL_F32, states, q, k, v, log_a, lambda, t, out,
+                    static_cast<hipStream_t>(stream));
+}
+
+int loglinear_level_table(signed char* lev, int T, void* stream) {
+  if (T < 1 || T > 8192) return LL_ERR_SHAPE;
+  if (!lev) return LL_ERR_NULL;
+  return ll::launch_level_table(lev, T, static_cast<hipStream_t>(stream));
+}
+
+const char* loglinear_strerror(int status) {
+  switch (status) {
+    case LL_OK: return "success";
+    case LL_ERR_NULL: return "a required pointer is NULL";
+    case LL_ERR_SHAPE: return "a size is negative, inconsistent or out of range";
+    case LL_ERR_UNSUPPORTED: return "sizes are valid but no kernel of this build supports them";
+    case LL_ERR_HIP: return "a HIP runtime call failed";
+    case LL_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,636 @@
+// Log-linear attention forward on gfx950 (MI355X).
+//
+//   O = (Q K^T ⊙ M^S ⊙ M^H) V,  M^H[t,s] = lambda[t, level(t,s)],
+//   M^S[t,s] = exp(cum[t] - cum[s])
+//
+// Pages (cited by title and section):
+//   [P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制"
+//   [P2] "算力终结者来了！华人天团「降维打击」注意力瓶颈，AI狂飙进对数时代"
+//
+// Decomposition ([P1] 训练：分块并行扫描算法; [P2] 高效训练算法).  With chunk size
+// C the level of a pair (t, s) in chunks n > m is log2(C) + bit_length(n ^ m),
+// and pairs inside one chunk have level <= log2(C).  So every query of chunk n
+// sees, besides its own chunk (dense, "intra"), one bucket of whole chunks per
+// set bit b of n: the 2^b chunks just below n's bit b, at level log2(C)+1+b.
+// The bucket's contribution is q_t^T G_{n,b} with G the decayed sum of k v^T
+// over the bucket, weighted by lambda[t, log2(C)+1+b] and the decay from the
+// bucket's end to t.
+//
+// Kernels (one pass over Q, one over K/V per dv slice; states stay on chip):
+//   seg_state_kernel  per (b,h, segment of 2^S chunks): decayed sum of k v^T
+//                     over the segment (bf16 / fp32 matrix cores).
+//   seg_node_kernel   per (b,h, state element): walks the segments with the
+//                     lssb merge rule ([P1] 解码) and emits, for every segment
+//                     g >= 1, the bucket state that starts at g.
+//   fwd_sweep_kernel  per (b,h, segment, 16-wide dv slice): walks the
+//                     segment's chunks in order, keeping the bucket states of
+//                     levels inside the segment in LDS and merging them with
+//                     the lssb rule at chunk granularity; bucket states of
+//                     levels that span whole segments come from
+//                     seg_node_kernel.  Per chunk: intra scores with the
+//                     Fenwick level mask computed in registers, P·V, one
+//                     Q·G product per live level, output, chunk state.
+//
+// bf16 path: Q, K, V are exact bf16 MFMA operands.  The masked scores P and
+// the states G are fp32 values; each is split into bf16 hi + lo and fed to two
+// MFMAs so that their rounding error is ~2^-16 instead of 2^-9.  K scaled by
+// the in-chunk decay (K~) is rounded once to bf16.  fp32 path: fp32 MFMA.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "ll_device.h"
+#include "ll_internal.h"
+
+namespace ll {
+
+__host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
+
+template <int C>
+struct Log2C;
+template <>
+struct Log2C<16> { static constexpr int v = 4; };
+template <>
+struct Log2C<32> { static constexpr int v = 5; };
+template <>
+struct Log2C<64> { static constexpr int v = 6; };
+
+// LDS layout of fwd_sweep_kernel (bytes).  Used by the kernel and by the host
+// to size the dynamic shared memory.
+template <typename IT, int C, int DKP>
+struct SweepCfg {
+  static constexpr bool BF = sizeof(IT) == 2;
+  static constexpr int NW = C / 16;          // waves; wave w owns query rows 16w..16w+15
+  static constexpr int NT = NW * 64;
+  static constexpr int PADE = BF ? 8 : 4;    // row padding (elements) against bank conflicts
+  static constexpr int LDQ = DKP + PADE;     // Q, K rows: [token][dk]
+  static constexpr int CK = C < 32 ? 32 : C; // key extent of transposed operands (>= one bf16 K-step)
+  static constexpr int LDK = CK + PADE;      // K~^T rows [dk][key], V^T rows [dv][key]
+  static constexpr int LDG = DKP + PADE;     // state rows G^T [dv][dk]
+  static constexpr int VEC = 16 / (int)sizeof(IT);
+  static constexpr int LOGC = Log2C<C>::v;
+  static constexpr int Q_OFF = 0;
+  static constexpr int K_OFF = Q_OFF + align16(C * LDQ * (int)sizeof(IT));
+  static constexpr int KT_OFF = K_OFF + align16(C * LDQ * (int)sizeof(IT));
+  static constexpr int VT_OFF = KT_OFF + align16(DKP * LDK * (int)sizeof(IT));
+  static constexpr int CL_OFF = VT_OFF + align16(16 * LDK * (int)sizeof(IT));
+  static constexpr int LAM_OFF = CL_OFF + align16(C * 4);
+  // one state slot: bf16 hi [16][LDG] + bf16 lo [16][LDG], or fp32 [16][LDG]
+  static constexpr int SLOT_BYTES = 16 * LDG * 4;
+  __host__ __device__ static int dec_off(int L) { return LAM_OFF + align16(C * L * 4); }
+  __host__ __device__ static int st_off(int L, int nslot) {
+    return dec_off(L) + align16((nslot > 0 ? nslot : 1) * 4);
+  }
+  __host__ __device__ static int bytes(int L, int nslot) { return st_off(L, nslot) + nslot * SLOT_BYTES; }
+};
+
+template <typename IT, int VEC>
+struct VecOf;
+template <>
+struct VecOf<bf16, 8> { typedef bf16x8 type; };
+template <>
+struct VecOf<float, 4> { typedef f32x4 type; };
+
+// ---------------------------------------------------------------------------
+// fwd_sweep_kernel
+// ---------------------------------------------------------------------------
+template <typename IT, int C, int DKP>
+__global__ void __launch_bounds__(C / 16 * 64)
+fwd_sweep_kernel(FwdArgs a) {
+  using Cfg = SweepCfg<IT, C, DKP>;
+  using F = Frag<IT>;
+  using vecT = typename VecOf<IT, Cfg::VEC>::type;
+  constexpr int NW = Cfg::NW, NT = Cfg::NT, LDQ = Cfg::LDQ, CK = Cfg::CK, LDK = Cfg::LDK;
+  constexpr int LDG = Cfg::LDG, VEC = Cfg::VEC, LOGC = Cfg::LOGC;
+  constexpr bool BF = Cfg::BF;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  IT* Qs = reinterpret_cast<IT*>(smem + Cfg::Q_OFF);
+  IT* Ks = reinterpret_cast<IT*>(smem + Cfg::K_OFF);
+  IT* KtT = reinterpret_cast<IT*>(smem + Cfg::KT_OFF);
+  IT* VtT = reinterpret_cast<IT*>(smem + Cfg::VT_OFF);
+  float* cl_s = reinterpret_cast<float*>(smem + Cfg::CL_OFF);
+  float* lam_s = reinterpret_cast<float*>(smem + Cfg::LAM_OFF);
+  float* dec_s = reinterpret_cast<float*>(smem + Cfg::dec_off(a.L));
+  unsigned char* st = smem + Cfg::st_off(a.L, a.nslot);
+
+  // Workgroup -> (pair p = (b,h,segment), dv slice ds).  The dv slices of one
+  // pair share Q and K; they get consecutive ids with the same id % 8 so they
+  // run together on one XCD and share its L2.
+  const int D = a.dv >> 4;
+  const int id = blockIdx.x;
+  const int px = id & 7, rest = id >> 3;
+  const int ds = rest % D, pg = rest / D;
+  const int p = pg * 8 + px;
+  if (p >= a.BH * a.nseg) return;
+  const int bh = p / a.nseg, seg = p - bh * a.nseg;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int T = a.T, L = a.L, dk = a.dk, dv = a.dv;
+  const int N = (T + C - 1) / C;
+  const int n0 = seg << a.seg_log2;
+  const int n1 = min(N, n0 + (1 << a.seg_log2));
+  const size_t bhT = (size_t)bh * T;
+  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + bhT * dk;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk;
+  const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv + 16 * ds;
+  const float* __restrict__ lag = a.log_a + bhT;
+  const float* __restrict__ lamg = a.lam + bhT * L;
+  float* __restrict__ outg = a.out + bhT * dv + 16 * ds;
+
+  // Key columns >= C of the transposed operands are padding and must read 0.
+  for (int i = tid; i < DKP * LDK; i += NT) KtT[i] = IT(0.f);
+  for (int i = tid; i < 16 * LDK; i += NT) VtT[i] = IT(0.f);
+  for (int i = tid; i < a.nslot; i += NT) dec_s[i] = 0.f;
+  __syncthreads();
+
+  // Prologue: bucket states of the levels that span whole segments.  Bit b >=
+  // seg_log2 of the first chunk index is bit b' = b - seg_log2 of the segment
+  // index; its bucket is the node that starts at segment (seg >> b') << b'.
+  {
+    unsigned bits = static_cast<unsigned>(n0);
+    while (bits) {
+      const int b = __builtin_ctz(bits);
+      bits &= bits - 1;
+      const int bp = b - a.seg_log2;
+      const int gc = (seg >> bp) << bp;
+      const float* __restrict__ node = a.nodes + ((size_t)(bh * a.nseg + gc) * dv + 16 * ds) * DKP;
+      unsigned char* slot = st + b * Cfg::SLOT_BYTES;
+      for (int i = tid; i < 16 * DKP; i += NT) {
+        const int r = i / DKP, c = i - r * DKP;
+        const float x = node[(size_t)r * DKP + c];
+        if constexpr (BF) {
+          bf16 h, l;
+          split_bf16(x, h, l);
+          reinterpret_cast<bf16*>(slot)[r * LDG + c] = h;
+          reinterpret_cast<bf16*>(slot)[16 * LDG + r * LDG + c] = l;
+        } else {
+          reinterpret_cast<float*>(slot)[r * LDG + c] = x;
+        }
+      }
+      if (tid == 0) {
+        float d = 0.f;  // decay from the start of segment gc to the start of seg
+        for (int r = gc; r < seg; ++r) d += a.seg_decay[bh * a.nseg + r];
+        dec_s[b] = d;
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int n = n0; n < n1; ++n) {
+    const int tok0 = n * C;
+
+    // In-chunk decay sums (every wave computes the same values, lane i <-> i):
+    // cl = inclusive prefix of log_a, sf = exclusive suffix (decay to the
+    // chunk's last token), Atot = chunk total.
+    float la = 0.f;
+    if (lane < C && tok0 + lane < T) la = lag[tok0 + lane];
+    float cl = la;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(cl, off);
+      if (lane >= off) cl += y;
+    }
+    float sf = __shfl_down(la, 1);
+    if (lane == 63) sf = 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(sf, off);
+      if (lane + off < 64) sf += y;
+    }
+    const float Atot = __shfl(cl, C - 1);
+    if (w == 0 && lane < C) cl_s[lane] = cl;
+
+    // Stage Q, K (row-major) and K~^T = (K * exp(sf))^T.
+    constexpr int RV = DKP / VEC;
+#pragma unroll 2
+    for (int idx = tid; idx < C * RV; idx += NT) {  // uniform trip count (DKP/(4*VEC))
+      const int row = idx / RV, col = (idx - row * RV) * VEC;
+      const int tok = tok0 + row;
+      vecT qv = {}, kv = {};
+      if (tok < T && col < dk) {
+        qv = *reinterpret_cast<const vecT*>(qg + (size_t)tok * dk + col);
+        kv = *reinterpret_cast<const vecT*>(kg + (size_t)tok * dk + col);
+      }
+      *reinterpret_cast<vecT*>(Qs + row * LDQ + col) = qv;
+      *reinterpret_cast<vecT*>(Ks + row * LDQ + col) = kv;
+      const float sc = __expf(__shfl(sf, row));
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) KtT[(col + e) * LDK + row] = IT(static_cast<float>(kv[e]) * sc);
+    }
+    // Stage V^T of this 16-wide dv slice.
+    constexpr int VV = 16 / VEC;
+    for (int idx = tid; idx < C * VV; idx += NT) {
+      const int row = idx / VV, col = (idx - row * VV) * VEC;
+      const int tok = tok0 + row;
+      vecT vv = {};
+      if (tok < T) vv = *reinterpret_cast<const vecT*>(vg + (size_t)tok * dv + col);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) VtT[(col + e) * LDK + row] = vv[e];
+    }
+    // Stage lambda rows of the chunk.
+    for (int idx = tid; idx < C * L; idx += NT) {
+      const int tok = tok0 + idx / L;
+      lam_s[idx] = tok < T ? lamg[(size_t)tok0 * L + idx] : 0.f;
+    }
+    __syncthreads();
+
+    // ---------------- intra chunk: levels 0..log2(C) -----------------------
+    const int qi = 16 * w + li;  // query row of this lane in the score tiles
+    const float cl_q = cl_s[qi];
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    constexpr int NP = (NW + 1) / 2;
+    f32x4 P[2 * NP];
+#pragma unroll
+    for (int kb = 0; kb < 2 * NP; ++kb) {
+      P[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (kb <= w) {
+        // S^T tile: rows = keys 16kb.., columns = queries 16w..
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < DKP; k0 += F::KS)
+          acc = F::mma(F::load(Ks, LDQ, 16 * kb, k0, lane), F::load(Qs, LDQ, 16 * w, k0, lane), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kj = 16 * kb + 4 * g4 + r;
+          float pv = 0.f;
+          if (kj <= qi)  // chunk-local indices give the same level: tok0 is a multiple of C
+            pv = acc[r] * lam_s[qi * L + level_of(qi, kj)] * __expf(cl_q - cl_s[kj]);
+          P[kb][r] = pv;
+        }
+      }
+    }
+    // O = P V.  The S^T tile layout already is the A-operand layout of P with
+    // the key index permuted; V^T is read with the same permutation.
+    if constexpr (BF) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        if (2 * pp <= w) {
+          bf16x8 ah, al;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bf16 h, l;
+            split_bf16(P[2 * pp][r], h, l);
+            ah[r] = h;
+            al[r] = l;
+            split_bf16(P[2 * pp + 1][r], h, l);
+            ah[4 + r] = h;
+            al[4 + r] = l;
+          }
+          const bf16* vb = VtT + li * LDK + 32 * pp + 4 * g4;
+          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vb);
+          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vb + 16);
+          const bf16x8 bv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          O = F::mma(ah, bv, O);
+          O = F::mma(al, bv, O);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NW; ++kb) {
+        if (kb <= w) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            O = F::mma(P[kb][r], VtT[li * LDK + 16 * kb + 4 * g4 + r], O);
+        }
+      }
+    }
+
+    // ---------------- inter chunk: one bucket per set bit of n -------------
+    typename F::V qf[DKP / F::KS];
+#pragma unroll
+    for (int i = 0; i < DKP / F::KS; ++i) qf[i] = F::load(Qs, LDQ, 16 * w, i * F::KS, lane);
+    unsigned live = static_cast<unsigned>(n);
+    while (live) {
+      const int b = __builtin_ctz(live);
+      live &= live - 1;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const unsigned char* slot = st + b * Cfg::SLOT_BYTES;
+      if constexpr (BF) {
+        const bf16* gh = reinterpret_cast<const bf16*>(slot);
+        const bf16* gl = gh + 16 * LDG;
+#pragma unroll
+        for (int i = 0; i < DKP / F::KS; ++i) {
+          acc = F::mma(qf[i], F::load(gh, LDG, 0, i * F::KS, lane), acc);
+          acc = F::mma(qf[i], F::load(gl, LDG, 0, i * F::KS, lane), acc);
+        }
+      } else {
+        const float* gf = reinterpret_cast<const float*>(slot);
+#pragma unroll
+        for (int i = 0; i < DKP / F::KS; ++i) acc = F::mma(qf[i], F::load(gf, LDG, 0, i * F::KS, lane), acc);
+      }
+      const int lev = LOGC + 1 + b;
+      const float db = dec_s[b];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * w + 4 * g4 + r;
+        O[r] += lam_s[row * L + lev] * __expf(cl_s[row] + db) * acc[r];
+      }
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tok0 + 16 * w + 4 * g4 + r;
+      if (tok < T) outg[(size_t)tok * dv + li] = O[r];
+    }
+
+    // ---------------- chunk state and lssb merge (chunk granularity) -------
+    // Transition n -> n+1 with m = lssb(n+1): the new level-m bucket is chunk
+    // n plus the buckets of levels < m of n, all decayed to the end of chunk n.
+    if (n + 1 < n1) {
+      const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
+      for (int t = w; t < DKP / 16; t += NW) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < CK; k0 += F::KS)
+          acc = F::mma(F::load(KtT, LDK, 16 * t, k0, lane), F::load(VtT, LDK, 0, k0, lane), acc);
+        const int col0 = 16 * t + 4 * g4;  // dk index of acc[0]; li is the dv column
+        for (int b = 0; b < m; ++b) {
+          const float f = __expf(dec_s[b] + Atot);
+          const unsigned char* slot = st + b * Cfg::SLOT_BYTES;
+          if constexpr (BF) {
+            const bf16* gh = reinterpret_cast<const bf16*>(slot) + li * LDG + col0;
+            const bf16x4 h = *reinterpret_cast<const bf16x4*>(gh);
+            const bf16x4 l = *reinterpret_cast<const bf16x4*>(gh + 16 * LDG);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += f * (static_cast<float>(h[r]) + static_cast<float>(l[r]));
+          } else {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(slot) + li * LDG + col0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += f * x[r];
+          }
+        }
+        unsigned char* slot = st + m * Cfg::SLOT_BYTES;
+        if constexpr (BF) {
+          bf16x4 h, l;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bf16 hh, ll;
+            split_bf16(acc[r], hh, ll);
+            h[r] = hh;
+            l[r] = ll;
+          }
+          bf16* gh = reinterpret_cast<bf16*>(slot) + li * LDG + col0;
+          *reinterpret_cast<bf16x4*>(gh) = h;
+          *reinterpret_cast<bf16x4*>(gh + 16 * LDG) = l;
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(slot) + li * LDG + col0) = acc;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0 && n + 1 < n1) {
+      const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
+      for (int b = m + 1; b < a.nslot; ++b) dec_s[b] += Atot;
+      dec_s[m] = 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// seg_state_kernel: T_g = sum_{s in segment g} exp(cum[end] - cum[s]) k_s v_s^T,
+// stored transposed ([dv][DKP], fp32), plus the segment's total log decay.
+// ---------------------------------------------------------------------------
+template <typename IT, int DKP>
+struct SegCfg {
+  static constexpr bool BF = sizeof(IT) == 2;
+  static constexpr int KB = 64;   // tokens per step
+  static constexpr int NT = 256;
+  static constexpr int PADE = BF ? 8 : 4;
+  static constexpr int LDK = KB + PADE;
+  static constexpr int DVG = 128;  // dv columns per workgroup
+  static constexpr int VEC = 16 / (int)sizeof(IT);
+  static constexpr int MAXT = (DKP / 16) * (DVG / 16) / 4;  // accumulator tiles per wave
+  static constexpr int KT_OFF = 0;
+  static constexpr int VT_OFF = align16(DKP * LDK * (int)sizeof(IT));
+  static constexpr int BYTES = VT_OFF + align16(DVG * LDK * (int)sizeof(IT));
+};
+
+template <typename IT, int DKP>
+__global__ void __launch_bounds__(256)
+seg_state_kernel(SegArgs a) {
+  using Cfg = SegCfg<IT, DKP>;
+  using F = Frag<IT>;
+  using vecT = typename VecOf<IT, Cfg::VEC>::type;
+  constexpr int KB = Cfg::KB, NT = Cfg::NT, LDK = Cfg::LDK, VEC = Cfg::VEC, MAXT = Cfg::MAXT;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  IT* KtT = reinterpret_cast<IT*>(smem + Cfg::KT_OFF);
+  IT* VtT = reinterpret_cast<IT*>(smem + Cfg::VT_OFF);
+
+  const int ndvg = (a.dv + Cfg::DVG - 1) / Cfg::DVG;
+  const int nsg = a.nseg - 1;  // the last segment's state is never used
+  const int id = blockIdx.x;
+  const int dvg = id % ndvg, rest = id / ndvg;
+  const int g = rest % nsg, bh = rest / nsg;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int T = a.T, dk = a.dk, dv = a.dv;
+  const int segtok = a.C << a.seg_log2;
+  const int s0 = g * segtok, s1 = min(T, s0 + segtok);
+  const int dv0 = dvg * Cfg::DVG;
+  const int dvw = min(Cfg::DVG, dv - dv0);
+  const int nu = dvw >> 4;
+  const int ntile = (DKP / 16) * nu;
+  const size_t bhT = (size_t)bh * T;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk;
+  const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv + dv0;
+  const float* __restrict__ lag = a.log_a + bhT;
+
+  f32x4 acc[MAXT];
+#pragma unroll
+  for (int j = 0; j < MAXT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float Aseg = 0.f;
+
+  for (int b0 = s0; b0 < s1; b0 += KB) {
+    float la = 0.f;
+    if (b0 + lane < s1) la = lag[b0 + lane];
+    float sf = __shfl_down(la, 1);
+    if (lane == 63) sf = 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(sf, off);
+      if (lane + off < 64) sf += y;
+    }
+    const float Ab = __shfl(sf, 0) + __shfl(la, 0);  // block total
+    constexpr int RV = DKP / VEC;
+    for (int idx = tid; idx < KB * RV; idx += NT) {  // uniform trip count
+      const int row = idx / RV, col = (idx - row * RV) * VEC;
+      const int tok = b0 + row;
+      vecT kv = {};
+      if (tok < s1 && col < dk) kv = *reinterpret_cast<const vecT*>(kg + (size_t)tok * dk + col);
+      const float sc = __expf(__shfl(sf, row));
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) KtT[(col + e) * LDK + row] = IT(static_cast<float>(kv[e]) * sc);
+    }
+    const int vrow = dvw / VEC;
+    for (int idx = tid; idx < KB * vrow; idx += NT) {
+      const int row = idx / vrow, col = (idx - row * vrow) * VEC;
+      const int tok = b0 + row;
+      vecT vv = {};
+      if (tok < s1) vv = *reinterpret_cast<const vecT*>(vg + (size_t)tok * dv + col);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) VtT[(col + e) * LDK + row] = vv[e];
+    }
+    __syncthreads();
+    const float fa = __expf(Ab);
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      const int ti = w + 4 * j;
+      if (ti < ntile) {
+        const int t = ti / nu, u = ti - t * nu;
+        f32x4 c = acc[j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[r] *= fa;
+#pragma unroll
+        for (int k0 = 0; k0 < KB; k0 += F::KS)
+          c = F::mma(F::load(KtT, LDK, 16 * t, k0, lane), F::load(VtT, LDK, 16 * u, k0, lane), c);
+        acc[j] = c;
+      }
+    }
+    Aseg += Ab;
+    __syncthreads();
+  }
+  float* __restrict__ Tout = a.seg_state + ((size_t)(bh * a.nseg + g) * dv + dv0) * DKP;
+#pragma unroll
+  for (int j = 0; j < MAXT; ++j) {
+    const int ti = w + 4 * j;
+    if (ti < ntile) {
+      const int t = ti / nu, u = ti - t * nu;
+      *reinterpret_cast<f32x4*>(Tout + (size_t)(16 * u + li) * DKP + 16 * t + 4 * g4) = acc[j];
+    }
+  }
+  if (tid == 0 && dvg == 0) a.seg_decay[bh * a.nseg + g] = Aseg;
+}
+
+// ---------------------------------------------------------------------------
+// seg_node_kernel: lssb walk over segments, one thread per state element.
+// At the step into segment g (g >= 1), with m = lssb(g), the bucket of level
+// m is segment g-1 plus the buckets of levels < m, decayed to the start of g.
+// That bucket is written as node g; segment g' uses node (g' >> b) << b for
+// every set bit b of g'.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) seg_node_kernel(NodeArgs a) {
+  constexpr int MAXB = 24;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int bh = blockIdx.y;
+  if (e >= a.E) return;
+  float stv[MAXB], dec[MAXB];
+#pragma unroll
+  for (int b = 0; b < MAXB; ++b) {
+    stv[b] = 0.f;
+    dec[b] = 0.f;
+  }
+  const size_t base = (size_t)bh * a.nseg;
+  for (int g = 1; g < a.nseg; ++g) {
+    const int m = lssb(static_cast<uint32_t>(g));
+    const float Ag = a.seg_decay[base + g - 1];
+    float x = a.seg_state[(base + g - 1) * a.E + e];
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b)
+      if (b < m) x += __expf(dec[b] + Ag) * stv[b];
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) {
+      if (b == m) {
+        stv[b] = x;
+        dec[b] = 0.f;
+      } else if (b > m) {
+        dec[b] += Ag;
+      }
+    }
+    a.nodes[(base + g) * a.E + e] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// level table export (test only): same device helper as the kernels.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) level_table_kernel(signed char* lev, int T) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)T * T) return;
+  const int t = static_cast<int>(idx / T), s = static_cast<int>(idx - (size_t)t * T);
+  lev[idx] = s <= t ? static_cast<signed char>(level_of(t, s)) : static_cast<signed char>(-1);
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers
+// ---------------------------------------------------------------------------
+template <typename IT, int C, int DKP>
+static int launch_sweep_t(const FwdArgs& a, int nblocks, hipStream_t stream) {
+  using Cfg = SweepCfg<IT, C, DKP>;
+  const int bytes = Cfg::bytes(a.L, a.nslot);
+  if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_sweep_kernel<IT, C, DKP>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return LL_ERR_HIP;
+  hipLaunchKernelGGL((fwd_sweep_kernel<IT, C, DKP>), dim3(nblocks), dim3(Cfg::NT), bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
+template <typename IT, int DKP>
+static int launch_seg_t(const SegArgs& a, int nblocks, hipStream_t stream) {
+  using Cfg = SegCfg<IT, DKP>;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_state_kernel<IT, DKP>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::BYTES) != hipSuccess)
+    return LL_ERR_HIP;
+  hipLaunchKernelGGL((seg_state_kernel<IT, DKP>), dim3(nblocks), dim3(Cfg::NT), Cfg::BYTES, stream, a);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
+template <typename IT>
+static int sweep_lds_t(int C, int DKP, int L, int nslot) {
+#define LL_CASE(CC, DD) \
+  if (C == CC && DKP == DD) return SweepCfg<IT, CC, DD>::bytes(L, nslot);
+  LL_CASE(16, 32) LL_CASE(16, 64) LL_CASE(16, 128)
+  LL_CASE(32, 32) LL_CASE(32, 64) LL_CASE(32, 128)
+  LL_CASE(64, 32) LL_CASE(64, 64) LL_CASE(64, 128)
+#undef LL_CASE
+  return -1;
+}
+
+int sweep_lds_bytes(int dtype, int C, int DKP, int L, int nslot) {
+  return dtype == LL_BF16 ? sweep_lds_t<bf16>(C, DKP, L, nslot) : sweep_lds_t<float>(C, DKP, L, nslot);
+}
+
+template <typename IT>
+static int launch_sweep_dispatch(int C, int DKP, const FwdArgs& a, int nblocks, hipStream_t s) {
+#define LL_CASE(CC, DD) \
+  if (C == CC && DKP == DD) return launch_sweep_t<IT, CC, DD>(a, nblocks, s);
+  LL_CASE(16, 32) LL_CASE(16, 64) LL_CASE(16, 128)
+  LL_CASE(32, 32) LL_CASE(32, 64) LL_CASE(32, 128)
+  LL_CASE(64, 32) LL_CASE(64, 64) LL_CASE(64, 128)
+#undef LL_CASE
+  return LL_ERR_UNSUPPORTED;
+}
+
+int launch_sweep(int dtype, int C, int DKP, const FwdArgs& a, int nblocks, hipStream_t s) {
+  return dtype == LL_BF16 ? launch_sweep_dispatch<bf16>(C, DKP, a, nblocks, s)
+                          : launch_sweep_dispatch<float>(C, DKP, a, nblocks, s);
+}
+
+int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStream_t s) {
+  if (dtype == LL_BF16) {
+    if (DKP == 32) return launch_seg_t<bf16, 32>(a, nblocks, s);
+    if (DKP == 64) return launch_seg_t<bf16, 64>(a, nblocks, s);
+    if (DKP == 128) return launch_seg_t<bf16, 128>(a, nblocks, s);
+  } else {
+    if (DKP == 32) return launch_seg_t<float, 32>(a, nblocks, s);
+    if (DKP == 64) return launch_seg_t<float, 64>(a, nblocks, s);
+    if (DKP == 128) return launch_seg_t<float, 128>(a, nblocks, s);
+  }
+  return LL_ERR_UNSUPPORTED;
+}
+
+int launch_seg_nodes(const NodeArgs& a, int BH, hipStream_t s) {
+  hipLaunchKernelGGL(seg_node_kernel, dim3((a.E + 255) / 256, BH), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
+int launch_level_table(signed char* lev, int T, hipStream_t s) {
+  const size_t n = (size_t)T * T;
+  hipLaunchKernelGGL(level_table_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, lev, T);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
+}  // namespace ll

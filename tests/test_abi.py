@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol that
+include/loglinear.h declares, and rejects bad arguments before touching the
+GPU (so these run on a machine without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import log_linear_attention_attn_amd as ll
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loglinear.h")
+
+LL_OK, LL_ERR_NULL, LL_ERR_SHAPE, LL_ERR_UNSUPPORTED, LL_ERR_HIP, LL_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ll.library_path()),
+                                reason="libloglinear.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(loglinear_\w+)\s*\(", text)))
+
+
+def test_header_declarations_all_exported():
+    declared = _declared_functions()
+    assert set(declared) == set(ll.EXPORTED_SYMBOLS)
+    L = ll.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_num_levels():
+    for T, L in [(0, 0), (1, 1), (2, 2), (3, 3), (64, 7), (65, 8), (2048, 12), (16384, 15), (65536, 17)]:
+        assert ll.num_levels(T) == L
+
+
+def _fwd(B=1, H=1, T=64, dk=16, dv=16, C=16, ptr=1, f=None):
+    L = ll.lib()
+    p = ctypes.c_void_p(ptr) if ptr else ctypes.c_void_p(0)
+    fn = f or L.loglinear_fwd
+    return fn(p, p, p, p, p, p, B, H, T, dk, dv, C, ctypes.c_void_p(0))
+
+
+def test_fwd_argument_errors():
+    assert _fwd(C=48) == LL_ERR_SHAPE          # not a power of two
+    assert _fwd(C=128) == LL_ERR_UNSUPPORTED   # power of two without a kernel
+    assert _fwd(C=0) == LL_ERR_SHAPE
+    assert _fwd(dk=8) == LL_ERR_SHAPE
+    assert _fwd(dk=24) == LL_ERR_SHAPE
+    assert _fwd(dk=256) == LL_ERR_UNSUPPORTED
+    assert _fwd(dv=0) == LL_ERR_SHAPE
+    assert _fwd(dv=2048) == LL_ERR_UNSUPPORTED
+    assert _fwd(B=-1) == LL_ERR_SHAPE
+    assert _fwd(T=-5) == LL_ERR_SHAPE
+    assert _fwd(ptr=0) == LL_ERR_NULL
+    assert _fwd(ptr=0, f=ll.lib().loglinear_fwd_f32) == LL_ERR_NULL
+
+
+def test_fwd_empty_is_noop():
+    # zero-sized problems succeed without touching (NULL) pointers or the GPU
+    assert _fwd(B=0, ptr=0) == LL_OK
+    assert _fwd(H=0, ptr=0) == LL_OK
+    assert _fwd(T=0, ptr=0) == LL_OK
+
+
+def test_fwd_ex_options():
+    L = ll.lib()
+    p = ctypes.c_void_p(1)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, None, None) == LL_ERR_NULL
+    bad = ll._FwdOpts(7, -1, None, 0, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(bad), None) == LL_ERR_SHAPE
+    bad = ll._FwdOpts(0, 13, None, 0, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(bad), None) == LL_ERR_SHAPE
+    # a caller workspace smaller than required is rejected before any launch
+    need = ll.fwd_workspace_size(1, 1, 4096, 64, 64, 64, 1)
+    assert need > 0
+    small = ll._FwdOpts(0, 1, ctypes.c_void_p(256), need - 1, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 4096, 64, 64, 64, ctypes.byref(small), None) == LL_ERR_WORKSPACE
+
+
+def test_workspace_size_formula():
+    # one segment -> no scratch
+    assert ll.fwd_workspace_size(1, 1, 64, 16, 16, 16, 4) == 0
+    # B=2,H=16,T=16384,dk=dv=128,C=64, 16-chunk segments: 16 segments
+    BH, nseg, dv, dkp = 32, 16, 128, 128
+    per = BH * nseg * dv * dkp * 4
+    dec = -(-BH * nseg * 4 // 256) * 256
+    assert ll.fwd_workspace_size(2, 16, 16384, 128, 128, 64, 4) == 2 * per + dec
+    with pytest.raises(ValueError):
+        ll.fwd_workspace_size(1, 1, 64, 10, 16, 16)
+
+
+def test_decode_argument_errors():
+    L = ll.lib()
+    p = ctypes.c_void_p(1)
+    assert L.loglinear_decode_step(None, p, p, p, p, p, p, p, None) == LL_ERR_NULL
+    for N, H, Lv, dk, dv, want in [
+        (1, 1, 0, 16, 16, LL_ERR_SHAPE), (1, 1, 32, 16, 16, LL_ERR_SHAPE),
+        (1, 1, 4, 6, 16, LL_ERR_SHAPE), (1, 1, 4, 16, 2, LL_ERR_SHAPE),
+        (-1, 1, 4, 16, 16, LL_ERR_SHAPE), (1, 1, 4, 2048, 16, LL_ERR_UNSUPPORTED),
+        (0, 4, 4, 16, 16, LL_OK), (1, 1, 4, 16, 16, LL_ERR_NULL),
+    ]:
+        desc = ll._States(0, N, H, Lv, dk, dv)
+        assert L.loglinear_decode_step(ctypes.byref(desc), p, p, p, p, p, p, p, None) == want, (N, H, Lv, dk, dv)
+
+
+def test_level_table_argument_errors():
+    L = ll.lib()
+    assert L.loglinear_level_table(ctypes.c_void_p(1), 0, None) == LL_ERR_SHAPE
+    assert L.loglinear_level_table(ctypes.c_void_p(1), 9000, None) == LL_ERR_SHAPE
+    assert L.loglinear_level_table(None, 16, None) == LL_ERR_NULL
+
+
+def test_strerror():
+    for s in (LL_OK, LL_ERR_NULL, LL_ERR_SHAPE, LL_ERR_UNSUPPORTED, LL_ERR_HIP, LL_ERR_WORKSPACE):
+        assert ll.strerror(s) and ll.strerror(s) != "unknown status"
+    assert ll.strerror(42) == "unknown status"
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 16, 16)
+    lam = torch.zeros(1, 1, 16, ll.num_levels(16))
+    with pytest.raises(ValueError):
+        ll.fwd(q, q, q, torch.zeros(1, 1, 16), lam, C=16)

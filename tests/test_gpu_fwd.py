@@ -1,0 +1,180 @@
+"""GPU parity of the forward (loglinear_fwd / _f32 / _ex) against the CPU oracle.
+
+Tolerances (written here, derived in the design doc): max |gpu - oracle| <=
+2e-2 * RMS(oracle) for bf16 inputs, 1e-4 * RMS for fp32 inputs; the level
+table is bit-exact; repeated runs are bitwise identical.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import log_linear_attention_attn_amd as ll
+import oracle
+import workloads as W
+from gpu_util import BF16_TOL, F32_TOL, announce, assert_parity, have_gpu, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+def _run(w, seg_log2=-1, inputs=None):
+    q, k, v, la, lam = inputs if inputs is not None else W.make_fwd_inputs(w)
+    announce(f"fwd {w} seg_log2={seg_log2}")
+    dq, dk_, dv_, dla, dlam = to_dev(q, k, v, la, lam)
+    out = ll.fwd_ex(dq, dk_, dv_, dla, dlam, C=w.C, seg_log2=seg_log2)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (q, k, v, la, lam)
+
+
+def _tol(w):
+    return BF16_TOL if w.dtype == "bf16" else F32_TOL
+
+
+# ---------------------------------------------------------------- index path
+
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 100, 4096])
+def test_level_table_bit_exact(T):
+    announce(f"level_table T={T}")
+    got = ll.level_table(T).cpu().numpy().astype(np.int16)
+    assert np.array_equal(got, oracle.level_matrix(T))
+
+
+# ---------------------------------------------------------------- small cases, full oracle
+
+def test_tiny_fp32_workload():
+    """T=64, dk=dv=16, fp32, C=16, no decay, seed 0: the small workload in full."""
+    w = W.TINY
+    got, inp = _run(w)
+    want = oracle.forward(*inp)
+    assert_parity(got, want, F32_TOL, w.name)
+    out2 = ll.fwd(*to_dev(*inp), C=w.C)  # the plain loglinear_fwd_f32 entry point
+    torch.cuda.synchronize()
+    assert_parity(out2.cpu().numpy(), want, F32_TOL, w.name + " (loglinear_fwd_f32)")
+
+
+SMALL = []
+for dtype in ("bf16", "f32"):
+    for C in (16, 32, 64):
+        for decay in ("none", "weak", "strong"):
+            SMALL.append(W.FwdWorkload(f"small_{dtype}_C{C}_{decay}", 1, 2, 777, 64, 32, C, dtype,
+                                       decay=decay, seed=C))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("seg_log2", [0, 2, -1])
+def test_small_parity(w, seg_log2):
+    """Ragged T = 777 over several chunks and segments, every chunk size,
+    no / weak / strong decay, explicit and automatic segment sizes."""
+    got, inp = _run(w, seg_log2)
+    assert_parity(got, oracle.forward(*inp), _tol(w), f"{w.name} seg{seg_log2}")
+
+
+SHAPES = [
+    # (B, H, T, dk, dv, C)
+    (1, 1, 1, 16, 16, 16),        # single token
+    (1, 1, 15, 16, 16, 16),       # shorter than one chunk
+    (2, 1, 64, 32, 16, 64),       # exactly one chunk
+    (1, 3, 130, 48, 48, 64),      # dk / dv padded, ragged tail of 2
+    (1, 1, 1024, 128, 128, 64),   # 16 chunks
+    (2, 2, 515, 96, 80, 32),
+    (1, 1, 2049, 128, 64, 16),    # 129 chunks of 16: deep chunk-level tree
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}T{}dk{}dv{}C{}".format(*s))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_shapes_parity(shape, dtype):
+    B, H, T, dk, dv, C = shape
+    w = W.FwdWorkload("shape", B, H, T, dk, dv, C, dtype, decay="weak", seed=T)
+    for s in (-1, 1):
+        got, inp = _run(w, s)
+        assert_parity(got, oracle.forward(*inp), _tol(w), f"{shape} {dtype} seg{s}")
+
+
+def test_one_hot_lambda_isolates_every_level():
+    """fp32, no decay, lambda one-hot at one level: the output is the attention
+    over exactly that Fenwick bucket, so a bucket-membership or level-index
+    error anywhere gives an O(1) mismatch."""
+    B, H, T, dk, dv, C = 1, 1, 700, 32, 16, 16
+    w = W.FwdWorkload("onehot", B, H, T, dk, dv, C, "f32", decay="none", knorm=False, seed=11)
+    q, k, v, la, _ = W.make_fwd_inputs(w)
+    L = W.num_levels(T)
+    for lev in range(L):
+        lam = torch.zeros(B, H, T, L)
+        lam[..., lev] = 1.0
+        for s in (0, 2):
+            got, inp = _run(w, s, (q, k, v, la, lam))
+            assert_parity(got, oracle.forward(*inp), F32_TOL, f"one-hot level {lev} seg{s}")
+
+
+def test_mamba2_T2048_full():
+    """B=8, H=8, T=2048, dk=128, dv=64, bf16, C=64: every output against the oracle."""
+    w = W.MAMBA2_T2K
+    got, inp = _run(w)
+    assert_parity(got, oracle.forward(*inp), BF16_TOL, w.name)
+
+
+@pytest.mark.parametrize("decay", ["none", "weak"])
+@pytest.mark.parametrize("base", [W.MAMBA2_T2K, W.LM_T16K], ids=lambda w: w.name)
+def test_weak_decay_coverage(base, decay):
+    """The workloads' strong decay makes distant levels negligible; without
+    decay (or with weak decay) every inter-chunk level carries weight."""
+    w = dataclasses.replace(base, name=base.name + "_" + decay, B=1, H=2, decay=decay)
+    got, inp = _run(w)
+    if w.T <= 4096:
+        assert_parity(got, oracle.forward(*inp), BF16_TOL, w.name)
+    else:
+        rows = _sample_rows(w.T, w.C, 48, seed=3)
+        for bh in [(0, 0), (0, 1)]:
+            want = oracle.forward_rows(*inp, bh, rows)
+            assert_parity(got[bh[0], bh[1], rows], want, BF16_TOL, f"{w.name} {bh}")
+
+
+def _sample_rows(T, C, n, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, C - 1, C, T // 2, T // 2 - 1, T - C, T - 2, T - 1]
+    seg = 16 * C
+    fixed += [x for x in (seg - 1, seg, 3 * seg + 5) if x < T]
+    rows = sorted(set(fixed) | set(rng.integers(0, T, n).tolist()))
+    return [r for r in rows if 0 <= r < T]
+
+
+@pytest.mark.parametrize("w", [W.LM_T16K, W.LONG_T64K], ids=lambda w: w.name)
+def test_full_size_sampled_rows(w):
+    """Full-size workloads in the launch configuration the bench uses
+    (loglinear_fwd), checked on sampled rows of a few (b, h) pairs."""
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    announce(f"fwd full-size {w.name}")
+    out = ll.fwd(*to_dev(q, k, v, la, lam), C=w.C)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(0)
+    pairs = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(2)]
+    rows = _sample_rows(w.T, w.C, 40, seed=1)
+    for bh in pairs[: 4 if w.T <= 16384 else 2]:
+        want = oracle.forward_rows(q, k, v, la, lam, bh, rows)
+        assert_parity(got[bh[0], bh[1], rows], want, BF16_TOL, f"{w.name} {bh}")
+
+
+def test_deterministic_bitwise():
+    w = dataclasses.replace(W.MAMBA2_T2K, B=2, H=4)
+    q, k, v, la, lam = to_dev(*W.make_fwd_inputs(w))
+    announce("determinism")
+    a = ll.fwd(q, k, v, la, lam, C=64)
+    b = ll.fwd(q, k, v, la, lam, C=64)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_caller_workspace_matches_owned():
+    w = dataclasses.replace(W.MAMBA2_T2K, B=1, H=4, decay="weak")
+    q, k, v, la, lam = to_dev(*W.make_fwd_inputs(w))
+    n = ll.fwd_workspace_size(1, 4, w.T, w.dk, w.dv, w.C, 2)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    announce("caller workspace")
+    a = ll.fwd_ex(q, k, v, la, lam, C=64, seg_log2=2)
+    b = ll.fwd_ex(q, k, v, la, lam, C=64, seg_log2=2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
