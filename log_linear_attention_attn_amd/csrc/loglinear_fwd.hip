@@ -31,10 +31,11 @@
 //                     Fenwick level mask computed in registers, P·V, one
 //                     Q·G product per live level, output, chunk state.
 //
-// bf16 path: Q, K, V are exact bf16 MFMA operands.  The masked scores P and
-// the states G are fp32 values; each is split into bf16 hi + lo and fed to two
-// MFMAs so that their rounding error is ~2^-16 instead of 2^-9.  K scaled by
-// the in-chunk decay (K~) is rounded once to bf16.  fp32 path: fp32 MFMA.
+// bf16 path: Q, K, V are exact bf16 MFMA operands.  The masked scores P, the
+// states G and the decay-scaled keys K~ are fp32 values; each is split into
+// bf16 hi + lo and fed to two MFMAs so that its rounding error is ~2^-16
+// instead of 2^-9 (a single bf16 K~ costs ~2e-2 of the output RMS once the
+// decay is weak enough for distant chunks to matter).  fp32 path: fp32 MFMA.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -63,16 +64,17 @@ struct SweepCfg {
   static constexpr int NW = C / 16;          // waves; wave w owns query rows 16w..16w+15
   static constexpr int NT = NW * 64;
   static constexpr int PADE = BF ? 8 : 4;    // row padding (elements) against bank conflicts
-  static constexpr int LDQ = DKP + PADE;     // Q, K rows: [token][dk]
+  static constexpr int LDQ = DKP + PADE;     // K rows: [token][dk]
   static constexpr int CK = C < 32 ? 32 : C; // key extent of transposed operands (>= one bf16 K-step)
   static constexpr int LDK = CK + PADE;      // K~^T rows [dk][key], V^T rows [dv][key]
   static constexpr int LDG = DKP + PADE;     // state rows G^T [dv][dk]
   static constexpr int VEC = 16 / (int)sizeof(IT);
   static constexpr int LOGC = Log2C<C>::v;
-  static constexpr int Q_OFF = 0;
-  static constexpr int K_OFF = Q_OFF + align16(C * LDQ * (int)sizeof(IT));
+  static constexpr int K_OFF = 0;
   static constexpr int KT_OFF = K_OFF + align16(C * LDQ * (int)sizeof(IT));
-  static constexpr int VT_OFF = KT_OFF + align16(DKP * LDK * (int)sizeof(IT));
+  // K~^T: bf16 keeps hi and lo halves (two consecutive [DKP][LDK] arrays)
+  static constexpr int KT_BYTES = align16(DKP * LDK * (int)sizeof(IT)) * (BF ? 2 : 1);
+  static constexpr int VT_OFF = KT_OFF + KT_BYTES;
   static constexpr int CL_OFF = VT_OFF + align16(16 * LDK * (int)sizeof(IT));
   static constexpr int LAM_OFF = CL_OFF + align16(C * 4);
   // one state slot: bf16 hi [16][LDG] + bf16 lo [16][LDG], or fp32 [16][LDG]
@@ -105,9 +107,9 @@ fwd_sweep_kernel(FwdArgs a) {
   constexpr bool BF = Cfg::BF;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  IT* Qs = reinterpret_cast<IT*>(smem + Cfg::Q_OFF);
   IT* Ks = reinterpret_cast<IT*>(smem + Cfg::K_OFF);
   IT* KtT = reinterpret_cast<IT*>(smem + Cfg::KT_OFF);
+  IT* KtL = reinterpret_cast<IT*>(smem + Cfg::KT_OFF + Cfg::KT_BYTES / 2);  // bf16 lo half
   IT* VtT = reinterpret_cast<IT*>(smem + Cfg::VT_OFF);
   float* cl_s = reinterpret_cast<float*>(smem + Cfg::CL_OFF);
   float* lam_s = reinterpret_cast<float*>(smem + Cfg::LAM_OFF);
@@ -141,6 +143,8 @@ fwd_sweep_kernel(FwdArgs a) {
 
   // Key columns >= C of the transposed operands are padding and must read 0.
   for (int i = tid; i < DKP * LDK; i += NT) KtT[i] = IT(0.f);
+  if constexpr (BF)
+    for (int i = tid; i < DKP * LDK; i += NT) KtL[i] = IT(0.f);
   for (int i = tid; i < 16 * LDK; i += NT) VtT[i] = IT(0.f);
   for (int i = tid; i < a.nslot; i += NT) dec_s[i] = 0.f;
   __syncthreads();
@@ -202,22 +206,47 @@ fwd_sweep_kernel(FwdArgs a) {
     const float Atot = __shfl(cl, C - 1);
     if (w == 0 && lane < C) cl_s[lane] = cl;
 
-    // Stage Q, K (row-major) and K~^T = (K * exp(sf))^T.
+    // This wave's 16 query rows as matrix-core fragments, straight from global
+    // memory: they are the B operand of the score tiles and the A operand of
+    // every Q.G product, so Q never goes through LDS.
+    typename F::V qf[DKP / F::KS];
+    {
+      const int tq = tok0 + 16 * w + li;
+#pragma unroll
+      for (int i = 0; i < DKP / F::KS; ++i) {
+        if constexpr (BF) {
+          const int col = i * F::KS + 8 * g4;
+          bf16x8 x = {};
+          if (tq < T && col < dk) x = *reinterpret_cast<const bf16x8*>(qg + (size_t)tq * dk + col);
+          qf[i] = x;
+        } else {
+          const int col = i * F::KS + g4;
+          qf[i] = (tq < T && col < dk) ? qg[(size_t)tq * dk + col] : 0.f;
+        }
+      }
+    }
+    // Stage K (row-major) and K~^T = (K * exp(sf))^T; bf16 splits K~ into hi + lo.
     constexpr int RV = DKP / VEC;
 #pragma unroll 2
     for (int idx = tid; idx < C * RV; idx += NT) {  // uniform trip count (DKP/(4*VEC))
       const int row = idx / RV, col = (idx - row * RV) * VEC;
       const int tok = tok0 + row;
-      vecT qv = {}, kv = {};
-      if (tok < T && col < dk) {
-        qv = *reinterpret_cast<const vecT*>(qg + (size_t)tok * dk + col);
-        kv = *reinterpret_cast<const vecT*>(kg + (size_t)tok * dk + col);
-      }
-      *reinterpret_cast<vecT*>(Qs + row * LDQ + col) = qv;
+      vecT kv = {};
+      if (tok < T && col < dk) kv = *reinterpret_cast<const vecT*>(kg + (size_t)tok * dk + col);
       *reinterpret_cast<vecT*>(Ks + row * LDQ + col) = kv;
       const float sc = __expf(__shfl(sf, row));
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) KtT[(col + e) * LDK + row] = IT(static_cast<float>(kv[e]) * sc);
+      for (int e = 0; e < VEC; ++e) {
+        const float x = static_cast<float>(kv[e]) * sc;
+        if constexpr (BF) {
+          bf16 h, l;
+          split_bf16(x, h, l);
+          KtT[(col + e) * LDK + row] = h;
+          KtL[(col + e) * LDK + row] = l;
+        } else {
+          KtT[(col + e) * LDK + row] = x;
+        }
+      }
     }
     // Stage V^T of this 16-wide dv slice.
     constexpr int VV = 16 / VEC;
@@ -250,7 +279,7 @@ fwd_sweep_kernel(FwdArgs a) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < DKP; k0 += F::KS)
-          acc = F::mma(F::load(Ks, LDQ, 16 * kb, k0, lane), F::load(Qs, LDQ, 16 * w, k0, lane), acc);
+          acc = F::mma(F::load(Ks, LDQ, 16 * kb, k0, lane), qf[k0 / F::KS], acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int kj = 16 * kb + 4 * g4 + r;
@@ -298,9 +327,6 @@ fwd_sweep_kernel(FwdArgs a) {
     }
 
     // ---------------- inter chunk: one bucket per set bit of n -------------
-    typename F::V qf[DKP / F::KS];
-#pragma unroll
-    for (int i = 0; i < DKP / F::KS; ++i) qf[i] = F::load(Qs, LDQ, 16 * w, i * F::KS, lane);
     unsigned live = static_cast<unsigned>(n);
     while (live) {
       const int b = __builtin_ctz(live);
@@ -341,10 +367,10 @@ fwd_sweep_kernel(FwdArgs a) {
     if (n + 1 < n1) {
       const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
       for (int t = w; t < DKP / 16; t += NW) {
+        // Decayed sum of the lower levels first; the chunk state is then
+        // accumulated onto it by the MFMAs, whose result is consumed in the
+        // same basic block (no branch between MFMA and the accumulator read).
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k0 = 0; k0 < CK; k0 += F::KS)
-          acc = F::mma(F::load(KtT, LDK, 16 * t, k0, lane), F::load(VtT, LDK, 0, k0, lane), acc);
         const int col0 = 16 * t + 4 * g4;  // dk index of acc[0]; li is the dv column
         for (int b = 0; b < m; ++b) {
           const float f = __expf(dec_s[b] + Atot);
@@ -360,6 +386,12 @@ fwd_sweep_kernel(FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] += f * x[r];
           }
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < CK; k0 += F::KS) {
+          const typename F::V vb = F::load(VtT, LDK, 0, k0, lane);
+          acc = F::mma(F::load(KtT, LDK, 16 * t, k0, lane), vb, acc);
+          if constexpr (BF) acc = F::mma(F::load(KtL, LDK, 16 * t, k0, lane), vb, acc);
         }
         unsigned char* slot = st + m * Cfg::SLOT_BYTES;
         if constexpr (BF) {
@@ -403,7 +435,8 @@ struct SegCfg {
   static constexpr int VEC = 16 / (int)sizeof(IT);
   static constexpr int MAXT = (DKP / 16) * (DVG / 16) / 4;  // accumulator tiles per wave
   static constexpr int KT_OFF = 0;
-  static constexpr int VT_OFF = align16(DKP * LDK * (int)sizeof(IT));
+  static constexpr int KT_BYTES = align16(DKP * LDK * (int)sizeof(IT)) * (BF ? 2 : 1);  // hi (+ lo)
+  static constexpr int VT_OFF = KT_BYTES;
   static constexpr int BYTES = VT_OFF + align16(DVG * LDK * (int)sizeof(IT));
 };
 
@@ -417,6 +450,7 @@ seg_state_kernel(SegArgs a) {
 
   extern __shared__ __align__(16) unsigned char smem[];
   IT* KtT = reinterpret_cast<IT*>(smem + Cfg::KT_OFF);
+  IT* KtL = reinterpret_cast<IT*>(smem + Cfg::KT_OFF + Cfg::KT_BYTES / 2);  // bf16 lo half
   IT* VtT = reinterpret_cast<IT*>(smem + Cfg::VT_OFF);
 
   const int ndvg = (a.dv + Cfg::DVG - 1) / Cfg::DVG;
@@ -462,7 +496,17 @@ seg_state_kernel(SegArgs a) {
       if (tok < s1 && col < dk) kv = *reinterpret_cast<const vecT*>(kg + (size_t)tok * dk + col);
       const float sc = __expf(__shfl(sf, row));
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) KtT[(col + e) * LDK + row] = IT(static_cast<float>(kv[e]) * sc);
+      for (int e = 0; e < VEC; ++e) {
+        const float x = static_cast<float>(kv[e]) * sc;
+        if constexpr (Cfg::BF) {
+          bf16 h, l;
+          split_bf16(x, h, l);
+          KtT[(col + e) * LDK + row] = h;
+          KtL[(col + e) * LDK + row] = l;
+        } else {
+          KtT[(col + e) * LDK + row] = x;
+        }
+      }
     }
     const int vrow = dvw / VEC;
     for (int idx = tid; idx < KB * vrow; idx += NT) {
@@ -484,8 +528,11 @@ seg_state_kernel(SegArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) c[r] *= fa;
 #pragma unroll
-        for (int k0 = 0; k0 < KB; k0 += F::KS)
-          c = F::mma(F::load(KtT, LDK, 16 * t, k0, lane), F::load(VtT, LDK, 16 * u, k0, lane), c);
+        for (int k0 = 0; k0 < KB; k0 += F::KS) {
+          const typename F::V vb = F::load(VtT, LDK, 16 * u, k0, lane);
+          c = F::mma(F::load(KtT, LDK, 16 * t, k0, lane), vb, c);
+          if constexpr (Cfg::BF) c = F::mma(F::load(KtL, LDK, 16 * t, k0, lane), vb, c);
+        }
         acc[j] = c;
       }
     }
