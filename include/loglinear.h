@@ -44,6 +44,15 @@ enum loglinear_status {
 
 enum loglinear_dtype { LL_BF16 = 0, LL_F32 = 1 };
 
+/* Sweep kernel selection (loglinear_fwd_opts.kernel). */
+enum loglinear_kernel {
+  LL_KERNEL_AUTO = 0,           /* register-state kernel where it applies, else LDS-state */
+  LL_KERNEL_LDS_STATE = 1,      /* bucket states in LDS, 16 dv columns per workgroup; all shapes */
+  LL_KERNEL_REGISTER_STATE = 2  /* bucket states in registers, 64 dv columns per workgroup;
+                                   bf16, C = 64, 64 < dk <= 128, dv % 64 == 0,
+                                   ceil(T / 64) <= 256 */
+};
+
 /* Number of lambda levels for sequence length T >= 1: bit_length(T-1) + 1
  * (T = 64 -> 7, 2048 -> 12, 16384 -> 15, 65536 -> 17).  Returns 0 for T < 1. */
 int loglinear_num_levels(int T);
@@ -83,6 +92,8 @@ int loglinear_fwd_f32(const float* q, const float* k, const float* v, const floa
  *                  span whole segments are built by a separate segment pass.
  *                  Changes only the rounding order, never the result's
  *                  definition; exposed so every path can be exercised at small T.
+ *   kernel       : a loglinear_kernel value; an explicit choice that does not
+ *                  apply to the sizes returns LL_ERR_UNSUPPORTED.
  *   workspace    : NULL = allocate stream-ordered on `stream`; otherwise a
  *                  device buffer of at least loglinear_fwd_workspace_size()
  *                  bytes, 256-byte aligned, owned by the caller, not used by
@@ -97,6 +108,7 @@ int loglinear_fwd_f32(const float* q, const float* k, const float* v, const floa
 typedef struct {
   int dtype;
   int seg_log2;
+  int kernel;
   void* workspace;
   size_t workspace_bytes;
   void* const* phase_events;

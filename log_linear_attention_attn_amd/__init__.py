@@ -44,7 +44,7 @@ class LogLinearError(RuntimeError):
 
 
 class _FwdOpts(ctypes.Structure):
-    _fields_ = [("dtype", ctypes.c_int), ("seg_log2", ctypes.c_int),
+    _fields_ = [("dtype", ctypes.c_int), ("seg_log2", ctypes.c_int), ("kernel", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("phase_events", ctypes.c_void_p)]
 
@@ -137,8 +137,11 @@ def fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1) -> int:
     return int(n)
 
 
+KERNEL_AUTO, KERNEL_LDS_STATE, KERNEL_REGISTER_STATE = 0, 1, 2
+
+
 def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, workspace=None,
-           phase_events=None):
+           phase_events=None, kernel: int = KERNEL_AUTO):
     """Log-linear attention forward through loglinear_fwd_ex.
 
     q, k: [B, H, T, dk]; v: [B, H, T, dv] (all bf16 or all fp32);
@@ -170,7 +173,7 @@ def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, works
         ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in phase_events])
         if not all(ev):
             raise ValueError("record each phase event once before passing it")
-    opts = _FwdOpts(LL_BF16 if q.dtype == torch.bfloat16 else LL_F32, int(seg_log2),
+    opts = _FwdOpts(LL_BF16 if q.dtype == torch.bfloat16 else LL_F32, int(seg_log2), int(kernel),
                     _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
                     ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
     st = lib().loglinear_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out),

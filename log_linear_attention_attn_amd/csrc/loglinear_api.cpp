@@ -68,16 +68,27 @@ int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* 
 
 int run_fwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
             const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
-            int seg_log2, void* workspace, size_t workspace_bytes, void* const* events,
-            hipStream_t stream) {
+            int seg_log2, int kernel, void* workspace, size_t workspace_bytes,
+            void* const* events, hipStream_t stream) {
   FwdPlan p;
   int st = plan_fwd(B, H, T, dk, dv, C, seg_log2, &p);
   if (st != LL_OK) return st;
   if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
   if (B == 0 || H == 0 || T == 0) return LL_OK;
   if (!q || !k || !v || !log_a || !lambda || !out) return LL_ERR_NULL;
-  const int lds = ll::sweep_lds_bytes(dtype, C, p.DKP, p.L, p.nslot);
-  if (lds < 0 || lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
+  // Sweep kernel: the register-state kernel covers bf16, C = 64, 64 < dk <= 128,
+  // dv a multiple of 64 and at most rs_max_slots() chunk-level Fenwick bits;
+  // the LDS-state kernel covers everything else.
+  const bool rs_ok = dtype == LL_BF16 && C == 64 && dk > 64 && dv % 64 == 0 &&
+                     p.nslot <= ll::rs_max_slots() && p.L <= 16 &&
+                     ll::rs_lds_bytes(p.L, p.nslot) <= ll::kMaxLds;
+  if (kernel < LL_KERNEL_AUTO || kernel > LL_KERNEL_REGISTER_STATE) return LL_ERR_SHAPE;
+  if (kernel == LL_KERNEL_REGISTER_STATE && !rs_ok) return LL_ERR_UNSUPPORTED;
+  const bool use_rs = kernel == LL_KERNEL_REGISTER_STATE || (kernel == LL_KERNEL_AUTO && rs_ok);
+  if (!use_rs) {
+    const int lds = ll::sweep_lds_bytes(dtype, C, p.DKP, p.L, p.nslot);
+    if (lds < 0 || lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
+  }
   if (workspace && workspace_bytes < p.ws_total) return LL_ERR_WORKSPACE;
 
   void* ws = workspace;
@@ -113,8 +124,9 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
     ll::FwdArgs fa{q, k, v, log_a, lambda, out, nodes, seg_decay, p.BH, T, dk, dv, p.L,
                    p.seg_log2, p.nseg, p.nslot};
     const long long pairs = (long long)p.BH * p.nseg;
-    const long long nblocks = ((pairs + 7) / 8) * 8 * (dv / 16);
+    const long long nblocks = ((pairs + 7) / 8) * 8 * (use_rs ? dv / 64 : dv / 16);
     if (nblocks > 0x7fffffffLL) st = LL_ERR_UNSUPPORTED;
+    else if (use_rs) st = ll::launch_sweep_rs(fa, static_cast<int>(nblocks), stream);
     else st = ll::launch_sweep(dtype, C, p.DKP, fa, static_cast<int>(nblocks), stream);
   }
   mark(3);
@@ -148,14 +160,14 @@ int loglinear_num_levels(int T) { return T >= 1 ? bit_length(T - 1) + 1 : 0; }
 int loglinear_fwd(const void* q, const void* k, const void* v, const float* log_a,
                   const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
                   void* stream) {
-  return run_fwd(LL_BF16, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, nullptr, 0, nullptr,
+  return run_fwd(LL_BF16, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
                  static_cast<hipStream_t>(stream));
 }
 
 int loglinear_fwd_f32(const float* q, const float* k, const float* v, const float* log_a,
                       const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
                       void* stream) {
-  return run_fwd(LL_F32, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, nullptr, 0, nullptr,
+  return run_fwd(LL_F32, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
                  static_cast<hipStream_t>(stream));
 }
 
@@ -164,7 +176,7 @@ int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* l
                      const loglinear_fwd_opts* opts, void* stream) {
   if (!opts) return LL_ERR_NULL;
   return run_fwd(opts->dtype, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, opts->seg_log2,
-                 opts->workspace, opts->workspace_bytes, opts->phase_events,
+                 opts->kernel, opts->workspace, opts->workspace_bytes, opts->phase_events,
                  static_cast<hipStream_t>(stream));
 }
 

@@ -1,0 +1,436 @@
+// Register-resident chunk sweep for the bf16 forward with C = 64, dk <= 128 and
+// dv a multiple of 64 (the log-linear Mamba-2 shapes).  Same decomposition as
+// fwd_sweep_kernel (loglinear_fwd.hip): per (b,h, segment) the chunks are
+// walked in order and the chunk-granular Fenwick bucket states are merged with
+// the lssb rule ([P1] 解码：基于 lssb 的状态更新, applied to whole chunks;
+// [P1] 训练：分块并行扫描算法 for the split into intra / inter chunk work).
+//
+//   [P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制"
+//
+// Work split of one 256-thread workgroup = (b,h, segment, 64 dv columns):
+//   phase 1  the 10 causal 16x16 score tiles of the chunk are shared out over
+//            the 4 waves; each masked tile P (Fenwick level x decay x lambda)
+//            is split bf16 hi/lo and parked in LDS in MFMA A-operand order.
+//   phase 2  wave w owns dv columns 16w..16w+15 of the workgroup for all 64
+//            rows: P V, one Q G_b product per live level b, the output, the
+//            chunk state K^T (V*decay) and the lssb merge.  The bucket states
+//            G_b (dk x 16 columns, bf16 hi + lo) never leave the wave's
+//            registers.
+// K, Q and V are staged row-major; the operands that contract over tokens are
+// read with the LDS transpose load (ds_read_b64_tr_b16), so no transposed
+// stores are needed.  The next chunk's global loads are issued before the
+// current chunk's math (register prefetch).
+#include <hip/hip_runtime.h>
+
+#include "ll_device.h"
+#include "ll_internal.h"
+
+namespace ll {
+
+namespace rs {
+
+constexpr int C = 64, DKP = 128, NKS = DKP / 32, LOGC = 6, NT = 256;
+constexpr int LDQ = DKP + 8;  // Qs, Ks row stride (bf16)
+constexpr int LDV = 64 + 8;   // Vs row stride (bf16): 64 dv columns
+constexpr int QS_OFF = 0;
+constexpr int KS_OFF = QS_OFF + C * LDQ * 2;
+constexpr int VS_OFF = KS_OFF + C * LDQ * 2;
+constexpr int PS_OFF = VS_OFF + C * LDV * 2;
+constexpr int PS_BYTES = 4 /*mi*/ * 2 /*ks*/ * 2 /*hi,lo*/ * 64 * 16;
+constexpr int CL_OFF = PS_OFF + PS_BYTES;  // cl[64], esf[64], ecl[64]
+constexpr int LAM_OFF = CL_OFF + 3 * C * 4;
+
+__host__ __device__ inline int lamw_off(int L) { return LAM_OFF + C * L * 4; }
+__host__ __device__ inline int lds_bytes(int L, int nslot) { return lamw_off(L) + (nslot > 0 ? nslot : 1) * C * 4; }
+
+typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed 8-byte LDS read: within each 16-lane group, lane i receives
+// element (i & 3) of the 4-element vectors addressed by lanes 4k + (i >> 2),
+// k = 0..3.
+__device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(reinterpret_cast<__attribute__((address_space(3))) char*>(
+          reinterpret_cast<uintptr_t>(p))));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace rs
+
+template <int NSLOT>
+__global__ void __launch_bounds__(256)
+fwd_rs_kernel(FwdArgs a) {
+  using namespace rs;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* Qs = reinterpret_cast<bf16*>(smem + QS_OFF);
+  bf16* Ks = reinterpret_cast<bf16*>(smem + KS_OFF);
+  bf16* Vs = reinterpret_cast<bf16*>(smem + VS_OFF);
+  bf16x8* Ps = reinterpret_cast<bf16x8*>(smem + PS_OFF);  // [mi][ks][hl][lane]
+  float* cl_s = reinterpret_cast<float*>(smem + CL_OFF);
+  float* esf_s = cl_s + C;
+  float* ecl_s = esf_s + C;
+  float* lam_s = reinterpret_cast<float*>(smem + LAM_OFF);
+  float* lamw_s = reinterpret_cast<float*>(smem + lamw_off(a.L));
+
+  const int D = a.dv >> 6;  // 64-column groups
+  const int id = blockIdx.x;
+  const int px = id & 7, rest = id >> 3;
+  const int dg = rest % D, pg = rest / D;
+  const int p = pg * 8 + px;
+  if (p >= a.BH * a.nseg) return;
+  const int bh = p / a.nseg, seg = p - bh * a.nseg;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int T = a.T, L = a.L, dk = a.dk, dv = a.dv;
+  const int N = (T + C - 1) / C;
+  const int n0 = seg << a.seg_log2;
+  const int n1 = min(N, n0 + (1 << a.seg_log2));
+  const int dv0 = dg * 64;
+  const size_t bhT = (size_t)bh * T;
+  const bf16* __restrict__ qg = static_cast<const bf16*>(a.q) + bhT * dk;
+  const bf16* __restrict__ kg = static_cast<const bf16*>(a.k) + bhT * dk;
+  const bf16* __restrict__ vg = static_cast<const bf16*>(a.v) + bhT * dv + dv0;
+  const float* __restrict__ lag = a.log_a + bhT;
+  const float* __restrict__ lamg = a.lam + bhT * L;
+  float* __restrict__ outg = a.out + bhT * dv + dv0 + 16 * w;
+
+  // ---- bucket states of this wave's 16 columns: G[b][ks] holds dk
+  // 32ks + 8*g4 + e (e = 0..7) of column li, split bf16 hi / lo.
+  bf16x8 Gh[NSLOT][NKS], Gl[NSLOT][NKS];
+  float dec[NSLOT];  // log decay since each bucket state was formed
+#pragma unroll
+  for (int b = 0; b < NSLOT; ++b) {
+    dec[b] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      Gh[b][ks] = bf16x8{};
+      Gl[b][ks] = bf16x8{};
+    }
+  }
+  // Levels spanning whole segments: bit b >= seg_log2 of n0 <-> bit
+  // b - seg_log2 of the segment; its bucket is the node starting at segment
+  // (seg >> b') << b'.
+#pragma unroll
+  for (int b = 0; b < NSLOT; ++b) {
+    if (b >= a.seg_log2 && ((n0 >> b) & 1)) {
+      const int bp = b - a.seg_log2;
+      const int gc = (seg >> bp) << bp;
+      const float* __restrict__ node =
+          a.nodes + ((size_t)(bh * a.nseg + gc) * dv + dv0 + 16 * w + li) * DKP + 8 * g4;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(node + 32 * ks);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(node + 32 * ks + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16 h, l;
+          split_bf16(x0[e], h, l);
+          Gh[b][ks][e] = h;
+          Gl[b][ks][e] = l;
+          split_bf16(x1[e], h, l);
+          Gh[b][ks][4 + e] = h;
+          Gl[b][ks][4 + e] = l;
+        }
+      }
+      float d = 0.f;
+      for (int r = gc; r < seg; ++r) d += a.seg_decay[bh * a.nseg + r];
+      dec[b] = d;
+    }
+  }
+
+  // ---- register prefetch of one chunk ----------------------------------
+  bf16x8 pq[4], pk[4], pv[2];
+  f32x4 plam;
+  float pla;
+  auto prefetch = [&](int n) {
+    const int tok0 = n * C;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
+      const int tok = tok0 + row;
+      bf16x8 x = {}, y = {};
+      if (tok < T && col < dk) {
+        x = *reinterpret_cast<const bf16x8*>(qg + (size_t)tok * dk + col);
+        y = *reinterpret_cast<const bf16x8*>(kg + (size_t)tok * dk + col);
+      }
+      pq[i] = x;
+      pk[i] = y;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + NT * i, row = v >> 3, col = (v & 7) * 8;
+      const int tok = tok0 + row;
+      bf16x8 x = {};
+      if (tok < T) x = *reinterpret_cast<const bf16x8*>(vg + (size_t)tok * dv + col);
+      pv[i] = x;
+    }
+    {
+      // lambda rows of the chunk: C*L floats, four per thread (scalar loads:
+      // rows of L floats need not be 16-byte aligned)
+      const int v4 = tid * 4;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (v4 < C * L) {
+        const size_t base = (size_t)tok0 * L + v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (tok0 + (v4 + e) / L < T) x[e] = lamg[base + e];
+      }
+      plam = x;
+    }
+    pla = (tok0 + lane < T) ? lag[tok0 + lane] : 0.f;
+  };
+
+  prefetch(n0);
+
+  for (int n = n0; n < n1; ++n) {
+    const int tok0 = n * C;
+    // ---------------- stage: registers -> LDS ------------------------------
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
+      *reinterpret_cast<bf16x8*>(Qs + row * LDQ + col) = pq[i];
+      *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + NT * i, row = v >> 3, col = (v & 7) * 8;
+      *reinterpret_cast<bf16x8*>(Vs + row * LDV + col) = pv[i];
+    }
+    if (tid * 4 < C * L) *reinterpret_cast<f32x4*>(lam_s + tid * 4) = plam;
+    // in-chunk decay sums (each wave computes them; wave 0 publishes)
+    float cl = pla;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(cl, off);
+      if (lane >= off) cl += y;
+    }
+    // chunk total, made wave-uniform so the per-level decays live in SGPRs
+    const float Atot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__shfl(cl, 63))));
+    // decay from token lane to the chunk's last token, summed directly
+    float sf = __shfl_down(pla, 1);
+    if (lane == 63) sf = 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(sf, off);
+      if (lane + off < 64) sf += y;
+    }
+    if (w == 0) {
+      cl_s[lane] = cl;
+      esf_s[lane] = __expf(sf);
+      ecl_s[lane] = __expf(cl);
+    }
+    __syncthreads();
+
+    if (n + 1 < n1) prefetch(n + 1);
+
+    // ---------------- phase 1: masked score tiles -> LDS -------------------
+    // tile table: wave 0 (0,0)(3,0); wave 1 (1,0)(1,1)(3,1); wave 2 (2,0)(2,1)(2,2);
+    // wave 3 (3,3)(3,2).  Slots above the diagonal inside the last K-step of
+    // an even query block, (0,1) and (2,3), are written as zeros.
+    {
+      const int ntile = (w == 0 || w == 3) ? 2 : 3;
+      for (int it = 0; it < ntile; ++it) {
+        int qb, kb;
+        if (w == 0) { qb = it ? 3 : 0; kb = 0; }
+        else if (w == 1) { qb = it == 2 ? 3 : 1; kb = it == 2 ? 1 : it; }
+        else if (w == 2) { qb = 2; kb = it; }
+        else { qb = 3; kb = it ? 2 : 3; }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + li) * LDQ + 32 * ks + 8 * g4);
+          const bf16x8 qb8 = *reinterpret_cast<const bf16x8*>(Qs + (16 * qb + li) * LDQ + 32 * ks + 8 * g4);
+          acc = mma(ka, qb8, acc);
+        }
+        // acc[r] = score(query 16qb+li, key 16kb+4g4+r)
+        const int qi = 16 * qb + li;
+        const float clq = cl_s[qi];
+        const f32x4 clk = *reinterpret_cast<const f32x4*>(cl_s + 16 * kb + 4 * g4);
+        f32x4 pv4;
+        if (kb < qb) {
+          const float lam = lam_s[qi * L + 4 + (32 - __clz(qb ^ kb))];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pv4[r] = acc[r] * lam * __expf(clq - clk[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kj = 16 * kb + 4 * g4 + r;
+            pv4[r] = kj <= qi ? acc[r] * lam_s[qi * L + level_of(qi, kj)] * __expf(clq - clk[r]) : 0.f;
+          }
+        }
+        bf16x4 h, l;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bf16 hh, ll;
+          split_bf16(pv4[r], hh, ll);
+          h[r] = hh;
+          l[r] = ll;
+        }
+        bf16* dst = reinterpret_cast<bf16*>(Ps + ((qb * 2 + (kb >> 1)) * 2) * 64 + lane) + 4 * (kb & 1);
+        *reinterpret_cast<bf16x4*>(dst) = h;
+        *reinterpret_cast<bf16x4*>(dst + 64 * 8) = l;
+      }
+      if (w == 0 || w == 3) {
+        const int qb = w == 0 ? 0 : 2;  // zero slot (qb, qb+1)
+        bf16* dst = reinterpret_cast<bf16*>(Ps + ((qb * 2 + (qb >> 1)) * 2) * 64 + lane) + 4;
+        *reinterpret_cast<bf16x4*>(dst) = bf16x4{};
+        *reinterpret_cast<bf16x4*>(dst + 64 * 8) = bf16x4{};
+      }
+      // lambda of each inter-chunk level times exp(cl), for the Q.G weights
+      for (int idx = tid; idx < a.nslot * C; idx += NT) {
+        const int b = idx >> 6, row = idx & 63;
+        lamw_s[idx] = lam_s[row * L + LOGC + 1 + b] * ecl_s[row];
+      }
+    }
+    __syncthreads();
+
+    // ---------------- phase 2: this wave's 16 dv columns -------------------
+    const int c0 = 16 * w;
+    f32x4 O[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) O[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // O = P V: V operand by transposed reads, keys in the order of the score
+    // tile layout (32ks + 4g4 + e, then +16).
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int j = li;  // lane within its 16-lane group addresses row (j >> 2), col quad (j & 3)
+      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (j >> 2)) * LDV + c0 + 4 * (j & 3);
+      const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
+#pragma unroll
+      for (int mi = 2 * ks; mi < 4; ++mi) {
+        const bf16x8 ph = Ps[((mi * 2 + ks) * 2 + 0) * 64 + lane];
+        const bf16x8 pl = Ps[((mi * 2 + ks) * 2 + 1) * 64 + lane];
+        O[mi] = mma(ph, vb, O[mi]);
+        O[mi] = mma(pl, vb, O[mi]);
+      }
+    }
+    // O += sum over live levels b of diag(lambda * decay) (Q G_b)
+    float edec[NSLOT];
+#pragma unroll
+    for (int b = 0; b < NSLOT; ++b) edec[b] = __expf(dec[b]);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      bf16x8 qa[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qa[ks] = *reinterpret_cast<const bf16x8*>(Qs + (16 * mi + li) * LDQ + 32 * ks + 8 * g4);
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b) {
+        if ((n >> b) & 1) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            acc = mma(qa[ks], Gh[b][ks], acc);
+            acc = mma(qa[ks], Gl[b][ks], acc);
+          }
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(lamw_s + b * C + 16 * mi + 4 * g4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[mi][r] += wv[r] * edec[b] * acc[r];
+        }
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = tok0 + 16 * mi + 4 * g4 + r;
+        if (tok < T) outg[(size_t)tok * dv + li] = O[mi][r];
+      }
+    }
+
+    // ---------------- chunk state + lssb merge (registers) -----------------
+    if (n + 1 < n1) {
+      const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
+      // decayed V of this wave's columns, tokens 32ks + 8g4 + e, split hi/lo
+      bf16x8 vh[2], vl[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int j = li;
+        const bf16* v0 = Vs + (32 * ks + 8 * g4 + (j >> 2)) * LDV + c0 + 4 * (j & 3);
+        const bf16x8 x = cat(tr_read(v0), tr_read(v0 + 4 * LDV));
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4 + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16 hh, ll;
+          split_bf16(static_cast<float>(x[e]) * (e < 4 ? e0[e] : e1[e - 4]), hh, ll);
+          vh[ks][e] = hh;
+          vl[ks][e] = ll;
+        }
+      }
+      // S tiles, one at a time: t = 2*kq + half covers dk
+      // 32kq + 8*(row>>2) + 4*half + (row&3); lower levels (decayed to the end
+      // of chunk n) are summed first, the chunk's K^T (V*decay) is accumulated
+      // onto them, and the result becomes the level-m bucket state.
+      float fl[NSLOT];
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b) fl[b] = b < m ? __expf(dec[b] + Atot) : 0.f;
+#pragma unroll
+      for (int t = 0; t < 2 * NKS; ++t) {
+        const int kq = t >> 1, half = t & 1;
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NSLOT; ++b) {
+          if (b < m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              S[r] += fl[b] * (static_cast<float>(Gh[b][kq][4 * half + r]) +
+                               static_cast<float>(Gl[b][kq][4 * half + r]));
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int j = li;
+          const bf16* k0 = Ks + (32 * ks + 8 * g4 + (j >> 2)) * LDQ + 32 * kq + 8 * (j & 3) + 4 * half;
+          const bf16x8 ka = cat(tr_read(k0), tr_read(k0 + 4 * LDQ));
+          S = mma(ka, vh[ks], S);
+          S = mma(ka, vl[ks], S);
+        }
+#pragma unroll
+        for (int b = 0; b < NSLOT; ++b) {
+          if (b == m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              bf16 hh, ll;
+              split_bf16(S[r], hh, ll);
+              Gh[b][kq][4 * half + r] = hh;
+              Gl[b][kq][4 * half + r] = ll;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b) {
+        if (b == m) dec[b] = 0.f;
+        else if (b > m) dec[b] += Atot;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+int rs_max_slots() { return 8; }
+
+int rs_lds_bytes(int L, int nslot) { return rs::lds_bytes(L, nslot); }
+
+int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t stream) {
+  const int bytes = rs::lds_bytes(a.L, a.nslot);
+  if (a.nslot > 8 || bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_rs_kernel<8>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return LL_ERR_HIP;
+  hipLaunchKernelGGL(fwd_rs_kernel<8>, dim3(nblocks), dim3(256), bytes, stream, a);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
+}  // namespace ll

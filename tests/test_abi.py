@@ -70,15 +70,23 @@ def test_fwd_ex_options():
     L = ll.lib()
     p = ctypes.c_void_p(1)
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, None, None) == LL_ERR_NULL
-    bad = ll._FwdOpts(7, -1, None, 0, None)
+    bad = ll._FwdOpts(7, -1, 0, None, 0, None)
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(bad), None) == LL_ERR_SHAPE
-    bad = ll._FwdOpts(0, 13, None, 0, None)
+    bad = ll._FwdOpts(0, 13, 0, None, 0, None)
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(bad), None) == LL_ERR_SHAPE
     # a caller workspace smaller than required is rejected before any launch
     need = ll.fwd_workspace_size(1, 1, 4096, 64, 64, 64, 1)
     assert need > 0
-    small = ll._FwdOpts(0, 1, ctypes.c_void_p(256), need - 1, None)
+    small = ll._FwdOpts(0, 1, 0, ctypes.c_void_p(256), need - 1, None)
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 4096, 64, 64, 64, ctypes.byref(small), None) == LL_ERR_WORKSPACE
+    # kernel selection: out-of-range value, and the register-state kernel on sizes it does not cover
+    bad = ll._FwdOpts(0, -1, 3, None, 0, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(bad), None) == LL_ERR_SHAPE
+    rs = ll._FwdOpts(0, -1, 2, None, 0, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(rs), None) == LL_ERR_UNSUPPORTED
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 128, 48, 64, ctypes.byref(rs), None) == LL_ERR_UNSUPPORTED
+    f32 = ll._FwdOpts(1, -1, 2, None, 0, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 128, 64, 64, ctypes.byref(f32), None) == LL_ERR_UNSUPPORTED
 
 
 def test_workspace_size_formula():
