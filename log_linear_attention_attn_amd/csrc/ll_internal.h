@@ -62,6 +62,7 @@ int launch_seg_nodes(const NodeArgs& a, int BH, hipStream_t s);
 int rs_max_slots();
 int rs_lds_bytes(int L, int nslot);
 int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t s);
+int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t s);
 int launch_level_table(signed char* lev, int T, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 

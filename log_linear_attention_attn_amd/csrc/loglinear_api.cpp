@@ -110,7 +110,10 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   if (p.nseg > 1) {
     ll::SegArgs sa{k, v, log_a, seg_state, seg_decay, p.BH, T, dk, dv, C, p.seg_log2, p.nseg};
     const int ndvg = (dv + 127) / 128;
-    st = ll::launch_seg_state(dtype, p.DKP, sa, p.BH * (p.nseg - 1) * ndvg, stream);
+    if (dtype == LL_BF16 && p.DKP == 128 && dv % 64 == 0)
+      st = ll::launch_seg_state_rs(sa, p.BH, stream);
+    else
+      st = ll::launch_seg_state(dtype, p.DKP, sa, p.BH * (p.nseg - 1) * ndvg, stream);
     mark(1);
     if (st == LL_OK) {
       ll::NodeArgs na{seg_state, seg_decay, nodes, p.nseg, dv * p.DKP};

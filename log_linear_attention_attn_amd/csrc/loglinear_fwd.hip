@@ -19,9 +19,9 @@
 // Kernels (one pass over Q, one over K/V per dv slice; states stay on chip):
 //   seg_state_kernel  per (b,h, segment of 2^S chunks): decayed sum of k v^T
 //                     over the segment (bf16 / fp32 matrix cores).
-//   seg_node_kernel   per (b,h, state element): walks the segments with the
-//                     lssb merge rule ([P1] 解码) and emits, for every segment
-//                     g >= 1, the bucket state that starts at g.
+//   seg_node_kernel   per (b,h, segment g >= 1, state element): the bucket
+//                     state that starts at g, i.e. the merge the lssb rule
+//                     ([P1] 解码) makes on the step into g.
 //   fwd_sweep_kernel  per (b,h, segment, 16-wide dv slice): walks the
 //                     segment's chunks in order, keeping the bucket states of
 //                     levels inside the segment in LDS and merging them with
@@ -552,42 +552,25 @@ seg_state_kernel(SegArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// seg_node_kernel: lssb walk over segments, one thread per state element.
-// At the step into segment g (g >= 1), with m = lssb(g), the bucket of level
-// m is segment g-1 plus the buckets of levels < m, decayed to the start of g.
-// That bucket is written as node g; segment g' uses node (g' >> b) << b for
-// every set bit b of g'.
+// seg_node_kernel: the bucket state that starts at segment g >= 1.  With
+// m = lssb(g) it covers segments [g - 2^m, g) (the merge the lssb rule makes
+// on the step into g, [P1] 解码), decayed to the start of g:
+//   node_g = sum_{g'} exp(A_{g'+1} + ... + A_{g-1}) T_{g'}.
+// One thread per (b,h, g, state element); the sum runs forward, rescaling the
+// partial sum by each segment's total decay.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) seg_node_kernel(NodeArgs a) {
-  constexpr int MAXB = 24;
   const int e = blockIdx.x * 256 + threadIdx.x;
-  const int bh = blockIdx.y;
+  const int g = blockIdx.y + 1;
+  const int bh = blockIdx.z;
   if (e >= a.E) return;
-  float stv[MAXB], dec[MAXB];
-#pragma unroll
-  for (int b = 0; b < MAXB; ++b) {
-    stv[b] = 0.f;
-    dec[b] = 0.f;
-  }
   const size_t base = (size_t)bh * a.nseg;
-  for (int g = 1; g < a.nseg; ++g) {
-    const int m = lssb(static_cast<uint32_t>(g));
-    const float Ag = a.seg_decay[base + g - 1];
-    float x = a.seg_state[(base + g - 1) * a.E + e];
-#pragma unroll
-    for (int b = 0; b < MAXB; ++b)
-      if (b < m) x += __expf(dec[b] + Ag) * stv[b];
-#pragma unroll
-    for (int b = 0; b < MAXB; ++b) {
-      if (b == m) {
-        stv[b] = x;
-        dec[b] = 0.f;
-      } else if (b > m) {
-        dec[b] += Ag;
-      }
-    }
-    a.nodes[(base + g) * a.E + e] = x;
-  }
+  const int m = lssb(static_cast<uint32_t>(g));
+  const int g0 = g - (1 << m);
+  float x = 0.f;
+  for (int gp = g0; gp < g; ++gp)
+    x = x * __expf(a.seg_decay[base + gp]) + a.seg_state[(base + gp) * a.E + e];
+  a.nodes[(base + g) * a.E + e] = x;
 }
 
 // ---------------------------------------------------------------------------
@@ -670,7 +653,8 @@ int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStrea
 }
 
 int launch_seg_nodes(const NodeArgs& a, int BH, hipStream_t s) {
-  hipLaunchKernelGGL(seg_node_kernel, dim3((a.E + 255) / 256, BH), dim3(256), 0, s, a);
+  if (a.nseg < 2) return LL_OK;
+  hipLaunchKernelGGL(seg_node_kernel, dim3((a.E + 255) / 256, a.nseg - 1, BH), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 

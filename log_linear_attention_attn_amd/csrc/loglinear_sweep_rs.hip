@@ -419,6 +419,114 @@ fwd_rs_kernel(FwdArgs a) {
   }
 }
 
+// Segment states for the register-state path (bf16, dk <= 128, dv % 64 == 0):
+// T_g = sum over segment g of exp(cum[end] - cum[s]) k_s v_s^T, written as
+// [dv][128] fp32, plus the segment's total log decay.  Same operand scheme as
+// the chunk state in fwd_rs_kernel: row-major K / V in LDS, transposed reads,
+// V scaled by the decay to the end of each 64-token block and split hi/lo;
+// the running sum is rescaled by each block's total decay.
+__global__ void __launch_bounds__(256) seg_state_rs_kernel(SegArgs a) {
+  using namespace rs;
+  __shared__ __align__(16) bf16 Ks[C * LDQ];
+  __shared__ __align__(16) bf16 Vs[C * LDV];
+  __shared__ __align__(16) float esf_s[C];
+  const int D = a.dv >> 6;
+  const int nsg = a.nseg - 1;  // the last segment's state is never used
+  const int id = blockIdx.x;
+  const int dg = id % D, rest = id / D;
+  const int g = rest % nsg, bh = rest / nsg;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int T = a.T, dk = a.dk, dv = a.dv;
+  const int segtok = a.C << a.seg_log2;
+  const int s0 = g * segtok, s1 = min(T, s0 + segtok);
+  const int dv0 = dg * 64, c0 = 16 * w;
+  const size_t bhT = (size_t)bh * T;
+  const bf16* __restrict__ kg = static_cast<const bf16*>(a.k) + bhT * dk;
+  const bf16* __restrict__ vg = static_cast<const bf16*>(a.v) + bhT * dv + dv0;
+  const float* __restrict__ lag = a.log_a + bhT;
+
+  f32x4 S[2 * NKS];
+#pragma unroll
+  for (int t = 0; t < 2 * NKS; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float Aseg = 0.f;
+  for (int b0 = s0; b0 < s1; b0 += C) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
+      const int tok = b0 + row;
+      bf16x8 x = {};
+      if (tok < s1 && col < dk) x = *reinterpret_cast<const bf16x8*>(kg + (size_t)tok * dk + col);
+      *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = x;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + NT * i, row = v >> 3, col = (v & 7) * 8;
+      const int tok = b0 + row;
+      bf16x8 x = {};
+      if (tok < s1) x = *reinterpret_cast<const bf16x8*>(vg + (size_t)tok * dv + col);
+      *reinterpret_cast<bf16x8*>(Vs + row * LDV + col) = x;
+    }
+    const float la = (b0 + lane < s1) ? lag[b0 + lane] : 0.f;
+    float sf = __shfl_down(la, 1);
+    if (lane == 63) sf = 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(sf, off);
+      if (lane + off < 64) sf += y;
+    }
+    const float Ab = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__shfl(sf, 0) + __shfl(la, 0))));
+    if (w == 0) esf_s[lane] = __expf(sf);
+    __syncthreads();
+    bf16x8 vh[2], vl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16* v0 = Vs + (32 * ks + 8 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
+      const bf16x8 x = cat(tr_read(v0), tr_read(v0 + 4 * LDV));
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4 + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 hh, ll;
+        split_bf16(static_cast<float>(x[e]) * (e < 4 ? e0[e] : e1[e - 4]), hh, ll);
+        vh[ks][e] = hh;
+        vl[ks][e] = ll;
+      }
+    }
+    const float fa = __expf(Ab);
+#pragma unroll
+    for (int t = 0; t < 2 * NKS; ++t) {
+      const int kq = t >> 1, half = t & 1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[t][r] *= fa;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16* k0 = Ks + (32 * ks + 8 * g4 + (li >> 2)) * LDQ + 32 * kq + 8 * (li & 3) + 4 * half;
+        const bf16x8 ka = cat(tr_read(k0), tr_read(k0 + 4 * LDQ));
+        S[t] = mma(ka, vh[ks], S[t]);
+        S[t] = mma(ka, vl[ks], S[t]);
+      }
+    }
+    Aseg += Ab;
+    __syncthreads();
+  }
+  float* __restrict__ Tout =
+      a.seg_state + ((size_t)(bh * a.nseg + g) * dv + dv0 + c0 + li) * DKP + 8 * g4;
+#pragma unroll
+  for (int kq = 0; kq < NKS; ++kq) {
+    *reinterpret_cast<f32x4*>(Tout + 32 * kq) = S[2 * kq];
+    *reinterpret_cast<f32x4*>(Tout + 32 * kq + 4) = S[2 * kq + 1];
+  }
+  if (tid == 0 && dg == 0) a.seg_decay[bh * a.nseg + g] = Aseg;
+}
+
+int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t stream) {
+  const long long nblocks = (long long)BH * (a.nseg - 1) * (a.dv / 64);
+  if (nblocks > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(seg_state_rs_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
 int rs_max_slots() { return 8; }
 
 int rs_lds_bytes(int L, int nslot) { return rs::lds_bytes(L, nslot); }

@@ -178,3 +178,38 @@ def test_caller_workspace_matches_owned():
     b = ll.fwd_ex(q, k, v, la, lam, C=64, seg_log2=2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+RS_CASES = [
+    # (B, H, T, dk, dv, decay, seg_log2)
+    (1, 2, 64, 128, 64, "none", -1),     # one chunk
+    (1, 1, 65, 128, 64, "weak", 0),      # ragged tail of one token
+    (2, 1, 1000, 128, 128, "weak", 2),
+    (1, 2, 1000, 96, 64, "strong", 0),   # dk padded to 128
+    (1, 1, 3000, 128, 192, "none", 3),   # three 64-column groups
+    (1, 1, 4096, 128, 64, "weak", 4),
+]
+
+
+@pytest.mark.parametrize("case", RS_CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}_{}_s{}".format(*c))
+def test_register_state_kernel_parity(case):
+    """The register-state sweep (bucket states in registers) forced on every
+    shape class it covers, against the oracle and against the LDS-state sweep."""
+    B, H, T, dk, dv, decay, s = case
+    w = W.FwdWorkload("rs", B, H, T, dk, dv, 64, "bf16", decay=decay, seed=T + dv)
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    dq, dk_, dv_, dla, dlam = to_dev(q, k, v, la, lam)
+    announce(f"register-state kernel {case}")
+    rs = ll.fwd_ex(dq, dk_, dv_, dla, dlam, C=64, seg_log2=s, kernel=ll.KERNEL_REGISTER_STATE)
+    lds = ll.fwd_ex(dq, dk_, dv_, dla, dlam, C=64, seg_log2=s, kernel=ll.KERNEL_LDS_STATE)
+    torch.cuda.synchronize()
+    want = oracle.forward(q, k, v, la, lam)
+    assert_parity(rs.cpu().numpy(), want, BF16_TOL, f"register-state {case}")
+    assert_parity(lds.cpu().numpy(), want, BF16_TOL, f"lds-state {case}")
+
+
+def test_register_state_kernel_rejects_other_shapes():
+    w = W.FwdWorkload("rs_no", 1, 1, 128, 128, 48, 64, "bf16")
+    dq, dk_, dv_, dla, dlam = to_dev(*W.make_fwd_inputs(w))
+    with pytest.raises(ll.LogLinearError):
+        ll.fwd_ex(dq, dk_, dv_, dla, dlam, C=64, kernel=ll.KERNEL_REGISTER_STATE)
