@@ -45,11 +45,8 @@ def algorithmic_bytes(B, H, T, dk, dv, L, in_bytes=2):
 
 
 def source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("loglinear_fwd.hip", "ll_device.h", "ll_internal.h", "loglinear_api.cpp"):
-        with open(os.path.join(ROOT, "log_linear_attention_attn_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from log_linear_attention_attn_amd.profiling import source_hash as h
+    return h()
 
 
 def load_traffic(workload: str):
@@ -63,6 +60,19 @@ def load_traffic(workload: str):
     if rec.get("source_hash") != source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def calibrate_copy(mib: int):
+    """A plain device-to-device copy of a known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}))
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -104,7 +114,12 @@ def main():
     ap.add_argument("--workload", default="lm_B2H16_T16384_dk128_dv128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-log2", type=int, default=-1)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
@@ -181,7 +196,8 @@ def main():
         "kernels_ms": {"seg_state": seg_ms, "seg_node": node_ms, "fwd_sweep": sweep_ms},
         "wall_ms_per_step": wall / K * 1e3,
         "roofline": {
-            "kernel": "fwd_sweep_kernel",
+            "kernel": "fwd_rs_kernel" if (w.dtype == "bf16" and w.C == 64 and w.dk > 64 and w.dv % 64 == 0
+                                          and -(-w.T // 64) <= 256) else "fwd_sweep_kernel",
             "bound": "hbm",
             "achieved": sweep_gbs,
             "peak": PEAK_HBM_GBS,
