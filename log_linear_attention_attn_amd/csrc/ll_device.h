@@ -13,6 +13,7 @@ typedef __bf16 bf16;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 // Fenwick level of key s seen from query t, s <= t ([P1] 层级判定算法).  The
 // bucket walk peels the low set bits of t; s lands in the bucket cut by the

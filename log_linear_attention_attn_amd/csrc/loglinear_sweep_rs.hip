@@ -14,8 +14,12 @@
 //   phase 2  wave w owns dv columns 16w..16w+15 of the workgroup for all 64
 //            rows: P V, one Q G_b product per live level b, the output, the
 //            chunk state K^T (V*decay) and the lssb merge.  The bucket states
-//            G_b (dk x 16 columns, bf16 hi + lo) never leave the wave's
-//            registers.
+//            G_b (dk x 16 columns) never leave the wave's registers; they are
+//            held in fp16 with a power-of-two scale per (level, wave), and the
+//            Q.G products run as fp16 MFMAs on a scaled fp16 copy of Q
+//            (bf16 values are exact in fp16 once scaled into range).  Error
+//            ~3e-3 of the output RMS with no decay (bf16 hi/lo states in the
+//            LDS-state kernel: ~1e-4).
 // K, Q and V are staged row-major; the operands that contract over tokens are
 // read with the LDS transpose load (ds_read_b64_tr_b16), so no transposed
 // stores are needed.  The next chunk's global loads are issued before the
@@ -37,8 +41,9 @@ constexpr int KS_OFF = QS_OFF + C * LDQ * 2;
 constexpr int VS_OFF = KS_OFF + C * LDQ * 2;
 constexpr int PS_OFF = VS_OFF + C * LDV * 2;
 constexpr int PS_BYTES = 4 /*mi*/ * 2 /*ks*/ * 2 /*hi,lo*/ * 64 * 16;
-constexpr int CL_OFF = PS_OFF + PS_BYTES;  // cl[64], esf[64], ecl[64]
-constexpr int LAM_OFF = CL_OFF + 3 * C * 4;
+constexpr int CL_OFF = PS_OFF + PS_BYTES;  // cl[64], qmax[4] (padded to 64)
+constexpr int QH_OFF = CL_OFF + 2 * C * 4;  // fp16 copy of Q, [64][LDQ]
+constexpr int LAM_OFF = QH_OFF + C * LDQ * 2;
 
 __host__ __device__ inline int lamw_off(int L) { return LAM_OFF + C * L * 4; }
 __host__ __device__ inline int lds_bytes(int L, int nslot) { return lamw_off(L) + (nslot > 0 ? nslot : 1) * C * 4; }
@@ -64,6 +69,27 @@ __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// max over the 64 lanes, returned wave-uniform
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Power-of-two scale exponent e such that mx * 2^-e lies in [2^14, 2^15)
+// (fp16 holds up to 65504); 0 for mx == 0, clamped so 2^+-e stays a normal float.
+__device__ __forceinline__ int scale_exp(float mx) {
+  if (!(mx > 0.f)) return 0;
+  const int e = static_cast<int>((__float_as_uint(mx) >> 23) & 0xff) - 127 - 14;
+  return max(-110, min(110, e));
+}
+
+__device__ __forceinline__ float exp2_int(int e) { return __uint_as_float(static_cast<unsigned>(e + 127) << 23); }
+
 }  // namespace rs
 
 template <int NSLOT>
@@ -76,8 +102,8 @@ fwd_rs_kernel(FwdArgs a) {
   bf16* Vs = reinterpret_cast<bf16*>(smem + VS_OFF);
   bf16x8* Ps = reinterpret_cast<bf16x8*>(smem + PS_OFF);  // [mi][ks][hl][lane]
   float* cl_s = reinterpret_cast<float*>(smem + CL_OFF);
-  float* esf_s = cl_s + C;
-  float* ecl_s = esf_s + C;
+  float* qmax_s = cl_s + C;  // per-wave max |q| of the chunk
+  _Float16* Qh = reinterpret_cast<_Float16*>(smem + QH_OFF);
   float* lam_s = reinterpret_cast<float*>(smem + LAM_OFF);
   float* lamw_s = reinterpret_cast<float*>(smem + lamw_off(a.L));
 
@@ -104,18 +130,18 @@ fwd_rs_kernel(FwdArgs a) {
   const float* __restrict__ lamg = a.lam + bhT * L;
   float* __restrict__ outg = a.out + bhT * dv + dv0 + 16 * w;
 
-  // ---- bucket states of this wave's 16 columns: G[b][ks] holds dk
-  // 32ks + 8*g4 + e (e = 0..7) of column li, split bf16 hi / lo.
-  bf16x8 Gh[NSLOT][NKS], Gl[NSLOT][NKS];
+  // ---- bucket states of this wave's 16 columns.  G[b][ks] holds dk
+  // 32ks + 8*g4 + e (e = 0..7) of column li as fp16 with a per-(level, wave)
+  // power-of-two scale: true value = stored * 2^eg[b].
+  f16x8 G[NSLOT][NKS];
+  int eg[NSLOT];     // wave-uniform scale exponents
   float dec[NSLOT];  // log decay since each bucket state was formed
 #pragma unroll
   for (int b = 0; b < NSLOT; ++b) {
     dec[b] = 0.f;
+    eg[b] = 0;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      Gh[b][ks] = bf16x8{};
-      Gl[b][ks] = bf16x8{};
-    }
+    for (int ks = 0; ks < NKS; ++ks) G[b][ks] = f16x8{};
   }
   // Levels spanning whole segments: bit b >= seg_log2 of n0 <-> bit
   // b - seg_log2 of the segment; its bucket is the node starting at segment
@@ -127,21 +153,25 @@ fwd_rs_kernel(FwdArgs a) {
       const int gc = (seg >> bp) << bp;
       const float* __restrict__ node =
           a.nodes + ((size_t)(bh * a.nseg + gc) * dv + dv0 + 16 * w + li) * DKP + 8 * g4;
+      f32x4 x[2 * NKS];
+      float mx = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(node + 32 * ks);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(node + 32 * ks + 4);
+        x[2 * ks] = *reinterpret_cast<const f32x4*>(node + 32 * ks);
+        x[2 * ks + 1] = *reinterpret_cast<const f32x4*>(node + 32 * ks + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(x[2 * ks][e]), fabsf(x[2 * ks + 1][e])));
+      }
+      const int e2 = scale_exp(wave_max(mx));
+      const float sc = exp2_int(-e2);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          bf16 h, l;
-          split_bf16(x0[e], h, l);
-          Gh[b][ks][e] = h;
-          Gl[b][ks][e] = l;
-          split_bf16(x1[e], h, l);
-          Gh[b][ks][4 + e] = h;
-          Gl[b][ks][4 + e] = l;
+          G[b][ks][e] = static_cast<_Float16>(x[2 * ks][e] * sc);
+          G[b][ks][4 + e] = static_cast<_Float16>(x[2 * ks + 1][e] * sc);
         }
-      }
+      eg[b] = e2;
       float d = 0.f;
       for (int r = gc; r < seg; ++r) d += a.seg_decay[bh * a.nseg + r];
       dec[b] = d;
@@ -154,6 +184,22 @@ fwd_rs_kernel(FwdArgs a) {
   float pla;
   auto prefetch = [&](int n) {
     const int tok0 = n * C;
+    // small loads first: vmcnt counts in order, so a later wait for one of
+    // these does not also wait for the large q / k / v loads
+    {
+      // lambda rows of the chunk: C*L floats, four per thread (scalar loads:
+      // rows of L floats need not be 16-byte aligned)
+      const int v4 = tid * 4;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (v4 < C * L) {
+        const size_t base = (size_t)tok0 * L + v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (tok0 + (v4 + e) / L < T) x[e] = lamg[base + e];
+      }
+      plam = x;
+    }
+    pla = (tok0 + lane < T) ? lag[tok0 + lane] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
@@ -174,20 +220,6 @@ fwd_rs_kernel(FwdArgs a) {
       if (tok < T) x = *reinterpret_cast<const bf16x8*>(vg + (size_t)tok * dv + col);
       pv[i] = x;
     }
-    {
-      // lambda rows of the chunk: C*L floats, four per thread (scalar loads:
-      // rows of L floats need not be 16-byte aligned)
-      const int v4 = tid * 4;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (v4 < C * L) {
-        const size_t base = (size_t)tok0 * L + v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (tok0 + (v4 + e) / L < T) x[e] = lamg[base + e];
-      }
-      plam = x;
-    }
-    pla = (tok0 + lane < T) ? lag[tok0 + lane] : 0.f;
   };
 
   prefetch(n0);
@@ -195,11 +227,19 @@ fwd_rs_kernel(FwdArgs a) {
   for (int n = n0; n < n1; ++n) {
     const int tok0 = n * C;
     // ---------------- stage: registers -> LDS ------------------------------
+    unsigned qm = 0;  // max |q| of this thread's values, as bf16 magnitude bits
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
       *reinterpret_cast<bf16x8*>(Qs + row * LDQ + col) = pq[i];
       *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
+      const uint4 bits = __builtin_bit_cast(uint4, pq[i]);
+      qm = max(qm, max(max(bits.x & 0x7fffu, bits.x >> 16 & 0x7fffu), max(bits.y & 0x7fffu, bits.y >> 16 & 0x7fffu)));
+      qm = max(qm, max(max(bits.z & 0x7fffu, bits.z >> 16 & 0x7fffu), max(bits.w & 0x7fffu, bits.w >> 16 & 0x7fffu)));
+    }
+    {
+      const float qmw = wave_max(__uint_as_float(qm << 16));
+      if (lane == 0) qmax_s[w] = qmw;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -207,7 +247,7 @@ fwd_rs_kernel(FwdArgs a) {
       *reinterpret_cast<bf16x8*>(Vs + row * LDV + col) = pv[i];
     }
     if (tid * 4 < C * L) *reinterpret_cast<f32x4*>(lam_s + tid * 4) = plam;
-    // in-chunk decay sums (each wave computes them; wave 0 publishes)
+    // in-chunk decay sums (each wave computes them; wave 0 publishes cl)
     float cl = pla;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -224,61 +264,88 @@ fwd_rs_kernel(FwdArgs a) {
       const float y = __shfl_down(sf, off);
       if (lane + off < 64) sf += y;
     }
-    if (w == 0) {
-      cl_s[lane] = cl;
-      esf_s[lane] = __expf(sf);
-      ecl_s[lane] = __expf(cl);
-    }
+    const float esf = __expf(sf);  // lane = token
+    if (w == 0) cl_s[lane] = cl;
     __syncthreads();
+
+    // fp16 copy of Q for the Q.G products, scaled by a power of two so the
+    // chunk's max |q| sits at 2^14..2^15 (exact for bf16 values in range)
+    const int eq = scale_exp(fmaxf(fmaxf(qmax_s[0], qmax_s[1]), fmaxf(qmax_s[2], qmax_s[3])));
+    {
+      const float sc = exp2_int(-eq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(static_cast<float>(pq[i][e]) * sc);
+        *reinterpret_cast<f16x8*>(Qh + row * LDQ + col) = h;
+      }
+    }
 
     if (n + 1 < n1) prefetch(n + 1);
 
     // ---------------- phase 1: masked score tiles -> LDS -------------------
     // tile table: wave 0 (0,0)(3,0); wave 1 (1,0)(1,1)(3,1); wave 2 (2,0)(2,1)(2,2);
     // wave 3 (3,3)(3,2).  Slots above the diagonal inside the last K-step of
-    // an even query block, (0,1) and (2,3), are written as zeros.
+    // an even query block, (0,1) and (2,3), are written as zeros.  The tiles
+    // of a wave are accumulated side by side so consecutive MFMAs are
+    // independent.
     {
       const int ntile = (w == 0 || w == 3) ? 2 : 3;
-      for (int it = 0; it < ntile; ++it) {
-        int qb, kb;
-        if (w == 0) { qb = it ? 3 : 0; kb = 0; }
-        else if (w == 1) { qb = it == 2 ? 3 : 1; kb = it == 2 ? 1 : it; }
-        else if (w == 2) { qb = 2; kb = it; }
-        else { qb = 3; kb = it ? 2 : 3; }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      int qbt[3], kbt[3];
+      if (w == 0) { qbt[0] = 0; kbt[0] = 0; qbt[1] = 3; kbt[1] = 0; qbt[2] = 0; kbt[2] = 0; }
+      else if (w == 1) { qbt[0] = 1; kbt[0] = 0; qbt[1] = 1; kbt[1] = 1; qbt[2] = 3; kbt[2] = 1; }
+      else if (w == 2) { qbt[0] = 2; kbt[0] = 0; qbt[1] = 2; kbt[1] = 1; qbt[2] = 2; kbt[2] = 2; }
+      else { qbt[0] = 3; kbt[0] = 3; qbt[1] = 3; kbt[1] = 2; qbt[2] = 3; kbt[2] = 3; }
+      f32x4 acc[3];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + li) * LDQ + 32 * ks + 8 * g4);
-          const bf16x8 qb8 = *reinterpret_cast<const bf16x8*>(Qs + (16 * qb + li) * LDQ + 32 * ks + 8 * g4);
-          acc = mma(ka, qb8, acc);
-        }
-        // acc[r] = score(query 16qb+li, key 16kb+4g4+r)
-        const int qi = 16 * qb + li;
-        const float clq = cl_s[qi];
-        const f32x4 clk = *reinterpret_cast<const f32x4*>(cl_s + 16 * kb + 4 * g4);
-        f32x4 pv4;
-        if (kb < qb) {
-          const float lam = lam_s[qi * L + 4 + (32 - __clz(qb ^ kb))];
+      for (int it = 0; it < 3; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) pv4[r] = acc[r] * lam * __expf(clq - clk[r]);
-        } else {
+      for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kj = 16 * kb + 4 * g4 + r;
-            pv4[r] = kj <= qi ? acc[r] * lam_s[qi * L + level_of(qi, kj)] * __expf(clq - clk[r]) : 0.f;
+        for (int it = 0; it < 3; ++it) {
+          if (it < ntile) {
+            const bf16x8 ka =
+                *reinterpret_cast<const bf16x8*>(Ks + (16 * kbt[it] + li) * LDQ + 32 * ks + 8 * g4);
+            const bf16x8 qb8 =
+                *reinterpret_cast<const bf16x8*>(Qs + (16 * qbt[it] + li) * LDQ + 32 * ks + 8 * g4);
+            acc[it] = mma(ka, qb8, acc[it]);
           }
         }
-        bf16x4 h, l;
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bf16 hh, ll;
-          split_bf16(pv4[r], hh, ll);
-          h[r] = hh;
-          l[r] = ll;
+      for (int it = 0; it < 3; ++it) {
+        if (it < ntile) {
+          const int qb = qbt[it], kb = kbt[it];
+          // acc[r] = score(query 16qb+li, key 16kb+4g4+r)
+          const int qi = 16 * qb + li;
+          const float clq = cl_s[qi];
+          const f32x4 clk = *reinterpret_cast<const f32x4*>(cl_s + 16 * kb + 4 * g4);
+          f32x4 pv4;
+          if (kb < qb) {
+            const float lam = lam_s[qi * L + 4 + (32 - __clz(qb ^ kb))];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv4[r] = acc[it][r] * lam * __expf(clq - clk[r]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int kj = 16 * kb + 4 * g4 + r;
+              pv4[r] = kj <= qi ? acc[it][r] * lam_s[qi * L + level_of(qi, kj)] * __expf(clq - clk[r]) : 0.f;
+            }
+          }
+          bf16x4 h, l;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bf16 hh, ll;
+            split_bf16(pv4[r], hh, ll);
+            h[r] = hh;
+            l[r] = ll;
+          }
+          bf16* dst = reinterpret_cast<bf16*>(Ps + ((qb * 2 + (kb >> 1)) * 2) * 64 + lane) + 4 * (kb & 1);
+          *reinterpret_cast<bf16x4*>(dst) = h;
+          *reinterpret_cast<bf16x4*>(dst + 64 * 8) = l;
         }
-        bf16* dst = reinterpret_cast<bf16*>(Ps + ((qb * 2 + (kb >> 1)) * 2) * 64 + lane) + 4 * (kb & 1);
-        *reinterpret_cast<bf16x4*>(dst) = h;
-        *reinterpret_cast<bf16x4*>(dst + 64 * 8) = l;
       }
       if (w == 0 || w == 3) {
         const int qb = w == 0 ? 0 : 2;  // zero slot (qb, qb+1)
@@ -286,10 +353,14 @@ fwd_rs_kernel(FwdArgs a) {
         *reinterpret_cast<bf16x4*>(dst) = bf16x4{};
         *reinterpret_cast<bf16x4*>(dst + 64 * 8) = bf16x4{};
       }
-      // lambda of each inter-chunk level times exp(cl), for the Q.G weights
-      for (int idx = tid; idx < a.nslot * C; idx += NT) {
-        const int b = idx >> 6, row = idx & 63;
-        lamw_s[idx] = lam_s[row * L + LOGC + 1 + b] * ecl_s[row];
+      // Q.G row weights of each inter-chunk level b for this chunk:
+      // lambda[row, log2C+1+b] * exp(cl_row + dec_b) (decay from the bucket's
+      // end to the row) * 2^eq (the fp16 Q scale); wave 0, lane = row.
+      if (w == 0) {
+        const float sq = exp2_int(eq);
+#pragma unroll
+        for (int b = 0; b < NSLOT; ++b)
+          if (b < a.nslot) lamw_s[b * C + lane] = lam_s[lane * L + LOGC + 1 + b] * __expf(cl + dec[b]) * sq;
       }
     }
     __syncthreads();
@@ -303,39 +374,45 @@ fwd_rs_kernel(FwdArgs a) {
     // tile layout (32ks + 4g4 + e, then +16).
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int j = li;  // lane within its 16-lane group addresses row (j >> 2), col quad (j & 3)
-      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (j >> 2)) * LDV + c0 + 4 * (j & 3);
+      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
       const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
+      bf16x8 ph[4], pl[4];
 #pragma unroll
       for (int mi = 2 * ks; mi < 4; ++mi) {
-        const bf16x8 ph = Ps[((mi * 2 + ks) * 2 + 0) * 64 + lane];
-        const bf16x8 pl = Ps[((mi * 2 + ks) * 2 + 1) * 64 + lane];
-        O[mi] = mma(ph, vb, O[mi]);
-        O[mi] = mma(pl, vb, O[mi]);
+        ph[mi] = Ps[((mi * 2 + ks) * 2 + 0) * 64 + lane];
+        pl[mi] = Ps[((mi * 2 + ks) * 2 + 1) * 64 + lane];
       }
+#pragma unroll
+      for (int mi = 2 * ks; mi < 4; ++mi) O[mi] = mma(ph[mi], vb, O[mi]);
+#pragma unroll
+      for (int mi = 2 * ks; mi < 4; ++mi) O[mi] = mma(pl[mi], vb, O[mi]);
     }
-    // O += sum over live levels b of diag(lambda * decay) (Q G_b)
-    float edec[NSLOT];
+    // O += sum over live levels b of diag(weight_b) (Q G_b), fp16 MFMAs; the
+    // fp16 Q fragments of all four row tiles stay in registers for every level.
+    {
+      f16x8 qa[4][NKS];
 #pragma unroll
-    for (int b = 0; b < NSLOT; ++b) edec[b] = __expf(dec[b]);
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      bf16x8 qa[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        qa[ks] = *reinterpret_cast<const bf16x8*>(Qs + (16 * mi + li) * LDQ + 32 * ks + 8 * g4);
+        for (int ks = 0; ks < NKS; ++ks)
+          qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 32 * ks + 8 * g4);
 #pragma unroll
       for (int b = 0; b < NSLOT; ++b) {
         if ((n >> b) & 1) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          f32x4 acc[4];
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            acc = mma(qa[ks], Gh[b][ks], acc);
-            acc = mma(qa[ks], Gl[b][ks], acc);
+          for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
+          const float sg = exp2_int(eg[b]);
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) {
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(lamw_s + b * C + 16 * mi + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[mi][r] += (wv[r] * sg) * acc[mi][r];
           }
-          const f32x4 wv = *reinterpret_cast<const f32x4*>(lamw_s + b * C + 16 * mi + 4 * g4);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[mi][r] += wv[r] * edec[b] * acc[r];
         }
       }
     }
@@ -355,64 +432,71 @@ fwd_rs_kernel(FwdArgs a) {
       bf16x8 vh[2], vl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int j = li;
-        const bf16* v0 = Vs + (32 * ks + 8 * g4 + (j >> 2)) * LDV + c0 + 4 * (j & 3);
+        const bf16* v0 = Vs + (32 * ks + 8 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
         const bf16x8 x = cat(tr_read(v0), tr_read(v0 + 4 * LDV));
-        const f32x4 e0 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4 + 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           bf16 hh, ll;
-          split_bf16(static_cast<float>(x[e]) * (e < 4 ? e0[e] : e1[e - 4]), hh, ll);
+          split_bf16(static_cast<float>(x[e]) * __shfl(esf, 32 * ks + 8 * g4 + e), hh, ll);
           vh[ks][e] = hh;
           vl[ks][e] = ll;
         }
       }
-      // S tiles, one at a time: t = 2*kq + half covers dk
-      // 32kq + 8*(row>>2) + 4*half + (row&3); lower levels (decayed to the end
-      // of chunk n) are summed first, the chunk's K^T (V*decay) is accumulated
-      // onto them, and the result becomes the level-m bucket state.
+      // S tiles t = 2*kq + half cover dk 32kq + 8*(row>>2) + 4*half + (row&3);
+      // S[t][r] is dk 32kq + 8*g4 + 4*half + r of column li, i.e. element
+      // 4*half + r of G[.][kq].  Lower levels, decayed to the end of chunk n,
+      // are added first; hi / lo halves of V accumulate separately.
       float fl[NSLOT];
 #pragma unroll
-      for (int b = 0; b < NSLOT; ++b) fl[b] = b < m ? __expf(dec[b] + Atot) : 0.f;
+      for (int b = 0; b < NSLOT; ++b) fl[b] = b < m ? __expf(dec[b] + Atot) * exp2_int(eg[b]) : 0.f;
+      f32x4 Sh[2 * NKS], Sl[2 * NKS];
 #pragma unroll
       for (int t = 0; t < 2 * NKS; ++t) {
         const int kq = t >> 1, half = t & 1;
-        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+        Sh[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Sl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < NSLOT; ++b) {
           if (b < m) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              S[r] += fl[b] * (static_cast<float>(Gh[b][kq][4 * half + r]) +
-                               static_cast<float>(Gl[b][kq][4 * half + r]));
-          }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int j = li;
-          const bf16* k0 = Ks + (32 * ks + 8 * g4 + (j >> 2)) * LDQ + 32 * kq + 8 * (j & 3) + 4 * half;
-          const bf16x8 ka = cat(tr_read(k0), tr_read(k0 + 4 * LDQ));
-          S = mma(ka, vh[ks], S);
-          S = mma(ka, vl[ks], S);
-        }
-#pragma unroll
-        for (int b = 0; b < NSLOT; ++b) {
-          if (b == m) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              bf16 hh, ll;
-              split_bf16(S[r], hh, ll);
-              Gh[b][kq][4 * half + r] = hh;
-              Gl[b][kq][4 * half + r] = ll;
-            }
+            for (int r = 0; r < 4; ++r) Sh[t][r] += fl[b] * static_cast<float>(G[b][kq][4 * half + r]);
           }
         }
       }
 #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int t = 0; t < 2 * NKS; ++t) {
+          const int kq = t >> 1, half = t & 1;
+          const bf16* k0 = Ks + (32 * ks + 8 * g4 + (li >> 2)) * LDQ + 32 * kq + 8 * (li & 3) + 4 * half;
+          const bf16x8 ka = cat(tr_read(k0), tr_read(k0 + 4 * LDQ));
+          Sh[t] = mma(ka, vh[ks], Sh[t]);
+          Sl[t] = mma(ka, vl[ks], Sl[t]);
+        }
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2 * NKS; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Sh[t][r] += Sl[t][r];
+          mx = fmaxf(mx, fabsf(Sh[t][r]));
+        }
+      const int em = scale_exp(wave_max(mx));
+      const float sc = exp2_int(-em);
+#pragma unroll
       for (int b = 0; b < NSLOT; ++b) {
-        if (b == m) dec[b] = 0.f;
-        else if (b > m) dec[b] += Atot;
+        if (b == m) {
+#pragma unroll
+          for (int t = 0; t < 2 * NKS; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              G[b][t >> 1][4 * (t & 1) + r] = static_cast<_Float16>(Sh[t][r] * sc);
+          eg[b] = em;
+          dec[b] = 0.f;
+        } else if (b > m) {
+          dec[b] += Atot;
+        }
       }
     }
     __syncthreads();
