@@ -7,24 +7,29 @@
 //
 //   [P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制"
 //
-// Work split of one 256-thread workgroup = (b,h, segment, 64 dv columns):
+// Work split of one 512-thread workgroup = (b,h, segment, 64 dv columns),
+// eight waves, two per SIMD:
 //   phase 1  the 10 causal 16x16 score tiles of the chunk are shared out over
-//            the 4 waves; each masked tile P (Fenwick level x decay x lambda)
+//            the waves; each masked tile P (Fenwick level x decay x lambda)
 //            is split bf16 hi/lo and parked in LDS in MFMA A-operand order.
-//   phase 2  wave w owns dv columns 16w..16w+15 of the workgroup for all 64
-//            rows: P V, one Q G_b product per live level b, the output, the
-//            chunk state K^T (V*decay) and the lssb merge.  The bucket states
-//            G_b (dk x 16 columns) never leave the wave's registers; they are
-//            held in fp16 with a power-of-two scale per (level, wave), and the
-//            Q.G products run as fp16 MFMAs on a scaled fp16 copy of Q
-//            (bf16 values are exact in fp16 once scaled into range).  Error
-//            ~3e-3 of the output RMS with no decay (bf16 hi/lo states in the
-//            LDS-state kernel: ~1e-4).
+//   phase 2  wave w owns dv columns 16(w&3)..+15 and dk half w>>2: the
+//            partial Q G_b products of its dk half for all 64 rows, P V for
+//            two of the four 16-row tiles, the chunk state K^T (V*decay) of
+//            its dk half and the lssb merge.  The two dk halves of a column
+//            slice add their partial outputs through LDS.  The bucket states
+//            G_b (64 dk x 16 columns per wave) never leave the registers;
+//            they are held in fp16 with a power-of-two scale per (level,
+//            wave), and the Q.G products run as fp16 MFMAs on a scaled fp16
+//            copy of Q (bf16 values are exact in fp16 once scaled into
+//            range).  Error ~3e-3 of the output RMS with no decay (bf16 hi/lo
+//            states in the LDS-state kernel: ~1e-4).
 // K, Q and V are staged row-major; the operands that contract over tokens are
 // read with the LDS transpose load (ds_read_b64_tr_b16), so no transposed
 // stores are needed.  The next chunk's global loads are issued before the
 // current chunk's math (register prefetch).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "ll_device.h"
 #include "ll_internal.h"
@@ -33,7 +38,8 @@ namespace ll {
 
 namespace rs {
 
-constexpr int C = 64, DKP = 128, NKS = DKP / 32, LOGC = 6, NT = 256;
+constexpr int C = 64, DKP = 128, NKS = DKP / 32, LOGC = 6;
+constexpr int NT = 256;  // threads of the segment-state kernel
 constexpr int LDQ = DKP + 8;  // Qs, Ks row stride (bf16)
 constexpr int LDV = 64 + 8;   // Vs row stride (bf16): 64 dv columns
 constexpr int QS_OFF = 0;
@@ -41,8 +47,10 @@ constexpr int KS_OFF = QS_OFF + C * LDQ * 2;
 constexpr int VS_OFF = KS_OFF + C * LDQ * 2;
 constexpr int PS_OFF = VS_OFF + C * LDV * 2;
 constexpr int PS_BYTES = 4 /*mi*/ * 2 /*ks*/ * 2 /*hi,lo*/ * 64 * 16;
-constexpr int CL_OFF = PS_OFF + PS_BYTES;  // cl[64], qmax[4] (padded to 64)
-constexpr int QH_OFF = CL_OFF + 2 * C * 4;  // fp16 copy of Q, [64][LDQ]
+constexpr int XC_OFF = PS_OFF + PS_BYTES;  // partial-output exchange [8 waves][2][64 lanes] f32x4
+constexpr int XC_BYTES = 8 * 2 * 64 * 16;
+constexpr int CL_OFF = XC_OFF + XC_BYTES;  // cl[64], esf[64], qmax[8] (padded to 64)
+constexpr int QH_OFF = CL_OFF + 3 * C * 4;  // fp16 copy of Q, [64][LDQ]
 constexpr int LAM_OFF = QH_OFF + C * LDQ * 2;
 
 __host__ __device__ inline int lamw_off(int L) { return LAM_OFF + C * L * 4; }
@@ -90,20 +98,40 @@ __device__ __forceinline__ int scale_exp(float mx) {
 
 __device__ __forceinline__ float exp2_int(int e) { return __uint_as_float(static_cast<unsigned>(e + 127) << 23); }
 
+// Raw buffer resource over [base, base + bytes): loads beyond the range return
+// zero and stores beyond it are dropped, so ragged tails need no branches and
+// the addresses stay 32-bit offsets from a wave-uniform base.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past every range used here
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ bf16x8 load_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 }  // namespace rs
 
+// Eight waves per workgroup (two per SIMD): wave w owns dv columns
+// 16*(w&3)..+15 of the workgroup's 64 and dk half h = w>>2 of the bucket
+// states.  The two dk halves of a column slice add their partial Q.G sums
+// through LDS; each wave finishes the output of two row tiles.
 template <int NSLOT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 fwd_rs_kernel(FwdArgs a) {
   using namespace rs;
+  constexpr int NTH = 512;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* Qs = reinterpret_cast<bf16*>(smem + QS_OFF);
   bf16* Ks = reinterpret_cast<bf16*>(smem + KS_OFF);
+  _Float16* Qh = reinterpret_cast<_Float16*>(smem + QH_OFF);
   bf16* Vs = reinterpret_cast<bf16*>(smem + VS_OFF);
   bf16x8* Ps = reinterpret_cast<bf16x8*>(smem + PS_OFF);  // [mi][ks][hl][lane]
+  f32x4* Xc = reinterpret_cast<f32x4*>(smem + XC_OFF);    // [wave][2][lane]
   float* cl_s = reinterpret_cast<float*>(smem + CL_OFF);
-  float* qmax_s = cl_s + C;  // per-wave max |q| of the chunk
-  _Float16* Qh = reinterpret_cast<_Float16*>(smem + QH_OFF);
+  float* esf_s = cl_s + C;
+  float* qmax_s = esf_s + C;  // per-wave max |q| of the chunk
   float* lam_s = reinterpret_cast<float*>(smem + LAM_OFF);
   float* lamw_s = reinterpret_cast<float*>(smem + lamw_off(a.L));
 
@@ -117,31 +145,37 @@ fwd_rs_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, g4 = lane >> 4;
+  const int cs = w & 3, hh = w >> 2;  // column slice, dk half
+  const int c0 = 16 * cs;
   const int T = a.T, L = a.L, dk = a.dk, dv = a.dv;
   const int N = (T + C - 1) / C;
   const int n0 = seg << a.seg_log2;
   const int n1 = min(N, n0 + (1 << a.seg_log2));
   const int dv0 = dg * 64;
   const size_t bhT = (size_t)bh * T;
-  const bf16* __restrict__ qg = static_cast<const bf16*>(a.q) + bhT * dk;
-  const bf16* __restrict__ kg = static_cast<const bf16*>(a.k) + bhT * dk;
-  const bf16* __restrict__ vg = static_cast<const bf16*>(a.v) + bhT * dv + dv0;
-  const float* __restrict__ lag = a.log_a + bhT;
-  const float* __restrict__ lamg = a.lam + bhT * L;
-  float* __restrict__ outg = a.out + bhT * dv + dv0 + 16 * w;
+  // per-(b,h) slices; every slice is < 2^31 bytes (checked by the launcher)
+  const rsrc_t qr = make_rsrc(static_cast<const bf16*>(a.q) + bhT * dk, T * dk * 2);
+  const rsrc_t kr = make_rsrc(static_cast<const bf16*>(a.k) + bhT * dk, T * dk * 2);
+  const rsrc_t vr = make_rsrc(static_cast<const bf16*>(a.v) + bhT * dv, T * dv * 2);
+  const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
+  const rsrc_t lamr = make_rsrc(a.lam + bhT * L, T * L * 4);
+  const rsrc_t outr = make_rsrc(a.out + bhT * dv, T * dv * 4);
+  // row tiles whose output this wave finishes, and the two it hands over
+  const int own0 = hh ? 1 : 0, own1 = hh ? 2 : 3;
+  const int oth0 = hh ? 0 : 1, oth1 = hh ? 3 : 2;
 
-  // ---- bucket states of this wave's 16 columns.  G[b][ks] holds dk
-  // 32ks + 8*g4 + e (e = 0..7) of column li as fp16 with a per-(level, wave)
-  // power-of-two scale: true value = stored * 2^eg[b].
-  f16x8 G[NSLOT][NKS];
-  int eg[NSLOT];     // wave-uniform scale exponents
+  // ---- bucket states: G[b][ks] holds dk 64*hh + 32ks + 8*g4 + e (e = 0..7)
+  // of column c0 + li, fp16 with a per-(level, wave) power-of-two scale:
+  // true value = stored * 2^eg[b].
+  f16x8 G[NSLOT][2];
+  int eg[NSLOT];
   float dec[NSLOT];  // log decay since each bucket state was formed
 #pragma unroll
   for (int b = 0; b < NSLOT; ++b) {
     dec[b] = 0.f;
     eg[b] = 0;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) G[b][ks] = f16x8{};
+    G[b][0] = f16x8{};
+    G[b][1] = f16x8{};
   }
   // Levels spanning whole segments: bit b >= seg_log2 of n0 <-> bit
   // b - seg_log2 of the segment; its bucket is the node starting at segment
@@ -152,11 +186,11 @@ fwd_rs_kernel(FwdArgs a) {
       const int bp = b - a.seg_log2;
       const int gc = (seg >> bp) << bp;
       const float* __restrict__ node =
-          a.nodes + ((size_t)(bh * a.nseg + gc) * dv + dv0 + 16 * w + li) * DKP + 8 * g4;
-      f32x4 x[2 * NKS];
+          a.nodes + ((size_t)(bh * a.nseg + gc) * dv + dv0 + c0 + li) * DKP + 64 * hh + 8 * g4;
+      f32x4 x[4];
       float mx = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
         x[2 * ks] = *reinterpret_cast<const f32x4*>(node + 32 * ks);
         x[2 * ks + 1] = *reinterpret_cast<const f32x4*>(node + 32 * ks + 4);
 #pragma unroll
@@ -165,7 +199,7 @@ fwd_rs_kernel(FwdArgs a) {
       const int e2 = scale_exp(wave_max(mx));
       const float sc = exp2_int(-e2);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           G[b][ks][e] = static_cast<_Float16>(x[2 * ks][e] * sc);
@@ -179,47 +213,29 @@ fwd_rs_kernel(FwdArgs a) {
   }
 
   // ---- register prefetch of one chunk ----------------------------------
-  bf16x8 pq[4], pk[4], pv[2];
-  f32x4 plam;
+  bf16x8 pq[2], pk[2], pv;
+  float plam[2];
   float pla;
   auto prefetch = [&](int n) {
     const int tok0 = n * C;
     // small loads first: vmcnt counts in order, so a later wait for one of
-    // these does not also wait for the large q / k / v loads
+    // these does not also wait for the large q / k / v loads.  Lambda words
+    // past C * L belong to the next chunk and are not staged.
     {
-      // lambda rows of the chunk: C*L floats, four per thread (scalar loads:
-      // rows of L floats need not be 16-byte aligned)
-      const int v4 = tid * 4;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (v4 < C * L) {
-        const size_t base = (size_t)tok0 * L + v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (tok0 + (v4 + e) / L < T) x[e] = lamg[base + e];
-      }
-      plam = x;
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(lamr, (tok0 * L + 2 * tid) * 4, 0, 0);
+      plam[0] = __uint_as_float(x[0]);
+      plam[1] = __uint_as_float(x[1]);
     }
-    pla = (tok0 + lane < T) ? lag[tok0 + lane] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
-      const int tok = tok0 + row;
-      bf16x8 x = {}, y = {};
-      if (tok < T && col < dk) {
-        x = *reinterpret_cast<const bf16x8*>(qg + (size_t)tok * dk + col);
-        y = *reinterpret_cast<const bf16x8*>(kg + (size_t)tok * dk + col);
-      }
-      pq[i] = x;
-      pk[i] = y;
-    }
+    pla = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lar, (tok0 + lane) * 4, 0, 0));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int v = tid + NT * i, row = v >> 3, col = (v & 7) * 8;
-      const int tok = tok0 + row;
-      bf16x8 x = {};
-      if (tok < T) x = *reinterpret_cast<const bf16x8*>(vg + (size_t)tok * dv + col);
-      pv[i] = x;
+      const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
+      // columns past dk (padded head dim) read zero: out-of-range offset, no branch
+      const uint32_t off = static_cast<uint32_t>(((tok0 + row) * dk + col) * 2) | ((static_cast<uint32_t>(dk - 1 - col) >> 31) << 31);
+      pq[i] = load_b128(qr, off);
+      pk[i] = load_b128(kr, off);
     }
+    pv = load_b128(vr, ((tok0 + (tid >> 3)) * dv + dv0 + (tid & 7) * 8) * 2);
   };
 
   prefetch(n0);
@@ -229,8 +245,8 @@ fwd_rs_kernel(FwdArgs a) {
     // ---------------- stage: registers -> LDS ------------------------------
     unsigned qm = 0;  // max |q| of this thread's values, as bf16 magnitude bits
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
       *reinterpret_cast<bf16x8*>(Qs + row * LDQ + col) = pq[i];
       *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
       const uint4 bits = __builtin_bit_cast(uint4, pq[i]);
@@ -241,70 +257,77 @@ fwd_rs_kernel(FwdArgs a) {
       const float qmw = wave_max(__uint_as_float(qm << 16));
       if (lane == 0) qmax_s[w] = qmw;
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = tid + NT * i, row = v >> 3, col = (v & 7) * 8;
-      *reinterpret_cast<bf16x8*>(Vs + row * LDV + col) = pv[i];
+    *reinterpret_cast<bf16x8*>(Vs + (tid >> 3) * LDV + (tid & 7) * 8) = pv;
+    if (tid * 2 < C * L) {  // C * L is even
+      lam_s[tid * 2] = plam[0];
+      lam_s[tid * 2 + 1] = plam[1];
     }
-    if (tid * 4 < C * L) *reinterpret_cast<f32x4*>(lam_s + tid * 4) = plam;
-    // in-chunk decay sums (each wave computes them; wave 0 publishes cl)
-    float cl = pla;
+    float cl = 0.f;
+    if (w == 0) {
+      // in-chunk decay sums: cl = inclusive prefix of log_a, sf = decay from
+      // the token to the chunk's last token (summed directly)
+      cl = pla;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(cl, off);
-      if (lane >= off) cl += y;
-    }
-    // chunk total, made wave-uniform so the per-level decays live in SGPRs
-    const float Atot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__shfl(cl, 63))));
-    // decay from token lane to the chunk's last token, summed directly
-    float sf = __shfl_down(pla, 1);
-    if (lane == 63) sf = 0.f;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(cl, off);
+        if (lane >= off) cl += y;
+      }
+      float sf = __shfl_down(pla, 1);
+      if (lane == 63) sf = 0.f;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_down(sf, off);
-      if (lane + off < 64) sf += y;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_down(sf, off);
+        if (lane + off < 64) sf += y;
+      }
+      cl_s[lane] = cl;
+      esf_s[lane] = __expf(sf);
     }
-    const float esf = __expf(sf);  // lane = token
-    if (w == 0) cl_s[lane] = cl;
     __syncthreads();
 
+    const float Atot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cl_s[C - 1])));
     // fp16 copy of Q for the Q.G products, scaled by a power of two so the
     // chunk's max |q| sits at 2^14..2^15 (exact for bf16 values in range)
-    const int eq = scale_exp(fmaxf(fmaxf(qmax_s[0], qmax_s[1]), fmaxf(qmax_s[2], qmax_s[3])));
+    int eq;
     {
+      float qmx = qmax_s[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) qmx = fmaxf(qmx, qmax_s[i]);
+      eq = scale_exp(qmx);
       const float sc = exp2_int(-eq);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
-        f16x8 h;
+      for (int i = 0; i < 2; ++i) {
+        const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
+        f16x8 hq;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(static_cast<float>(pq[i][e]) * sc);
-        *reinterpret_cast<f16x8*>(Qh + row * LDQ + col) = h;
+        for (int e = 0; e < 8; ++e) hq[e] = static_cast<_Float16>(static_cast<float>(pq[i][e]) * sc);
+        *reinterpret_cast<f16x8*>(Qh + row * LDQ + col) = hq;
       }
     }
 
     if (n + 1 < n1) prefetch(n + 1);
 
     // ---------------- phase 1: masked score tiles -> LDS -------------------
-    // tile table: wave 0 (0,0)(3,0); wave 1 (1,0)(1,1)(3,1); wave 2 (2,0)(2,1)(2,2);
-    // wave 3 (3,3)(3,2).  Slots above the diagonal inside the last K-step of
-    // an even query block, (0,1) and (2,3), are written as zeros.  The tiles
-    // of a wave are accumulated side by side so consecutive MFMAs are
-    // independent.
+    // Waves 0..3 take the diagonal tile (w,w); waves 4..7 take (1,0) (2,0)
+    // (2,1) (3,0); waves 0 and 1 also take (3,1) and (3,2).  Waves 2 and 3
+    // zero the slots above the diagonal inside the last K-step of an even
+    // query block, (0,1) and (2,3).
     {
-      const int ntile = (w == 0 || w == 3) ? 2 : 3;
-      int qbt[3], kbt[3];
-      if (w == 0) { qbt[0] = 0; kbt[0] = 0; qbt[1] = 3; kbt[1] = 0; qbt[2] = 0; kbt[2] = 0; }
-      else if (w == 1) { qbt[0] = 1; kbt[0] = 0; qbt[1] = 1; kbt[1] = 1; qbt[2] = 3; kbt[2] = 1; }
-      else if (w == 2) { qbt[0] = 2; kbt[0] = 0; qbt[1] = 2; kbt[1] = 1; qbt[2] = 2; kbt[2] = 2; }
-      else { qbt[0] = 3; kbt[0] = 3; qbt[1] = 3; kbt[1] = 2; qbt[2] = 3; kbt[2] = 3; }
-      f32x4 acc[3];
+      const int ntile = w < 2 ? 2 : 1;
+      int qbt[2], kbt[2];
+      if (w < 4) { qbt[0] = w; kbt[0] = w; }
+      else if (w == 4) { qbt[0] = 1; kbt[0] = 0; }
+      else if (w == 5) { qbt[0] = 2; kbt[0] = 0; }
+      else if (w == 6) { qbt[0] = 2; kbt[0] = 1; }
+      else { qbt[0] = 3; kbt[0] = 0; }
+      qbt[1] = 3;
+      kbt[1] = w == 0 ? 1 : 2;
+      f32x4 acc[2];
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int it = 0; it < 3; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int it = 0; it < 3; ++it) {
+        for (int it = 0; it < 2; ++it) {
           if (it < ntile) {
             const bf16x8 ka =
                 *reinterpret_cast<const bf16x8*>(Ks + (16 * kbt[it] + li) * LDQ + 32 * ks + 8 * g4);
@@ -315,7 +338,7 @@ fwd_rs_kernel(FwdArgs a) {
         }
       }
 #pragma unroll
-      for (int it = 0; it < 3; ++it) {
+      for (int it = 0; it < 2; ++it) {
         if (it < ntile) {
           const int qb = qbt[it], kb = kbt[it];
           // acc[r] = score(query 16qb+li, key 16kb+4g4+r)
@@ -337,18 +360,18 @@ fwd_rs_kernel(FwdArgs a) {
           bf16x4 h, l;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            bf16 hh, ll;
-            split_bf16(pv4[r], hh, ll);
-            h[r] = hh;
-            l[r] = ll;
+            bf16 x1, x2;
+            split_bf16(pv4[r], x1, x2);
+            h[r] = x1;
+            l[r] = x2;
           }
           bf16* dst = reinterpret_cast<bf16*>(Ps + ((qb * 2 + (kb >> 1)) * 2) * 64 + lane) + 4 * (kb & 1);
           *reinterpret_cast<bf16x4*>(dst) = h;
           *reinterpret_cast<bf16x4*>(dst + 64 * 8) = l;
         }
       }
-      if (w == 0 || w == 3) {
-        const int qb = w == 0 ? 0 : 2;  // zero slot (qb, qb+1)
+      if (w == 2 || w == 3) {
+        const int qb = w == 2 ? 0 : 2;  // zero slot (qb, qb+1)
         bf16* dst = reinterpret_cast<bf16*>(Ps + ((qb * 2 + (qb >> 1)) * 2) * 64 + lane) + 4;
         *reinterpret_cast<bf16x4*>(dst) = bf16x4{};
         *reinterpret_cast<bf16x4*>(dst + 64 * 8) = bf16x4{};
@@ -365,37 +388,18 @@ fwd_rs_kernel(FwdArgs a) {
     }
     __syncthreads();
 
-    // ---------------- phase 2: this wave's 16 dv columns -------------------
-    const int c0 = 16 * w;
-    f32x4 O[4];
+    // ---------------- phase 2 ----------------------------------------------
+    // Q.G over this wave's dk half for all four row tiles (fp16 MFMAs).
+    f32x4 Op[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) O[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // O = P V: V operand by transposed reads, keys in the order of the score
-    // tile layout (32ks + 4g4 + e, then +16).
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
-      const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
-      bf16x8 ph[4], pl[4];
-#pragma unroll
-      for (int mi = 2 * ks; mi < 4; ++mi) {
-        ph[mi] = Ps[((mi * 2 + ks) * 2 + 0) * 64 + lane];
-        pl[mi] = Ps[((mi * 2 + ks) * 2 + 1) * 64 + lane];
-      }
-#pragma unroll
-      for (int mi = 2 * ks; mi < 4; ++mi) O[mi] = mma(ph[mi], vb, O[mi]);
-#pragma unroll
-      for (int mi = 2 * ks; mi < 4; ++mi) O[mi] = mma(pl[mi], vb, O[mi]);
-    }
-    // O += sum over live levels b of diag(weight_b) (Q G_b), fp16 MFMAs; the
-    // fp16 Q fragments of all four row tiles stay in registers for every level.
+    for (int mi = 0; mi < 4; ++mi) Op[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      f16x8 qa[4][NKS];
+      f16x8 qa[4][2];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 32 * ks + 8 * g4);
+        for (int ks = 0; ks < 2; ++ks)
+          qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 * ks + 8 * g4);
 #pragma unroll
       for (int b = 0; b < NSLOT; ++b) {
         if ((n >> b) & 1) {
@@ -403,7 +407,7 @@ fwd_rs_kernel(FwdArgs a) {
 #pragma unroll
           for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
+          for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
           const float sg = exp2_int(eg[b]);
@@ -411,21 +415,33 @@ fwd_rs_kernel(FwdArgs a) {
           for (int mi = 0; mi < 4; ++mi) {
             const f32x4 wv = *reinterpret_cast<const f32x4*>(lamw_s + b * C + 16 * mi + 4 * g4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) O[mi][r] += (wv[r] * sg) * acc[mi][r];
+            for (int r = 0; r < 4; ++r) Op[mi][r] += (wv[r] * sg) * acc[mi][r];
           }
         }
       }
     }
+    // hand the partial sums of the partner's row tiles over
+    Xc[(w * 2 + 0) * 64 + lane] = Op[oth0];
+    Xc[(w * 2 + 1) * 64 + lane] = Op[oth1];
+    // P V for this wave's two row tiles; keys in the score tile order
+    // (32ks + 4g4 + e, then +16), V operand by transposed reads.
+    f32x4 O0 = Op[own0], O1 = Op[own1];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = tok0 + 16 * mi + 4 * g4 + r;
-        if (tok < T) outg[(size_t)tok * dv + li] = O[mi][r];
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
+      const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
+      if (2 * ks <= own0) {
+        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 0) * 64 + lane], vb, O0);
+        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 1) * 64 + lane], vb, O0);
+      }
+      if (2 * ks <= own1) {
+        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 0) * 64 + lane], vb, O1);
+        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 1) * 64 + lane], vb, O1);
       }
     }
 
     // ---------------- chunk state + lssb merge (registers) -----------------
+    // (before the exchange barrier, so the two overlap)
     if (n + 1 < n1) {
       const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
       // decayed V of this wave's columns, tokens 32ks + 8g4 + e, split hi/lo
@@ -434,40 +450,42 @@ fwd_rs_kernel(FwdArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const bf16* v0 = Vs + (32 * ks + 8 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
         const bf16x8 x = cat(tr_read(v0), tr_read(v0 + 4 * LDV));
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4 + 4);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          bf16 hh, ll;
-          split_bf16(static_cast<float>(x[e]) * __shfl(esf, 32 * ks + 8 * g4 + e), hh, ll);
-          vh[ks][e] = hh;
-          vl[ks][e] = ll;
+          bf16 x1, x2;
+          split_bf16(static_cast<float>(x[e]) * (e < 4 ? e0[e] : e1[e - 4]), x1, x2);
+          vh[ks][e] = x1;
+          vl[ks][e] = x2;
         }
       }
-      // S tiles t = 2*kq + half cover dk 32kq + 8*(row>>2) + 4*half + (row&3);
-      // S[t][r] is dk 32kq + 8*g4 + 4*half + r of column li, i.e. element
-      // 4*half + r of G[.][kq].  Lower levels, decayed to the end of chunk n,
+      // S tiles t = 2*kl + half (kl = local K-step of the dk half) cover dk
+      // 64hh + 32kl + 8*(row>>2) + 4*half + (row&3); S[t][r] is element
+      // 4*half + r of G[.][kl].  Lower levels, decayed to the end of chunk n,
       // are added first; hi / lo halves of V accumulate separately.
       float fl[NSLOT];
 #pragma unroll
       for (int b = 0; b < NSLOT; ++b) fl[b] = b < m ? __expf(dec[b] + Atot) * exp2_int(eg[b]) : 0.f;
-      f32x4 Sh[2 * NKS], Sl[2 * NKS];
+      f32x4 Sh[4], Sl[4];
 #pragma unroll
-      for (int t = 0; t < 2 * NKS; ++t) {
-        const int kq = t >> 1, half = t & 1;
+      for (int t = 0; t < 4; ++t) {
+        const int kl = t >> 1, half = t & 1;
         Sh[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         Sl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < NSLOT; ++b) {
           if (b < m) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sh[t][r] += fl[b] * static_cast<float>(G[b][kq][4 * half + r]);
+            for (int r = 0; r < 4; ++r) Sh[t][r] += fl[b] * static_cast<float>(G[b][kl][4 * half + r]);
           }
         }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int t = 0; t < 2 * NKS; ++t) {
-          const int kq = t >> 1, half = t & 1;
+        for (int t = 0; t < 4; ++t) {
+          const int kq = 2 * hh + (t >> 1), half = t & 1;
           const bf16* k0 = Ks + (32 * ks + 8 * g4 + (li >> 2)) * LDQ + 32 * kq + 8 * (li & 3) + 4 * half;
           const bf16x8 ka = cat(tr_read(k0), tr_read(k0 + 4 * LDQ));
           Sh[t] = mma(ka, vh[ks], Sh[t]);
@@ -476,7 +494,7 @@ fwd_rs_kernel(FwdArgs a) {
       }
       float mx = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2 * NKS; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           Sh[t][r] += Sl[t][r];
@@ -488,7 +506,7 @@ fwd_rs_kernel(FwdArgs a) {
       for (int b = 0; b < NSLOT; ++b) {
         if (b == m) {
 #pragma unroll
-          for (int t = 0; t < 2 * NKS; ++t)
+          for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               G[b][t >> 1][4 * (t & 1) + r] = static_cast<_Float16>(Sh[t][r] * sc);
@@ -500,6 +518,26 @@ fwd_rs_kernel(FwdArgs a) {
       }
     }
     __syncthreads();
+
+    // ---------------- finish two row tiles, write the output ---------------
+    {
+      const int partner = w ^ 4;
+      const f32x4 x0 = Xc[(partner * 2 + 0) * 64 + lane];
+      const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        O0[r] += x0[r];
+        O1[r] += x1[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // rows past T fall outside the output range and are dropped
+        const int t0 = tok0 + 16 * own0 + 4 * g4 + r;
+        const int t1 = tok0 + 16 * own1 + 4 * g4 + r;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r]), outr, (t0 * dv + dv0 + c0 + li) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
+      }
+    }
   }
 }
 
@@ -618,10 +656,14 @@ int rs_lds_bytes(int L, int nslot) { return rs::lds_bytes(L, nslot); }
 int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t stream) {
   const int bytes = rs::lds_bytes(a.L, a.nslot);
   if (a.nslot > 8 || bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
+  // buffer offsets are 32-bit: every per-(b,h) slice, tail chunk included,
+  // must stay below 2^31 bytes
+  const size_t row_bytes = std::max({(size_t)a.dk * 2, (size_t)a.dv * 4, (size_t)a.L * 4});
+  if ((size_t)(a.T + 2 * rs::C) * row_bytes >= (size_t)1 << 31) return LL_ERR_UNSUPPORTED;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_rs_kernel<8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
     return LL_ERR_HIP;
-  hipLaunchKernelGGL(fwd_rs_kernel<8>, dim3(nblocks), dim3(256), bytes, stream, a);
+  hipLaunchKernelGGL(fwd_rs_kernel<8>, dim3(nblocks), dim3(512), bytes, stream, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
