@@ -39,7 +39,6 @@ namespace ll {
 namespace rs {
 
 constexpr int C = 64, DKP = 128, NKS = DKP / 32, LOGC = 6;
-constexpr int NT = 256;  // threads of the segment-state kernel
 constexpr int LDQ = DKP + 8;  // Qs, Ks row stride (bf16)
 constexpr int LDV = 64 + 8;   // Vs row stride (bf16): 64 dv columns
 constexpr int QS_OFF = 0;
@@ -86,6 +85,23 @@ __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each
+// 16-lane row, then the row totals carried across rows by the row broadcasts
+// of lanes 15 and 31 (DPP).  Lanes without a source add zero.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
 }
 
 // Power-of-two scale exponent e such that mx * 2^-e lies in [2^14, 2^15)
@@ -264,21 +280,10 @@ fwd_rs_kernel(FwdArgs a) {
     }
     float cl = 0.f;
     if (w == 0) {
-      // in-chunk decay sums: cl = inclusive prefix of log_a, sf = decay from
-      // the token to the chunk's last token (summed directly)
-      cl = pla;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(cl, off);
-        if (lane >= off) cl += y;
-      }
-      float sf = __shfl_down(pla, 1);
-      if (lane == 63) sf = 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_down(sf, off);
-        if (lane + off < 64) sf += y;
-      }
+      // in-chunk decay sums: cl = inclusive prefix of log_a; the decay from a
+      // token to the chunk's last token is the chunk total minus cl
+      cl = wave_prefix_sum(pla);
+      const float sf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63)) - cl;
       cl_s[lane] = cl;
       esf_s[lane] = __expf(sf);
     }
@@ -543,109 +548,142 @@ fwd_rs_kernel(FwdArgs a) {
 
 // Segment states for the register-state path (bf16, dk <= 128, dv % 64 == 0):
 // T_g = sum over segment g of exp(cum[end] - cum[s]) k_s v_s^T, written as
-// [dv][128] fp32, plus the segment's total log decay.  Same operand scheme as
-// the chunk state in fwd_rs_kernel: row-major K / V in LDS, transposed reads,
-// V scaled by the decay to the end of each 64-token block and split hi/lo;
-// the running sum is rescaled by each block's total decay.
-__global__ void __launch_bounds__(256) seg_state_rs_kernel(SegArgs a) {
+// [dv][128] fp32, plus the segment's total log decay.  One 512-thread
+// workgroup per (b,h, segment, 64 dv columns); the segment is walked in
+// 64-token tiles.  Each tile's V is scaled by the decay to the tile's end and
+// split bf16 hi/lo once, at staging; K and V stay row-major in LDS (double
+// buffered, one barrier per tile) and are read transposed.  Wave w keeps the
+// 64 x 16 block (dk half w>>2, columns 16(w&3)) of the running sum, which is
+// rescaled by each tile's total decay.  Workgroups of the same (b,h, segment)
+// sit on the same XCD so the second column group finds K in L2.
+namespace ss {
+constexpr int NTH = 512;
+constexpr int KS_OFF = 0;
+constexpr int VH_OFF = KS_OFF + rs::C * rs::LDQ * 2;
+constexpr int VL_OFF = VH_OFF + rs::C * rs::LDV * 2;
+constexpr int BUF = VL_OFF + rs::C * rs::LDV * 2;
+constexpr int LDS_BYTES = 2 * BUF;
+}  // namespace ss
+
+__global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
   using namespace rs;
-  __shared__ __align__(16) bf16 Ks[C * LDQ];
-  __shared__ __align__(16) bf16 Vs[C * LDV];
-  __shared__ __align__(16) float esf_s[C];
+  extern __shared__ __align__(16) unsigned char smem[];
   const int D = a.dv >> 6;
   const int nsg = a.nseg - 1;  // the last segment's state is never used
   const int id = blockIdx.x;
-  const int dg = id % D, rest = id / D;
-  const int g = rest % nsg, bh = rest / nsg;
+  const int px = id & 7, rest = id >> 3;
+  const int dg = rest % D, pg = rest / D;
+  const int p = pg * 8 + px;
+  if (p >= a.BH * nsg) return;
+  const int bh = p / nsg, g = p - bh * nsg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, g4 = lane >> 4;
+  const int cs = w & 3, hh = w >> 2, c0 = 16 * cs;
   const int T = a.T, dk = a.dk, dv = a.dv;
   const int segtok = a.C << a.seg_log2;
   const int s0 = g * segtok, s1 = min(T, s0 + segtok);
-  const int dv0 = dg * 64, c0 = 16 * w;
+  const int dv0 = dg * 64;
   const size_t bhT = (size_t)bh * T;
-  const bf16* __restrict__ kg = static_cast<const bf16*>(a.k) + bhT * dk;
-  const bf16* __restrict__ vg = static_cast<const bf16*>(a.v) + bhT * dv + dv0;
-  const float* __restrict__ lag = a.log_a + bhT;
+  const rsrc_t kr = make_rsrc(static_cast<const bf16*>(a.k) + bhT * dk, T * dk * 2);
+  const rsrc_t vr = make_rsrc(static_cast<const bf16*>(a.v) + bhT * dv, T * dv * 2);
+  const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
 
-  f32x4 S[2 * NKS];
-#pragma unroll
-  for (int t = 0; t < 2 * NKS; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float Aseg = 0.f;
-  for (int b0 = s0; b0 < s1; b0 += C) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = tid + NT * i, row = v >> 4, col = (v & 15) * 8;
-      const int tok = b0 + row;
-      bf16x8 x = {};
-      if (tok < s1 && col < dk) x = *reinterpret_cast<const bf16x8*>(kg + (size_t)tok * dk + col);
-      *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = x;
-    }
+  // register prefetch of one 64-token tile; tokens at or past s1 read zero
+  bf16x8 pk[2], pv;
+  float pla;
+  auto prefetch = [&](int b0) {
+    pla = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        lar, b0 + lane < s1 ? (b0 + lane) * 4 : kOutOfRange, 0, 0));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int v = tid + NT * i, row = v >> 3, col = (v & 7) * 8;
-      const int tok = b0 + row;
-      bf16x8 x = {};
-      if (tok < s1) x = *reinterpret_cast<const bf16x8*>(vg + (size_t)tok * dv + col);
-      *reinterpret_cast<bf16x8*>(Vs + row * LDV + col) = x;
+      const int v = tid + ss::NTH * i, row = v >> 4, col = (v & 15) * 8;
+      const bool ok = b0 + row < s1 && col < dk;
+      pk[i] = load_b128(kr, ok ? ((b0 + row) * dk + col) * 2 : kOutOfRange);
     }
-    const float la = (b0 + lane < s1) ? lag[b0 + lane] : 0.f;
-    float sf = __shfl_down(la, 1);
-    if (lane == 63) sf = 0.f;
+    const int row = tid >> 3;
+    pv = load_b128(vr, b0 + row < s1 ? ((b0 + row) * dv + dv0 + (tid & 7) * 8) * 2 : kOutOfRange);
+  };
+
+  f32x4 S[4];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_down(sf, off);
-      if (lane + off < 64) sf += y;
+  for (int t = 0; t < 4; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float Aseg = 0.f;
+  prefetch(s0);
+  int buf = 0;
+  for (int b0 = s0; b0 < s1; b0 += C, buf ^= 1) {
+    unsigned char* base = smem + buf * ss::BUF;
+    bf16* Ks = reinterpret_cast<bf16*>(base + ss::KS_OFF);
+    bf16* Vh = reinterpret_cast<bf16*>(base + ss::VH_OFF);
+    bf16* Vl = reinterpret_cast<bf16*>(base + ss::VL_OFF);
+    // decay of each token to the tile's last token, every wave redundantly
+    const float cl = wave_prefix_sum(pla);
+    const float Ab = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63));
+    const float esf = __expf(Ab - cl);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int v = tid + ss::NTH * i, row = v >> 4, col = (v & 15) * 8;
+      *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
     }
-    const float Ab = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__shfl(sf, 0) + __shfl(la, 0))));
-    if (w == 0) esf_s[lane] = __expf(sf);
-    __syncthreads();
-    bf16x8 vh[2], vl[2];
+    {
+      const int row = tid >> 3, col = (tid & 7) * 8;
+      const float e = __shfl(esf, row);
+      bf16x8 h, l;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16* v0 = Vs + (32 * ks + 8 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
-      const bf16x8 x = cat(tr_read(v0), tr_read(v0 + 4 * LDV));
-      const f32x4 e0 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4);
-      const f32x4 e1 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4 + 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16 hh, ll;
-        split_bf16(static_cast<float>(x[e]) * (e < 4 ? e0[e] : e1[e - 4]), hh, ll);
-        vh[ks][e] = hh;
-        vl[ks][e] = ll;
+      for (int j = 0; j < 8; ++j) {
+        bf16 x1, x2;
+        split_bf16(static_cast<float>(pv[j]) * e, x1, x2);
+        h[j] = x1;
+        l[j] = x2;
       }
+      *reinterpret_cast<bf16x8*>(Vh + row * LDV + col) = h;
+      *reinterpret_cast<bf16x8*>(Vl + row * LDV + col) = l;
     }
+    if (b0 + C < s1) prefetch(b0 + C);
+    __syncthreads();
+
     const float fa = __expf(Ab);
 #pragma unroll
-    for (int t = 0; t < 2 * NKS; ++t) {
-      const int kq = t >> 1, half = t & 1;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[t][r] *= fa;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
+      const int vrow = (32 * ks + 8 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
+      const bf16x8 vh = cat(tr_read(Vh + vrow), tr_read(Vh + vrow + 4 * LDV));
+      const bf16x8 vl = cat(tr_read(Vl + vrow), tr_read(Vl + vrow + 4 * LDV));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kq = 2 * hh + (t >> 1), half = t & 1;
         const bf16* k0 = Ks + (32 * ks + 8 * g4 + (li >> 2)) * LDQ + 32 * kq + 8 * (li & 3) + 4 * half;
         const bf16x8 ka = cat(tr_read(k0), tr_read(k0 + 4 * LDQ));
-        S[t] = mma(ka, vh[ks], S[t]);
-        S[t] = mma(ka, vl[ks], S[t]);
+        S[t] = mma(ka, vh, S[t]);
+        S[t] = mma(ka, vl, S[t]);
       }
     }
     Aseg += Ab;
-    __syncthreads();
   }
+  // element r of S[t] is dk 64hh + 32(t>>1) + 8g4 + 4(t&1) + r, column c0 + li
   float* __restrict__ Tout =
-      a.seg_state + ((size_t)(bh * a.nseg + g) * dv + dv0 + c0 + li) * DKP + 8 * g4;
+      a.seg_state + ((size_t)(bh * a.nseg + g) * dv + dv0 + c0 + li) * DKP + 64 * hh + 8 * g4;
 #pragma unroll
-  for (int kq = 0; kq < NKS; ++kq) {
-    *reinterpret_cast<f32x4*>(Tout + 32 * kq) = S[2 * kq];
-    *reinterpret_cast<f32x4*>(Tout + 32 * kq + 4) = S[2 * kq + 1];
+  for (int kl = 0; kl < 2; ++kl) {
+    *reinterpret_cast<f32x4*>(Tout + 32 * kl) = S[2 * kl];
+    *reinterpret_cast<f32x4*>(Tout + 32 * kl + 4) = S[2 * kl + 1];
   }
   if (tid == 0 && dg == 0) a.seg_decay[bh * a.nseg + g] = Aseg;
 }
 
 int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t stream) {
-  const long long nblocks = (long long)BH * (a.nseg - 1) * (a.dv / 64);
+  const long long pairs = (long long)BH * (a.nseg - 1);
+  const long long nblocks = (pairs + 7) / 8 * 8 * (a.dv / 64);
   if (nblocks > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(seg_state_rs_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, stream, a);
+  const size_t row_bytes = std::max((size_t)a.dk * 2, (size_t)a.dv * 2);
+  if ((size_t)(a.T + 2 * rs::C) * row_bytes >= (size_t)1 << 31) return LL_ERR_UNSUPPORTED;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_state_rs_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, ss::LDS_BYTES) != hipSuccess)
+    return LL_ERR_HIP;
+  hipLaunchKernelGGL(seg_state_rs_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(ss::NTH), ss::LDS_BYTES,
+                     stream, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
