@@ -41,21 +41,28 @@ namespace rs {
 constexpr int C = 64, DKP = 128, NKS = DKP / 32, LOGC = 6;
 constexpr int LDQ = DKP + 8;  // Qs, Ks row stride (bf16)
 constexpr int LDV = 64 + 8;   // Vs row stride (bf16): 64 dv columns
-constexpr int QS_OFF = 0;
-constexpr int KS_OFF = QS_OFF + C * LDQ * 2;
-constexpr int VS_OFF = KS_OFF + C * LDQ * 2;
-constexpr int PS_OFF = VS_OFF + C * LDV * 2;
+// LDS layout of the sweep.  K, V and the in-chunk decay sums are double
+// buffered by chunk parity (they are read until the end of a chunk, while the
+// next chunk is staged); everything else is single.
+constexpr int QS_OFF = 0;                        // Q tile, bf16 [64][LDQ]
+constexpr int KS_OFF = QS_OFF + C * LDQ * 2;     // K tiles, bf16 [2][64][LDQ]
+constexpr int VS_OFF = KS_OFF + 2 * C * LDQ * 2; // V tiles, bf16 [2][64][LDV]
+constexpr int PS_OFF = VS_OFF + 2 * C * LDV * 2; // masked scores, hi/lo A fragments
 constexpr int PS_BYTES = 4 /*mi*/ * 2 /*ks*/ * 2 /*hi,lo*/ * 64 * 16;
-constexpr int XC_OFF = PS_OFF + PS_BYTES;  // partial-output exchange [8 waves][2][64 lanes] f32x4
+constexpr int XC_OFF = PS_OFF + PS_BYTES;        // partial outputs [8 waves][2][64 lanes] f32x4
 constexpr int XC_BYTES = 8 * 2 * 64 * 16;
-constexpr int CL_OFF = XC_OFF + XC_BYTES;  // cl[64], esf[64], qmax[8] (padded to 64)
-constexpr int QH_OFF = CL_OFF + 3 * C * 4;  // fp16 copy of Q, [64][LDQ]
-constexpr int LAM_OFF = QH_OFF + C * LDQ * 2;
+constexpr int CL_OFF = XC_OFF + XC_BYTES;        // [2] x (cl[64], esf[64]) fp32
+constexpr int QM_OFF = CL_OFF + 2 * 2 * C * 4;   // per-wave max |q| [8] (padded to 64 B)
+constexpr int QH_OFF = QM_OFF + 64;              // fp16 copy of Q, [64][LDQ]
+constexpr int LW_OFF = QH_OFF + C * LDQ * 2;     // per-wave Q.G row weights [8][8 levels][64]
+constexpr int LAM_OFF = LW_OFF + 8 * 8 * C * 4;  // lambda of the chunk [64][L], + 8 words of slack
 
-__host__ __device__ inline int lamw_off(int L) { return LAM_OFF + C * L * 4; }
-__host__ __device__ inline int lds_bytes(int L, int nslot) { return lamw_off(L) + (nslot > 0 ? nslot : 1) * C * 4; }
+// Rows past T of a ragged last chunk look up levels up to log2(C) that a short
+// sequence's lambda may lack; the slack keeps those (discarded) reads in bounds.
+__host__ __device__ inline int lds_bytes(int L, int nslot) { (void)nslot; return LAM_OFF + (C * L + 8) * 4; }
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef unsigned short __attribute__((ext_vector_type(2))) u16x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Transposed 8-byte LDS read: within each 16-lane group, lane i receives
@@ -140,16 +147,11 @@ fwd_rs_kernel(FwdArgs a) {
   constexpr int NTH = 512;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* Qs = reinterpret_cast<bf16*>(smem + QS_OFF);
-  bf16* Ks = reinterpret_cast<bf16*>(smem + KS_OFF);
   _Float16* Qh = reinterpret_cast<_Float16*>(smem + QH_OFF);
-  bf16* Vs = reinterpret_cast<bf16*>(smem + VS_OFF);
   bf16x8* Ps = reinterpret_cast<bf16x8*>(smem + PS_OFF);  // [mi][ks][hl][lane]
   f32x4* Xc = reinterpret_cast<f32x4*>(smem + XC_OFF);    // [wave][2][lane]
-  float* cl_s = reinterpret_cast<float*>(smem + CL_OFF);
-  float* esf_s = cl_s + C;
-  float* qmax_s = esf_s + C;  // per-wave max |q| of the chunk
+  float* qmax_s = reinterpret_cast<float*>(smem + QM_OFF);
   float* lam_s = reinterpret_cast<float*>(smem + LAM_OFF);
-  float* lamw_s = reinterpret_cast<float*>(smem + lamw_off(a.L));
 
   const int D = a.dv >> 6;  // 64-column groups
   const int id = blockIdx.x;
@@ -256,21 +258,30 @@ fwd_rs_kernel(FwdArgs a) {
 
   prefetch(n0);
 
+  f32x4 O0, O1;  // this wave's two output row tiles, written after the next barrier
+  float* lw = reinterpret_cast<float*>(smem + LW_OFF) + w * (8 * C);  // this wave's row weights
   for (int n = n0; n < n1; ++n) {
-    const int tok0 = n * C;
+    const int tok0 = n * C, par = n & 1;
+    bf16* Ks = reinterpret_cast<bf16*>(smem + KS_OFF) + par * (C * LDQ);
+    bf16* Vs = reinterpret_cast<bf16*>(smem + VS_OFF) + par * (C * LDV);
+    float* cl_s = reinterpret_cast<float*>(smem + CL_OFF) + par * (2 * C);
+    float* esf_s = cl_s + C;
     // ---------------- stage: registers -> LDS ------------------------------
-    unsigned qm = 0;  // max |q| of this thread's values, as bf16 magnitude bits
+    u16x2 qm = {0, 0};  // max |q| of this thread's values, as bf16 magnitude bits
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
       *reinterpret_cast<bf16x8*>(Qs + row * LDQ + col) = pq[i];
       *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
       const uint4 bits = __builtin_bit_cast(uint4, pq[i]);
-      qm = max(qm, max(max(bits.x & 0x7fffu, bits.x >> 16 & 0x7fffu), max(bits.y & 0x7fffu, bits.y >> 16 & 0x7fffu)));
-      qm = max(qm, max(max(bits.z & 0x7fffu, bits.z >> 16 & 0x7fffu), max(bits.w & 0x7fffu, bits.w >> 16 & 0x7fffu)));
+      qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.x & 0x7fff7fffu));
+      qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.y & 0x7fff7fffu));
+      qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.z & 0x7fff7fffu));
+      qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.w & 0x7fff7fffu));
     }
     {
-      const float qmw = wave_max(__uint_as_float(qm << 16));
+      const unsigned m16 = max(static_cast<unsigned>(qm[0]), static_cast<unsigned>(qm[1]));
+      const float qmw = wave_max(__uint_as_float(m16 << 16));
       if (lane == 0) qmax_s[w] = qmw;
     }
     *reinterpret_cast<bf16x8*>(Vs + (tid >> 3) * LDV + (tid & 7) * 8) = pv;
@@ -278,18 +289,32 @@ fwd_rs_kernel(FwdArgs a) {
       lam_s[tid * 2] = plam[0];
       lam_s[tid * 2 + 1] = plam[1];
     }
-    float cl = 0.f;
+    // in-chunk decay sums, every wave: cl = inclusive prefix of log_a (lane =
+    // token); the decay from a token to the chunk's last token is Atot - cl
+    const float cl = wave_prefix_sum(pla);
+    const float Atot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63));
     if (w == 0) {
-      // in-chunk decay sums: cl = inclusive prefix of log_a; the decay from a
-      // token to the chunk's last token is the chunk total minus cl
-      cl = wave_prefix_sum(pla);
-      const float sf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63)) - cl;
       cl_s[lane] = cl;
-      esf_s[lane] = __expf(sf);
+      esf_s[lane] = __expf(Atot - cl);
     }
     __syncthreads();
 
-    const float Atot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cl_s[C - 1])));
+    // ---------------- previous chunk: add the partner's partial sums, store
+    if (n > n0) {
+      const int partner = w ^ 4;
+      const f32x4 x0 = Xc[(partner * 2 + 0) * 64 + lane];
+      const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
+      const int tp = tok0 - C;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // rows past T fall outside the output range and are dropped
+        const int t0 = tp + 16 * own0 + 4 * g4 + r;
+        const int t1 = tp + 16 * own1 + 4 * g4 + r;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), outr, (t0 * dv + dv0 + c0 + li) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
+      }
+    }
+
     // fp16 copy of Q for the Q.G products, scaled by a power of two so the
     // chunk's max |q| sits at 2^14..2^15 (exact for bf16 values in range)
     int eq;
@@ -381,15 +406,16 @@ fwd_rs_kernel(FwdArgs a) {
         *reinterpret_cast<bf16x4*>(dst) = bf16x4{};
         *reinterpret_cast<bf16x4*>(dst + 64 * 8) = bf16x4{};
       }
-      // Q.G row weights of each inter-chunk level b for this chunk:
-      // lambda[row, log2C+1+b] * exp(cl_row + dec_b) (decay from the bucket's
-      // end to the row) * 2^eq (the fp16 Q scale); wave 0, lane = row.
-      if (w == 0) {
-        const float sq = exp2_int(eq);
+    }
+    // Row weights of this wave's Q.G products for each live inter-chunk
+    // level b (lane = row): lambda[row, log2C+1+b] * exp(cl_row + dec_b) (decay
+    // from the bucket's end to the row) * 2^eq (fp16 Q scale) * 2^eg[b] (this
+    // wave's state scale).  Written and read by this wave only.
+    {
+      const float ecl = __expf(cl) * exp2_int(eq);
 #pragma unroll
-        for (int b = 0; b < NSLOT; ++b)
-          if (b < a.nslot) lamw_s[b * C + lane] = lam_s[lane * L + LOGC + 1 + b] * __expf(cl + dec[b]) * sq;
-      }
+      for (int b = 0; b < NSLOT; ++b)
+        if ((n >> b) & 1) lw[b * C + lane] = lam_s[lane * L + LOGC + 1 + b] * ecl * (__expf(dec[b]) * exp2_int(eg[b]));
     }
     __syncthreads();
 
@@ -415,22 +441,23 @@ fwd_rs_kernel(FwdArgs a) {
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
-          const float sg = exp2_int(eg[b]);
 #pragma unroll
           for (int mi = 0; mi < 4; ++mi) {
-            const f32x4 wv = *reinterpret_cast<const f32x4*>(lamw_s + b * C + 16 * mi + 4 * g4);
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(lw + b * C + 16 * mi + 4 * g4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Op[mi][r] += (wv[r] * sg) * acc[mi][r];
+            for (int r = 0; r < 4; ++r) Op[mi][r] += wv[r] * acc[mi][r];
           }
         }
       }
     }
-    // hand the partial sums of the partner's row tiles over
+    // hand the partial sums of the partner's row tiles over (read after the
+    // next barrier)
     Xc[(w * 2 + 0) * 64 + lane] = Op[oth0];
     Xc[(w * 2 + 1) * 64 + lane] = Op[oth1];
     // P V for this wave's two row tiles; keys in the score tile order
     // (32ks + 4g4 + e, then +16), V operand by transposed reads.
-    f32x4 O0 = Op[own0], O1 = Op[own1];
+    O0 = Op[own0];
+    O1 = Op[own1];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
@@ -446,7 +473,6 @@ fwd_rs_kernel(FwdArgs a) {
     }
 
     // ---------------- chunk state + lssb merge (registers) -----------------
-    // (before the exchange barrier, so the two overlap)
     if (n + 1 < n1) {
       const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
       // decayed V of this wave's columns, tokens 32ks + 8g4 + e, split hi/lo
@@ -522,26 +548,21 @@ fwd_rs_kernel(FwdArgs a) {
         }
       }
     }
-    __syncthreads();
+  }
 
-    // ---------------- finish two row tiles, write the output ---------------
-    {
-      const int partner = w ^ 4;
-      const f32x4 x0 = Xc[(partner * 2 + 0) * 64 + lane];
-      const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
+  // ---------------- last chunk: add the partner's partial sums, store -------
+  __syncthreads();
+  if (n1 > n0) {
+    const int partner = w ^ 4;
+    const f32x4 x0 = Xc[(partner * 2 + 0) * 64 + lane];
+    const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
+    const int tp = (n1 - 1) * C;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        O0[r] += x0[r];
-        O1[r] += x1[r];
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // rows past T fall outside the output range and are dropped
-        const int t0 = tok0 + 16 * own0 + 4 * g4 + r;
-        const int t1 = tok0 + 16 * own1 + 4 * g4 + r;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r]), outr, (t0 * dv + dv0 + c0 + li) * 4, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int t0 = tp + 16 * own0 + 4 * g4 + r;
+      const int t1 = tp + 16 * own1 + 4 * g4 + r;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), outr, (t0 * dv + dv0 + c0 + li) * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
     }
   }
 }
