@@ -55,11 +55,12 @@ constexpr int CL_OFF = XC_OFF + XC_BYTES;        // [2] x (cl[64], esf[64]) fp32
 constexpr int QM_OFF = CL_OFF + 2 * 2 * C * 4;   // per-wave max |q| [8] (padded to 64 B)
 constexpr int QH_OFF = QM_OFF + 64;              // fp16 copy of Q, [64][LDQ]
 constexpr int LW_OFF = QH_OFF + C * LDQ * 2;     // per-wave Q.G row weights [8][8 levels][64]
-constexpr int LAM_OFF = LW_OFF + 8 * 8 * C * 4;  // lambda of the chunk [64][L], + 8 words of slack
+constexpr int LAM_OFF = LW_OFF + 8 * 8 * C * 4;  // lambda of the chunk [64][L], + 16 words of slack
 
-// Rows past T of a ragged last chunk look up levels up to log2(C) that a short
-// sequence's lambda may lack; the slack keeps those (discarded) reads in bounds.
-__host__ __device__ inline int lds_bytes(int L, int nslot) { (void)nslot; return LAM_OFF + (C * L + 8) * 4; }
+// Rows past T of a ragged last chunk look up levels up to log2(C), and the
+// row weights read all eight inter-chunk levels, which a short sequence's
+// lambda may lack; the slack keeps those (discarded) reads in bounds.
+__host__ __device__ inline int lds_bytes(int L, int nslot) { (void)nslot; return LAM_OFF + (C * L + 16) * 4; }
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
 typedef unsigned short __attribute__((ext_vector_type(2))) u16x2;
@@ -87,11 +88,23 @@ __device__ __forceinline__ f32x4 mma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// max over the 64 lanes, returned wave-uniform
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false)));
+}
+// Max over the 64 lanes of a NON-NEGATIVE value, returned wave-uniform: DPP
+// swaps within quads and rotations within 16-lane rows, then the four row
+// maxima compared as integers (the bit patterns of non-negative floats order
+// like the values).
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+  x = dpp_max<0xb1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max<0x4e>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max<0x124>(x);  // row_ror:4
+  x = dpp_max<0x128>(x);  // row_ror:8
+  const int xi = __float_as_int(x);
+  const unsigned a0 = __builtin_amdgcn_readlane(xi, 0), a1 = __builtin_amdgcn_readlane(xi, 16);
+  const unsigned a2 = __builtin_amdgcn_readlane(xi, 32), a3 = __builtin_amdgcn_readlane(xi, 48);
+  return __uint_as_float(max(max(a0, a1), max(a2, a3)));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within each
@@ -258,7 +271,8 @@ fwd_rs_kernel(FwdArgs a) {
 
   prefetch(n0);
 
-  f32x4 O0, O1;  // this wave's two output row tiles, written after the next barrier
+  f32x4 O0, O1;      // this wave's two output row tiles, written after the next barrier
+  float Aprev = 0.f;  // total log decay of the previous chunk
   float* lw = reinterpret_cast<float*>(smem + LW_OFF) + w * (8 * C);  // this wave's row weights
   for (int n = n0; n < n1; ++n) {
     const int tok0 = n * C, par = n & 1;
@@ -266,6 +280,9 @@ fwd_rs_kernel(FwdArgs a) {
     bf16* Vs = reinterpret_cast<bf16*>(smem + VS_OFF) + par * (C * LDV);
     float* cl_s = reinterpret_cast<float*>(smem + CL_OFF) + par * (2 * C);
     float* esf_s = cl_s + C;
+    const bf16* Kp = reinterpret_cast<const bf16*>(smem + KS_OFF) + (par ^ 1) * (C * LDQ);
+    const bf16* Vp = reinterpret_cast<const bf16*>(smem + VS_OFF) + (par ^ 1) * (C * LDV);
+    const float* esfp = reinterpret_cast<const float*>(smem + CL_OFF) + (par ^ 1) * (2 * C) + C;
     // ---------------- stage: registers -> LDS ------------------------------
     u16x2 qm = {0, 0};  // max |q| of this thread's values, as bf16 magnitude bits
 #pragma unroll
@@ -407,74 +424,16 @@ fwd_rs_kernel(FwdArgs a) {
         *reinterpret_cast<bf16x4*>(dst + 64 * 8) = bf16x4{};
       }
     }
-    // Row weights of this wave's Q.G products for each live inter-chunk
-    // level b (lane = row): lambda[row, log2C+1+b] * exp(cl_row + dec_b) (decay
-    // from the bucket's end to the row) * 2^eq (fp16 Q scale) * 2^eg[b] (this
-    // wave's state scale).  Written and read by this wave only.
-    {
-      const float ecl = __expf(cl) * exp2_int(eq);
-#pragma unroll
-      for (int b = 0; b < NSLOT; ++b)
-        if ((n >> b) & 1) lw[b * C + lane] = lam_s[lane * L + LOGC + 1 + b] * ecl * (__expf(dec[b]) * exp2_int(eg[b]));
-    }
-    __syncthreads();
-
-    // ---------------- phase 2 ----------------------------------------------
-    // Q.G over this wave's dk half for all four row tiles (fp16 MFMAs).
-    f32x4 Op[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) Op[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      f16x8 qa[4][2];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 * ks + 8 * g4);
-#pragma unroll
-      for (int b = 0; b < NSLOT; ++b) {
-        if ((n >> b) & 1) {
-          f32x4 acc[4];
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            const f32x4 wv = *reinterpret_cast<const f32x4*>(lw + b * C + 16 * mi + 4 * g4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Op[mi][r] += wv[r] * acc[mi][r];
-          }
-        }
-      }
-    }
-    // hand the partial sums of the partner's row tiles over (read after the
-    // next barrier)
-    Xc[(w * 2 + 0) * 64 + lane] = Op[oth0];
-    Xc[(w * 2 + 1) * 64 + lane] = Op[oth1];
-    // P V for this wave's two row tiles; keys in the score tile order
-    // (32ks + 4g4 + e, then +16), V operand by transposed reads.
-    O0 = Op[own0];
-    O1 = Op[own1];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
-      const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
-      if (2 * ks <= own0) {
-        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 0) * 64 + lane], vb, O0);
-        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 1) * 64 + lane], vb, O0);
-      }
-      if (2 * ks <= own1) {
-        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 0) * 64 + lane], vb, O1);
-        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 1) * 64 + lane], vb, O1);
-      }
-    }
-
-    // ---------------- chunk state + lssb merge (registers) -----------------
-    if (n + 1 < n1) {
-      const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
+    // ---------------- previous chunk's state + lssb merge (registers) ------
+    // Chunk n-1 -> n: its state joins the buckets before this chunk's Q.G
+    // products.  Done here, next to the score tiles of chunk n, so the two
+    // independent instruction streams overlap.
+    if (n > n0) {
+      const int m = __builtin_ctz(static_cast<unsigned>(n));
+      const bf16* Ks = Kp;
+      const bf16* Vs = Vp;
+      const float* esf_s = esfp;
+      const float Atot = Aprev;
       // decayed V of this wave's columns, tokens 32ks + 8g4 + e, split hi/lo
       bf16x8 vh[2], vl[2];
 #pragma unroll
@@ -548,6 +507,75 @@ fwd_rs_kernel(FwdArgs a) {
         }
       }
     }
+    // Row weights of this wave's Q.G products for each live inter-chunk
+    // level b (lane = row): lambda[row, log2C+1+b] * exp(cl_row + dec_b) (decay
+    // from the bucket's end to the row) * 2^eq (fp16 Q scale) * 2^eg[b] (this
+    // wave's state scale).  Written and read by this wave only.
+    {
+      const float ecl = __expf(cl) * exp2_int(eq);
+      float lv[NSLOT];
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b) lv[b] = lam_s[lane * L + LOGC + 1 + b];
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b)
+        if ((n >> b) & 1) lw[b * C + lane] = lv[b] * ecl * (__expf(dec[b]) * exp2_int(eg[b]));
+    }
+    __syncthreads();
+
+    // ---------------- phase 2 ----------------------------------------------
+    // Q.G over this wave's dk half for all four row tiles (fp16 MFMAs).
+    f32x4 Op[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) Op[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      f16x8 qa[4][2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 * ks + 8 * g4);
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b) {
+        if ((n >> b) & 1) {
+          f32x4 acc[4];
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) {
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(lw + b * C + 16 * mi + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Op[mi][r] += wv[r] * acc[mi][r];
+          }
+        }
+      }
+    }
+    // hand the partial sums of the partner's row tiles over (read after the
+    // next barrier)
+    Xc[(w * 2 + 0) * 64 + lane] = Op[oth0];
+    Xc[(w * 2 + 1) * 64 + lane] = Op[oth1];
+    // P V for this wave's two row tiles; keys in the score tile order
+    // (32ks + 4g4 + e, then +16), V operand by transposed reads.
+    O0 = Op[own0];
+    O1 = Op[own1];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
+      const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
+      if (2 * ks <= own0) {
+        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 0) * 64 + lane], vb, O0);
+        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 1) * 64 + lane], vb, O0);
+      }
+      if (2 * ks <= own1) {
+        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 0) * 64 + lane], vb, O1);
+        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 1) * 64 + lane], vb, O1);
+      }
+    }
+
+    Aprev = Atot;
   }
 
   // ---------------- last chunk: add the partner's partial sums, store -------
