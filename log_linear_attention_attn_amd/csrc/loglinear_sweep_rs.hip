@@ -132,6 +132,10 @@ __device__ __forceinline__ int scale_exp(float mx) {
   return max(-110, min(110, e));
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x on the transcendental unit (v_exp_f32)
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float exp2_int(int e) { return __uint_as_float(static_cast<unsigned>(e + 127) << 23); }
 
 // Raw buffer resource over [base, base + bytes): loads beyond the range return
@@ -247,8 +251,17 @@ fwd_rs_kernel(FwdArgs a) {
   bf16x8 pq[2], pk[2], pv;
   float plam[2];
   float pla;
+  // per-thread parts of the chunk loads' offsets; columns past dk (padded
+  // head dim) get an out-of-range offset and read zero
+  uint32_t off_qk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
+    off_qk[i] = static_cast<uint32_t>((row * dk + col) * 2) | (col < dk ? 0u : kOutOfRange);
+  }
+  const uint32_t off_v = static_cast<uint32_t>(((tid >> 3) * dv + dv0 + (tid & 7) * 8) * 2);
   auto prefetch = [&](int n) {
-    const int tok0 = n * C;
+    const uint32_t tok0 = static_cast<uint32_t>(n * C);
     // small loads first: vmcnt counts in order, so a later wait for one of
     // these does not also wait for the large q / k / v loads.  Lambda words
     // past C * L belong to the next chunk and are not staged.
@@ -258,19 +271,26 @@ fwd_rs_kernel(FwdArgs a) {
       plam[1] = __uint_as_float(x[1]);
     }
     pla = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lar, (tok0 + lane) * 4, 0, 0));
+    const uint32_t cq = tok0 * dk * 2;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
-      // columns past dk (padded head dim) read zero: out-of-range offset, no branch
-      const uint32_t off = static_cast<uint32_t>(((tok0 + row) * dk + col) * 2) | ((static_cast<uint32_t>(dk - 1 - col) >> 31) << 31);
-      pq[i] = load_b128(qr, off);
-      pk[i] = load_b128(kr, off);
+      pq[i] = load_b128(qr, off_qk[i] + cq);
+      pk[i] = load_b128(kr, off_qk[i] + cq);
     }
-    pv = load_b128(vr, ((tok0 + (tid >> 3)) * dv + dv0 + (tid & 7) * 8) * 2);
+    pv = load_b128(vr, off_v + tok0 * dv * 2);
   };
 
   prefetch(n0);
 
+  // level and causal mask of the diagonal score tiles (query 16qb + li,
+  // key 16qb + 4g4 + r): functions of the in-block positions only
+  int dlev[4];
+  unsigned dmask = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    dlev[r] = level_of(li, 4 * g4 + r);
+    dmask |= (4 * g4 + r <= li ? 1u : 0u) << r;
+  }
   f32x4 O0, O1;      // this wave's two output row tiles, written after the next barrier
   float Aprev = 0.f;  // total log decay of the previous chunk
   float* lw = reinterpret_cast<float*>(smem + LW_OFF) + w * (8 * C);  // this wave's row weights
@@ -311,7 +331,7 @@ fwd_rs_kernel(FwdArgs a) {
     const float cl = wave_prefix_sum(pla);
     const float Atot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63));
     if (w == 0) {
-      cl_s[lane] = cl;
+      cl_s[lane] = cl * kLog2e;  // base-2 units for the score decays
       esf_s[lane] = __expf(Atot - cl);
     }
     __syncthreads();
@@ -396,13 +416,13 @@ fwd_rs_kernel(FwdArgs a) {
           if (kb < qb) {
             const float lam = lam_s[qi * L + 4 + (32 - __clz(qb ^ kb))];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pv4[r] = acc[it][r] * lam * __expf(clq - clk[r]);
+            for (int r = 0; r < 4; ++r) pv4[r] = acc[it][r] * lam * exp2f_fast(clq - clk[r]);
           } else {
+            // diagonal tile: same 16-block, so the level and the causal
+            // mask depend on the in-block positions only
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int kj = 16 * kb + 4 * g4 + r;
-              pv4[r] = kj <= qi ? acc[it][r] * lam_s[qi * L + level_of(qi, kj)] * __expf(clq - clk[r]) : 0.f;
-            }
+            for (int r = 0; r < 4; ++r)
+              pv4[r] = (dmask >> r) & 1 ? acc[it][r] * lam_s[qi * L + dlev[r]] * exp2f_fast(clq - clk[r]) : 0.f;
           }
           bf16x4 h, l;
 #pragma unroll
@@ -454,21 +474,20 @@ fwd_rs_kernel(FwdArgs a) {
       // 64hh + 32kl + 8*(row>>2) + 4*half + (row&3); S[t][r] is element
       // 4*half + r of G[.][kl].  Lower levels, decayed to the end of chunk n,
       // are added first; hi / lo halves of V accumulate separately.
-      float fl[NSLOT];
-#pragma unroll
-      for (int b = 0; b < NSLOT; ++b) fl[b] = b < m ? __expf(dec[b] + Atot) * exp2_int(eg[b]) : 0.f;
       f32x4 Sh[4], Sl[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int kl = t >> 1, half = t & 1;
         Sh[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         Sl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-        for (int b = 0; b < NSLOT; ++b) {
-          if (b < m) {
+      for (int b = 0; b < NSLOT; ++b) {
+        if (b < m) {
+          const float fl = __expf(dec[b] + Atot) * exp2_int(eg[b]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sh[t][r] += fl[b] * static_cast<float>(G[b][kl][4 * half + r]);
-          }
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sh[t][r] += fl * static_cast<float>(G[b][t >> 1][4 * (t & 1) + r]);
         }
       }
 #pragma unroll
