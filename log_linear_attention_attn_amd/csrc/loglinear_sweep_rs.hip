@@ -481,7 +481,7 @@ fwd_rs_kernel(FwdArgs a) {
         Sl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int b = 0; b < NSLOT; ++b) {
+      for (int b = 0; b < NSLOT - 1; ++b) {
         if (b < m) {
           const float fl = __expf(dec[b] + Atot) * exp2_int(eg[b]);
 #pragma unroll
@@ -511,18 +511,27 @@ fwd_rs_kernel(FwdArgs a) {
         }
       const int em = scale_exp(wave_max(mx));
       const float sc = exp2_int(-em);
+      f16x8 gn[2];
 #pragma unroll
-      for (int b = 0; b < NSLOT; ++b) {
-        if (b == m) {
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
+        for (int r = 0; r < 4; ++r) gn[t >> 1][4 * (t & 1) + r] = static_cast<_Float16>(Sh[t][r] * sc);
+      if (m == 0) {  // every other chunk: the new state is level 0, nothing merged
+        G[0][0] = gn[0];
+        G[0][1] = gn[1];
+        eg[0] = em;
+        dec[0] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              G[b][t >> 1][4 * (t & 1) + r] = static_cast<_Float16>(Sh[t][r] * sc);
-          eg[b] = em;
-          dec[b] = 0.f;
-        } else if (b > m) {
-          dec[b] += Atot;
+        for (int b = 1; b < NSLOT; ++b) dec[b] += Atot;
+      } else {
+#pragma unroll
+        for (int b = 1; b < NSLOT; ++b) {
+          if (b == m) {
+            G[b][0] = gn[0];
+            G[b][1] = gn[1];
+            eg[b] = em;
+          }
+          dec[b] = b == m ? 0.f : (b > m ? dec[b] + Atot : dec[b]);
         }
       }
     }
