@@ -81,11 +81,21 @@ def cpu_baseline(w, budget_s: float = 12.0):
     import numpy as np
     import oracle
     import workloads as W
+    threads, blas = 0, "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 0) for i in threadpool_info()] or [0])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 0) for i in info] or [0])
+        blas = ",".join(sorted({f"{i.get('internal_api')}:{i.get('version')}" for i in info
+                                if i.get("user_api") == "blas"})) or blas
     except Exception:
-        threads = 0
+        pass
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     q, k, v, la, lam = W.make_fwd_inputs(w)
     done, t0 = 0, time.perf_counter()
     while True:
@@ -102,7 +112,10 @@ def cpu_baseline(w, budget_s: float = 12.0):
         "kind": "oracle",
         "sample": f"oracle.forward (fp64 NumPy, dense masked QK^T V) on {done} of {w.B * w.H} (b,h) "
                   f"head-sequences of T={w.T}, {el:.1f} s; rate = {done}*T/H tokens / time",
-        "cpu": platform.processor() or platform.machine(),
+        "seconds_per_head_sequence": el / done,
+        "full_config_seconds_extrapolated": el / done * w.B * w.H,
+        "cpu": cpu,
+        "blas": blas,
     }
 
 
@@ -134,35 +147,43 @@ def main():
     torch.cuda.set_device(dev)
     base = W.make_fwd_inputs(w)
     sets = [[t.to(dev) for t in base]]
-    # a second input set (same values, other buffers) so consecutive steps do not
-    # find their inputs in the 256 MB infinity cache
-    sets.append([t.clone() for t in sets[0]])
+    # three input sets (same values, other buffers), rotated so consecutive
+    # steps do not find their inputs in the 256 MB infinity cache
+    sets += [[t.clone() for t in sets[0]] for _ in range(2)]
     out = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.float32, device=dev)
     K, Wm = args.steps, args.warmup
 
-    def step(i, ev=None):
-        q, k, v, la, lam = sets[i % len(sets)]
-        ll.fwd_ex(q, k, v, la, lam, C=w.C, out=out, seg_log2=args.seg_log2, phase_events=ev)
+    def timed(input_sets):
+        def step(i, ev=None):
+            q, k, v, la, lam = input_sets[i % len(input_sets)]
+            ll.fwd_ex(q, k, v, la, lam, C=w.C, out=out, seg_log2=args.seg_log2, phase_events=ev)
 
-    for i in range(Wm):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    for s in evs:
-        for e in s:
-            e.record()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(K):
-        step(i, evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / K
-    phases = [[s[j].elapsed_time(s[j + 1]) for j in range(3)] for s in evs]
+        for i in range(Wm):
+            step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        for s_ in evs:
+            for e in s_:
+                e.record()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(K):
+            step(i, evs[i])
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        phases = [[s_[j].elapsed_time(s_[j + 1]) for j in range(3)] for s_ in evs]
+        return start.elapsed_time(stop) / K, wall, phases
+
+    ms, wall, phases = timed(sets)
     seg_ms, node_ms, sweep_ms = (sum(p[j] for p in phases) / K for j in range(3))
+    step_ms = sorted(sum(p) for p in phases)
+    median_ms = step_ms[len(step_ms) // 2]
+    # the kernels are data-oblivious: the same shapes with log_a = 0 must time the same
+    zero_sets = [[q, k, v, torch.zeros_like(la), lam] for q, k, v, la, lam in sets]
+    ms_zero, _, _ = timed(zero_sets)
 
     flops = algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv, w.C)
     in_bytes = 2 if w.dtype == "bf16" else 4
@@ -194,6 +215,8 @@ def main():
         "algorithmic_bytes": abytes,
         "frac_roofline_step": max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBS * 1e9)) / (ms * 1e-3),
         "kernels_ms": {"seg_state": seg_ms, "seg_node": node_ms, "fwd_sweep": sweep_ms},
+        "median_ms_per_step": median_ms,
+        "ms_per_step_log_a_zero": ms_zero,
         "wall_ms_per_step": wall / K * 1e3,
         "roofline": {
             "kernel": "fwd_rs_kernel" if (w.dtype == "bf16" and w.C == 64 and w.dk > 64 and w.dv % 64 == 0
