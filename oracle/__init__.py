@@ -10,4 +10,5 @@ from .loglinear_oracle import (  # noqa: F401
     lssb,
     mask_rows,
     recurrent_forward,
+    states_at,
 )

@@ -246,3 +246,29 @@ def recurrent_forward(q, k, v, log_a, lam) -> np.ndarray:
                                 log_a[:, :, t], lam[:, :, t], np.full(B, t))
         out[:, :, t] = o
     return out
+
+
+def states_at(k, v, log_a, t: int, L: int) -> np.ndarray:
+    """Per-level decode states S_t after the tokens 0..t, for every (b, h).
+
+    By definition ([P1] 循环形式与输出计算; [P4] 多状态线性注意力): the level-l
+    state is the decayed sum over the level-l Fenwick bucket of query t,
+        S_t^l = sum_{s in bucket l of t} exp(cum[t] - cum[s]) k_s v_s^T,
+    stored k-major (dk x dv); levels with no bucket at t are 0.  These are the
+    states a decode step at position t+1 starts from (prefill -> decode).
+    k: [B, H, T, dk], v: [B, H, T, dv], log_a: [B, H, T] with T > t.
+    Returns [B, H, L, dk, dv] fp64.
+    """
+    k, v, log_a = (_f64(x) for x in (k, v, log_a))
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    if not 0 <= t < T:
+        raise ValueError("need 0 <= t < T")
+    cum = np.cumsum(log_a, axis=-1)
+    S = np.zeros((B, H, L, dk, dv))
+    for level, lo, hi in fenwick_buckets(t):
+        if level >= L:
+            raise ValueError(f"level {level} of t={t} does not fit in L={L}")
+        w = np.exp(cum[:, :, t:t + 1] - cum[:, :, lo:hi])          # [B, H, n]
+        S[:, :, level] = np.einsum("bhs,bhsd,bhse->bhde", w, k[:, :, lo:hi], v[:, :, lo:hi])
+    return S

@@ -309,3 +309,42 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
     dense = O.forward(q, k, v, log_a, lam)
     rec = O.recurrent_forward(q, k, v, log_a, lam)
     assert not np.allclose(dense, rec, rtol=1e-6, atol=1e-8)
+
+
+# ---------------------------------------------------------------- prefill -> decode states
+
+def test_states_at_matches_recurrent_states():
+    """The by-definition states at t equal the states the decode rule reaches
+    after stepping through 0..t ([P1] 解码：基于 lssb 的状态更新)."""
+    q, k, v, la, lam = _rand_inputs(np.random.default_rng(21), 1, 2, 45, 6, 5)
+    L = lam.shape[-1]
+    states = np.zeros((1, 2, L, 6, 5))
+    for t in range(45):
+        _, states = oracle.decode_step(states, q[:, :, t], k[:, :, t], v[:, :, t], la[:, :, t],
+                                       lam[:, :, t], np.full(1, t))
+        if t in (0, 1, 6, 7, 8, 31, 44):
+            np.testing.assert_allclose(oracle.states_at(k, v, la, t, L), states, rtol=1e-12, atol=1e-13)
+
+
+def test_states_at_readout_is_the_parallel_output():
+    """o_t = sum_l lambda[t, l] q_t^T S_t^l reproduces the dense forward row t
+    ([P1] 循环形式与输出计算 and 并行形式 describe one operator)."""
+    q, k, v, la, lam = _rand_inputs(np.random.default_rng(5), 2, 1, 70, 8, 4)
+    L = lam.shape[-1]
+    full = oracle.forward(q, k, v, la, lam)
+    for t in (0, 5, 32, 63, 69):
+        S = oracle.states_at(k, v, la, t, L)
+        o = np.einsum("bhl,bhd,bhlde->bhe", lam[:, :, t], q[:, :, t], S)
+        np.testing.assert_allclose(o, full[:, :, t], rtol=1e-11, atol=1e-12)
+
+
+def test_states_at_zero_pattern():
+    """Level 0 always holds k_t v_t^T; level l >= 1 is non-zero exactly when bit
+    l-1 of t is set ([P1] 前缀的层次化分解: one bucket per set bit)."""
+    _, k, v, la, _ = _rand_inputs(np.random.default_rng(9), 1, 1, 200, 4, 4)
+    L = 9
+    for t in (0, 1, 2, 3, 100, 127, 128, 199):
+        S = oracle.states_at(k, v, la, t, L)[0, 0]
+        np.testing.assert_allclose(S[0], np.outer(k[0, 0, t], v[0, 0, t]))
+        for l in range(1, L):
+            assert (np.abs(S[l]).max() > 0) == bool((t >> (l - 1)) & 1), (t, l)
