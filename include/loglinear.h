@@ -85,6 +85,17 @@ int loglinear_fwd_f32(const float* q, const float* k, const float* v, const floa
                       int C, void* stream);
 
 /*
+ * Decode states: a HOST struct describing a caller-owned DEVICE buffer
+ *   data : [N, H, L, dk, dv] fp32, row-major (dv fastest).
+ * Slot l holds the level-l state S^(l) = sum over the level-l bucket of
+ * decay * k v^T, stored k-major (dk x dv) — the transpose of the pages' v k^T.
+ */
+typedef struct {
+  float* data;
+  int N, H, L, dk, dv;
+} loglinear_states;
+
+/*
  * Options for loglinear_fwd_ex.
  *   dtype        : LL_BF16 or LL_F32 (type of q, k, v).
  *   seg_log2     : -1 = automatic.  Otherwise the sequence is processed in
@@ -104,6 +115,9 @@ int loglinear_fwd_f32(const float* q, const float* k, const float* v, const floa
  *                  before the sweep kernel and after it (kernels that a plan
  *                  does not need are skipped, their events still recorded), so
  *                  a caller can time each kernel of one call.
+ *   final_states : NULL, or a states buffer (see loglinear_states) that
+ *                  receives the per-level decode states at position T-1, as
+ *                  loglinear_prefill describes.
  */
 typedef struct {
   int dtype;
@@ -112,26 +126,41 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   void* const* phase_events;
+  const loglinear_states* final_states;
 } loglinear_fwd_opts;
 
 int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* log_a,
                      const float* lambda, float* out, int B, int H, int T, int dk, int dv,
                      int C, const loglinear_fwd_opts* opts, void* stream);
 
+/*
+ * Prefill: the forward of loglinear_fwd, plus the decode states that continue
+ * the sequence (page above, sections 循环形式与输出计算 and 解码：基于 lssb 的状态更新).
+ *   states : a states buffer with N = B, the same H, dk, dv, and
+ *            L >= loglinear_num_levels(T) (more levels are allowed, so decoding
+ *            can run past 2^(L_T - 1) tokens).  On return level l holds
+ *            S^(l) = sum over the level-l Fenwick bucket of query T-1 of
+ *            exp(cum[T-1] - cum[s]) k_s v_s^T, and levels with no bucket at
+ *            T-1 hold 0: exactly the states a loglinear_decode_step at t = T
+ *            expects on entry.  Every element of the buffer is written.
+ * Other arguments, sizes and errors as loglinear_fwd; a states buffer whose
+ * N, H, dk or dv differ from the forward's, or whose L is too small, gives
+ * LL_ERR_SHAPE.  The bf16 register-state path keeps the inter-chunk bucket
+ * states in fp16 with power-of-two scales, so its states carry the forward's
+ * rounding (about 1e-3 of their RMS).
+ */
+int loglinear_prefill(const void* q, const void* k, const void* v, const float* log_a,
+                      const float* lambda, float* out, const loglinear_states* states, int B,
+                      int H, int T, int dk, int dv, int C, void* stream);
+
+/* Same as loglinear_prefill with fp32 q, k, v. */
+int loglinear_prefill_f32(const float* q, const float* k, const float* v, const float* log_a,
+                          const float* lambda, float* out, const loglinear_states* states,
+                          int B, int H, int T, int dk, int dv, int C, void* stream);
+
 /* Workspace bytes loglinear_fwd_ex needs for these sizes (0 if none); seg_log2
  * as in loglinear_fwd_opts.  Returns (size_t)-1 for invalid sizes. */
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2);
-
-/*
- * Decode states: a HOST struct describing a caller-owned DEVICE buffer
- *   data : [N, H, L, dk, dv] fp32, row-major (dv fastest).
- * Slot l holds the level-l state S^(l) = sum over the level-l bucket of
- * decay * k v^T, stored k-major (dk x dv) — the transpose of the pages' v k^T.
- */
-typedef struct {
-  float* data;
-  int N, H, L, dk, dv;
-} loglinear_states;
 
 /*
  * One O(log T) decode step for N sequences x H heads (page above, section

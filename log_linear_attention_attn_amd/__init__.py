@@ -8,6 +8,7 @@ the library is not built, every call raises.
 Entry points (same names as the C ABI in include/loglinear.h):
     fwd(q, k, v, log_a, lam, C=64, out=None)            bf16 or fp32 q/k/v
     fwd_ex(..., seg_log2=-1, workspace=None)            explicit options
+    prefill(q, k, v, log_a, lam, C=64, L=None)          forward + decode states at T-1
     fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1)
     decode_step(states, q, k, v, log_a, lam, t, out=None)
     level_table(T, device=None)                          int8 [T, T]
@@ -21,7 +22,7 @@ import os
 import torch
 
 __all__ = [
-    "LogLinearError", "lib", "library_path", "num_levels", "fwd", "fwd_ex",
+    "LogLinearError", "lib", "library_path", "num_levels", "fwd", "fwd_ex", "prefill",
     "fwd_workspace_size", "decode_step", "level_table", "strerror",
 ]
 
@@ -32,8 +33,9 @@ _lib = None
 LL_BF16, LL_F32 = 0, 1
 EXPORTED_SYMBOLS = (
     "loglinear_num_levels", "loglinear_fwd", "loglinear_fwd_f32", "loglinear_fwd_ex",
-    "loglinear_fwd_workspace_size", "loglinear_decode_step", "loglinear_decode_step_f32",
-    "loglinear_level_table", "loglinear_strerror",
+    "loglinear_prefill", "loglinear_prefill_f32", "loglinear_fwd_workspace_size",
+    "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_level_table",
+    "loglinear_strerror",
 )
 
 
@@ -43,15 +45,15 @@ class LogLinearError(RuntimeError):
         self.status = status
 
 
-class _FwdOpts(ctypes.Structure):
-    _fields_ = [("dtype", ctypes.c_int), ("seg_log2", ctypes.c_int), ("kernel", ctypes.c_int),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("phase_events", ctypes.c_void_p)]
-
-
 class _States(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("N", ctypes.c_int), ("H", ctypes.c_int),
                 ("L", ctypes.c_int), ("dk", ctypes.c_int), ("dv", ctypes.c_int)]
+
+
+class _FwdOpts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("seg_log2", ctypes.c_int), ("kernel", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("phase_events", ctypes.c_void_p), ("final_states", ctypes.POINTER(_States))]
 
 
 def library_path() -> str:
@@ -78,6 +80,11 @@ def lib():
     L.loglinear_fwd_f32.restype = i
     L.loglinear_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(_FwdOpts), vp]
     L.loglinear_fwd_ex.restype = i
+    pre_args = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(_States), i, i, i, i, i, i, vp]
+    L.loglinear_prefill.argtypes = pre_args
+    L.loglinear_prefill.restype = i
+    L.loglinear_prefill_f32.argtypes = pre_args
+    L.loglinear_prefill_f32.restype = i
     L.loglinear_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     L.loglinear_fwd_workspace_size.restype = sz
     dec_args = [ctypes.POINTER(_States), vp, vp, vp, vp, vp, vp, vp, vp]
@@ -141,13 +148,15 @@ KERNEL_AUTO, KERNEL_LDS_STATE, KERNEL_REGISTER_STATE = 0, 1, 2
 
 
 def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, workspace=None,
-           phase_events=None, kernel: int = KERNEL_AUTO):
+           phase_events=None, kernel: int = KERNEL_AUTO, final_states=None):
     """Log-linear attention forward through loglinear_fwd_ex.
 
     q, k: [B, H, T, dk]; v: [B, H, T, dv] (all bf16 or all fp32);
     log_a: [B, H, T] fp32; lam: [B, H, T, L] fp32 with L = num_levels(T).
     phase_events: None or 4 recorded torch.cuda.Event(enable_timing=True)
     objects, re-recorded before / between / after the library's kernels.
+    final_states: None or an fp32 [B, H, Ls, dk, dv] tensor that receives the
+    decode states at position T-1 (see prefill).
     Returns out [B, H, T, dv] fp32 (allocated unless given).
     """
     if q.dtype not in (torch.bfloat16, torch.float32):
@@ -173,9 +182,16 @@ def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, works
         ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in phase_events])
         if not all(ev):
             raise ValueError("record each phase event once before passing it")
+    fin = None
+    if final_states is not None:
+        if final_states.dim() != 5:
+            raise ValueError("final_states must be [B, H, Ls, dk, dv]")
+        _check_dev("final_states", final_states, torch.float32, (B, H, final_states.shape[2], dk, dv), dev)
+        fin = _States(final_states.data_ptr(), B, H, final_states.shape[2], dk, dv)
     opts = _FwdOpts(LL_BF16 if q.dtype == torch.bfloat16 else LL_F32, int(seg_log2), int(kernel),
                     _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                    ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
+                    ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
+                    ctypes.pointer(fin) if fin is not None else None)
     st = lib().loglinear_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out),
                                 B, H, T, dk, dv, int(C), ctypes.byref(opts), _stream(dev))
     _raise(st, "loglinear_fwd_ex")
@@ -205,6 +221,41 @@ def fwd(q, k, v, log_a, lam, C: int = 64, out=None):
            _stream(dev))
     _raise(st, "loglinear_fwd")
     return out
+
+
+def prefill(q, k, v, log_a, lam, C: int = 64, L: int | None = None, out=None, states=None):
+    """Forward plus the per-level decode states at position T-1
+    (loglinear_prefill / loglinear_prefill_f32).
+
+    Returns (out [B, H, T, dv] fp32, states [B, H, L, dk, dv] fp32); L defaults
+    to num_levels(T) and may be larger so decoding can continue past 2^(L-1).
+    """
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    Lf = num_levels(T) if T > 0 else 0
+    _check_dev("q", q, q.dtype, (B, H, T, dk), dev)
+    _check_dev("k", k, q.dtype, (B, H, T, dk), dev)
+    _check_dev("v", v, q.dtype, (B, H, T, dv), dev)
+    _check_dev("log_a", log_a, torch.float32, (B, H, T), dev)
+    _check_dev("lam", lam, torch.float32, (B, H, T, Lf), dev)
+    Ls = int(L) if L is not None else max(Lf, 1)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (B, H, T, dv), dev)
+    if states is None:
+        states = torch.empty((B, H, Ls, dk, dv), dtype=torch.float32, device=dev)
+    _check_dev("states", states, torch.float32, (B, H, Ls, dk, dv), dev)
+    desc = _States(states.data_ptr(), B, H, Ls, dk, dv)
+    f = lib().loglinear_prefill if q.dtype == torch.bfloat16 else lib().loglinear_prefill_f32
+    st = f(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out), ctypes.byref(desc),
+           B, H, T, dk, dv, int(C), _stream(dev))
+    _raise(st, "loglinear_prefill")
+    return out, states
 
 
 def decode_step(states, q, k, v, log_a, lam, t, out=None):

@@ -24,6 +24,18 @@ struct FwdArgs {
   int seg_log2;  // chunks per segment = 2^seg_log2
   int nseg;
   int nslot;  // chunk-level Fenwick bits = bit_length(N - 1)
+  // Decode states at position T-1 (prefill), or null: [BH][st_L][dk][dv] fp32.
+  // The sweep's last segment writes the inter-chunk levels log2(C)+1 .. st_L-1.
+  float* st_out;
+  int st_L;
+};
+
+struct HandoffArgs {
+  const void* k;
+  const void* v;
+  const float* log_a;
+  float* st_out;  // [BH][st_L][dk][dv]
+  int BH, T, dk, dv, C, st_L;
 };
 
 struct SegArgs {
@@ -64,6 +76,7 @@ int rs_lds_bytes(int L, int nslot);
 int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t s);
 int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t s);
 int launch_level_table(signed char* lev, int T, hipStream_t s);
+int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 
 }  // namespace ll

@@ -69,13 +69,17 @@ int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* 
 int run_fwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
             const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
             int seg_log2, int kernel, void* workspace, size_t workspace_bytes,
-            void* const* events, hipStream_t stream) {
+            void* const* events, const loglinear_states* fin, hipStream_t stream) {
   FwdPlan p;
   int st = plan_fwd(B, H, T, dk, dv, C, seg_log2, &p);
   if (st != LL_OK) return st;
   if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
+  if (fin && (fin->N != B || fin->H != H || fin->dk != dk || fin->dv != dv || fin->L > 31 ||
+              fin->L < (T > 0 ? p.L : 1)))
+    return LL_ERR_SHAPE;
   if (B == 0 || H == 0 || T == 0) return LL_OK;
   if (!q || !k || !v || !log_a || !lambda || !out) return LL_ERR_NULL;
+  if (fin && !fin->data) return LL_ERR_NULL;
   // Sweep kernel: the register-state kernel covers bf16, C = 64, 64 < dk <= 128,
   // dv a multiple of 64 and at most rs_max_slots() chunk-level Fenwick bits;
   // the LDS-state kernel covers everything else.
@@ -125,12 +129,17 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   mark(2);
   if (st == LL_OK) {
     ll::FwdArgs fa{q, k, v, log_a, lambda, out, nodes, seg_decay, p.BH, T, dk, dv, p.L,
-                   p.seg_log2, p.nseg, p.nslot};
+                   p.seg_log2, p.nseg, p.nslot, fin ? fin->data : nullptr, fin ? fin->L : 0};
     const long long pairs = (long long)p.BH * p.nseg;
     const long long nblocks = ((pairs + 7) / 8) * 8 * (use_rs ? dv / 64 : dv / 16);
     if (nblocks > 0x7fffffffLL) st = LL_ERR_UNSUPPORTED;
     else if (use_rs) st = ll::launch_sweep_rs(fa, static_cast<int>(nblocks), stream);
     else st = ll::launch_sweep(dtype, C, p.DKP, fa, static_cast<int>(nblocks), stream);
+  }
+  if (st == LL_OK && fin) {
+    // levels 0..log2(C) of the prefill states; the sweep wrote the others
+    ll::HandoffArgs ha{k, v, log_a, fin->data, p.BH, T, dk, dv, C, fin->L};
+    st = ll::launch_handoff_intra(dtype, ha, stream);
   }
   mark(3);
   if (owned) {
@@ -164,14 +173,30 @@ int loglinear_fwd(const void* q, const void* k, const void* v, const float* log_
                   const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
                   void* stream) {
   return run_fwd(LL_BF16, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
-                 static_cast<hipStream_t>(stream));
+                 nullptr, static_cast<hipStream_t>(stream));
 }
 
 int loglinear_fwd_f32(const float* q, const float* k, const float* v, const float* log_a,
                       const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
                       void* stream) {
   return run_fwd(LL_F32, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
-                 static_cast<hipStream_t>(stream));
+                 nullptr, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_prefill(const void* q, const void* k, const void* v, const float* log_a,
+                      const float* lambda, float* out, const loglinear_states* states, int B,
+                      int H, int T, int dk, int dv, int C, void* stream) {
+  if (!states) return LL_ERR_NULL;
+  return run_fwd(LL_BF16, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
+                 states, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_prefill_f32(const float* q, const float* k, const float* v, const float* log_a,
+                          const float* lambda, float* out, const loglinear_states* states,
+                          int B, int H, int T, int dk, int dv, int C, void* stream) {
+  if (!states) return LL_ERR_NULL;
+  return run_fwd(LL_F32, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
+                 states, static_cast<hipStream_t>(stream));
 }
 
 int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* log_a,
@@ -180,7 +205,7 @@ int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* l
   if (!opts) return LL_ERR_NULL;
   return run_fwd(opts->dtype, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, opts->seg_log2,
                  opts->kernel, opts->workspace, opts->workspace_bytes, opts->phase_events,
-                 static_cast<hipStream_t>(stream));
+                 opts->final_states, static_cast<hipStream_t>(stream));
 }
 
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2) {

@@ -182,6 +182,7 @@ fwd_sweep_kernel(FwdArgs a) {
   }
   __syncthreads();
 
+  float Alast = 0.f;  // total log decay of the latest chunk
   for (int n = n0; n < n1; ++n) {
     const int tok0 = n * C;
 
@@ -204,6 +205,7 @@ fwd_sweep_kernel(FwdArgs a) {
       if (lane + off < 64) sf += y;
     }
     const float Atot = __shfl(cl, C - 1);
+    Alast = Atot;
     if (w == 0 && lane < C) cl_s[lane] = cl;
 
     // This wave's 16 query rows as matrix-core fragments, straight from global
@@ -418,6 +420,34 @@ fwd_sweep_kernel(FwdArgs a) {
       dec_s[m] = 0.f;
     }
   }
+
+  // Prefill: decode states at T-1, inter-chunk levels.  The last segment ends
+  // at the last chunk, whose bucket states are the level-(log2C+1+b) states of
+  // its queries; decayed from each bucket's end to token T-1 (cl of the last
+  // token is the chunk total, the tail reads zero).
+  if (a.st_out && seg == a.nseg - 1 && n1 > n0) {
+    const int nl = n1 - 1;
+    float* __restrict__ so = a.st_out + (size_t)bh * a.st_L * dk * dv + 16 * ds;
+    for (int lev = LOGC + 1; lev < a.st_L; ++lev) {
+      const int b = lev - LOGC - 1;
+      const bool live = b < a.nslot && ((nl >> b) & 1);
+      const float f = live ? __expf(Alast + dec_s[b]) : 0.f;
+      const unsigned char* slot = st + (live ? b : 0) * Cfg::SLOT_BYTES;
+      for (int i = tid; i < 16 * dk; i += NT) {
+        const int r = i / dk, c = i - r * dk;  // dv column r of the slice, dk index c
+        float x = 0.f;
+        if (live) {
+          if constexpr (BF) {
+            const bf16* gh = reinterpret_cast<const bf16*>(slot) + r * LDG + c;
+            x = f * (static_cast<float>(gh[0]) + static_cast<float>(gh[16 * LDG]));
+          } else {
+            x = f * reinterpret_cast<const float*>(slot)[r * LDG + c];
+          }
+        }
+        so[((size_t)lev * dk + c) * dv + r] = x;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -576,6 +606,55 @@ __global__ void __launch_bounds__(256) seg_node_kernel(NodeArgs a) {
 // ---------------------------------------------------------------------------
 // level table export (test only): same device helper as the kernels.
 // ---------------------------------------------------------------------------
+// handoff_intra_kernel: the levels 0..log2(C) of the decode states at
+// position t = T-1 (prefill -> decode).  Their buckets lie inside the last
+// chunk: level 0 is {t}, level l >= 1 (when bit l-1 of t is set) the 2^(l-1)
+// tokens below t's bit l-1 (page above, section 前缀的层次化分解).  Each is
+// sum_s exp(cum[t] - cum[s]) k_s v_s^T, in plain fp32 FMAs: at most C tokens
+// per (b,h) in total.  One workgroup per (b,h, 64 dv columns).
+template <typename IT>
+__global__ void __launch_bounds__(256) handoff_intra_kernel(HandoffArgs a) {
+  __shared__ float wdec[64];  // exp(cum[t] - cum[s]) for s = tok0 + i
+  const int bh = blockIdx.x, dv0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const int T = a.T, dk = a.dk, dv = a.dv, C = a.C;
+  const int t = T - 1, tok0 = (t / C) * C;
+  const size_t bhT = (size_t)bh * T;
+  if (tid < 64) {
+    float d = 0.f;  // sum of log_a over (s, t], summed directly
+    const int s = tok0 + tid;
+    if (s <= t)
+      for (int r = s + 1; r <= t; ++r) d += a.log_a[bhT + r];
+    wdec[tid] = s <= t ? __expf(d) : 0.f;
+  }
+  __syncthreads();
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk;
+  const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
+  float* __restrict__ so = a.st_out + (size_t)bh * a.st_L * dk * dv;
+  int logc = 0;
+  while ((1 << logc) < C) ++logc;
+  const int nlev = min(logc + 1, a.st_L);
+  const int ncol = min(64, dv - dv0);
+  for (int lev = 0; lev < nlev; ++lev) {
+    int lo = t, hi = t + 1;  // level 0: {t}
+    if (lev > 0) {
+      if ((t >> (lev - 1)) & 1) {
+        lo = (t >> lev) << lev;
+        hi = lo + (1 << (lev - 1));
+      } else {
+        lo = hi = 0;  // no bucket at this level
+      }
+    }
+    for (int i = tid; i < dk * ncol; i += 256) {
+      const int d = i / ncol, j = dv0 + (i - d * ncol);
+      float x = 0.f;
+      for (int s = lo; s < hi; ++s)
+        x += wdec[s - tok0] * to_float(kg[(size_t)s * dk + d]) * to_float(vg[(size_t)s * dv + j]);
+      so[((size_t)lev * dk + d) * dv + j] = x;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) level_table_kernel(signed char* lev, int T) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)T * T) return;
@@ -637,6 +716,16 @@ static int launch_sweep_dispatch(int C, int DKP, const FwdArgs& a, int nblocks, 
 int launch_sweep(int dtype, int C, int DKP, const FwdArgs& a, int nblocks, hipStream_t s) {
   return dtype == LL_BF16 ? launch_sweep_dispatch<bf16>(C, DKP, a, nblocks, s)
                           : launch_sweep_dispatch<float>(C, DKP, a, nblocks, s);
+}
+
+int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s) {
+  if (a.BH <= 0) return LL_OK;
+  const dim3 grid(static_cast<unsigned>(a.BH), static_cast<unsigned>((a.dv + 63) / 64));
+  if (dtype == LL_BF16)
+    hipLaunchKernelGGL(handoff_intra_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(handoff_intra_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
 int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStream_t s) {

@@ -157,7 +157,9 @@ __device__ __forceinline__ bf16x8 load_b128(rsrc_t r, uint32_t off) {
 // 16*(w&3)..+15 of the workgroup's 64 and dk half h = w>>2 of the bucket
 // states.  The two dk halves of a column slice add their partial Q.G sums
 // through LDS; each wave finishes the output of two row tiles.
-template <int NSLOT>
+// EMIT: also write the prefill decode states (a separate instantiation, so the
+// plain forward does not carry the extra live registers).
+template <int NSLOT, bool EMIT>
 __global__ void __launch_bounds__(512)
 fwd_rs_kernel(FwdArgs a) {
   using namespace rs;
@@ -621,6 +623,35 @@ fwd_rs_kernel(FwdArgs a) {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
     }
   }
+
+  // ---------------- prefill: decode states at T-1, inter-chunk levels -------
+  // The last segment ends at the last chunk, whose bucket states are the
+  // level-(log2C+1+b) states of its queries; decayed from each bucket's end to
+  // token T-1 (cl of the last token = the chunk total, the tail reads zero).
+  if (EMIT && seg == a.nseg - 1 && n1 > n0) {
+    const int nl = n1 - 1;
+    float* __restrict__ so = a.st_out + (size_t)bh * a.st_L * dk * dv + dv0 + c0 + li;
+    for (int lev = LOGC + 1; lev < a.st_L; ++lev) {
+      const int b = lev - LOGC - 1;
+      float f = 0.f;
+      f16x8 g[2] = {f16x8{}, f16x8{}};
+#pragma unroll
+      for (int bb = 0; bb < NSLOT; ++bb) {
+        if (bb == b && ((nl >> bb) & 1)) {
+          f = __expf(Aprev + dec[bb]) * exp2_int(eg[bb]);
+          g[0] = G[bb][0];
+          g[1] = G[bb][1];
+        }
+      }
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 64 * hh + 32 * kl + 8 * g4 + e;  // dk index of G[.][kl][e]
+          if (d < dk) so[((size_t)lev * dk + d) * dv] = f * static_cast<float>(g[kl][e]);
+        }
+    }
+  }
 }
 
 // Segment states for the register-state path (bf16, dk <= 128, dv % 64 == 0):
@@ -775,10 +806,14 @@ int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t stream) {
   // must stay below 2^31 bytes
   const size_t row_bytes = std::max({(size_t)a.dk * 2, (size_t)a.dv * 4, (size_t)a.L * 4});
   if ((size_t)(a.T + 2 * rs::C) * row_bytes >= (size_t)1 << 31) return LL_ERR_UNSUPPORTED;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_rs_kernel<8>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+  const void* fn = a.st_out ? reinterpret_cast<const void*>(&fwd_rs_kernel<8, true>)
+                            : reinterpret_cast<const void*>(&fwd_rs_kernel<8, false>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
     return LL_ERR_HIP;
-  hipLaunchKernelGGL(fwd_rs_kernel<8>, dim3(nblocks), dim3(512), bytes, stream, a);
+  if (a.st_out)
+    hipLaunchKernelGGL((fwd_rs_kernel<8, true>), dim3(nblocks), dim3(512), bytes, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_rs_kernel<8, false>), dim3(nblocks), dim3(512), bytes, stream, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 

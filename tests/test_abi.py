@@ -134,3 +134,30 @@ def test_binding_refuses_cpu_tensors():
     lam = torch.zeros(1, 1, 16, ll.num_levels(16))
     with pytest.raises(ValueError):
         ll.fwd(q, q, q, torch.zeros(1, 1, 16), lam, C=16)
+
+
+def test_prefill_argument_errors():
+    """States buffers that do not match the forward are rejected before any
+    GPU work; a zero-sized problem is a no-op."""
+    L = ll.lib()
+    p = ctypes.c_void_p(1)
+    B, H, T, dk, dv, C = 2, 3, 100, 32, 16, 16  # num_levels(100) = 8
+    assert L.loglinear_prefill(p, p, p, p, p, p, None, B, H, T, dk, dv, C, None) == LL_ERR_NULL
+    for N_, H_, Lv, dk_, dv_, want in [
+        (1, 3, 8, 32, 16, LL_ERR_SHAPE),    # N != B
+        (2, 2, 8, 32, 16, LL_ERR_SHAPE),    # H differs
+        (2, 3, 7, 32, 16, LL_ERR_SHAPE),    # fewer levels than T needs
+        (2, 3, 32, 32, 16, LL_ERR_SHAPE),   # more than 31 levels
+        (2, 3, 8, 16, 16, LL_ERR_SHAPE),    # dk differs
+        (2, 3, 8, 32, 32, LL_ERR_SHAPE),    # dv differs
+        (2, 3, 8, 32, 16, LL_ERR_NULL),     # shapes fine, NULL data
+    ]:
+        desc = ll._States(0, N_, H_, Lv, dk_, dv_)
+        for f in (L.loglinear_prefill, L.loglinear_prefill_f32):
+            assert f(p, p, p, p, p, p, ctypes.byref(desc), B, H, T, dk, dv, C, None) == want, (N_, H_, Lv, dk_, dv_)
+    desc = ll._States(0, 0, H, 8, dk, dv)
+    assert L.loglinear_prefill(p, p, p, p, p, p, ctypes.byref(desc), 0, H, T, dk, dv, C, None) == LL_OK
+    # the same checks through loglinear_fwd_ex's final_states option
+    bad = ll._States(0, 1, H, 8, dk, dv)
+    opts = ll._FwdOpts(0, -1, 0, None, 0, None, ctypes.pointer(bad))
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, B, H, T, dk, dv, C, ctypes.byref(opts), None) == LL_ERR_SHAPE
