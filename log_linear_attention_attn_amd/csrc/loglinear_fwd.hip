@@ -586,21 +586,29 @@ seg_state_kernel(SegArgs a) {
 // m = lssb(g) it covers segments [g - 2^m, g) (the merge the lssb rule makes
 // on the step into g, [P1] 解码), decayed to the start of g:
 //   node_g = sum_{g'} exp(A_{g'+1} + ... + A_{g-1}) T_{g'}.
-// One thread per (b,h, g, state element); the sum runs forward, rescaling the
-// partial sum by each segment's total decay.
+// One thread per (b,h, g, four state elements).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) seg_node_kernel(NodeArgs a) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;  // four consecutive elements
   const int g = blockIdx.y + 1;
   const int bh = blockIdx.z;
   if (e >= a.E) return;
   const size_t base = (size_t)bh * a.nseg;
   const int m = lssb(static_cast<uint32_t>(g));
   const int g0 = g - (1 << m);
-  float x = 0.f;
-  for (int gp = g0; gp < g; ++gp)
-    x = x * __expf(a.seg_decay[base + gp]) + a.seg_state[(base + gp) * a.E + e];
-  a.nodes[(base + g) * a.E + e] = x;
+  // each term is independent: weight exp(A_{g'+1} + ... + A_{g-1}), summed
+  // from the end so the weights come out of one running sum
+  f32x4 x = {0.f, 0.f, 0.f, 0.f};
+  float d = 0.f;
+#pragma unroll 4
+  for (int gp = g - 1; gp >= g0; --gp) {
+    const float wgt = __expf(d);
+    const f32x4 t = *reinterpret_cast<const f32x4*>(a.seg_state + (base + gp) * a.E + e);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] += wgt * t[r];
+    d += a.seg_decay[base + gp];
+  }
+  *reinterpret_cast<f32x4*>(a.nodes + (base + g) * a.E + e) = x;
 }
 
 // ---------------------------------------------------------------------------
@@ -743,7 +751,8 @@ int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStrea
 
 int launch_seg_nodes(const NodeArgs& a, int BH, hipStream_t s) {
   if (a.nseg < 2) return LL_OK;
-  hipLaunchKernelGGL(seg_node_kernel, dim3((a.E + 255) / 256, a.nseg - 1, BH), dim3(256), 0, s, a);
+  if (a.E % 4 != 0) return LL_ERR_UNSUPPORTED;  // E = dv * DKP, DKP a multiple of 32
+  hipLaunchKernelGGL(seg_node_kernel, dim3((a.E / 4 + 255) / 256, a.nseg - 1, BH), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 

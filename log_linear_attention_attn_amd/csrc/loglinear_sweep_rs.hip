@@ -660,7 +660,8 @@ fwd_rs_kernel(FwdArgs a) {
 // workgroup per (b,h, segment, 64 dv columns); the segment is walked in
 // 64-token tiles.  Each tile's V is scaled by the decay to the tile's end and
 // split bf16 hi/lo once, at staging; K and V stay row-major in LDS (double
-// buffered, one barrier per tile) and are read transposed.  Wave w keeps the
+// buffered, one barrier per tile, loads issued two tiles ahead) and are read
+// transposed.  Wave w keeps the
 // 64 x 16 block (dk half w>>2, columns 16(w&3)) of the running sum, which is
 // rescaled by each tile's total decay.  Workgroups of the same (b,h, segment)
 // sit on the same XCD so the second column group finds K in L2.
@@ -696,41 +697,43 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
   const rsrc_t vr = make_rsrc(static_cast<const bf16*>(a.v) + bhT * dv, T * dv * 2);
   const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
 
-  // register prefetch of one 64-token tile; tokens at or past s1 read zero
-  bf16x8 pk[2], pv;
-  float pla;
-  auto prefetch = [&](int b0) {
-    pla = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+  // Register prefetch two tiles ahead: tiles alternate between two register
+  // sets (and the two LDS buffers); tokens at or past s1 read zero.
+  struct Regs {
+    bf16x8 k[2], v;
+    float la;
+  };
+  auto prefetch = [&](Regs& r, int b0) {
+    r.la = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
         lar, b0 + lane < s1 ? (b0 + lane) * 4 : kOutOfRange, 0, 0));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + ss::NTH * i, row = v >> 4, col = (v & 15) * 8;
       const bool ok = b0 + row < s1 && col < dk;
-      pk[i] = load_b128(kr, ok ? ((b0 + row) * dk + col) * 2 : kOutOfRange);
+      r.k[i] = load_b128(kr, ok ? ((b0 + row) * dk + col) * 2 : kOutOfRange);
     }
     const int row = tid >> 3;
-    pv = load_b128(vr, b0 + row < s1 ? ((b0 + row) * dv + dv0 + (tid & 7) * 8) * 2 : kOutOfRange);
+    r.v = load_b128(vr, b0 + row < s1 ? ((b0 + row) * dv + dv0 + (tid & 7) * 8) * 2 : kOutOfRange);
   };
 
   f32x4 S[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float Aseg = 0.f;
-  prefetch(s0);
-  int buf = 0;
-  for (int b0 = s0; b0 < s1; b0 += C, buf ^= 1) {
+  // one 64-token tile from register set r into LDS buffer buf, then its MFMAs
+  auto tile = [&](Regs& r, int buf, int b0) {
     unsigned char* base = smem + buf * ss::BUF;
     bf16* Ks = reinterpret_cast<bf16*>(base + ss::KS_OFF);
     bf16* Vh = reinterpret_cast<bf16*>(base + ss::VH_OFF);
     bf16* Vl = reinterpret_cast<bf16*>(base + ss::VL_OFF);
     // decay of each token to the tile's last token, every wave redundantly
-    const float cl = wave_prefix_sum(pla);
+    const float cl = wave_prefix_sum(r.la);
     const float Ab = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63));
     const float esf = __expf(Ab - cl);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + ss::NTH * i, row = v >> 4, col = (v & 15) * 8;
-      *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
+      *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = r.k[i];
     }
     {
       const int row = tid >> 3, col = (tid & 7) * 8;
@@ -739,21 +742,21 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         bf16 x1, x2;
-        split_bf16(static_cast<float>(pv[j]) * e, x1, x2);
+        split_bf16(static_cast<float>(r.v[j]) * e, x1, x2);
         h[j] = x1;
         l[j] = x2;
       }
       *reinterpret_cast<bf16x8*>(Vh + row * LDV + col) = h;
       *reinterpret_cast<bf16x8*>(Vl + row * LDV + col) = l;
     }
-    if (b0 + C < s1) prefetch(b0 + C);
+    if (b0 + 2 * C < s1) prefetch(r, b0 + 2 * C);
     __syncthreads();
 
     const float fa = __expf(Ab);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[t][r] *= fa;
+      for (int q = 0; q < 4; ++q) S[t][q] *= fa;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int vrow = (32 * ks + 8 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
@@ -769,6 +772,13 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
       }
     }
     Aseg += Ab;
+  };
+  Regs ra, rb;
+  prefetch(ra, s0);
+  if (s0 + C < s1) prefetch(rb, s0 + C);
+  for (int b0 = s0; b0 < s1; b0 += 2 * C) {
+    tile(ra, 0, b0);
+    if (b0 + C < s1) tile(rb, 1, b0 + C);
   }
   // element r of S[t] is dk 64hh + 32(t>>1) + 8g4 + 4(t&1) + r, column c0 + li
   float* __restrict__ Tout =
