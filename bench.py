@@ -220,7 +220,7 @@ def main():
         "wall_ms_per_step": wall / K * 1e3,
         "roofline": {
             "kernel": "fwd_rs_kernel" if (w.dtype == "bf16" and w.C == 64 and w.dk > 64 and w.dv % 64 == 0
-                                          and -(-w.T // 64) <= 256) else "fwd_sweep_kernel",
+                                          and -(-w.T // 64) <= 1024) else "fwd_sweep_kernel",
             "bound": "hbm",
             "achieved": sweep_gbs,
             "peak": PEAK_HBM_GBS,

@@ -26,13 +26,20 @@ struct FwdPlan {
 };
 
 // Chunks per segment: as large as possible (fewer segment states, less
-// prologue traffic) while still giving the sweep at least ~2048 workgroups
-// (8 per CU on 256 CUs), capped at 16 chunks.
-int auto_seg_log2(long long BH, int D, int N) {
-  int s = 4;
+// prologue traffic) while still giving the sweep enough workgroups: for the
+// shapes the register-state sweep covers (64 dv columns per workgroup, one
+// workgroup per CU at a time) at least 256 workgroups, up to 64 chunks per
+// segment; otherwise (16 dv columns per workgroup) at least 2048, up to 16
+// chunks.  Depends on shapes only, so the workspace size is known without the
+// dtype.
+int auto_seg_log2(long long BH, int dk, int dv, int C, int N) {
+  const bool rs_shape = C == 64 && dk > 64 && dv % 64 == 0 && N <= 1024;
+  const long long per_seg = rs_shape ? BH * (dv / 64) : BH * (dv / 16);
+  const long long want = rs_shape ? 256 : 2048;
+  int s = rs_shape ? 6 : 4;
   while (s > 0) {
     const long long nseg = (N + (1LL << s) - 1) >> s;
-    if (BH * D * nseg >= 2048) break;
+    if (per_seg * nseg >= want) break;
     --s;
   }
   return s;
@@ -52,7 +59,7 @@ int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* 
   p->L = T > 0 ? bit_length(T - 1) + 1 : 0;
   p->DKP = dk <= 32 ? 32 : (dk <= 64 ? 64 : 128);
   p->nslot = p->N > 1 ? bit_length(p->N - 1) : 0;
-  p->seg_log2 = seg_log2 >= 0 ? seg_log2 : auto_seg_log2(p->BH, dv / 16, p->N);
+  p->seg_log2 = seg_log2 >= 0 ? seg_log2 : auto_seg_log2(p->BH, dk, dv, C, p->N);
   p->nseg = p->N > 0 ? (p->N + (1 << p->seg_log2) - 1) >> p->seg_log2 : 0;
   if (p->nseg > 1) {
     const size_t elems = (size_t)p->BH * p->nseg * dv * p->DKP;
@@ -84,7 +91,7 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   // dv a multiple of 64 and at most rs_max_slots() chunk-level Fenwick bits;
   // the LDS-state kernel covers everything else.
   const bool rs_ok = dtype == LL_BF16 && C == 64 && dk > 64 && dv % 64 == 0 &&
-                     p.nslot <= ll::rs_max_slots() && p.L <= 16 &&
+                     p.nslot <= ll::rs_max_slots() && p.L <= 17 &&
                      ll::rs_lds_bytes(p.L, p.nslot) <= ll::kMaxLds;
   if (kernel < LL_KERNEL_AUTO || kernel > LL_KERNEL_REGISTER_STATE) return LL_ERR_SHAPE;
   if (kernel == LL_KERNEL_REGISTER_STATE && !rs_ok) return LL_ERR_UNSUPPORTED;

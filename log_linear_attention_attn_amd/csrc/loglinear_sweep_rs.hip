@@ -54,13 +54,16 @@ constexpr int XC_BYTES = 8 * 2 * 64 * 16;
 constexpr int CL_OFF = XC_OFF + XC_BYTES;        // [2] x (cl[64], esf[64]) fp32
 constexpr int QM_OFF = CL_OFF + 2 * 2 * C * 4;   // per-wave max |q| [8] (padded to 64 B)
 constexpr int QH_OFF = QM_OFF + 64;              // fp16 copy of Q, [64][LDQ]
-constexpr int LW_OFF = QH_OFF + C * LDQ * 2;     // per-wave Q.G row weights [8][8 levels][64]
-constexpr int LAM_OFF = LW_OFF + 8 * 8 * C * 4;  // lambda of the chunk [64][L], + 16 words of slack
+constexpr int LW_OFF = QH_OFF + C * LDQ * 2;     // per-wave Q.G row weights [8][NSLOT levels][64]
+// lambda of the chunk [64][L] (+ 16 words of slack) follows the row weights
+__host__ __device__ constexpr int lam_off(int nsl) { return LW_OFF + 8 * nsl * C * 4; }
+// register slots of a kernel instantiation for nslot chunk-level bits
+__host__ __device__ constexpr int nsl_for(int nslot) { return nslot <= 8 ? 8 : 10; }
 
 // Rows past T of a ragged last chunk look up levels up to log2(C), and the
-// row weights read all eight inter-chunk levels, which a short sequence's
-// lambda may lack; the slack keeps those (discarded) reads in bounds.
-__host__ __device__ inline int lds_bytes(int L, int nslot) { (void)nslot; return LAM_OFF + (C * L + 16) * 4; }
+// row weights read all inter-chunk levels of the instantiation, which a short
+// sequence's lambda may lack; the slack keeps those (discarded) reads in bounds.
+__host__ __device__ inline int lds_bytes(int L, int nslot) { return lam_off(nsl_for(nslot)) + (C * L + 16) * 4; }
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
 typedef unsigned short __attribute__((ext_vector_type(2))) u16x2;
@@ -136,6 +139,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 2^x on the transcendental unit (v_exp_f32)
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A wave-uniform float kept in a scalar register (readfirstlane), so per-level
+// bookkeeping does not occupy vector registers.
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 __device__ __forceinline__ float exp2_int(int e) { return __uint_as_float(static_cast<unsigned>(e + 127) << 23); }
 
 // Raw buffer resource over [base, base + bytes): loads beyond the range return
@@ -170,7 +179,7 @@ fwd_rs_kernel(FwdArgs a) {
   bf16x8* Ps = reinterpret_cast<bf16x8*>(smem + PS_OFF);  // [mi][ks][hl][lane]
   f32x4* Xc = reinterpret_cast<f32x4*>(smem + XC_OFF);    // [wave][2][lane]
   float* qmax_s = reinterpret_cast<float*>(smem + QM_OFF);
-  float* lam_s = reinterpret_cast<float*>(smem + LAM_OFF);
+  float* lam_s = reinterpret_cast<float*>(smem + lam_off(NSLOT));
 
   const int D = a.dv >> 6;  // 64-column groups
   const int id = blockIdx.x;
@@ -245,13 +254,13 @@ fwd_rs_kernel(FwdArgs a) {
       eg[b] = e2;
       float d = 0.f;
       for (int r = gc; r < seg; ++r) d += a.seg_decay[bh * a.nseg + r];
-      dec[b] = d;
+      dec[b] = uniform(d);
     }
   }
 
   // ---- register prefetch of one chunk ----------------------------------
   bf16x8 pq[2], pk[2], pv;
-  float plam[2];
+  float plam[3];  // lambda words 2*tid, 2*tid+1 and, for L > 16, 1024+tid of the chunk
   float pla;
   // per-thread parts of the chunk loads' offsets; columns past dk (padded
   // head dim) get an out-of-range offset and read zero
@@ -271,6 +280,7 @@ fwd_rs_kernel(FwdArgs a) {
       const auto x = __builtin_amdgcn_raw_buffer_load_b64(lamr, (tok0 * L + 2 * tid) * 4, 0, 0);
       plam[0] = __uint_as_float(x[0]);
       plam[1] = __uint_as_float(x[1]);
+      if (NSLOT > 8) plam[2] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lamr, (tok0 * L + 1024 + tid) * 4, 0, 0));
     }
     pla = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lar, (tok0 + lane) * 4, 0, 0));
     const uint32_t cq = tok0 * dk * 2;
@@ -295,7 +305,7 @@ fwd_rs_kernel(FwdArgs a) {
   }
   f32x4 O0, O1;      // this wave's two output row tiles, written after the next barrier
   float Aprev = 0.f;  // total log decay of the previous chunk
-  float* lw = reinterpret_cast<float*>(smem + LW_OFF) + w * (8 * C);  // this wave's row weights
+  float* lw = reinterpret_cast<float*>(smem + LW_OFF) + w * (NSLOT * C);  // this wave's row weights
   for (int n = n0; n < n1; ++n) {
     const int tok0 = n * C, par = n & 1;
     bf16* Ks = reinterpret_cast<bf16*>(smem + KS_OFF) + par * (C * LDQ);
@@ -328,6 +338,7 @@ fwd_rs_kernel(FwdArgs a) {
       lam_s[tid * 2] = plam[0];
       lam_s[tid * 2 + 1] = plam[1];
     }
+    if (NSLOT > 8 && 1024 + tid < C * L) lam_s[1024 + tid] = plam[2];
     // in-chunk decay sums, every wave: cl = inclusive prefix of log_a (lane =
     // token); the decay from a token to the chunk's last token is Atot - cl
     const float cl = wave_prefix_sum(pla);
@@ -524,7 +535,7 @@ fwd_rs_kernel(FwdArgs a) {
         eg[0] = em;
         dec[0] = 0.f;
 #pragma unroll
-        for (int b = 1; b < NSLOT; ++b) dec[b] += Atot;
+        for (int b = 1; b < NSLOT; ++b) dec[b] = uniform(dec[b] + Atot);
       } else {
 #pragma unroll
         for (int b = 1; b < NSLOT; ++b) {
@@ -533,7 +544,7 @@ fwd_rs_kernel(FwdArgs a) {
             G[b][1] = gn[1];
             eg[b] = em;
           }
-          dec[b] = b == m ? 0.f : (b > m ? dec[b] + Atot : dec[b]);
+          dec[b] = uniform(b == m ? 0.f : (b > m ? dec[b] + Atot : dec[b]));
         }
       }
     }
@@ -805,22 +816,31 @@ int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
-int rs_max_slots() { return 8; }
+int rs_max_slots() { return 10; }
 
 int rs_lds_bytes(int L, int nslot) { return rs::lds_bytes(L, nslot); }
 
 int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t stream) {
   const int bytes = rs::lds_bytes(a.L, a.nslot);
-  if (a.nslot > 8 || bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
+  if (a.nslot > 10 || a.L > 24 || bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
   // buffer offsets are 32-bit: every per-(b,h) slice, tail chunk included,
   // must stay below 2^31 bytes
   const size_t row_bytes = std::max({(size_t)a.dk * 2, (size_t)a.dv * 4, (size_t)a.L * 4});
   if ((size_t)(a.T + 2 * rs::C) * row_bytes >= (size_t)1 << 31) return LL_ERR_UNSUPPORTED;
-  const void* fn = a.st_out ? reinterpret_cast<const void*>(&fwd_rs_kernel<8, true>)
-                            : reinterpret_cast<const void*>(&fwd_rs_kernel<8, false>);
+  // instantiations: 8 register slots (up to 256 chunks) or 10 (up to 1024);
+  // EMIT adds the prefill state output
+  const bool wide = a.nslot > 8;
+  const void* fn = wide ? (a.st_out ? reinterpret_cast<const void*>(&fwd_rs_kernel<10, true>)
+                                    : reinterpret_cast<const void*>(&fwd_rs_kernel<10, false>))
+                        : (a.st_out ? reinterpret_cast<const void*>(&fwd_rs_kernel<8, true>)
+                                    : reinterpret_cast<const void*>(&fwd_rs_kernel<8, false>));
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
     return LL_ERR_HIP;
-  if (a.st_out)
+  if (wide && a.st_out)
+    hipLaunchKernelGGL((fwd_rs_kernel<10, true>), dim3(nblocks), dim3(512), bytes, stream, a);
+  else if (wide)
+    hipLaunchKernelGGL((fwd_rs_kernel<10, false>), dim3(nblocks), dim3(512), bytes, stream, a);
+  else if (a.st_out)
     hipLaunchKernelGGL((fwd_rs_kernel<8, true>), dim3(nblocks), dim3(512), bytes, stream, a);
   else
     hipLaunchKernelGGL((fwd_rs_kernel<8, false>), dim3(nblocks), dim3(512), bytes, stream, a);

@@ -188,6 +188,7 @@ RS_CASES = [
     (1, 2, 1000, 96, 64, "strong", 0),   # dk padded to 128
     (1, 1, 3000, 128, 192, "none", 3),   # three 64-column groups
     (1, 1, 4096, 128, 64, "weak", 4),
+    (1, 1, 20000, 128, 64, "weak", 3),   # 313 chunks: the ten-slot instantiation
 ]
 
 
