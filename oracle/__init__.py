@@ -1,5 +1,6 @@
 """CPU oracle (test infrastructure only; never imported by the product path)."""
 from .loglinear_oracle import (  # noqa: F401
+    backward,
     decode_step,
     fenwick_buckets,
     forward,

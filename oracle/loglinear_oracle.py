@@ -272,3 +272,42 @@ def states_at(k, v, log_a, t: int, L: int) -> np.ndarray:
         w = np.exp(cum[:, :, t:t + 1] - cum[:, :, lo:hi])          # [B, H, n]
         S[:, :, level] = np.einsum("bhs,bhsd,bhse->bhde", w, k[:, :, lo:hi], v[:, :, lo:hi])
     return S
+
+
+# --------------------------------------------------------------------------
+# Backward (gradients of the forward)
+# --------------------------------------------------------------------------
+
+def backward(q, k, v, log_a, lam, dout):
+    """Gradients of sum(out * dout) with respect to q, k, v, log_a and lambda.
+
+    Reverse-mode differentiation (torch autograd, fp64, CPU) of the dense
+    definition O = ((Q K^T) ⊙ M^S ⊙ M^H) V, one (b, h) at a time, with M^H and
+    M^S exactly as in ``mask_rows`` ([P1] 并行形式, 与已有模型的组合).
+    Returns (dq, dk, dv, dlog_a, dlam) as float64 arrays shaped like the inputs.
+    """
+    import torch
+
+    q, k, v, log_a, lam, dout = (_f64(x) for x in (q, k, v, log_a, lam, dout))
+    B, H, T, dk = q.shape
+    L = int(T - 1).bit_length() + 1
+    if lam.shape[-1] != L:
+        raise ValueError(f"lambda has {lam.shape[-1]} levels, expected {L}")
+    lev = torch.from_numpy(level_matrix(T).astype(np.int64))
+    causal = lev >= 0
+    idx = lev.clamp(min=0)
+    grads = [np.zeros_like(x) for x in (q, k, v, log_a, lam)]
+    for b in range(B):
+        for h in range(H):
+            ts = [torch.tensor(x[b, h], dtype=torch.float64, requires_grad=True)
+                  for x in (q, k, v, log_a, lam)]
+            tq, tk, tv, tla, tlam = ts
+            cum = torch.cumsum(tla, 0)
+            diff = torch.where(causal, cum[:, None] - cum[None, :], torch.zeros((), dtype=torch.float64))
+            ms = torch.where(causal, torch.exp(diff), torch.zeros((), dtype=torch.float64))
+            mh = torch.where(causal, torch.gather(tlam, 1, idx), torch.zeros((), dtype=torch.float64))
+            out = ((tq @ tk.T) * mh * ms) @ tv
+            (out * torch.from_numpy(dout[b, h])).sum().backward()
+            for g, t in zip(grads, ts):
+                g[b, h] = t.grad.numpy()
+    return tuple(grads)

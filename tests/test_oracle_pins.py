@@ -348,3 +348,74 @@ def test_states_at_zero_pattern():
         np.testing.assert_allclose(S[0], np.outer(k[0, 0, t], v[0, 0, t]))
         for l in range(1, L):
             assert (np.abs(S[l]).max() > 0) == bool((t >> (l - 1)) & 1), (t, l)
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(q, k, v, la, lam, dout):
+    return float(np.sum(oracle.forward(q, k, v, la, lam) * dout))
+
+
+def test_backward_matches_finite_differences():
+    """Every gradient entry against central differences of the (NumPy) forward."""
+    rng = np.random.default_rng(17)
+    q, k, v, la, lam = _rand_inputs(rng, 1, 1, 9, 3, 2, decay=0.4)
+    dout = rng.standard_normal((1, 1, 9, 2))
+    grads = oracle.backward(q, k, v, la, lam, dout)
+    eps = 1e-6
+    for x, g in zip((q, k, v, la, lam), grads):
+        num = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            old = x[i]
+            x[i] = old + eps
+            fp = _loss(q, k, v, la, lam, dout)
+            x[i] = old - eps
+            fm = _loss(q, k, v, la, lam, dout)
+            x[i] = old
+            num[i] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_backward_causal_linear_attention_closed_form():
+    """lambda = 1, no decay: out = tril(Q K^T) V, whose gradients are the
+    textbook products (dV = S^T dO, dQ = tril(dO V^T) K, dK = tril(dO V^T)^T Q)."""
+    rng = np.random.default_rng(4)
+    T, dk, dv = 33, 5, 4
+    q, k, v, _, _ = _rand_inputs(rng, 1, 1, T, dk, dv)
+    la = np.zeros((1, 1, T))
+    lam = np.ones((1, 1, T, int(T - 1).bit_length() + 1))
+    dout = rng.standard_normal((1, 1, T, dv))
+    dq, dk_, dv_, _, _ = oracle.backward(q, k, v, la, lam, dout)
+    Q, K, V, dO = q[0, 0], k[0, 0], v[0, 0], dout[0, 0]
+    S = np.tril(Q @ K.T)
+    G = np.tril(dO @ V.T)
+    np.testing.assert_allclose(dv_[0, 0], S.T @ dO, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dq[0, 0], G @ K, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dk_[0, 0], G.T @ Q, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_decay_gradient_identity():
+    """d log_a[r] = sum_{t >= r} (dO_t . O_t - v_t . dV_t): the decay of token r
+    sits in exactly the pairs s < r <= t (reverse prefix sum of row minus column
+    sums of dM ⊙ M)."""
+    rng = np.random.default_rng(8)
+    q, k, v, la, lam = _rand_inputs(rng, 2, 1, 40, 4, 3, decay=0.5)
+    dout = rng.standard_normal((2, 1, 40, 3))
+    _, _, dv_, dla, _ = oracle.backward(q, k, v, la, lam, dout)
+    out = oracle.forward(q, k, v, la, lam)
+    dc = np.sum(dout * out, -1) - np.sum(v * dv_, -1)
+    want = np.flip(np.cumsum(np.flip(dc, -1), -1), -1)
+    np.testing.assert_allclose(dla, want, rtol=1e-10, atol=1e-11)
+
+
+def test_backward_lambda_gradient_euler_identity():
+    """out is linear in lambda, so sum_l lambda[t,l] dlam[t,l] = dO_t . O_t."""
+    rng = np.random.default_rng(12)
+    q, k, v, la, lam = _rand_inputs(rng, 1, 2, 50, 4, 3, decay=0.2)
+    dout = rng.standard_normal((1, 2, 50, 3))
+    dlam = oracle.backward(q, k, v, la, lam, dout)[4]
+    out = oracle.forward(q, k, v, la, lam)
+    np.testing.assert_allclose(np.sum(lam * dlam, -1), np.sum(dout * out, -1), rtol=1e-10, atol=1e-11)
+    # entries of levels no pair reaches are exactly zero (row t uses levels <= bit_length(t))
+    for t in range(50):
+        assert not np.any(dlam[:, :, t, t.bit_length() + 1:])
