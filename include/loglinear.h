@@ -158,6 +158,35 @@ int loglinear_prefill_f32(const float* q, const float* k, const float* v, const 
                           const float* lambda, float* out, const loglinear_states* states,
                           int B, int H, int T, int dk, int dv, int C, void* stream);
 
+/*
+ * Backward: gradients of sum(out * dout) with respect to every input of
+ * loglinear_fwd (page above, sections 并行形式 and 与已有模型的组合 define the
+ * operator being differentiated; 训练：分块并行扫描算法 the chunking reused here).
+ *   q, k, v, log_a, lambda : the forward's inputs (bf16 q, k, v)
+ *   out    : [B, H, T, dv] fp32, the forward's output for these inputs
+ *   dout   : [B, H, T, dv] fp32, gradient with respect to out
+ *   grad_q, grad_k : [B, H, T, dk] fp32;  grad_v : [B, H, T, dv] fp32
+ *   grad_log_a : [B, H, T] fp32;  grad_lambda : [B, H, T, L] fp32
+ * All outputs are written completely (grad_lambda is 0 for levels a row never
+ * reaches).  Sizes and C as loglinear_fwd; additionally at most 4096 chunks,
+ * and the staging and per-level states of one workgroup must fit in LDS (bf16
+ * with C = 64 and dk = dv = 128: up to 1024 chunks), else LL_ERR_UNSUPPORTED.
+ * Scratch (per-slice partial sums of grad_lambda, (dk/16) * B * H * T *
+ * bit_length(N-1) floats) is allocated stream-ordered on `stream`.
+ * Arithmetic: fp32 matrix-core instructions throughout; no atomics, so the
+ * results are deterministic.
+ */
+int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_a,
+                  const float* lambda, const float* out, const float* dout, float* grad_q,
+                  float* grad_k, float* grad_v, float* grad_log_a, float* grad_lambda, int B,
+                  int H, int T, int dk, int dv, int C, void* stream);
+
+/* Same as loglinear_bwd with fp32 q, k, v. */
+int loglinear_bwd_f32(const float* q, const float* k, const float* v, const float* log_a,
+                      const float* lambda, const float* out, const float* dout, float* grad_q,
+                      float* grad_k, float* grad_v, float* grad_log_a, float* grad_lambda, int B,
+                      int H, int T, int dk, int dv, int C, void* stream);
+
 /* Workspace bytes loglinear_fwd_ex needs for these sizes (0 if none); seg_log2
  * as in loglinear_fwd_opts.  Returns (size_t)-1 for invalid sizes. */
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2);

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI in include/loglinear.h):
     fwd(q, k, v, log_a, lam, C=64, out=None)            bf16 or fp32 q/k/v
     fwd_ex(..., seg_log2=-1, workspace=None)            explicit options
     prefill(q, k, v, log_a, lam, C=64, L=None)          forward + decode states at T-1
+    bwd(q, k, v, log_a, lam, out, dout, C=64)           gradients of sum(out * dout)
     fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1)
     decode_step(states, q, k, v, log_a, lam, t, out=None)
     level_table(T, device=None)                          int8 [T, T]
@@ -22,7 +23,7 @@ import os
 import torch
 
 __all__ = [
-    "LogLinearError", "lib", "library_path", "num_levels", "fwd", "fwd_ex", "prefill",
+    "LogLinearError", "lib", "library_path", "num_levels", "fwd", "fwd_ex", "prefill", "bwd",
     "fwd_workspace_size", "decode_step", "level_table", "strerror",
 ]
 
@@ -33,7 +34,8 @@ _lib = None
 LL_BF16, LL_F32 = 0, 1
 EXPORTED_SYMBOLS = (
     "loglinear_num_levels", "loglinear_fwd", "loglinear_fwd_f32", "loglinear_fwd_ex",
-    "loglinear_prefill", "loglinear_prefill_f32", "loglinear_fwd_workspace_size",
+    "loglinear_prefill", "loglinear_prefill_f32", "loglinear_bwd", "loglinear_bwd_f32",
+    "loglinear_fwd_workspace_size",
     "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_level_table",
     "loglinear_strerror",
 )
@@ -85,6 +87,11 @@ def lib():
     L.loglinear_prefill.restype = i
     L.loglinear_prefill_f32.argtypes = pre_args
     L.loglinear_prefill_f32.restype = i
+    bwd_args = [vp] * 12 + [i, i, i, i, i, i, vp]
+    L.loglinear_bwd.argtypes = bwd_args
+    L.loglinear_bwd.restype = i
+    L.loglinear_bwd_f32.argtypes = bwd_args
+    L.loglinear_bwd_f32.restype = i
     L.loglinear_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     L.loglinear_fwd_workspace_size.restype = sz
     dec_args = [ctypes.POINTER(_States), vp, vp, vp, vp, vp, vp, vp, vp]
@@ -256,6 +263,38 @@ def prefill(q, k, v, log_a, lam, C: int = 64, L: int | None = None, out=None, st
            B, H, T, dk, dv, int(C), _stream(dev))
     _raise(st, "loglinear_prefill")
     return out, states
+
+
+def bwd(q, k, v, log_a, lam, out, dout, C: int = 64):
+    """Gradients of sum(out * dout) with respect to q, k, v, log_a and lam
+    (loglinear_bwd / loglinear_bwd_f32); out is the forward's output.
+
+    Returns (dq, dk, dv, dlog_a, dlam), all fp32, shaped like the inputs.
+    """
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T) if T > 0 else 0
+    _check_dev("q", q, q.dtype, (B, H, T, dk), dev)
+    _check_dev("k", k, q.dtype, (B, H, T, dk), dev)
+    _check_dev("v", v, q.dtype, (B, H, T, dv), dev)
+    _check_dev("log_a", log_a, torch.float32, (B, H, T), dev)
+    _check_dev("lam", lam, torch.float32, (B, H, T, L), dev)
+    _check_dev("out", out, torch.float32, (B, H, T, dv), dev)
+    _check_dev("dout", dout, torch.float32, (B, H, T, dv), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    gq, gk = torch.empty((B, H, T, dk), **f32), torch.empty((B, H, T, dk), **f32)
+    gv = torch.empty((B, H, T, dv), **f32)
+    gla, glam = torch.empty((B, H, T), **f32), torch.empty((B, H, T, L), **f32)
+    f = lib().loglinear_bwd if q.dtype == torch.bfloat16 else lib().loglinear_bwd_f32
+    st = f(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out), _ptr(dout), _ptr(gq), _ptr(gk),
+           _ptr(gv), _ptr(gla), _ptr(glam), B, H, T, dk, dv, int(C), _stream(dev))
+    _raise(st, "loglinear_bwd")
+    return gq, gk, gv, gla, glam
 
 
 def decode_step(states, q, k, v, log_a, lam, t, out=None):

@@ -38,6 +38,24 @@ struct HandoffArgs {
   int BH, T, dk, dv, C, st_L;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_a;
+  const float* lam;
+  const float* out;    // forward output (for the decay gradient)
+  const float* dout;   // gradient of the loss with respect to out
+  float* dq;           // [BH][T][dk]
+  float* dk_out;       // [BH][T][dk]
+  float* dvo;          // [BH][T][dv]
+  float* dlog_a;       // [BH][T]
+  float* dlam;         // [BH][T][L]
+  float* dlam_part;    // [dk/16][BH][T][nslot] chunk-level dlam partial sums
+  int BH, T, dk, dv, L;
+  int nslot;           // chunk-level Fenwick bits = bit_length(N - 1)
+};
+
 struct SegArgs {
   const void* k;
   const void* v;
@@ -78,5 +96,7 @@ int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t s);
 int launch_level_table(signed char* lev, int T, hipStream_t s);
 int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
+int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot);
+int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s);
 
 }  // namespace ll

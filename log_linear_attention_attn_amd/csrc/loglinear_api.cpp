@@ -170,6 +170,30 @@ int run_decode(int dtype, const loglinear_states* s, const void* q, const void* 
   return ll::launch_decode(dtype, a, stream);
 }
 
+int run_bwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
+            const float* lambda, const float* out, const float* dout, float* dq, float* dk_out,
+            float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T, int dk, int dv, int C,
+            hipStream_t stream) {
+  FwdPlan p;
+  int st = plan_fwd(B, H, T, dk, dv, C, 0, &p);
+  if (st != LL_OK) return st;
+  if (B == 0 || H == 0 || T == 0) return LL_OK;
+  if (!q || !k || !v || !log_a || !lambda || !out || !dout || !dq || !dk_out || !dv_out || !dlog_a ||
+      !dlambda)
+    return LL_ERR_NULL;
+  if (p.nslot > 16 || p.N > 4096) return LL_ERR_UNSUPPORTED;
+  const int lds = ll::bwd_lds_bytes(dtype, C, dk, dv, p.L, p.N, p.nslot);
+  if (lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
+  const size_t part = (size_t)(dk / 16) * p.BH * T * (p.nslot > 0 ? p.nslot : 1) * sizeof(float);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, part, stream) != hipSuccess) return LL_ERR_HIP;
+  ll::BwdArgs a{q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda,
+                static_cast<float*>(ws), p.BH, T, dk, dv, p.L, p.nslot};
+  st = ll::launch_bwd(dtype, C, a, stream);
+  if (hipFreeAsync(ws, stream) != hipSuccess && st == LL_OK) st = LL_ERR_HIP;
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,6 +237,22 @@ int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* l
   return run_fwd(opts->dtype, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, opts->seg_log2,
                  opts->kernel, opts->workspace, opts->workspace_bytes, opts->phase_events,
                  opts->final_states, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_a,
+                  const float* lambda, const float* out, const float* dout, float* dq, float* dk_out,
+                  float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T, int dk, int dv,
+                  int C, void* stream) {
+  return run_bwd(LL_BF16, q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda, B, H, T,
+                 dk, dv, C, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_bwd_f32(const float* q, const float* k, const float* v, const float* log_a,
+                      const float* lambda, const float* out, const float* dout, float* dq,
+                      float* dk_out, float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T,
+                      int dk, int dv, int C, void* stream) {
+  return run_bwd(LL_F32, q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda, B, H, T,
+                 dk, dv, C, static_cast<hipStream_t>(stream));
 }
 
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2) {

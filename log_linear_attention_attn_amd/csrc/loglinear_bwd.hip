@@ -1,0 +1,625 @@
+// Backward of the log-linear attention forward: gradients of sum(out * dout)
+// with respect to q, k, v, log_a and lambda.
+//
+//   [P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制"
+//        sections 并行形式 (O = (QK^T ⊙ M^H) V), 与已有模型的组合 (⊙ M^S),
+//        训练：分块并行扫描算法 (chunk decomposition).
+//
+// With M[t,s] = lambda[t, l(t,s)] exp(cum_t - cum_s) for s <= t:
+//   dQ_t      = sum_{s<=t} M[t,s] (dO_t . v_s) k_s
+//   dK_s      = sum_{t>=s} M[t,s] (dO_t . v_s) q_t
+//   dV_s      = sum_{t>=s} M[t,s] (q_t . k_s) dO_t
+//   dlam[t,l] = sum_{s in bucket l of t} exp(cum_t - cum_s) (q_t . k_s)(dO_t . v_s)
+//   dlog_a[r] = sum_{t>=r} (dO_t . O_t - v_t . dV_t)
+// (the decay of token r sits in exactly the pairs s < r <= t, whose row sums
+// of dM ⊙ M are dO_t . O_t and column sums v_s . dV_s).
+//
+// Chunkwise, as the forward: pairs inside one C-token chunk (levels
+// <= log2 C) densely, and for chunk-level bit b the pairs between the left and
+// the right half of each aligned block of 2^(b+1) chunks (level log2C+1+b).
+// Unlike the forward's lssb merge, every level keeps its own state here,
+// because the backward's query-side states carry lambda of their level:
+//   bwd_dq_kernel   forward chunk order; per level the decayed left-half sum
+//                   St_b = sum v_s k_s^T, read by the right-half queries:
+//                   dQ, and the inter-chunk dlam as per-slice partial sums.
+//   bwd_kv_kernel   reverse chunk order; per level the right-half sum
+//                   R_b = sum lambda[t,l_b] w_t a_t c_t^T, read by the
+//                   left-half keys: dV (a = dO, c = q, x = k) or
+//                   dK (a = q, c = dO, x = v), y_s = sum R_b x_s.
+//   bwd_dlam_intra_kernel  dlam of the in-chunk levels.
+//   bwd_finish_kernel      sums the dlam partials, writes dlog_a.
+// Each output row slice of 16 columns belongs to one workgroup (no atomics).
+// All products run as fp32 matrix-core instructions (v_mfma_f32_16x16x4f32);
+// bf16 inputs are widened when staged.
+#include <hip/hip_runtime.h>
+
+#include "ll_device.h"
+#include "ll_internal.h"
+
+namespace ll {
+namespace bwd {
+
+using F = Frag<float>;
+
+template <int C>
+struct Lg;
+template <>
+struct Lg<16> { static constexpr int v = 4; };
+template <>
+struct Lg<32> { static constexpr int v = 5; };
+template <>
+struct Lg<64> { static constexpr int v = 6; };
+
+__host__ __device__ constexpr int al16(int x) { return (x + 15) & ~15; }
+
+template <typename IT>
+__device__ __forceinline__ float ldf(const IT* p) { return static_cast<float>(*p); }
+
+// sum over the 16 lanes of each row (DPP rotations and quad swaps)
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x = dpp_sum<0x128>(x);  // row_ror:8
+  x = dpp_sum<0x124>(x);  // row_ror:4
+  x = dpp_sum<0x4e>(x);   // quad_perm [2,3,0,1]
+  x = dpp_sum<0xb1>(x);   // quad_perm [1,0,3,2]
+  return x;
+}
+
+// Separation after a chain of fp32 matrix-core instructions whose result is
+// read past a branch: the scheduling barrier keeps the MFMAs above the nops,
+// which cover the read-after-write distance on every path.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 3");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// In-chunk decay sums of chunk n for one wave: lane i -> cl_i (inclusive
+// prefix of log_a over the chunk; tokens past T count 0), and the chunk total.
+// Kept in fp64 so that the differences cl_t - cl_s the masks exponentiate
+// carry no cancellation error from the large prefix values.
+template <int C>
+__device__ __forceinline__ double chunk_prefix(const float* lag, int tok0, int T, int lane, double* total) {
+  double la = (lane < C && tok0 + lane < T) ? (double)lag[tok0 + lane] : 0.0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(la, off);
+    if (lane >= off) la += y;
+  }
+  *total = __shfl(la, C - 1);
+  return la;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dq_kernel: one workgroup per (b,h, 16-column slice js of dk).
+// ---------------------------------------------------------------------------
+template <typename IT, int C>
+struct DqCfg {
+  static constexpr int NW = C / 16, NT = NW * 64;
+  __host__ __device__ static int ldd(int dv) { return dv + 4; }           // dO rows, states (fp32)
+  __host__ __device__ static int ldv(int dv) { return dv + (sizeof(IT) == 2 ? 8 : 4); }
+  static constexpr int LDKT = C + 4;                                       // K slice transposed [16][C]
+  static constexpr int LDQ = 17;                                           // Q slice [C][16]
+  __host__ __device__ static int off_v(int dv) { return al16(C * ldd(dv) * 4); }
+  __host__ __device__ static int off_kt(int dv) { return off_v(dv) + al16(C * ldv(dv) * (int)sizeof(IT)); }
+  __host__ __device__ static int off_q(int dv) { return off_kt(dv) + al16(16 * LDKT * 4); }
+  __host__ __device__ static int off_lam(int dv) { return off_q(dv) + al16(C * LDQ * 4); }
+  __host__ __device__ static int off_cl(int dv, int L) { return off_lam(dv) + al16(C * L * 4); }
+  __host__ __device__ static int off_dl(int dv, int L) { return off_cl(dv, L) + al16(2 * C * 8); }
+  __host__ __device__ static int off_st(int dv, int L) { return off_dl(dv, L) + 16 * 4; }
+  __host__ __device__ static int bytes(int dv, int L, int nslot) {
+    return off_st(dv, L) + (nslot > 0 ? nslot : 1) * 16 * ldd(dv) * 4;
+  }
+};
+
+template <typename IT, int C>
+__global__ void __launch_bounds__(C / 16 * 64) bwd_dq_kernel(BwdArgs a) {
+  using Cfg = DqCfg<IT, C>;
+  constexpr int NW = Cfg::NW, NT = Cfg::NT, LOGC = Lg<C>::v, LDKT = Cfg::LDKT, LDQ = Cfg::LDQ;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int dk = a.dk, dv = a.dv, T = a.T, L = a.L, nslot = a.nslot;
+  const int LDD = Cfg::ldd(dv), LDV = Cfg::ldv(dv);
+  float* dOs = reinterpret_cast<float*>(smem);
+  IT* Vs = reinterpret_cast<IT*>(smem + Cfg::off_v(dv));
+  float* KT = reinterpret_cast<float*>(smem + Cfg::off_kt(dv));
+  float* Qs = reinterpret_cast<float*>(smem + Cfg::off_q(dv));
+  float* lam_s = reinterpret_cast<float*>(smem + Cfg::off_lam(dv));
+  double* cl_s = reinterpret_cast<double*>(smem + Cfg::off_cl(dv, L));  // in-chunk prefix of log_a
+  float* esf_s = reinterpret_cast<float*>(cl_s + C);                      // decay to the chunk end
+  float* dlt_s = reinterpret_cast<float*>(smem + Cfg::off_dl(dv, L));  // per level, see below
+  float* St = reinterpret_cast<float*>(smem + Cfg::off_st(dv, L));
+
+  const int nsl = dk / 16;
+  const int bh = blockIdx.x / nsl, js = blockIdx.x - bh * nsl;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int N = (T + C - 1) / C;
+  const size_t bhT = (size_t)bh * T;
+  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + bhT * dk + 16 * js;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk + 16 * js;
+  const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
+  const float* __restrict__ dog = a.dout + bhT * dv;
+  const float* __restrict__ lag = a.log_a + bhT;
+  const float* __restrict__ lamg = a.lam + bhT * L;
+  float* __restrict__ dqg = a.dq + bhT * dk + 16 * js;
+  float* __restrict__ part = a.dlam_part + ((size_t)js * a.BH + bh) * T * (nslot > 0 ? nslot : 1);
+
+  // dlt_s[b]: for a level whose right half holds this chunk, the log decay
+  // from the level's reference (the last token of the left half) to the token
+  // before this chunk; kept by thread 0, read after the staging barrier.
+  float Aprev = 0.f;
+  for (int n = 0; n < N; ++n) {
+    const int tok0 = n * C;
+    double Atd;
+    const double cl = chunk_prefix<C>(lag, tok0, T, lane, &Atd);
+    const float Atot = static_cast<float>(Atd);
+    if (tid == 0)
+      for (int b = 0; b < nslot; ++b)
+        if ((n >> b) & 1) {
+          const int rs = ((n >> (b + 1)) << (b + 1)) + (1 << b);
+          dlt_s[b] = n == rs ? 0.f : dlt_s[b] + Aprev;
+        }
+    // ---- stage the chunk
+    for (int i = tid; i < C * dv; i += NT) {
+      const int r = i / dv, c = i - r * dv;
+      const bool ok = tok0 + r < T;
+      dOs[r * LDD + c] = ok ? dog[(size_t)(tok0 + r) * dv + c] : 0.f;
+      Vs[r * LDV + c] = ok ? vg[(size_t)(tok0 + r) * dv + c] : IT(0.f);
+    }
+    for (int i = tid; i < C * 16; i += NT) {
+      const int r = i >> 4, c = i & 15;
+      const bool ok = tok0 + r < T && 16 * js + c < dk;
+      KT[c * LDKT + r] = ok ? ldf(kg + (size_t)(tok0 + r) * dk + c) : 0.f;
+      Qs[r * LDQ + c] = ok ? ldf(qg + (size_t)(tok0 + r) * dk + c) : 0.f;
+    }
+    for (int i = tid; i < C * L; i += NT) lam_s[i] = tok0 + i / L < T ? lamg[(size_t)tok0 * L + i] : 0.f;
+    if (w == 0 && lane < C) {
+      cl_s[lane] = cl;
+      esf_s[lane] = __expf(static_cast<float>(Atd - cl));
+    }
+    __syncthreads();
+
+    // ---- intra chunk: dQ rows 16w.. from the masked S^T tiles (dO . v)
+    const int tq = 16 * w + li;  // query of this lane in the S^T tiles
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb <= w; ++kb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < dv; k0 += 4) {
+        const float av = static_cast<float>(Vs[(16 * kb + li) * LDV + k0 + g4]);
+        acc = F::mma(av, dOs[(16 * w + li) * LDD + k0 + g4], acc);
+      }
+      // acc[r] = dO_tq . v_s with s = 16kb + 4g4 + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * kb + 4 * g4 + r;
+        const float p =
+            s <= tq ? acc[r] * lam_s[tq * L + level_of(tq, s)] * __expf(static_cast<float>(cl_s[tq] - cl_s[s])) : 0.f;
+        O = F::mma(p, KT[li * LDKT + s], O);
+      }
+    }
+    mfma_drain();
+    // ---- inter chunk: one level per set bit b of n (right half of its block)
+    for (int b = 0; b < nslot; ++b) {
+      const bool right = (n >> b) & 1;
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (right) {
+        const float* stb = St + b * 16 * LDD;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < dv; k0 += 4) acc = F::mma(F::load(dOs, LDD, 16 * w, k0, lane), stb[li * LDD + k0 + g4], acc);
+        mfma_drain();
+        // acc[r] = (dO_t St_b)[j = li], t = 16w + 4g4 + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * w + 4 * g4 + r;
+          const float wt = __expf(static_cast<float>(cl_s[t] + dlt_s[b])) * acc[r];
+          O[r] += lam_s[t * L + LOGC + 1 + b] * wt;
+          x[r] = wt * Qs[t * LDQ + li];
+        }
+      }
+      // partial dlam of this slice (0 where the level has no bucket)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sx = row_sum16(x[r]);
+        const int t = tok0 + 16 * w + 4 * g4 + r;
+        if (li == 0 && t < T) part[(size_t)t * nslot + b] = sx;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tok0 + 16 * w + 4 * g4 + r;
+      if (t < T) dqg[(size_t)t * dk + li] = O[r];
+    }
+    // ---- key side: this chunk joins the left half of every level whose bit
+    // is clear and whose right half exists.  Disjoint from the levels read above.
+    for (int it = w; it < dv / 16; it += NW) {
+      const int i0 = 16 * it;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < C; k0 += 4) {
+        const int s = k0 + g4;
+        acc = F::mma(KT[li * LDKT + s], esf_s[s] * static_cast<float>(Vs[s * LDV + i0 + li]), acc);
+      }
+      mfma_drain();
+      // acc[r] = sum_s K[s][j] esf_s V[s][i], j = 4g4 + r, i = i0 + li
+      for (int b = 0; b < nslot; ++b) {
+        const int base = (n >> (b + 1)) << (b + 1);
+        if (((n >> b) & 1) || base + (1 << b) >= N) continue;
+        float* stb = St + b * 16 * LDD;
+        const float f = n == base ? 0.f : __expf(Atot);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* p = stb + (4 * g4 + r) * LDD + i0 + li;
+          *p = (n == base ? 0.f : *p * f) + acc[r];
+        }
+      }
+    }
+    Aprev = Atot;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_kv_kernel: y_s = sum_{t>=s} M[t,s] (c_t . x_s) a_t, one workgroup per
+// (b,h, 16-column slice js of a).  MODE 0: dV (a = dO, c = q, x = k);
+// MODE 1: dK (a = q, c = dO, x = v).  Reverse chunk order.
+// ---------------------------------------------------------------------------
+template <typename IT, int C, int MODE>
+struct KvCfg {
+  static constexpr int NW = C / 16, NT = NW * 64;
+  typedef typename std::conditional<MODE == 0, IT, float>::type CT;  // c: q (MODE 0) or dO
+  __host__ __device__ static int ldc(int dc) { return dc + (sizeof(CT) == 2 ? 8 : 4); }
+  __host__ __device__ static int ldx(int dc) { return dc + (sizeof(IT) == 2 ? 8 : 4); }
+  __host__ __device__ static int ldr(int dc) { return dc + 4; }
+  static constexpr int LDAT = C + 4;  // a slice transposed [16][C]
+  __host__ __device__ static int off_x(int dc) { return al16(C * ldc(dc) * (int)sizeof(CT)); }
+  __host__ __device__ static int off_at(int dc) { return off_x(dc) + al16(C * ldx(dc) * (int)sizeof(IT)); }
+  __host__ __device__ static int off_lam(int dc) { return off_at(dc) + al16(16 * LDAT * 4); }
+  __host__ __device__ static int off_cl(int dc, int L) { return off_lam(dc) + al16(C * L * 4); }
+  __host__ __device__ static int off_tot(int dc, int L) { return off_cl(dc, L) + al16(C * 8); }
+  __host__ __device__ static int off_dl(int dc, int L, int N) { return off_tot(dc, L) + al16(N * 4); }
+  __host__ __device__ static int off_r(int dc, int L, int N) { return off_dl(dc, L, N) + 2 * 16 * 4; }
+  __host__ __device__ static int bytes(int dc, int L, int N, int nslot) {
+    return off_r(dc, L, N) + (nslot > 0 ? nslot : 1) * 16 * ldr(dc) * 4;
+  }
+};
+
+template <typename IT, int C, int MODE>
+__global__ void __launch_bounds__(C / 16 * 64) bwd_kv_kernel(BwdArgs a) {
+  using Cfg = KvCfg<IT, C, MODE>;
+  using CT = typename Cfg::CT;
+  constexpr int NW = Cfg::NW, NT = Cfg::NT, LOGC = Lg<C>::v, LDAT = Cfg::LDAT;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int T = a.T, L = a.L, nslot = a.nslot;
+  const int da = MODE == 0 ? a.dv : a.dk;  // columns of a (and of the output)
+  const int dc = MODE == 0 ? a.dk : a.dv;  // contraction dim of c and x
+  const int LDC = Cfg::ldc(dc), LDX = Cfg::ldx(dc), LDR = Cfg::ldr(dc);
+  const int N = (T + C - 1) / C;
+  CT* Cs = reinterpret_cast<CT*>(smem);
+  IT* Xs = reinterpret_cast<IT*>(smem + Cfg::off_x(dc));
+  float* AT = reinterpret_cast<float*>(smem + Cfg::off_at(dc));
+  float* lam_s = reinterpret_cast<float*>(smem + Cfg::off_lam(dc));
+  double* cl_s = reinterpret_cast<double*>(smem + Cfg::off_cl(dc, L));
+  float* tot_s = reinterpret_cast<float*>(smem + Cfg::off_tot(dc, L));
+  float* dlt_s = reinterpret_cast<float*>(smem + Cfg::off_dl(dc, L, N));
+  float* gam_s = dlt_s + 16;
+  float* R = reinterpret_cast<float*>(smem + Cfg::off_r(dc, L, N));
+
+  const int nsl = da / 16;
+  const int bh = blockIdx.x / nsl, js = blockIdx.x - bh * nsl;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const size_t bhT = (size_t)bh * T;
+  const CT* __restrict__ cg = MODE == 0 ? reinterpret_cast<const CT*>(static_cast<const IT*>(a.q) + bhT * dc)
+                                        : reinterpret_cast<const CT*>(a.dout + bhT * dc);
+  const IT* __restrict__ xg = static_cast<const IT*>(MODE == 0 ? a.k : a.v) + bhT * dc;
+  const float* __restrict__ lag = a.log_a + bhT;
+  const float* __restrict__ lamg = a.lam + bhT * L;
+  float* __restrict__ yg = (MODE == 0 ? a.dvo : a.dk_out) + bhT * da + 16 * js;
+
+  // chunk totals of log_a, every chunk (reverse-order decay bookkeeping)
+  for (int nn = w; nn < N; nn += NW) {
+    double tot;
+    chunk_prefix<C>(lag, nn * C, T, lane, &tot);
+    if (lane == 0) tot_s[nn] = static_cast<float>(tot);
+  }
+  __syncthreads();
+
+  // Per level, kept by thread 0 and read after the staging barrier:
+  //   dlt_s[b] (chunk in the right half): log decay from the level's reference
+  //            (last token of the left half) to the token before this chunk;
+  //   gam_s[b] (chunk in the left half): log decay from this chunk's last
+  //            token to the reference.
+  for (int n = N - 1; n >= 0; --n) {
+    const int tok0 = n * C;
+    double Atd;
+    const double cl = chunk_prefix<C>(lag, tok0, T, lane, &Atd);
+    if (tid == 0)
+      for (int b = 0; b < nslot; ++b) {
+        const int base = (n >> (b + 1)) << (b + 1);
+        const int rs = base + (1 << b);               // first chunk of the right half
+        const int re = min(N, base + (1 << (b + 1))); // one past its last chunk
+        if ((n >> b) & 1) {
+          if (n == re - 1) {  // first visit of this right half
+            float d = 0.f;
+            for (int m = rs; m < n; ++m) d += tot_s[m];
+            dlt_s[b] = d;
+          } else {
+            dlt_s[b] -= tot_s[n];
+          }
+        } else if (rs < N) {
+          gam_s[b] = n == rs - 1 ? 0.f : gam_s[b] + tot_s[n + 1];
+        }
+      }
+    for (int i = tid; i < C * dc; i += NT) {
+      const int r = i / dc, c = i - r * dc;
+      const bool ok = tok0 + r < T;
+      Cs[r * LDC + c] = ok ? cg[(size_t)(tok0 + r) * dc + c] : CT(0.f);
+      Xs[r * LDX + c] = ok ? xg[(size_t)(tok0 + r) * dc + c] : IT(0.f);
+    }
+    for (int i = tid; i < C * 16; i += NT) {
+      const int r = i >> 4, c = i & 15;
+      const bool ok = tok0 + r < T && 16 * js + c < da;
+      float x = 0.f;
+      if (ok) {
+        if (MODE == 0) x = a.dout[(bhT + tok0 + r) * da + 16 * js + c];
+        else x = ldf(static_cast<const IT*>(a.q) + (bhT + tok0 + r) * da + 16 * js + c);
+      }
+      AT[c * LDAT + r] = x;
+    }
+    for (int i = tid; i < C * L; i += NT) lam_s[i] = tok0 + i / L < T ? lamg[(size_t)tok0 * L + i] : 0.f;
+    if (w == 0 && lane < C) cl_s[lane] = cl;
+    __syncthreads();
+
+    // ---- intra chunk: output rows s = 16w.. from the masked Z tiles (c . x)
+    const int s_l = 16 * w + li;  // key of this lane
+    f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+    for (int tb = w; tb < NW; ++tb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < dc; k0 += 4)
+        acc = F::mma(static_cast<float>(Cs[(16 * tb + li) * LDC + k0 + g4]),
+                     static_cast<float>(Xs[(16 * w + li) * LDX + k0 + g4]), acc);
+      // acc[r] = c_t . x_s with t = 16tb + 4g4 + r, s = s_l
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tb + 4 * g4 + r;
+        const float p = t >= s_l ? acc[r] * lam_s[t * L + level_of(t, s_l)] *
+                                         __expf(static_cast<float>(cl_s[t] - cl_s[s_l]))
+                                 : 0.f;
+        Y = F::mma(p, AT[li * LDAT + t], Y);
+      }
+    }
+    mfma_drain();
+    // ---- key side: levels whose bit is clear read the finished right-half state
+    for (int b = 0; b < nslot; ++b) {
+      const int base = (n >> (b + 1)) << (b + 1);
+      if (((n >> b) & 1) || base + (1 << b) >= N) continue;
+      const float* rb = R + b * 16 * LDR;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < dc; k0 += 4)
+        acc = F::mma(static_cast<float>(Xs[(16 * w + li) * LDX + k0 + g4]), rb[li * LDR + k0 + g4], acc);
+      mfma_drain();
+      // acc[r] = x_s . R_b[j = li], s = 16w + 4g4 + r; decay from s to the reference
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * w + 4 * g4 + r;
+        Y[r] += __expf(static_cast<float>(gam_s[b] + (Atd - cl_s[s]))) * acc[r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = tok0 + 16 * w + 4 * g4 + r;
+      if (s < T) yg[(size_t)s * da + li] = Y[r];
+    }
+    // ---- query side: levels whose bit is set add this chunk to their state
+    for (int it = w; it < dc / 16; it += NW) {
+      const int i0 = 16 * it;
+      for (int b = 0; b < nslot; ++b) {
+        if (!((n >> b) & 1)) continue;
+        const int base = (n >> (b + 1)) << (b + 1);
+        const int re = min(N, base + (1 << (b + 1)));
+        float* rb = R + b * 16 * LDR;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < C; k0 += 4) {
+          const int t = k0 + g4;
+          const float wq = lam_s[t * L + LOGC + 1 + b] * __expf(static_cast<float>(cl_s[t] + dlt_s[b]));
+          acc = F::mma(wq * AT[li * LDAT + t], static_cast<float>(Cs[t * LDC + i0 + li]), acc);
+        }
+        mfma_drain();
+        // acc[r] = sum_t w_t a_t[j] c_t[i], j = 4g4 + r, i = i0 + li
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* p = rb + (4 * g4 + r) * LDR + i0 + li;
+          *p = (n == re - 1 ? 0.f : *p) + acc[r];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dlam_intra_kernel: dlam of the levels 0..log2 C, one workgroup per
+// (b,h, chunk); wave w owns query rows 16w..
+// ---------------------------------------------------------------------------
+template <typename IT, int C>
+__global__ void __launch_bounds__(C / 16 * 64) bwd_dlam_intra_kernel(BwdArgs a) {
+  constexpr int NW = C / 16, LOGC = Lg<C>::v;
+  const int T = a.T, L = a.L, dk = a.dk, dv = a.dv;
+  const int N = (T + C - 1) / C;
+  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int tok0 = n * C;
+  const size_t bhT = (size_t)bh * T;
+  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + bhT * dk;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk;
+  const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
+  const float* __restrict__ dog = a.dout + bhT * dv;
+  __shared__ double cl_s[C];
+  double Atot;
+  const double cl = chunk_prefix<C>(a.log_a + bhT, tok0, T, lane, &Atot);
+  if (w == 0 && lane < C) cl_s[lane] = cl;
+  __syncthreads();
+  const int tq = 16 * w + li;
+  const bool qok = tok0 + tq < T;
+  float acc_l[LOGC + 1];
+#pragma unroll
+  for (int l = 0; l <= LOGC; ++l) acc_l[l] = 0.f;
+  for (int kb = 0; kb <= w; ++kb) {
+    const int s_row = 16 * kb + li;  // key row this lane loads for the A operands
+    const bool sok = tok0 + s_row < T;
+    f32x4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < dk; k0 += 4) {
+      const float ka = sok ? ldf(kg + (size_t)(tok0 + s_row) * dk + k0 + g4) : 0.f;
+      const float qb = qok ? ldf(qg + (size_t)(tok0 + tq) * dk + k0 + g4) : 0.f;
+      z1 = F::mma(ka, qb, z1);
+    }
+    for (int k0 = 0; k0 < dv; k0 += 4) {
+      const float va = sok ? ldf(vg + (size_t)(tok0 + s_row) * dv + k0 + g4) : 0.f;
+      const float db = qok ? dog[(size_t)(tok0 + tq) * dv + k0 + g4] : 0.f;
+      z2 = F::mma(va, db, z2);
+    }
+    mfma_drain();
+    // z1[r] = k_s . q_t, z2[r] = v_s . dO_t with s = 16kb + 4g4 + r, t = tq
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = 16 * kb + 4 * g4 + r;
+      if (s <= tq) {
+        const float x = z1[r] * z2[r] * __expf(static_cast<float>(cl_s[tq] - cl_s[s]));
+        const int lev = level_of(tq, s);
+#pragma unroll
+        for (int l = 0; l <= LOGC; ++l) acc_l[l] += l == lev ? x : 0.f;
+      }
+    }
+  }
+  // sum over the four lane groups (keys 4g4 + r) of each query
+  float* __restrict__ dl = a.dlam + (bhT + tok0 + tq) * L;
+#pragma unroll
+  for (int l = 0; l <= LOGC; ++l) {
+    float x = acc_l[l];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    if (g4 == 0 && qok && l < L) dl[l] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_finish_kernel: one workgroup (256 threads) per (b,h).  dlam of the
+// chunk levels from the per-slice partials; dlog_a as the reverse prefix sum
+// of dO_t . O_t - v_t . dV_t.
+// ---------------------------------------------------------------------------
+template <typename IT>
+__global__ void __launch_bounds__(256) bwd_finish_kernel(BwdArgs a, int logc, int nparts) {
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int T = a.T, L = a.L, dv = a.dv, nslot = a.nslot;
+  const size_t bhT = (size_t)bh * T;
+  for (int i = tid; i < T * (L - logc - 1 > 0 ? L - logc - 1 : 0); i += 256) {
+    const int nl = L - logc - 1;
+    const int t = i / nl, b = i - t * nl;
+    float x = 0.f;
+    if (b < nslot)
+      for (int p = 0; p < nparts; ++p) x += a.dlam_part[(((size_t)p * a.BH + bh) * T + t) * nslot + b];
+    a.dlam[(bhT + t) * L + logc + 1 + b] = x;
+  }
+  // reverse prefix sum over T: each thread owns a contiguous range.  The
+  // terms and the running sums are kept in fp64: the sum runs over up to T
+  // terms whose two parts largely cancel.
+  __shared__ double part[256];
+  const int per = (T + 255) / 256;
+  const int t0 = min(T, tid * per), t1 = min(T, t0 + per);
+  const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
+  auto dc = [&](int t) {
+    double x = 0.0;
+    for (int j = 0; j < dv; ++j)
+      x += (double)a.dout[(bhT + t) * dv + j] * a.out[(bhT + t) * dv + j] -
+           (double)ldf(vg + (size_t)t * dv + j) * a.dvo[(bhT + t) * dv + j];
+    return x;
+  };
+  double s = 0.0;
+  for (int t = t0; t < t1; ++t) s += dc(t);
+  part[tid] = s;
+  __syncthreads();
+  double run = 0.0;  // sum of the ranges of the threads above
+  for (int i = tid + 1; i < 256; ++i) run += part[i];
+  for (int t = t1 - 1; t >= t0; --t) {
+    run += dc(t);
+    a.dlog_a[bhT + t] = static_cast<float>(run);
+  }
+}
+
+}  // namespace bwd
+
+int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot) {
+  using namespace bwd;
+  auto pick = [&](auto tag_it) {
+    using IT = decltype(tag_it);
+    int q = 0, kv0 = 0, kv1 = 0;
+    switch (C) {
+      case 16: q = DqCfg<IT, 16>::bytes(dv, L, nslot); kv0 = KvCfg<IT, 16, 0>::bytes(dk, L, N, nslot);
+               kv1 = KvCfg<IT, 16, 1>::bytes(dv, L, N, nslot); break;
+      case 32: q = DqCfg<IT, 32>::bytes(dv, L, nslot); kv0 = KvCfg<IT, 32, 0>::bytes(dk, L, N, nslot);
+               kv1 = KvCfg<IT, 32, 1>::bytes(dv, L, N, nslot); break;
+      default: q = DqCfg<IT, 64>::bytes(dv, L, nslot); kv0 = KvCfg<IT, 64, 0>::bytes(dk, L, N, nslot);
+               kv1 = KvCfg<IT, 64, 1>::bytes(dv, L, N, nslot); break;
+    }
+    return max(q, max(kv0, kv1));
+  };
+  return dtype == LL_BF16 ? pick(bf16(0.f)) : pick(0.f);
+}
+
+template <typename IT, int C>
+static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  using namespace bwd;
+  const int N = (a.T + C - 1) / C;
+  constexpr int NT = C / 16 * 64;
+  // dQ and the chunk-level dlam partials
+  {
+    const int bytes = DqCfg<IT, C>::bytes(a.dv, a.L, a.nslot);
+    if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<IT, C>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return LL_ERR_HIP;
+    hipLaunchKernelGGL((bwd_dq_kernel<IT, C>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
+  }
+  // dV and dK
+  {
+    const int bytes = KvCfg<IT, C, 0>::bytes(a.dk, a.L, N, a.nslot);
+    if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv_kernel<IT, C, 0>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return LL_ERR_HIP;
+    hipLaunchKernelGGL((bwd_kv_kernel<IT, C, 0>), dim3(a.BH * (a.dv / 16)), dim3(NT), bytes, s, a);
+  }
+  {
+    const int bytes = KvCfg<IT, C, 1>::bytes(a.dv, a.L, N, a.nslot);
+    if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv_kernel<IT, C, 1>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return LL_ERR_HIP;
+    hipLaunchKernelGGL((bwd_kv_kernel<IT, C, 1>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
+  }
+  hipLaunchKernelGGL((bwd_dlam_intra_kernel<IT, C>), dim3(a.BH * N), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((bwd_finish_kernel<IT>), dim3(a.BH), dim3(256), 0, s, a, Lg<C>::v, a.dk / 16);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
+int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s) {
+  if (dtype == LL_BF16) {
+    switch (C) {
+      case 16: return launch_bwd_t<bf16, 16>(a, s);
+      case 32: return launch_bwd_t<bf16, 32>(a, s);
+      case 64: return launch_bwd_t<bf16, 64>(a, s);
+    }
+  } else {
+    switch (C) {
+      case 16: return launch_bwd_t<float, 16>(a, s);
+      case 32: return launch_bwd_t<float, 32>(a, s);
+      case 64: return launch_bwd_t<float, 64>(a, s);
+    }
+  }
+  return LL_ERR_UNSUPPORTED;
+}
+
+}  // namespace ll

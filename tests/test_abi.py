@@ -161,3 +161,15 @@ def test_prefill_argument_errors():
     bad = ll._States(0, 1, H, 8, dk, dv)
     opts = ll._FwdOpts(0, -1, 0, None, 0, None, ctypes.pointer(bad))
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, B, H, T, dk, dv, C, ctypes.byref(opts), None) == LL_ERR_SHAPE
+
+
+def test_bwd_argument_errors():
+    L = ll.lib()
+    p = ctypes.c_void_p(1)
+    args = [p] * 12
+    assert L.loglinear_bwd(*args, 1, 1, 64, 16, 16, 48, None) == LL_ERR_SHAPE       # C not a power of two
+    assert L.loglinear_bwd(*args, 1, 1, 64, 24, 16, 16, None) == LL_ERR_SHAPE       # dk not a multiple of 16
+    assert L.loglinear_bwd(*args, 1, 1, 16 * 5000, 16, 16, 16, None) == LL_ERR_UNSUPPORTED  # > 4096 chunks
+    assert L.loglinear_bwd(*([ctypes.c_void_p(0)] + args[1:]), 1, 1, 64, 16, 16, 16, None) == LL_ERR_NULL
+    assert L.loglinear_bwd(*[ctypes.c_void_p(0)] * 12, 0, 1, 64, 16, 16, 16, None) == LL_OK  # empty: no-op
+    assert L.loglinear_bwd_f32(*args, 1, 1, 64, 16, 16, 48, None) == LL_ERR_SHAPE

@@ -1,0 +1,83 @@
+"""GPU parity of the backward (loglinear_bwd / _f32) against the oracle's
+gradients of the dense definition (fp64 autograd).
+
+Tolerance per gradient: max |gpu - oracle| <= tol * RMS(oracle gradient), with
+tol = 1e-4 (the arithmetic is fp32 for both input types: bf16 inputs are exact
+in fp32).  The oracle receives the same (bf16-rounded) inputs and the forward
+output `out` is the oracle's, so the backward is checked on its own; one
+pipeline case feeds the GPU forward's output instead (bf16 tolerance).
+"""
+import numpy as np
+import pytest
+import torch
+
+import log_linear_attention_attn_amd as ll
+import oracle
+import workloads as W
+from gpu_util import BF16_TOL, announce, assert_parity, have_gpu, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+BWD_TOL = 1e-4
+NAMES = ("dq", "dk", "dv", "dlog_a", "dlam")
+
+CASES = [
+    # (B, H, T, dk, dv, C, dtype, decay)
+    (1, 1, 1, 16, 16, 16, "f32", "weak"),        # one token
+    (1, 2, 64, 16, 16, 64, "f32", "weak"),       # one chunk
+    (1, 2, 200, 32, 32, 16, "f32", "weak"),      # ragged, several chunk levels
+    (1, 1, 777, 64, 32, 32, "f32", "strong"),
+    (2, 1, 300, 128, 64, 64, "bf16", "weak"),
+    (1, 1, 1000, 128, 128, 64, "bf16", "none"),  # every level carries weight
+    (1, 2, 1024, 64, 128, 32, "bf16", "weak"),   # T a power of two
+]
+
+
+def _inputs(case, seed):
+    B, H, T, dk, dv, C, dtype, decay = case
+    w = W.FwdWorkload("bwd", B, H, T, dk, dv, C, dtype, decay=decay, seed=seed)
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    dout = torch.from_numpy(np.random.default_rng(seed + 1).standard_normal((B, H, T, dv)).astype(np.float32))
+    return w, (q, k, v, la, lam), dout
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}C{}_{}_{}".format(*c))
+def test_bwd_matches_oracle(case):
+    w, inp, dout = _inputs(case, seed=case[2] + case[3])
+    q, k, v, la, lam = inp
+    out = torch.from_numpy(oracle.forward(*inp).astype(np.float32))
+    announce(f"bwd {case}")
+    dq_, dk_, dv_, dla, dlam = to_dev(q, k, v, la, lam)
+    grads = ll.bwd(dq_, dk_, dv_, dla, dlam, out.cuda(), dout.cuda(), C=w.C)
+    torch.cuda.synchronize()
+    want = oracle.backward(q, k, v, la, lam, dout)
+    for name, g, ref in zip(NAMES, grads, want):
+        assert_parity(g.cpu().numpy(), ref, BWD_TOL, f"{name} {case}")
+
+
+def test_bwd_after_gpu_forward():
+    """The pipeline as a trainer runs it: GPU forward, then the backward with
+    the GPU forward's output (bf16 path; its rounding enters d log_a)."""
+    case = (1, 2, 1000, 128, 64, 64, "bf16", "weak")
+    w, inp, dout = _inputs(case, seed=5)
+    announce("bwd after the GPU forward")
+    dev = to_dev(*inp)
+    out = ll.fwd(*dev, C=w.C)
+    grads = ll.bwd(*dev, out, dout.cuda(), C=w.C)
+    torch.cuda.synchronize()
+    want = oracle.backward(*inp, dout)
+    for name, g, ref in zip(NAMES, grads, want):
+        assert_parity(g.cpu().numpy(), ref, BF16_TOL, f"{name} pipeline")
+
+
+def test_bwd_deterministic():
+    case = (1, 2, 500, 64, 64, 32, "bf16", "weak")
+    w, inp, dout = _inputs(case, seed=9)
+    dev = to_dev(*inp)
+    out = ll.fwd(*dev, C=w.C)
+    announce("bwd determinism")
+    g1 = ll.bwd(*dev, out, dout.cuda(), C=w.C)
+    g2 = ll.bwd(*dev, out, dout.cuda(), C=w.C)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
