@@ -44,6 +44,22 @@ def algorithmic_bytes(B, H, T, dk, dv, L, in_bytes=2):
     return B * H * T * per
 
 
+def algorithmic_flops_bwd(B, H, T, dk, dv, C):
+    """dQ, dK and dV each have the forward's pair structure (causal in-chunk
+    pairs, chunk states, popcount-weighted bucket reads), and the in-chunk
+    dlambda needs the two score matrices q.k and dO.v once more."""
+    N = -(-T // C)
+    pairs = sum(min(C, T - n * C) * (min(C, T - n * C) + 1) // 2 for n in range(N))
+    return 3 * algorithmic_flops(B, H, T, dk, dv, C) + B * H * pairs * 2 * (dk + dv)
+
+
+def algorithmic_bytes_bwd(B, H, T, dk, dv, L, in_bytes=2):
+    """q, k, v, log_a, lambda, out and dout read once; fp32 dq, dk, dv, dlog_a,
+    dlambda written once."""
+    per = (2 * dk + dv) * in_bytes + 4 + 4 * L + 4 * dv + 4 * dv + 4 * (2 * dk + dv) + 4 + 4 * L
+    return B * H * T * per
+
+
 def source_hash() -> str:
     from log_linear_attention_attn_amd.profiling import source_hash as h
     return h()
@@ -127,6 +143,8 @@ def main():
     ap.add_argument("--workload", default="lm_B2H16_T16384_dk128_dv128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-log2", type=int, default=-1)
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward (default, the headline) or the backward")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -145,6 +163,9 @@ def main():
     w = W.FWD_WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.which == "bwd":
+        bench_bwd(args, w, dev)
+        return
     base = W.make_fwd_inputs(w)
     sets = [[t.to(dev) for t in base]]
     # three input sets (same values, other buffers), rotated so consecutive
@@ -233,6 +254,49 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec))
+
+
+PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix
+
+
+def bench_bwd(args, w, dev):
+    """Backward (loglinear_bwd) of the same workload: gradients of sum(out * dout)
+    for a random dout; inputs and out resident in HBM, timed over K steps."""
+    import numpy as np
+    import torch
+    import log_linear_attention_attn_amd as ll
+    import workloads as W
+    q, k, v, la, lam = [t.to(dev) for t in W.make_fwd_inputs(w)]
+    out = ll.fwd(q, k, v, la, lam, C=w.C)
+    dout = torch.from_numpy(np.random.default_rng(w.seed + 1).standard_normal(tuple(out.shape)).astype(np.float32)).to(dev)
+    K, Wm = args.steps, args.warmup
+    for _ in range(Wm):
+        ll.bwd(q, k, v, la, lam, out, dout, C=w.C)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(K):
+        ll.bwd(q, k, v, la, lam, out, dout, C=w.C)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+    flops = algorithmic_flops_bwd(w.B, w.H, w.T, w.dk, w.dv, w.C)
+    abytes = algorithmic_bytes_bwd(w.B, w.H, w.T, w.dk, w.dv, w.L, 2 if w.dtype == "bf16" else 4)
+    tflops = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "bwd tokens/sec (gradients of q, k, v, log_a, lambda), log-linear Mamba-2",
+        "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "C": w.C,
+                   "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_a/lambda/out/dout", "pass": "backward"},
+        "algorithmic_flops": flops, "algorithmic_bytes": abytes,
+        "roofline": {"kernel": "whole backward (fp32 matrix-core arithmetic)", "bound": "mfma",
+                     "achieved": tflops, "peak": PEAK_F32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_F32_MFMA_TFLOPS, "traffic": None},
+        "hbm_gbs_algorithmic": abytes / (ms * 1e-3) / 1e9,
+    }
     print(json.dumps(rec))
 
 

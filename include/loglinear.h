@@ -172,7 +172,8 @@ int loglinear_prefill_f32(const float* q, const float* k, const float* v, const 
  * and the staging and per-level states of one workgroup must fit in LDS (bf16
  * with C = 64 and dk = dv = 128: up to 1024 chunks), else LL_ERR_UNSUPPORTED.
  * Scratch (per-slice partial sums of grad_lambda, (dk/16) * B * H * T *
- * bit_length(N-1) floats) is allocated stream-ordered on `stream`.
+ * bit_length(N-1) floats, and B * H * T doubles) is allocated stream-ordered
+ * on `stream`.
  * Arithmetic: fp32 matrix-core instructions throughout; no atomics, so the
  * results are deterministic.
  */

@@ -52,6 +52,7 @@ struct BwdArgs {
   float* dlog_a;       // [BH][T]
   float* dlam;         // [BH][T][L]
   float* dlam_part;    // [dk/16][BH][T][nslot] chunk-level dlam partial sums
+  double* dc;          // [BH][T] dO.O - v.dV per token
   int BH, T, dk, dv, L;
   int nslot;           // chunk-level Fenwick bits = bit_length(N - 1)
 };

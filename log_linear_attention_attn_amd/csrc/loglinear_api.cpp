@@ -184,11 +184,13 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   if (p.nslot > 16 || p.N > 4096) return LL_ERR_UNSUPPORTED;
   const int lds = ll::bwd_lds_bytes(dtype, C, dk, dv, p.L, p.N, p.nslot);
   if (lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
-  const size_t part = (size_t)(dk / 16) * p.BH * T * (p.nslot > 0 ? p.nslot : 1) * sizeof(float);
+  const size_t part = align256((size_t)(dk / 16) * p.BH * T * (p.nslot > 0 ? p.nslot : 1) * sizeof(float));
+  const size_t dcb = (size_t)p.BH * T * sizeof(double);
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, part, stream) != hipSuccess) return LL_ERR_HIP;
+  if (hipMallocAsync(&ws, part + dcb, stream) != hipSuccess) return LL_ERR_HIP;
   ll::BwdArgs a{q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda,
-                static_cast<float*>(ws), p.BH, T, dk, dv, p.L, p.nslot};
+                static_cast<float*>(ws), reinterpret_cast<double*>(static_cast<char*>(ws) + part),
+                p.BH, T, dk, dv, p.L, p.nslot};
   st = ll::launch_bwd(dtype, C, a, stream);
   if (hipFreeAsync(ws, stream) != hipSuccess && st == LL_OK) st = LL_ERR_HIP;
   return st;

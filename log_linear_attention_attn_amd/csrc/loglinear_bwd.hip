@@ -27,7 +27,8 @@
 //                   left-half keys: dV (a = dO, c = q, x = k) or
 //                   dK (a = q, c = dO, x = v), y_s = sum R_b x_s.
 //   bwd_dlam_intra_kernel  dlam of the in-chunk levels.
-//   bwd_finish_kernel      sums the dlam partials, writes dlog_a.
+//   bwd_dlam_inter_kernel  dlam of the chunk levels from the partials.
+//   bwd_dcum_kernel, bwd_dlog_a_kernel  dlog_a.
 // Each output row slice of 16 columns belongs to one workgroup (no atomics).
 // All products run as fp32 matrix-core instructions (v_mfma_f32_16x16x4f32);
 // bf16 inputs are widened when staged.
@@ -54,6 +55,19 @@ __host__ __device__ constexpr int al16(int x) { return (x + 15) & ~15; }
 
 template <typename IT>
 __device__ __forceinline__ float ldf(const IT* p) { return static_cast<float>(*p); }
+
+// four consecutive elements (16 bytes of fp32, 8 of bf16) as one access
+template <typename T>
+struct Vec4;
+template <>
+struct Vec4<float> { typedef f32x4 type; };
+template <>
+struct Vec4<bf16> { typedef bf16x4 type; };
+template <typename T>
+__device__ __forceinline__ void copy4(T* dst, const T* src, bool ok) {
+  typedef typename Vec4<T>::type V;
+  *reinterpret_cast<V*>(dst) = ok ? *reinterpret_cast<const V*>(src) : V{};
+}
 
 // sum over the 16 lanes of each row (DPP rotations and quad swaps)
 template <int CTRL>
@@ -163,11 +177,11 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dq_kernel(BwdArgs a) {
           dlt_s[b] = n == rs ? 0.f : dlt_s[b] + Aprev;
         }
     // ---- stage the chunk
-    for (int i = tid; i < C * dv; i += NT) {
-      const int r = i / dv, c = i - r * dv;
+    for (int i = tid; i < C * (dv / 4); i += NT) {
+      const int r = i / (dv / 4), c = (i - r * (dv / 4)) * 4;
       const bool ok = tok0 + r < T;
-      dOs[r * LDD + c] = ok ? dog[(size_t)(tok0 + r) * dv + c] : 0.f;
-      Vs[r * LDV + c] = ok ? vg[(size_t)(tok0 + r) * dv + c] : IT(0.f);
+      copy4(dOs + r * LDD + c, dog + (size_t)(tok0 + r) * dv + c, ok);
+      copy4(Vs + r * LDV + c, vg + (size_t)(tok0 + r) * dv + c, ok);
     }
     for (int i = tid; i < C * 16; i += NT) {
       const int r = i >> 4, c = i & 15;
@@ -187,6 +201,7 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dq_kernel(BwdArgs a) {
     f32x4 O = {0.f, 0.f, 0.f, 0.f};
     for (int kb = 0; kb <= w; ++kb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      #pragma unroll 8
       for (int k0 = 0; k0 < dv; k0 += 4) {
         const float av = static_cast<float>(Vs[(16 * kb + li) * LDV + k0 + g4]);
         acc = F::mma(av, dOs[(16 * w + li) * LDD + k0 + g4], acc);
@@ -208,6 +223,7 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dq_kernel(BwdArgs a) {
       if (right) {
         const float* stb = St + b * 16 * LDD;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        #pragma unroll 8
         for (int k0 = 0; k0 < dv; k0 += 4) acc = F::mma(F::load(dOs, LDD, 16 * w, k0, lane), stb[li * LDD + k0 + g4], acc);
         mfma_drain();
         // acc[r] = (dO_t St_b)[j = li], t = 16w + 4g4 + r
@@ -237,6 +253,7 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dq_kernel(BwdArgs a) {
     for (int it = w; it < dv / 16; it += NW) {
       const int i0 = 16 * it;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      #pragma unroll 8
       for (int k0 = 0; k0 < C; k0 += 4) {
         const int s = k0 + g4;
         acc = F::mma(KT[li * LDKT + s], esf_s[s] * static_cast<float>(Vs[s * LDV + i0 + li]), acc);
@@ -352,11 +369,11 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_kv_kernel(BwdArgs a) {
           gam_s[b] = n == rs - 1 ? 0.f : gam_s[b] + tot_s[n + 1];
         }
       }
-    for (int i = tid; i < C * dc; i += NT) {
-      const int r = i / dc, c = i - r * dc;
+    for (int i = tid; i < C * (dc / 4); i += NT) {
+      const int r = i / (dc / 4), c = (i - r * (dc / 4)) * 4;
       const bool ok = tok0 + r < T;
-      Cs[r * LDC + c] = ok ? cg[(size_t)(tok0 + r) * dc + c] : CT(0.f);
-      Xs[r * LDX + c] = ok ? xg[(size_t)(tok0 + r) * dc + c] : IT(0.f);
+      copy4(Cs + r * LDC + c, cg + (size_t)(tok0 + r) * dc + c, ok);
+      copy4(Xs + r * LDX + c, xg + (size_t)(tok0 + r) * dc + c, ok);
     }
     for (int i = tid; i < C * 16; i += NT) {
       const int r = i >> 4, c = i & 15;
@@ -377,6 +394,7 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_kv_kernel(BwdArgs a) {
     f32x4 Y = {0.f, 0.f, 0.f, 0.f};
     for (int tb = w; tb < NW; ++tb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      #pragma unroll 8
       for (int k0 = 0; k0 < dc; k0 += 4)
         acc = F::mma(static_cast<float>(Cs[(16 * tb + li) * LDC + k0 + g4]),
                      static_cast<float>(Xs[(16 * w + li) * LDX + k0 + g4]), acc);
@@ -397,6 +415,7 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_kv_kernel(BwdArgs a) {
       if (((n >> b) & 1) || base + (1 << b) >= N) continue;
       const float* rb = R + b * 16 * LDR;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      #pragma unroll 8
       for (int k0 = 0; k0 < dc; k0 += 4)
         acc = F::mma(static_cast<float>(Xs[(16 * w + li) * LDX + k0 + g4]), rb[li * LDR + k0 + g4], acc);
       mfma_drain();
@@ -421,6 +440,7 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_kv_kernel(BwdArgs a) {
         const int re = min(N, base + (1 << (b + 1)));
         float* rb = R + b * 16 * LDR;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        #pragma unroll 8
         for (int k0 = 0; k0 < C; k0 += 4) {
           const int t = k0 + g4;
           const float wq = lam_s[t * L + LOGC + 1 + b] * __expf(static_cast<float>(cl_s[t] + dlt_s[b]));
@@ -471,11 +491,13 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dlam_intra_kernel(BwdArgs a) 
     const int s_row = 16 * kb + li;  // key row this lane loads for the A operands
     const bool sok = tok0 + s_row < T;
     f32x4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll 8
     for (int k0 = 0; k0 < dk; k0 += 4) {
       const float ka = sok ? ldf(kg + (size_t)(tok0 + s_row) * dk + k0 + g4) : 0.f;
       const float qb = qok ? ldf(qg + (size_t)(tok0 + tq) * dk + k0 + g4) : 0.f;
       z1 = F::mma(ka, qb, z1);
     }
+    #pragma unroll 8
     for (int k0 = 0; k0 < dv; k0 += 4) {
       const float va = sok ? ldf(vg + (size_t)(tok0 + s_row) * dv + k0 + g4) : 0.f;
       const float db = qok ? dog[(size_t)(tok0 + tq) * dv + k0 + g4] : 0.f;
@@ -506,46 +528,60 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dlam_intra_kernel(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// bwd_finish_kernel: one workgroup (256 threads) per (b,h).  dlam of the
-// chunk levels from the per-slice partials; dlog_a as the reverse prefix sum
-// of dO_t . O_t - v_t . dV_t.
+// bwd_dlam_inter_kernel: dlam of the chunk levels, the sum of the per-slice
+// partials (0 past the levels a row reaches); one thread per (b,h, t).
 // ---------------------------------------------------------------------------
-template <typename IT>
-__global__ void __launch_bounds__(256) bwd_finish_kernel(BwdArgs a, int logc, int nparts) {
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int T = a.T, L = a.L, dv = a.dv, nslot = a.nslot;
-  const size_t bhT = (size_t)bh * T;
-  for (int i = tid; i < T * (L - logc - 1 > 0 ? L - logc - 1 : 0); i += 256) {
-    const int nl = L - logc - 1;
-    const int t = i / nl, b = i - t * nl;
+__global__ void __launch_bounds__(256) bwd_dlam_inter_kernel(BwdArgs a, int logc, int nparts) {
+  const int T = a.T, L = a.L, nslot = a.nslot;
+  const int bh = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  for (int b = 0; b + logc + 1 < L; ++b) {
     float x = 0.f;
     if (b < nslot)
       for (int p = 0; p < nparts; ++p) x += a.dlam_part[(((size_t)p * a.BH + bh) * T + t) * nslot + b];
-    a.dlam[(bhT + t) * L + logc + 1 + b] = x;
+    a.dlam[((size_t)bh * T + t) * L + logc + 1 + b] = x;
   }
-  // reverse prefix sum over T: each thread owns a contiguous range.  The
-  // terms and the running sums are kept in fp64: the sum runs over up to T
-  // terms whose two parts largely cancel.
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dcum_kernel: dc_t = dO_t . O_t - v_t . dV_t (fp64), one wave per token.
+// bwd_dlog_a_kernel: dlog_a = reverse prefix sum of dc over T, one workgroup
+// per (b,h), each thread a contiguous range, fp64 (the two parts of dc largely
+// cancel and the sum runs over up to T terms).
+// ---------------------------------------------------------------------------
+template <typename IT>
+__global__ void __launch_bounds__(256) bwd_dcum_kernel(BwdArgs a, double* dc) {
+  const int T = a.T, dv = a.dv;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b,h, t) flattened
+  const int lane = threadIdx.x & 63;
+  if (row >= (size_t)a.BH * T) return;
+  const float* __restrict__ dO = a.dout + row * dv;
+  const float* __restrict__ O = a.out + row * dv;
+  const float* __restrict__ dV = a.dvo + row * dv;
+  const IT* __restrict__ v = static_cast<const IT*>(a.v) + row * dv;
+  double x = 0.0;
+  for (int j = lane; j < dv; j += 64)
+    x += (double)dO[j] * O[j] - (double)static_cast<float>(v[j]) * dV[j];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if (lane == 0) dc[row] = x;
+}
+
+__global__ void __launch_bounds__(256) bwd_dlog_a_kernel(BwdArgs a, const double* dc) {
+  const int bh = blockIdx.x, tid = threadIdx.x, T = a.T;
+  const double* __restrict__ d = dc + (size_t)bh * T;
   __shared__ double part[256];
   const int per = (T + 255) / 256;
   const int t0 = min(T, tid * per), t1 = min(T, t0 + per);
-  const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
-  auto dc = [&](int t) {
-    double x = 0.0;
-    for (int j = 0; j < dv; ++j)
-      x += (double)a.dout[(bhT + t) * dv + j] * a.out[(bhT + t) * dv + j] -
-           (double)ldf(vg + (size_t)t * dv + j) * a.dvo[(bhT + t) * dv + j];
-    return x;
-  };
   double s = 0.0;
-  for (int t = t0; t < t1; ++t) s += dc(t);
+  for (int t = t0; t < t1; ++t) s += d[t];
   part[tid] = s;
   __syncthreads();
   double run = 0.0;  // sum of the ranges of the threads above
   for (int i = tid + 1; i < 256; ++i) run += part[i];
   for (int t = t1 - 1; t >= t0; --t) {
-    run += dc(t);
-    a.dlog_a[bhT + t] = static_cast<float>(run);
+    run += d[t];
+    a.dlog_a[(size_t)bh * T + t] = static_cast<float>(run);
   }
 }
 
@@ -601,7 +637,10 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_kv_kernel<IT, C, 1>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
   }
   hipLaunchKernelGGL((bwd_dlam_intra_kernel<IT, C>), dim3(a.BH * N), dim3(NT), 0, s, a);
-  hipLaunchKernelGGL((bwd_finish_kernel<IT>), dim3(a.BH), dim3(256), 0, s, a, Lg<C>::v, a.dk / 16);
+  hipLaunchKernelGGL(bwd_dlam_inter_kernel, dim3((a.T + 255) / 256, a.BH), dim3(256), 0, s, a, Lg<C>::v, a.dk / 16);
+  const size_t rows = (size_t)a.BH * a.T;
+  hipLaunchKernelGGL((bwd_dcum_kernel<IT>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, a, a.dc);
+  hipLaunchKernelGGL(bwd_dlog_a_kernel, dim3(a.BH), dim3(256), 0, s, a, a.dc);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
