@@ -3,7 +3,10 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--no-cpu-baseline]
 
 A step is one loglinear_fwd call (segment-state, node and sweep kernels) over
-one batch of synthetic inputs already resident in HBM.  Prints ONE JSON line.
+one batch of synthetic inputs already resident in HBM.  Prints ONE JSON line;
+at the default workload it also carries a "decode" object: one decode step of
+64 sequences x 16 heads (L = 17) timed the same way.  --pass bwd / decode time
+the backward or only the decode step instead.
 Default workload: log-linear Mamba-2 forward, B=2, H=16, T=16384, dk=dv=128,
 bf16 q/k/v, fp32 log_a / lambda / out, L=15, C=64.
 """
@@ -58,6 +61,60 @@ def algorithmic_bytes_bwd(B, H, T, dk, dv, L, in_bytes=2):
     dlambda written once."""
     per = (2 * dk + dv) * in_bytes + 4 + 4 * L + 4 * dv + 4 * dv + 4 * (2 * dk + dv) + 4 + 4 * L
     return B * H * T * per
+
+
+def decode_bytes(t, H, L, dk, dv, in_bytes=2):
+    """HBM bytes one decode step must move for the positions t (one per
+    sequence, all H heads): with m = lssb(t), read S^0..S^m and the live levels
+    above m+1, write S^0..S^(m+1) (levels 1..m cleared) and those live levels;
+    plus q, k, v, log_a, lambda, out and t.  t = 0 writes every level."""
+    lvl = dk * dv * 4
+    total = 0
+    for x in t:
+        x = int(x)
+        if x == 0:
+            rd, wr = 0, L
+        else:
+            m = (x & -x).bit_length() - 1
+            high = bin(x >> (m + 1)).count("1")
+            rd, wr = m + 1 + high, m + 2 + high
+        total += H * ((rd + wr) * lvl + (2 * dk + dv) * in_bytes + 4 + 4 * L + 4 * dv) + 4
+    return total
+
+
+def bench_decode(dev, steps: int, warmup: int):
+    """One decode step (loglinear_decode_step) for 64 sequences x 16 heads,
+    dk = dv = 128, L = 17, t ~ U{1..65535}: states [64,16,17,128,128] fp32
+    (1.14 GB) resident in HBM and updated in place.  Every timed step repeats
+    the step at the same positions, so each moves the same bytes."""
+    import torch
+    import log_linear_attention_attn_amd as ll
+    import workloads as W
+    w = W.DECODE_64x16
+    S, q, k, v, la, lam, t = W.make_decode_inputs(w)
+    t_host = t.numpy().copy()
+    S, q, k, v, la, lam, t = (x.to(dev) for x in (S, q, k, v, la, lam, t))
+    out = torch.empty(w.N, w.H, w.dv, dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        ll.decode_step(S, q, k, v, la, lam, t, out=out)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        ll.decode_step(S, q, k, v, la, lam, t, out=out)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    nbytes = decode_bytes(t_host, w.H, w.L, w.dk, w.dv, 2 if w.dtype == "bf16" else 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del S
+    return {
+        "workload": w.name, "N": w.N, "H": w.H, "dk": w.dk, "dv": w.dv, "L": w.L,
+        "t": "U{1..65535} per sequence, seed 0", "steps": steps, "ms_per_step": ms,
+        "tokens_per_s": w.N / (ms * 1e-3), "algorithmic_bytes": nbytes,
+        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
+    }
 
 
 def source_hash() -> str:
@@ -143,8 +200,9 @@ def main():
     ap.add_argument("--workload", default="lm_B2H16_T16384_dk128_dv128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-log2", type=int, default=-1)
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
-                    help="time the forward (default, the headline) or the backward")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode"], default="fwd",
+                    help="time the forward (default, the headline; its line also carries one "
+                         "decode measurement), the backward, or only the decode step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -165,6 +223,19 @@ def main():
     torch.cuda.set_device(dev)
     if args.which == "bwd":
         bench_bwd(args, w, dev)
+        return
+    if args.which == "decode":
+        rec = bench_decode(dev, args.steps, args.warmup)
+        gbs = rec["roofline"]["achieved"]
+        print(json.dumps({
+            "metric": "decode step GB/s (algorithmic HBM bytes / time), 64 sequences x 16 heads, L=17",
+            "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": rec["workload"], "N": rec["N"], "H": rec["H"], "dk": rec["dk"],
+                       "dv": rec["dv"], "L": rec["L"], "t": rec["t"]},
+            "roofline": rec["roofline"], "tokens_per_s": rec["tokens_per_s"],
+            "algorithmic_bytes": rec["algorithmic_bytes"]}))
         return
     base = W.make_fwd_inputs(w)
     sets = [[t.to(dev) for t in base]]
@@ -252,6 +323,8 @@ def main():
         },
         "source_hash": source_hash(),
     }
+    if args.workload == W.LM_T16K.name:
+        rec["decode"] = bench_decode(dev, K, Wm)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec))

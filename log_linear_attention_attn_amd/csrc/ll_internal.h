@@ -66,12 +66,17 @@ struct SegArgs {
   int BH, T, dk, dv, C, seg_log2, nseg;
 };
 
+// Segment states are built from blocks of 2^blk_log2 chunks (a segment holds
+// 2^rlog2 blocks), so that the state kernel has enough workgroups.
 struct NodeArgs {
-  const float* seg_state;
-  const float* seg_decay;
-  float* nodes;
+  const float* blk_state;  // [BH][nblk1][dv][DKP] decayed k v^T sum of each block
+  const float* blk_decay;  // [BH][nblk1] total log decay of each block
+  float* nodes;            // [BH][nseg][dv][DKP]
+  float* seg_decay;        // [BH][nseg] total log decay of each segment (all but the last)
   int nseg;
-  int E;  // elements per state = dv * DKP
+  int nblk1;  // block slots per (b,h) = blocks of the first nseg - 1 segments + 1
+  int rlog2;  // blocks per segment = 2^rlog2
+  int E;      // elements per state = dv * DKP
 };
 
 struct DecArgs {

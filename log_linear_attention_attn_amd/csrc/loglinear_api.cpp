@@ -22,7 +22,8 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct FwdPlan {
   int BH, N, L, DKP, seg_log2, nseg, nslot;
-  size_t ws_state, ws_nodes, ws_decay, ws_total;
+  int blk_log2, nblk1;  // state blocks: 2^blk_log2 chunks; slots per (b,h)
+  size_t ws_state, ws_nodes, ws_decay, ws_bdecay, ws_total;
 };
 
 // Chunks per segment: as large as possible (fewer segment states, less
@@ -45,6 +46,16 @@ int auto_seg_log2(long long BH, int dk, int dv, int C, int N) {
   return s;
 }
 
+// Chunks per state block: segments are split into blocks until the state
+// kernel has at least 512 workgroups (one per (b,h, block, 64 dv columns)),
+// keeping at least 8 chunks per block; the node kernel adds the blocks up.
+int auto_blk_log2(long long BH, int dv, int seg_log2, int nseg) {
+  const long long per = BH * (nseg - 1) * (dv >= 64 ? dv / 64 : 1);
+  int b = seg_log2;
+  while (b > 3 && (per << (seg_log2 - b)) < 512) --b;
+  return b;
+}
+
 int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* p) {
   if (B < 0 || H < 0 || T < 0) return LL_ERR_SHAPE;
   if (C <= 0 || (C & (C - 1)) != 0) return LL_ERR_SHAPE;
@@ -61,15 +72,18 @@ int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* 
   p->nslot = p->N > 1 ? bit_length(p->N - 1) : 0;
   p->seg_log2 = seg_log2 >= 0 ? seg_log2 : auto_seg_log2(p->BH, dk, dv, C, p->N);
   p->nseg = p->N > 0 ? (p->N + (1 << p->seg_log2) - 1) >> p->seg_log2 : 0;
+  p->blk_log2 = p->nseg > 1 ? auto_blk_log2(p->BH, dv, p->seg_log2, p->nseg) : p->seg_log2;
+  p->nblk1 = ((p->nseg - 1) << (p->seg_log2 - p->blk_log2)) + 1;
   if (p->nseg > 1) {
-    const size_t elems = (size_t)p->BH * p->nseg * dv * p->DKP;
-    p->ws_state = align256(elems * sizeof(float));
-    p->ws_nodes = align256(elems * sizeof(float));
+    const size_t elems = (size_t)p->BH * dv * p->DKP;
+    p->ws_state = align256(elems * p->nblk1 * sizeof(float));
+    p->ws_nodes = align256(elems * p->nseg * sizeof(float));
     p->ws_decay = align256((size_t)p->BH * p->nseg * sizeof(float));
+    p->ws_bdecay = align256((size_t)p->BH * p->nblk1 * sizeof(float));
   } else {
-    p->ws_state = p->ws_nodes = p->ws_decay = 0;
+    p->ws_state = p->ws_nodes = p->ws_decay = p->ws_bdecay = 0;
   }
-  p->ws_total = p->ws_state + p->ws_nodes + p->ws_decay;
+  p->ws_total = p->ws_state + p->ws_nodes + p->ws_decay + p->ws_bdecay;
   return LL_OK;
 }
 
@@ -108,10 +122,12 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
     if (hipMallocAsync(&ws, p.ws_total, stream) != hipSuccess) return LL_ERR_HIP;
     owned = true;
   }
-  float* seg_state = static_cast<float*>(ws);
-  float* nodes = p.ws_total ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_state) : nullptr;
-  float* seg_decay =
-      p.ws_total ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_state + p.ws_nodes) : nullptr;
+  char* wsb = static_cast<char*>(ws);
+  float* blk_state = reinterpret_cast<float*>(wsb);
+  float* nodes = p.ws_total ? reinterpret_cast<float*>(wsb + p.ws_state) : nullptr;
+  float* seg_decay = p.ws_total ? reinterpret_cast<float*>(wsb + p.ws_state + p.ws_nodes) : nullptr;
+  float* blk_decay =
+      p.ws_total ? reinterpret_cast<float*>(wsb + p.ws_state + p.ws_nodes + p.ws_decay) : nullptr;
 
   auto mark = [&](int i) {
     if (events && st == LL_OK && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess)
@@ -119,15 +135,18 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   };
   mark(0);
   if (p.nseg > 1) {
-    ll::SegArgs sa{k, v, log_a, seg_state, seg_decay, p.BH, T, dk, dv, C, p.seg_log2, p.nseg};
+    // block states: the state kernels see the blocks as segments, with one
+    // unused slot at the end
+    ll::SegArgs sa{k, v, log_a, blk_state, blk_decay, p.BH, T, dk, dv, C, p.blk_log2, p.nblk1};
     const int ndvg = (dv + 127) / 128;
     if (dtype == LL_BF16 && p.DKP == 128 && dv % 64 == 0)
       st = ll::launch_seg_state_rs(sa, p.BH, stream);
     else
-      st = ll::launch_seg_state(dtype, p.DKP, sa, p.BH * (p.nseg - 1) * ndvg, stream);
+      st = ll::launch_seg_state(dtype, p.DKP, sa, p.BH * (p.nblk1 - 1) * ndvg, stream);
     mark(1);
     if (st == LL_OK) {
-      ll::NodeArgs na{seg_state, seg_decay, nodes, p.nseg, dv * p.DKP};
+      ll::NodeArgs na{blk_state, blk_decay, nodes, seg_decay, p.nseg, p.nblk1,
+                      p.seg_log2 - p.blk_log2, dv * p.DKP};
       st = ll::launch_seg_nodes(na, p.BH, stream);
     }
   } else {

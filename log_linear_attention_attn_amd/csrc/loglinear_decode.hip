@@ -17,7 +17,10 @@
 
 namespace ll {
 
-template <typename IT>
+// All loads of a row's live levels are issued before any of its stores (the
+// level loop is unrolled to LMAX >= L with wave-uniform predicates), so each
+// thread keeps up to L loads in flight.
+template <typename IT, int LMAX>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs a) {
   __shared__ f32x4 red[16][16];
   const int nh = blockIdx.x;
@@ -43,44 +46,53 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs a) {
   float* __restrict__ S = a.S + (size_t)nh * L * dk * dv + col;
   const size_t lvl = (size_t)dk * dv;
   const int m = t ? lssb(static_cast<uint32_t>(t)) : -1;
-  // live levels above m+1: bit b of t (b > m) <-> level b+1
-  const unsigned high = t ? (static_cast<unsigned>(t) >> (m + 1)) : 0u;
+  // levels holding state at t-1: level 0 and level b+1 for each set bit b of
+  // t-1 (that is 0..m, and the levels above m+1 that t keeps)
+  const unsigned live = t ? (1u | (static_cast<unsigned>(t - 1) << 1)) : 0u;
 
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   if (colok) {
     f32x4 vv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) vv[i] = static_cast<float>(v[col + i]);
+    // output weight of each level's new state: lambda (level m+1 holds the
+    // merge, the kept levels above it are decayed copies, 1..m are cleared)
+    float wl[LMAX];
+#pragma unroll
+    for (int l = 0; l < LMAX; ++l)
+      wl[l] = (l < L && l > m && ((live >> l) & 1 || l == m + 1)) ? lam[l] : 0.f;
     const float lam0 = lam[0];
-    const float lamm = t ? lam[m + 1] : 0.f;
     for (int r = rg; r < dk; r += 16) {
       const float qr = static_cast<float>(q[r]);
       const float kr = static_cast<float>(k[r]);
       float* __restrict__ Sr = S + (size_t)r * dv;
-      if (t == 0) {
-        for (int l = 1; l < L; ++l) *reinterpret_cast<f32x4*>(Sr + l * lvl) = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else {
-        f32x4 acc = *reinterpret_cast<const f32x4*>(Sr);
-        for (int l = 1; l <= m; ++l) {
-          acc += *reinterpret_cast<const f32x4*>(Sr + l * lvl);
-          *reinterpret_cast<f32x4*>(Sr + l * lvl) = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        acc *= at;
-        *reinterpret_cast<f32x4*>(Sr + (m + 1) * lvl) = acc;
-        o += (lamm * qr) * acc;
-        unsigned bits = high;
-        while (bits) {
-          const int l = m + 2 + __builtin_ctz(bits);
-          bits &= bits - 1;
-          f32x4 x = *reinterpret_cast<const f32x4*>(Sr + l * lvl);
-          x *= at;
-          *reinterpret_cast<f32x4*>(Sr + l * lvl) = x;
-          o += (lam[l] * qr) * x;
+      f32x4 x[LMAX];
+#pragma unroll
+      for (int l = 0; l < LMAX; ++l) {
+        x[l] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (l < L && ((live >> l) & 1)) x[l] = *reinterpret_cast<const f32x4*>(Sr + l * lvl);
+      }
+      // merge of levels 0..m into level m+1, decayed by a_t
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int l = 0; l < LMAX; ++l)
+        if (l <= m) acc += x[l];
+      acc *= at;
+      f32x4 ol = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int l = 1; l < LMAX; ++l) {
+        if (l < L) {
+          f32x4 y;
+          if (l <= m || t == 0) y = f32x4{0.f, 0.f, 0.f, 0.f};  // cleared (t = 0: every level)
+          else if (l == m + 1) y = acc;
+          else y = x[l] * at;  // kept (zero stays zero for dead levels)
+          if (t == 0 || l <= m + 1 || ((live >> l) & 1)) *reinterpret_cast<f32x4*>(Sr + l * lvl) = y;
+          ol += wl[l] * y;
         }
       }
       const f32x4 s0 = kr * vv;
       *reinterpret_cast<f32x4*>(Sr) = s0;
-      o += (lam0 * qr) * s0;
+      o += qr * (ol + lam0 * s0);
     }
   }
   red[rg][c] = o;
@@ -95,10 +107,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs a) {
 
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s) {
   const dim3 grid(a.N * a.H, (a.dv + 63) / 64);
-  if (dtype == LL_BF16)
-    hipLaunchKernelGGL(decode_kernel<bf16>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<float>, grid, dim3(256), 0, s, a);
+  if (a.L > 31) return LL_ERR_UNSUPPORTED;
+  const bool small = a.L <= 17;
+  if (dtype == LL_BF16) {
+    if (small) hipLaunchKernelGGL((decode_kernel<bf16, 17>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<bf16, 31>), grid, dim3(256), 0, s, a);
+  } else {
+    if (small) hipLaunchKernelGGL((decode_kernel<float, 17>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<float, 31>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 

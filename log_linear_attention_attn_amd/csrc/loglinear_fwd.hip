@@ -584,31 +584,39 @@ seg_state_kernel(SegArgs a) {
 // ---------------------------------------------------------------------------
 // seg_node_kernel: the bucket state that starts at segment g >= 1.  With
 // m = lssb(g) it covers segments [g - 2^m, g) (the merge the lssb rule makes
-// on the step into g, [P1] 解码), decayed to the start of g:
-//   node_g = sum_{g'} exp(A_{g'+1} + ... + A_{g-1}) T_{g'}.
+// on the step into g, [P1] 解码), decayed to the start of g.  It is summed
+// from the block states T_j of those segments (R = 2^rlog2 blocks each):
+//   node_g = sum_{j = (g - 2^m) R}^{g R - 1} exp(A_{j+1} + ... + A_{gR-1}) T_j,
+// A_j the total log decay of block j.  The first workgroup of each (b,h, g)
+// also writes the total log decay of segment g - 1.
 // One thread per (b,h, g, four state elements).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) seg_node_kernel(NodeArgs a) {
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;  // four consecutive elements
   const int g = blockIdx.y + 1;
   const int bh = blockIdx.z;
+  const size_t bbase = (size_t)bh * a.nblk1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    float sd = 0.f;
+    for (int j = (g - 1) << a.rlog2; j < g << a.rlog2; ++j) sd += a.blk_decay[bbase + j];
+    a.seg_decay[(size_t)bh * a.nseg + g - 1] = sd;
+  }
   if (e >= a.E) return;
-  const size_t base = (size_t)bh * a.nseg;
   const int m = lssb(static_cast<uint32_t>(g));
-  const int g0 = g - (1 << m);
-  // each term is independent: weight exp(A_{g'+1} + ... + A_{g-1}), summed
+  const int j0 = (g - (1 << m)) << a.rlog2;
+  // each term is independent: weight exp(A_{j+1} + ... + A_{gR-1}), summed
   // from the end so the weights come out of one running sum
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
   float d = 0.f;
 #pragma unroll 4
-  for (int gp = g - 1; gp >= g0; --gp) {
+  for (int j = (g << a.rlog2) - 1; j >= j0; --j) {
     const float wgt = __expf(d);
-    const f32x4 t = *reinterpret_cast<const f32x4*>(a.seg_state + (base + gp) * a.E + e);
+    const f32x4 t = *reinterpret_cast<const f32x4*>(a.blk_state + (bbase + j) * a.E + e);
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] += wgt * t[r];
-    d += a.seg_decay[base + gp];
+    d += a.blk_decay[bbase + j];
   }
-  *reinterpret_cast<f32x4*>(a.nodes + (base + g) * a.E + e) = x;
+  *reinterpret_cast<f32x4*>(a.nodes + ((size_t)bh * a.nseg + g) * a.E + e) = x;
 }
 
 // ---------------------------------------------------------------------------

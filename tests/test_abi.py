@@ -92,11 +92,21 @@ def test_fwd_ex_options():
 def test_workspace_size_formula():
     # one segment -> no scratch
     assert ll.fwd_workspace_size(1, 1, 64, 16, 16, 16, 4) == 0
-    # B=2,H=16,T=16384,dk=dv=128,C=64, 16-chunk segments: 16 segments
+    def a256(x):
+        return -(-x // 256) * 256
+
+    # B=2,H=16,T=16384,dk=dv=128,C=64, 16-chunk segments: 16 segments; the
+    # state kernel already has 32 * 15 * 2 = 960 >= 512 workgroups, so the
+    # state blocks are the segments (15 used + 1 slot)
     BH, nseg, dv, dkp = 32, 16, 128, 128
-    per = BH * nseg * dv * dkp * 4
-    dec = -(-BH * nseg * 4 // 256) * 256
-    assert ll.fwd_workspace_size(2, 16, 16384, 128, 128, 64, 4) == 2 * per + dec
+    st = BH * dv * dkp * 4
+    assert ll.fwd_workspace_size(2, 16, 16384, 128, 128, 64, 4) == (
+        st * 16 + st * nseg + a256(BH * nseg * 4) + a256(BH * 16 * 4))
+    # 64-chunk segments: 4 segments, 32 * 3 * 2 = 192 workgroups -> blocks of
+    # 16 chunks (768 workgroups): 12 blocks + 1 slot
+    nseg, nblk1 = 4, 13
+    assert ll.fwd_workspace_size(2, 16, 16384, 128, 128, 64, 6) == (
+        st * nblk1 + st * nseg + a256(BH * nseg * 4) + a256(BH * nblk1 * 4))
     with pytest.raises(ValueError):
         ll.fwd_workspace_size(1, 1, 64, 10, 16, 16)
 
