@@ -311,3 +311,47 @@ def backward(q, k, v, log_a, lam, dout):
             for g, t in zip(grads, ts):
                 g[b, h] = t.grad.numpy()
     return tuple(grads)
+
+
+# --------------------------------------------------------------------------
+# q and k shared by groups of heads (multi-value attention, MVA)
+# --------------------------------------------------------------------------
+# [P2] Fig. 4 (the benchmark setup under the figure) runs log-linear Mamba-2
+# with MVA: as in Mamba-2, the query / key projections (C and B there) are
+# shared by a group of heads while v, the decay and lambda stay per head.
+# Reading: Hk q/k heads, Hk dividing H, and head h reads q/k head
+# h // (H / Hk) (consecutive heads form a group).  The operator per head is the
+# unchanged dense definition above.
+
+def heads_of_qk(x, H: int) -> np.ndarray:
+    """q or k [B, Hk, T, d] (or [N, Hk, d]) laid out per head: head h gets
+    q/k head h // (H // Hk).  fp64."""
+    x = _f64(x)
+    Hk = x.shape[1]
+    if Hk < 1 or H % Hk != 0:
+        raise ValueError(f"{Hk} q/k heads do not divide {H} heads")
+    return np.repeat(x, H // Hk, axis=1)
+
+
+def forward_mva(q, k, v, log_a, lam) -> np.ndarray:
+    """Forward with q, k [B, Hk, T, dk] shared by groups of heads; v, log_a,
+    lam per head [B, H, ...].  Returns out [B, H, T, dv] float64."""
+    H = v.shape[1]
+    return forward(heads_of_qk(q, H), heads_of_qk(k, H), v, log_a, lam)
+
+
+def backward_mva(q, k, v, log_a, lam, dout):
+    """Gradients of sum(out * dout) for ``forward_mva``.  A q/k head feeds every
+    head of its group, so its gradient is the sum of the per-head gradients
+    over the group (chain rule through the repetition)."""
+    H, Hk = v.shape[1], q.shape[1]
+    dq, dk, dv, dla, dlam = backward(heads_of_qk(q, H), heads_of_qk(k, H), v, log_a, lam, dout)
+    B, _, T, d = dq.shape
+    G = H // Hk
+    return dq.reshape(B, Hk, G, T, d).sum(2), dk.reshape(B, Hk, G, T, d).sum(2), dv, dla, dlam
+
+
+def decode_step_mva(states, q, k, v, log_a, lam, t):
+    """``decode_step`` with q, k [N, Hk, dk] shared by groups of heads."""
+    H = states.shape[1]
+    return decode_step(states, heads_of_qk(q, H), heads_of_qk(k, H), v, log_a, lam, t)

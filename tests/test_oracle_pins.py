@@ -419,3 +419,80 @@ def test_backward_lambda_gradient_euler_identity():
     # entries of levels no pair reaches are exactly zero (row t uses levels <= bit_length(t))
     for t in range(50):
         assert not np.any(dlam[:, :, t, t.bit_length() + 1:])
+
+
+# ---------------------------------------------------- q/k shared across heads
+
+def test_mva_forward_bucket_brute_force():
+    """q, k shared by groups of heads ([P2] Fig. 4 setup: MVA): every head's
+    output by explicit bucket loops, reading q/k head h // (H / Hk)."""
+    rng = np.random.default_rng(41)
+    B, H, Hk, T, dk, dv = 2, 6, 2, 11, 3, 2
+    q, k, v, log_a, lam = _rand_inputs(rng, B, H, T, dk, dv, decay=0.6)
+    q, k = q[:, :Hk], k[:, :Hk]
+    got = oracle.forward_mva(q, k, v, log_a, lam)
+    assert got.shape == (B, H, T, dv)
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // Hk)
+            for t in range(T):
+                o = np.zeros(dv)
+                for lev, lo, hi in oracle.fenwick_buckets(t):
+                    for s in range(lo, hi):
+                        decay = math.exp(sum(log_a[b, h, r] for r in range(s + 1, t + 1)))
+                        o += lam[b, h, t, lev] * decay * (q[b, g, t] @ k[b, g, s]) * v[b, h, s]
+                np.testing.assert_allclose(got[b, h, t], o, rtol=1e-11, atol=1e-12)
+
+
+def test_mva_one_group_per_head_is_the_plain_forward():
+    rng = np.random.default_rng(42)
+    q, k, v, log_a, lam = _rand_inputs(rng, 1, 3, 17, 4, 2)
+    np.testing.assert_array_equal(oracle.forward_mva(q, k, v, log_a, lam), oracle.forward(q, k, v, log_a, lam))
+
+
+def test_mva_backward_matches_finite_differences():
+    """Gradients of the shared q / k (summed over their group) and of the
+    per-head v, log_a, lambda against central differences of forward_mva."""
+    rng = np.random.default_rng(43)
+    B, H, Hk, T, dk, dv = 1, 4, 2, 7, 2, 2
+    q, k, v, la, lam = _rand_inputs(rng, B, H, T, dk, dv, decay=0.4)
+    q, k = q[:, :Hk].copy(), k[:, :Hk].copy()
+    dout = rng.standard_normal((B, H, T, dv))
+    grads = oracle.backward_mva(q, k, v, la, lam, dout)
+    assert grads[0].shape == q.shape and grads[1].shape == k.shape
+
+    def loss():
+        return float((oracle.forward_mva(q, k, v, la, lam) * dout).sum())
+
+    eps = 1e-6
+    for x, g in zip((q, k, v, la, lam), grads):
+        num = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            old = x[i]
+            x[i] = old + eps
+            fp = loss()
+            x[i] = old - eps
+            fm = loss()
+            x[i] = old
+            num[i] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_mva_decode_is_the_per_head_decode_on_repeated_qk():
+    """decode_step_mva against decode_step with q / k written out per head by
+    hand (not through heads_of_qk)."""
+    rng = np.random.default_rng(44)
+    N, H, Hk, L, dk, dv = 3, 4, 2, 6, 3, 2
+    S = rng.standard_normal((N, H, L, dk, dv))
+    q = rng.standard_normal((N, Hk, dk))
+    k = rng.standard_normal((N, Hk, dk))
+    v = rng.standard_normal((N, H, dv))
+    la = -rng.random((N, H))
+    lam = rng.random((N, H, L))
+    t = np.array([5, 12, 0])
+    qh = np.stack([q[:, h // 2] for h in range(H)], axis=1)
+    kh = np.stack([k[:, h // 2] for h in range(H)], axis=1)
+    o1, s1 = oracle.decode_step_mva(S, q, k, v, la, lam, t)
+    o2, s2 = oracle.decode_step(S, qh, kh, v, la, lam, t)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
