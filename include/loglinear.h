@@ -118,6 +118,14 @@ typedef struct {
  *   final_states : NULL, or a states buffer (see loglinear_states) that
  *                  receives the per-level decode states at position T-1, as
  *                  loglinear_prefill describes.
+ *   qk_heads     : 0 (or H) = every head has its own q and k.  Otherwise the
+ *                  number Hk of q/k heads, a divisor of H: q and k are
+ *                  [B, Hk, T, dk] and head h uses q/k head h / (H / Hk) — the
+ *                  multi-value layout (MVA) of log-linear Mamba-2, where the
+ *                  pages' kernel benchmark shares q and k across heads ("Log-
+ *                  Linear Attention" article, experiment setup).  v, log_a,
+ *                  lambda and out stay per head.  A value that does not divide
+ *                  H gives LL_ERR_SHAPE.
  */
 typedef struct {
   int dtype;
@@ -127,6 +135,7 @@ typedef struct {
   size_t workspace_bytes;
   void* const* phase_events;
   const loglinear_states* final_states;
+  int qk_heads;
 } loglinear_fwd_opts;
 
 int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* log_a,
@@ -188,6 +197,19 @@ int loglinear_bwd_f32(const float* q, const float* k, const float* v, const floa
                       float* grad_k, float* grad_v, float* grad_log_a, float* grad_lambda, int B,
                       int H, int T, int dk, int dv, int C, void* stream);
 
+/*
+ * loglinear_bwd with the element type as an argument (dtype: LL_BF16 or LL_F32)
+ * and q / k shared by groups of heads (qk_heads as in loglinear_fwd_opts):
+ * q, k, grad_q and grad_k are then [B, Hk, T, dk], and grad_q / grad_k hold
+ * the sum over the H / Hk heads of each group (summed in head order after
+ * per-head gradients in stream-ordered scratch of 2 * B * H * T * dk floats).
+ * qk_heads = 0 is exactly loglinear_bwd / _f32.
+ */
+int loglinear_bwd_ex(const void* q, const void* k, const void* v, const float* log_a,
+                     const float* lambda, const float* out, const float* dout, float* grad_q,
+                     float* grad_k, float* grad_v, float* grad_log_a, float* grad_lambda, int B,
+                     int H, int T, int dk, int dv, int C, int dtype, int qk_heads, void* stream);
+
 /* Workspace bytes loglinear_fwd_ex needs for these sizes (0 if none); seg_log2
  * as in loglinear_fwd_opts.  Returns (size_t)-1 for invalid sizes. */
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2);
@@ -218,6 +240,16 @@ int loglinear_decode_step(const loglinear_states* states, const void* q, const v
 int loglinear_decode_step_f32(const loglinear_states* states, const float* q,
                               const float* k, const float* v, const float* log_a,
                               const float* lambda, const int* t, float* out, void* stream);
+
+/*
+ * loglinear_decode_step with the element type as an argument (dtype: LL_BF16
+ * or LL_F32) and q / k shared by groups of heads (qk_heads as in
+ * loglinear_fwd_opts): q and k are [N, Hk, dk]; states, v, log_a, lambda and
+ * out stay per head.  qk_heads = 0 is exactly loglinear_decode_step / _f32.
+ */
+int loglinear_decode_step_ex(const loglinear_states* states, const void* q, const void* k,
+                             const void* v, const float* log_a, const float* lambda,
+                             const int* t, float* out, int dtype, int qk_heads, void* stream);
 
 /*
  * Test export: lev[t*T + s] = level(t, s) for s <= t and -1 for s > t (int8,

@@ -35,8 +35,9 @@ LL_BF16, LL_F32 = 0, 1
 EXPORTED_SYMBOLS = (
     "loglinear_num_levels", "loglinear_fwd", "loglinear_fwd_f32", "loglinear_fwd_ex",
     "loglinear_prefill", "loglinear_prefill_f32", "loglinear_bwd", "loglinear_bwd_f32",
-    "loglinear_fwd_workspace_size",
-    "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_level_table",
+    "loglinear_bwd_ex", "loglinear_fwd_workspace_size",
+    "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_decode_step_ex",
+    "loglinear_level_table",
     "loglinear_strerror",
 )
 
@@ -55,7 +56,8 @@ class _States(ctypes.Structure):
 class _FwdOpts(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("seg_log2", ctypes.c_int), ("kernel", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("phase_events", ctypes.c_void_p), ("final_states", ctypes.POINTER(_States))]
+                ("phase_events", ctypes.c_void_p), ("final_states", ctypes.POINTER(_States)),
+                ("qk_heads", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -92,6 +94,8 @@ def lib():
     L.loglinear_bwd.restype = i
     L.loglinear_bwd_f32.argtypes = bwd_args
     L.loglinear_bwd_f32.restype = i
+    L.loglinear_bwd_ex.argtypes = bwd_args[:-1] + [i, i, vp]
+    L.loglinear_bwd_ex.restype = i
     L.loglinear_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     L.loglinear_fwd_workspace_size.restype = sz
     dec_args = [ctypes.POINTER(_States), vp, vp, vp, vp, vp, vp, vp, vp]
@@ -99,6 +103,8 @@ def lib():
     L.loglinear_decode_step.restype = i
     L.loglinear_decode_step_f32.argtypes = dec_args
     L.loglinear_decode_step_f32.restype = i
+    L.loglinear_decode_step_ex.argtypes = dec_args[:-1] + [i, i, vp]
+    L.loglinear_decode_step_ex.restype = i
     L.loglinear_level_table.argtypes = [vp, i, vp]
     L.loglinear_level_table.restype = i
     L.loglinear_strerror.argtypes = [i]
@@ -144,6 +150,17 @@ def _raise(status: int, what: str):
         raise LogLinearError(status, what)
 
 
+def _qk_heads(q, v) -> int:
+    """qk_heads argument of the C ABI: 0 when every head has its own q / k,
+    else the number of q / k heads (shared by groups of v heads, MVA)."""
+    Hk, H = q.shape[1], v.shape[1]
+    if Hk == H:
+        return 0
+    if Hk < 1 or H % Hk != 0:
+        raise ValueError(f"q/k heads ({Hk}) must divide the heads of v ({H})")
+    return Hk
+
+
 def fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1) -> int:
     n = lib().loglinear_fwd_workspace_size(B, H, T, dk, dv, C, seg_log2)
     if n == ctypes.c_size_t(-1).value:
@@ -158,7 +175,8 @@ def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, works
            phase_events=None, kernel: int = KERNEL_AUTO, final_states=None):
     """Log-linear attention forward through loglinear_fwd_ex.
 
-    q, k: [B, H, T, dk]; v: [B, H, T, dv] (all bf16 or all fp32);
+    q, k: [B, Hk, T, dk]; v: [B, H, T, dv] (all bf16 or all fp32), Hk = H or
+    a divisor of H (q / k shared by H / Hk heads each, MVA);
     log_a: [B, H, T] fp32; lam: [B, H, T, L] fp32 with L = num_levels(T).
     phase_events: None or 4 recorded torch.cuda.Event(enable_timing=True)
     objects, re-recorded before / between / after the library's kernels.
@@ -171,11 +189,12 @@ def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, works
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    B, Hk, T, dk = q.shape
+    H, dv = v.shape[1], v.shape[-1]
+    qk_heads = _qk_heads(q, v)
     L = num_levels(T) if T > 0 else 0
-    _check_dev("q", q, q.dtype, (B, H, T, dk), dev)
-    _check_dev("k", k, q.dtype, (B, H, T, dk), dev)
+    _check_dev("q", q, q.dtype, (B, Hk, T, dk), dev)
+    _check_dev("k", k, q.dtype, (B, Hk, T, dk), dev)
     _check_dev("v", v, q.dtype, (B, H, T, dv), dev)
     _check_dev("log_a", log_a, torch.float32, (B, H, T), dev)
     _check_dev("lam", lam, torch.float32, (B, H, T, L), dev)
@@ -198,7 +217,7 @@ def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, works
     opts = _FwdOpts(LL_BF16 if q.dtype == torch.bfloat16 else LL_F32, int(seg_log2), int(kernel),
                     _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None else 0,
                     ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
-                    ctypes.pointer(fin) if fin is not None else None)
+                    ctypes.pointer(fin) if fin is not None else None, qk_heads)
     st = lib().loglinear_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out),
                                 B, H, T, dk, dv, int(C), ctypes.byref(opts), _stream(dev))
     _raise(st, "loglinear_fwd_ex")
@@ -206,9 +225,12 @@ def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, works
 
 
 def fwd(q, k, v, log_a, lam, C: int = 64, out=None):
-    """Log-linear attention forward (loglinear_fwd for bf16, loglinear_fwd_f32 for fp32)."""
+    """Log-linear attention forward (loglinear_fwd for bf16, loglinear_fwd_f32 for
+    fp32; q / k shared across heads go through loglinear_fwd_ex)."""
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q, k, v must be bfloat16 or float32")
+    if q.dim() == 4 and v.dim() == 4 and q.shape[1] != v.shape[1]:
+        return fwd_ex(q, k, v, log_a, lam, C=C, out=out)
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")
@@ -236,9 +258,18 @@ def prefill(q, k, v, log_a, lam, C: int = 64, L: int | None = None, out=None, st
 
     Returns (out [B, H, T, dv] fp32, states [B, H, L, dk, dv] fp32); L defaults
     to num_levels(T) and may be larger so decoding can continue past 2^(L-1).
+    q / k shared across heads go through loglinear_fwd_ex's final_states.
     """
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q, k, v must be bfloat16 or float32")
+    if q.dim() == 4 and v.dim() == 4 and q.shape[1] != v.shape[1]:
+        B, _, T, dk = q.shape
+        H, dv = v.shape[1], v.shape[-1]
+        Ls = int(L) if L is not None else max(num_levels(T) if T > 0 else 0, 1)
+        if states is None:
+            states = torch.empty((B, H, Ls, dk, dv), dtype=torch.float32, device=q.device)
+        out = fwd_ex(q, k, v, log_a, lam, C=C, out=out, final_states=states)
+        return out, states
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")
@@ -269,30 +300,38 @@ def bwd(q, k, v, log_a, lam, out, dout, C: int = 64):
     """Gradients of sum(out * dout) with respect to q, k, v, log_a and lam
     (loglinear_bwd / loglinear_bwd_f32); out is the forward's output.
 
-    Returns (dq, dk, dv, dlog_a, dlam), all fp32, shaped like the inputs.
+    Returns (dq, dk, dv, dlog_a, dlam), all fp32, shaped like the inputs.  With
+    q / k shared across heads (MVA) dq and dk are summed over each group
+    (loglinear_bwd_ex).
     """
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q, k, v must be bfloat16 or float32")
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device")
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    B, Hk, T, dk = q.shape
+    H, dv = v.shape[1], v.shape[-1]
+    qk_heads = _qk_heads(q, v)
     L = num_levels(T) if T > 0 else 0
-    _check_dev("q", q, q.dtype, (B, H, T, dk), dev)
-    _check_dev("k", k, q.dtype, (B, H, T, dk), dev)
+    _check_dev("q", q, q.dtype, (B, Hk, T, dk), dev)
+    _check_dev("k", k, q.dtype, (B, Hk, T, dk), dev)
     _check_dev("v", v, q.dtype, (B, H, T, dv), dev)
     _check_dev("log_a", log_a, torch.float32, (B, H, T), dev)
     _check_dev("lam", lam, torch.float32, (B, H, T, L), dev)
     _check_dev("out", out, torch.float32, (B, H, T, dv), dev)
     _check_dev("dout", dout, torch.float32, (B, H, T, dv), dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    gq, gk = torch.empty((B, H, T, dk), **f32), torch.empty((B, H, T, dk), **f32)
+    gq, gk = torch.empty((B, Hk, T, dk), **f32), torch.empty((B, Hk, T, dk), **f32)
     gv = torch.empty((B, H, T, dv), **f32)
     gla, glam = torch.empty((B, H, T), **f32), torch.empty((B, H, T, L), **f32)
-    f = lib().loglinear_bwd if q.dtype == torch.bfloat16 else lib().loglinear_bwd_f32
-    st = f(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out), _ptr(dout), _ptr(gq), _ptr(gk),
-           _ptr(gv), _ptr(gla), _ptr(glam), B, H, T, dk, dv, int(C), _stream(dev))
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out), _ptr(dout), _ptr(gq), _ptr(gk),
+            _ptr(gv), _ptr(gla), _ptr(glam), B, H, T, dk, dv, int(C))
+    if qk_heads:
+        st = lib().loglinear_bwd_ex(*ptrs, LL_BF16 if q.dtype == torch.bfloat16 else LL_F32, qk_heads,
+                                    _stream(dev))
+    else:
+        f = lib().loglinear_bwd if q.dtype == torch.bfloat16 else lib().loglinear_bwd_f32
+        st = f(*ptrs, _stream(dev))
     _raise(st, "loglinear_bwd")
     return gq, gk, gv, gla, glam
 
@@ -300,7 +339,8 @@ def bwd(q, k, v, log_a, lam, out, dout, C: int = 64):
 def decode_step(states, q, k, v, log_a, lam, t, out=None):
     """One decode step; updates ``states`` [N, H, L, dk, dv] fp32 in place.
 
-    q, k: [N, H, dk]; v: [N, H, dv] (bf16 or fp32); log_a: [N, H] fp32;
+    q, k: [N, Hk, dk] with Hk = H or a divisor of H (shared by H / Hk heads
+    each, MVA); v: [N, H, dv] (bf16 or fp32); log_a: [N, H] fp32;
     lam: [N, H, L] fp32; t: [N] int32.  Returns out [N, H, dv] fp32.
     """
     dev = states.device
@@ -310,8 +350,11 @@ def decode_step(states, q, k, v, log_a, lam, t, out=None):
     _check_dev("states", states, torch.float32, (N, H, L, dk, dv), dev)
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q, k, v must be bfloat16 or float32")
-    _check_dev("q", q, q.dtype, (N, H, dk), dev)
-    _check_dev("k", k, q.dtype, (N, H, dk), dev)
+    Hk = q.shape[1] if q.dim() == 3 else H
+    if Hk < 1 or H % Hk != 0:
+        raise ValueError(f"q/k heads ({Hk}) must divide the heads of the states ({H})")
+    _check_dev("q", q, q.dtype, (N, Hk, dk), dev)
+    _check_dev("k", k, q.dtype, (N, Hk, dk), dev)
     _check_dev("v", v, q.dtype, (N, H, dv), dev)
     _check_dev("log_a", log_a, torch.float32, (N, H), dev)
     _check_dev("lam", lam, torch.float32, (N, H, L), dev)
@@ -320,9 +363,13 @@ def decode_step(states, q, k, v, log_a, lam, t, out=None):
         out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     _check_dev("out", out, torch.float32, (N, H, dv), dev)
     desc = _States(states.data_ptr(), N, H, L, dk, dv)
-    f = lib().loglinear_decode_step if q.dtype == torch.bfloat16 else lib().loglinear_decode_step_f32
-    st = f(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(t), _ptr(out),
-           _stream(dev))
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(t), _ptr(out))
+    if Hk != H:
+        st = lib().loglinear_decode_step_ex(*args, LL_BF16 if q.dtype == torch.bfloat16 else LL_F32, Hk,
+                                            _stream(dev))
+    else:
+        f = lib().loglinear_decode_step if q.dtype == torch.bfloat16 else lib().loglinear_decode_step_f32
+        st = f(*args, _stream(dev))
     _raise(st, "loglinear_decode_step")
     return out
 

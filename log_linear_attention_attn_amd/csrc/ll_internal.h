@@ -28,6 +28,7 @@ struct FwdArgs {
   // The sweep's last segment writes the inter-chunk levels log2(C)+1 .. st_L-1.
   float* st_out;
   int st_L;
+  int G = 1;  // heads per q/k head: q and k of head bh are row bh / G
 };
 
 struct HandoffArgs {
@@ -36,6 +37,7 @@ struct HandoffArgs {
   const float* log_a;
   float* st_out;  // [BH][st_L][dk][dv]
   int BH, T, dk, dv, C, st_L;
+  int G = 1;  // heads per q/k head: q and k of head bh are row bh / G
 };
 
 struct BwdArgs {
@@ -55,6 +57,7 @@ struct BwdArgs {
   double* dc;          // [BH][T] dO.O - v.dV per token
   int BH, T, dk, dv, L;
   int nslot;           // chunk-level Fenwick bits = bit_length(N - 1)
+  int G = 1;  // heads per q/k head: q and k of head bh are row bh / G
 };
 
 struct SegArgs {
@@ -64,6 +67,7 @@ struct SegArgs {
   float* seg_state;  // [BH][nseg][dv][DKP]
   float* seg_decay;  // [BH][nseg]
   int BH, T, dk, dv, C, seg_log2, nseg;
+  int G = 1;  // heads per q/k head: q and k of head bh are row bh / G
 };
 
 // Segment states are built from blocks of 2^blk_log2 chunks (a segment holds
@@ -89,6 +93,7 @@ struct DecArgs {
   const int* t;
   float* out;
   int N, H, L, dk, dv;
+  int G = 1;  // heads per q/k head: q and k of head bh are row bh / G
 };
 
 int sweep_lds_bytes(int dtype, int C, int DKP, int L, int nslot);
@@ -104,5 +109,7 @@ int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot);
 int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s);
+// out[i][e] = sum_{g < G} in[i * G + g][e] for i < rows, e < elems (elems % 4 == 0)
+int launch_group_sum(const float* in, float* out, long long rows, int G, long long elems, hipStream_t s);
 
 }  // namespace ll

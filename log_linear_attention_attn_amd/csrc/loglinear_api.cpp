@@ -56,6 +56,14 @@ int auto_blk_log2(long long BH, int dv, int seg_log2, int nseg) {
   return b;
 }
 
+// Heads per q/k head for qk_heads q/k heads (0 = one per head); 0 if
+// qk_heads does not divide H.
+int heads_per_qk(int H, int qk_heads) {
+  if (qk_heads == 0 || qk_heads == H) return 1;
+  if (qk_heads < 0 || H <= 0 || H % qk_heads != 0) return 0;
+  return H / qk_heads;
+}
+
 int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* p) {
   if (B < 0 || H < 0 || T < 0) return LL_ERR_SHAPE;
   if (C <= 0 || (C & (C - 1)) != 0) return LL_ERR_SHAPE;
@@ -90,10 +98,12 @@ int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* 
 int run_fwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
             const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
             int seg_log2, int kernel, void* workspace, size_t workspace_bytes,
-            void* const* events, const loglinear_states* fin, hipStream_t stream) {
+            void* const* events, const loglinear_states* fin, int qk_heads, hipStream_t stream) {
   FwdPlan p;
   int st = plan_fwd(B, H, T, dk, dv, C, seg_log2, &p);
   if (st != LL_OK) return st;
+  const int G = heads_per_qk(H, qk_heads);
+  if (G < 1) return LL_ERR_SHAPE;
   if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
   if (fin && (fin->N != B || fin->H != H || fin->dk != dk || fin->dv != dv || fin->L > 31 ||
               fin->L < (T > 0 ? p.L : 1)))
@@ -137,7 +147,7 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   if (p.nseg > 1) {
     // block states: the state kernels see the blocks as segments, with one
     // unused slot at the end
-    ll::SegArgs sa{k, v, log_a, blk_state, blk_decay, p.BH, T, dk, dv, C, p.blk_log2, p.nblk1};
+    ll::SegArgs sa{k, v, log_a, blk_state, blk_decay, p.BH, T, dk, dv, C, p.blk_log2, p.nblk1, G};
     const int ndvg = (dv + 127) / 128;
     if (dtype == LL_BF16 && p.DKP == 128 && dv % 64 == 0)
       st = ll::launch_seg_state_rs(sa, p.BH, stream);
@@ -155,7 +165,7 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   mark(2);
   if (st == LL_OK) {
     ll::FwdArgs fa{q, k, v, log_a, lambda, out, nodes, seg_decay, p.BH, T, dk, dv, p.L,
-                   p.seg_log2, p.nseg, p.nslot, fin ? fin->data : nullptr, fin ? fin->L : 0};
+                   p.seg_log2, p.nseg, p.nslot, fin ? fin->data : nullptr, fin ? fin->L : 0, G};
     const long long pairs = (long long)p.BH * p.nseg;
     const long long nblocks = ((pairs + 7) / 8) * 8 * (use_rs ? dv / 64 : dv / 16);
     if (nblocks > 0x7fffffffLL) st = LL_ERR_UNSUPPORTED;
@@ -164,7 +174,7 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   }
   if (st == LL_OK && fin) {
     // levels 0..log2(C) of the prefill states; the sweep wrote the others
-    ll::HandoffArgs ha{k, v, log_a, fin->data, p.BH, T, dk, dv, C, fin->L};
+    ll::HandoffArgs ha{k, v, log_a, fin->data, p.BH, T, dk, dv, C, fin->L, G};
     st = ll::launch_handoff_intra(dtype, ha, stream);
   }
   mark(3);
@@ -175,27 +185,33 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
 }
 
 int run_decode(int dtype, const loglinear_states* s, const void* q, const void* k, const void* v,
-               const float* log_a, const float* lambda, const int* t, float* out,
+               const float* log_a, const float* lambda, const int* t, float* out, int qk_heads,
                hipStream_t stream) {
   if (!s) return LL_ERR_NULL;
   if (s->N < 0 || s->H < 0) return LL_ERR_SHAPE;
+  if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
+  const int G = s->H > 0 ? heads_per_qk(s->H, qk_heads) : 1;
+  if (G < 1) return LL_ERR_SHAPE;
   if (s->L < 1 || s->L > 31) return LL_ERR_SHAPE;
   if (s->dk < 4 || s->dk % 4 != 0 || s->dv < 4 || s->dv % 4 != 0) return LL_ERR_SHAPE;
   if (s->dk > 1024 || s->dv > 1024) return LL_ERR_UNSUPPORTED;
   if ((long long)s->N * s->H > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
   if (s->N == 0 || s->H == 0) return LL_OK;
   if (!s->data || !q || !k || !v || !log_a || !lambda || !t || !out) return LL_ERR_NULL;
-  ll::DecArgs a{s->data, q, k, v, log_a, lambda, t, out, s->N, s->H, s->L, s->dk, s->dv};
+  ll::DecArgs a{s->data, q, k, v, log_a, lambda, t, out, s->N, s->H, s->L, s->dk, s->dv, G};
   return ll::launch_decode(dtype, a, stream);
 }
 
 int run_bwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
             const float* lambda, const float* out, const float* dout, float* dq, float* dk_out,
             float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T, int dk, int dv, int C,
-            hipStream_t stream) {
+            int qk_heads, hipStream_t stream) {
   FwdPlan p;
   int st = plan_fwd(B, H, T, dk, dv, C, 0, &p);
   if (st != LL_OK) return st;
+  if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
+  const int G = heads_per_qk(H, qk_heads);
+  if (G < 1) return LL_ERR_SHAPE;
   if (B == 0 || H == 0 || T == 0) return LL_OK;
   if (!q || !k || !v || !log_a || !lambda || !out || !dout || !dq || !dk_out || !dv_out || !dlog_a ||
       !dlambda)
@@ -204,13 +220,23 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   const int lds = ll::bwd_lds_bytes(dtype, C, dk, dv, p.L, p.N, p.nslot);
   if (lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
   const size_t part = align256((size_t)(dk / 16) * p.BH * T * (p.nslot > 0 ? p.nslot : 1) * sizeof(float));
-  const size_t dcb = (size_t)p.BH * T * sizeof(double);
+  const size_t dcb = align256((size_t)p.BH * T * sizeof(double));
+  // shared q / k: per-head gradients first, then summed over each group
+  const size_t per_head = G > 1 ? align256((size_t)p.BH * T * dk * sizeof(float)) : 0;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, part + dcb, stream) != hipSuccess) return LL_ERR_HIP;
-  ll::BwdArgs a{q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda,
-                static_cast<float*>(ws), reinterpret_cast<double*>(static_cast<char*>(ws) + part),
-                p.BH, T, dk, dv, p.L, p.nslot};
+  if (hipMallocAsync(&ws, part + dcb + 2 * per_head, stream) != hipSuccess) return LL_ERR_HIP;
+  char* wsb = static_cast<char*>(ws);
+  float* dq_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb) : dq;
+  float* dk_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb + per_head) : dk_out;
+  ll::BwdArgs a{q, k, v, log_a, lambda, out, dout, dq_h, dk_h, dv_out, dlog_a, dlambda,
+                reinterpret_cast<float*>(wsb), reinterpret_cast<double*>(wsb + part),
+                p.BH, T, dk, dv, p.L, p.nslot, G};
   st = ll::launch_bwd(dtype, C, a, stream);
+  if (st == LL_OK && G > 1) {
+    const long long rows = (long long)p.BH / G, elems = (long long)T * dk;
+    st = ll::launch_group_sum(dq_h, dq, rows, G, elems, stream);
+    if (st == LL_OK) st = ll::launch_group_sum(dk_h, dk_out, rows, G, elems, stream);
+  }
   if (hipFreeAsync(ws, stream) != hipSuccess && st == LL_OK) st = LL_ERR_HIP;
   return st;
 }
@@ -225,14 +251,14 @@ int loglinear_fwd(const void* q, const void* k, const void* v, const float* log_
                   const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
                   void* stream) {
   return run_fwd(LL_BF16, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
-                 nullptr, static_cast<hipStream_t>(stream));
+                 nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
 int loglinear_fwd_f32(const float* q, const float* k, const float* v, const float* log_a,
                       const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
                       void* stream) {
   return run_fwd(LL_F32, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
-                 nullptr, static_cast<hipStream_t>(stream));
+                 nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
 int loglinear_prefill(const void* q, const void* k, const void* v, const float* log_a,
@@ -240,7 +266,7 @@ int loglinear_prefill(const void* q, const void* k, const void* v, const float* 
                       int H, int T, int dk, int dv, int C, void* stream) {
   if (!states) return LL_ERR_NULL;
   return run_fwd(LL_BF16, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
-                 states, static_cast<hipStream_t>(stream));
+                 states, 0, static_cast<hipStream_t>(stream));
 }
 
 int loglinear_prefill_f32(const float* q, const float* k, const float* v, const float* log_a,
@@ -248,7 +274,7 @@ int loglinear_prefill_f32(const float* q, const float* k, const float* v, const 
                           int B, int H, int T, int dk, int dv, int C, void* stream) {
   if (!states) return LL_ERR_NULL;
   return run_fwd(LL_F32, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0, nullptr,
-                 states, static_cast<hipStream_t>(stream));
+                 states, 0, static_cast<hipStream_t>(stream));
 }
 
 int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* log_a,
@@ -257,7 +283,7 @@ int loglinear_fwd_ex(const void* q, const void* k, const void* v, const float* l
   if (!opts) return LL_ERR_NULL;
   return run_fwd(opts->dtype, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, opts->seg_log2,
                  opts->kernel, opts->workspace, opts->workspace_bytes, opts->phase_events,
-                 opts->final_states, static_cast<hipStream_t>(stream));
+                 opts->final_states, opts->qk_heads, static_cast<hipStream_t>(stream));
 }
 
 int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_a,
@@ -265,7 +291,7 @@ int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_
                   float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T, int dk, int dv,
                   int C, void* stream) {
   return run_bwd(LL_BF16, q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda, B, H, T,
-                 dk, dv, C, static_cast<hipStream_t>(stream));
+                 dk, dv, C, 0, static_cast<hipStream_t>(stream));
 }
 
 int loglinear_bwd_f32(const float* q, const float* k, const float* v, const float* log_a,
@@ -273,7 +299,15 @@ int loglinear_bwd_f32(const float* q, const float* k, const float* v, const floa
                       float* dk_out, float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T,
                       int dk, int dv, int C, void* stream) {
   return run_bwd(LL_F32, q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda, B, H, T,
-                 dk, dv, C, static_cast<hipStream_t>(stream));
+                 dk, dv, C, 0, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_bwd_ex(const void* q, const void* k, const void* v, const float* log_a,
+                     const float* lambda, const float* out, const float* dout, float* dq,
+                     float* dk_out, float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T,
+                     int dk, int dv, int C, int dtype, int qk_heads, void* stream) {
+  return run_bwd(dtype, q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda, B, H, T,
+                 dk, dv, C, qk_heads, static_cast<hipStream_t>(stream));
 }
 
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2) {
@@ -285,14 +319,21 @@ size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, 
 int loglinear_decode_step(const loglinear_states* states, const void* q, const void* k,
                           const void* v, const float* log_a, const float* lambda, const int* t,
                           float* out, void* stream) {
-  return run_decode(LL_BF16, states, q, k, v, log_a, lambda, t, out,
+  return run_decode(LL_BF16, states, q, k, v, log_a, lambda, t, out, 0,
                     static_cast<hipStream_t>(stream));
 }
 
 int loglinear_decode_step_f32(const loglinear_states* states, const float* q, const float* k,
                               const float* v, const float* log_a, const float* lambda,
                               const int* t, float* out, void* stream) {
-  return run_decode(LL_F32, states, q, k, v, log_a, lambda, t, out,
+  return run_decode(LL_F32, states, q, k, v, log_a, lambda, t, out, 0,
+                    static_cast<hipStream_t>(stream));
+}
+
+int loglinear_decode_step_ex(const loglinear_states* states, const void* q, const void* k,
+                             const void* v, const float* log_a, const float* lambda, const int* t,
+                             float* out, int dtype, int qk_heads, void* stream) {
+  return run_decode(dtype, states, q, k, v, log_a, lambda, t, out, qk_heads,
                     static_cast<hipStream_t>(stream));
 }
 

@@ -151,9 +151,9 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, g4 = lane >> 4;
   const int N = (T + C - 1) / C;
-  const size_t bhT = (size_t)bh * T;
-  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + bhT * dk + 16 * js;
-  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk + 16 * js;
+  const size_t bhT = (size_t)bh * T, qkT = (size_t)(bh / a.G) * T;
+  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + qkT * dk + 16 * js;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + qkT * dk + 16 * js;
   const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
   const float* __restrict__ dog = a.dout + bhT * dv;
   const float* __restrict__ lag = a.log_a + bhT;
@@ -327,10 +327,10 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_kv_kernel(BwdArgs a) {
   const int bh = blockIdx.x / nsl, js = blockIdx.x - bh * nsl;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, g4 = lane >> 4;
-  const size_t bhT = (size_t)bh * T;
-  const CT* __restrict__ cg = MODE == 0 ? reinterpret_cast<const CT*>(static_cast<const IT*>(a.q) + bhT * dc)
+  const size_t bhT = (size_t)bh * T, qkT = (size_t)(bh / a.G) * T;
+  const CT* __restrict__ cg = MODE == 0 ? reinterpret_cast<const CT*>(static_cast<const IT*>(a.q) + qkT * dc)
                                         : reinterpret_cast<const CT*>(a.dout + bhT * dc);
-  const IT* __restrict__ xg = static_cast<const IT*>(MODE == 0 ? a.k : a.v) + bhT * dc;
+  const IT* __restrict__ xg = static_cast<const IT*>(MODE == 0 ? a.k : a.v) + (MODE == 0 ? qkT : bhT) * dc;
   const float* __restrict__ lag = a.log_a + bhT;
   const float* __restrict__ lamg = a.lam + bhT * L;
   float* __restrict__ yg = (MODE == 0 ? a.dvo : a.dk_out) + bhT * da + 16 * js;
@@ -381,7 +381,7 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_kv_kernel(BwdArgs a) {
       float x = 0.f;
       if (ok) {
         if (MODE == 0) x = a.dout[(bhT + tok0 + r) * da + 16 * js + c];
-        else x = ldf(static_cast<const IT*>(a.q) + (bhT + tok0 + r) * da + 16 * js + c);
+        else x = ldf(static_cast<const IT*>(a.q) + (qkT + tok0 + r) * da + 16 * js + c);
       }
       AT[c * LDAT + r] = x;
     }
@@ -472,9 +472,9 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dlam_intra_kernel(BwdArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, g4 = lane >> 4;
   const int tok0 = n * C;
-  const size_t bhT = (size_t)bh * T;
-  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + bhT * dk;
-  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk;
+  const size_t bhT = (size_t)bh * T, qkT = (size_t)(bh / a.G) * T;
+  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + qkT * dk;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + qkT * dk;
   const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
   const float* __restrict__ dog = a.dout + bhT * dv;
   __shared__ double cl_s[C];
@@ -659,6 +659,29 @@ int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s) {
     }
   }
   return LL_ERR_UNSUPPORTED;
+}
+
+// Gradients of q and k shared by G heads: the per-head gradients summed over
+// each group, in head order (deterministic).  Four elements per thread.
+__global__ void __launch_bounds__(256) group_sum_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                        int G, long long elems, long long total4) {
+  const long long i4 = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i4 >= total4) return;
+  const long long e = i4 * 4, row = e / elems, off = e - row * elems;
+  const float* src = in + (row * G) * elems + off;
+  f32x4 s = *reinterpret_cast<const f32x4*>(src);
+  for (int g = 1; g < G; ++g) s += *reinterpret_cast<const f32x4*>(src + (long long)g * elems);
+  *reinterpret_cast<f32x4*>(out + e) = s;
+}
+
+int launch_group_sum(const float* in, float* out, long long rows, int G, long long elems, hipStream_t s) {
+  if (elems % 4 != 0) return LL_ERR_UNSUPPORTED;
+  const long long total4 = rows * elems / 4;
+  if (total4 == 0) return LL_OK;
+  const long long nb = (total4 + 255) / 256;
+  if (nb > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(group_sum_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, in, out, G, elems, total4);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
 }  // namespace ll

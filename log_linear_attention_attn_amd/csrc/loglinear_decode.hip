@@ -40,8 +40,8 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs a) {
   }
   const float at = __expf(a.log_a[nh]);
   const float* __restrict__ lam = a.lam + (size_t)nh * L;
-  const IT* __restrict__ q = static_cast<const IT*>(a.q) + (size_t)nh * dk;
-  const IT* __restrict__ k = static_cast<const IT*>(a.k) + (size_t)nh * dk;
+  const IT* __restrict__ q = static_cast<const IT*>(a.q) + (size_t)(nh / a.G) * dk;
+  const IT* __restrict__ k = static_cast<const IT*>(a.k) + (size_t)(nh / a.G) * dk;
   const IT* __restrict__ v = static_cast<const IT*>(a.v) + (size_t)nh * dv;
   float* __restrict__ S = a.S + (size_t)nh * L * dk * dv + col;
   const size_t lvl = (size_t)dk * dv;

@@ -133,9 +133,9 @@ fwd_sweep_kernel(FwdArgs a) {
   const int N = (T + C - 1) / C;
   const int n0 = seg << a.seg_log2;
   const int n1 = min(N, n0 + (1 << a.seg_log2));
-  const size_t bhT = (size_t)bh * T;
-  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + bhT * dk;
-  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk;
+  const size_t bhT = (size_t)bh * T, qkT = (size_t)(bh / a.G) * T;
+  const IT* __restrict__ qg = static_cast<const IT*>(a.q) + qkT * dk;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + qkT * dk;
   const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv + 16 * ds;
   const float* __restrict__ lag = a.log_a + bhT;
   const float* __restrict__ lamg = a.lam + bhT * L;
@@ -498,7 +498,7 @@ seg_state_kernel(SegArgs a) {
   const int nu = dvw >> 4;
   const int ntile = (DKP / 16) * nu;
   const size_t bhT = (size_t)bh * T;
-  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + (size_t)(bh / a.G) * T * dk;
   const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv + dv0;
   const float* __restrict__ lag = a.log_a + bhT;
 
@@ -644,7 +644,7 @@ __global__ void __launch_bounds__(256) handoff_intra_kernel(HandoffArgs a) {
     wdec[tid] = s <= t ? __expf(d) : 0.f;
   }
   __syncthreads();
-  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + bhT * dk;
+  const IT* __restrict__ kg = static_cast<const IT*>(a.k) + (size_t)(bh / a.G) * T * dk;
   const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
   float* __restrict__ so = a.st_out + (size_t)bh * a.st_L * dk * dv;
   int logc = 0;

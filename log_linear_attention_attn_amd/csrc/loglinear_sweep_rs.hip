@@ -200,8 +200,9 @@ fwd_rs_kernel(FwdArgs a) {
   const int dv0 = dg * 64;
   const size_t bhT = (size_t)bh * T;
   // per-(b,h) slices; every slice is < 2^31 bytes (checked by the launcher)
-  const rsrc_t qr = make_rsrc(static_cast<const bf16*>(a.q) + bhT * dk, T * dk * 2);
-  const rsrc_t kr = make_rsrc(static_cast<const bf16*>(a.k) + bhT * dk, T * dk * 2);
+  const size_t qkT = (size_t)(bh / a.G) * T;
+  const rsrc_t qr = make_rsrc(static_cast<const bf16*>(a.q) + qkT * dk, T * dk * 2);
+  const rsrc_t kr = make_rsrc(static_cast<const bf16*>(a.k) + qkT * dk, T * dk * 2);
   const rsrc_t vr = make_rsrc(static_cast<const bf16*>(a.v) + bhT * dv, T * dv * 2);
   const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
   const rsrc_t lamr = make_rsrc(a.lam + bhT * L, T * L * 4);
@@ -704,7 +705,7 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
   const int s0 = g * segtok, s1 = min(T, s0 + segtok);
   const int dv0 = dg * 64;
   const size_t bhT = (size_t)bh * T;
-  const rsrc_t kr = make_rsrc(static_cast<const bf16*>(a.k) + bhT * dk, T * dk * 2);
+  const rsrc_t kr = make_rsrc(static_cast<const bf16*>(a.k) + (size_t)(bh / a.G) * T * dk, T * dk * 2);
   const rsrc_t vr = make_rsrc(static_cast<const bf16*>(a.v) + bhT * dv, T * dv * 2);
   const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
 

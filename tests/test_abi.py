@@ -183,3 +183,18 @@ def test_bwd_argument_errors():
     assert L.loglinear_bwd(*([ctypes.c_void_p(0)] + args[1:]), 1, 1, 64, 16, 16, 16, None) == LL_ERR_NULL
     assert L.loglinear_bwd(*[ctypes.c_void_p(0)] * 12, 0, 1, 64, 16, 16, 16, None) == LL_OK  # empty: no-op
     assert L.loglinear_bwd_f32(*args, 1, 1, 64, 16, 16, 48, None) == LL_ERR_SHAPE
+
+
+def test_qk_heads_must_divide_heads():
+    """qk_heads that do not divide H are rejected before any GPU work."""
+    L = ll.lib()
+    p = ctypes.c_void_p(1)
+    bad = ll._FwdOpts(0, -1, 0, None, 0, None, None, 3)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 4, 64, 16, 16, 16, ctypes.byref(bad), None) == LL_ERR_SHAPE
+    neg = ll._FwdOpts(0, -1, 0, None, 0, None, None, -2)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 4, 64, 16, 16, 16, ctypes.byref(neg), None) == LL_ERR_SHAPE
+    assert L.loglinear_bwd_ex(*([p] * 12), 1, 4, 64, 16, 16, 16, 0, 3, None) == LL_ERR_SHAPE
+    assert L.loglinear_bwd_ex(*([p] * 12), 1, 4, 64, 16, 16, 16, 7, 2, None) == LL_ERR_SHAPE  # dtype
+    desc = ll._States(1, 2, 4, 8, 16, 16)
+    assert L.loglinear_decode_step_ex(ctypes.byref(desc), p, p, p, p, p, p, p, 0, 3, None) == LL_ERR_SHAPE
+    assert L.loglinear_decode_step_ex(ctypes.byref(desc), p, p, p, p, p, p, p, 5, 2, None) == LL_ERR_SHAPE

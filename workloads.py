@@ -8,7 +8,9 @@ Recipe (one NumPy ``default_rng(seed)`` stream per workload, float32 draws in
 C order, in this order: q, k, v, log_a, lambda, then t and states for decode):
 
 * q, k, v ~ N(0, 1) / sqrt(dk); for the Mamba-2-style workloads k is then
-  L2-normalised over dk for every (b, h, t).
+  L2-normalised over dk for every (b, h, t).  Workloads that share q and k
+  across heads (multi-value attention, the pages' benchmark setup) draw q and
+  k for their Hk q/k heads only.
 * log_a = -softplus(N(0, 1) + 2)   (strong decay)  or 0 (no decay) or a
   weak-decay variant -softplus(N(0,1)+2) / 1024.
 * lambda[b, h, t, l] = softplus(N(0, 1)) with L = bit_length(T - 1) + 1 levels.
@@ -50,10 +52,15 @@ class FwdWorkload:
     decay: str = "strong"  # "strong", "none", "weak"
     knorm: bool = True
     seed: int = 0
+    Hk: int = 0  # q/k heads shared by groups of H / Hk heads (MVA); 0 = one per head
 
     @property
     def L(self) -> int:
         return num_levels(self.T)
+
+    @property
+    def qk_heads(self) -> int:
+        return self.Hk or self.H
 
 
 # The forward workloads the library is measured and checked on.
@@ -68,14 +75,18 @@ FWD_WORKLOADS = {w.name: w for w in (TINY, MAMBA2_T2K, LM_T16K, LONG_T64K)}
 def make_fwd_inputs(w: FwdWorkload):
     """Draw (q, k, v, log_a, lam) for a forward workload as CPU tensors.
 
-    q, k, v: [B, H, T, dk|dv] bf16 or f32; log_a: [B, H, T] f32;
+    q, k: [B, Hk, T, dk] (Hk = H unless the workload shares q/k across heads);
+    v: [B, H, T, dv]; all bf16 or f32; log_a: [B, H, T] f32;
     lam: [B, H, T, L] f32.
     """
     rng = np.random.default_rng(w.seed)
     B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    Hk = w.qk_heads
+    if H % Hk != 0:
+        raise ValueError("q/k heads must divide H")
     scale = np.float32(1.0 / math.sqrt(dk))
-    q = rng.standard_normal((B, H, T, dk), dtype=np.float32) * scale
-    k = rng.standard_normal((B, H, T, dk), dtype=np.float32) * scale
+    q = rng.standard_normal((B, Hk, T, dk), dtype=np.float32) * scale
+    k = rng.standard_normal((B, Hk, T, dk), dtype=np.float32) * scale
     v = rng.standard_normal((B, H, T, dv), dtype=np.float32) * scale
     if w.knorm:
         nrm = np.sqrt(np.sum(k.astype(np.float64) ** 2, axis=-1, keepdims=True))
@@ -111,6 +122,7 @@ class DecodeWorkload:
     t_max: int  # t ~ U{1 .. t_max}
     dtype: str = "bf16"
     seed: int = 0
+    Hk: int = 0  # q/k heads shared by groups of H / Hk heads (MVA); 0 = one per head
 
 
 DECODE_64x16 = DecodeWorkload("decode_N64_H16_dk128_dv128_L17", 64, 16, 128, 128, 17, 65535)
@@ -131,14 +143,15 @@ def make_decode_inputs(w: DecodeWorkload, t: np.ndarray | None = None):
     """Draw (states, q, k, v, log_a, lam, t) for one decode step.
 
     states: [N, H, L, dk, dv] f32 holding S_{t-1}; levels that are dead at
-    t-1 are exactly 0, live ones are N(0,1)/dk.  q, k: [N, H, dk]; v: [N, H, dv]
+    t-1 are exactly 0, live ones are N(0,1)/dk.  q, k: [N, Hk, dk]; v: [N, H, dv]
     (bf16 or f32); log_a: [N, H] f32; lam: [N, H, L] f32; t: [N] int32.
     """
     rng = np.random.default_rng(w.seed)
     N, H, dk, dv, L = w.N, w.H, w.dk, w.dv, w.L
     scale = np.float32(1.0 / math.sqrt(dk))
-    q = rng.standard_normal((N, H, dk), dtype=np.float32) * scale
-    k = rng.standard_normal((N, H, dk), dtype=np.float32) * scale
+    Hk = w.Hk or H
+    q = rng.standard_normal((N, Hk, dk), dtype=np.float32) * scale
+    k = rng.standard_normal((N, Hk, dk), dtype=np.float32) * scale
     v = rng.standard_normal((N, H, dv), dtype=np.float32) * scale
     log_a = -_softplus(rng.standard_normal((N, H), dtype=np.float32) + 2.0)
     lam = _softplus(rng.standard_normal((N, H, L), dtype=np.float32))
