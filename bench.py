@@ -174,7 +174,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
     while True:
         b, h = divmod(done, w.H)
         sl = (slice(b, b + 1), slice(h, h + 1))
-        oracle.forward(q[sl], k[sl], v[sl], la[sl], lam[sl])
+        g = h // (w.H // w.qk_heads)  # the q/k head this head reads
+        qs = (slice(b, b + 1), slice(g, g + 1))
+        oracle.forward(q[qs], k[qs], v[sl], la[sl], lam[sl])
         done += 1
         el = time.perf_counter() - t0
         if el >= budget_s or done >= w.B * w.H:
@@ -280,6 +282,9 @@ def main():
     flops = algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv, w.C)
     in_bytes = 2 if w.dtype == "bf16" else 4
     abytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv, w.L, in_bytes)
+    if w.Hk:
+        # q and k are read once per q/k head, not once per head
+        abytes -= w.B * (w.H - w.Hk) * w.T * 2 * w.dk * in_bytes
     tokens = w.B * w.T
     tflops = flops / (ms * 1e-3) / 1e12
     sweep_gbs = abytes / (sweep_ms * 1e-3) / 1e9
@@ -299,7 +304,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
                    "C": w.C, "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_a/lambda/out",
-                   "decay": w.decay, "seed": w.seed},
+                   "decay": w.decay, "seed": w.seed, "qk_heads": w.qk_heads},
         "head_tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
         "tflops": tflops,
         "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,

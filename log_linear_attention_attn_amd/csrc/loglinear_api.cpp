@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ll_internal.h"
 #include "loglinear.h"
 
@@ -26,21 +28,39 @@ struct FwdPlan {
   size_t ws_state, ws_nodes, ws_decay, ws_bdecay, ws_total;
 };
 
-// Chunks per segment: as large as possible (fewer segment states, less
-// prologue traffic) while still giving the sweep enough workgroups: for the
-// shapes the register-state sweep covers (64 dv columns per workgroup, one
-// workgroup per CU at a time) at least 256 workgroups, up to 64 chunks per
-// segment; otherwise (16 dv columns per workgroup) at least 2048, up to 16
-// chunks.  Depends on shapes only, so the workspace size is known without the
-// dtype.
+// Chunks per segment.  The register-state sweep runs one 512-thread workgroup
+// per CU (its LDS use), each walking its segment's chunks in order, so the
+// critical path is (rounds of workgroups over the 256 CUs of an MI355X) x
+// (chunks per segment + ~2 chunks' worth of prologue): the segment size
+// minimising that, the largest on a tie (fewer segment states, less prologue
+// traffic), up to 64 chunks.  Other
+// shapes (16 dv columns per workgroup, several workgroups per CU): the largest
+// size, up to 16 chunks, that still gives at least 2048 workgroups.  Depends
+// on shapes only, so the workspace size is known without the dtype.
+constexpr long long kCUs = 256;
+
 int auto_seg_log2(long long BH, int dk, int dv, int C, int N) {
   const bool rs_shape = C == 64 && dk > 64 && dv % 64 == 0 && N <= 1024;
-  const long long per_seg = rs_shape ? BH * (dv / 64) : BH * (dv / 16);
-  const long long want = rs_shape ? 256 : 2048;
-  int s = rs_shape ? 6 : 4;
+  if (rs_shape) {
+    const long long per_seg = BH * (dv / 64);
+    int best = 6;
+    long long best_cost = -1;
+    for (int s = 6; s >= 0; --s) {
+      const long long nseg = (N + (1LL << s) - 1) >> s;
+      const long long rounds = (per_seg * nseg + kCUs - 1) / kCUs;
+      const long long cost = rounds * (std::min<long long>(1LL << s, N) + 2);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best = s;
+      }
+    }
+    return best;
+  }
+  const long long per_seg = BH * (dv / 16);
+  int s = 4;
   while (s > 0) {
     const long long nseg = (N + (1LL << s) - 1) >> s;
-    if (per_seg * nseg >= want) break;
+    if (per_seg * nseg >= 2048) break;
     --s;
   }
   return s;

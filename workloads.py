@@ -69,7 +69,12 @@ MAMBA2_T2K = FwdWorkload("mamba2_B8H8_T2048_dk128_dv64", 8, 8, 2048, 128, 64, 64
 LM_T16K = FwdWorkload("lm_B2H16_T16384_dk128_dv128", 2, 16, 16384, 128, 128, 64, "bf16")
 LONG_T64K = FwdWorkload("long_B1H16_T65536_dk128_dv128", 1, 16, 65536, 128, 128, 64, "bf16")
 
-FWD_WORKLOADS = {w.name: w for w in (TINY, MAMBA2_T2K, LM_T16K, LONG_T64K)}
+# The pages' kernel benchmark setup (batch 2, 48 heads, head dim 64, state dim
+# 128, chunk 64, q/k shared by all heads as in Mamba-2's multi-value layout),
+# at one of its sequence lengths.
+PAGES_MVA_T16K = FwdWorkload("pages_mva_B2H48_T16384_dk128_dv64", 2, 48, 16384, 128, 64, 64, "bf16", Hk=1)
+
+FWD_WORKLOADS = {w.name: w for w in (TINY, MAMBA2_T2K, LM_T16K, LONG_T64K, PAGES_MVA_T16K)}
 
 
 def make_fwd_inputs(w: FwdWorkload):
