@@ -355,3 +355,33 @@ def decode_step_mva(states, q, k, v, log_a, lam, t):
     """``decode_step`` with q, k [N, Hk, dk] shared by groups of heads."""
     H = states.shape[1]
     return decode_step(states, heads_of_qk(q, H), heads_of_qk(k, H), v, log_a, lam, t)
+
+
+# --------------------------------------------------------------------------
+# lambda from the hidden state
+# --------------------------------------------------------------------------
+# [P1] 循环形式与输出计算: the level weights lambda_t^l are data dependent and
+# non-negative, obtained by a linear projection of the token's hidden
+# representation x_t with per-head parameters.  Reading (the map that makes
+# them non-negative is not named): softplus of an affine map,
+#   lambda[b, h, t, l] = softplus(sum_d x[b, t, d] W[h*L + l, d] + bias[h*L + l]),
+# softplus(z) = log(1 + exp(z)).
+
+def softplus(z) -> np.ndarray:
+    """log(1 + exp(z)) in fp64, without overflow for large z."""
+    z = _f64(z)
+    return np.logaddexp(0.0, z)
+
+
+def lambda_projection(x, W, bias, H: int, L: int) -> np.ndarray:
+    """x: [B, T, D]; W: [H*L, D] (row h*L + l holds head h, level l);
+    bias: [H*L] or None.  Returns lambda [B, H, T, L] float64."""
+    x, W = _f64(x), _f64(W)
+    B, T, D = x.shape
+    if W.shape != (H * L, D):
+        raise ValueError(f"W must be [{H * L}, {D}]")
+    z = x.reshape(B * T, D) @ W.T
+    if bias is not None:
+        z = z + _f64(bias)[None, :]
+    lam = softplus(z).reshape(B, T, H, L)
+    return np.ascontiguousarray(lam.transpose(0, 2, 1, 3))

@@ -496,3 +496,47 @@ def test_mva_decode_is_the_per_head_decode_on_repeated_qk():
     o2, s2 = oracle.decode_step(S, qh, kh, v, la, lam, t)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(s1, s2)
+
+
+# ------------------------------------------------- lambda from the hidden state
+
+def test_softplus_closed_forms():
+    """softplus(0) = ln 2; softplus(z) - softplus(-z) = z; large z -> z;
+    very negative z -> exp(z)."""
+    assert oracle.softplus(0.0) == pytest.approx(math.log(2.0), rel=0, abs=1e-15)
+    z = np.linspace(-30, 30, 61)
+    np.testing.assert_allclose(oracle.softplus(z) - oracle.softplus(-z), z, rtol=0, atol=1e-12)
+    assert oracle.softplus(800.0) == 800.0
+    assert oracle.softplus(-50.0) == pytest.approx(math.exp(-50.0), rel=1e-12)
+
+
+def test_lambda_projection_brute_force():
+    """[P1] 循环形式与输出计算: per-head linear map of x_t, made non-negative
+    (softplus reading), by explicit loops over every output element."""
+    rng = np.random.default_rng(51)
+    B, T, D, H, L = 2, 5, 7, 3, 4
+    x = rng.standard_normal((B, T, D))
+    W = rng.standard_normal((H * L, D))
+    bias = rng.standard_normal(H * L)
+    got = oracle.lambda_projection(x, W, bias, H, L)
+    assert got.shape == (B, H, T, L)
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                for l in range(L):
+                    z = sum(x[b, t, d] * W[h * L + l, d] for d in range(D)) + bias[h * L + l]
+                    assert got[b, h, t, l] == pytest.approx(math.log1p(math.exp(z)), rel=1e-12)
+    assert np.all(got > 0)
+
+
+def test_lambda_projection_one_hot_rows_land_in_place():
+    """A one-hot row of W copies one hidden coordinate to exactly one
+    (head, level) slot: the output layout is [B, H, T, L]."""
+    B, T, D, H, L = 1, 3, 4, 2, 3
+    x = np.arange(B * T * D, dtype=np.float64).reshape(B, T, D) / 10.0
+    W = np.zeros((H * L, D))
+    W[1 * L + 2, 3] = 1.0          # head 1, level 2 <- x[..., 3]
+    got = oracle.lambda_projection(x, W, None, H, L)
+    want = np.full((B, H, T, L), math.log(2.0))
+    want[0, 1, :, 2] = np.log1p(np.exp(x[0, :, 3]))
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=0)
