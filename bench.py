@@ -4,9 +4,11 @@
 
 A step is one loglinear_fwd call (segment-state, node and sweep kernels) over
 one batch of synthetic inputs already resident in HBM.  Prints ONE JSON line;
-at the default workload it also carries a "decode" object: one decode step of
-64 sequences x 16 heads (L = 17) timed the same way.  --pass bwd / decode time
-the backward or only the decode step instead.
+at the default workload it also carries a "decode" object (one decode step of
+64 sequences x 16 heads, L = 17) and a "lambda_proj" object (the level-weight
+projection at the same B, T, H, L with hidden width 2048), timed the same way.
+--pass bwd / decode / lambda time only the backward, the decode step or the
+projection.
 Default workload: log-linear Mamba-2 forward, B=2, H=16, T=16384, dk=dv=128,
 bf16 q/k/v, fp32 log_a / lambda / out, L=15, C=64.
 """
@@ -117,6 +119,41 @@ def bench_decode(dev, steps: int, warmup: int):
     }
 
 
+def bench_lambda(dev, steps: int, warmup: int):
+    """The level-weight projection (loglinear_lambda_proj) at the bench
+    forward's shape: x [2, 16384, 2048] bf16 (hidden width H * dv), W [240, 2048]
+    bf16, bias fp32 -> lambda [2, 16, 16384, 15] fp32; three x buffers rotated."""
+    import torch
+    import log_linear_attention_attn_amd as ll
+    import workloads as W
+    w = W.LAMBDA_LM_T16K
+    x, Wt, b = W.make_lambda_proj_inputs(w)
+    xs = [x.to(dev)] + [x.to(dev) for _ in range(2)]
+    Wt, b = Wt.to(dev), b.to(dev)
+    out = torch.empty(w.B, w.H, w.T, w.L, dtype=torch.float32, device=dev)
+    for i in range(warmup):
+        ll.lambda_proj(xs[i % 3], Wt, b, w.H, w.L, out=out)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        ll.lambda_proj(xs[i % 3], Wt, b, w.H, w.L, out=out)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    ib = 2 if w.dtype == "bf16" else 4
+    nbytes = w.B * w.T * w.D * ib + w.H * w.L * (w.D * ib + 4) + w.B * w.H * w.T * w.L * 4
+    flops = 2 * w.B * w.T * w.D * w.H * w.L
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": w.name, "B": w.B, "T": w.T, "D": w.D, "H": w.H, "L": w.L, "dtype": w.dtype,
+        "steps": steps, "ms_per_step": ms, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "roofline": {"kernel": "lambda_proj_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
+    }
+
+
 def source_hash() -> str:
     from log_linear_attention_attn_amd.profiling import source_hash as h
     return h()
@@ -202,9 +239,10 @@ def main():
     ap.add_argument("--workload", default="lm_B2H16_T16384_dk128_dv128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-log2", type=int, default=-1)
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode"], default="fwd",
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode", "lambda"], default="fwd",
                     help="time the forward (default, the headline; its line also carries one "
-                         "decode measurement), the backward, or only the decode step")
+                         "decode and one lambda-projection measurement), the backward, or only the "
+                         "decode step or the lambda projection")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -225,6 +263,16 @@ def main():
     torch.cuda.set_device(dev)
     if args.which == "bwd":
         bench_bwd(args, w, dev)
+        return
+    if args.which == "lambda":
+        rec = bench_lambda(dev, args.steps, args.warmup)
+        print(json.dumps({
+            "metric": "lambda projection GB/s (algorithmic HBM bytes / time)", "value": rec["roofline"]["achieved"],
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": rec["dtype"], "data": "synthetic",
+            "config": {k: rec[k] for k in ("workload", "B", "T", "D", "H", "L")},
+            "roofline": rec["roofline"], "tflops": rec["tflops"]}))
         return
     if args.which == "decode":
         rec = bench_decode(dev, args.steps, args.warmup)
@@ -330,6 +378,7 @@ def main():
     }
     if args.workload == W.LM_T16K.name:
         rec["decode"] = bench_decode(dev, K, Wm)
+        rec["lambda_proj"] = bench_lambda(dev, K, Wm)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec))

@@ -210,6 +210,26 @@ int loglinear_bwd_ex(const void* q, const void* k, const void* v, const float* l
                      float* grad_k, float* grad_v, float* grad_log_a, float* grad_lambda, int B,
                      int H, int T, int dk, int dv, int C, int dtype, int qk_heads, void* stream);
 
+/*
+ * Level weights from the hidden state (page above, section 循环形式与输出计算:
+ * a per-head linear projection of the token's hidden representation, made
+ * non-negative; the map is read as softplus):
+ *   lambda[b, h, t, l] = softplus(sum_d x[b, t, d] * W[h*L + l, d] + bias[h*L + l])
+ * with softplus(z) = log(1 + exp(z)), fused into one kernel (matrix cores,
+ * fp32 accumulation; bias, softplus and the [B, H, T, L] layout applied before
+ * the only store).
+ *   x      : [B, T, D] DEVICE, LL_BF16 (bf16 bits) or LL_F32 per `dtype`
+ *   W      : [H*L, D] DEVICE, same type as x; row h*L + l is head h, level l
+ *   bias   : [H*L] fp32 DEVICE, or NULL for none
+ *   lambda : [B, H, T, L] fp32 DEVICE output (L = loglinear_num_levels(T)
+ *            for use with loglinear_fwd; any 1 <= L <= 31 is accepted)
+ * D must be a multiple of 8 (bf16) or 4 (fp32) and x, W 16-byte aligned, else
+ * LL_ERR_SHAPE; D or H*L above 2^20 give LL_ERR_UNSUPPORTED.  B = 0 or T = 0
+ * is a no-op.  Asynchronous on `stream`; allocates nothing.
+ */
+int loglinear_lambda_proj(const void* x, const void* W, const float* bias, float* lambda, int B,
+                          int T, int D, int H, int L, int dtype, void* stream);
+
 /* Workspace bytes loglinear_fwd_ex needs for these sizes (0 if none); seg_log2
  * as in loglinear_fwd_opts.  Returns (size_t)-1 for invalid sizes. */
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2);

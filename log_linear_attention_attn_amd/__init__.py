@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "loglinear_prefill", "loglinear_prefill_f32", "loglinear_bwd", "loglinear_bwd_f32",
     "loglinear_bwd_ex", "loglinear_fwd_workspace_size",
     "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_decode_step_ex",
-    "loglinear_level_table",
+    "loglinear_level_table", "loglinear_lambda_proj",
     "loglinear_strerror",
 )
 
@@ -105,6 +105,8 @@ def lib():
     L.loglinear_decode_step_f32.restype = i
     L.loglinear_decode_step_ex.argtypes = dec_args[:-1] + [i, i, vp]
     L.loglinear_decode_step_ex.restype = i
+    L.loglinear_lambda_proj.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    L.loglinear_lambda_proj.restype = i
     L.loglinear_level_table.argtypes = [vp, i, vp]
     L.loglinear_level_table.restype = i
     L.loglinear_strerror.argtypes = [i]
@@ -371,6 +373,32 @@ def decode_step(states, q, k, v, log_a, lam, t, out=None):
         f = lib().loglinear_decode_step if q.dtype == torch.bfloat16 else lib().loglinear_decode_step_f32
         st = f(*args, _stream(dev))
     _raise(st, "loglinear_decode_step")
+    return out
+
+
+def lambda_proj(x, W, bias, H: int, L: int, out=None):
+    """Level weights from the hidden state (loglinear_lambda_proj):
+    lambda[b, h, t, l] = softplus(x[b, t] . W[h*L + l] + bias[h*L + l]).
+
+    x: [B, T, D] and W: [H*L, D], both bf16 or both fp32; bias: [H*L] fp32 or
+    None.  Returns lambda [B, H, T, L] fp32 (allocated unless given).
+    """
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x, W must be bfloat16 or float32")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, T, D = x.shape
+    _check_dev("x", x, x.dtype, (B, T, D), dev)
+    _check_dev("W", W, x.dtype, (H * L, D), dev)
+    if bias is not None:
+        _check_dev("bias", bias, torch.float32, (H * L,), dev)
+    if out is None:
+        out = torch.empty((B, H, T, L), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (B, H, T, L), dev)
+    st = lib().loglinear_lambda_proj(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), B, T, D, int(H), int(L),
+                                     LL_BF16 if x.dtype == torch.bfloat16 else LL_F32, _stream(dev))
+    _raise(st, "loglinear_lambda_proj")
     return out
 
 

@@ -96,6 +96,15 @@ struct DecArgs {
   int G = 1;  // heads per q/k head: q and k of head bh are row bh / G
 };
 
+struct LamProjArgs {
+  const void* x;      // [B][T][D]
+  const void* W;      // [H*L][D]
+  const float* bias;  // [H*L] or null
+  float* lam;         // [B][H][T][L]
+  int B, T, D, H, L;
+  int ncb;  // column blocks of 256 output columns
+};
+
 int sweep_lds_bytes(int dtype, int C, int DKP, int L, int nslot);
 int launch_sweep(int dtype, int C, int DKP, const FwdArgs& a, int nblocks, hipStream_t s);
 int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStream_t s);
@@ -110,6 +119,8 @@ int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot);
 int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s);
 // out[i][e] = sum_{g < G} in[i * G + g][e] for i < rows, e < elems (elems % 4 == 0)
+int lambda_proj_lds_bytes(int dtype);
+int launch_lambda_proj(int dtype, const LamProjArgs& a, hipStream_t s);
 int launch_group_sum(const float* in, float* out, long long rows, int G, long long elems, hipStream_t s);
 
 }  // namespace ll

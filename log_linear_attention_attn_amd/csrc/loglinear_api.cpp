@@ -222,6 +222,21 @@ int run_decode(int dtype, const loglinear_states* s, const void* q, const void* 
   return ll::launch_decode(dtype, a, stream);
 }
 
+int run_lambda_proj(int dtype, const void* x, const void* W, const float* bias, float* lam, int B, int T,
+                    int D, int H, int L, hipStream_t stream) {
+  if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
+  if (B < 0 || T < 0 || D < 1 || H < 1 || L < 1 || L > 31) return LL_ERR_SHAPE;
+  if (D % (dtype == LL_BF16 ? 8 : 4) != 0) return LL_ERR_SHAPE;  // 16-byte rows
+  if (D > (1 << 20) || (long long)H * L > (1 << 20)) return LL_ERR_UNSUPPORTED;
+  if ((long long)B * T > (1LL << 40)) return LL_ERR_UNSUPPORTED;
+  if (B == 0 || T == 0) return LL_OK;
+  if (!x || !W || !lam) return LL_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(W)) & 15) return LL_ERR_SHAPE;
+  const int ncb = (H * L + 255) / 256;
+  ll::LamProjArgs a{x, W, bias, lam, B, T, D, H, L, ncb};
+  return ll::launch_lambda_proj(dtype, a, stream);
+}
+
 int run_bwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
             const float* lambda, const float* out, const float* dout, float* dq, float* dk_out,
             float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T, int dk, int dv, int C,
@@ -328,6 +343,11 @@ int loglinear_bwd_ex(const void* q, const void* k, const void* v, const float* l
                      int dk, int dv, int C, int dtype, int qk_heads, void* stream) {
   return run_bwd(dtype, q, k, v, log_a, lambda, out, dout, dq, dk_out, dv_out, dlog_a, dlambda, B, H, T,
                  dk, dv, C, qk_heads, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_lambda_proj(const void* x, const void* W, const float* bias, float* lambda, int B, int T,
+                          int D, int H, int L, int dtype, void* stream) {
+  return run_lambda_proj(dtype, x, W, bias, lambda, B, T, D, H, L, static_cast<hipStream_t>(stream));
 }
 
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2) {

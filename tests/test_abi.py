@@ -198,3 +198,16 @@ def test_qk_heads_must_divide_heads():
     desc = ll._States(1, 2, 4, 8, 16, 16)
     assert L.loglinear_decode_step_ex(ctypes.byref(desc), p, p, p, p, p, p, p, 0, 3, None) == LL_ERR_SHAPE
     assert L.loglinear_decode_step_ex(ctypes.byref(desc), p, p, p, p, p, p, p, 5, 2, None) == LL_ERR_SHAPE
+
+
+def test_lambda_proj_argument_errors():
+    L = ll.lib()
+    p = ctypes.c_void_p(16)
+    assert L.loglinear_lambda_proj(p, p, None, p, 1, 4, 16, 2, 3, 2, None) == LL_ERR_SHAPE      # dtype
+    assert L.loglinear_lambda_proj(p, p, None, p, 1, 4, 12, 2, 3, 0, None) == LL_ERR_SHAPE      # D % 8 (bf16)
+    assert L.loglinear_lambda_proj(p, p, None, p, 1, 4, 16, 2, 0, 0, None) == LL_ERR_SHAPE      # L
+    assert L.loglinear_lambda_proj(p, p, None, p, 1, 4, 16, 2, 32, 0, None) == LL_ERR_SHAPE     # L > 31
+    assert L.loglinear_lambda_proj(p, p, None, p, 0, 4, 16, 2, 3, 0, None) == LL_OK            # empty
+    assert L.loglinear_lambda_proj(None, p, None, p, 1, 4, 16, 2, 3, 0, None) == LL_ERR_NULL
+    q = ctypes.c_void_p(18)  # not 16-byte aligned
+    assert L.loglinear_lambda_proj(q, p, None, p, 1, 4, 16, 2, 3, 0, None) == LL_ERR_SHAPE

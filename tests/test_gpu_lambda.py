@@ -1,0 +1,59 @@
+"""GPU parity of the level-weight projection (loglinear_lambda_proj) against
+the oracle's lambda_projection (fp64).  bf16 inputs are exact in fp32 and the
+accumulation is fp32, so the bound is max |gpu - oracle| <= 1e-4 * RMS(oracle)
+for both input types."""
+import numpy as np
+import pytest
+import torch
+
+import log_linear_attention_attn_amd as ll
+import oracle
+import workloads as W
+from gpu_util import F32_TOL, announce, assert_parity, have_gpu, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+CASES = [
+    # (B, T, D, H, L, dtype, bias)
+    (1, 1, 8, 1, 1, "bf16", True),          # one row, one output column
+    (2, 300, 256, 4, 9, "bf16", True),      # ragged rows, one partial column tile
+    (1, 1000, 2048, 16, 15, "bf16", True),  # the bench shape's width, 240 columns
+    (1, 200, 512, 48, 15, "bf16", False),   # 720 columns: three column blocks, no bias
+    (1, 130, 64, 20, 15, "f32", True),      # fp32, two column blocks
+    (3, 77, 100, 3, 7, "f32", False),       # D not a multiple of the 64-wide K slice
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}T{}D{}H{}L{}_{}_bias{}".format(*c))
+def test_lambda_proj_matches_oracle(case):
+    B, T, D, H, L, dtype, bias = case
+    w = W.LambdaProjWorkload("lp", B, T, D, H, L, dtype, bias, seed=T + D)
+    x, Wt, b = W.make_lambda_proj_inputs(w)
+    announce(f"lambda_proj {case}")
+    dx, dW = to_dev(x, Wt)
+    db = b.cuda() if b is not None else None
+    out = torch.full((B, H, T, L), float("nan"), device="cuda")  # every element must be written
+    got = ll.lambda_proj(dx, dW, db, H, L, out=out)
+    torch.cuda.synchronize()
+    want = oracle.lambda_projection(x, Wt, b, H, L)
+    g = got.cpu().numpy()
+    assert np.all(g > 0), "softplus output must be positive"
+    assert_parity(g, want, F32_TOL, f"lambda {case}")
+
+
+def test_lambda_proj_feeds_the_forward():
+    """The projection's output used as the forward's lambda: the result equals
+    the oracle forward on the oracle's lambda (bf16 forward tolerance)."""
+    B, H, T, dk, dv, D = 1, 2, 300, 64, 64, 128
+    L = W.num_levels(T)
+    fw = W.FwdWorkload("lp_fwd", B, H, T, dk, dv, 64, "bf16", decay="weak", seed=3)
+    q, k, v, la, _ = W.make_fwd_inputs(fw)
+    x, Wt, b = W.make_lambda_proj_inputs(W.LambdaProjWorkload("lp_fwd", B, T, D, H, L, "bf16", seed=4))
+    announce("lambda_proj -> fwd")
+    dq, dk_, dv_, dla, dx, dW = to_dev(q, k, v, la, x, Wt)
+    lam = ll.lambda_proj(dx, dW, b.cuda(), H, L)
+    out = ll.fwd(dq, dk_, dv_, dla, lam, C=64)
+    torch.cuda.synchronize()
+    lam_ref = oracle.lambda_projection(x, Wt, b, H, L)
+    from gpu_util import BF16_TOL
+    assert_parity(out.cpu().numpy(), oracle.forward(q, k, v, la, lam_ref), BF16_TOL, "fwd with projected lambda")

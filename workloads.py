@@ -181,3 +181,34 @@ def make_decode_inputs(w: DecodeWorkload, t: np.ndarray | None = None):
         torch.from_numpy(lam),
         torch.from_numpy(t),
     )
+
+
+@dataclasses.dataclass(frozen=True)
+class LambdaProjWorkload:
+    """Hidden states and per-head projection for the level weights."""
+    name: str
+    B: int
+    T: int
+    D: int  # hidden width
+    H: int
+    L: int
+    dtype: str = "bf16"
+    bias: bool = True
+    seed: int = 0
+
+
+# The bench forward's shape with hidden width H * dv = 16 * 128.
+LAMBDA_LM_T16K = LambdaProjWorkload("lambda_B2T16384_D2048_H16_L15", 2, 16384, 2048, 16, 15)
+
+
+def make_lambda_proj_inputs(w: LambdaProjWorkload):
+    """Draw (x, W, bias): x [B, T, D] ~ N(0, 1); W [H*L, D] ~ N(0, 1) / sqrt(D);
+    bias [H*L] ~ N(0, 1) f32 (None when the workload has no bias).  x and W
+    are rounded once to bf16 for bf16 workloads."""
+    rng = np.random.default_rng(w.seed)
+    x = rng.standard_normal((w.B, w.T, w.D), dtype=np.float32)
+    W = rng.standard_normal((w.H * w.L, w.D), dtype=np.float32) * np.float32(1.0 / math.sqrt(w.D))
+    bias = rng.standard_normal(w.H * w.L, dtype=np.float32)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return (torch.from_numpy(x).to(tdt), torch.from_numpy(W).to(tdt),
+            torch.from_numpy(bias) if w.bias else None)
