@@ -118,6 +118,9 @@ int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot);
 int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s);
+// dV / dK reverse sweep on bf16 matrix cores (bf16 inputs, C = 64)
+bool bwd_kv16_ok(const BwdArgs& a);
+int launch_bwd_kv16(const BwdArgs& a, hipStream_t s);
 // out[i][e] = sum_{g < G} in[i * G + g][e] for i < rows, e < elems (elems % 4 == 0)
 int lambda_proj_lds_bytes(int dtype);
 int launch_lambda_proj(int dtype, const LamProjArgs& a, hipStream_t s);

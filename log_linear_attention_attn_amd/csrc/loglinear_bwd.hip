@@ -620,6 +620,10 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dq_kernel<IT, C>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
   }
   // dV and dK
+  if (sizeof(IT) == 2 && C == 64 && bwd_kv16_ok(a)) {
+    const int st = launch_bwd_kv16(a, s);
+    if (st != LL_OK) return st;
+  } else {
   {
     const int bytes = KvCfg<IT, C, 0>::bytes(a.dk, a.L, N, a.nslot);
     if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
@@ -635,6 +639,7 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
       return LL_ERR_HIP;
     hipLaunchKernelGGL((bwd_kv_kernel<IT, C, 1>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
+  }
   }
   hipLaunchKernelGGL((bwd_dlam_intra_kernel<IT, C>), dim3(a.BH * N), dim3(NT), 0, s, a);
   hipLaunchKernelGGL(bwd_dlam_inter_kernel, dim3((a.T + 255) / 256, a.BH), dim3(256), 0, s, a, Lg<C>::v, a.dk / 16);

@@ -1,0 +1,439 @@
+// Backward reverse sweep (dV and dK) on bf16 matrix cores, for bf16 inputs,
+// C = 64, contraction widths that are multiples of 32 up to 128 and up to 8
+// chunk-level Fenwick bits.  Same decomposition as bwd_kv_kernel
+// (loglinear_bwd.hip; [P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制",
+// sections 并行形式, 与已有模型的组合, 训练：分块并行扫描算法):
+//
+//   y_s = sum_{t >= s} M[t,s] (c_t . x_s) a_t,   M[t,s] = lambda[t, l(t,s)] exp(cum_t - cum_s)
+//   MODE 0: dV (a = dO, c = q, x = k);  MODE 1: dK (a = q, c = dO, x = v).
+//
+// One 512-thread workgroup per (b,h, 16 output columns), two waves per SIMD;
+// chunks in reverse order.  Wave w works on key rows 16(w&3)..+15 of a chunk:
+// the two waves of a row tile (w>>2 = 0, 1) take one pair of score tiles and
+// half of the left-half levels each and add their partial outputs through
+// LDS; each wave updates one 16-column tile of the right-half states.  Every product runs as
+// v_mfma_f32_16x16x32_bf16: bf16 inputs are exact operands, fp32 ones (dO,
+// the masked scores, the level states, the weighted a) are split into bf16
+// hi + lo and multiplied term by term (hi*hi + lo*hi + hi*lo where both
+// sides are split), which keeps ~2^-16 of each product.
+//   intra    scores c_t . x_s for the t tiles at or after the wave's s tile,
+//            masked in registers; the masked tile is the A operand of the
+//            product with a^T directly from the accumulator layout (the
+//            contraction order over t is the same permutation on both sides).
+//   left     levels whose bit of n is clear read R_b (complete: converted once
+//            from fp32 to bf16 hi / lo in place when the sweep enters its left
+//            half): y_s += exp(decay s -> reference) x_s . R_b.
+//   right    levels whose bit is set add this chunk to their fp32 state:
+//            R_b[j][i] += sum_t lambda[t, b] exp(cum_t - ref) a_t[j] c_t[i],
+//            with c^T read by the LDS transpose load.
+#include <hip/hip_runtime.h>
+
+#include "ll_device.h"
+#include "ll_internal.h"
+
+namespace ll {
+namespace b16 {
+
+constexpr int C = 64, NW = 8, NT = NW * 64, LOGC = 6, NSMAX = 8;
+constexpr int LDC = 136;  // bf16 rows of c and x (contraction <= 128): 272 bytes
+constexpr int LDAT = 68;  // fp32 a^T rows [16][68]
+constexpr int LDAB = 72;  // bf16 a^T rows [16][72]
+constexpr int LDR = 136;  // level state: fp32 [16][136], or bf16 hi [16][136] + lo [16][136]
+constexpr int R_BYTES = 16 * LDR * 4;
+
+template <int MODE>
+struct KvLay {
+  static constexpr int NCB = MODE == 1 ? 2 : 1;  // c copies: MODE 1 holds dO as bf16 hi, lo
+  static constexpr int NAB = MODE == 0 ? 2 : 1;  // bf16 a^T copies: MODE 0 holds dO hi, lo
+  static constexpr int CS = 0;
+  static constexpr int XS = CS + NCB * C * LDC * 2;
+  static constexpr int ATF = XS + C * LDC * 2;
+  static constexpr int ATB = ATF + 16 * LDAT * 4;
+  static constexpr int WL = ATB + NAB * 16 * LDAB * 2;  // right-half weights [NSMAX][C]
+  static constexpr int CL = WL + NSMAX * C * 4;         // in-chunk prefix of log_a, fp64 [C]
+  static constexpr int R = CL + C * 8;                  // level states [NSMAX]
+  static constexpr int YX = R + NSMAX * R_BYTES;        // partial outputs [4][64] f32x4
+  static constexpr int LAM = YX + 4 * 64 * 16;          // lambda rows of the chunk [C][L]
+  __host__ __device__ static int tot(int L) { return LAM + C * L * 4; }  // chunk totals [N]
+  __host__ __device__ static int bytes(int L, int N) { return tot(L) + ((N * 4 + 15) & ~15); }
+};
+
+typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed 8-byte LDS read: within each 16-lane group, lane i receives
+// element (i & 3) of the 4-element vectors addressed by lanes 4k + (i >> 2).
+__device__ __forceinline__ bf16x4 tr_read(const bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(reinterpret_cast<__attribute__((address_space(3))) char*>(reinterpret_cast<uintptr_t>(p))));
+  return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 frag(const bf16* base, int ld, int row0, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// In-chunk inclusive prefix of log_a (lane = token; tokens past T count 0) and
+// the chunk total, in fp64 like the other backward kernels.
+__device__ __forceinline__ double chunk_prefix(const float* lag, int tok0, int T, int lane, double* total) {
+  double la = tok0 + lane < T ? (double)lag[tok0 + lane] : 0.0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(la, off);
+    if (lane >= off) la += y;
+  }
+  *total = __shfl(la, C - 1);
+  return la;
+}
+
+}  // namespace b16
+
+template <int MODE>
+__global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
+  using namespace b16;
+  using Lay = KvLay<MODE>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int T = a.T, L = a.L, nslot = a.nslot;
+  const int da = MODE == 0 ? a.dv : a.dk;  // output columns
+  const int dc = MODE == 0 ? a.dk : a.dv;  // contraction of c . x
+  const int N = (T + C - 1) / C;
+  bf16* Ch = reinterpret_cast<bf16*>(smem + Lay::CS);
+  bf16* Cl = Ch + C * LDC;  // MODE 1 only
+  bf16* Xs = reinterpret_cast<bf16*>(smem + Lay::XS);
+  float* ATf = reinterpret_cast<float*>(smem + Lay::ATF);
+  bf16* ATh = reinterpret_cast<bf16*>(smem + Lay::ATB);
+  bf16* ATl = ATh + 16 * LDAB;  // MODE 0 only
+  float* WL = reinterpret_cast<float*>(smem + Lay::WL);
+  double* cl_s = reinterpret_cast<double*>(smem + Lay::CL);
+  unsigned char* Rbase = smem + Lay::R;
+  float* lam_s = reinterpret_cast<float*>(smem + Lay::LAM);
+  float* tot_s = reinterpret_cast<float*>(smem + Lay::tot(L));
+  f32x4* Yx = reinterpret_cast<f32x4*>(smem + Lay::YX);
+
+  const int nsl = da / 16;
+  const int bh = blockIdx.x / nsl, js = blockIdx.x - bh * nsl;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int st = w & 3, hf = w >> 2;  // key row tile, half
+  const size_t bhT = (size_t)bh * T, qkT = (size_t)(bh / a.G) * T;
+  const float* __restrict__ lag = a.log_a + bhT;
+  const float* __restrict__ lamg = a.lam + bhT * L;
+  float* __restrict__ yg = (MODE == 0 ? a.dvo : a.dk_out) + bhT * da + 16 * js;
+
+  for (int nn = w; nn < N; nn += NW) {
+    double tot;
+    chunk_prefix(lag, nn * C, T, lane, &tot);
+    if (lane == 0) tot_s[nn] = static_cast<float>(tot);
+  }
+  __syncthreads();
+
+  // Per level (identical in every lane):
+  //   dlt[b] (chunk in the right half): log decay from the level's reference
+  //          (last token of the left half) to the token before this chunk;
+  //   gam[b] (chunk in the left half): log decay from this chunk's last token
+  //          to the reference.
+  float dlt[NSMAX], gam[NSMAX];
+#pragma unroll
+  for (int b = 0; b < NSMAX; ++b) dlt[b] = gam[b] = 0.f;
+
+  for (int n = N - 1; n >= 0; --n) {
+    const int tok0 = n * C;
+    double Atd;
+    const double cl = chunk_prefix(lag, tok0, T, lane, &Atd);
+#pragma unroll
+    for (int b = 0; b < NSMAX; ++b) {
+      if (b < nslot) {
+        const int base = (n >> (b + 1)) << (b + 1);
+        const int rs = base + (1 << b), re = min(N, base + (1 << (b + 1)));
+        if ((n >> b) & 1) {
+          if (n == re - 1) {
+            float d = 0.f;
+            for (int m = rs; m < n; ++m) d += tot_s[m];
+            dlt[b] = uniform(d);
+          } else {
+            dlt[b] = uniform(dlt[b] - tot_s[n]);
+          }
+        } else if (rs < N) {
+          gam[b] = uniform(n == rs - 1 ? 0.f : gam[b] + tot_s[n + 1]);
+        }
+      }
+    }
+    // The level whose right half starts at chunk n + 1 is complete: its state
+    // is converted to bf16 hi / lo (in place, after the staging barrier) for
+    // the left-half reads from this chunk on.
+    const int bc = n + 1 < N ? __builtin_ctz(static_cast<unsigned>(n + 1)) : 32;
+    const bool conv = bc < nslot;
+    const int per = dc / 32;  // state elements per thread: row tid >> 5, columns (tid & 31) * per ..
+    float rv[4];
+    if (conv) {
+      const float* Rf = reinterpret_cast<const float*>(Rbase + bc * R_BYTES) + (tid >> 5) * LDR + (tid & 31) * per;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < per) rv[e] = Rf[e];
+    }
+
+    // ---- stage chunk n (tokens past T are zero)
+    if (MODE == 0) {
+      const bf16* cg = static_cast<const bf16*>(a.q) + qkT * dc;
+      for (int i = tid; i < C * dc / 8; i += NT) {
+        const int r = i / (dc / 8), c = (i - r * (dc / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(Ch + r * LDC + c) =
+            tok0 + r < T ? *reinterpret_cast<const bf16x8*>(cg + (size_t)(tok0 + r) * dc + c) : bf16x8{};
+      }
+    } else {
+      const float* cg = a.dout + bhT * dc;
+      for (int i = tid; i < C * dc / 4; i += NT) {
+        const int r = i / (dc / 4), c = (i - r * (dc / 4)) * 4;
+        const f32x4 x = tok0 + r < T ? *reinterpret_cast<const f32x4*>(cg + (size_t)(tok0 + r) * dc + c) : f32x4{};
+        bf16x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16 x1, x2;
+          split_bf16(x[e], x1, x2);
+          h[e] = x1;
+          l[e] = x2;
+        }
+        *reinterpret_cast<bf16x4*>(Ch + r * LDC + c) = h;
+        *reinterpret_cast<bf16x4*>(Cl + r * LDC + c) = l;
+      }
+    }
+    {
+      const bf16* xg = static_cast<const bf16*>(MODE == 0 ? a.k : a.v) + (MODE == 0 ? qkT : bhT) * dc;
+      for (int i = tid; i < C * dc / 8; i += NT) {
+        const int r = i / (dc / 8), c = (i - r * (dc / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(Xs + r * LDC + c) =
+            tok0 + r < T ? *reinterpret_cast<const bf16x8*>(xg + (size_t)(tok0 + r) * dc + c) : bf16x8{};
+      }
+    }
+    // a^T slice [16][C]: fp32 copy (weights) and bf16 copies (operands)
+    if (tid < 4 * C) {
+      const int r = tid >> 2, c = (tid & 3) * 4;  // one token, four columns per thread
+      const bool ok = tok0 + r < T;
+      float v[4];
+      if (MODE == 0) {
+        const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(a.dout + (bhT + tok0 + r) * da + 16 * js + c) : f32x4{};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = x[e];
+      } else {
+        const bf16x4 x = ok ? *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.q) + (qkT + tok0 + r) * da + 16 * js + c)
+                            : bf16x4{};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(x[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ATf[(c + e) * LDAT + r] = v[e];
+        bf16 x1, x2;
+        split_bf16(v[e], x1, x2);
+        ATh[(c + e) * LDAB + r] = x1;
+        if (MODE == 0) ATl[(c + e) * LDAB + r] = x2;
+      }
+    }
+    for (int i = tid; i < C * L; i += NT) lam_s[i] = tok0 + i / L < T ? lamg[(size_t)tok0 * L + i] : 0.f;
+    if (w == 0) cl_s[lane] = cl;
+    // right-half weights: wave w forms those of level w (lane = token)
+#pragma unroll
+    for (int b = 0; b < NSMAX; ++b)
+      if (b < nslot && b == w && ((n >> b) & 1)) {
+        const float lv = tok0 + lane < T ? lamg[(size_t)(tok0 + lane) * L + LOGC + 1 + b] : 0.f;
+        WL[b * C + lane] = lv * __expf(static_cast<float>(cl) + dlt[b]);
+      }
+    __syncthreads();
+    if (conv) {
+      bf16* Rh = reinterpret_cast<bf16*>(Rbase + bc * R_BYTES) + (tid >> 5) * LDR + (tid & 31) * per;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < per) {
+          bf16 x1, x2;
+          split_bf16(rv[e], x1, x2);
+          Rh[e] = x1;
+          Rh[16 * LDR + e] = x2;
+        }
+      __syncthreads();
+    }
+
+    // ---- intra chunk: this half's pair of t tiles (2hf, 2hf + 1), where at
+    // or after the key tile st (pair 0 is empty for st >= 2)
+    f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+    if (2 * hf + 1 >= st) {
+      f32x4 z[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int tb = 2 * hf + q;
+        z[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tb >= st) {
+          for (int k0 = 0; k0 < dc; k0 += 32) {
+            const bf16x8 xb = frag(Xs, LDC, 16 * st, k0, lane);
+            z[q] = mma(frag(Ch, LDC, 16 * tb, k0, lane), xb, z[q]);
+            if (MODE == 1) z[q] = mma(frag(Cl, LDC, 16 * tb, k0, lane), xb, z[q]);
+          }
+        }
+      }
+      // z[q][r] = c_t . x_s, t = 16(2hf + q) + 4g4 + r, s = 16st + li; masked in place
+      const int s = 16 * st + li;
+      const double cls = cl_s[s];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tb = 2 * hf + q, t = 16 * tb + 4 * g4 + r;
+          z[q][r] = (tb >= st && t >= s)
+                        ? z[q][r] * lam_s[t * L + level_of(t, s)] * __expf(static_cast<float>(cl_s[t] - cls))
+                        : 0.f;
+        }
+      // Y[s][j] += sum_t p[t][s] a_t[j]: the lane's eight t values (4g4 + r of
+      // each tile of the pair) are the contraction slots of both operands
+      {
+        bf16x8 ph, pl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16 x1, x2;
+          split_bf16(z[e >> 2][e & 3], x1, x2);
+          ph[e] = x1;
+          pl[e] = x2;
+        }
+        const int t0 = 32 * hf + 4 * g4;
+        const bf16x8 bh8 = cat(*reinterpret_cast<const bf16x4*>(ATh + li * LDAB + t0),
+                               *reinterpret_cast<const bf16x4*>(ATh + li * LDAB + t0 + 16));
+        Y = mma(ph, bh8, Y);
+        Y = mma(pl, bh8, Y);
+        if (MODE == 0) {
+          const bf16x8 bl8 = cat(*reinterpret_cast<const bf16x4*>(ATl + li * LDAB + t0),
+                                 *reinterpret_cast<const bf16x4*>(ATl + li * LDAB + t0 + 16));
+          Y = mma(ph, bl8, Y);
+        }
+      }
+    }
+
+    // ---- left-half levels (this half's parity): y_s += exp(decay s -> reference) x_s . R_b
+    {
+      bf16x8 xa[4];
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+        if (32 * kq < dc) xa[kq] = frag(Xs, LDC, 16 * st, 32 * kq, lane);
+#pragma unroll
+      for (int b = 0; b < NSMAX; ++b) {
+        if (b < nslot && (b & 1) == hf && !((n >> b) & 1) && ((n >> (b + 1)) << (b + 1)) + (1 << b) < N) {
+          const bf16* Rh = reinterpret_cast<const bf16*>(Rbase + b * R_BYTES);
+          const bf16* Rl = Rh + 16 * LDR;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kq = 0; kq < 4; ++kq)
+            if (32 * kq < dc) {
+              acc = mma(xa[kq], frag(Rh, LDR, 0, 32 * kq, lane), acc);
+              acc = mma(xa[kq], frag(Rl, LDR, 0, 32 * kq, lane), acc);
+            }
+          // acc[r] = x_s . R_b[j], s = 16st + 4g4 + r, j = li
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int s = 16 * st + 4 * g4 + r;
+            Y[r] += __expf(gam[b] + static_cast<float>(Atd - cl_s[s])) * acc[r];
+          }
+        }
+      }
+    }
+    // the second half hands its partial sums to the first, which stores
+    if (hf == 1) Yx[st * 64 + lane] = Y;
+    __syncthreads();
+    if (hf == 0) {
+      const f32x4 y2 = Yx[st * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = tok0 + 16 * st + 4 * g4 + r;
+        if (s < T) yg[(size_t)s * da + li] = Y[r] + y2[r];
+      }
+    }
+
+    // ---- right-half levels: R_b[j][i] += sum_t WL_b[t] a_t[j] c_t[i]
+    {
+      float av[2][8];  // a_t[j = li], t = 32ks + 8g4 + e
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          av[ks][e] = x0[e];
+          av[ks][4 + e] = x1[e];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < NSMAX; ++b) {
+        if (b < nslot && ((n >> b) & 1)) {
+          const int base = (n >> (b + 1)) << (b + 1);
+          const bool first = n == min(N, base + (1 << (b + 1))) - 1;
+          bf16x8 ah[2], al[2];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4 + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              bf16 x1, x2;
+              split_bf16(av[ks][e] * (e < 4 ? w0[e] : w1[e - 4]), x1, x2);
+              ah[ks][e] = x1;
+              al[ks][e] = x2;
+            }
+          }
+          float* Rf = reinterpret_cast<float*>(Rbase + b * R_BYTES);
+          for (int it = w; it < dc / 16; it += NW) {
+            const int i0 = 16 * it;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const int off = (32 * ks + 8 * g4 + (li >> 2)) * LDC + i0 + 4 * (li & 3);
+              const bf16x8 cb = cat(tr_read(Ch + off), tr_read(Ch + off + 4 * LDC));
+              acc = mma(ah[ks], cb, acc);
+              acc = mma(al[ks], cb, acc);
+              if (MODE == 1) acc = mma(ah[ks], cat(tr_read(Cl + off), tr_read(Cl + off + 4 * LDC)), acc);
+            }
+            // acc[r] = sum_t WL_b[t] a_t[j] c_t[i], j = 4g4 + r, i = i0 + li
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float* p = Rf + (4 * g4 + r) * LDR + i0 + li;
+              *p = (first ? 0.f : *p) + acc[r];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+bool bwd_kv16_ok(const BwdArgs& a) {
+  if (a.nslot > b16::NSMAX) return false;
+  for (int dc : {a.dk, a.dv})
+    if (dc % 32 != 0 || dc > 128) return false;
+  const int N = (a.T + b16::C - 1) / b16::C;
+  return b16::KvLay<1>::bytes(a.L, N) <= kMaxLds && b16::KvLay<0>::bytes(a.L, N) <= kMaxLds;
+}
+
+int launch_bwd_kv16(const BwdArgs& a, hipStream_t s) {
+  const int N = (a.T + b16::C - 1) / b16::C;
+  {
+    const int bytes = b16::KvLay<0>::bytes(a.L, N);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv16_kernel<0>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return LL_ERR_HIP;
+    hipLaunchKernelGGL(bwd_kv16_kernel<0>, dim3(a.BH * (a.dv / 16)), dim3(b16::NT), bytes, s, a);
+  }
+  {
+    const int bytes = b16::KvLay<1>::bytes(a.L, N);
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv16_kernel<1>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return LL_ERR_HIP;
+    hipLaunchKernelGGL(bwd_kv16_kernel<1>, dim3(a.BH * (a.dk / 16)), dim3(b16::NT), bytes, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
+}  // namespace ll

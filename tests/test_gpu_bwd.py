@@ -2,10 +2,13 @@
 gradients of the dense definition (fp64 autograd).
 
 Tolerance per gradient: max |gpu - oracle| <= tol * RMS(oracle gradient), with
-tol = 1e-4 (the arithmetic is fp32 for both input types: bf16 inputs are exact
-in fp32).  The oracle receives the same (bf16-rounded) inputs and the forward
-output `out` is the oracle's, so the backward is checked on its own; one
-pipeline case feeds the GPU forward's output instead (bf16 tolerance).
+tol = 1e-4 for fp32 inputs (fp32 matrix-core arithmetic) and the bf16 bound
+2e-2 for bf16 inputs, the same bound as the bf16 forward (the bf16 path runs
+bf16 matrix cores with hi/lo splits of its fp32 operands; its measured error
+is ~1e-3 of the RMS at most, in d log_a under strong decay).  The oracle
+receives the same (bf16-rounded) inputs and the forward output `out` is the
+oracle's, so the backward is checked on its own; one pipeline case feeds the
+GPU forward's output instead.
 """
 import numpy as np
 import pytest
@@ -30,6 +33,8 @@ CASES = [
     (2, 1, 300, 128, 64, 64, "bf16", "weak"),
     (1, 1, 1000, 128, 128, 64, "bf16", "none"),  # every level carries weight
     (1, 2, 1024, 64, 128, 32, "bf16", "weak"),   # T a power of two
+    (1, 2, 700, 128, 128, 64, "bf16", "strong"), # strong decay: heavy-tailed gradients
+    (1, 1, 3000, 128, 64, 64, "bf16", "weak"),   # 47 chunks, six chunk-level bits, ragged
 ]
 
 
@@ -51,8 +56,9 @@ def test_bwd_matches_oracle(case):
     grads = ll.bwd(dq_, dk_, dv_, dla, dlam, out.cuda(), dout.cuda(), C=w.C)
     torch.cuda.synchronize()
     want = oracle.backward(q, k, v, la, lam, dout)
+    tol = BWD_TOL if case[6] == "f32" else BF16_TOL
     for name, g, ref in zip(NAMES, grads, want):
-        assert_parity(g.cpu().numpy(), ref, BWD_TOL, f"{name} {case}")
+        assert_parity(g.cpu().numpy(), ref, tol, f"{name} {case}")
 
 
 def test_bwd_after_gpu_forward():

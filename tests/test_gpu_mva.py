@@ -5,7 +5,8 @@ against the oracle's *_mva functions.
 
 Tolerances as for the per-head paths: forward, states and decode
 max |gpu - oracle| <= 2e-2 * RMS(oracle) for bf16 inputs and 1e-4 * RMS for
-fp32 inputs; backward 1e-4 * RMS of each gradient.
+fp32 inputs; backward 1e-4 * RMS of each gradient for fp32 inputs and the
+bf16 bound for bf16 inputs.
 """
 import numpy as np
 import pytest
@@ -92,4 +93,4 @@ def test_mva_backward(case):
     want = oracle.backward_mva(*inp, dout)
     for name, g, ref in zip(("dq", "dk", "dv", "dlog_a", "dlam"), grads, want):
         assert g.shape == ref.shape, name
-        assert_parity(g.cpu().numpy(), ref, 1e-4, f"{name} {case}")
+        assert_parity(g.cpu().numpy(), ref, 1e-4 if dtype == "f32" else BF16_TOL, f"{name} {case}")
