@@ -121,6 +121,9 @@ int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s);
 // dV / dK reverse sweep on bf16 matrix cores (bf16 inputs, C = 64)
 bool bwd_kv16_ok(const BwdArgs& a);
 int launch_bwd_kv16(const BwdArgs& a, hipStream_t s);
+// dQ / chunk-level dlambda forward sweep on bf16 matrix cores (bf16 inputs, C = 64)
+bool bwd_dq16_ok(const BwdArgs& a);
+int launch_bwd_dq16(const BwdArgs& a, hipStream_t s);
 // out[i][e] = sum_{g < G} in[i * G + g][e] for i < rows, e < elems (elems % 4 == 0)
 int lambda_proj_lds_bytes(int dtype);
 int launch_lambda_proj(int dtype, const LamProjArgs& a, hipStream_t s);

@@ -611,7 +611,10 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int N = (a.T + C - 1) / C;
   constexpr int NT = C / 16 * 64;
   // dQ and the chunk-level dlam partials
-  {
+  if (sizeof(IT) == 2 && C == 64 && bwd_dq16_ok(a)) {
+    const int st = launch_bwd_dq16(a, s);
+    if (st != LL_OK) return st;
+  } else {
     const int bytes = DqCfg<IT, C>::bytes(a.dv, a.L, a.nslot);
     if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<IT, C>),

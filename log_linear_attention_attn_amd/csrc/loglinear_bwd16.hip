@@ -1,4 +1,5 @@
-// Backward reverse sweep (dV and dK) on bf16 matrix cores, for bf16 inputs,
+// Backward sweeps on bf16 matrix cores for bf16 inputs: the reverse sweep
+// (dV and dK) and the forward sweep (dQ and the chunk-level dlambda partials),
 // C = 64, contraction widths that are multiples of 32 up to 128 and up to 8
 // chunk-level Fenwick bits.  Same decomposition as bwd_kv_kernel
 // (loglinear_bwd.hip; [P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制",
@@ -407,6 +408,315 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dq16_kernel: dQ and the chunk-level dlambda partials, forward chunk order
+// (as bwd_dq_kernel): per level b the decayed left-half state
+// St_b[j][i] = sum_s exp(cum_ref - cum_s) k_s[j] v_s[i] is read by the
+// right-half queries, dQ_t[j] += lambda[t, b] exp(cum_t - ref) (dO_t . St_b[j]),
+// and the same products dotted with q_t give the slice's dlambda partial.
+// One 512-thread workgroup per (b,h, 16 columns of dk); wave w works on query
+// rows 16(w&3)..+15 with half w>>2 of the score tiles and of the levels.
+// ---------------------------------------------------------------------------
+namespace b16 {
+struct DqLay {
+  static constexpr int LDQS = 17;                    // fp32 q slice rows [C][17]
+  static constexpr int DH = 0;                       // dO rows, bf16 hi / lo [C][LDC]
+  static constexpr int DL = DH + C * LDC * 2;
+  static constexpr int VS = DL + C * LDC * 2;        // v rows bf16 [C][LDC]
+  static constexpr int KT = VS + C * LDC * 2;        // k slice transposed bf16 [16][LDAB]
+  static constexpr int QS = KT + 16 * LDAB * 2;      // q slice fp32 [C][LDQS]
+  static constexpr int ESF = QS + ((C * LDQS * 4 + 15) & ~15);  // decay to the chunk end [C]
+  static constexpr int CL = ESF + C * 4;             // in-chunk prefix of log_a, fp64 [C]
+  static constexpr int ST = CL + C * 8;              // level states [NSMAX]
+  static constexpr int YX = ST + NSMAX * R_BYTES;    // partial outputs [4][64] f32x4
+  static constexpr int LAM = YX + 4 * 64 * 16;       // lambda rows [C][L]
+  __host__ __device__ static int bytes(int L) { return LAM + C * L * 4; }
+};
+
+// sum over the 16 lanes of each row (DPP rotations and quad swaps)
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x = dpp_sum<0x128>(x);  // row_ror:8
+  x = dpp_sum<0x124>(x);  // row_ror:4
+  x = dpp_sum<0x4e>(x);   // quad_perm [2,3,0,1]
+  x = dpp_sum<0xb1>(x);   // quad_perm [1,0,3,2]
+  return x;
+}
+}  // namespace b16
+
+__global__ void __launch_bounds__(b16::NT) bwd_dq16_kernel(BwdArgs a) {
+  using namespace b16;
+  using Lay = DqLay;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int T = a.T, L = a.L, nslot = a.nslot, dk = a.dk, dv = a.dv;
+  const int N = (T + C - 1) / C;
+  bf16* Dh = reinterpret_cast<bf16*>(smem + Lay::DH);
+  bf16* Dl = reinterpret_cast<bf16*>(smem + Lay::DL);
+  bf16* Vs = reinterpret_cast<bf16*>(smem + Lay::VS);
+  bf16* KTb = reinterpret_cast<bf16*>(smem + Lay::KT);
+  float* Qs = reinterpret_cast<float*>(smem + Lay::QS);
+  float* esf_s = reinterpret_cast<float*>(smem + Lay::ESF);
+  double* cl_s = reinterpret_cast<double*>(smem + Lay::CL);
+  unsigned char* Sbase = smem + Lay::ST;
+  f32x4* Yx = reinterpret_cast<f32x4*>(smem + Lay::YX);
+  float* lam_s = reinterpret_cast<float*>(smem + Lay::LAM);
+
+  const int nsl = dk / 16;
+  const int bh = blockIdx.x / nsl, js = blockIdx.x - bh * nsl;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int tt = w & 3, hf = w >> 2;  // query row tile, half
+  const size_t bhT = (size_t)bh * T, qkT = (size_t)(bh / a.G) * T;
+  const bf16* __restrict__ qg = static_cast<const bf16*>(a.q) + qkT * dk + 16 * js;
+  const bf16* __restrict__ kg = static_cast<const bf16*>(a.k) + qkT * dk + 16 * js;
+  const bf16* __restrict__ vg = static_cast<const bf16*>(a.v) + bhT * dv;
+  const float* __restrict__ dog = a.dout + bhT * dv;
+  const float* __restrict__ lag = a.log_a + bhT;
+  const float* __restrict__ lamg = a.lam + bhT * L;
+  float* __restrict__ dqg = a.dq + bhT * dk + 16 * js;
+  const int nsl1 = nslot > 0 ? nslot : 1;
+  float* __restrict__ part = a.dlam_part + ((size_t)js * a.BH + bh) * T * nsl1;
+
+  // dlt[b] (chunk in the right half of level b): log decay from the level's
+  // reference (last token of the left half) to the token before this chunk
+  float dlt[NSMAX];
+#pragma unroll
+  for (int b = 0; b < NSMAX; ++b) dlt[b] = 0.f;
+  float Aprev = 0.f;
+  for (int n = 0; n < N; ++n) {
+    const int tok0 = n * C;
+    double Atd;
+    const double cl = chunk_prefix(lag, tok0, T, lane, &Atd);
+#pragma unroll
+    for (int b = 0; b < NSMAX; ++b)
+      if (b < nslot && ((n >> b) & 1)) {
+        const int rs = ((n >> (b + 1)) << (b + 1)) + (1 << b);
+        dlt[b] = uniform(n == rs ? 0.f : dlt[b] + Aprev);
+      }
+    // the level whose right half starts here has a complete left-half state:
+    // converted to bf16 hi / lo in place after the staging barrier
+    const int bc = n > 0 ? __builtin_ctz(static_cast<unsigned>(n)) : 32;
+    const bool conv = bc < nslot;
+    const int per = dv / 32;
+    float rv[4];
+    if (conv) {
+      const float* Sf = reinterpret_cast<const float*>(Sbase + bc * R_BYTES) + (tid >> 5) * LDR + (tid & 31) * per;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < per) rv[e] = Sf[e];
+    }
+
+    // ---- stage chunk n (tokens past T are zero)
+    for (int i = tid; i < C * dv / 4; i += NT) {
+      const int r = i / (dv / 4), c = (i - r * (dv / 4)) * 4;
+      const f32x4 x = tok0 + r < T ? *reinterpret_cast<const f32x4*>(dog + (size_t)(tok0 + r) * dv + c) : f32x4{};
+      bf16x4 h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf16 x1, x2;
+        split_bf16(x[e], x1, x2);
+        h[e] = x1;
+        l[e] = x2;
+      }
+      *reinterpret_cast<bf16x4*>(Dh + r * LDC + c) = h;
+      *reinterpret_cast<bf16x4*>(Dl + r * LDC + c) = l;
+    }
+    for (int i = tid; i < C * dv / 8; i += NT) {
+      const int r = i / (dv / 8), c = (i - r * (dv / 8)) * 8;
+      *reinterpret_cast<bf16x8*>(Vs + r * LDC + c) =
+          tok0 + r < T ? *reinterpret_cast<const bf16x8*>(vg + (size_t)(tok0 + r) * dv + c) : bf16x8{};
+    }
+    if (tid < 4 * C) {  // k and q slices: one token, four columns per thread
+      const int r = tid >> 2, c = (tid & 3) * 4;
+      const bool ok = tok0 + r < T;
+      const bf16x4 kx = ok ? *reinterpret_cast<const bf16x4*>(kg + (size_t)(tok0 + r) * dk + c) : bf16x4{};
+      const bf16x4 qx = ok ? *reinterpret_cast<const bf16x4*>(qg + (size_t)(tok0 + r) * dk + c) : bf16x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        KTb[(c + e) * LDAB + r] = kx[e];
+        Qs[r * DqLay::LDQS + c + e] = static_cast<float>(qx[e]);
+      }
+    }
+    for (int i = tid; i < C * L; i += NT) lam_s[i] = tok0 + i / L < T ? lamg[(size_t)tok0 * L + i] : 0.f;
+    if (w == 0) {
+      cl_s[lane] = cl;
+      esf_s[lane] = tok0 + lane < T ? __expf(static_cast<float>(Atd - cl)) : 0.f;
+    }
+    __syncthreads();
+    if (conv) {
+      bf16* Sh = reinterpret_cast<bf16*>(Sbase + bc * R_BYTES) + (tid >> 5) * LDR + (tid & 31) * per;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < per) {
+          bf16 x1, x2;
+          split_bf16(rv[e], x1, x2);
+          Sh[e] = x1;
+          Sh[16 * LDR + e] = x2;
+        }
+      __syncthreads();
+    }
+
+    // ---- intra chunk: this half's pair of s tiles (2hf, 2hf + 1) at or before tt
+    f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+    if (2 * hf <= tt) {
+      f32x4 z[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int sb = 2 * hf + q;
+        z[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (sb <= tt) {
+          for (int k0 = 0; k0 < dv; k0 += 32) {
+            const bf16x8 va = frag(Vs, LDC, 16 * sb, k0, lane);
+            z[q] = mma(va, frag(Dh, LDC, 16 * tt, k0, lane), z[q]);
+            z[q] = mma(va, frag(Dl, LDC, 16 * tt, k0, lane), z[q]);
+          }
+        }
+      }
+      // z[q][r] = v_s . dO_t, s = 16(2hf + q) + 4g4 + r, t = 16tt + li; masked in place
+      const int t = 16 * tt + li;
+      const double clt = cl_s[t];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sb = 2 * hf + q, s = 16 * sb + 4 * g4 + r;
+          z[q][r] = (sb <= tt && s <= t)
+                        ? z[q][r] * lam_s[t * L + level_of(t, s)] * __expf(static_cast<float>(clt - cl_s[s]))
+                        : 0.f;
+        }
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 x1, x2;
+        split_bf16(z[e >> 2][e & 3], x1, x2);
+        ph[e] = x1;
+        pl[e] = x2;
+      }
+      // dQ[t][j] += sum_s p[t][s] k_s[j]: the lane's eight s values are the
+      // contraction slots of both operands
+      const int s0 = 32 * hf + 4 * g4;
+      const bf16x8 kb8 = cat(*reinterpret_cast<const bf16x4*>(KTb + li * LDAB + s0),
+                             *reinterpret_cast<const bf16x4*>(KTb + li * LDAB + s0 + 16));
+      Y = mma(ph, kb8, Y);
+      Y = mma(pl, kb8, Y);
+    }
+    // Y[r]: t = 16tt + 4g4 + r, j = li
+
+    // ---- inter chunk: right-half levels of this half's parity
+    {
+      bf16x8 dah[4], dal[4];
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+        if (32 * kq < dv) {
+          dah[kq] = frag(Dh, LDC, 16 * tt, 32 * kq, lane);
+          dal[kq] = frag(Dl, LDC, 16 * tt, 32 * kq, lane);
+        }
+#pragma unroll
+      for (int b = 0; b < NSMAX; ++b) {
+        if (b < nslot && (b & 1) == hf) {
+          float x[4] = {0.f, 0.f, 0.f, 0.f};
+          if ((n >> b) & 1) {
+            const bf16* Sh = reinterpret_cast<const bf16*>(Sbase + b * R_BYTES);
+            const bf16* Sl = Sh + 16 * LDR;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+              if (32 * kq < dv) {
+                const bf16x8 sh = frag(Sh, LDR, 0, 32 * kq, lane);
+                acc = mma(dah[kq], sh, acc);
+                acc = mma(dal[kq], sh, acc);
+                acc = mma(dah[kq], frag(Sl, LDR, 0, 32 * kq, lane), acc);
+              }
+            // acc[r] = dO_t . St_b[j], t = 16tt + 4g4 + r, j = li
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 16 * tt + 4 * g4 + r;
+              const float wt = __expf(static_cast<float>(cl_s[t]) + dlt[b]) * acc[r];
+              Y[r] += lam_s[t * L + LOGC + 1 + b] * wt;
+              x[r] = wt * Qs[t * DqLay::LDQS + li];
+            }
+          }
+          // this slice's dlambda partial (0 where the level has no bucket)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sx = row_sum16(x[r]);
+            const int t = tok0 + 16 * tt + 4 * g4 + r;
+            if (li == 0 && t < T) part[(size_t)t * nslot + b] = sx;
+          }
+        }
+      }
+    }
+    if (hf == 1) Yx[tt * 64 + lane] = Y;
+    __syncthreads();
+    if (hf == 0) {
+      const f32x4 y2 = Yx[tt * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tok0 + 16 * tt + 4 * g4 + r;
+        if (t < T) dqg[(size_t)t * dk + li] = Y[r] + y2[r];
+      }
+    }
+
+    // ---- key side: this chunk joins the left half of every level whose bit
+    // is clear and whose right half exists; one 16-column tile of v per wave
+    if (16 * w < dv) {
+      const int i0 = 16 * w;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        // A[j][s] = esf_s k_s[j], s = 32ks + 8g4 + e
+        const bf16x8 kx = *reinterpret_cast<const bf16x8*>(KTb + li * LDAB + 32 * ks + 8 * g4);
+        const f32x4 e0 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(esf_s + 32 * ks + 8 * g4 + 4);
+        bf16x8 ah, al;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16 x1, x2;
+          split_bf16(static_cast<float>(kx[e]) * (e < 4 ? e0[e] : e1[e - 4]), x1, x2);
+          ah[e] = x1;
+          al[e] = x2;
+        }
+        const int off = (32 * ks + 8 * g4 + (li >> 2)) * LDC + i0 + 4 * (li & 3);
+        const bf16x8 vb = cat(tr_read(Vs + off), tr_read(Vs + off + 4 * LDC));
+        acc = mma(ah, vb, acc);
+        acc = mma(al, vb, acc);
+      }
+      // acc[r] = sum_s esf_s k_s[j] v_s[i], j = 4g4 + r, i = i0 + li
+      const float fa = __expf(static_cast<float>(Atd));
+#pragma unroll
+      for (int b = 0; b < NSMAX; ++b) {
+        const int base = (n >> (b + 1)) << (b + 1);
+        if (b < nslot && !((n >> b) & 1) && base + (1 << b) < N) {
+          float* Sf = reinterpret_cast<float*>(Sbase + b * R_BYTES);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* p = Sf + (4 * g4 + r) * LDR + i0 + li;
+            *p = (n == base ? 0.f : *p * fa) + acc[r];
+          }
+        }
+      }
+    }
+    Aprev = static_cast<float>(Atd);
+    __syncthreads();
+  }
+}
+
+bool bwd_dq16_ok(const BwdArgs& a) {
+  return a.nslot <= b16::NSMAX && a.dv % 32 == 0 && a.dv <= 128 && b16::DqLay::bytes(a.L) <= kMaxLds;
+}
+
+int launch_bwd_dq16(const BwdArgs& a, hipStream_t s) {
+  const int bytes = b16::DqLay::bytes(a.L);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq16_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          bytes) != hipSuccess)
+    return LL_ERR_HIP;
+  hipLaunchKernelGGL(bwd_dq16_kernel, dim3(a.BH * (a.dk / 16)), dim3(b16::NT), bytes, s, a);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
 bool bwd_kv16_ok(const BwdArgs& a) {
