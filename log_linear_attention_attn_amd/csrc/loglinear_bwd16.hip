@@ -29,6 +29,8 @@
 //            with c^T read by the LDS transpose load.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ll_device.h"
 #include "ll_internal.h"
 
@@ -84,6 +86,16 @@ __device__ __forceinline__ float uniform(float x) {
 
 // In-chunk inclusive prefix of log_a (lane = token; tokens past T count 0) and
 // the chunk total, in fp64 like the other backward kernels.
+__device__ __forceinline__ double prefix64(float x, int lane, double* total) {
+  double la = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(la, off);
+    if (lane >= off) la += y;
+  }
+  *total = __shfl(la, C - 1);
+  return la;
+}
 __device__ __forceinline__ double chunk_prefix(const float* lag, int tok0, int T, int lane, double* total) {
   double la = tok0 + lane < T ? (double)lag[tok0 + lane] : 0.0;
 #pragma unroll
@@ -145,10 +157,55 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
 #pragma unroll
   for (int b = 0; b < NSMAX; ++b) dlt[b] = gam[b] = 0.f;
 
+  // register prefetch of one chunk (issued a chunk ahead of its staging)
+  typedef typename std::conditional<MODE == 0, bf16x8, f32x4>::type CV;  // 16-byte vector of c
+  constexpr int CE = MODE == 0 ? 8 : 4;  // elements of c per vector
+  typedef typename std::conditional<MODE == 0, f32x4, bf16x4>::type AV;  // four columns of a
+  CV pc[4];       // c rows, vectors tid + NT*i
+  bf16x8 px[2];   // x rows
+  AV pa;          // a slice (threads < 4C)
+  float plam[4];  // lambda words tid + NT*i of the chunk
+  float pla;      // log_a of token lane
+  const void* cbase = MODE == 0 ? static_cast<const void*>(static_cast<const bf16*>(a.q) + qkT * dc)
+                                : static_cast<const void*>(a.dout + bhT * dc);
+  const bf16* xg = static_cast<const bf16*>(MODE == 0 ? a.k : a.v) + (MODE == 0 ? qkT : bhT) * dc;
+  auto load = [&](int nn) {
+    const int t0 = nn * C;
+    pla = t0 + lane < T ? lag[t0 + lane] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i, r = idx / (dc / CE), c = (idx - r * (dc / CE)) * CE;
+      if (idx < C * dc / CE)
+        pc[i] = t0 + r < T ? *reinterpret_cast<const CV*>(static_cast<const char*>(cbase) +
+                                                         ((size_t)(t0 + r) * dc + c) * (MODE == 0 ? 2 : 4))
+                           : CV{};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + NT * i, r = idx / (dc / 8), c = (idx - r * (dc / 8)) * 8;
+      if (idx < C * dc / 8)
+        px[i] = t0 + r < T ? *reinterpret_cast<const bf16x8*>(xg + (size_t)(t0 + r) * dc + c) : bf16x8{};
+    }
+    if (tid < 4 * C) {
+      const int r = tid >> 2, c = (tid & 3) * 4;
+      const bool ok = t0 + r < T;
+      if (MODE == 0)
+        pa = ok ? *reinterpret_cast<const AV*>(a.dout + (bhT + t0 + r) * da + 16 * js + c) : AV{};
+      else
+        pa = ok ? *reinterpret_cast<const AV*>(static_cast<const bf16*>(a.q) + (qkT + t0 + r) * da + 16 * js + c)
+                : AV{};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i;
+      if (idx < C * L) plam[i] = t0 + idx / L < T ? lamg[(size_t)t0 * L + idx] : 0.f;
+    }
+  };
+  load(N - 1);
   for (int n = N - 1; n >= 0; --n) {
     const int tok0 = n * C;
     double Atd;
-    const double cl = chunk_prefix(lag, tok0, T, lane, &Atd);
+    const double cl = prefix64(pla, lane, &Atd);
 #pragma unroll
     for (int b = 0; b < NSMAX; ++b) {
       if (b < nslot) {
@@ -181,54 +238,40 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
         if (e < per) rv[e] = Rf[e];
     }
 
-    // ---- stage chunk n (tokens past T are zero)
-    if (MODE == 0) {
-      const bf16* cg = static_cast<const bf16*>(a.q) + qkT * dc;
-      for (int i = tid; i < C * dc / 8; i += NT) {
-        const int r = i / (dc / 8), c = (i - r * (dc / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(Ch + r * LDC + c) =
-            tok0 + r < T ? *reinterpret_cast<const bf16x8*>(cg + (size_t)(tok0 + r) * dc + c) : bf16x8{};
-      }
-    } else {
-      const float* cg = a.dout + bhT * dc;
-      for (int i = tid; i < C * dc / 4; i += NT) {
-        const int r = i / (dc / 4), c = (i - r * (dc / 4)) * 4;
-        const f32x4 x = tok0 + r < T ? *reinterpret_cast<const f32x4*>(cg + (size_t)(tok0 + r) * dc + c) : f32x4{};
-        bf16x4 h, l;
+    // ---- stage chunk n from the registers (tokens past T are zero), then
+    // prefetch chunk n - 1
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bf16 x1, x2;
-          split_bf16(x[e], x1, x2);
-          h[e] = x1;
-          l[e] = x2;
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i, r = idx / (dc / CE), c = (idx - r * (dc / CE)) * CE;
+      if (idx < C * dc / CE) {
+        if (MODE == 0) {
+          *reinterpret_cast<bf16x8*>(Ch + r * LDC + c) = __builtin_bit_cast(bf16x8, pc[i]);
+        } else {
+          const f32x4 x = __builtin_bit_cast(f32x4, pc[i]);
+          bf16x4 h, l;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bf16 x1, x2;
+            split_bf16(x[e], x1, x2);
+            h[e] = x1;
+            l[e] = x2;
+          }
+          *reinterpret_cast<bf16x4*>(Ch + r * LDC + c) = h;
+          *reinterpret_cast<bf16x4*>(Cl + r * LDC + c) = l;
         }
-        *reinterpret_cast<bf16x4*>(Ch + r * LDC + c) = h;
-        *reinterpret_cast<bf16x4*>(Cl + r * LDC + c) = l;
       }
     }
-    {
-      const bf16* xg = static_cast<const bf16*>(MODE == 0 ? a.k : a.v) + (MODE == 0 ? qkT : bhT) * dc;
-      for (int i = tid; i < C * dc / 8; i += NT) {
-        const int r = i / (dc / 8), c = (i - r * (dc / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(Xs + r * LDC + c) =
-            tok0 + r < T ? *reinterpret_cast<const bf16x8*>(xg + (size_t)(tok0 + r) * dc + c) : bf16x8{};
-      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + NT * i, r = idx / (dc / 8), c = (idx - r * (dc / 8)) * 8;
+      if (idx < C * dc / 8) *reinterpret_cast<bf16x8*>(Xs + r * LDC + c) = px[i];
     }
     // a^T slice [16][C]: fp32 copy (weights) and bf16 copies (operands)
     if (tid < 4 * C) {
       const int r = tid >> 2, c = (tid & 3) * 4;  // one token, four columns per thread
-      const bool ok = tok0 + r < T;
       float v[4];
-      if (MODE == 0) {
-        const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(a.dout + (bhT + tok0 + r) * da + 16 * js + c) : f32x4{};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = x[e];
-      } else {
-        const bf16x4 x = ok ? *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.q) + (qkT + tok0 + r) * da + 16 * js + c)
-                            : bf16x4{};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(x[e]);
-      }
+      for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(pa[e]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ATf[(c + e) * LDAT + r] = v[e];
@@ -238,7 +281,12 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
         if (MODE == 0) ATl[(c + e) * LDAB + r] = x2;
       }
     }
-    for (int i = tid; i < C * L; i += NT) lam_s[i] = tok0 + i / L < T ? lamg[(size_t)tok0 * L + i] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i;
+      if (idx < C * L) lam_s[idx] = plam[i];
+    }
+    if (n > 0) load(n - 1);
     if (w == 0) cl_s[lane] = cl;
     // right-half weights: wave w forms those of level w (lane = token)
 #pragma unroll
@@ -488,10 +536,44 @@ __global__ void __launch_bounds__(b16::NT) bwd_dq16_kernel(BwdArgs a) {
 #pragma unroll
   for (int b = 0; b < NSMAX; ++b) dlt[b] = 0.f;
   float Aprev = 0.f;
+  // register prefetch of one chunk (issued a chunk ahead of its staging)
+  f32x4 pd[4];     // dO rows, 16-byte vectors tid + NT*i
+  bf16x8 pv[2];    // v rows
+  bf16x4 pk, pq;   // k and q slices (threads < 4C)
+  float plam[4];   // lambda words tid + NT*i of the chunk
+  float pla;       // log_a of token lane
+  auto load = [&](int nn) {
+    const int t0 = nn * C;
+    pla = t0 + lane < T ? lag[t0 + lane] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i, r = idx / (dv / 4), c = (idx - r * (dv / 4)) * 4;
+      if (idx < C * dv / 4)
+        pd[i] = t0 + r < T ? *reinterpret_cast<const f32x4*>(dog + (size_t)(t0 + r) * dv + c) : f32x4{};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + NT * i, r = idx / (dv / 8), c = (idx - r * (dv / 8)) * 8;
+      if (idx < C * dv / 8)
+        pv[i] = t0 + r < T ? *reinterpret_cast<const bf16x8*>(vg + (size_t)(t0 + r) * dv + c) : bf16x8{};
+    }
+    if (tid < 4 * C) {
+      const int r = tid >> 2, c = (tid & 3) * 4;
+      const bool ok = t0 + r < T;
+      pk = ok ? *reinterpret_cast<const bf16x4*>(kg + (size_t)(t0 + r) * dk + c) : bf16x4{};
+      pq = ok ? *reinterpret_cast<const bf16x4*>(qg + (size_t)(t0 + r) * dk + c) : bf16x4{};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i;
+      if (idx < C * L) plam[i] = t0 + idx / L < T ? lamg[(size_t)t0 * L + idx] : 0.f;
+    }
+  };
+  load(0);
   for (int n = 0; n < N; ++n) {
     const int tok0 = n * C;
     double Atd;
-    const double cl = chunk_prefix(lag, tok0, T, lane, &Atd);
+    const double cl = prefix64(pla, lane, &Atd);
 #pragma unroll
     for (int b = 0; b < NSMAX; ++b)
       if (b < nslot && ((n >> b) & 1)) {
@@ -511,38 +593,43 @@ __global__ void __launch_bounds__(b16::NT) bwd_dq16_kernel(BwdArgs a) {
         if (e < per) rv[e] = Sf[e];
     }
 
-    // ---- stage chunk n (tokens past T are zero)
-    for (int i = tid; i < C * dv / 4; i += NT) {
-      const int r = i / (dv / 4), c = (i - r * (dv / 4)) * 4;
-      const f32x4 x = tok0 + r < T ? *reinterpret_cast<const f32x4*>(dog + (size_t)(tok0 + r) * dv + c) : f32x4{};
-      bf16x4 h, l;
+    // ---- stage chunk n from the registers (tokens past T are zero), then
+    // prefetch chunk n + 1
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bf16 x1, x2;
-        split_bf16(x[e], x1, x2);
-        h[e] = x1;
-        l[e] = x2;
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i, r = idx / (dv / 4), c = (idx - r * (dv / 4)) * 4;
+      if (idx < C * dv / 4) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16 x1, x2;
+          split_bf16(pd[i][e], x1, x2);
+          h[e] = x1;
+          l[e] = x2;
+        }
+        *reinterpret_cast<bf16x4*>(Dh + r * LDC + c) = h;
+        *reinterpret_cast<bf16x4*>(Dl + r * LDC + c) = l;
       }
-      *reinterpret_cast<bf16x4*>(Dh + r * LDC + c) = h;
-      *reinterpret_cast<bf16x4*>(Dl + r * LDC + c) = l;
     }
-    for (int i = tid; i < C * dv / 8; i += NT) {
-      const int r = i / (dv / 8), c = (i - r * (dv / 8)) * 8;
-      *reinterpret_cast<bf16x8*>(Vs + r * LDC + c) =
-          tok0 + r < T ? *reinterpret_cast<const bf16x8*>(vg + (size_t)(tok0 + r) * dv + c) : bf16x8{};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + NT * i, r = idx / (dv / 8), c = (idx - r * (dv / 8)) * 8;
+      if (idx < C * dv / 8) *reinterpret_cast<bf16x8*>(Vs + r * LDC + c) = pv[i];
     }
     if (tid < 4 * C) {  // k and q slices: one token, four columns per thread
       const int r = tid >> 2, c = (tid & 3) * 4;
-      const bool ok = tok0 + r < T;
-      const bf16x4 kx = ok ? *reinterpret_cast<const bf16x4*>(kg + (size_t)(tok0 + r) * dk + c) : bf16x4{};
-      const bf16x4 qx = ok ? *reinterpret_cast<const bf16x4*>(qg + (size_t)(tok0 + r) * dk + c) : bf16x4{};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        KTb[(c + e) * LDAB + r] = kx[e];
-        Qs[r * DqLay::LDQS + c + e] = static_cast<float>(qx[e]);
+        KTb[(c + e) * LDAB + r] = pk[e];
+        Qs[r * DqLay::LDQS + c + e] = static_cast<float>(pq[e]);
       }
     }
-    for (int i = tid; i < C * L; i += NT) lam_s[i] = tok0 + i / L < T ? lamg[(size_t)tok0 * L + i] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i;
+      if (idx < C * L) lam_s[idx] = plam[i];
+    }
+    if (n + 1 < N) load(n + 1);
     if (w == 0) {
       cl_s[lane] = cl;
       esf_s[lane] = tok0 + lane < T ? __expf(static_cast<float>(Atd - cl)) : 0.f;
