@@ -124,6 +124,9 @@ int launch_bwd_kv16(const BwdArgs& a, hipStream_t s);
 // dQ / chunk-level dlambda forward sweep on bf16 matrix cores (bf16 inputs, C = 64)
 bool bwd_dq16_ok(const BwdArgs& a);
 int launch_bwd_dq16(const BwdArgs& a, hipStream_t s);
+// in-chunk dlambda on bf16 matrix cores (bf16 inputs, C = 64)
+bool bwd_dlam_intra16_ok(const BwdArgs& a);
+int launch_bwd_dlam_intra16(const BwdArgs& a, hipStream_t s);
 // out[i][e] = sum_{g < G} in[i * G + g][e] for i < rows, e < elems (elems % 4 == 0)
 int lambda_proj_lds_bytes(int dtype);
 int launch_lambda_proj(int dtype, const LamProjArgs& a, hipStream_t s);

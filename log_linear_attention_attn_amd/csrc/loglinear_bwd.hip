@@ -644,7 +644,12 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_kv_kernel<IT, C, 1>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
   }
   }
-  hipLaunchKernelGGL((bwd_dlam_intra_kernel<IT, C>), dim3(a.BH * N), dim3(NT), 0, s, a);
+  if (sizeof(IT) == 2 && C == 64 && bwd_dlam_intra16_ok(a)) {
+    const int st = launch_bwd_dlam_intra16(a, s);
+    if (st != LL_OK) return st;
+  } else {
+    hipLaunchKernelGGL((bwd_dlam_intra_kernel<IT, C>), dim3(a.BH * N), dim3(NT), 0, s, a);
+  }
   hipLaunchKernelGGL(bwd_dlam_inter_kernel, dim3((a.T + 255) / 256, a.BH), dim3(256), 0, s, a, Lg<C>::v, a.dk / 16);
   const size_t rows = (size_t)a.BH * a.T;
   hipLaunchKernelGGL((bwd_dcum_kernel<IT>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, a, a.dc);

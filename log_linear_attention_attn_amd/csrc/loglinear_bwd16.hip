@@ -806,6 +806,103 @@ int launch_bwd_dq16(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// bwd_dlam_intra16_kernel: dlambda of the in-chunk levels 0..log2 C,
+//   dlam[t, l] = sum_{s in the chunk, l(t,s) = l} exp(cum_t - cum_s) (q_t . k_s)(dO_t . v_s),
+// one 256-thread workgroup per (b,h, chunk), wave w owning query rows 16w..
+// The two score products run on bf16 matrix cores with fragments loaded
+// straight from global memory (no LDS): q . k exact, dO split hi / lo.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_dlam_intra16_kernel(BwdArgs a) {
+  using namespace b16;
+  const int T = a.T, L = a.L, dk = a.dk, dv = a.dv;
+  const int N = (T + C - 1) / C;
+  const int bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int tok0 = n * C;
+  const size_t bhT = (size_t)bh * T, qkT = (size_t)(bh / a.G) * T;
+  const bf16* __restrict__ qg = static_cast<const bf16*>(a.q) + (qkT + tok0) * dk;
+  const bf16* __restrict__ kg = static_cast<const bf16*>(a.k) + (qkT + tok0) * dk;
+  const bf16* __restrict__ vg = static_cast<const bf16*>(a.v) + (bhT + tok0) * dv;
+  const float* __restrict__ dog = a.dout + (bhT + tok0) * dv;
+  __shared__ double cl_s[C];
+  double Atot;
+  const double cl = chunk_prefix(a.log_a + bhT, tok0, T, lane, &Atot);
+  if (w == 0) cl_s[lane] = cl;
+  __syncthreads();
+  const int t = 16 * w + li;  // query row of this lane in the B operands
+  const bool tok = tok0 + t < T;
+  // B operands of this wave's query rows: q (exact) and dO (hi / lo)
+  bf16x8 qb[4], dh[4], dl[4];
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) {
+    if (32 * kq < dk) qb[kq] = tok ? *reinterpret_cast<const bf16x8*>(qg + (size_t)t * dk + 32 * kq + 8 * g4) : bf16x8{};
+    if (32 * kq < dv) {
+      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+      if (tok) {
+        x0 = *reinterpret_cast<const f32x4*>(dog + (size_t)t * dv + 32 * kq + 8 * g4);
+        x1 = *reinterpret_cast<const f32x4*>(dog + (size_t)t * dv + 32 * kq + 8 * g4 + 4);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16 h, l;
+        split_bf16(e < 4 ? x0[e] : x1[e - 4], h, l);
+        dh[kq][e] = h;
+        dl[kq][e] = l;
+      }
+    }
+  }
+  float acc_l[LOGC + 1];
+#pragma unroll
+  for (int l = 0; l <= LOGC; ++l) acc_l[l] = 0.f;
+  for (int kb = 0; kb <= w; ++kb) {
+    const int srow = 16 * kb + li;  // key row this lane loads for the A operands
+    const bool sok = tok0 + srow < T;
+    f32x4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      if (32 * kq < dk) {
+        const bf16x8 ka = sok ? *reinterpret_cast<const bf16x8*>(kg + (size_t)srow * dk + 32 * kq + 8 * g4) : bf16x8{};
+        z1 = mma(ka, qb[kq], z1);
+      }
+      if (32 * kq < dv) {
+        const bf16x8 va = sok ? *reinterpret_cast<const bf16x8*>(vg + (size_t)srow * dv + 32 * kq + 8 * g4) : bf16x8{};
+        z2 = mma(va, dh[kq], z2);
+        z2 = mma(va, dl[kq], z2);
+      }
+    }
+    // z1[r] = k_s . q_t, z2[r] = v_s . dO_t, s = 16kb + 4g4 + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = 16 * kb + 4 * g4 + r;
+      if (s <= t) {
+        const float x = z1[r] * z2[r] * __expf(static_cast<float>(cl_s[t] - cl_s[s]));
+        const int lev = level_of(t, s);
+#pragma unroll
+        for (int l = 0; l <= LOGC; ++l) acc_l[l] += l == lev ? x : 0.f;
+      }
+    }
+  }
+  // sum over the four lane groups (keys 4g4 + r) of each query
+  float* __restrict__ dl_out = a.dlam + (bhT + tok0 + t) * L;
+#pragma unroll
+  for (int l = 0; l <= LOGC; ++l) {
+    float x = acc_l[l];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    if (g4 == 0 && tok && l < L) dl_out[l] = x;
+  }
+}
+
+bool bwd_dlam_intra16_ok(const BwdArgs& a) { return a.dk % 32 == 0 && a.dk <= 128 && a.dv % 32 == 0 && a.dv <= 128; }
+
+int launch_bwd_dlam_intra16(const BwdArgs& a, hipStream_t s) {
+  const int N = (a.T + b16::C - 1) / b16::C;
+  hipLaunchKernelGGL(bwd_dlam_intra16_kernel, dim3(a.BH * N), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
+
 bool bwd_kv16_ok(const BwdArgs& a) {
   if (a.nslot > b16::NSMAX) return false;
   for (int dc : {a.dk, a.dv})
