@@ -411,17 +411,20 @@ def bench_bwd(args, w, dev):
     flops = algorithmic_flops_bwd(w.B, w.H, w.T, w.dk, w.dv, w.C)
     abytes = algorithmic_bytes_bwd(w.B, w.H, w.T, w.dk, w.dv, w.L, 2 if w.dtype == "bf16" else 4)
     tflops = flops / (ms * 1e-3) / 1e12
+    bf16 = w.dtype == "bf16" and w.C == 64
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_MFMA_TFLOPS
     rec = {
         "metric": "bwd tokens/sec (gradients of q, k, v, log_a, lambda), log-linear Mamba-2",
         "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "C": w.C,
                    "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_a/lambda/out/dout", "pass": "backward"},
         "algorithmic_flops": flops, "algorithmic_bytes": abytes,
-        "roofline": {"kernel": "whole backward (fp32 matrix-core arithmetic)", "bound": "mfma",
-                     "achieved": tflops, "peak": PEAK_F32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_F32_MFMA_TFLOPS, "traffic": None},
+        "roofline": {"kernel": ("whole backward (bf16 matrix cores, hi/lo splits of fp32 operands)"
+                                if bf16 else "whole backward (fp32 matrix-core arithmetic)"),
+                     "bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tflops / peak, "traffic": None},
         "hbm_gbs_algorithmic": abytes / (ms * 1e-3) / 1e9,
     }
     print(json.dumps(rec))
