@@ -1,6 +1,6 @@
 """Benchmark of the log-linear attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 300] [--workload NAME] [--no-cpu-baseline]
 
 A step is one loglinear_fwd call (segment-state, node and sweep kernels) over
 one batch of synthetic inputs already resident in HBM.  Prints ONE JSON line;
@@ -234,8 +234,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: the GPU clocks take ~0.1 s of load to reach steady state")
     ap.add_argument("--workload", default="lm_B2H16_T16384_dk128_dv128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seg-log2", type=int, default=-1)
