@@ -12,7 +12,7 @@
 // chunks in reverse order.  Wave w works on key rows 16(w&3)..+15 of a chunk:
 // the two waves of a row tile (w>>2 = 0, 1) take one pair of score tiles and
 // half of the left-half levels each and add their partial outputs through
-// LDS; each wave updates one 16-column tile of the right-half states.  Every product runs as
+// LDS; wave w updates the state of level w when the chunk is in its right half.  Every product runs as
 // v_mfma_f32_16x16x32_bf16: bf16 inputs are exact operands, fp32 ones (dO,
 // the masked scores, the level states, the weighted a) are split into bf16
 // hi + lo and multiplied term by term (hi*hi + lo*hi + hi*lo where both
@@ -85,17 +85,25 @@ __device__ __forceinline__ float uniform(float x) {
 }
 
 // In-chunk inclusive prefix of log_a (lane = token; tokens past T count 0) and
-// the chunk total, in fp64 like the other backward kernels.
-__device__ __forceinline__ double prefix64(float x, int lane, double* total) {
-  double la = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(la, off);
-    if (lane >= off) la += y;
-  }
-  *total = __shfl(la, C - 1);
-  return la;
+// the chunk total, per chunk of the sweeps: fp32 DPP row shifts and row
+// broadcasts (the sweeps' bf16 arithmetic keeps ~2^-17 anyway; the fp64
+// shuffle version cost ~2K cycles per chunk on the critical path).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
 }
+__device__ __forceinline__ double prefix_dpp(float x, int lane, double* total) {
+  x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  *total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), C - 1));
+  (void)lane;
+  return x;
+}
+// fp64 version for the chunk totals the reverse sweep sums over many chunks
 __device__ __forceinline__ double chunk_prefix(const float* lag, int tok0, int T, int lane, double* total) {
   double la = tok0 + lane < T ? (double)lag[tok0 + lane] : 0.0;
 #pragma unroll
@@ -166,12 +174,15 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
   AV pa;          // a slice (threads < 4C)
   float plam[4];  // lambda words tid + NT*i of the chunk
   float pla;      // log_a of token lane
+  float plw;      // lambda[token lane][log2C + 1 + w]: this wave's right-half weights
   const void* cbase = MODE == 0 ? static_cast<const void*>(static_cast<const bf16*>(a.q) + qkT * dc)
                                 : static_cast<const void*>(a.dout + bhT * dc);
   const bf16* xg = static_cast<const bf16*>(MODE == 0 ? a.k : a.v) + (MODE == 0 ? qkT : bhT) * dc;
   auto load = [&](int nn) {
     const int t0 = nn * C;
     pla = t0 + lane < T ? lag[t0 + lane] : 0.f;
+    // level w + log2C + 1 < L whenever w < nslot
+    plw = w < nslot && t0 + lane < T ? lamg[(size_t)(t0 + lane) * L + LOGC + 1 + w] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + NT * i, r = idx / (dc / CE), c = (idx - r * (dc / CE)) * CE;
@@ -205,7 +216,8 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
   for (int n = N - 1; n >= 0; --n) {
     const int tok0 = n * C;
     double Atd;
-    const double cl = prefix64(pla, lane, &Atd);
+    const double cl = prefix_dpp(pla, lane, &Atd);
+    const float wl_lam = plw;  // this chunk's; the registers are refilled below
 #pragma unroll
     for (int b = 0; b < NSMAX; ++b) {
       if (b < nslot) {
@@ -291,10 +303,7 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
     // right-half weights: wave w forms those of level w (lane = token)
 #pragma unroll
     for (int b = 0; b < NSMAX; ++b)
-      if (b < nslot && b == w && ((n >> b) & 1)) {
-        const float lv = tok0 + lane < T ? lamg[(size_t)(tok0 + lane) * L + LOGC + 1 + b] : 0.f;
-        WL[b * C + lane] = lv * __expf(static_cast<float>(cl) + dlt[b]);
-      }
+      if (b < nslot && b == w && ((n >> b) & 1)) WL[b * C + lane] = wl_lam * __expf(static_cast<float>(cl) + dlt[b]);
     __syncthreads();
     if (conv) {
       bf16* Rh = reinterpret_cast<bf16*>(Rbase + bc * R_BYTES) + (tid >> 5) * LDR + (tid & 31) * per;
@@ -401,55 +410,46 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
       }
     }
 
-    // ---- right-half levels: R_b[j][i] += sum_t WL_b[t] a_t[j] c_t[i]
+    // ---- right-half levels: R_b[j][i] += sum_t WL_b[t] a_t[j] c_t[i].  Wave w
+    // updates level w (when its bit of n is set) over every column tile, so
+    // the weighted A operand of a level is formed once.
     {
-      float av[2][8];  // a_t[j = li], t = 32ks + 8g4 + e
+      const int b = w;
+      if (b < nslot && ((n >> b) & 1)) {
+        const int base = (n >> (b + 1)) << (b + 1);
+        const bool first = n == min(N, base + (1 << (b + 1))) - 1;
+        bf16x8 ah[2], al[2];  // A[j = li][t = 32ks + 8g4 + e] = WL_b[t] a_t[j]
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4 + 4);
+        for (int ks = 0; ks < 2; ++ks) {
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4 + 4);
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4 + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          av[ks][e] = x0[e];
-          av[ks][4 + e] = x1[e];
+          for (int e = 0; e < 8; ++e) {
+            bf16 x1_, x2_;
+            split_bf16(e < 4 ? x0[e] * w0[e] : x1[e - 4] * w1[e - 4], x1_, x2_);
+            ah[ks][e] = x1_;
+            al[ks][e] = x2_;
+          }
         }
-      }
-#pragma unroll
-      for (int b = 0; b < NSMAX; ++b) {
-        if (b < nslot && ((n >> b) & 1)) {
-          const int base = (n >> (b + 1)) << (b + 1);
-          const bool first = n == min(N, base + (1 << (b + 1))) - 1;
-          bf16x8 ah[2], al[2];
+        float* Rf = reinterpret_cast<float*>(Rbase + b * R_BYTES);
+        for (int it = 0; it < dc / 16; ++it) {
+          const int i0 = 16 * it;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const f32x4 w0 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4);
-            const f32x4 w1 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4 + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              bf16 x1, x2;
-              split_bf16(av[ks][e] * (e < 4 ? w0[e] : w1[e - 4]), x1, x2);
-              ah[ks][e] = x1;
-              al[ks][e] = x2;
-            }
+            const int off = (32 * ks + 8 * g4 + (li >> 2)) * LDC + i0 + 4 * (li & 3);
+            const bf16x8 cb = cat(tr_read(Ch + off), tr_read(Ch + off + 4 * LDC));
+            acc = mma(ah[ks], cb, acc);
+            acc = mma(al[ks], cb, acc);
+            if (MODE == 1) acc = mma(ah[ks], cat(tr_read(Cl + off), tr_read(Cl + off + 4 * LDC)), acc);
           }
-          float* Rf = reinterpret_cast<float*>(Rbase + b * R_BYTES);
-          for (int it = w; it < dc / 16; it += NW) {
-            const int i0 = 16 * it;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          // acc[r] = sum_t WL_b[t] a_t[j] c_t[i], j = 4g4 + r, i = i0 + li
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              const int off = (32 * ks + 8 * g4 + (li >> 2)) * LDC + i0 + 4 * (li & 3);
-              const bf16x8 cb = cat(tr_read(Ch + off), tr_read(Ch + off + 4 * LDC));
-              acc = mma(ah[ks], cb, acc);
-              acc = mma(al[ks], cb, acc);
-              if (MODE == 1) acc = mma(ah[ks], cat(tr_read(Cl + off), tr_read(Cl + off + 4 * LDC)), acc);
-            }
-            // acc[r] = sum_t WL_b[t] a_t[j] c_t[i], j = 4g4 + r, i = i0 + li
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float* p = Rf + (4 * g4 + r) * LDR + i0 + li;
-              *p = (first ? 0.f : *p) + acc[r];
-            }
+          for (int r = 0; r < 4; ++r) {
+            float* p = Rf + (4 * g4 + r) * LDR + i0 + li;
+            *p = (first ? 0.f : *p) + acc[r];
           }
         }
       }
@@ -573,7 +573,7 @@ __global__ void __launch_bounds__(b16::NT) bwd_dq16_kernel(BwdArgs a) {
   for (int n = 0; n < N; ++n) {
     const int tok0 = n * C;
     double Atd;
-    const double cl = prefix64(pla, lane, &Atd);
+    const double cl = prefix_dpp(pla, lane, &Atd);
 #pragma unroll
     for (int b = 0; b < NSMAX; ++b)
       if (b < nslot && ((n >> b) & 1)) {
