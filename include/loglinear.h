@@ -183,7 +183,10 @@ int loglinear_prefill_f32(const float* q, const float* k, const float* v, const 
  * Scratch (per-slice partial sums of grad_lambda, (dk/16) * B * H * T *
  * bit_length(N-1) floats, and B * H * T doubles) is allocated stream-ordered
  * on `stream`.
- * Arithmetic: fp32 matrix-core instructions throughout; no atomics, so the
+ * Arithmetic: with bf16 inputs and C = 64 (dk, dv multiples of 32 up to 128,
+ * at most 256 chunks) bf16 matrix cores with the fp32 operands (dO, masked
+ * scores, level states) split into bf16 hi + lo, ~1e-3 of each gradient's RMS
+ * at worst; otherwise fp32 matrix-core instructions.  No atomics, so the
  * results are deterministic.
  */
 int loglinear_bwd(const void* q, const void* k, const void* v, const float* log_a,
