@@ -35,6 +35,7 @@ CASES = [
     (1, 2, 1024, 64, 128, 32, "bf16", "weak"),   # T a power of two
     (1, 2, 700, 128, 128, 64, "bf16", "strong"), # strong decay: heavy-tailed gradients
     (1, 1, 3000, 128, 64, 64, "bf16", "weak"),   # 47 chunks, six chunk-level bits, ragged
+    (1, 2, 500, 32, 96, 64, "bf16", "strong"),   # contraction widths 32 and 96 on the bf16 kernels
 ]
 
 
