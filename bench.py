@@ -4,7 +4,8 @@
 
 A step is one loglinear_fwd call (segment-state, node and sweep kernels) over
 one batch of synthetic inputs already resident in HBM.  Prints ONE JSON line;
-at the default workload it also carries a "decode" object (one decode step of
+at the default workload it also carries a "prefill" object (the same forward
+plus the decode states at T-1), a "decode" object (one decode step of
 64 sequences x 16 heads, L = 17) and a "lambda_proj" object (the level-weight
 projection at the same B, T, H, L with hidden width 2048), timed the same way.
 --pass bwd / decode / lambda time only the backward, the decode step or the
@@ -152,6 +153,29 @@ def bench_lambda(dev, steps: int, warmup: int):
         "roofline": {"kernel": "lambda_proj_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
     }
+
+
+def bench_prefill(sets, w, steps: int, warmup: int):
+    """Forward plus the decode states at T-1 (loglinear_prefill) on the same
+    inputs: the extra cost over the forward is the state emit of the last
+    segment and the in-chunk handoff kernel."""
+    import torch
+    import log_linear_attention_attn_amd as ll
+    dev = sets[0][0].device
+    states = torch.empty(w.B, w.H, w.L, w.dk, w.dv, dtype=torch.float32, device=dev)
+    out = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.float32, device=dev)
+    for i in range(warmup):
+        ll.prefill(*sets[i % len(sets)], C=w.C, out=out, states=states)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        ll.prefill(*sets[i % len(sets)], C=w.C, out=out, states=states)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    return {"ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+            "states_bytes": states.numel() * 4, "L": w.L}
 
 
 def source_hash() -> str:
@@ -378,6 +402,7 @@ def main():
         "source_hash": source_hash(),
     }
     if args.workload == W.LM_T16K.name:
+        rec["prefill"] = bench_prefill(sets, w, K, Wm)
         rec["decode"] = bench_decode(dev, K, Wm)
         rec["lambda_proj"] = bench_lambda(dev, K, Wm)
     if not args.no_cpu_baseline:

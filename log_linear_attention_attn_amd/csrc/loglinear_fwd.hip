@@ -38,6 +38,7 @@
 // decay is weak enough for distant chunks to matter).  fp32 path: fp32 MFMA.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ll_device.h"
@@ -626,48 +627,50 @@ __global__ void __launch_bounds__(256) seg_node_kernel(NodeArgs a) {
 // position t = T-1 (prefill -> decode).  Their buckets lie inside the last
 // chunk: level 0 is {t}, level l >= 1 (when bit l-1 of t is set) the 2^(l-1)
 // tokens below t's bit l-1 (page above, section 前缀的层次化分解).  Each is
-// sum_s exp(cum[t] - cum[s]) k_s v_s^T, in plain fp32 FMAs: at most C tokens
-// per (b,h) in total.  One workgroup per (b,h, 64 dv columns).
+// sum_s exp(cum[t] - cum[s]) k_s v_s^T in fp32.  One workgroup per (b,h, 64
+// dv columns, level): the bucket's k and decayed v rows (at most C/2 tokens)
+// are staged in LDS, then each thread sums its (dk, dv) elements.
 template <typename IT>
 __global__ void __launch_bounds__(256) handoff_intra_kernel(HandoffArgs a) {
-  __shared__ float wdec[64];  // exp(cum[t] - cum[s]) for s = tok0 + i
-  const int bh = blockIdx.x, dv0 = blockIdx.y * 64;
+  __shared__ float ks[32][128];   // k rows of the bucket
+  __shared__ float vw[32][64];    // exp(cum[t] - cum[s]) v_s, this workgroup's columns
+  const int bh = blockIdx.x, dv0 = blockIdx.y * 64, lev = blockIdx.z;
   const int tid = threadIdx.x;
-  const int T = a.T, dk = a.dk, dv = a.dv, C = a.C;
-  const int t = T - 1, tok0 = (t / C) * C;
+  const int T = a.T, dk = a.dk, dv = a.dv;
+  const int t = T - 1;
   const size_t bhT = (size_t)bh * T;
-  if (tid < 64) {
-    float d = 0.f;  // sum of log_a over (s, t], summed directly
-    const int s = tok0 + tid;
-    if (s <= t)
-      for (int r = s + 1; r <= t; ++r) d += a.log_a[bhT + r];
-    wdec[tid] = s <= t ? __expf(d) : 0.f;
+  int lo = t, hi = t + 1;  // level 0: {t}
+  if (lev > 0) {
+    if ((t >> (lev - 1)) & 1) {
+      lo = (t >> lev) << lev;
+      hi = lo + (1 << (lev - 1));
+    } else {
+      lo = hi = 0;  // no bucket at this level
+    }
   }
-  __syncthreads();
+  const int nb = hi - lo;  // <= C / 2 <= 32
+  const int ncol = min(64, dv - dv0);
   const IT* __restrict__ kg = static_cast<const IT*>(a.k) + (size_t)(bh / a.G) * T * dk;
   const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
-  float* __restrict__ so = a.st_out + (size_t)bh * a.st_L * dk * dv;
-  int logc = 0;
-  while ((1 << logc) < C) ++logc;
-  const int nlev = min(logc + 1, a.st_L);
-  const int ncol = min(64, dv - dv0);
-  for (int lev = 0; lev < nlev; ++lev) {
-    int lo = t, hi = t + 1;  // level 0: {t}
-    if (lev > 0) {
-      if ((t >> (lev - 1)) & 1) {
-        lo = (t >> lev) << lev;
-        hi = lo + (1 << (lev - 1));
-      } else {
-        lo = hi = 0;  // no bucket at this level
-      }
+  float* __restrict__ so = a.st_out + ((size_t)bh * a.st_L + lev) * dk * dv;
+  if (nb > 0) {
+    for (int i = tid; i < nb * dk; i += 256) {
+      const int s = i / dk, d = i - s * dk;
+      ks[s][d] = to_float(kg[(size_t)(lo + s) * dk + d]);
     }
-    for (int i = tid; i < dk * ncol; i += 256) {
-      const int d = i / ncol, j = dv0 + (i - d * ncol);
-      float x = 0.f;
-      for (int s = lo; s < hi; ++s)
-        x += wdec[s - tok0] * to_float(kg[(size_t)s * dk + d]) * to_float(vg[(size_t)s * dv + j]);
-      so[((size_t)lev * dk + d) * dv + j] = x;
+    for (int i = tid; i < nb * 64; i += 256) {
+      const int s = i >> 6, j = i & 63;
+      float dec = 0.f;  // sum of log_a over (lo + s, t], summed directly
+      for (int r = lo + s + 1; r <= t; ++r) dec += a.log_a[bhT + r];
+      vw[s][j] = j < ncol ? __expf(dec) * to_float(vg[(size_t)(lo + s) * dv + dv0 + j]) : 0.f;
     }
+  }
+  __syncthreads();
+  for (int i = tid; i < dk * ncol; i += 256) {
+    const int d = i / ncol, j = i - d * ncol;
+    float x = 0.f;
+    for (int s = 0; s < nb; ++s) x += ks[s][d] * vw[s][j];
+    so[(size_t)d * dv + dv0 + j] = x;
   }
 }
 
@@ -736,7 +739,11 @@ int launch_sweep(int dtype, int C, int DKP, const FwdArgs& a, int nblocks, hipSt
 
 int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s) {
   if (a.BH <= 0) return LL_OK;
-  const dim3 grid(static_cast<unsigned>(a.BH), static_cast<unsigned>((a.dv + 63) / 64));
+  if (a.C > 64 || a.dk > 128) return LL_ERR_UNSUPPORTED;  // buckets of <= 32 tokens, staged k rows
+  int logc = 0;
+  while ((1 << logc) < a.C) ++logc;
+  const int nlev = std::min(logc + 1, a.st_L);
+  const dim3 grid(static_cast<unsigned>(a.BH), static_cast<unsigned>((a.dv + 63) / 64), static_cast<unsigned>(nlev));
   if (dtype == LL_BF16)
     hipLaunchKernelGGL(handoff_intra_kernel<bf16>, grid, dim3(256), 0, s, a);
   else
