@@ -313,9 +313,6 @@ fwd_rs_kernel(FwdArgs a) {
     bf16* Vs = reinterpret_cast<bf16*>(smem + VS_OFF) + par * (C * LDV);
     float* cl_s = reinterpret_cast<float*>(smem + CL_OFF) + par * (2 * C);
     float* esf_s = cl_s + C;
-    const bf16* Kp = reinterpret_cast<const bf16*>(smem + KS_OFF) + (par ^ 1) * (C * LDQ);
-    const bf16* Vp = reinterpret_cast<const bf16*>(smem + VS_OFF) + (par ^ 1) * (C * LDV);
-    const float* esfp = reinterpret_cast<const float*>(smem + CL_OFF) + (par ^ 1) * (2 * C) + C;
     // ---------------- stage: registers -> LDS ------------------------------
     u16x2 qm = {0, 0};  // max |q| of this thread's values, as bf16 magnitude bits
 #pragma unroll
@@ -458,16 +455,83 @@ fwd_rs_kernel(FwdArgs a) {
         *reinterpret_cast<bf16x4*>(dst + 64 * 8) = bf16x4{};
       }
     }
-    // ---------------- previous chunk's state + lssb merge (registers) ------
-    // Chunk n-1 -> n: its state joins the buckets before this chunk's Q.G
-    // products.  Done here, next to the score tiles of chunk n, so the two
-    // independent instruction streams overlap.
-    if (n > n0) {
-      const int m = __builtin_ctz(static_cast<unsigned>(n));
-      const bf16* Ks = Kp;
-      const bf16* Vs = Vp;
-      const float* esf_s = esfp;
-      const float Atot = Aprev;
+    // Row weights of this wave's Q.G products for each live inter-chunk
+    // level b (lane = row): lambda[row, log2C+1+b] * exp(cl_row + dec_b) (decay
+    // from the bucket's end to the row) * 2^eq (fp16 Q scale) * 2^eg[b] (this
+    // wave's state scale).  Written and read by this wave only.
+    {
+      const float ecl = __expf(cl) * exp2_int(eq);
+      float lv[NSLOT];
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b) lv[b] = lam_s[lane * L + LOGC + 1 + b];
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b)
+        if ((n >> b) & 1) lw[b * C + lane] = lv[b] * ecl * (__expf(dec[b]) * exp2_int(eg[b]));
+    }
+    __syncthreads();
+
+    // ---------------- phase 2 ----------------------------------------------
+    // Q.G over this wave's dk half for all four row tiles (fp16 MFMAs).
+    f32x4 Op[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) Op[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      f16x8 qa[4][2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 * ks + 8 * g4);
+#pragma unroll
+      for (int b = 0; b < NSLOT; ++b) {
+        if ((n >> b) & 1) {
+          f32x4 acc[4];
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) {
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(lw + b * C + 16 * mi + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Op[mi][r] += wv[r] * acc[mi][r];
+          }
+        }
+      }
+    }
+    // hand the partial sums of the partner's row tiles over (read after the
+    // next barrier)
+    Xc[(w * 2 + 0) * 64 + lane] = Op[oth0];
+    Xc[(w * 2 + 1) * 64 + lane] = Op[oth1];
+    // P V for this wave's two row tiles; keys in the score tile order
+    // (32ks + 4g4 + e, then +16), V operand by transposed reads.
+    O0 = Op[own0];
+    O1 = Op[own1];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
+      const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
+      if (2 * ks <= own0) {
+        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 0) * 64 + lane], vb, O0);
+        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 1) * 64 + lane], vb, O0);
+      }
+      if (2 * ks <= own1) {
+        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 0) * 64 + lane], vb, O1);
+        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 1) * 64 + lane], vb, O1);
+      }
+    }
+
+    // ---------------- this chunk's state + lssb merge (registers) ----------
+    // Chunk n -> n+1: its state joins the buckets the next chunk reads.  The
+    // merge writes level m = lssb(n+1), which chunk n does not read (bit m of
+    // n is clear), and only reads the levels below m, so it can follow this
+    // chunk's Q.G products and overlap the P V products.  K and V of chunk n
+    // stay in their parity buffer until the staging of chunk n+2, which comes
+    // after the next chunk's second barrier.
+    if (n + 1 < n1) {
+      const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
       // decayed V of this wave's columns, tokens 32ks + 8g4 + e, split hi/lo
       bf16x8 vh[2], vl[2];
 #pragma unroll
@@ -549,74 +613,6 @@ fwd_rs_kernel(FwdArgs a) {
         }
       }
     }
-    // Row weights of this wave's Q.G products for each live inter-chunk
-    // level b (lane = row): lambda[row, log2C+1+b] * exp(cl_row + dec_b) (decay
-    // from the bucket's end to the row) * 2^eq (fp16 Q scale) * 2^eg[b] (this
-    // wave's state scale).  Written and read by this wave only.
-    {
-      const float ecl = __expf(cl) * exp2_int(eq);
-      float lv[NSLOT];
-#pragma unroll
-      for (int b = 0; b < NSLOT; ++b) lv[b] = lam_s[lane * L + LOGC + 1 + b];
-#pragma unroll
-      for (int b = 0; b < NSLOT; ++b)
-        if ((n >> b) & 1) lw[b * C + lane] = lv[b] * ecl * (__expf(dec[b]) * exp2_int(eg[b]));
-    }
-    __syncthreads();
-
-    // ---------------- phase 2 ----------------------------------------------
-    // Q.G over this wave's dk half for all four row tiles (fp16 MFMAs).
-    f32x4 Op[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) Op[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      f16x8 qa[4][2];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 * ks + 8 * g4);
-#pragma unroll
-      for (int b = 0; b < NSLOT; ++b) {
-        if ((n >> b) & 1) {
-          f32x4 acc[4];
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            const f32x4 wv = *reinterpret_cast<const f32x4*>(lw + b * C + 16 * mi + 4 * g4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Op[mi][r] += wv[r] * acc[mi][r];
-          }
-        }
-      }
-    }
-    // hand the partial sums of the partner's row tiles over (read after the
-    // next barrier)
-    Xc[(w * 2 + 0) * 64 + lane] = Op[oth0];
-    Xc[(w * 2 + 1) * 64 + lane] = Op[oth1];
-    // P V for this wave's two row tiles; keys in the score tile order
-    // (32ks + 4g4 + e, then +16), V operand by transposed reads.
-    O0 = Op[own0];
-    O1 = Op[own1];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
-      const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
-      if (2 * ks <= own0) {
-        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 0) * 64 + lane], vb, O0);
-        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 1) * 64 + lane], vb, O0);
-      }
-      if (2 * ks <= own1) {
-        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 0) * 64 + lane], vb, O1);
-        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 1) * 64 + lane], vb, O1);
-      }
-    }
-
     Aprev = Atot;
   }
 
