@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd tokens/sec + TFLOP/s vs bf16 MFMA peak, log-linear Mamba-2 at T=16K"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 matrix
 
 
 def algorithmic_flops(B, H, T, dk, dv, C):
@@ -146,12 +147,32 @@ def bench_lambda(dev, steps: int, warmup: int):
     nbytes = w.B * w.T * w.D * ib + w.H * w.L * (w.D * ib + 4) + w.B * w.H * w.T * w.L * 4
     flops = 2 * w.B * w.T * w.D * w.H * w.L
     gbs = nbytes / (ms * 1e-3) / 1e9
+    # gradient (loglinear_lambda_proj_bwd) from the last lambda and a fixed
+    # dlambda: dx = dz W and dW = dz^T x (+ dbias), fp32 matrix cores
+    dlam = torch.randn(w.B, w.H, w.T, w.L, generator=torch.Generator().manual_seed(0)).to(dev)
+    bsteps, bwarm = max(3, steps // 2), 3
+    for i in range(bwarm):
+        ll.lambda_proj_bwd(xs[i % 3], Wt, out, dlam)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(bsteps):
+        ll.lambda_proj_bwd(xs[i % 3], Wt, out, dlam)
+    stop.record()
+    torch.cuda.synchronize()
+    bms = start.elapsed_time(stop) / bsteps
+    bflops = 2 * flops + w.B * w.T * w.H * w.L * 2
+    bbytes = (w.B * w.T * w.D * (ib + 4) + w.H * w.L * (w.D * (ib + 4) + 4)
+              + 2 * w.B * w.H * w.T * w.L * 4)
+    btf = bflops / (bms * 1e-3) / 1e12
     return {
         "workload": w.name, "B": w.B, "T": w.T, "D": w.D, "H": w.H, "L": w.L, "dtype": w.dtype,
         "steps": steps, "ms_per_step": ms, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
         "tflops": flops / (ms * 1e-3) / 1e12,
         "roofline": {"kernel": "lambda_proj_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
+        "bwd": {"steps": bsteps, "ms_per_step": bms, "algorithmic_flops": bflops, "algorithmic_bytes": bbytes,
+                "roofline": {"kernel": "lam_gemm_kernel", "bound": "mfma", "achieved": btf,
+                             "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": btf / PEAK_FP32_TFLOPS}},
     }
 
 
@@ -297,7 +318,7 @@ def main():
             "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": rec["dtype"], "data": "synthetic",
             "config": {k: rec[k] for k in ("workload", "B", "T", "D", "H", "L")},
-            "roofline": rec["roofline"], "tflops": rec["tflops"]}))
+            "roofline": rec["roofline"], "tflops": rec["tflops"], "bwd": rec["bwd"]}))
         return
     if args.which == "decode":
         rec = bench_decode(dev, args.steps, args.warmup)
@@ -410,8 +431,6 @@ def main():
     print(json.dumps(rec))
 
 
-PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix
-
 
 def bench_bwd(args, w, dev):
     """Backward (loglinear_bwd) of the same workload: gradients of sum(out * dout)
@@ -438,7 +457,7 @@ def bench_bwd(args, w, dev):
     abytes = algorithmic_bytes_bwd(w.B, w.H, w.T, w.dk, w.dv, w.L, 2 if w.dtype == "bf16" else 4)
     tflops = flops / (ms * 1e-3) / 1e12
     bf16 = w.dtype == "bf16" and w.C == 64
-    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_MFMA_TFLOPS
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     rec = {
         "metric": "bwd tokens/sec (gradients of q, k, v, log_a, lambda), log-linear Mamba-2",
         "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,

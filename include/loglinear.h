@@ -233,6 +233,31 @@ int loglinear_bwd_ex(const void* q, const void* k, const void* v, const float* l
 int loglinear_lambda_proj(const void* x, const void* W, const float* bias, float* lambda, int B,
                           int T, int D, int H, int L, int dtype, void* stream);
 
+/*
+ * Gradient of loglinear_lambda_proj (same page and section) for a training
+ * step: with z = x W^T + bias, m = b*T + t and n = h*L + l,
+ *   dz[m, n]     = grad_lambda[b, h, t, l] * sigmoid(z[m, n])
+ *   grad_x       = dz W            [B, T, D]  fp32
+ *   grad_W       = dz^T x          [H*L, D]   fp32
+ *   grad_bias[n] = sum_m dz[m, n]  [H*L]      fp32 (NULL: not computed)
+ * sigmoid(z) is recovered from the forward's output as 1 - exp(-lambda), so
+ * the bias is not needed.
+ *   x, W        : as for loglinear_lambda_proj (dtype LL_BF16 or LL_F32)
+ *   lambda      : [B, H, T, L] fp32, the forward's output
+ *   grad_lambda : [B, H, T, L] fp32
+ * All DEVICE pointers; outputs are overwritten.  Products on fp32 matrix cores
+ * (bf16 inputs widened exactly), fp32 accumulation, no atomics (bitwise
+ * repeatable).  Stream-ordered scratch of B*T*H*L floats for dz plus the dW
+ * split partials (allocated and released on `stream`).  B*T = 0 writes zeros
+ * to grad_W and grad_bias.  Errors: bad dtype or sizes (L outside 1..31)
+ * LL_ERR_SHAPE; D > 2^20, H*L > 2^16 or B*T >= 2^31 LL_ERR_UNSUPPORTED; a NULL
+ * required pointer LL_ERR_NULL.
+ */
+int loglinear_lambda_proj_bwd(const void* x, const void* W, const float* lambda,
+                              const float* grad_lambda, float* grad_x, float* grad_W,
+                              float* grad_bias, int B, int T, int D, int H, int L, int dtype,
+                              void* stream);
+
 /* Workspace bytes loglinear_fwd_ex needs for these sizes (0 if none); seg_log2
  * as in loglinear_fwd_opts.  Returns (size_t)-1 for invalid sizes. */
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2);

@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "loglinear_prefill", "loglinear_prefill_f32", "loglinear_bwd", "loglinear_bwd_f32",
     "loglinear_bwd_ex", "loglinear_fwd_workspace_size",
     "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_decode_step_ex",
-    "loglinear_level_table", "loglinear_lambda_proj",
+    "loglinear_level_table", "loglinear_lambda_proj", "loglinear_lambda_proj_bwd",
     "loglinear_strerror",
 )
 
@@ -107,6 +107,8 @@ def lib():
     L.loglinear_decode_step_ex.restype = i
     L.loglinear_lambda_proj.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
     L.loglinear_lambda_proj.restype = i
+    L.loglinear_lambda_proj_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    L.loglinear_lambda_proj_bwd.restype = i
     L.loglinear_level_table.argtypes = [vp, i, vp]
     L.loglinear_level_table.restype = i
     L.loglinear_strerror.argtypes = [i]
@@ -400,6 +402,34 @@ def lambda_proj(x, W, bias, H: int, L: int, out=None):
                                      LL_BF16 if x.dtype == torch.bfloat16 else LL_F32, _stream(dev))
     _raise(st, "loglinear_lambda_proj")
     return out
+
+
+def lambda_proj_bwd(x, W, lam, dlam, want_bias: bool = True):
+    """Gradient of lambda_proj (loglinear_lambda_proj_bwd): from the forward's
+    lambda [B, H, T, L] and the incoming dlambda (both fp32), returns
+    (dx [B, T, D], dW [H*L, D], dbias [H*L] or None), all fp32.
+    x: [B, T, D] and W: [H*L, D] as for lambda_proj."""
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x, W must be bfloat16 or float32")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, T, D = x.shape
+    if lam.dim() != 4:
+        raise ValueError("lambda must be [B, H, T, L]")
+    H, L = int(lam.shape[1]), int(lam.shape[3])
+    _check_dev("x", x, x.dtype, (B, T, D), dev)
+    _check_dev("W", W, x.dtype, (H * L, D), dev)
+    _check_dev("lambda", lam, torch.float32, (B, H, T, L), dev)
+    _check_dev("dlambda", dlam, torch.float32, (B, H, T, L), dev)
+    dx = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    dW = torch.empty((H * L, D), dtype=torch.float32, device=dev)
+    db = torch.empty((H * L,), dtype=torch.float32, device=dev) if want_bias else None
+    st = lib().loglinear_lambda_proj_bwd(_ptr(x), _ptr(W), _ptr(lam), _ptr(dlam), _ptr(dx), _ptr(dW), _ptr(db),
+                                         B, T, D, H, L, LL_BF16 if x.dtype == torch.bfloat16 else LL_F32,
+                                         _stream(dev))
+    _raise(st, "loglinear_lambda_proj_bwd")
+    return dx, dW, db
 
 
 def level_table(T: int, device=None):

@@ -105,6 +105,31 @@ struct LamProjArgs {
   int ncb;  // column blocks of 256 output columns
 };
 
+// Gradient of the level-weight projection.
+struct LamBwdArgs {
+  const void* x;      // [B][T][D]
+  const void* W;      // [H*L][D]
+  const float* lam;   // [B][H][T][L], the forward's output
+  const float* dlam;  // [B][H][T][L]
+  float* dz;          // scratch [B*T][H*L]
+  float* dx;          // [B][T][D]
+  float* dW;          // [H*L][D]
+  float* dbias;       // [H*L] or null
+  int B, T, D, H, L;
+};
+
+// C(m, n) = sum_{k in split} A(m, k) B(k, n) for the split given by the
+// workgroup, written at C + split * split_stride + m * ldc + n; A(m, k) =
+// A[m * sam + k * sak], B(k, n) = B[k * sbk + n * sbn] for n < nb_real, and
+// for n >= nb_real 1 (n == nb_real with ones set) or 0.
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  float* C;
+  long long sam, sak, sbk, sbn, ldc, split_stride;
+  int M, N, K, kper, nb_real, ones;
+};
+
 int sweep_lds_bytes(int dtype, int C, int DKP, int L, int nslot);
 int launch_sweep(int dtype, int C, int DKP, const FwdArgs& a, int nblocks, hipStream_t s);
 int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStream_t s);
@@ -127,9 +152,14 @@ int launch_bwd_dq16(const BwdArgs& a, hipStream_t s);
 // in-chunk dlambda on bf16 matrix cores (bf16 inputs, C = 64)
 bool bwd_dlam_intra16_ok(const BwdArgs& a);
 int launch_bwd_dlam_intra16(const BwdArgs& a, hipStream_t s);
-// out[i][e] = sum_{g < G} in[i * G + g][e] for i < rows, e < elems (elems % 4 == 0)
 int lambda_proj_lds_bytes(int dtype);
 int launch_lambda_proj(int dtype, const LamProjArgs& a, hipStream_t s);
+// split count and rows per split of the dW product, and the launch
+// (part: nsplit * H*L * (D + 1) floats of scratch)
+int lambda_bwd_nsplit(long long rows, int HL, int D);
+long long lambda_bwd_kper(long long rows, int nsplit);
+int launch_lambda_bwd(int dtype, const LamBwdArgs& a, float* part, int nsplit, hipStream_t s);
+// out[i][e] = sum_{g < G} in[i * G + g][e] for i < rows, e < elems (elems % 4 == 0)
 int launch_group_sum(const float* in, float* out, long long rows, int G, long long elems, hipStream_t s);
 
 }  // namespace ll

@@ -237,6 +237,32 @@ int run_lambda_proj(int dtype, const void* x, const void* W, const float* bias, 
   return ll::launch_lambda_proj(dtype, a, stream);
 }
 
+int run_lambda_proj_bwd(int dtype, const void* x, const void* W, const float* lam, const float* dlam,
+                        float* dx, float* dW, float* dbias, int B, int T, int D, int H, int L,
+                        hipStream_t stream) {
+  if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
+  if (B < 0 || T < 0 || D < 1 || H < 1 || L < 1 || L > 31) return LL_ERR_SHAPE;
+  if (D > (1 << 20) || (long long)H * L > (1 << 16)) return LL_ERR_UNSUPPORTED;
+  const long long M = (long long)B * T;
+  if (M > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
+  if (!W || !dW) return LL_ERR_NULL;
+  if (M > 0 && (!x || !lam || !dlam || !dx)) return LL_ERR_NULL;
+  const int HL = H * L;
+  const int nsplit = M > 0 ? ll::lambda_bwd_nsplit(M, HL, D) : 0;
+  const size_t dz_bytes = align256((size_t)M * HL * sizeof(float));
+  const size_t part_bytes = align256((size_t)nsplit * HL * (D + 1) * sizeof(float));
+  void* ws = nullptr;
+  if (dz_bytes + part_bytes > 0 && hipMallocAsync(&ws, dz_bytes + part_bytes, stream) != hipSuccess)
+    return LL_ERR_HIP;
+  char* wsb = static_cast<char*>(ws);
+  float* dz = reinterpret_cast<float*>(wsb);
+  float* part = reinterpret_cast<float*>(wsb + dz_bytes);
+  ll::LamBwdArgs a{x, W, lam, dlam, dz, dx, dW, dbias, B, T, D, H, L};
+  int st = ll::launch_lambda_bwd(dtype, a, part, nsplit, stream);
+  if (ws && hipFreeAsync(ws, stream) != hipSuccess && st == LL_OK) st = LL_ERR_HIP;
+  return st;
+}
+
 int run_bwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
             const float* lambda, const float* out, const float* dout, float* dq, float* dk_out,
             float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T, int dk, int dv, int C,
@@ -348,6 +374,14 @@ int loglinear_bwd_ex(const void* q, const void* k, const void* v, const float* l
 int loglinear_lambda_proj(const void* x, const void* W, const float* bias, float* lambda, int B, int T,
                           int D, int H, int L, int dtype, void* stream) {
   return run_lambda_proj(dtype, x, W, bias, lambda, B, T, D, H, L, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_lambda_proj_bwd(const void* x, const void* W, const float* lambda,
+                              const float* grad_lambda, float* grad_x, float* grad_W,
+                              float* grad_bias, int B, int T, int D, int H, int L, int dtype,
+                              void* stream) {
+  return run_lambda_proj_bwd(dtype, x, W, lambda, grad_lambda, grad_x, grad_W, grad_bias, B, T, D, H, L,
+                             static_cast<hipStream_t>(stream));
 }
 
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2) {

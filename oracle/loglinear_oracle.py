@@ -385,3 +385,22 @@ def lambda_projection(x, W, bias, H: int, L: int) -> np.ndarray:
         z = z + _f64(bias)[None, :]
     lam = softplus(z).reshape(B, T, H, L)
     return np.ascontiguousarray(lam.transpose(0, 2, 1, 3))
+
+
+def lambda_projection_grad(x, W, bias, dlam, H: int, L: int):
+    """Gradient of lambda_projection by the chain rule, in fp64: with
+    z = x W^T + bias (rows m = (b, t), columns n = h*L + l),
+    dz[m, n] = dlam[b, h, t, l] * sigmoid(z[m, n]) (softplus' = sigmoid),
+    dx = dz W, dW = dz^T x, dbias = column sums of dz.
+    Returns (dx [B, T, D], dW [H*L, D], dbias [H*L])."""
+    x, W, dlam = _f64(x), _f64(W), _f64(dlam)
+    B, T, D = x.shape
+    if W.shape != (H * L, D) or dlam.shape != (B, H, T, L):
+        raise ValueError("shape mismatch")
+    X = x.reshape(B * T, D)
+    z = X @ W.T
+    if bias is not None:
+        z = z + _f64(bias)[None, :]
+    sig = 0.5 * (1.0 + np.tanh(0.5 * z))  # logistic function, no overflow
+    dz = dlam.transpose(0, 2, 1, 3).reshape(B * T, H * L) * sig
+    return (dz @ W).reshape(B, T, D), dz.T @ X, dz.sum(axis=0)

@@ -211,3 +211,18 @@ def test_lambda_proj_argument_errors():
     assert L.loglinear_lambda_proj(None, p, None, p, 1, 4, 16, 2, 3, 0, None) == LL_ERR_NULL
     q = ctypes.c_void_p(18)  # not 16-byte aligned
     assert L.loglinear_lambda_proj(q, p, None, p, 1, 4, 16, 2, 3, 0, None) == LL_ERR_SHAPE
+
+
+def test_lambda_proj_bwd_argument_errors():
+    L = ll.lib()
+    p = ctypes.c_void_p(16)
+    args = [p] * 7
+    assert L.loglinear_lambda_proj_bwd(*args, 1, 4, 16, 2, 3, 2, None) == LL_ERR_SHAPE       # dtype
+    assert L.loglinear_lambda_proj_bwd(*args, 1, 4, 16, 2, 0, 0, None) == LL_ERR_SHAPE       # L
+    assert L.loglinear_lambda_proj_bwd(*args, 1, 4, 16, 2, 32, 0, None) == LL_ERR_SHAPE      # L > 31
+    assert L.loglinear_lambda_proj_bwd(*args, 1, 4, 0, 2, 3, 0, None) == LL_ERR_SHAPE        # D
+    assert L.loglinear_lambda_proj_bwd(*args, 1, 4, 16, 4096, 31, 0, None) == LL_ERR_UNSUPPORTED  # H*L
+    assert L.loglinear_lambda_proj_bwd(*args, 1 << 16, 1 << 16, 16, 2, 3, 0, None) == LL_ERR_UNSUPPORTED
+    assert L.loglinear_lambda_proj_bwd(p, p, p, p, None, p, p, 1, 4, 16, 2, 3, 0, None) == LL_ERR_NULL
+    assert L.loglinear_lambda_proj_bwd(p, None, p, p, p, p, p, 0, 4, 16, 2, 3, 0, None) == LL_ERR_NULL
+

@@ -1,7 +1,8 @@
-"""GPU parity of the level-weight projection (loglinear_lambda_proj) against
-the oracle's lambda_projection (fp64).  bf16 inputs are exact in fp32 and the
-accumulation is fp32, so the bound is max |gpu - oracle| <= 1e-4 * RMS(oracle)
-for both input types."""
+"""GPU parity of the level-weight projection (loglinear_lambda_proj) and of
+its gradient (loglinear_lambda_proj_bwd) against the oracle's
+lambda_projection / lambda_projection_grad (fp64).  bf16 inputs are exact in
+fp32 and the accumulation is fp32, so the bound is
+max |gpu - oracle| <= 1e-4 * RMS(oracle) for both input types, per output."""
 import numpy as np
 import pytest
 import torch
@@ -57,3 +58,48 @@ def test_lambda_proj_feeds_the_forward():
     lam_ref = oracle.lambda_projection(x, Wt, b, H, L)
     from gpu_util import BF16_TOL
     assert_parity(out.cpu().numpy(), oracle.forward(q, k, v, la, lam_ref), BF16_TOL, "fwd with projected lambda")
+
+
+BWD_CASES = [
+    # (B, T, D, H, L, dtype)
+    (1, 1, 8, 1, 1, "bf16"),          # one row, one output column
+    (2, 300, 256, 4, 9, "bf16"),      # ragged rows (600), 36 columns
+    (1, 1000, 2048, 16, 15, "bf16"),  # the bench shape's width, 240 columns
+    (3, 77, 100, 3, 7, "f32"),        # D not a multiple of the 64-wide tile
+    (1, 130, 64, 20, 15, "f32"),      # 300 columns: five column tiles
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}T{}D{}H{}L{}_{}".format(*c))
+def test_lambda_proj_bwd_matches_oracle(case):
+    """The gradient from the GPU's own lambda (as a training step chains it)
+    against the chain rule in fp64; two calls are bitwise equal."""
+    B, T, D, H, L, dtype = case
+    w = W.LambdaProjWorkload("lpb", B, T, D, H, L, dtype, True, seed=T + 2 * D)
+    x, Wt, b = W.make_lambda_proj_inputs(w)
+    dlam = torch.from_numpy(np.random.default_rng(T + D).standard_normal((B, H, T, L)).astype(np.float32))
+    announce(f"lambda_proj_bwd {case}")
+    dx_, dW_ = to_dev(x, Wt)
+    lam = ll.lambda_proj(dx_, dW_, b.cuda(), H, L)
+    gx, gW, gb = ll.lambda_proj_bwd(dx_, dW_, lam, dlam.cuda())
+    gx2, gW2, gb2 = ll.lambda_proj_bwd(dx_, dW_, lam, dlam.cuda())
+    torch.cuda.synchronize()
+    want = oracle.lambda_projection_grad(x, Wt, b, dlam, H, L)
+    for name, g, ref in zip(("dx", "dW", "dbias"), (gx, gW, gb), want):
+        assert tuple(g.shape) == ref.shape, name
+        assert_parity(g.cpu().numpy(), ref, F32_TOL, f"{name} {case}")
+    assert torch.equal(gx, gx2) and torch.equal(gW, gW2) and torch.equal(gb, gb2)
+
+
+def test_lambda_proj_bwd_empty_batch_gives_zero_weight_gradients():
+    """No rows: the weight and bias gradients are sums over nothing."""
+    D, H, L = 16, 2, 3
+    x = torch.empty((0, 5, D), dtype=torch.bfloat16, device="cuda")
+    Wt = torch.ones((H * L, D), dtype=torch.bfloat16, device="cuda")
+    lam = torch.empty((0, H, 5, L), device="cuda")
+    announce("lambda_proj_bwd empty")
+    gx, gW, gb = ll.lambda_proj_bwd(x, Wt, lam, lam.clone())
+    torch.cuda.synchronize()
+    assert gx.shape == (0, 5, D)
+    assert torch.equal(gW.cpu(), torch.zeros(H * L, D)) and torch.equal(gb.cpu(), torch.zeros(H * L))
+

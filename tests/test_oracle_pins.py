@@ -540,3 +540,42 @@ def test_lambda_projection_one_hot_rows_land_in_place():
     want = np.full((B, H, T, L), math.log(2.0))
     want[0, 1, :, 2] = np.log1p(np.exp(x[0, :, 3]))
     np.testing.assert_allclose(got, want, rtol=1e-14, atol=0)
+
+
+def test_lambda_projection_grad_matches_central_differences():
+    """The gradient of F = sum(dlam * lambda_projection(x, W, bias)) with
+    respect to every entry of x, W and bias, against central differences of
+    lambda_projection itself (pins the chain rule, the sigmoid factor and the
+    [B, H, T, L] <-> (row, column) layout)."""
+    rng = np.random.default_rng(52)
+    B, T, D, H, L = 2, 3, 4, 2, 3
+    x = rng.standard_normal((B, T, D))
+    W = rng.standard_normal((H * L, D))
+    bias = rng.standard_normal(H * L)
+    dlam = rng.standard_normal((B, H, T, L))
+    dx, dW, db = oracle.lambda_projection_grad(x, W, bias, dlam, H, L)
+
+    def F(x_, W_, b_):
+        return float(np.sum(dlam * oracle.lambda_projection(x_, W_, b_, H, L)))
+
+    eps = 1e-6
+    for arr, grad, name in ((x, dx, "dx"), (W, dW, "dW"), (bias, db, "dbias")):
+        assert grad.shape == arr.shape, name
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            fp = F(x, W, bias)
+            arr[idx] = old - eps
+            fm = F(x, W, bias)
+            arr[idx] = old
+            assert grad[idx] == pytest.approx((fp - fm) / (2 * eps), rel=1e-6, abs=1e-8), (name, idx)
+
+
+def test_lambda_projection_grad_sigmoid_limits():
+    """One input column, one output: dz -> dlam for z >> 0 (softplus is the
+    identity there) and dz -> dlam * e^z for z << 0; dbias = dz."""
+    x = np.ones((1, 1, 1))
+    dlam = np.full((1, 1, 1, 1), 2.0)
+    for z, want in ((40.0, 2.0), (-40.0, 2.0 * math.exp(-40.0))):
+        _, _, db = oracle.lambda_projection_grad(x, np.zeros((1, 1)), np.array([z]), dlam, 1, 1)
+        assert db[0] == pytest.approx(want, rel=1e-12)
