@@ -10,11 +10,11 @@
 // sigmoid(z) = 1 - e^-lambda = -expm1(-lambda), which stays accurate where
 // lambda is tiny.
 //
-// Three kernels: dz into a [B*T, H*L] fp32 scratch matrix; a tiled fp32
-// matrix-core product (v_mfma_f32_16x16x4_f32; bf16 operands are widened
-// exactly when staged) used for both products, dW split over row ranges of
-// B*T into partial sums with dbias as one extra column of ones on the x side;
-// and an in-order sum of the partials.  No atomics, so results are
+// Three kernels: dz into a [B*T, H*L] fp32 scratch matrix; a tiled
+// matrix-core product used for both products (fp32 MFMAs for fp32 inputs;
+// for bf16 x and W, bf16 MFMAs on dz split into bf16 hi + lo), dW split over
+// row ranges of B*T into partial sums with dbias as one extra column of ones
+// on the x side; and an in-order sum of the partials.  No atomics, so results are
 // deterministic.
 #include <hip/hip_runtime.h>
 
@@ -53,6 +53,20 @@ constexpr int BM = 64, BN = 64, BK = 32, NT = 256, LD = BK + 4;
 template <typename T>
 __device__ __forceinline__ float widen(const T* p, long long i) { return static_cast<float>(p[i]); }
 
+// Element i (0 <= i < rows * BK / 256) of a thread's share of a (rows x BK)
+// tile sits at row r0 + dr * i, k index k0 + dk * i: with k contiguous in
+// memory the 256 threads walk rows of BK consecutive k, otherwise columns of
+// consecutive rows, so a wave's loads are always one contiguous run.
+template <int ROWS, int BK>
+struct TileMap {
+  int r0, k0, dr, dk;
+  __device__ TileMap(int tid, bool kc) {
+    constexpr int T = 256;
+    if (kc) { r0 = tid / BK; k0 = tid % BK; dr = T / BK; dk = 0; }
+    else { r0 = tid % ROWS; k0 = tid / ROWS; dr = 0; dk = T / ROWS; }
+  }
+};
+
 // C(m, n) = sum_k A(m, k) B(k, n) over this workgroup's K range, fp32 MFMA.
 // One 256-thread workgroup per (64 x 64 tile, K split); the four waves form a
 // 2 x 2 grid of 32 x 32 blocks.  A and B tiles are staged in LDS as [row][k]
@@ -78,23 +92,28 @@ __global__ void __launch_bounds__(lg::NT) lam_gemm_kernel(GemmArgs g) {
   const int wm = w >> 1, wn = w & 1;
   const bool a_kc = g.sak == 1, b_kc = g.sbk == 1;
 
-  float ra[8], rb[8];
+  constexpr int PER = BM * BK / NT;
+  const TileMap<BM, BK> am(tid, a_kc);
+  const TileMap<BN, BK> bm(tid, b_kc);
+  // in-tile element steps: i * step stays below 2^27 (i < 16, a step of at
+  // most 8 rows of at most 2^20 elements, checked by the host)
+  const int astep = static_cast<int>(am.dr * g.sam + am.dk * g.sak);
+  const int bstep = static_cast<int>(bm.dk * g.sbk + bm.dr * g.sbn);
+  float ra[PER], rb[PER];
   auto load = [&](long long k0) {
+    const TA* pa = A + (m0 + am.r0) * g.sam + (k0 + am.k0) * g.sak;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + NT * i;
-      const int r = a_kc ? idx / BK : idx % BM, k = a_kc ? idx % BK : idx / BM;
-      const long long m = m0 + r, kk = k0 + k;
-      ra[i] = (m < g.M && kk < ke) ? widen(A, m * g.sam + kk * g.sak) : 0.f;
+    for (int i = 0; i < PER; ++i) {
+      const bool ok = m0 + am.r0 + am.dr * i < g.M && k0 + am.k0 + am.dk * i < ke;
+      ra[i] = ok ? widen(pa, i * astep) : 0.f;
     }
+    const TB* pb = Bp + (k0 + bm.k0) * g.sbk + (n0 + bm.r0) * g.sbn;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + NT * i;
-      const int c = b_kc ? idx / BK : idx % BN, k = b_kc ? idx % BK : idx / BN;
-      const long long n = n0 + c, kk = k0 + k;
+    for (int i = 0; i < PER; ++i) {
+      const long long n = n0 + bm.r0 + bm.dr * i;
       float v = 0.f;
-      if (kk < ke) {
-        if (n < g.nb_real) v = widen(Bp, kk * g.sbk + n * g.sbn);
+      if (k0 + bm.k0 + bm.dk * i < ke) {
+        if (n < g.nb_real) v = widen(pb, i * bstep);
         else if (g.ones && n == g.nb_real) v = 1.f;
       }
       rb[i] = v;
@@ -102,17 +121,9 @@ __global__ void __launch_bounds__(lg::NT) lam_gemm_kernel(GemmArgs g) {
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + NT * i;
-      const int r = a_kc ? idx / BK : idx % BM, k = a_kc ? idx % BK : idx / BM;
-      As[r][k] = ra[i];
-    }
+    for (int i = 0; i < PER; ++i) As[am.r0 + am.dr * i][am.k0 + am.dk * i] = ra[i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + NT * i;
-      const int c = b_kc ? idx / BK : idx % BN, k = b_kc ? idx % BK : idx / BN;
-      Bs[c][k] = rb[i];
-    }
+    for (int i = 0; i < PER; ++i) Bs[bm.r0 + bm.dr * i][bm.k0 + bm.dk * i] = rb[i];
   };
 
   f32x4 acc[2][2];
@@ -155,6 +166,118 @@ __global__ void __launch_bounds__(lg::NT) lam_gemm_kernel(GemmArgs g) {
     }
 }
 
+// The same product for a bf16 B operand on bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16): the fp32 A operand (dz) is split at staging
+// into bf16 hi + lo with |a - hi - lo| <= 2^-16 |a|, and each product is
+// hi*B + lo*B with fp32 accumulation.  LDS rows of 64 k (+8 pad, 144 bytes).
+namespace lg16 {
+constexpr int BM = 64, BN = 64, BK = 64, NT = 256, LD = BK + 8, PER = BM * BK / NT;
+}
+
+__global__ void __launch_bounds__(lg16::NT) lam_gemm16_kernel(GemmArgs g) {
+  using namespace lg16;
+  __shared__ __align__(16) bf16 Ah[BM][LD];
+  __shared__ __align__(16) bf16 Al[BM][LD];
+  __shared__ __align__(16) bf16 Bs[BN][LD];
+  const int ntn = (g.N + BN - 1) / BN, ntm = (g.M + BM - 1) / BM;
+  const long long id = blockIdx.x;
+  const int tn = static_cast<int>(id % ntn);
+  const long long rest = id / ntn;
+  const int tm = static_cast<int>(rest % ntm);
+  const int split = static_cast<int>(rest / ntm);
+  const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
+  const long long kb = (long long)split * g.kper;
+  const long long ke = min((long long)g.K, kb + g.kper);
+  const float* A = static_cast<const float*>(g.A);
+  const bf16* Bp = static_cast<const bf16*>(g.B);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g4 = lane >> 4;
+  const int wm = w >> 1, wn = w & 1;
+  const bool a_kc = g.sak == 1, b_kc = g.sbk == 1;
+
+  const TileMap<BM, BK> am(tid, a_kc);
+  const TileMap<BN, BK> bm(tid, b_kc);
+  const int astep = static_cast<int>(am.dr * g.sam + am.dk * g.sak);
+  const int bstep = static_cast<int>(bm.dk * g.sbk + bm.dr * g.sbn);
+  float ra[PER];
+  bf16 rb[PER];
+  auto load = [&](long long k0) {
+    const float* pa = A + (m0 + am.r0) * g.sam + (k0 + am.k0) * g.sak;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool ok = m0 + am.r0 + am.dr * i < g.M && k0 + am.k0 + am.dk * i < ke;
+      ra[i] = ok ? pa[i * astep] : 0.f;
+    }
+    const bf16* pb = Bp + (k0 + bm.k0) * g.sbk + (n0 + bm.r0) * g.sbn;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const long long n = n0 + bm.r0 + bm.dr * i;
+      bf16 v = static_cast<bf16>(0.f);
+      if (k0 + bm.k0 + bm.dk * i < ke) {
+        if (n < g.nb_real) v = pb[i * bstep];
+        else if (g.ones && n == g.nb_real) v = static_cast<bf16>(1.f);
+      }
+      rb[i] = v;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      bf16 hi, lo;
+      split_bf16(ra[i], hi, lo);
+      Ah[am.r0 + am.dr * i][am.k0 + am.dk * i] = hi;
+      Al[am.r0 + am.dr * i][am.k0 + am.dk * i] = lo;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) Bs[bm.r0 + bm.dr * i][bm.k0 + bm.dk * i] = rb[i];
+  };
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kb < ke) load(kb);
+  for (long long k0 = kb; k0 < ke; k0 += BK) {
+    __syncthreads();  // the previous tile's reads are done
+    stage();
+    __syncthreads();
+    if (k0 + BK < ke) load(k0 + BK);  // next tile's global reads overlap the products
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8 ah[2], al[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ah[i] = *reinterpret_cast<const bf16x8*>(&Ah[32 * wm + 16 * i + li][kk + 8 * g4]);
+        al[i] = *reinterpret_cast<const bf16x8*>(&Al[32 * wm + 16 * i + li][kk + 8 * g4]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bv[j] = *reinterpret_cast<const bf16x8*>(&Bs[32 * wn + 16 * j + li][kk + 8 * g4]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+  // acc[i][j][r] = C(m0 + 32wm + 16i + 4g4 + r, n0 + 32wn + 16j + li)
+  float* C = g.C + split * g.split_stride;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const long long n = n0 + 32 * wn + 16 * j + li;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const long long m = m0 + 32 * wm + 16 * i + 4 * g4 + r;
+        if (m < g.M) C[m * g.ldc + n] = acc[i][j][r];
+      }
+    }
+}
+
 // dW[n, d] and dbias[n] from the split partials [nsplit][HL][D + 1] (column D
 // holds the bias sums), summed in split order; nsplit = 0 writes zeros.
 __global__ void __launch_bounds__(256) lam_split_sum_kernel(const float* part, int nsplit, long long stride, int HL,
@@ -179,7 +302,7 @@ int launch_gemm(int dtype_a, int dtype_b, const GemmArgs& g, int nsplit, hipStre
   if (dtype_a == LL_F32 && dtype_b == LL_F32)
     hipLaunchKernelGGL((lam_gemm_kernel<float, float>), grid, dim3(lg::NT), 0, s, g);
   else if (dtype_a == LL_F32 && dtype_b == LL_BF16)
-    hipLaunchKernelGGL((lam_gemm_kernel<float, bf16>), grid, dim3(lg::NT), 0, s, g);
+    hipLaunchKernelGGL(lam_gemm16_kernel, grid, dim3(lg16::NT), 0, s, g);
   else
     return LL_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
@@ -200,7 +323,7 @@ int lambda_bwd_nsplit(long long rows, int HL, int D) {
 
 long long lambda_bwd_kper(long long rows, int nsplit) {
   const long long per = (rows + nsplit - 1) / nsplit;
-  return (per + lg::BK - 1) / lg::BK * lg::BK;
+  return (per + 63) / 64 * 64;  // whole K tiles of both product kernels
 }
 
 int launch_lambda_bwd(int dtype, const LamBwdArgs& a, float* part, int nsplit, hipStream_t s) {
