@@ -148,7 +148,8 @@ def bench_lambda(dev, steps: int, warmup: int):
     flops = 2 * w.B * w.T * w.D * w.H * w.L
     gbs = nbytes / (ms * 1e-3) / 1e9
     # gradient (loglinear_lambda_proj_bwd) from the last lambda and a fixed
-    # dlambda: dx = dz W and dW = dz^T x (+ dbias), fp32 matrix cores
+    # dlambda: dx = dz W and dW = dz^T x (+ dbias); bf16 inputs on bf16 matrix
+    # cores with dz split hi/lo, fp32 inputs on fp32 matrix cores
     dlam = torch.randn(w.B, w.H, w.T, w.L, generator=torch.Generator().manual_seed(0)).to(dev)
     bsteps, bwarm = max(3, steps // 2), 3
     for i in range(bwarm):
@@ -167,10 +168,11 @@ def bench_lambda(dev, steps: int, warmup: int):
     bgbs = bbytes / (bms * 1e-3) / 1e9
     # bf16 inputs: bf16 matrix cores (dz split hi/lo), intensity ~137 flop/B is
     # below the bf16 ridge -> HBM-bound; fp32 inputs: fp32 matrix cores, above
-    # the fp32 ridge (~20 flop/B) -> bound by the fp32 matrix peak
+    # the fp32 ridge (~20 flop/B) -> bound by the fp32 matrix peak.  The rate
+    # is over the whole call (dz kernel, the two products, the in-order sums).
     if w.dtype == "bf16":
-        broof = {"kernel": "lam_gemm16_kernel", "bound": "hbm", "achieved": bgbs, "peak": PEAK_HBM_GBS,
-                 "unit": "GB/s", "frac": bgbs / PEAK_HBM_GBS}
+        broof = {"kernel": "whole gradient (lam_dz16_kernel, lam_mm16_kernel x2, sums)", "bound": "hbm",
+                 "achieved": bgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": bgbs / PEAK_HBM_GBS}
     else:
         broof = {"kernel": "lam_gemm_kernel", "bound": "mfma", "achieved": btf, "peak": PEAK_FP32_TFLOPS,
                  "unit": "TFLOP/s", "frac": btf / PEAK_FP32_TFLOPS}

@@ -245,10 +245,14 @@ int loglinear_lambda_proj(const void* x, const void* W, const float* bias, float
  *   x, W        : as for loglinear_lambda_proj (dtype LL_BF16 or LL_F32)
  *   lambda      : [B, H, T, L] fp32, the forward's output
  *   grad_lambda : [B, H, T, L] fp32
- * All DEVICE pointers; outputs are overwritten.  Products on fp32 matrix cores
- * (bf16 inputs widened exactly), fp32 accumulation, no atomics (bitwise
- * repeatable).  Stream-ordered scratch of B*T*H*L floats for dz plus the dW
- * split partials (allocated and released on `stream`).  B*T = 0 writes zeros
+ * All DEVICE pointers; outputs are overwritten.  Arithmetic: fp32 inputs on
+ * fp32 matrix cores; bf16 inputs on bf16 matrix cores with dz split into bf16
+ * hi + lo (each product term within 2^-16 of the fp32 one); fp32
+ * accumulation, no atomics (bitwise repeatable).  Stream-ordered scratch
+ * (allocated and released on `stream`): for bf16 inputs with D % 8 == 0 and
+ * 16-byte aligned x, W, dz as two bf16 arrays of B*T rows of H*L rounded up to
+ * 128, per-64-token column sums and the dW split partials; otherwise B*T*H*L
+ * floats for dz plus the dW split partials.  B*T = 0 writes zeros
  * to grad_W and grad_bias.  Errors: bad dtype or sizes (L outside 1..31)
  * LL_ERR_SHAPE; D > 2^20, H*L > 2^16 or B*T >= 2^31 LL_ERR_UNSUPPORTED; a NULL
  * required pointer LL_ERR_NULL.

@@ -159,6 +159,17 @@ int launch_lambda_proj(int dtype, const LamProjArgs& a, hipStream_t s);
 int lambda_bwd_nsplit(long long rows, int HL, int D);
 long long lambda_bwd_kper(long long rows, int nsplit);
 int launch_lambda_bwd(int dtype, const LamBwdArgs& a, float* part, int nsplit, hipStream_t s);
+// bf16 inputs with D % 8 == 0 and 16-byte aligned x, W: dz split once into bf16
+// hi / lo, both products on bf16 matrix cores.  plan() returns false where the
+// path does not apply (then launch_lambda_bwd serves the call).
+struct Lam16Plan {
+  int HLp, nsplit, ntb;
+  long long kper;
+  size_t dz_bytes, colsum_bytes, part_bytes;
+};
+bool lambda_bwd16_plan(const LamBwdArgs& a, Lam16Plan* p);
+size_t lambda_bwd16_workspace(const Lam16Plan& p);
+int launch_lambda_bwd16(const LamBwdArgs& a, const Lam16Plan& p, void* ws, hipStream_t s);
 // out[i][e] = sum_{g < G} in[i * G + g][e] for i < rows, e < elems (elems % 4 == 0)
 int launch_group_sum(const float* in, float* out, long long rows, int G, long long elems, hipStream_t s);
 

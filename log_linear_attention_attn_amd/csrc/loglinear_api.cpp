@@ -248,6 +248,17 @@ int run_lambda_proj_bwd(int dtype, const void* x, const void* W, const float* la
   if (!W || !dW) return LL_ERR_NULL;
   if (M > 0 && (!x || !lam || !dlam || !dx)) return LL_ERR_NULL;
   const int HL = H * L;
+  if (dtype == LL_BF16) {
+    ll::LamBwdArgs a{x, W, lam, dlam, nullptr, dx, dW, dbias, B, T, D, H, L};
+    ll::Lam16Plan p;
+    if (ll::lambda_bwd16_plan(a, &p)) {
+      void* ws = nullptr;
+      if (hipMallocAsync(&ws, ll::lambda_bwd16_workspace(p), stream) != hipSuccess) return LL_ERR_HIP;
+      int st = ll::launch_lambda_bwd16(a, p, ws, stream);
+      if (hipFreeAsync(ws, stream) != hipSuccess && st == LL_OK) st = LL_ERR_HIP;
+      return st;
+    }
+  }
   const int nsplit = M > 0 ? ll::lambda_bwd_nsplit(M, HL, D) : 0;
   const size_t dz_bytes = align256((size_t)M * HL * sizeof(float));
   const size_t part_bytes = align256((size_t)nsplit * HL * (D + 1) * sizeof(float));

@@ -64,7 +64,9 @@ BWD_CASES = [
     # (B, T, D, H, L, dtype)
     (1, 1, 8, 1, 1, "bf16"),          # one row, one output column
     (2, 300, 256, 4, 9, "bf16"),      # ragged rows (600), 36 columns
-    (1, 1000, 2048, 16, 15, "bf16"),  # the bench shape's width, 240 columns
+    (1, 1000, 2048, 16, 15, "bf16"),  # the bench shape's width, 240 columns, four row splits
+    (3, 77, 200, 20, 15, "bf16"),     # 231 rows, 300 columns (3 tiles), D = 200 (ragged tile)
+    (2, 50, 100, 3, 7, "bf16"),       # D % 8 != 0: the small-tile kernels
     (3, 77, 100, 3, 7, "f32"),        # D not a multiple of the 64-wide tile
     (1, 130, 64, 20, 15, "f32"),      # 300 columns: five column tiles
 ]
@@ -73,14 +75,19 @@ BWD_CASES = [
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}T{}D{}H{}L{}_{}".format(*c))
 def test_lambda_proj_bwd_matches_oracle(case):
     """The gradient from the GPU's own lambda (as a training step chains it)
-    against the chain rule in fp64; two calls are bitwise equal."""
+    against the chain rule in fp64; two calls are bitwise equal.  Where the
+    forward does not take the shape (bf16 rows need D % 8 == 0) lambda is the
+    oracle's, rounded to fp32."""
     B, T, D, H, L, dtype = case
     w = W.LambdaProjWorkload("lpb", B, T, D, H, L, dtype, True, seed=T + 2 * D)
     x, Wt, b = W.make_lambda_proj_inputs(w)
     dlam = torch.from_numpy(np.random.default_rng(T + D).standard_normal((B, H, T, L)).astype(np.float32))
     announce(f"lambda_proj_bwd {case}")
     dx_, dW_ = to_dev(x, Wt)
-    lam = ll.lambda_proj(dx_, dW_, b.cuda(), H, L)
+    if dtype == "bf16" and D % 8:
+        lam = torch.from_numpy(oracle.lambda_projection(x, Wt, b, H, L).astype(np.float32)).cuda()
+    else:
+        lam = ll.lambda_proj(dx_, dW_, b.cuda(), H, L)
     gx, gW, gb = ll.lambda_proj_bwd(dx_, dW_, lam, dlam.cuda())
     gx2, gW2, gb2 = ll.lambda_proj_bwd(dx_, dW_, lam, dlam.cuda())
     torch.cuda.synchronize()
