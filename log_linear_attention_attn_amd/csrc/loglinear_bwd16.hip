@@ -12,7 +12,8 @@
 // chunks in reverse order.  Wave w works on key rows 16(w&3)..+15 of a chunk:
 // the two waves of a row tile (w>>2 = 0, 1) take one pair of score tiles and
 // half of the left-half levels each and add their partial outputs through
-// LDS; wave w updates the state of level w when the chunk is in its right half.  Every product runs as
+// LDS; the state updates of the levels whose right half holds the chunk are
+// shared out over all waves.  Every product runs as
 // v_mfma_f32_16x16x32_bf16: bf16 inputs are exact operands, fp32 ones (dO,
 // the masked scores, the level states, the weighted a) are split into bf16
 // hi + lo and multiplied term by term (hi*hi + lo*hi + hi*lo where both
@@ -371,15 +372,18 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
       }
     }
 
-    // ---- left-half levels (this half's parity): y_s += exp(decay s -> reference) x_s . R_b
+    // ---- left-half levels: y_s += exp(decay s -> reference) x_s . R_b; the
+    // k-th level that has one goes to half k & 1 (balanced for any bit pattern)
     {
       bf16x8 xa[4];
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq)
         if (32 * kq < dc) xa[kq] = frag(Xs, LDC, 16 * st, 32 * kq, lane);
+      int rank = 0;
 #pragma unroll
       for (int b = 0; b < NSMAX; ++b) {
-        if (b < nslot && (b & 1) == hf && !((n >> b) & 1) && ((n >> (b + 1)) << (b + 1)) + (1 << b) < N) {
+        if (!(b < nslot && !((n >> b) & 1) && ((n >> (b + 1)) << (b + 1)) + (1 << b) < N)) continue;
+        if (((rank++) & 1) == hf) {
           const bf16* Rh = reinterpret_cast<const bf16*>(Rbase + b * R_BYTES);
           const bf16* Rl = Rh + 16 * LDR;
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -410,47 +414,61 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
       }
     }
 
-    // ---- right-half levels: R_b[j][i] += sum_t WL_b[t] a_t[j] c_t[i].  Wave w
-    // updates level w (when its bit of n is set) over every column tile, so
-    // the weighted A operand of a level is formed once.
+    // ---- right-half levels: R_b[j][i] += sum_t WL_b[t] a_t[j] c_t[i] for
+    // every level whose bit of n is set.  The (level, 16-column tile) items
+    // are shared out evenly over the waves, each taking a contiguous run, so
+    // a chunk costs popcount(n) tiles per wave rather than every tile of one
+    // level; a wave forms the weighted A operand once per level it meets.
     {
-      const int b = w;
-      if (b < nslot && ((n >> b) & 1)) {
-        const int base = (n >> (b + 1)) << (b + 1);
-        const bool first = n == min(N, base + (1 << (b + 1))) - 1;
-        bf16x8 ah[2], al[2];  // A[j = li][t = 32ks + 8g4 + e] = WL_b[t] a_t[j]
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4 + 4);
-          const f32x4 w0 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4);
-          const f32x4 w1 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4 + 4);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            bf16 x1_, x2_;
-            split_bf16(e < 4 ? x0[e] * w0[e] : x1[e - 4] * w1[e - 4], x1_, x2_);
-            ah[ks][e] = x1_;
-            al[ks][e] = x2_;
-          }
-        }
-        float* Rf = reinterpret_cast<float*>(Rbase + b * R_BYTES);
-        for (int it = 0; it < dc / 16; ++it) {
-          const int i0 = 16 * it;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int ntile = dc / 16;
+      const unsigned live = static_cast<unsigned>(n) & ((1u << nslot) - 1u);
+      const int items = __builtin_popcount(live) * ntile;
+      const int per = (items + NW - 1) / NW;
+      const int k0 = w * per, k1 = min(items, k0 + per);
+      int cur = -1;
+      bool first = false;
+      bf16x8 ah[2], al[2];  // A[j = li][t = 32ks + 8g4 + e] = WL_b[t] a_t[j]
+      float* Rf = nullptr;
+      for (int k = k0; k < k1; ++k) {
+        const int lv = k / ntile, it = k - lv * ntile;
+        unsigned rest = live;  // b = the lv-th set bit of live
+        for (int q = 0; q < lv; ++q) rest &= rest - 1u;
+        const int b = __builtin_ctz(rest);
+        if (b != cur) {
+          cur = b;
+          const int base = (n >> (b + 1)) << (b + 1);
+          first = n == min(N, base + (1 << (b + 1))) - 1;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const int off = (32 * ks + 8 * g4 + (li >> 2)) * LDC + i0 + 4 * (li & 3);
-            const bf16x8 cb = cat(tr_read(Ch + off), tr_read(Ch + off + 4 * LDC));
-            acc = mma(ah[ks], cb, acc);
-            acc = mma(al[ks], cb, acc);
-            if (MODE == 1) acc = mma(ah[ks], cat(tr_read(Cl + off), tr_read(Cl + off + 4 * LDC)), acc);
-          }
-          // acc[r] = sum_t WL_b[t] a_t[j] c_t[i], j = 4g4 + r, i = i0 + li
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4 + 4);
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4 + 4);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float* p = Rf + (4 * g4 + r) * LDR + i0 + li;
-            *p = (first ? 0.f : *p) + acc[r];
+            for (int e = 0; e < 8; ++e) {
+              bf16 x1_, x2_;
+              split_bf16(e < 4 ? x0[e] * w0[e] : x1[e - 4] * w1[e - 4], x1_, x2_);
+              ah[ks][e] = x1_;
+              al[ks][e] = x2_;
+            }
           }
+          Rf = reinterpret_cast<float*>(Rbase + b * R_BYTES);
+        }
+        const int i0 = 16 * it;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int off = (32 * ks + 8 * g4 + (li >> 2)) * LDC + i0 + 4 * (li & 3);
+          const bf16x8 cb = cat(tr_read(Ch + off), tr_read(Ch + off + 4 * LDC));
+          acc = mma(ah[ks], cb, acc);
+          acc = mma(al[ks], cb, acc);
+          if (MODE == 1) acc = mma(ah[ks], cat(tr_read(Cl + off), tr_read(Cl + off + 4 * LDC)), acc);
+        }
+        // acc[r] = sum_t WL_b[t] a_t[j] c_t[i], j = 4g4 + r, i = i0 + li
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* p = Rf + (4 * g4 + r) * LDR + i0 + li;
+          *p = (first ? 0.f : *p) + acc[r];
         }
       }
     }
@@ -694,7 +712,8 @@ __global__ void __launch_bounds__(b16::NT) bwd_dq16_kernel(BwdArgs a) {
     }
     // Y[r]: t = 16tt + 4g4 + r, j = li
 
-    // ---- inter chunk: right-half levels of this half's parity
+    // ---- inter chunk: right-half levels; the k-th live level goes to half
+    // k & 1, and the zero dlambda partials of the other levels by parity
     {
       bf16x8 dah[4], dal[4];
 #pragma unroll
@@ -703,38 +722,49 @@ __global__ void __launch_bounds__(b16::NT) bwd_dq16_kernel(BwdArgs a) {
           dah[kq] = frag(Dh, LDC, 16 * tt, 32 * kq, lane);
           dal[kq] = frag(Dl, LDC, 16 * tt, 32 * kq, lane);
         }
+      int rank = 0;
 #pragma unroll
       for (int b = 0; b < NSMAX; ++b) {
-        if (b < nslot && (b & 1) == hf) {
-          float x[4] = {0.f, 0.f, 0.f, 0.f};
-          if ((n >> b) & 1) {
-            const bf16* Sh = reinterpret_cast<const bf16*>(Sbase + b * R_BYTES);
-            const bf16* Sl = Sh + 16 * LDR;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kq = 0; kq < 4; ++kq)
-              if (32 * kq < dv) {
-                const bf16x8 sh = frag(Sh, LDR, 0, 32 * kq, lane);
-                acc = mma(dah[kq], sh, acc);
-                acc = mma(dal[kq], sh, acc);
-                acc = mma(dah[kq], frag(Sl, LDR, 0, 32 * kq, lane), acc);
-              }
-            // acc[r] = dO_t . St_b[j], t = 16tt + 4g4 + r, j = li
+        if (b >= nslot) continue;
+        if (!((n >> b) & 1)) {  // no bucket at this level: zero partial
+          if ((b & 1) == hf && li == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int t = 16 * tt + 4 * g4 + r;
-              const float wt = __expf(static_cast<float>(cl_s[t]) + dlt[b]) * acc[r];
-              Y[r] += lam_s[t * L + LOGC + 1 + b] * wt;
-              x[r] = wt * Qs[t * DqLay::LDQS + li];
+              const int t = tok0 + 16 * tt + 4 * g4 + r;
+              if (t < T) part[(size_t)t * nslot + b] = 0.f;
             }
           }
-          // this slice's dlambda partial (0 where the level has no bucket)
+          continue;
+        }
+        if (((rank++) & 1) != hf) continue;
+        float x[4];
+        {
+          const bf16* Sh = reinterpret_cast<const bf16*>(Sbase + b * R_BYTES);
+          const bf16* Sl = Sh + 16 * LDR;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kq = 0; kq < 4; ++kq)
+            if (32 * kq < dv) {
+              const bf16x8 sh = frag(Sh, LDR, 0, 32 * kq, lane);
+              acc = mma(dah[kq], sh, acc);
+              acc = mma(dal[kq], sh, acc);
+              acc = mma(dah[kq], frag(Sl, LDR, 0, 32 * kq, lane), acc);
+            }
+          // acc[r] = dO_t . St_b[j], t = 16tt + 4g4 + r, j = li
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float sx = row_sum16(x[r]);
-            const int t = tok0 + 16 * tt + 4 * g4 + r;
-            if (li == 0 && t < T) part[(size_t)t * nslot + b] = sx;
+            const int t = 16 * tt + 4 * g4 + r;
+            const float wt = __expf(static_cast<float>(cl_s[t]) + dlt[b]) * acc[r];
+            Y[r] += lam_s[t * L + LOGC + 1 + b] * wt;
+            x[r] = wt * Qs[t * DqLay::LDQS + li];
           }
+        }
+        // this slice's dlambda partial
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sx = row_sum16(x[r]);
+          const int t = tok0 + 16 * tt + 4 * g4 + r;
+          if (li == 0 && t < T) part[(size_t)t * nslot + b] = sx;
         }
       }
     }
