@@ -425,51 +425,71 @@ __global__ void __launch_bounds__(b16::NT) bwd_kv16_kernel(BwdArgs a) {
       const int items = __builtin_popcount(live) * ntile;
       const int per = (items + NW - 1) / NW;
       const int k0 = w * per, k1 = min(items, k0 + per);
-      int cur = -1;
-      bool first = false;
       bf16x8 ah[2], al[2];  // A[j = li][t = 32ks + 8g4 + e] = WL_b[t] a_t[j]
-      float* Rf = nullptr;
-      for (int k = k0; k < k1; ++k) {
-        const int lv = k / ntile, it = k - lv * ntile;
+      // the run [k0, k1) covers at most a few levels; each level's tiles are
+      // done in batches of four with independent accumulators, written as
+      // straight-line code (tile indices clamped to the level's last tile,
+      // stores predicated) so the reads, products and state updates of a
+      // batch overlap instead of forming one chain per tile
+      for (int k = k0; k < k1;) {
+        const int lv = k / ntile, it0 = k - lv * ntile;
+        const int cnt = min(k1 - k, ntile - it0);
         unsigned rest = live;  // b = the lv-th set bit of live
         for (int q = 0; q < lv; ++q) rest &= rest - 1u;
         const int b = __builtin_ctz(rest);
-        if (b != cur) {
-          cur = b;
-          const int base = (n >> (b + 1)) << (b + 1);
-          first = n == min(N, base + (1 << (b + 1))) - 1;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4 + 4);
-            const f32x4 w0 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4);
-            const f32x4 w1 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4 + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              bf16 x1_, x2_;
-              split_bf16(e < 4 ? x0[e] * w0[e] : x1[e - 4] * w1[e - 4], x1_, x2_);
-              ah[ks][e] = x1_;
-              al[ks][e] = x2_;
-            }
-          }
-          Rf = reinterpret_cast<float*>(Rbase + b * R_BYTES);
-        }
-        const int i0 = 16 * it;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int base = (n >> (b + 1)) << (b + 1);
+        const bool first = n == min(N, base + (1 << (b + 1))) - 1;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int off = (32 * ks + 8 * g4 + (li >> 2)) * LDC + i0 + 4 * (li & 3);
-          const bf16x8 cb = cat(tr_read(Ch + off), tr_read(Ch + off + 4 * LDC));
-          acc = mma(ah[ks], cb, acc);
-          acc = mma(al[ks], cb, acc);
-          if (MODE == 1) acc = mma(ah[ks], cat(tr_read(Cl + off), tr_read(Cl + off + 4 * LDC)), acc);
-        }
-        // acc[r] = sum_t WL_b[t] a_t[j] c_t[i], j = 4g4 + r, i = i0 + li
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(ATf + li * LDAT + 32 * ks + 8 * g4 + 4);
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(WL + b * C + 32 * ks + 8 * g4 + 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float* p = Rf + (4 * g4 + r) * LDR + i0 + li;
-          *p = (first ? 0.f : *p) + acc[r];
+          for (int e = 0; e < 8; ++e) {
+            bf16 x1_, x2_;
+            split_bf16(e < 4 ? x0[e] * w0[e] : x1[e - 4] * w1[e - 4], x1_, x2_);
+            ah[ks][e] = x1_;
+            al[ks][e] = x2_;
+          }
         }
+        float* Rf = reinterpret_cast<float*>(Rbase + b * R_BYTES);
+        for (int j0 = 0; j0 < cnt; j0 += 4) {
+          int i0[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) i0[u] = 16 * (it0 + min(j0 + u, cnt - 1));
+          f32x4 acc[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 cb[4], cl8[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int off = (32 * ks + 8 * g4 + (li >> 2)) * LDC + i0[u] + 4 * (li & 3);
+              cb[u] = cat(tr_read(Ch + off), tr_read(Ch + off + 4 * LDC));
+              if (MODE == 1) cl8[u] = cat(tr_read(Cl + off), tr_read(Cl + off + 4 * LDC));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              acc[u] = mma(ah[ks], cb[u], acc[u]);
+              acc[u] = mma(al[ks], cb[u], acc[u]);
+              if (MODE == 1) acc[u] = mma(ah[ks], cl8[u], acc[u]);
+            }
+          }
+          // acc[u][r] = sum_t WL_b[t] a_t[j] c_t[i], j = 4g4 + r, i = i0[u] + li
+          float old[4][4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) old[u][r] = first ? 0.f : Rf[(4 * g4 + r) * LDR + i0[u] + li];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (j0 + u < cnt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) Rf[(4 * g4 + r) * LDR + i0[u] + li] = old[u][r] + acc[u][r];
+        }
+        k += cnt;
       }
     }
     __syncthreads();
