@@ -628,12 +628,16 @@ __global__ void __launch_bounds__(256) seg_node_kernel(NodeArgs a) {
 // chunk: level 0 is {t}, level l >= 1 (when bit l-1 of t is set) the 2^(l-1)
 // tokens below t's bit l-1 (page above, section 前缀的层次化分解).  Each is
 // sum_s exp(cum[t] - cum[s]) k_s v_s^T in fp32.  One workgroup per (b,h, 64
-// dv columns, level): the bucket's k and decayed v rows (at most C/2 tokens)
-// are staged in LDS, then each thread sums its (dk, dv) elements.
+// dv columns, level): the decay of each bucket token to t is one suffix sum of
+// log_a over (lo, t] (a shuffle scan in one wave), the bucket's k and decayed v
+// rows (at most C/2 tokens) are staged in LDS, and each thread forms 4 x 4
+// blocks of the (dk, dv) state from float4 reads and writes them as float4
+// rows.
 template <typename IT>
 __global__ void __launch_bounds__(256) handoff_intra_kernel(HandoffArgs a) {
-  __shared__ float ks[32][128];   // k rows of the bucket
-  __shared__ float vw[32][64];    // exp(cum[t] - cum[s]) v_s, this workgroup's columns
+  __shared__ __align__(16) float ks[32][128];  // k rows of the bucket
+  __shared__ __align__(16) float vw[32][64];   // exp(cum[t] - cum[s]) v_s, this workgroup's columns
+  __shared__ float es[32];                     // exp(cum[t] - cum[s]) per bucket token
   const int bh = blockIdx.x, dv0 = blockIdx.y * 64, lev = blockIdx.z;
   const int tid = threadIdx.x;
   const int T = a.T, dk = a.dk, dv = a.dv;
@@ -654,23 +658,59 @@ __global__ void __launch_bounds__(256) handoff_intra_kernel(HandoffArgs a) {
   const IT* __restrict__ vg = static_cast<const IT*>(a.v) + bhT * dv;
   float* __restrict__ so = a.st_out + ((size_t)bh * a.st_L + lev) * dk * dv;
   if (nb > 0) {
+    if (tid < 64) {
+      // lane i holds log_a of token lo + 1 + i (tokens up to t; t - lo <= C - 1 <= 63);
+      // the suffix sum from lane s is the log decay from token lo + s to t
+      float x = tid < t - lo ? a.log_a[bhT + lo + 1 + tid] : 0.f;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_down(x, off);
+        if (tid + off < 64) x += y;
+      }
+      if (tid < nb) es[tid] = __expf(x);
+    }
     for (int i = tid; i < nb * dk; i += 256) {
       const int s = i / dk, d = i - s * dk;
       ks[s][d] = to_float(kg[(size_t)(lo + s) * dk + d]);
     }
+  }
+  __syncthreads();
+  if (nb > 0) {
     for (int i = tid; i < nb * 64; i += 256) {
       const int s = i >> 6, j = i & 63;
-      float dec = 0.f;  // sum of log_a over (lo + s, t], summed directly
-      for (int r = lo + s + 1; r <= t; ++r) dec += a.log_a[bhT + r];
-      vw[s][j] = j < ncol ? __expf(dec) * to_float(vg[(size_t)(lo + s) * dv + dv0 + j]) : 0.f;
+      vw[s][j] = j < ncol ? es[s] * to_float(vg[(size_t)(lo + s) * dv + dv0 + j]) : 0.f;
     }
   }
   __syncthreads();
-  for (int i = tid; i < dk * ncol; i += 256) {
-    const int d = i / ncol, j = i - d * ncol;
-    float x = 0.f;
-    for (int s = 0; s < nb; ++s) x += ks[s][d] * vw[s][j];
-    so[(size_t)d * dv + dv0 + j] = x;
+  // thread: columns 4jq..4jq+3, rows 4dq + 64u .. +3 (u = 0, 1)
+  const int jq = tid & 15, dq = tid >> 4;
+  const bool vec = ((reinterpret_cast<uintptr_t>(so) | static_cast<uintptr_t>(dv0 * 4) |
+                     static_cast<uintptr_t>(dv * 4)) & 15) == 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int d0 = 4 * dq + 64 * u;
+    if (d0 >= dk || 4 * jq >= ncol) continue;
+    f32x4 acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nb; ++s) {
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(&ks[s][d0]);
+      const f32x4 vv = *reinterpret_cast<const f32x4*>(&vw[s][4 * jq]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += kv[r] * vv;
+    }
+    const int nc = min(4, ncol - 4 * jq);  // columns of this group inside the slice
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (d0 + r >= dk) break;
+      float* p = so + (size_t)(d0 + r) * dv + dv0 + 4 * jq;
+      if (vec && nc == 4) {
+        *reinterpret_cast<f32x4*>(p) = acc[r];
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (c < nc) p[c] = acc[r][c];
+      }
+    }
   }
 }
 
