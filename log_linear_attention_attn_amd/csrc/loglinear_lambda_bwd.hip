@@ -427,8 +427,9 @@ struct MmArgs {
 // false, element at a[m * lda + k]) or [k][m] (AT = true, a[k * lda + m]); B
 // is stored [k][n] (b[k * ldb + n]).  Elements with m >= M, n >= N or k >= K
 // read as zero.  Host preconditions: lda, ldb multiples of 8 and 16-byte
-// aligned bases; AT = false needs the A rows zero-padded to lda >= K rounded
-// up to 32; AT = true needs lda a multiple of 128 (whole m tiles in range).
+// aligned bases; N and ldc multiples of 4 and C 16-byte aligned (float4
+// rows); AT = false needs the A rows zero-padded to lda >= K rounded up to
+// 32; AT = true needs lda a multiple of 128 (whole m tiles in range).
 // 256 threads, a 128 x 128 tile, waves in a 2 x 2 grid of 64 x 64; K steps of
 // 32 through double-buffered LDS, each step's loads issued two steps ahead into
 // one of two register sets, one barrier per step.  Workgroup ids are remapped so that
@@ -559,20 +560,31 @@ __global__ void __launch_bounds__(lmm::NT, 2) lam_mm16_kernel(MmArgs g) {
     __syncthreads();
   }
 
-  // acc[i][j][r] = C(m0 + 64wm + 16i + 4g4 + r, n0 + 64wn + 16j + li)
+  // acc[i][j][r] = C(m0 + 64wm + 16i + 4g4 + r, n0 + 64wn + 16j + li).  The
+  // wave's 64 x 64 block goes out through its own LDS region (the operand
+  // buffers are free after the loop's last barrier), 32 rows at a time, so
+  // each row leaves as one 256-byte piece of float4 stores instead of four
+  // 64-byte pieces (partial lines cost full-line writes).
   float* C = g.c + split * g.split_stride;
+  constexpr int LDO = 64 + 4;  // staging row stride (floats): 16-byte aligned rows
+  float* stg = reinterpret_cast<float*>(sm) + w * (32 * LDO);
+  const long long mw = m0 + 64 * wm, nw = n0 + 64 * wn;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long long n = n0 + 64 * wn + 16 * j + li;
-      if (n >= g.N) continue;
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const long long m = m0 + 64 * wm + 16 * i + 4 * g4 + r;
-        if (m < g.M) __builtin_nontemporal_store(acc[i][j][r], C + m * g.ldc + n);
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stg[(16 * ii + 4 * g4 + r) * LDO + 16 * j + li] = acc[2 * h + ii][j][r];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = 4 * it + (lane >> 4), c4 = 4 * (lane & 15);
+      const long long m = mw + 32 * h + row, n = nw + c4;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(stg + row * LDO + c4);
+      if (m < g.M && n < g.N) __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(C + m * g.ldc + n));
     }
+  }
 }
 
 namespace {
@@ -612,7 +624,8 @@ bool lambda_bwd16_plan(const LamBwdArgs& a, Lam16Plan* p) {
   const long long M = (long long)a.B * a.T;
   const long long HL = (long long)a.H * a.L;
   if (M <= 0 || a.D % 8 != 0) return false;
-  if ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.W)) & 15) return false;
+  if ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.W) | reinterpret_cast<uintptr_t>(a.dx)) & 15)
+    return false;
   const long long HLp = (HL + 127) / 128 * 128;
   const long long ntm = (HL + 127) / 128, ntn = (a.D + 127) / 128;
   long long ns = (512 + ntm * ntn - 1) / (ntm * ntn);
