@@ -529,18 +529,32 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dlam_intra_kernel(BwdArgs a) 
 
 // ---------------------------------------------------------------------------
 // bwd_dlam_inter_kernel: dlam of the chunk levels, the sum of the per-slice
-// partials (0 past the levels a row reaches); one thread per (b,h, t).
+// partials in slice order (0 past the levels a row reaches).  One thread per
+// (b,h, t, level b < nslot): the partials of one slice and (b,h) are one
+// contiguous [T][nslot] block, so consecutive threads read consecutive words.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_dlam_inter_kernel(BwdArgs a, int logc, int nparts) {
   const int T = a.T, L = a.L, nslot = a.nslot;
-  const int bh = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
-  for (int b = 0; b + logc + 1 < L; ++b) {
-    float x = 0.f;
-    if (b < nslot)
-      for (int p = 0; p < nparts; ++p) x += a.dlam_part[(((size_t)p * a.BH + bh) * T + t) * nslot + b];
-    a.dlam[((size_t)bh * T + t) * L + logc + 1 + b] = x;
+  const int ns = nslot > 0 ? nslot : 1;  // nslot = 0: one thread per row writes its zeros
+  const int bh = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // t * ns + b
+  if (e >= (long long)T * ns) return;
+  const int t = static_cast<int>(e / ns), b = static_cast<int>(e - (long long)t * ns);
+  float* __restrict__ row = a.dlam + ((size_t)bh * T + t) * L + logc + 1;
+  float x = 0.f;
+  if (b < nslot) {
+    // every slice's load is issued before the in-order sum (nparts <= 8)
+    const size_t pstride = (size_t)a.BH * T * nslot;
+    const float* __restrict__ src = a.dlam_part + (size_t)bh * T * nslot + e;
+    float v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) v[p] = p < nparts ? src[p * pstride] : 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) x += v[p];
   }
+  if (b + logc + 1 < L) row[b] = x;
+  if (b == ns - 1)
+    for (int q = ns; q + logc + 1 < L; ++q) row[q] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -650,7 +664,11 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((bwd_dlam_intra_kernel<IT, C>), dim3(a.BH * N), dim3(NT), 0, s, a);
   }
-  hipLaunchKernelGGL(bwd_dlam_inter_kernel, dim3((a.T + 255) / 256, a.BH), dim3(256), 0, s, a, Lg<C>::v, a.dk / 16);
+  {
+    const long long elems = (long long)a.T * (a.nslot > 0 ? a.nslot : 1);
+    hipLaunchKernelGGL(bwd_dlam_inter_kernel, dim3(static_cast<unsigned>((elems + 255) / 256), a.BH), dim3(256), 0, s,
+                       a, Lg<C>::v, a.dk / 16);
+  }
   const size_t rows = (size_t)a.BH * a.T;
   hipLaunchKernelGGL((bwd_dcum_kernel<IT>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, a, a.dc);
   hipLaunchKernelGGL(bwd_dlog_a_kernel, dim3(a.BH), dim3(256), 0, s, a, a.dc);
