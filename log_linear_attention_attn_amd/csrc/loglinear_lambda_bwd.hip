@@ -350,7 +350,15 @@ __global__ void __launch_bounds__(256) lam_rowsum_kernel(const float* in, int nr
                                                          long long count, float* out) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < count; i += (long long)gridDim.x * 256) {
     float s = 0.f;
-    for (int r = 0; r < nrows; ++r) s += in[r * stride + i];
+    int r = 0;
+    for (; r + 8 <= nrows; r += 8) {  // eight loads in flight, added in row order
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = in[(r + q) * stride + i];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    for (; r < nrows; ++r) s += in[r * stride + i];
     out[i] = s;
   }
 }
@@ -364,8 +372,18 @@ __global__ void __launch_bounds__(256) lam_colsum_kernel(const float* in, int nr
   const int c = threadIdx.x & 15, grp = threadIdx.x >> 4;
   const long long col = (long long)blockIdx.x * 16 + c;
   float s = 0.f;
-  if (col < ncols)
-    for (int r = grp; r < nrows; r += 16) s += in[r * ld + col];
+  if (col < ncols) {
+    // eight loads in flight, added in row order
+    int r = grp;
+    for (; r + 7 * 16 < nrows; r += 8 * 16) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = in[(long long)(r + 16 * q) * ld + col];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    for (; r < nrows; r += 16) s += in[(long long)r * ld + col];
+  }
   ps[grp][c] = s;
   __syncthreads();
   if (grp == 0 && col < ncols) {
