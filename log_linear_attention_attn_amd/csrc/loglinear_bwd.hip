@@ -584,18 +584,46 @@ __global__ void __launch_bounds__(256) bwd_dcum_kernel(BwdArgs a, double* dc) {
 __global__ void __launch_bounds__(256) bwd_dlog_a_kernel(BwdArgs a, const double* dc) {
   const int bh = blockIdx.x, tid = threadIdx.x, T = a.T;
   const double* __restrict__ d = dc + (size_t)bh * T;
+  float* __restrict__ out = a.dlog_a + (size_t)bh * T;
   __shared__ double part[256];
   const int per = (T + 255) / 256;
   const int t0 = min(T, tid * per), t1 = min(T, t0 + per);
+  // this thread's range total, eight loads in flight
   double s = 0.0;
-  for (int t = t0; t < t1; ++t) s += d[t];
+  int t = t0;
+  for (; t + 8 <= t1; t += 8) {
+    double v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = d[t + q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[q];
+  }
+  for (; t < t1; ++t) s += d[t];
   part[tid] = s;
   __syncthreads();
-  double run = 0.0;  // sum of the ranges of the threads above
-  for (int i = tid + 1; i < 256; ++i) run += part[i];
-  for (int t = t1 - 1; t >= t0; --t) {
-    run += d[t];
-    a.dlog_a[(size_t)bh * T + t] = static_cast<float>(run);
+  // inclusive suffix sums of the range totals (log-step scan)
+  for (int off = 1; off < 256; off <<= 1) {
+    const double v = tid + off < 256 ? part[tid + off] : 0.0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  double run = tid + 1 < 256 ? part[tid + 1] : 0.0;  // sum of the ranges of the threads above
+  // reverse prefix over the range, eight loads in flight
+  t = t1;
+  for (; t - 8 >= t0; t -= 8) {
+    double v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = d[t - 1 - q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      run += v[q];
+      out[t - 1 - q] = static_cast<float>(run);
+    }
+  }
+  for (; t > t0; --t) {
+    run += d[t - 1];
+    out[t - 1] = static_cast<float>(run);
   }
 }
 
