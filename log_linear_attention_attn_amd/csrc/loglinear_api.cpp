@@ -33,7 +33,7 @@ struct FwdPlan {
 // critical path is (rounds of workgroups over the 256 CUs of an MI355X) x
 // (chunks per segment + ~2 chunks' worth of prologue): the segment size
 // minimising that, the largest on a tie (fewer segment states, less prologue
-// traffic), up to 64 chunks.  Other
+// traffic, one round instead of several), up to 1024 chunks.  Other
 // shapes (16 dv columns per workgroup, several workgroups per CU): the largest
 // size, up to 16 chunks, that still gives at least 2048 workgroups.  Depends
 // on shapes only, so the workspace size is known without the dtype.
@@ -45,7 +45,7 @@ int auto_seg_log2(long long BH, int dk, int dv, int C, int N) {
     const long long per_seg = BH * (dv / 64);
     int best = 6;
     long long best_cost = -1;
-    for (int s = 6; s >= 0; --s) {
+    for (int s = 10; s >= 0; --s) {
       const long long nseg = (N + (1LL << s) - 1) >> s;
       const long long rounds = (per_seg * nseg + kCUs - 1) / kCUs;
       const long long cost = rounds * (std::min<long long>(1LL << s, N) + 2);
