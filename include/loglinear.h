@@ -172,7 +172,9 @@ int loglinear_prefill_f32(const float* q, const float* k, const float* v, const 
  * loglinear_fwd (page above, sections 并行形式 and 与已有模型的组合 define the
  * operator being differentiated; 训练：分块并行扫描算法 the chunking reused here).
  *   q, k, v, log_a, lambda : the forward's inputs (bf16 q, k, v)
- *   out    : [B, H, T, dv] fp32, the forward's output for these inputs
+ *   out    : [B, H, T, dv] fp32, the forward's output for these inputs (kept in
+ *            the signature; the gradients do not read it: d log_a takes
+ *            dO_t . O_t as sum_l lambda[t,l] grad_lambda[t,l], the same sum)
  *   dout   : [B, H, T, dv] fp32, gradient with respect to out
  *   grad_q, grad_k : [B, H, T, dk] fp32;  grad_v : [B, H, T, dv] fp32
  *   grad_log_a : [B, H, T] fp32;  grad_lambda : [B, H, T, L] fp32

@@ -558,7 +558,8 @@ __global__ void __launch_bounds__(256) bwd_dlam_inter_kernel(BwdArgs a, int logc
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dcum_kernel: dc_t = dO_t . O_t - v_t . dV_t (fp64), one wave per token.
+// bwd_dcum_kernel: dc_t = dO_t . O_t - v_t . dV_t (fp64), one wave per token;
+// dO_t . O_t is taken as sum_l lambda[t,l] dlambda[t,l] once dlambda is final.
 // bwd_dlog_a_kernel: dlog_a = reverse prefix sum of dc over T, one workgroup
 // per (b,h), each thread a contiguous range, fp64 (the two parts of dc largely
 // cancel and the sum runs over up to T terms).
@@ -569,16 +570,47 @@ __global__ void __launch_bounds__(256) bwd_dcum_kernel(BwdArgs a, double* dc) {
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b,h, t) flattened
   const int lane = threadIdx.x & 63;
   if (row >= (size_t)a.BH * T) return;
-  const float* __restrict__ dO = a.dout + row * dv;
-  const float* __restrict__ O = a.out + row * dv;
+  // dO_t . O_t = sum_l lambda[t, l] dlambda[t, l] (both sum the same pairs
+  // (q_t . k_s)(dO_t . v_s) exp(cum_t - cum_s) lambda[t, l(t,s)]), so the
+  // forward output and dO need not be read again
+  const int L = a.L;
+  const float* __restrict__ lam = a.lam + row * L;
+  const float* __restrict__ dlam = a.dlam + row * L;
   const float* __restrict__ dV = a.dvo + row * dv;
   const IT* __restrict__ v = static_cast<const IT*>(a.v) + row * dv;
   double x = 0.0;
-  for (int j = lane; j < dv; j += 64)
-    x += (double)dO[j] * O[j] - (double)static_cast<float>(v[j]) * dV[j];
+  for (int l = lane; l < L; l += 64) x += (double)lam[l] * dlam[l];
+  for (int j = lane; j < dv; j += 64) x -= (double)static_cast<float>(v[j]) * dV[j];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
   if (lane == 0) dc[row] = x;
+}
+
+// The same for dv / 8 a power of two up to 64 (bf16 v): G = dv / 8 lanes per
+// token, each with eight columns as 16-byte loads, so a wave covers 64 / G
+// tokens; the lane group's sums are reduced by xor shuffles inside the group.
+template <int G>
+__global__ void __launch_bounds__(256) bwd_dcum16_kernel(BwdArgs a, double* dc) {
+  constexpr int TPW = 64 / G;  // tokens per wave
+  const int T = a.T, dv = a.dv, L = a.L;
+  const int lane = threadIdx.x & 63, gl = lane & (G - 1);
+  const size_t row = ((size_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW + lane / G;
+  const bool ok = row < (size_t)a.BH * T;
+  double x = 0.0;
+  if (ok) {
+    const bf16x8 vv = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.v) + row * dv + 8 * gl);
+    const f32x4 d0 = *reinterpret_cast<const f32x4*>(a.dvo + row * dv + 8 * gl);
+    const f32x4 d1 = *reinterpret_cast<const f32x4*>(a.dvo + row * dv + 8 * gl + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x -= (double)static_cast<float>(vv[e]) * d0[e];
+      x -= (double)static_cast<float>(vv[e + 4]) * d1[e];
+    }
+    for (int l = gl; l < L; l += G) x += (double)a.lam[row * L + l] * a.dlam[row * L + l];
+  }
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if (ok && gl == 0) dc[row] = x;
 }
 
 __global__ void __launch_bounds__(256) bwd_dlog_a_kernel(BwdArgs a, const double* dc) {
@@ -698,7 +730,27 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
                        a, Lg<C>::v, a.dk / 16);
   }
   const size_t rows = (size_t)a.BH * a.T;
-  hipLaunchKernelGGL((bwd_dcum_kernel<IT>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, a, a.dc);
+  {
+    // bf16 v with dv / 8 a power of two <= 64: grouped lanes and vector loads
+    const int g = a.dv / 8;
+    const bool aligned = ((reinterpret_cast<uintptr_t>(a.v) | reinterpret_cast<uintptr_t>(a.dvo)) & 15) == 0;
+    const bool grouped = sizeof(IT) == 2 && aligned && a.dv % 8 == 0 && g >= 1 && g <= 64 && (g & (g - 1)) == 0;
+    if (grouped) {
+      const size_t waves = (rows * g + 63) / 64;
+      const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+      switch (g) {
+        case 1: hipLaunchKernelGGL(bwd_dcum16_kernel<1>, grid, dim3(256), 0, s, a, a.dc); break;
+        case 2: hipLaunchKernelGGL(bwd_dcum16_kernel<2>, grid, dim3(256), 0, s, a, a.dc); break;
+        case 4: hipLaunchKernelGGL(bwd_dcum16_kernel<4>, grid, dim3(256), 0, s, a, a.dc); break;
+        case 8: hipLaunchKernelGGL(bwd_dcum16_kernel<8>, grid, dim3(256), 0, s, a, a.dc); break;
+        case 16: hipLaunchKernelGGL(bwd_dcum16_kernel<16>, grid, dim3(256), 0, s, a, a.dc); break;
+        case 32: hipLaunchKernelGGL(bwd_dcum16_kernel<32>, grid, dim3(256), 0, s, a, a.dc); break;
+        default: hipLaunchKernelGGL(bwd_dcum16_kernel<64>, grid, dim3(256), 0, s, a, a.dc); break;
+      }
+    } else {
+      hipLaunchKernelGGL((bwd_dcum_kernel<IT>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, a, a.dc);
+    }
+  }
   hipLaunchKernelGGL(bwd_dlog_a_kernel, dim3(a.BH), dim3(256), 0, s, a, a.dc);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
