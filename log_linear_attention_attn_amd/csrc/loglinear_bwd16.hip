@@ -906,20 +906,33 @@ __global__ void __launch_bounds__(256) bwd_dlam_intra16_kernel(BwdArgs a) {
   float acc_l[LOGC + 1];
 #pragma unroll
   for (int l = 0; l <= LOGC; ++l) acc_l[l] = 0.f;
-  for (int kb = 0; kb <= w; ++kb) {
+  // key tiles 0..w; each tile's k and v rows are loaded one tile ahead
+  bf16x8 kn[4], vn[4];
+  auto load_kv = [&](int kb) {
     const int srow = 16 * kb + li;  // key row this lane loads for the A operands
     const bool sok = tok0 + srow < T;
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      if (32 * kq < dk) kn[kq] = sok ? *reinterpret_cast<const bf16x8*>(kg + (size_t)srow * dk + 32 * kq + 8 * g4) : bf16x8{};
+      if (32 * kq < dv) vn[kq] = sok ? *reinterpret_cast<const bf16x8*>(vg + (size_t)srow * dv + 32 * kq + 8 * g4) : bf16x8{};
+    }
+  };
+  load_kv(0);
+  for (int kb = 0; kb <= w; ++kb) {
+    bf16x8 ka[4], va[4];
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      ka[kq] = kn[kq];
+      va[kq] = vn[kq];
+    }
+    if (kb < w) load_kv(kb + 1);
     f32x4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
-      if (32 * kq < dk) {
-        const bf16x8 ka = sok ? *reinterpret_cast<const bf16x8*>(kg + (size_t)srow * dk + 32 * kq + 8 * g4) : bf16x8{};
-        z1 = mma(ka, qb[kq], z1);
-      }
+      if (32 * kq < dk) z1 = mma(ka[kq], qb[kq], z1);
       if (32 * kq < dv) {
-        const bf16x8 va = sok ? *reinterpret_cast<const bf16x8*>(vg + (size_t)srow * dv + 32 * kq + 8 * g4) : bf16x8{};
-        z2 = mma(va, dh[kq], z2);
-        z2 = mma(va, dl[kq], z2);
+        z2 = mma(va[kq], dh[kq], z2);
+        z2 = mma(va[kq], dl[kq], z2);
       }
     }
     // z1[r] = k_s . q_t, z2[r] = v_s . dO_t, s = 16kb + 4g4 + r
