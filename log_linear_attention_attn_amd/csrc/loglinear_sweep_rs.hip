@@ -530,6 +530,10 @@ fwd_rs_kernel(FwdArgs a) {
     // chunk's Q.G products and overlap the P V products.  K and V of chunk n
     // stay in their parity buffer until the staging of chunk n+2, which comes
     // after the next chunk's second barrier.
+    // The fold runs at raised wave priority: its vector work then issues ahead
+    // of the partner wave's, which is still in its matrix products (measured
+    // ~1.5% faster for the whole sweep).
+    __builtin_amdgcn_s_setprio(1);
     if (n + 1 < n1) {
       const int m = __builtin_ctz(static_cast<unsigned>(n + 1));
       // decayed V of this wave's columns, tokens 32ks + 8g4 + e, split hi/lo
@@ -613,6 +617,7 @@ fwd_rs_kernel(FwdArgs a) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     Aprev = Atot;
   }
 
