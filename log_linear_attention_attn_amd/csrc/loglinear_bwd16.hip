@@ -733,7 +733,9 @@ __global__ void __launch_bounds__(b16::NT) bwd_dq16_kernel(BwdArgs a) {
     // Y[r]: t = 16tt + 4g4 + r, j = li
 
     // ---- inter chunk: right-half levels; the k-th live level goes to half
-    // k & 1, and the zero dlambda partials of the other levels by parity
+    // k & 1, and the zero dlambda partials of the other levels by parity.  Run
+    // at raised wave priority (measured ~0.6% faster for the whole backward).
+    __builtin_amdgcn_s_setprio(1);
     {
       bf16x8 dah[4], dal[4];
 #pragma unroll
@@ -788,6 +790,7 @@ __global__ void __launch_bounds__(b16::NT) bwd_dq16_kernel(BwdArgs a) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (hf == 1) Yx[tt * 64 + lane] = Y;
     __syncthreads();
     if (hf == 0) {
