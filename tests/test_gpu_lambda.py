@@ -110,3 +110,25 @@ def test_lambda_proj_bwd_empty_batch_gives_zero_weight_gradients():
     assert gx.shape == (0, 5, D)
     assert torch.equal(gW.cpu(), torch.zeros(H * L, D)) and torch.equal(gb.cpu(), torch.zeros(H * L))
 
+
+
+def test_lambda_proj_bwd_unaligned_rows_take_the_general_kernels():
+    """bf16 x starting 2 bytes past a 16-byte boundary: the gradient takes the
+    small-tile kernels (the matrix-core path needs 16-byte aligned rows) and
+    still matches the oracle."""
+    B, T, D, H, L = 1, 200, 256, 4, 9
+    w = W.LambdaProjWorkload("lpb_unaligned", B, T, D, H, L, "bf16", True, seed=7)
+    x, Wt, b = W.make_lambda_proj_inputs(w)
+    dlam = torch.from_numpy(np.random.default_rng(8).standard_normal((B, H, T, L)).astype(np.float32))
+    announce("lambda_proj_bwd unaligned x")
+    store = torch.empty(B * T * D + 1, dtype=torch.bfloat16, device="cuda")
+    xu = store[1:].view(B, T, D)  # contiguous, data pointer 2 bytes past the allocation
+    xu.copy_(x.cuda())
+    assert xu.data_ptr() % 16 != 0
+    dW_ = Wt.cuda()
+    lam = torch.from_numpy(oracle.lambda_projection(x, Wt, b, H, L).astype(np.float32)).cuda()
+    gx, gW, gb = ll.lambda_proj_bwd(xu, dW_, lam, dlam.cuda())
+    torch.cuda.synchronize()
+    want = oracle.lambda_projection_grad(x, Wt, b, dlam, H, L)
+    for name, g, ref in zip(("dx", "dW", "dbias"), (gx, gW, gb), want):
+        assert_parity(g.cpu().numpy(), ref, F32_TOL, f"{name} unaligned")
