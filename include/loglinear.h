@@ -14,6 +14,11 @@
  * Common conventions
  *   - Every tensor pointer is a DEVICE pointer to row-major, contiguous memory
  *     owned by the caller.  Nothing is retained after a call returns.
+ *   - q, k, v, lambda, out, the decode states and the gradient buffers of the
+ *     forward, prefill, decode and backward calls must be 16-byte aligned (the
+ *     kernels move them in 16-byte vectors; device allocations are), else
+ *     LL_ERR_SHAPE.  log_a, t and the decode step's log_a / lambda may sit
+ *     anywhere.
  *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = the null stream)
  *     and return once the work is enqueued.  No host/device synchronisation.
  *   - Return value: LL_OK (0) or a negative status; loglinear_strerror() gives

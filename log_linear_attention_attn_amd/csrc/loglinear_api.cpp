@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include "ll_internal.h"
 #include "loglinear.h"
@@ -38,6 +39,14 @@ struct FwdPlan {
 // size, up to 16 chunks, that still gives at least 2048 workgroups.  Depends
 // on shapes only, so the workspace size is known without the dtype.
 constexpr long long kCUs = 256;
+
+// The kernels move q, k, v, out and the level states with 16-byte vector
+// accesses; pointers that are not 16-byte aligned are rejected up front.
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+  return true;
+}
 
 int auto_seg_log2(long long BH, int dk, int dv, int C, int N) {
   const bool rs_shape = C == 64 && dk > 64 && dv % 64 == 0 && N <= 1024;
@@ -145,6 +154,7 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
     if (lds < 0 || lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
   }
   if (workspace && workspace_bytes < p.ws_total) return LL_ERR_WORKSPACE;
+  if (!aligned16({q, k, v, lambda, out, fin ? fin->data : nullptr})) return LL_ERR_SHAPE;
 
   void* ws = workspace;
   bool owned = false;
@@ -218,6 +228,7 @@ int run_decode(int dtype, const loglinear_states* s, const void* q, const void* 
   if ((long long)s->N * s->H > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
   if (s->N == 0 || s->H == 0) return LL_OK;
   if (!s->data || !q || !k || !v || !log_a || !lambda || !t || !out) return LL_ERR_NULL;
+  if (!aligned16({s->data, q, k, v, out})) return LL_ERR_SHAPE;
   ll::DecArgs a{s->data, q, k, v, log_a, lambda, t, out, s->N, s->H, s->L, s->dk, s->dv, G};
   return ll::launch_decode(dtype, a, stream);
 }
@@ -291,6 +302,7 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   if (p.nslot > 16 || p.N > 4096) return LL_ERR_UNSUPPORTED;
   const int lds = ll::bwd_lds_bytes(dtype, C, dk, dv, p.L, p.N, p.nslot);
   if (lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
+  if (!aligned16({q, k, v, lambda, dout, dq, dk_out, dv_out, dlambda})) return LL_ERR_SHAPE;
   const size_t part = align256((size_t)(dk / 16) * p.BH * T * (p.nslot > 0 ? p.nslot : 1) * sizeof(float));
   const size_t dcb = align256((size_t)p.BH * T * sizeof(double));
   // shared q / k: per-head gradients first, then summed over each group

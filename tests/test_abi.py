@@ -226,3 +226,27 @@ def test_lambda_proj_bwd_argument_errors():
     assert L.loglinear_lambda_proj_bwd(p, p, p, p, None, p, p, 1, 4, 16, 2, 3, 0, None) == LL_ERR_NULL
     assert L.loglinear_lambda_proj_bwd(p, None, p, p, p, p, p, 0, 4, 16, 2, 3, 0, None) == LL_ERR_NULL
 
+
+
+def test_misaligned_pointers_are_rejected():
+    """Pointers the kernels access with 16-byte vectors must be 16-byte
+    aligned; any other is LL_ERR_SHAPE, returned on the host before any GPU work."""
+    L = ll.lib()
+    good, bad = ctypes.c_void_p(256), ctypes.c_void_p(258)
+    # forward: q, ..., out (one misaligned at a time); log_a may be anywhere
+    fwd_args = [good] * 6
+    for i in (0, 1, 2, 4, 5):
+        a = list(fwd_args)
+        a[i] = bad
+        assert L.loglinear_fwd(*a, 1, 1, 64, 16, 16, 16, None) == LL_ERR_SHAPE, i
+    # backward: q, k, v, log_a, lambda, out, dout, grads
+    bwd_args = [good] * 12
+    for i in (0, 2, 6, 7, 9, 11):
+        a = list(bwd_args)
+        a[i] = bad
+        assert L.loglinear_bwd(*a, 1, 1, 64, 16, 16, 16, None) == LL_ERR_SHAPE, i
+    # decode: the state buffer and q
+    desc = ll._States(258, 1, 1, 4, 16, 16)
+    assert L.loglinear_decode_step(ctypes.byref(desc), good, good, good, good, good, good, good, None) == LL_ERR_SHAPE
+    desc = ll._States(256, 1, 1, 4, 16, 16)
+    assert L.loglinear_decode_step(ctypes.byref(desc), bad, good, good, good, good, good, good, None) == LL_ERR_SHAPE
