@@ -313,6 +313,82 @@ def backward(q, k, v, log_a, lam, dout):
     return tuple(grads)
 
 
+def _levels_seen_from(s: int, t_end: int) -> np.ndarray:
+    """Levels of key s as seen from every query t = s .. t_end-1.
+
+    The bucket walk of ``fenwick_buckets`` run for all those queries at once:
+    start at end = t, cut off the bucket (end - low, end] of the lowest set bit
+    low of end, and stop at the bucket that holds s.  Level 0 where t == s.
+    """
+    t = np.arange(s, t_end, dtype=np.int64)
+    lev = np.zeros(t.shape, dtype=np.int64)
+    end = t.copy()
+    todo = t != s
+    while np.any(todo):
+        low = end & -end
+        hit = todo & (end - low <= s) & (s < end)
+        lev[hit] = np.log2(low[hit]).astype(np.int64) + 1  # low = 2^(level-1)
+        todo &= ~hit
+        end = np.where(todo, end - low, end)
+    return lev
+
+
+def backward_rows(q, k, v, log_a, lam, dout, bh: tuple[int, int], rows):
+    """dq and dlam at selected query rows of one (b, h), by the chain rule
+    written out on the dense definition o_t = sum_{s<=t} M[t,s] (q_t.k_s) v_s,
+    M[t,s] = lam[t, level(t,s)] exp(cum[t] - cum[s]):
+
+        dq_t        = sum_{s<=t} M[t,s] (dO_t . v_s) k_s
+        dlam[t, l]  = sum over the level-l bucket of t of
+                      exp(cum[t] - cum[s]) (q_t . k_s) (dO_t . v_s)
+
+    For spot checks where the full autograd backward is too large.
+    Returns (dq [n, dk], dlam [n, L]) float64."""
+    b, h = bh
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+    la, lm, do = _f64(log_a[b, h]), _f64(lam[b, h]), _f64(dout[b, h])
+    cum = np.cumsum(la)
+    L = lm.shape[-1]
+    dq, dl = [], []
+    for t in rows:
+        t = int(t)
+        g = np.zeros(L)
+        dqt = np.zeros(qh.shape[-1])
+        for level, lo, hi in fenwick_buckets(t):
+            d = np.exp(cum[t] - cum[lo:hi])
+            a = kh[lo:hi] @ qh[t]          # q_t . k_s
+            c = vh[lo:hi] @ do[t]          # dO_t . v_s
+            g[level] = np.sum(d * a * c)
+            dqt += (lm[t, level] * d * c) @ kh[lo:hi]
+        dq.append(dqt)
+        dl.append(g)
+    return np.array(dq).reshape(-1, qh.shape[-1]), np.array(dl).reshape(-1, L)
+
+
+def backward_cols(q, k, v, log_a, lam, dout, bh: tuple[int, int], cols):
+    """dk and dv at selected key positions of one (b, h), by the chain rule on
+    the dense definition (see ``backward_rows``):
+
+        dk_s = sum_{t>=s} M[t,s] (dO_t . v_s) q_t
+        dv_s = sum_{t>=s} M[t,s] (q_t . k_s) dO_t
+
+    Returns (dk [n, dk], dv [n, dv]) float64."""
+    b, h = bh
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+    la, lm, do = _f64(log_a[b, h]), _f64(lam[b, h]), _f64(dout[b, h])
+    T = qh.shape[0]
+    cum = np.cumsum(la)
+    dk, dv = [], []
+    for s in cols:
+        s = int(s)
+        lev = _levels_seen_from(s, T)
+        ts = np.arange(s, T)
+        m = lm[ts, lev] * np.exp(cum[s:] - cum[s])
+        dk.append((m * (do[s:] @ vh[s])) @ qh[s:])
+        dv.append((m * (qh[s:] @ kh[s])) @ do[s:])
+    return np.array(dk).reshape(-1, kh.shape[-1]), np.array(dv).reshape(-1, vh.shape[-1])
+
+
 # --------------------------------------------------------------------------
 # q and k shared by groups of heads (multi-value attention, MVA)
 # --------------------------------------------------------------------------

@@ -579,3 +579,92 @@ def test_lambda_projection_grad_sigmoid_limits():
     for z, want in ((40.0, 2.0), (-40.0, 2.0 * math.exp(-40.0))):
         _, _, db = oracle.lambda_projection_grad(x, np.zeros((1, 1)), np.array([z]), dlam, 1, 1)
         assert db[0] == pytest.approx(want, rel=1e-12)
+
+
+# ---------------------------------------------------- level_of and sampled backward
+
+def test_level_of_matches_page_table_and_partition():
+    """level_of (one pair at a time) against the printed 8x8 table ([P1] 并行形式),
+    the t = 7 partition ([P1] 前缀的层次化分解; [P5] slides 19-20), and the
+    closed form bit_length(t xor s) for every pair s <= t < 64; s > t is refused."""
+    rows = []
+    with open(os.path.join(GOLDEN, "level_table_8x8.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            rows.append([-1 if x == "-" else int(x) for x in line.split()])
+    for t in range(8):
+        for s in range(t + 1):
+            assert oracle.level_of(t, s) == rows[t][s], (t, s)
+    with open(os.path.join(GOLDEN, "t7_partition.json")) as f:
+        g = json.load(f)
+    for lev, members in g["buckets"].items():
+        for s in members:
+            assert oracle.level_of(g["t"], s) == int(lev)
+    for t in range(64):
+        for s in range(t + 1):
+            assert oracle.level_of(t, s) == (0 if s == t else int(t ^ s).bit_length())
+    with pytest.raises(ValueError):
+        oracle.level_of(3, 4)
+
+
+def test_levels_seen_from_key_match_level_matrix():
+    """The column-wise bucket walk used by backward_cols against the row-wise
+    level matrix, every key s < 300."""
+    T = 300
+    lv = oracle.level_matrix(T)
+    for s in range(T):
+        assert np.array_equal(O._levels_seen_from(s, T), lv[s:, s]), s
+
+
+@pytest.mark.parametrize("seed,T,decay", [(21, 37, 0.4), (22, 70, 0.0), (23, 64, 1.5)])
+def test_sampled_backward_matches_autograd(seed, T, decay):
+    """backward_rows / backward_cols (chain rule written out per row / column)
+    against the fp64 autograd backward of the dense definition, every row and
+    every column of a few (b, h)."""
+    rng = np.random.default_rng(seed)
+    q, k, v, la, lam = _rand_inputs(rng, 2, 2, T, 5, 3, decay=decay)
+    dout = rng.standard_normal((2, 2, T, 3))
+    dq, dk_, dv_, _, dlam = oracle.backward(q, k, v, la, lam, dout)
+    idx = list(range(T))
+    for bh in [(0, 1), (1, 0)]:
+        gq, gl = oracle.backward_rows(q, k, v, la, lam, dout, bh, idx)
+        gk, gv = oracle.backward_cols(q, k, v, la, lam, dout, bh, idx)
+        np.testing.assert_allclose(gq, dq[bh], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(gl, dlam[bh], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(gk, dk_[bh], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(gv, dv_[bh], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("mistake", ["dq_no_lambda", "dk_wrong_side", "dv_untransposed_decay"])
+def test_sampled_backward_planted_mistakes_are_caught(mistake):
+    """A dropped lambda, a q/k side swap or a decay taken the wrong way in the
+    sampled formulas must fail the autograd comparison above."""
+    rng = np.random.default_rng(31)
+    T = 40
+    q, k, v, la, lam = _rand_inputs(rng, 1, 1, T, 4, 3, decay=0.4)
+    dout = rng.standard_normal((1, 1, T, 3))
+    dq, dk_, dv_, _, _ = oracle.backward(q, k, v, la, lam, dout)
+    Q, K, V, dO = q[0, 0], k[0, 0], v[0, 0], dout[0, 0]
+    cum = np.cumsum(la[0, 0])
+    lv = oracle.level_matrix(T)
+    t, s = 29, 11
+    if mistake == "dq_no_lambda":
+        ss = np.arange(t + 1)
+        bad = (np.exp(cum[t] - cum[ss]) * (V[ss] @ dO[t])) @ K[ss]
+        assert not np.allclose(bad, dq[0, 0, t], rtol=1e-6)
+    elif mistake == "dk_wrong_side":
+        ts = np.arange(s, T)
+        m = lam[0, 0, ts, lv[ts, s]] * np.exp(cum[ts] - cum[s])
+        bad = (m * (dO[ts] @ V[s])) @ K[ts]
+        assert not np.allclose(bad, dk_[0, 0, s], rtol=1e-6)
+    else:
+        ts = np.arange(s, T)
+        m = lam[0, 0, ts, lv[ts, s]] * np.exp(cum[s] - cum[ts])
+        bad = (m * (Q[ts] @ K[s])) @ dO[ts]
+        assert not np.allclose(bad, dv_[0, 0, s], rtol=1e-6)
+    gq, _ = oracle.backward_rows(q, k, v, la, lam, dout, (0, 0), [t])
+    gk, gv = oracle.backward_cols(q, k, v, la, lam, dout, (0, 0), [s])
+    np.testing.assert_allclose(gq[0], dq[0, 0, t], rtol=1e-10)
+    np.testing.assert_allclose(gk[0], dk_[0, 0, s], rtol=1e-10)
+    np.testing.assert_allclose(gv[0], dv_[0, 0, s], rtol=1e-10)
