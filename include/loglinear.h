@@ -14,11 +14,11 @@
  * Common conventions
  *   - Every tensor pointer is a DEVICE pointer to row-major, contiguous memory
  *     owned by the caller.  Nothing is retained after a call returns.
- *   - q, k, v, lambda, out, the decode states and the gradient buffers of the
- *     forward, prefill, decode and backward calls must be 16-byte aligned (the
- *     kernels move them in 16-byte vectors; device allocations are), else
- *     LL_ERR_SHAPE.  log_a, t and the decode step's log_a / lambda may sit
- *     anywhere.
+ *   - q, k, v, lambda, out and the gradient buffers of the forward, prefill
+ *     and backward calls, and the decode step's states and out, must be
+ *     16-byte aligned (the kernels move them in 16-byte vectors; device
+ *     allocations are), else LL_ERR_SHAPE.  log_a, t and the decode step's
+ *     q, k, v, log_a and lambda (read one element at a time) may sit anywhere.
  *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = the null stream)
  *     and return once the work is enqueued.  No host/device synchronisation.
  *   - Return value: LL_OK (0) or a negative status; loglinear_strerror() gives
@@ -112,8 +112,8 @@ typedef struct {
  *                  apply to the sizes returns LL_ERR_UNSUPPORTED.
  *   workspace    : NULL = allocate stream-ordered on `stream`; otherwise a
  *                  device buffer of at least loglinear_fwd_workspace_size()
- *                  bytes, 256-byte aligned, owned by the caller, not used by
- *                  any concurrent call.
+ *                  bytes, 256-byte aligned (else LL_ERR_WORKSPACE), owned by
+ *                  the caller, not used by any concurrent call.
  *   workspace_bytes : size of `workspace`.
  *   phase_events : NULL, or 4 caller-created hipEvent_t recorded on `stream`
  *                  before the segment-state kernel, before the node kernel,
@@ -177,9 +177,10 @@ int loglinear_prefill_f32(const float* q, const float* k, const float* v, const 
  * loglinear_fwd (page above, sections 并行形式 and 与已有模型的组合 define the
  * operator being differentiated; 训练：分块并行扫描算法 the chunking reused here).
  *   q, k, v, log_a, lambda : the forward's inputs (bf16 q, k, v)
- *   out    : [B, H, T, dv] fp32, the forward's output for these inputs (kept in
- *            the signature; the gradients do not read it: d log_a takes
- *            dO_t . O_t as sum_l lambda[t,l] grad_lambda[t,l], the same sum)
+ *   out    : [B, H, T, dv] fp32, the forward's output for these inputs, or
+ *            NULL: the gradients do not read it (d log_a takes dO_t . O_t as
+ *            sum_l lambda[t,l] grad_lambda[t,l], the same sum); kept in the
+ *            signature so a caller may pass what it has
  *   dout   : [B, H, T, dv] fp32, gradient with respect to out
  *   grad_q, grad_k : [B, H, T, dk] fp32;  grad_v : [B, H, T, dv] fp32
  *   grad_log_a : [B, H, T] fp32;  grad_lambda : [B, H, T, L] fp32

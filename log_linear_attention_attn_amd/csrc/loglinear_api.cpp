@@ -154,6 +154,9 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
     if (lds < 0 || lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
   }
   if (workspace && workspace_bytes < p.ws_total) return LL_ERR_WORKSPACE;
+  // the node states are read from the workspace as 16-byte vectors; the
+  // header promises 256-byte alignment, which is what is checked
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255)) return LL_ERR_WORKSPACE;
   if (!aligned16({q, k, v, lambda, out, fin ? fin->data : nullptr})) return LL_ERR_SHAPE;
 
   void* ws = workspace;
@@ -228,7 +231,8 @@ int run_decode(int dtype, const loglinear_states* s, const void* q, const void* 
   if ((long long)s->N * s->H > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
   if (s->N == 0 || s->H == 0) return LL_OK;
   if (!s->data || !q || !k || !v || !log_a || !lambda || !t || !out) return LL_ERR_NULL;
-  if (!aligned16({s->data, q, k, v, out})) return LL_ERR_SHAPE;
+  // states and out move as 16-byte vectors; q, k, v are read one element at a time
+  if (!aligned16({s->data, out})) return LL_ERR_SHAPE;
   ll::DecArgs a{s->data, q, k, v, log_a, lambda, t, out, s->N, s->H, s->L, s->dk, s->dv, G};
   return ll::launch_decode(dtype, a, stream);
 }
@@ -296,8 +300,9 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   const int G = heads_per_qk(H, qk_heads);
   if (G < 1) return LL_ERR_SHAPE;
   if (B == 0 || H == 0 || T == 0) return LL_OK;
-  if (!q || !k || !v || !log_a || !lambda || !out || !dout || !dq || !dk_out || !dv_out || !dlog_a ||
-      !dlambda)
+  // `out` is not read (d log_a takes dO_t . O_t as sum_l lambda dlambda), so it may be NULL
+  (void)out;
+  if (!q || !k || !v || !log_a || !lambda || !dout || !dq || !dk_out || !dv_out || !dlog_a || !dlambda)
     return LL_ERR_NULL;
   if (p.nslot > 16 || p.N > 4096) return LL_ERR_UNSUPPORTED;
   const int lds = ll::bwd_lds_bytes(dtype, C, dk, dv, p.L, p.N, p.nslot);
@@ -447,7 +452,7 @@ const char* loglinear_strerror(int status) {
     case LL_ERR_SHAPE: return "a size is negative, inconsistent or out of range";
     case LL_ERR_UNSUPPORTED: return "sizes are valid but no kernel of this build supports them";
     case LL_ERR_HIP: return "a HIP runtime call failed";
-    case LL_ERR_WORKSPACE: return "workspace too small";
+    case LL_ERR_WORKSPACE: return "workspace too small or misaligned";
     default: return "unknown status";
   }
 }

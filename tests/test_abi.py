@@ -245,8 +245,12 @@ def test_misaligned_pointers_are_rejected():
         a = list(bwd_args)
         a[i] = bad
         assert L.loglinear_bwd(*a, 1, 1, 64, 16, 16, 16, None) == LL_ERR_SHAPE, i
-    # decode: the state buffer and q
+    # decode: the state buffer and out (q, k, v are read one element at a time)
     desc = ll._States(258, 1, 1, 4, 16, 16)
     assert L.loglinear_decode_step(ctypes.byref(desc), good, good, good, good, good, good, good, None) == LL_ERR_SHAPE
     desc = ll._States(256, 1, 1, 4, 16, 16)
-    assert L.loglinear_decode_step(ctypes.byref(desc), bad, good, good, good, good, good, good, None) == LL_ERR_SHAPE
+    assert L.loglinear_decode_step(ctypes.byref(desc), good, good, good, good, good, good, bad, None) == LL_ERR_SHAPE
+    # a caller workspace must be 256-byte aligned
+    opts = ll._FwdOpts(ll.LL_BF16, 2, 0, ctypes.c_void_p(256 + 16), 1 << 30, None, None, 0)
+    assert L.loglinear_fwd_ex(*fwd_args, 1, 1, 4096, 128, 64, 64, ctypes.byref(opts), None) == -5
+

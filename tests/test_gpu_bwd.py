@@ -36,6 +36,7 @@ CASES = [
     (1, 2, 700, 128, 128, 64, "bf16", "strong"), # strong decay: heavy-tailed gradients
     (1, 1, 3000, 128, 64, 64, "bf16", "weak"),   # 47 chunks, six chunk-level bits, ragged
     (1, 2, 500, 32, 96, 64, "bf16", "strong"),   # contraction widths 32 and 96 on the bf16 kernels
+    (1, 1, 4200, 128, 128, 64, "bf16", "weak"),  # 66 chunks: chunk-level bits 0-6, ragged
 ]
 
 
@@ -88,3 +89,32 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("decay", ["none", "weak"])
+def test_bwd_256_chunks_sampled(decay):
+    """T=16384, C=64: 256 chunks, so the bf16 sweeps run chunk-level bits 0-7
+    (the bench's backward shape per head).  dq and dlambda on sampled query
+    rows and dk, dv on sampled key columns against the oracle's per-row /
+    per-column chain rule; no or weak decay so every level carries weight."""
+    B, H, T = 1, 2, 16384
+    w = W.FwdWorkload("bwd256", B, H, T, 128, 128, 64, "bf16", decay=decay, seed=7)
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    dout = torch.from_numpy(np.random.default_rng(8).standard_normal((B, H, T, 128)).astype(np.float32))
+    announce(f"bwd 256 chunks sampled {decay}")
+    dev = to_dev(q, k, v, la, lam)
+    out = ll.fwd(*dev, C=64)
+    grads = [g.cpu().numpy() for g in ll.bwd(*dev, out, dout.cuda(), C=64)]
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    fixed = []
+    for n in (1, 2, 4, 8, 16, 32, 64, 96, 128, 129, 192, 255):
+        fixed += [n * 64 - 1, n * 64]
+    idx = sorted(set(fixed) | set(rng.integers(0, T, 24).tolist()))
+    for bh in [(0, 0), (0, 1)]:
+        dq, dlam = oracle.backward_rows(q, k, v, la, lam, dout, bh, idx)
+        dk_, dv_ = oracle.backward_cols(q, k, v, la, lam, dout, bh, idx)
+        assert_parity(grads[0][bh][idx], dq, BF16_TOL, f"dq rows {decay} {bh}")
+        assert_parity(grads[4][bh][idx], dlam, BF16_TOL, f"dlam rows {decay} {bh}")
+        assert_parity(grads[1][bh][idx], dk_, BF16_TOL, f"dk cols {decay} {bh}")
+        assert_parity(grads[2][bh][idx], dv_, BF16_TOL, f"dv cols {decay} {bh}")

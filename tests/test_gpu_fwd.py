@@ -125,17 +125,27 @@ def test_weak_decay_coverage(base, decay):
     if w.T <= 4096:
         assert_parity(got, oracle.forward(*inp), BF16_TOL, w.name)
     else:
-        rows = _sample_rows(w.T, w.C, 48, seed=3)
+        rows = _sample_rows(w.T, w.C, 48, seed=3, seg_chunks=64)
         for bh in [(0, 0), (0, 1)]:
             want = oracle.forward_rows(*inp, bh, rows)
             assert_parity(got[bh[0], bh[1], rows], want, BF16_TOL, f"{w.name} {bh}")
 
 
-def _sample_rows(T, C, n, seed):
+def _sample_rows(T, C, n, seed, seg_chunks=16):
+    """Random rows plus fixed ones: the ends of the sequence and of its first
+    chunk, every segment boundary of a plan with seg_chunks chunks per segment
+    (first row of each segment and the rows either side of it), and the first
+    rows of chunks n whose lowest set bit is 4..7 (the chunks that read a
+    freshly merged deep bucket state) with the last row before each."""
     rng = np.random.default_rng(seed)
     fixed = [0, 1, C - 1, C, T // 2, T // 2 - 1, T - C, T - 2, T - 1]
-    seg = 16 * C
-    fixed += [x for x in (seg - 1, seg, 3 * seg + 5) if x < T]
+    seg = seg_chunks * C
+    for x in range(seg, T, seg):
+        fixed += [x - 1, x, x + 1]
+    N = (T + C - 1) // C
+    deep = [n for n in range(1, N) if 4 <= (n & -n).bit_length() - 1 <= 7]
+    for n in deep[:24]:
+        fixed += [n * C - 1, n * C, n * C + 37]
     rows = sorted(set(fixed) | set(rng.integers(0, T, n).tolist()))
     return [r for r in rows if 0 <= r < T]
 
@@ -152,7 +162,7 @@ def test_full_size_sampled_rows(w):
     assert np.all(np.isfinite(got))
     rng = np.random.default_rng(0)
     pairs = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(2)]
-    rows = _sample_rows(w.T, w.C, 40, seed=1)
+    rows = _sample_rows(w.T, w.C, 40, seed=1, seg_chunks=64 if w.T <= 16384 else 128)
     for bh in pairs[: 4 if w.T <= 16384 else 2]:
         want = oracle.forward_rows(q, k, v, la, lam, bh, rows)
         assert_parity(got[bh[0], bh[1], rows], want, BF16_TOL, f"{w.name} {bh}")
@@ -214,3 +224,49 @@ def test_register_state_kernel_rejects_other_shapes():
     dq, dk_, dv_, dla, dlam = to_dev(*W.make_fwd_inputs(w))
     with pytest.raises(ll.LogLinearError):
         ll.fwd_ex(dq, dk_, dv_, dla, dlam, C=64, kernel=ll.KERNEL_REGISTER_STATE)
+
+
+# ------------------------------------------------ the bench's launch plans, deep merges weighted
+
+DEEP = [
+    # (B, H, T, decay, seg_log2): seg_log2 6 is the plan at B=2 H=16 T=16384;
+    # 7 with more than 256 chunks is the ten-slot plan of B=1 H=16 T=65536
+    (1, 1, 16384, "none", 6),
+    (1, 2, 16384, "weak", 6),
+    (1, 1, 20000, "none", 7),
+    (1, 1, 65536, "weak", 7),
+]
+
+
+@pytest.mark.parametrize("case", DEEP, ids=lambda c: "B{}H{}T{}_{}_s{}".format(*c))
+def test_register_state_deep_merges(case):
+    """Register-state sweep at the segment sizes the bench's plans use, with no
+    or weak decay so the in-register merges at lssb 4..7 and the segment-
+    spanning node states all carry weight; sampled rows include every
+    segment boundary and the chunks that read a freshly merged deep state."""
+    B, H, T, decay, s = case
+    w = W.FwdWorkload("deep", B, H, T, 128, 128, 64, "bf16", decay=decay, seed=T + s)
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    announce(f"register-state deep merges {case}")
+    out = ll.fwd_ex(*to_dev(q, k, v, la, lam), C=64, seg_log2=s, kernel=ll.KERNEL_REGISTER_STATE)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rows = _sample_rows(T, 64, 48, seed=5, seg_chunks=1 << s)
+    for bh in [(b, h) for b in range(B) for h in range(H)]:
+        want = oracle.forward_rows(q, k, v, la, lam, bh, rows)
+        assert_parity(got[bh[0], bh[1], rows], want, BF16_TOL, f"deep {case} {bh}")
+
+
+def test_bench_shape_weak_decay_auto_plan():
+    """B=2, H=16, T=16384 (the bench's shape and automatic plan) with weak
+    decay, on sampled rows of two (b, h) pairs."""
+    w = dataclasses.replace(W.LM_T16K, name="lm_weak", decay="weak")
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    announce("bench shape, weak decay, automatic plan")
+    out = ll.fwd(*to_dev(q, k, v, la, lam), C=64)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rows = _sample_rows(w.T, w.C, 40, seed=7, seg_chunks=64)
+    for bh in [(0, 3), (1, 15)]:
+        want = oracle.forward_rows(q, k, v, la, lam, bh, rows)
+        assert_parity(got[bh[0], bh[1], rows], want, BF16_TOL, f"lm weak auto {bh}")

@@ -95,3 +95,20 @@ def test_decode_continues_from_prefill(dtype, T, C):
         assert_parity(o.cpu().numpy(), want[:, :, t], tol, f"decode t={t} after prefill {T}")
     torch.cuda.synchronize()
     assert_parity(out.cpu().numpy(), want[:, :, :T], tol, f"prefill out T={T}")
+
+
+@pytest.mark.parametrize("T,decay,s", [(16384, "none", 6), (20000, "weak", 7)])
+def test_prefill_states_at_bench_plans(T, decay, s):
+    """Prefill states at the bench's segment sizes (64-chunk segments at
+    T=16384, the ten-slot kernel with 128-chunk segments beyond 256 chunks),
+    with no or weak decay so every inter-chunk level carries weight."""
+    w = W.FwdWorkload("prefill_deep", 1, 1, T, 128, 128, 64, "bf16", decay=decay, seed=T)
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    Ls = W.num_levels(T)
+    announce(f"prefill at bench plan T={T} s={s}")
+    states = torch.full((1, 1, Ls, 128, 128), float("nan"), device="cuda")
+    ll.fwd_ex(*to_dev(q, k, v, la, lam), C=64, seg_log2=s, kernel=ll.KERNEL_REGISTER_STATE,
+              final_states=states)
+    torch.cuda.synchronize()
+    want = oracle.states_at(k, v, la, T - 1, Ls)
+    assert_parity(states.cpu().numpy(), want, BF16_TOL, f"states T={T} s={s}")
