@@ -275,6 +275,31 @@ int loglinear_lambda_proj_bwd(const void* x, const void* W, const float* lambda,
 size_t loglinear_fwd_workspace_size(int B, int H, int T, int dk, int dv, int C, int seg_log2);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, arithmetic and result as loglinear_fwd (bf16
+ * q, k, v; the same kernels and launch plan, so the output is bitwise equal),
+ * but the workspace lives in a static device array of
+ * LOGLINEAR_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends, and the call allocates and frees nothing.
+ *   - Sizes whose workspace (loglinear_fwd_workspace_size with seg_log2 = -1)
+ *     exceeds LOGLINEAR_NOALLOC_SCRATCH_BYTES give LL_ERR_WORKSPACE, checked on
+ *     the host before any HIP call.  The automatic plans at dk = dv = 128
+ *     need at most ~37 MiB (B=2, H=16, T=16384: 34 MiB; B=1, H=16, T=65536:
+ *     37 MiB); wide dv with small C can need more.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on a
+ *     GPU (other streams, other host threads) race and must be serialised by
+ *     the caller; calls on one stream are ordered and safe.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress) with that device current; a failure is LL_ERR_HIP.
+ * Other errors as loglinear_fwd.
+ */
+#define LOGLINEAR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int loglinear_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_a,
+                          const float* lambda, float* out, int B, int H, int T, int dk, int dv,
+                          int C, void* stream);
+
+/*
  * One O(log T) decode step for N sequences x H heads (page above, section
  * 解码：基于 lssb 的状态更新; slide 21 of "論文紹介：Log Linear Attention").
  *   states : on entry S_{t-1} of every (sequence, head), levels dead at t-1

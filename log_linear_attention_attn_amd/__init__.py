@@ -38,8 +38,12 @@ EXPORTED_SYMBOLS = (
     "loglinear_bwd_ex", "loglinear_fwd_workspace_size",
     "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_decode_step_ex",
     "loglinear_level_table", "loglinear_lambda_proj", "loglinear_lambda_proj_bwd",
-    "loglinear_strerror",
+    "loglinear_strerror", "loglinear_fwd_noalloc",
 )
+
+# bytes of the static scratch behind loglinear_fwd_noalloc (the header's
+# LOGLINEAR_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LogLinearError(RuntimeError):
@@ -84,6 +88,8 @@ def lib():
     L.loglinear_fwd_f32.restype = i
     L.loglinear_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(_FwdOpts), vp]
     L.loglinear_fwd_ex.restype = i
+    L.loglinear_fwd_noalloc.argtypes = fwd_args + [vp]
+    L.loglinear_fwd_noalloc.restype = i
     pre_args = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(_States), i, i, i, i, i, i, vp]
     L.loglinear_prefill.argtypes = pre_args
     L.loglinear_prefill.restype = i
@@ -253,6 +259,33 @@ def fwd(q, k, v, log_a, lam, C: int = 64, out=None):
     st = f(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out), B, H, T, dk, dv, int(C),
            _stream(dev))
     _raise(st, "loglinear_fwd")
+    return out
+
+
+def fwd_noalloc(q, k, v, log_a, lam, C: int = 64, out=None):
+    """loglinear_fwd_noalloc: the bf16 forward with its workspace in the
+    library's static device scratch (no allocation inside the call; calls that
+    overlap on one GPU race).  Same result as fwd.  `out` is allocated here
+    unless given, so a caller that must not allocate passes it."""
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T) if T > 0 else 0
+    _check_dev("q", q, q.dtype, (B, H, T, dk), dev)
+    _check_dev("k", k, q.dtype, (B, H, T, dk), dev)
+    _check_dev("v", v, q.dtype, (B, H, T, dv), dev)
+    _check_dev("log_a", log_a, torch.float32, (B, H, T), dev)
+    _check_dev("lam", lam, torch.float32, (B, H, T, L), dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (B, H, T, dv), dev)
+    st = lib().loglinear_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(lam), _ptr(out),
+                                     B, H, T, dk, dv, int(C), _stream(dev))
+    _raise(st, "loglinear_fwd_noalloc")
     return out
 
 

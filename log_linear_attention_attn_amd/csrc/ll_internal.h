@@ -130,6 +130,18 @@ struct GemmArgs {
   int M, N, K, kper, nb_real, ones;
 };
 
+// A workspace of fixed size that is not allocated per call: max_bytes bounds
+// it, get() returns its device address (null on a HIP error) and is called
+// only after every argument has been checked.
+struct ScratchProvider {
+  size_t max_bytes;
+  void* (*get)();
+};
+// loglinear_fwd with the workspace taken from `provider` (no allocation).
+int fwd_bf16_with_scratch(const void* q, const void* k, const void* v, const float* log_a,
+                          const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
+                          const ScratchProvider& provider, hipStream_t stream);
+
 int sweep_lds_bytes(int dtype, int C, int DKP, int L, int nslot);
 int launch_sweep(int dtype, int C, int DKP, const FwdArgs& a, int nblocks, hipStream_t s);
 int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStream_t s);

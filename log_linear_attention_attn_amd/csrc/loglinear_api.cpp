@@ -127,7 +127,8 @@ int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* 
 int run_fwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
             const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
             int seg_log2, int kernel, void* workspace, size_t workspace_bytes,
-            void* const* events, const loglinear_states* fin, int qk_heads, hipStream_t stream) {
+            void* const* events, const loglinear_states* fin, int qk_heads, hipStream_t stream,
+            const ll::ScratchProvider* provider = nullptr) {
   FwdPlan p;
   int st = plan_fwd(B, H, T, dk, dv, C, seg_log2, &p);
   if (st != LL_OK) return st;
@@ -153,6 +154,9 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
     const int lds = ll::sweep_lds_bytes(dtype, C, p.DKP, p.L, p.nslot);
     if (lds < 0 || lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
   }
+  // a fixed-size scratch (allocation-free entry point): reject sizes beyond it
+  // before any HIP call
+  if (provider && p.ws_total > provider->max_bytes) return LL_ERR_WORKSPACE;
   if (workspace && workspace_bytes < p.ws_total) return LL_ERR_WORKSPACE;
   // the node states are read from the workspace as 16-byte vectors; the
   // header promises 256-byte alignment, which is what is checked
@@ -161,6 +165,11 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
 
   void* ws = workspace;
   bool owned = false;
+  if (p.ws_total > 0 && provider) {
+    // every argument is checked: now the scratch's device address
+    ws = provider->get();
+    if (!ws) return LL_ERR_HIP;
+  }
   if (p.ws_total > 0 && !ws) {
     if (hipMallocAsync(&ws, p.ws_total, stream) != hipSuccess) return LL_ERR_HIP;
     owned = true;
@@ -332,6 +341,15 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
 
 }  // namespace
 
+namespace ll {
+int fwd_bf16_with_scratch(const void* q, const void* k, const void* v, const float* log_a,
+                          const float* lambda, float* out, int B, int H, int T, int dk, int dv, int C,
+                          const ScratchProvider& provider, hipStream_t stream) {
+  return run_fwd(LL_BF16, q, k, v, log_a, lambda, out, B, H, T, dk, dv, C, -1, LL_KERNEL_AUTO, nullptr, 0,
+                 nullptr, nullptr, 0, stream, &provider);
+}
+}  // namespace ll
+
 extern "C" {
 
 int loglinear_num_levels(int T) { return T >= 1 ? bit_length(T - 1) + 1 : 0; }
@@ -452,7 +470,9 @@ const char* loglinear_strerror(int status) {
     case LL_ERR_SHAPE: return "a size is negative, inconsistent or out of range";
     case LL_ERR_UNSUPPORTED: return "sizes are valid but no kernel of this build supports them";
     case LL_ERR_HIP: return "a HIP runtime call failed";
-    case LL_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case LL_ERR_WORKSPACE:
+      return "workspace too small or misaligned (caller workspace, or the static scratch of "
+             "loglinear_fwd_noalloc)";
     default: return "unknown status";
   }
 }

@@ -254,3 +254,20 @@ def test_misaligned_pointers_are_rejected():
     opts = ll._FwdOpts(ll.LL_BF16, 2, 0, ctypes.c_void_p(256 + 16), 1 << 30, None, None, 0)
     assert L.loglinear_fwd_ex(*fwd_args, 1, 1, 4096, 128, 64, 64, ctypes.byref(opts), None) == -5
 
+
+def test_fwd_noalloc_rejects_sizes_beyond_its_scratch():
+    """loglinear_fwd_noalloc checks its workspace against the static scratch
+    on the host, before any HIP call: a plan that needs more is
+    LL_ERR_WORKSPACE, argument errors are reported as for loglinear_fwd."""
+    L = ll.lib()
+    p = ctypes.c_void_p(256)
+    fn = L.loglinear_fwd_noalloc
+    # B=H=1, T=65536, dk=128, dv=1024, C=16: the automatic plan needs 256 MiB
+    assert ll.fwd_workspace_size(1, 1, 65536, 128, 1024, 16, -1) > ll.NOALLOC_SCRATCH_BYTES
+    assert fn(p, p, p, p, p, p, 1, 1, 65536, 128, 1024, 16, None) == LL_ERR_WORKSPACE
+    # the bench shapes fit
+    assert ll.fwd_workspace_size(2, 16, 16384, 128, 128, 64, -1) <= ll.NOALLOC_SCRATCH_BYTES
+    assert ll.fwd_workspace_size(1, 16, 65536, 128, 128, 64, -1) <= ll.NOALLOC_SCRATCH_BYTES
+    assert fn(p, p, p, p, p, p, 1, 1, 64, 16, 16, 48, None) == LL_ERR_SHAPE
+    assert fn(None, p, p, p, p, p, 1, 1, 64, 16, 16, 16, None) == LL_ERR_NULL
+    assert fn(p, p, p, p, p, p, 0, 1, 64, 16, 16, 16, None) == LL_OK
