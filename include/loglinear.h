@@ -53,9 +53,12 @@ enum loglinear_dtype { LL_BF16 = 0, LL_F32 = 1 };
 enum loglinear_kernel {
   LL_KERNEL_AUTO = 0,           /* register-state kernel where it applies, else LDS-state */
   LL_KERNEL_LDS_STATE = 1,      /* bucket states in LDS, 16 dv columns per workgroup; all shapes */
-  LL_KERNEL_REGISTER_STATE = 2  /* bucket states in registers, 64 dv columns per workgroup;
+  LL_KERNEL_REGISTER_STATE = 2, /* bucket states in registers, 64 dv columns per workgroup;
                                    bf16, C = 64, 64 < dk <= 128, dv % 64 == 0,
-                                   ceil(T / 64) <= 256 */
+                                   ceil(T / 64) <= 1024 */
+  LL_KERNEL_WIDE = 3            /* bucket states in registers, all dv columns of a segment in
+                                   one workgroup, each wave over the whole of dk; bf16,
+                                   C = 64, 64 < dk <= 128, dv = 128, ceil(T / 64) <= 256 */
 };
 
 /* Number of lambda levels for sequence length T >= 1: bit_length(T-1) + 1

@@ -178,7 +178,7 @@ def fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1) -> int:
     return int(n)
 
 
-KERNEL_AUTO, KERNEL_LDS_STATE, KERNEL_REGISTER_STATE = 0, 1, 2
+KERNEL_AUTO, KERNEL_LDS_STATE, KERNEL_REGISTER_STATE, KERNEL_WIDE = 0, 1, 2, 3
 
 
 def fwd_ex(q, k, v, log_a, lam, C: int = 64, out=None, seg_log2: int = -1, workspace=None,

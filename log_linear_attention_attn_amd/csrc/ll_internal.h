@@ -3,6 +3,9 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
+
+#include <atomic>
 
 #include "loglinear.h"
 
@@ -10,6 +13,19 @@ namespace ll {
 
 // Largest dynamic LDS allocation of one workgroup on gfx950 (160 KiB per CU).
 constexpr int kMaxLds = 160 * 1024;
+
+// Raises a kernel's dynamic LDS limit (default kMaxLds, less for kernels
+// with static LDS) once per (kernel, device): `done` is the kernel's own bit
+// set of devices already raised.
+inline bool raise_lds_limit(const void* fn, std::atomic<uint64_t>& done, int bytes = kMaxLds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return true;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return false;
+  done.fetch_or(bit, std::memory_order_relaxed);
+  return true;
+}
 
 struct FwdArgs {
   const void* q;
@@ -29,6 +45,11 @@ struct FwdArgs {
   float* st_out;
   int st_L;
   int G = 1;  // heads per q/k head: q and k of head bh are row bh / G
+  // full-width sweep: the segment-spanning bucket states as fp16 MFMA
+  // fragments [BH][nseg][8 waves][4][64 lanes] x 16 bytes, and their
+  // power-of-two exponents [BH][nseg][8 waves] (node_pack_kernel)
+  const void* node16 = nullptr;
+  const int* node_exp = nullptr;
 };
 
 struct HandoffArgs {
@@ -146,6 +167,16 @@ int sweep_lds_bytes(int dtype, int C, int DKP, int L, int nslot);
 int launch_sweep(int dtype, int C, int DKP, const FwdArgs& a, int nblocks, hipStream_t s);
 int launch_seg_state(int dtype, int DKP, const SegArgs& a, int nblocks, hipStream_t s);
 int launch_seg_nodes(const NodeArgs& a, int BH, hipStream_t s);
+// full-width register-state sweep (bf16, C = 64, 64 < dk <= 128, dv = 128,
+// at most 8 chunk-level bits): one workgroup per (b,h, segment)
+bool sweep_wide_ok(int C, int dk, int dv, int L, int nslot, int seg_log2);
+// segment sizes the full-width sweep is built for (2^seg_log2 chunks)
+bool sweep_wide_seg_ok(int seg_log2, int nslot);
+int launch_sweep_wide(const FwdArgs& a, hipStream_t s);
+// packed node states for the full-width sweep (node16 / node_exp of FwdArgs),
+// plus the segments' total log decays; bytes of workspace they take
+size_t node_pack_bytes(int BH, int nseg);
+int launch_node_pack(const NodeArgs& a, void* node16, int* node_exp, int BH, hipStream_t s);
 int rs_max_slots();
 int rs_lds_bytes(int L, int nslot);
 int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t s);

@@ -39,6 +39,10 @@ struct FwdPlan {
 // size, up to 16 chunks, that still gives at least 2048 workgroups.  Depends
 // on shapes only, so the workspace size is known without the dtype.
 constexpr long long kCUs = 256;
+// Whether the automatic choice takes the full-width sweep for the shapes it
+// covers (it needs 8 segments per (b,h) at B=2 H=16 T=16384, whose segment
+// prepass costs more than its faster sweep saves, so not yet).
+constexpr bool kWideAuto = false;
 
 // The kernels move q, k, v, out and the level states with 16-byte vector
 // accesses; pointers that are not 16-byte aligned are rejected up front.
@@ -48,9 +52,31 @@ bool aligned16(std::initializer_list<const void*> ps) {
   return true;
 }
 
-int auto_seg_log2(long long BH, int dk, int dv, int C, int N) {
+int auto_seg_log2(long long BH, int dk, int dv, int C, int N, int L) {
+  const int nslot = N > 1 ? bit_length(N - 1) : 0;
+  const bool wide_shape = kWideAuto && ll::sweep_wide_ok(C, dk, dv, L, nslot, -1);
   const bool rs_shape = C == 64 && dk > 64 && dv % 64 == 0 && N <= 1024;
+  if (wide_shape) {
+    // full-width sweep: one workgroup (all 128 columns) per (b,h, segment),
+    // one per CU; among the segment sizes it is built for, the one that
+    // minimises rounds x (chunks per segment + ~2 chunks of prologue), the
+    // largest on a tie
+    int best = -1;
+    long long best_cost = -1;
+    for (int s = 6; s >= 3; --s) {
+      if (!ll::sweep_wide_seg_ok(s, nslot)) continue;
+      const long long nseg = (N + (1LL << s) - 1) >> s;
+      const long long rounds = (BH * nseg + kCUs - 1) / kCUs;
+      const long long cost = rounds * (std::min<long long>(1LL << s, N) + 2);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best = s;
+      }
+    }
+    if (best >= 0) return best;
+  }
   if (rs_shape) {
+    // workgroups per segment: one per 64 columns
     const long long per_seg = BH * (dv / 64);
     int best = 6;
     long long best_cost = -1;
@@ -107,14 +133,18 @@ int plan_fwd(int B, int H, int T, int dk, int dv, int C, int seg_log2, FwdPlan* 
   p->L = T > 0 ? bit_length(T - 1) + 1 : 0;
   p->DKP = dk <= 32 ? 32 : (dk <= 64 ? 64 : 128);
   p->nslot = p->N > 1 ? bit_length(p->N - 1) : 0;
-  p->seg_log2 = seg_log2 >= 0 ? seg_log2 : auto_seg_log2(p->BH, dk, dv, C, p->N);
+  p->seg_log2 = seg_log2 >= 0 ? seg_log2 : auto_seg_log2(p->BH, dk, dv, C, p->N, p->L);
   p->nseg = p->N > 0 ? (p->N + (1 << p->seg_log2) - 1) >> p->seg_log2 : 0;
   p->blk_log2 = p->nseg > 1 ? auto_blk_log2(p->BH, dv, p->seg_log2, p->nseg) : p->seg_log2;
   p->nblk1 = ((p->nseg - 1) << (p->seg_log2 - p->blk_log2)) + 1;
   if (p->nseg > 1) {
     const size_t elems = (size_t)p->BH * dv * p->DKP;
     p->ws_state = align256(elems * p->nblk1 * sizeof(float));
-    p->ws_nodes = align256(elems * p->nseg * sizeof(float));
+    // fp32 node states, or (full-width sweep) the packed fp16 fragments and
+    // exponents, which take less room
+    p->ws_nodes = align256(std::max(elems * p->nseg * sizeof(float),
+                                    ll::sweep_wide_ok(C, dk, dv, p->L, p->nslot, p->seg_log2)
+                                        ? ll::node_pack_bytes(p->BH, p->nseg) : 0));
     p->ws_decay = align256((size_t)p->BH * p->nseg * sizeof(float));
     p->ws_bdecay = align256((size_t)p->BH * p->nblk1 * sizeof(float));
   } else {
@@ -147,10 +177,13 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   const bool rs_ok = dtype == LL_BF16 && C == 64 && dk > 64 && dv % 64 == 0 &&
                      p.nslot <= ll::rs_max_slots() && p.L <= 17 &&
                      ll::rs_lds_bytes(p.L, p.nslot) <= ll::kMaxLds;
-  if (kernel < LL_KERNEL_AUTO || kernel > LL_KERNEL_REGISTER_STATE) return LL_ERR_SHAPE;
+  const bool wide_ok = dtype == LL_BF16 && ll::sweep_wide_ok(C, dk, dv, p.L, p.nslot, p.seg_log2);
+  if (kernel < LL_KERNEL_AUTO || kernel > LL_KERNEL_WIDE) return LL_ERR_SHAPE;
   if (kernel == LL_KERNEL_REGISTER_STATE && !rs_ok) return LL_ERR_UNSUPPORTED;
-  const bool use_rs = kernel == LL_KERNEL_REGISTER_STATE || (kernel == LL_KERNEL_AUTO && rs_ok);
-  if (!use_rs) {
+  if (kernel == LL_KERNEL_WIDE && !wide_ok) return LL_ERR_UNSUPPORTED;
+  const bool use_wide = kernel == LL_KERNEL_WIDE || (kernel == LL_KERNEL_AUTO && kWideAuto && wide_ok);
+  const bool use_rs = !use_wide && (kernel == LL_KERNEL_REGISTER_STATE || (kernel == LL_KERNEL_AUTO && rs_ok));
+  if (!use_rs && !use_wide) {
     const int lds = ll::sweep_lds_bytes(dtype, C, p.DKP, p.L, p.nslot);
     if (lds < 0 || lds > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
   }
@@ -180,6 +213,10 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   float* seg_decay = p.ws_total ? reinterpret_cast<float*>(wsb + p.ws_state + p.ws_nodes) : nullptr;
   float* blk_decay =
       p.ws_total ? reinterpret_cast<float*>(wsb + p.ws_state + p.ws_nodes + p.ws_decay) : nullptr;
+  // the full-width sweep's packed nodes share the node region
+  void* node16 = nodes;
+  int* node_exp = p.ws_total ? reinterpret_cast<int*>(wsb + p.ws_state + (size_t)p.BH * p.nseg * 8 * 4 * 64 * 16)
+                             : nullptr;
 
   auto mark = [&](int i) {
     if (events && st == LL_OK && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess)
@@ -199,7 +236,10 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
     if (st == LL_OK) {
       ll::NodeArgs na{blk_state, blk_decay, nodes, seg_decay, p.nseg, p.nblk1,
                       p.seg_log2 - p.blk_log2, dv * p.DKP};
-      st = ll::launch_seg_nodes(na, p.BH, stream);
+      if (use_wide)
+        st = ll::launch_node_pack(na, node16, node_exp, p.BH, stream);
+      else
+        st = ll::launch_seg_nodes(na, p.BH, stream);
     }
   } else {
     mark(1);
@@ -207,10 +247,12 @@ int run_fwd(int dtype, const void* q, const void* k, const void* v, const float*
   mark(2);
   if (st == LL_OK) {
     ll::FwdArgs fa{q, k, v, log_a, lambda, out, nodes, seg_decay, p.BH, T, dk, dv, p.L,
-                   p.seg_log2, p.nseg, p.nslot, fin ? fin->data : nullptr, fin ? fin->L : 0, G};
+                   p.seg_log2, p.nseg, p.nslot, fin ? fin->data : nullptr, fin ? fin->L : 0, G,
+                   node16, node_exp};
     const long long pairs = (long long)p.BH * p.nseg;
     const long long nblocks = ((pairs + 7) / 8) * 8 * (use_rs ? dv / 64 : dv / 16);
-    if (nblocks > 0x7fffffffLL) st = LL_ERR_UNSUPPORTED;
+    if (use_wide) st = ll::launch_sweep_wide(fa, stream);
+    else if (nblocks > 0x7fffffffLL) st = LL_ERR_UNSUPPORTED;
     else if (use_rs) st = ll::launch_sweep_rs(fa, static_cast<int>(nblocks), stream);
     else st = ll::launch_sweep(dtype, C, p.DKP, fa, static_cast<int>(nblocks), stream);
   }

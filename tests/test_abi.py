@@ -80,8 +80,16 @@ def test_fwd_ex_options():
     small = ll._FwdOpts(0, 1, 0, ctypes.c_void_p(256), need - 1, None)
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 4096, 64, 64, 64, ctypes.byref(small), None) == LL_ERR_WORKSPACE
     # kernel selection: out-of-range value, and the register-state kernel on sizes it does not cover
-    bad = ll._FwdOpts(0, -1, 3, None, 0, None)
+    bad = ll._FwdOpts(0, -1, 4, None, 0, None)
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(bad), None) == LL_ERR_SHAPE
+    # the full-width kernel: dv = 128, C = 64, 64 < dk <= 128, bf16, its segment sizes only
+    wide = ll._FwdOpts(0, -1, 3, None, 0, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(wide), None) == LL_ERR_UNSUPPORTED
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 4096, 128, 64, 64, ctypes.byref(wide), None) == LL_ERR_UNSUPPORTED
+    wide2 = ll._FwdOpts(0, 2, 3, None, 0, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 4096, 128, 128, 64, ctypes.byref(wide2), None) == LL_ERR_UNSUPPORTED
+    widef = ll._FwdOpts(1, -1, 3, None, 0, None)
+    assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 4096, 128, 128, 64, ctypes.byref(widef), None) == LL_ERR_UNSUPPORTED
     rs = ll._FwdOpts(0, -1, 2, None, 0, None)
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 16, 16, 16, ctypes.byref(rs), None) == LL_ERR_UNSUPPORTED
     assert L.loglinear_fwd_ex(p, p, p, p, p, p, 1, 1, 64, 128, 48, 64, ctypes.byref(rs), None) == LL_ERR_UNSUPPORTED

@@ -270,3 +270,50 @@ def test_bench_shape_weak_decay_auto_plan():
     for bh in [(0, 3), (1, 15)]:
         want = oracle.forward_rows(q, k, v, la, lam, bh, rows)
         assert_parity(got[bh[0], bh[1], rows], want, BF16_TOL, f"lm weak auto {bh}")
+
+
+WIDE_CASES = [
+    # (B, H, T, dk, decay, seg_log2): dv = 128
+    (1, 2, 64, 128, "none", 3),      # one chunk
+    (1, 1, 65, 128, "weak", 3),      # ragged tail of one token
+    (2, 1, 1000, 128, "weak", 3),
+    (1, 2, 1000, 96, "strong", 4),   # dk padded to 128
+    (1, 1, 3000, 128, "none", 4),
+    (1, 1, 4096, 128, "weak", 5),
+    (1, 1, 8000, 128, "none", 5),
+    (1, 1, 9000, 128, "weak", 6),
+    (1, 1, 20000, 128, "weak", 6),   # ten chunk-level bits
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: "B{}H{}T{}dk{}_{}_s{}".format(*c))
+def test_wide_kernel_parity(case):
+    """The full-width sweep (one workgroup per (b,h, segment), all 128 dv
+    columns) forced on each segment size it is built for, against the oracle:
+    full output up to T=4096, sampled rows (every segment boundary, chunks
+    reading freshly merged deep states) beyond."""
+    B, H, T, dk, decay, s = case
+    w = W.FwdWorkload("wide", B, H, T, dk, 128, 64, "bf16", decay=decay, seed=T + dk + s)
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    announce(f"wide kernel {case}")
+    out = ll.fwd_ex(*to_dev(q, k, v, la, lam), C=64, seg_log2=s, kernel=ll.KERNEL_WIDE)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    if T <= 4096:
+        assert_parity(got, oracle.forward(q, k, v, la, lam), BF16_TOL, f"wide {case}")
+    else:
+        rows = _sample_rows(T, 64, 48, seed=11, seg_chunks=1 << s)
+        for bh in [(b, h) for b in range(B) for h in range(H)]:
+            want = oracle.forward_rows(q, k, v, la, lam, bh, rows)
+            assert_parity(got[bh[0], bh[1], rows], want, BF16_TOL, f"wide {case} {bh}")
+
+
+def test_wide_kernel_rejects_other_shapes():
+    w = W.FwdWorkload("wide_no", 1, 1, 128, 128, 64, 64, "bf16")
+    dq, dk_, dv_, dla, dlam = to_dev(*W.make_fwd_inputs(w))
+    with pytest.raises(ll.LogLinearError):
+        ll.fwd_ex(dq, dk_, dv_, dla, dlam, C=64, kernel=ll.KERNEL_WIDE)
+    w = W.FwdWorkload("wide_no2", 1, 1, 4096, 128, 128, 64, "bf16")
+    dq, dk_, dv_, dla, dlam = to_dev(*W.make_fwd_inputs(w))
+    with pytest.raises(ll.LogLinearError):  # a segment size it is not built for
+        ll.fwd_ex(dq, dk_, dv_, dla, dlam, C=64, seg_log2=2, kernel=ll.KERNEL_WIDE)

@@ -28,6 +28,8 @@ CASES = [
     (1, 1, 3000, 96, 128, 64, "bf16", "strong", 0, 3, ll.KERNEL_REGISTER_STATE),  # dk padded
     (1, 1, 4096, 128, 128, 64, "bf16", "none", 0, -1, ll.KERNEL_AUTO),    # T a power of two
     (1, 1, 4095, 128, 64, 64, "bf16", "none", 0, -1, ll.KERNEL_AUTO),     # every level live
+    (1, 2, 3000, 128, 128, 64, "bf16", "weak", 1, 3, ll.KERNEL_WIDE),     # full-width sweep, node levels
+    (1, 1, 4095, 96, 128, 64, "bf16", "none", 0, 4, ll.KERNEL_WIDE),
 ]
 
 
@@ -97,8 +99,9 @@ def test_decode_continues_from_prefill(dtype, T, C):
     assert_parity(out.cpu().numpy(), want[:, :, :T], tol, f"prefill out T={T}")
 
 
-@pytest.mark.parametrize("T,decay,s", [(16384, "none", 6), (20000, "weak", 7)])
-def test_prefill_states_at_bench_plans(T, decay, s):
+@pytest.mark.parametrize("T,decay,s,kernel", [(16384, "none", 6, "rs"), (20000, "weak", 7, "rs"),
+                                              (16384, "none", 5, "wide"), (20000, "weak", 6, "wide")])
+def test_prefill_states_at_bench_plans(T, decay, s, kernel):
     """Prefill states at the bench's segment sizes (64-chunk segments at
     T=16384, the ten-slot kernel with 128-chunk segments beyond 256 chunks),
     with no or weak decay so every inter-chunk level carries weight."""
@@ -107,8 +110,8 @@ def test_prefill_states_at_bench_plans(T, decay, s):
     Ls = W.num_levels(T)
     announce(f"prefill at bench plan T={T} s={s}")
     states = torch.full((1, 1, Ls, 128, 128), float("nan"), device="cuda")
-    ll.fwd_ex(*to_dev(q, k, v, la, lam), C=64, seg_log2=s, kernel=ll.KERNEL_REGISTER_STATE,
-              final_states=states)
+    ll.fwd_ex(*to_dev(q, k, v, la, lam), C=64, seg_log2=s,
+              kernel=ll.KERNEL_REGISTER_STATE if kernel == "rs" else ll.KERNEL_WIDE, final_states=states)
     torch.cuda.synchronize()
     want = oracle.states_at(k, v, la, T - 1, Ls)
     assert_parity(states.cpu().numpy(), want, BF16_TOL, f"states T={T} s={s}")
