@@ -1,13 +1,22 @@
 """Benchmark of the log-linear attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 300] [--workload NAME] [--no-cpu-baseline]
+                    [--headline-only] [--pass fwd|bwd|decode|lambda]
 
-A step is one loglinear_fwd call (segment-state, node and sweep kernels) over
-one batch of synthetic inputs already resident in HBM.  Prints ONE JSON line;
-at the default workload it also carries a "prefill" object (the same forward
-plus the decode states at T-1), a "decode" object (one decode step of
-64 sequences x 16 heads, L = 17) and a "lambda_proj" object (the level-weight
-projection at the same B, T, H, L with hidden width 2048), timed the same way.
+A step is one loglinear_fwd_ex call (segment-state, node and sweep kernels,
+caller-owned workspace) over one batch of synthetic inputs already resident in
+HBM.  Prints ONE JSON line.  At the default workload the line also carries,
+each timed the same way:
+  "configs"     the forward at B=8 H=8 T=2048 dk=128 dv=64 (L=12) and at
+                B=1 H=16 T=65536 dk=dv=128 (L=17), each with its own roofline;
+  "bwd"         the backward (gradients of q, k, v, log_a, lambda) of the
+                headline workload;
+  "prefill"     the forward plus the decode states at T-1;
+  "decode"      one decode step of 64 sequences x 16 heads, L = 17;
+  "lambda_proj" the level-weight projection at the same B, T, H, L with hidden
+                width 2048, and its gradient;
+  "pages_context" the pages' own speed statements (context, not a target).
+The backward and the configs run before the headline forward is timed.
 --pass bwd / decode / lambda time only the backward, the decode step or the
 projection.
 Default workload: log-linear Mamba-2 forward, B=2, H=16, T=16384, dk=dv=128,
@@ -30,6 +39,19 @@ METRIC = "fwd tokens/sec + TFLOP/s vs bf16 MFMA peak, log-linear Mamba-2 at T=16
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 matrix
+
+# What the pages say about speed, restated, with the hardware they name.
+# Context only: they print no runtime or throughput figure for this path.
+PAGES_CONTEXT = (
+    "Context, not a target: the pages publish no kernel time or throughput for this path. "
+    "In their words restated: a custom Triton chunkwise kernel for log-linear Mamba-2 overtakes "
+    "FlashAttention-2 in forward+backward kernel time once sequences pass roughly 8K tokens, "
+    "and the whole log-linear Mamba-2 model trains faster than a Transformer at 32K; all on one "
+    "NVIDIA H100, batch 2, 48 heads, head dim 64, state dim 128, chunk 64, Mamba-2 with "
+    "multi-value attention against FlashAttention-2 with grouped-query attention, lengths up to "
+    "131K, precision not stated (paper-reading blog, experiment results / training efficiency; "
+    "news write-up, Fig. 4 and its setup; journal-club slides, slide 39)."
+)
 
 
 def algorithmic_flops(B, H, T, dk, dv, C):
@@ -187,6 +209,167 @@ def bench_lambda(dev, steps: int, warmup: int):
     }
 
 
+def sweep_kernel(w) -> str:
+    """The sweep kernel the automatic plan launches for workload w."""
+    rs = (w.dtype == "bf16" and w.C == 64 and w.dk > 64 and w.dv % 64 == 0
+          and -(-w.T // 64) <= 1024)
+    return "fwd_rs_kernel" if rs else "fwd_sweep_kernel"
+
+
+def upload_fwd(w, dev, nsets: int = 1, base=None):
+    """Device input sets (nsets buffers holding the same values), the output
+    and the caller-owned workspace for timing workload w; base: the host
+    inputs, made here when not given."""
+    import torch
+    import log_linear_attention_attn_amd as ll
+    import workloads as W
+    if base is None:
+        base = W.make_fwd_inputs(w)
+    sets = [[t.to(dev) for t in base]]
+    sets += [[t.clone() for t in sets[0]] for _ in range(nsets - 1)]
+    out = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.float32, device=dev)
+    return sets, out
+
+
+def bench_fwd(w, dev, K: int, Wm: int, seg_log2: int = -1, nsets: int = 1, zero_check: bool = False,
+              uploaded=None):
+    """Time K forwards (loglinear_fwd_ex, caller-owned workspace, so no device
+    allocation inside the timed loop) of workload w after Wm untimed ones.
+
+    Inputs are rotated over nsets buffers holding the same values, so that a
+    workload smaller than the 256 MB last-level cache does not find its inputs
+    there on the next step.  Four events per step, re-recorded around the
+    library's kernels, give the per-kernel times; the sweep's time divides the
+    algorithmic bytes for the roofline record.  uploaded: what upload_fwd
+    returned, so the host-to-device copies need not sit between measurements."""
+    import torch
+    import log_linear_attention_attn_amd as ll
+    sets, out = uploaded if uploaded is not None else upload_fwd(w, dev, nsets)
+    ws_bytes = ll.fwd_workspace_size(w.B, w.H, w.T, w.dk, w.dv, w.C, seg_log2)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def timed(input_sets, n_warm=Wm):
+        def step(i, ev=None):
+            q, k, v, la, lam = input_sets[i % len(input_sets)]
+            ll.fwd_ex(q, k, v, la, lam, C=w.C, out=out, seg_log2=seg_log2, workspace=ws, phase_events=ev)
+
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        for s_ in evs:
+            for e in s_:
+                e.record()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(n_warm):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(K):
+            step(i, evs[i])
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        phases = [[s_[j].elapsed_time(s_[j + 1]) for j in range(3)] for s_ in evs]
+        return start.elapsed_time(stop) / K, wall, phases
+
+    ms, wall, phases = timed(sets)
+    seg_ms, node_ms, sweep_ms = (sum(p[j] for p in phases) / K for j in range(3))
+    step_ms = sorted(sum(p) for p in phases)
+    ms_zero = None
+    if zero_check:
+        # the kernels are data-oblivious: the same shapes with log_a = 0 must time the same
+        zero_sets = [[q, k, v, torch.zeros_like(la), lam] for q, k, v, la, lam in sets]
+        ms_zero, _, _ = timed(zero_sets, max(Wm, 20))
+        del zero_sets
+    del sets
+
+    flops = algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv, w.C)
+    in_bytes = 2 if w.dtype == "bf16" else 4
+    abytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv, w.L, in_bytes)
+    if w.Hk:
+        # q and k are read once per q/k head, not once per head
+        abytes -= w.B * (w.H - w.Hk) * w.T * 2 * w.dk * in_bytes
+    tflops = flops / (ms * 1e-3) / 1e12
+    sweep_gbs = abytes / (sweep_ms * 1e-3) / 1e9
+    step_gbs = abytes / (ms * 1e-3) / 1e9
+    floor_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+    traffic = load_traffic(w.name)
+    rec = {
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "C": w.C, "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_a/lambda/out",
+                   "decay": w.decay, "seed": w.seed, "qk_heads": w.qk_heads},
+        "steps": K, "warmup": Wm,
+        "ms_per_step": ms,
+        "tokens_per_s": w.B * w.T / (ms * 1e-3),
+        "head_tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+        "tflops": tflops,
+        "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "algorithmic_flops": flops,
+        "algorithmic_bytes": abytes,
+        "roofline_floor_ms": floor_ms,
+        "frac_roofline_step": floor_ms / ms,
+        "hbm_gbs_step": step_gbs,
+        "kernels_ms": {"seg_state": seg_ms, "seg_node": node_ms, "fwd_sweep": sweep_ms},
+        "median_ms_per_step": step_ms[len(step_ms) // 2],
+        "wall_ms_per_step": wall / K * 1e3,
+        "workspace_bytes": ws_bytes,
+        "roofline": {
+            "kernel": sweep_kernel(w),
+            "bound": "hbm",
+            "achieved": sweep_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": sweep_gbs / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "mfma_tflops": flops / (sweep_ms * 1e-3) / 1e12,
+            "note": "achieved = algorithmic bytes of the whole forward / the sweep kernel's "
+                    "event-timed duration; traffic = its rocprofv3 FETCH_SIZE + WRITE_SIZE "
+                    "bytes per launch (calibrated on a plain copy), null when taken on other sources",
+        },
+        "source_hash": source_hash(),
+    }
+    if ms_zero is not None:
+        rec["ms_per_step_log_a_zero"] = ms_zero
+    return rec
+
+
+def bwd_record(w, dev, K: int, Wm: int, base=None):
+    """The backward of workload w timed like the forward (see bench_bwd)."""
+    import numpy as np
+    import torch
+    import log_linear_attention_attn_amd as ll
+    import workloads as W
+    q, k, v, la, lam = [t.to(dev) for t in (base if base is not None else W.make_fwd_inputs(w))]
+    out = ll.fwd(q, k, v, la, lam, C=w.C)
+    dout = torch.from_numpy(np.random.default_rng(w.seed + 1).standard_normal(tuple(out.shape))
+                            .astype(np.float32)).to(dev)
+    for _ in range(Wm):
+        ll.bwd(q, k, v, la, lam, out, dout, C=w.C)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(K):
+        ll.bwd(q, k, v, la, lam, out, dout, C=w.C)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+    flops = algorithmic_flops_bwd(w.B, w.H, w.T, w.dk, w.dv, w.C)
+    abytes = algorithmic_bytes_bwd(w.B, w.H, w.T, w.dk, w.dv, w.L, 2 if w.dtype == "bf16" else 4)
+    tflops = flops / (ms * 1e-3) / 1e12
+    bf16 = w.dtype == "bf16" and w.C == 64
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    return {
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "C": w.C,
+                   "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_a/lambda/out/dout", "pass": "backward"},
+        "steps": K, "warmup": Wm, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+        "tflops": tflops, "algorithmic_flops": flops, "algorithmic_bytes": abytes,
+        "hbm_gbs_algorithmic": abytes / (ms * 1e-3) / 1e9,
+        "roofline": {"kernel": ("whole backward (bf16 matrix cores, hi/lo splits of fp32 operands)"
+                                if bf16 else "whole backward (fp32 matrix-core arithmetic)"),
+                     "bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tflops / peak, "traffic": None},
+    }
+
+
 def bench_prefill(sets, w, steps: int, warmup: int):
     """Forward plus the decode states at T-1 (loglinear_prefill) on the same
     inputs: the extra cost over the forward is the state emit of the last
@@ -295,6 +478,9 @@ def main():
                     help="untimed steps first: the GPU clocks take ~0.1 s of load to reach steady state")
     ap.add_argument("--workload", default="lm_B2H16_T16384_dk128_dv128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline forward (no other configs, backward, prefill, "
+                         "decode or projection objects)")
     ap.add_argument("--seg-log2", type=int, default=-1)
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode", "lambda"], default="fwd",
                     help="time the forward (default, the headline; its line also carries one "
@@ -344,145 +530,64 @@ def main():
             "roofline": rec["roofline"], "tokens_per_s": rec["tokens_per_s"],
             "algorithmic_bytes": rec["algorithmic_bytes"]}))
         return
-    base = W.make_fwd_inputs(w)
-    sets = [[t.to(dev) for t in base]]
-    # three input sets (same values, other buffers), rotated so consecutive
-    # steps do not find their inputs in the 256 MB infinity cache
-    sets += [[t.clone() for t in sets[0]] for _ in range(2)]
-    out = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.float32, device=dev)
     K, Wm = args.steps, args.warmup
-
-    def timed(input_sets):
-        def step(i, ev=None):
-            q, k, v, la, lam = input_sets[i % len(input_sets)]
-            ll.fwd_ex(q, k, v, la, lam, C=w.C, out=out, seg_log2=args.seg_log2, phase_events=ev)
-
-        for i in range(Wm):
-            step(i)
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-        for s_ in evs:
-            for e in s_:
-                e.record()
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record()
-        for i in range(K):
-            step(i, evs[i])
-        stop.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        phases = [[s_[j].elapsed_time(s_[j + 1]) for j in range(3)] for s_ in evs]
-        return start.elapsed_time(stop) / K, wall, phases
-
-    ms, wall, phases = timed(sets)
-    seg_ms, node_ms, sweep_ms = (sum(p[j] for p in phases) / K for j in range(3))
-    step_ms = sorted(sum(p) for p in phases)
-    median_ms = step_ms[len(step_ms) // 2]
-    # the kernels are data-oblivious: the same shapes with log_a = 0 must time the same
-    zero_sets = [[q, k, v, torch.zeros_like(la), lam] for q, k, v, la, lam in sets]
-    ms_zero, _, _ = timed(zero_sets)
-
-    flops = algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv, w.C)
-    in_bytes = 2 if w.dtype == "bf16" else 4
-    abytes = algorithmic_bytes(w.B, w.H, w.T, w.dk, w.dv, w.L, in_bytes)
-    if w.Hk:
-        # q and k are read once per q/k head, not once per head
-        abytes -= w.B * (w.H - w.Hk) * w.T * 2 * w.dk * in_bytes
-    tokens = w.B * w.T
-    tflops = flops / (ms * 1e-3) / 1e12
-    sweep_gbs = abytes / (sweep_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.name)
+    # the backward and the other configs first: they are part of the line, and
+    # they bring the GPU clocks to steady state before the headline is timed
+    # (all inputs are drawn and uploaded first, so the GPU does not idle
+    # between the measurements)
+    extra = {}
+    base = W.make_fwd_inputs(w)
+    full = args.workload == W.LM_T16K.name and not args.headline_only
+    aux = [(x, upload_fwd(x, dev, 3 if x is W.MAMBA2_T2K else 1)) for x in (W.MAMBA2_T2K, W.LONG_T64K)] if full else []
+    head = upload_fwd(w, dev, 3, base)
+    if full:
+        aux_w = max(Wm, 20)
+        extra["bwd"] = bwd_record(w, dev, max(3, K // 4), 3, base=base)
+        extra["configs"] = {x.name: bench_fwd(x, dev, K, aux_w, uploaded=xu) for x, xu in aux}
+    del aux
+    rec_f = bench_fwd(w, dev, K, Wm, args.seg_log2, zero_check=True, uploaded=head)
+    sets = head[0]
+    del head
     rec = {
         "metric": METRIC,
-        "value": tokens / (ms * 1e-3),
+        "value": rec_f["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
-        "ms_per_step": ms,
+        "ms_per_step": rec_f["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
-                   "C": w.C, "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_a/lambda/out",
-                   "decay": w.decay, "seed": w.seed, "qk_heads": w.qk_heads},
-        "head_tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
-        "tflops": tflops,
-        "frac_bf16_peak": tflops / PEAK_BF16_TFLOPS,
-        "algorithmic_flops": flops,
-        "algorithmic_bytes": abytes,
-        "frac_roofline_step": max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBS * 1e9)) / (ms * 1e-3),
-        "kernels_ms": {"seg_state": seg_ms, "seg_node": node_ms, "fwd_sweep": sweep_ms},
-        "median_ms_per_step": median_ms,
-        "ms_per_step_log_a_zero": ms_zero,
-        "wall_ms_per_step": wall / K * 1e3,
-        "roofline": {
-            "kernel": "fwd_rs_kernel" if (w.dtype == "bf16" and w.C == 64 and w.dk > 64 and w.dv % 64 == 0
-                                          and -(-w.T // 64) <= 1024) else "fwd_sweep_kernel",
-            "bound": "hbm",
-            "achieved": sweep_gbs,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": sweep_gbs / PEAK_HBM_GBS,
-            "traffic": traffic,
-            "mfma_tflops": flops / (sweep_ms * 1e-3) / 1e12,
-        },
-        "source_hash": source_hash(),
+        "config": rec_f["config"],
     }
-    if args.workload == W.LM_T16K.name:
+    rec.update({k: v for k, v in rec_f.items() if k not in ("config", "ms_per_step", "tokens_per_s")})
+    rec.update(extra)
+    if full:
         rec["prefill"] = bench_prefill(sets, w, K, Wm)
+        del sets
         rec["decode"] = bench_decode(dev, K, Wm)
         rec["lambda_proj"] = bench_lambda(dev, K, Wm)
+    rec["pages_context"] = PAGES_CONTEXT
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec))
 
 
-
 def bench_bwd(args, w, dev):
     """Backward (loglinear_bwd) of the same workload: gradients of sum(out * dout)
     for a random dout; inputs and out resident in HBM, timed over K steps."""
-    import numpy as np
-    import torch
-    import log_linear_attention_attn_amd as ll
-    import workloads as W
-    q, k, v, la, lam = [t.to(dev) for t in W.make_fwd_inputs(w)]
-    out = ll.fwd(q, k, v, la, lam, C=w.C)
-    dout = torch.from_numpy(np.random.default_rng(w.seed + 1).standard_normal(tuple(out.shape)).astype(np.float32)).to(dev)
-    K, Wm = args.steps, args.warmup
-    for _ in range(Wm):
-        ll.bwd(q, k, v, la, lam, out, dout, C=w.C)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(K):
-        ll.bwd(q, k, v, la, lam, out, dout, C=w.C)
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / K
-    flops = algorithmic_flops_bwd(w.B, w.H, w.T, w.dk, w.dv, w.C)
-    abytes = algorithmic_bytes_bwd(w.B, w.H, w.T, w.dk, w.dv, w.L, 2 if w.dtype == "bf16" else 4)
-    tflops = flops / (ms * 1e-3) / 1e12
-    bf16 = w.dtype == "bf16" and w.C == 64
-    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    r = bwd_record(w, dev, args.steps, args.warmup)
     rec = {
         "metric": "bwd tokens/sec (gradients of q, k, v, log_a, lambda), log-linear Mamba-2",
-        "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": Wm,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "C": w.C,
-                   "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_a/lambda/out/dout", "pass": "backward"},
-        "algorithmic_flops": flops, "algorithmic_bytes": abytes,
-        "roofline": {"kernel": ("whole backward (bf16 matrix cores, hi/lo splits of fp32 operands)"
-                                if bf16 else "whole backward (fp32 matrix-core arithmetic)"),
-                     "bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": tflops / peak, "traffic": None},
-        "hbm_gbs_algorithmic": abytes / (ms * 1e-3) / 1e9,
+        "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": r["steps"],
+        "warmup": r["warmup"], "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": r["config"],
     }
+    rec.update({k: v for k, v in r.items() if k not in rec and k != "tokens_per_s"})
     print(json.dumps(rec))
 
 

@@ -23,7 +23,8 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "log_linear_attention_attn_amd", "csrc")
-HASHED = ("loglinear_fwd.hip", "loglinear_sweep_rs.hip", "ll_device.h", "ll_internal.h", "loglinear_api.cpp")
+HASHED = ("loglinear_fwd.hip", "loglinear_sweep_rs.hip", "loglinear_sweep_wide.hip", "ll_device.h",
+          "ll_internal.h", "loglinear_api.cpp")
 
 
 def source_hash() -> str:
