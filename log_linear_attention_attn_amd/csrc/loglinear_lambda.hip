@@ -127,11 +127,13 @@ __global__ void __launch_bounds__(lp::NT) lambda_proj_kernel(LamProjArgs a) {
   // K slices in a per-block rotated order: blocks running at the same time
   // read different slices of W (and of their x rows), so their requests do not
   // all land on the same L2 / HBM channels
+  // Slices past the last one (the loop runs a multiple of NS of them) start
+  // at D, so all their loads fall outside the resource and read zeros.
   const int nsl = (D + BK - 1) / BK;
   const int rot = static_cast<int>(rb % nsl);
   auto kof = [&](int i) {
     const int j = i + rot;
-    return (j >= nsl ? j - nsl : j) * BK;
+    return i >= nsl ? D : (j >= nsl ? j - nsl : j) * BK;
   };
   auto compute = [&](int buf) {
     if (njt <= 0) return;
@@ -155,25 +157,24 @@ __global__ void __launch_bounds__(lp::NT) lambda_proj_kernel(LamProjArgs a) {
   // Pipeline: slice i is computed from LDS buffer i & 1 while slice i + 1 is
   // staged into the other buffer (last read in iteration i - 1, before the
   // barrier that ends it) and slice i + 1 + NS is loaded into the register
-  // slot slice i + 1 vacated: one barrier per slice.
+  // slot slice i + 1 vacated: one barrier per slice.  Every load and stage is
+  // unconditional (slices past the end are zeros), so the count of loads in
+  // flight is the same on every path and the wait for a slice's registers
+  // leaves the later slices' loads outstanding.
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (s < nsl) load(rx[s], rw[s], kof(s));
+  for (int s = 0; s < NS; ++s) load(rx[s], rw[s], kof(s));
   stage(rx[0], rw[0], 0);
-  if (NS < nsl) load(rx[0], rw[0], kof(NS));
+  load(rx[0], rw[0], kof(NS));
   __syncthreads();
   static_assert(NS % 2 == 0, "slice i uses register slot i % NS and buffer i & 1");
   for (int ib = 0; ib < nsl; ib += NS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int i = ib + s;
-      if (i >= nsl) break;
       compute(s & 1);
-      if (i + 1 < nsl) {
-        const int sn = (s + 1) % NS;  // a constant once the loop is unrolled
-        stage(rx[sn], rw[sn], (s + 1) & 1);
-        if (i + 1 + NS < nsl) load(rx[sn], rw[sn], kof(i + 1 + NS));
-      }
+      const int sn = (s + 1) % NS;  // a constant once the loop is unrolled
+      stage(rx[sn], rw[sn], (s + 1) & 1);
+      load(rx[sn], rw[sn], kof(i + 1 + NS));
       __syncthreads();
     }
   }

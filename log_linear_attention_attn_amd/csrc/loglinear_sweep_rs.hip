@@ -711,7 +711,8 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
   const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
 
   // Register prefetch two tiles ahead: tiles alternate between two register
-  // sets (and the two LDS buffers); tokens at or past s1 read zero.
+  // sets (and the two LDS buffers); tokens at or past s1 read zero (offsets
+  // out of the resource's range).
   struct Regs {
     bf16x8 k[2], v;
     float la;
@@ -735,6 +736,9 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
   float Aseg = 0.f;
   // one 64-token tile from register set r into LDS buffer buf, then its MFMAs
   auto tile = [&](Regs& r, int buf, int b0) {
+    // keep the scheduler from hoisting this tile's register work above the
+    // previous tile: that would wait for loads meant to stay in flight
+    __builtin_amdgcn_sched_barrier(0);
     unsigned char* base = smem + buf * ss::BUF;
     bf16* Ks = reinterpret_cast<bf16*>(base + ss::KS_OFF);
     bf16* Vh = reinterpret_cast<bf16*>(base + ss::VH_OFF);
@@ -762,7 +766,7 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
       *reinterpret_cast<bf16x8*>(Vh + row * LDV + col) = h;
       *reinterpret_cast<bf16x8*>(Vl + row * LDV + col) = l;
     }
-    if (b0 + 2 * C < s1) prefetch(r, b0 + 2 * C);
+    prefetch(r, b0 + 2 * C);
     __syncthreads();
 
     const float fa = __expf(Ab);
@@ -786,12 +790,16 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
     }
     Aseg += Ab;
   };
+  // Every prefetch and tile is unconditional: tiles past s1 read zeros (k, v
+  // and log_a alike, so they add nothing and decay by exp(0)).  With a fixed
+  // count of loads per tile the wait for a tile's registers leaves the
+  // following tile's loads in flight.
   Regs ra, rb;
   prefetch(ra, s0);
-  if (s0 + C < s1) prefetch(rb, s0 + C);
+  prefetch(rb, s0 + C);
   for (int b0 = s0; b0 < s1; b0 += 2 * C) {
     tile(ra, 0, b0);
-    if (b0 + C < s1) tile(rb, 1, b0 + C);
+    tile(rb, 1, b0 + C);
   }
   // element r of S[t] is dk 64hh + 32(t>>1) + 8g4 + 4(t&1) + r, column c0 + li
   float* __restrict__ Tout =
