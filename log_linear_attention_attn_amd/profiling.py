@@ -1,6 +1,7 @@
 """Turn rocprofv3 CSV output into the per-kernel summaries kept under profiles/.
 
     python -m log_linear_attention_attn_amd.profiling stats  <kernel_stats.csv>  [--title T] [--command C]
+    python -m log_linear_attention_attn_amd.profiling trace  <kernel_trace.csv>
     python -m log_linear_attention_attn_amd.profiling traffic --fetch <dir> --write <dir>
            --copy-fetch <dir> --copy-write <dir> --copy-bytes N --kernel NAME --workload W --command C
 
@@ -84,11 +85,40 @@ def stats(path: str) -> list[dict]:
     return out
 
 
+def trace(path: str, context: str | None = None) -> list[dict]:
+    """Per (kernel, grid size) dispatch count and mean / median duration from
+    a rocprofv3 kernel_trace.csv: one bench run times several workloads with
+    the same kernels, and the grid tells their launches apart.  With context
+    (a kernel-name substring), dispatches are further keyed by the grid of the
+    latest dispatch of that kernel before them (e.g. the segment-state kernel,
+    whose grid differs between the workloads a sweep kernel serves)."""
+    groups: dict[tuple, list[float]] = {}
+    with open(path) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+    ctx = 0
+    for r in rows:
+        gx = int(r["Grid_Size_X"])
+        if context and context in r["Kernel_Name"]:
+            ctx = gx
+        key = (r["Kernel_Name"], gx, int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]),
+               int(r["Workgroup_Size_X"]), ctx if context else 0)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = []
+    for (name, gx, gy, gz, wx, cg), d in groups.items():
+        out.append({"name": name, "grid": (gx, gy, gz), "block": wx, "context_grid": cg, "calls": len(d),
+                    "mean_us": statistics.fmean(d), "median_us": statistics.median(d), "total_us": sum(d)})
+    out.sort(key=lambda r: -r["total_us"])
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
+    tr.add_argument("--context")
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write", "kernel", "workload", "command"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
@@ -96,7 +126,13 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--out")
     args = ap.parse_args(argv)
-    if args.mode == "stats":
+    if args.mode == "trace":
+        for r in trace(args.csv, args.context):
+            g = "x".join(str(v) for v in r["grid"])
+            c = f" after {args.context} grid {r['context_grid']}" if args.context else ""
+            print(f"{r['calls']:6d}  mean {r['mean_us']:9.2f} us  median {r['median_us']:9.2f} us  "
+                  f"grid {g:>16s} block {r['block']:4d}  {r['name'][:80]}{c}")
+    elif args.mode == "stats":
         for r in stats(args.csv):
             print(f"{r['calls']:6d}  {r['avg_ns'] / 1e3:10.2f} us  {r['pct']:6.2f}%  {r['name'][:110]}")
     else:
