@@ -50,6 +50,12 @@ struct FwdArgs {
   // power-of-two exponents [BH][nseg][8 waves] (node_pack_kernel)
   const void* node16 = nullptr;
   const int* node_exp = nullptr;
+  // backward use (dQ as the forward of (dO, v, k)): the forward's own q
+  // [BH][T][dv] bf16 and the chunk-level dlambda partials
+  // [dv / 64][BH][T][nslot] this sweep writes (one part per 64-column group)
+  const void* qo = nullptr;
+  float* dlam_part = nullptr;
+  int accum = 0;  // add to `out` instead of writing it (the second of two passes)
 };
 
 struct HandoffArgs {
@@ -79,6 +85,11 @@ struct BwdArgs {
   int BH, T, dk, dv, L;
   int nslot;           // chunk-level Fenwick bits = bit_length(N - 1)
   int G = 1;  // heads per q/k head: q and k of head bh are row bh / G
+  // dQ and the chunk-level dlambda partials already formed by the
+  // register-state sweep (launch_sweep_rs_dlam): the backward then skips its
+  // own dQ sweep and sums dlam_parts partials per (t, level)
+  int dq_done = 0;
+  int dlam_parts = 0;
 };
 
 struct SegArgs {
@@ -178,6 +189,10 @@ int launch_sweep_wide(const FwdArgs& a, hipStream_t s);
 size_t node_pack_bytes(int BH, int nseg);
 int launch_node_pack(const NodeArgs& a, void* node16, int* node_exp, int BH, hipStream_t s);
 int rs_max_slots();
+// dQ of the backward as the forward of (dO as bf16, v, k) plus the chunk-level
+// dlambda partials (FwdArgs::qo, dlam_part); register-state shapes only
+int launch_sweep_rs_dlam(const FwdArgs& a, int nblocks, hipStream_t stream);
+int rs_dlam_lds_bytes(int L, int nslot);
 int rs_lds_bytes(int L, int nslot);
 int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t s);
 int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t s);
@@ -186,6 +201,9 @@ int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot);
 int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s);
+// fp32 -> bf16 hi + lo (hi = x rounded to nearest even, lo = x - hi rounded)
+// of n elements, n a multiple of 8 and every buffer 16-byte aligned
+int launch_split_bf16(const float* in, void* hi, void* lo, long long n, hipStream_t s);
 // dV / dK reverse sweep on bf16 matrix cores (bf16 inputs, C = 64)
 bool bwd_kv16_ok(const BwdArgs& a);
 int launch_bwd_kv16(const BwdArgs& a, hipStream_t s);

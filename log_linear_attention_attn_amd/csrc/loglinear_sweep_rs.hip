@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "ll_device.h"
 #include "ll_internal.h"
@@ -64,8 +65,15 @@ __host__ __device__ constexpr int nsl_for(int nslot) { return nslot <= 8 ? 8 : 1
 // row weights read all inter-chunk levels of the instantiation, which a short
 // sequence's lambda may lack; the slack keeps those (discarded) reads in bounds.
 __host__ __device__ inline int lds_bytes(int L, int nslot) { return lam_off(nsl_for(nslot)) + (C * L + 16) * 4; }
+// Backward variant (dQ as the forward of (dO, v, k), with the chunk-level
+// dlambda): the forward's q tile [64][LDQO] bf16 follows lambda; the row
+// weight region holds the per-wave dlambda partials [8][64 rows][slots].
+constexpr int LDQO = 64 + 8;
+__host__ __device__ inline int qo_off(int L, int nslot) { return (lds_bytes(L, nslot) + 15) & ~15; }
+__host__ __device__ inline int lds_bytes_dlam(int L, int nslot) { return qo_off(L, nslot) + C * LDQO * 2; }
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef _Float16 __attribute__((ext_vector_type(4))) f16x4;
 typedef unsigned short __attribute__((ext_vector_type(2))) u16x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -159,6 +167,26 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ bf16x8 load_b128(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+typedef unsigned int __attribute__((ext_vector_type(4))) u32x4;
+// x + x of the lane 16 (resp. 32) apart, in every lane, through the gfx950
+// row-pair swaps (v_permlane16_swap / v_permlane32_swap with both operands x:
+// the two results hold the lane's own half and the partner half, lane layout
+// checked by an on-GPU probe)
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ f32x4 load_f4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// four consecutive fp32 outputs as one 16-byte store (dropped past the range)
+__device__ __forceinline__ void store_row(rsrc_t r, f32x4 x, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
 
 }  // namespace rs
 
@@ -168,7 +196,16 @@ __device__ __forceinline__ bf16x8 load_b128(rsrc_t r, uint32_t off) {
 // through LDS; each wave finishes the output of two row tiles.
 // EMIT: also write the prefill decode states (a separate instantiation, so the
 // plain forward does not carry the extra live registers).
-template <int NSLOT, bool EMIT>
+// DLAM: the backward's dQ sweep.  The kernel then runs on (q, k, v) = (dO as
+// bf16, v, k) of the forward, so `out` is dQ, and it also forms the
+// chunk-level dlambda: dlambda[t, log2C+1+b] = q_t . (level-b read of row t),
+// the read being exactly the per-level product this sweep computes for dQ
+// before its lambda weight.  Its products are taken transposed (lane = row,
+// four consecutive columns), so the dot of a row's read with the forward's q
+// over a wave's 16 columns is four products per lane and two row-pair swaps;
+// the eight waves' partials are summed through LDS after the next barrier and
+// written per 64-column group.
+template <int NSLOT, bool EMIT, bool DLAM = false>
 __global__ void __launch_bounds__(512)
 fwd_rs_kernel(FwdArgs a) {
   using namespace rs;
@@ -180,6 +217,7 @@ fwd_rs_kernel(FwdArgs a) {
   f32x4* Xc = reinterpret_cast<f32x4*>(smem + XC_OFF);    // [wave][2][lane]
   float* qmax_s = reinterpret_cast<float*>(smem + QM_OFF);
   float* lam_s = reinterpret_cast<float*>(smem + lam_off(NSLOT));
+  _Float16* Qo = reinterpret_cast<_Float16*>(smem + ((lam_off(NSLOT) + (C * a.L + 16) * 4 + 15) & ~15));  // DLAM only
 
   const int D = a.dv >> 6;  // 64-column groups
   const int id = blockIdx.x;
@@ -207,6 +245,7 @@ fwd_rs_kernel(FwdArgs a) {
   const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
   const rsrc_t lamr = make_rsrc(a.lam + bhT * L, T * L * 4);
   const rsrc_t outr = make_rsrc(a.out + bhT * dv, T * dv * 4);
+  const rsrc_t qor = DLAM ? make_rsrc(static_cast<const bf16*>(a.qo) + bhT * dv, T * dv * 2) : outr;
   // row tiles whose output this wave finishes, and the two it hands over
   const int own0 = hh ? 1 : 0, own1 = hh ? 2 : 3;
   const int oth0 = hh ? 0 : 1, oth1 = hh ? 3 : 2;
@@ -260,7 +299,7 @@ fwd_rs_kernel(FwdArgs a) {
   }
 
   // ---- register prefetch of one chunk ----------------------------------
-  bf16x8 pq[2], pk[2], pv;
+  bf16x8 pq[2], pk[2], pv, pqo;
   float plam[3];  // lambda words 2*tid, 2*tid+1 and, for L > 16, 1024+tid of the chunk
   float pla;
   // per-thread parts of the chunk loads' offsets; columns past dk (padded
@@ -291,6 +330,7 @@ fwd_rs_kernel(FwdArgs a) {
       pk[i] = load_b128(kr, off_qk[i] + cq);
     }
     pv = load_b128(vr, off_v + tok0 * dv * 2);
+    if constexpr (DLAM) pqo = load_b128(qor, off_v + tok0 * dv * 2);
   };
 
   prefetch(n0);
@@ -304,6 +344,23 @@ fwd_rs_kernel(FwdArgs a) {
     dlev[r] = level_of(li, 4 * g4 + r);
     dmask |= (4 * g4 + r <= li ? 1u : 0u) << r;
   }
+  // DLAM: chunk nc's dlambda partials (written by the eight waves before the
+  // last barrier) summed in wave order and stored for its live levels, zero
+  // for the others; one thread per (row, slot), slots contiguous in memory
+  auto dlam_flush = [&](int nc) {
+    const float* dl = reinterpret_cast<const float*>(smem + LW_OFF);
+    for (int e = tid; e < C * NSLOT; e += NTH) {
+      const int row = e / NSLOT, b = e - row * NSLOT;
+      const int t = nc * C + row;
+      if (b >= a.nslot || t >= T) continue;
+      float x = 0.f;
+      if ((nc >> b) & 1) {
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) x += dl[(ww * C + row) * NSLOT + b];
+      }
+      a.dlam_part[(((size_t)dg * a.BH + bh) * T + t) * a.nslot + b] = x;
+    }
+  };
   f32x4 O0, O1;      // this wave's two output row tiles, written after the next barrier
   float Aprev = 0.f;  // total log decay of the previous chunk
   float* lw = reinterpret_cast<float*>(smem + LW_OFF) + w * (NSLOT * C);  // this wave's row weights
@@ -332,6 +389,12 @@ fwd_rs_kernel(FwdArgs a) {
       if (lane == 0) qmax_s[w] = qmw;
     }
     *reinterpret_cast<bf16x8*>(Vs + (tid >> 3) * LDV + (tid & 7) * 8) = pv;
+    if constexpr (DLAM) {  // the forward's q as fp16 (exact for bf16 values in range)
+      f16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(static_cast<float>(pqo[e]));
+      *reinterpret_cast<f16x8*>(Qo + (tid >> 3) * LDQO + (tid & 7) * 8) = h;
+    }
     if (tid * 2 < C * L) {  // C * L is even
       lam_s[tid * 2] = plam[0];
       lam_s[tid * 2 + 1] = plam[1];
@@ -353,13 +416,27 @@ fwd_rs_kernel(FwdArgs a) {
       const f32x4 x0 = Xc[(partner * 2 + 0) * 64 + lane];
       const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
       const int tp = tok0 - C;
+      if constexpr (DLAM) {
+        // transposed tiles: row li, columns c0 + 4 g4 .. + 3
+        const uint32_t o0 = ((tp + 16 * own0 + li) * dv + dv0 + c0 + 4 * g4) * 4;
+        const uint32_t o1 = ((tp + 16 * own1 + li) * dv + dv0 + c0 + 4 * g4) * 4;
+        f32x4 y0 = O0 + x0, y1 = O1 + x1;
+        if (a.accum) {
+          y0 += load_f4(outr, o0);
+          y1 += load_f4(outr, o1);
+        }
+        store_row(outr, y0, o0);
+        store_row(outr, y1, o1);
+        dlam_flush(n - 1);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // rows past T fall outside the output range and are dropped
-        const int t0 = tp + 16 * own0 + 4 * g4 + r;
-        const int t1 = tp + 16 * own1 + 4 * g4 + r;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), outr, (t0 * dv + dv0 + c0 + li) * 4, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          // rows past T fall outside the output range and are dropped
+          const int t0 = tp + 16 * own0 + 4 * g4 + r;
+          const int t1 = tp + 16 * own1 + 4 * g4 + r;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), outr, (t0 * dv + dv0 + c0 + li) * 4, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
+        }
       }
     }
 
@@ -459,7 +536,7 @@ fwd_rs_kernel(FwdArgs a) {
     // level b (lane = row): lambda[row, log2C+1+b] * exp(cl_row + dec_b) (decay
     // from the bucket's end to the row) * 2^eq (fp16 Q scale) * 2^eg[b] (this
     // wave's state scale).  Written and read by this wave only.
-    {
+    if constexpr (!DLAM) {
       const float ecl = __expf(cl) * exp2_int(eq);
       float lv[NSLOT];
 #pragma unroll
@@ -482,21 +559,63 @@ fwd_rs_kernel(FwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
           qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 * ks + 8 * g4);
+      if constexpr (DLAM) {
+        // lane li is row 16 mi + li, element r column c0 + 4 g4 + r.  Row
+        // factor exp(cl_row) 2^eq; the forward's q of the row and columns.
+        float ecr[4];
+        f16x4 qof[4];
 #pragma unroll
-      for (int b = 0; b < NSLOT; ++b) {
-        if ((n >> b) & 1) {
-          f32x4 acc[4];
+        for (int mi = 0; mi < 4; ++mi) {
+          ecr[mi] = exp2f_fast(cl_s[16 * mi + li]) * exp2_int(eq);
+          qof[mi] = *reinterpret_cast<const f16x4*>(Qo + (16 * mi + li) * LDQO + c0 + 4 * g4);
+        }
+        float* dlw = reinterpret_cast<float*>(smem + LW_OFF) + w * (C * NSLOT);
 #pragma unroll
-          for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NSLOT; ++b) {
+          if ((n >> b) & 1) {
+            f32x4 acc[4];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
+            for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            const f32x4 wv = *reinterpret_cast<const f32x4*>(lw + b * C + 16 * mi + 4 * g4);
+              for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(G[b][ks], qa[mi][ks], acc[mi]);
+            const float fb = __expf(dec[b]) * exp2_int(eg[b]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Op[mi][r] += wv[r] * acc[mi][r];
+            for (int mi = 0; mi < 4; ++mi) {
+              const float wd = ecr[mi] * fb;  // the level's read of this row: wd * acc
+              const float wq = lam_s[(16 * mi + li) * L + LOGC + 1 + b] * wd;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) Op[mi][r] += wq * acc[mi][r];
+              // dot of the row's read with the forward's q over this wave's
+              // 16 columns: four products here, the other twelve in the
+              // lanes li + 16, + 32, + 48 (same row, next column groups)
+              float pd = 0.f;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) pd += static_cast<float>(qof[mi][r]) * acc[mi][r];
+              pd = xor16_sum(pd);
+              pd = xor32_sum(pd);
+              if (g4 == 0) dlw[(16 * mi + li) * NSLOT + b] = pd * wd;
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NSLOT; ++b) {
+          if ((n >> b) & 1) {
+            f32x4 acc[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+              for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(qa[mi][ks], G[b][ks], acc[mi]);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+              const f32x4 wv = *reinterpret_cast<const f32x4*>(lw + b * C + 16 * mi + 4 * g4);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) Op[mi][r] += wv[r] * acc[mi][r];
+            }
           }
         }
       }
@@ -513,13 +632,24 @@ fwd_rs_kernel(FwdArgs a) {
     for (int ks = 0; ks < 2; ++ks) {
       const bf16* v0 = Vs + (32 * ks + 4 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
       const bf16x8 vb = cat(tr_read(v0), tr_read(v0 + 16 * LDV));
-      if (2 * ks <= own0) {
-        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 0) * 64 + lane], vb, O0);
-        O0 = mma(Ps[((own0 * 2 + ks) * 2 + 1) * 64 + lane], vb, O0);
-      }
-      if (2 * ks <= own1) {
-        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 0) * 64 + lane], vb, O1);
-        O1 = mma(Ps[((own1 * 2 + ks) * 2 + 1) * 64 + lane], vb, O1);
+      if constexpr (DLAM) {  // transposed tiles
+        if (2 * ks <= own0) {
+          O0 = mma(vb, Ps[((own0 * 2 + ks) * 2 + 0) * 64 + lane], O0);
+          O0 = mma(vb, Ps[((own0 * 2 + ks) * 2 + 1) * 64 + lane], O0);
+        }
+        if (2 * ks <= own1) {
+          O1 = mma(vb, Ps[((own1 * 2 + ks) * 2 + 0) * 64 + lane], O1);
+          O1 = mma(vb, Ps[((own1 * 2 + ks) * 2 + 1) * 64 + lane], O1);
+        }
+      } else {
+        if (2 * ks <= own0) {
+          O0 = mma(Ps[((own0 * 2 + ks) * 2 + 0) * 64 + lane], vb, O0);
+          O0 = mma(Ps[((own0 * 2 + ks) * 2 + 1) * 64 + lane], vb, O0);
+        }
+        if (2 * ks <= own1) {
+          O1 = mma(Ps[((own1 * 2 + ks) * 2 + 0) * 64 + lane], vb, O1);
+          O1 = mma(Ps[((own1 * 2 + ks) * 2 + 1) * 64 + lane], vb, O1);
+        }
       }
     }
 
@@ -628,12 +758,25 @@ fwd_rs_kernel(FwdArgs a) {
     const f32x4 x0 = Xc[(partner * 2 + 0) * 64 + lane];
     const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
     const int tp = (n1 - 1) * C;
+    if constexpr (DLAM) {
+      const uint32_t o0 = ((tp + 16 * own0 + li) * dv + dv0 + c0 + 4 * g4) * 4;
+      const uint32_t o1 = ((tp + 16 * own1 + li) * dv + dv0 + c0 + 4 * g4) * 4;
+      f32x4 y0 = O0 + x0, y1 = O1 + x1;
+      if (a.accum) {
+        y0 += load_f4(outr, o0);
+        y1 += load_f4(outr, o1);
+      }
+      store_row(outr, y0, o0);
+      store_row(outr, y1, o1);
+      dlam_flush(n1 - 1);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t0 = tp + 16 * own0 + 4 * g4 + r;
-      const int t1 = tp + 16 * own1 + 4 * g4 + r;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), outr, (t0 * dv + dv0 + c0 + li) * 4, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        const int t0 = tp + 16 * own0 + 4 * g4 + r;
+        const int t1 = tp + 16 * own1 + 4 * g4 + r;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), outr, (t0 * dv + dv0 + c0 + li) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), outr, (t1 * dv + dv0 + c0 + li) * 4, 0, 0);
+      }
     }
   }
 
@@ -827,6 +970,25 @@ int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t stream) {
 }
 
 int rs_max_slots() { return 10; }
+
+int rs_dlam_lds_bytes(int L, int nslot) { return rs::lds_bytes_dlam(L, nslot); }
+
+int launch_sweep_rs_dlam(const FwdArgs& a, int nblocks, hipStream_t stream) {
+  const int bytes = rs::lds_bytes_dlam(a.L, a.nslot);
+  if (a.nslot > 10 || a.L > 24 || bytes > kMaxLds || !a.qo || !a.dlam_part || a.G != 1 || a.st_out)
+    return LL_ERR_UNSUPPORTED;
+  const size_t row_bytes = std::max({(size_t)a.dk * 2, (size_t)a.dv * 4, (size_t)a.L * 4});
+  if ((size_t)(a.T + 2 * rs::C) * row_bytes >= (size_t)1 << 31) return LL_ERR_UNSUPPORTED;
+  static std::atomic<uint64_t> raised8{0}, raised10{0};
+  if (a.nslot > 8) {
+    if (!raise_lds_limit(reinterpret_cast<const void*>(&fwd_rs_kernel<10, false, true>), raised10)) return LL_ERR_HIP;
+    hipLaunchKernelGGL((fwd_rs_kernel<10, false, true>), dim3(nblocks), dim3(512), bytes, stream, a);
+  } else {
+    if (!raise_lds_limit(reinterpret_cast<const void*>(&fwd_rs_kernel<8, false, true>), raised8)) return LL_ERR_HIP;
+    hipLaunchKernelGGL((fwd_rs_kernel<8, false, true>), dim3(nblocks), dim3(512), bytes, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+}
 
 int rs_lds_bytes(int L, int nslot) { return rs::lds_bytes(L, nslot); }
 
