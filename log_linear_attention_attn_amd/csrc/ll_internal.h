@@ -55,7 +55,6 @@ struct FwdArgs {
   // [dv / 64][BH][T][nslot] this sweep writes (one part per 64-column group)
   const void* qo = nullptr;
   float* dlam_part = nullptr;
-  int accum = 0;  // add to `out` instead of writing it (the second of two passes)
 };
 
 struct HandoffArgs {
@@ -189,7 +188,7 @@ int launch_sweep_wide(const FwdArgs& a, hipStream_t s);
 size_t node_pack_bytes(int BH, int nseg);
 int launch_node_pack(const NodeArgs& a, void* node16, int* node_exp, int BH, hipStream_t s);
 int rs_max_slots();
-// dQ of the backward as the forward of (dO as bf16, v, k) plus the chunk-level
+// dQ of the backward as the forward of (dO in fp32, v, k) plus the chunk-level
 // dlambda partials (FwdArgs::qo, dlam_part); register-state shapes only
 int launch_sweep_rs_dlam(const FwdArgs& a, int nblocks, hipStream_t stream);
 int rs_dlam_lds_bytes(int L, int nslot);
@@ -201,9 +200,6 @@ int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot);
 int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s);
-// fp32 -> bf16 hi + lo (hi = x rounded to nearest even, lo = x - hi rounded)
-// of n elements, n a multiple of 8 and every buffer 16-byte aligned
-int launch_split_bf16(const float* in, void* hi, void* lo, long long n, hipStream_t s);
 // dV / dK reverse sweep on bf16 matrix cores (bf16 inputs, C = 64)
 bool bwd_kv16_ok(const BwdArgs& a);
 int launch_bwd_kv16(const BwdArgs& a, hipStream_t s);

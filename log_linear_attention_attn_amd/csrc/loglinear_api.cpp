@@ -366,21 +366,19 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   // dQ through the register-state forward sweep run on (dO, v, k): dQ_t =
   // sum_s M[t,s] (dO_t . v_s) k_s is the forward with q, k, v taken as dO, v,
   // k, and the same sweep forms the chunk-level dlambda (the dot of each
-  // level's read with q).  Both are linear in dO, so dO is split into bf16
-  // hi + lo and swept twice (the segment pre-pass of (v, k) is shared; the
-  // second pass adds to dQ and writes its own dlambda partials), which keeps
-  // dO to ~2^-16 where one bf16 rounding measured up to 3e-2 of the RMS.
-  // Shapes: bf16, C = 64, q / k per head, the register-state sweep's
-  // (contraction dv in (64, 128], dk a multiple of 64).
+  // level's read with q).  Its variant reads dO in fp32 and runs the score
+  // tiles and the level reads on fp16 with a per-row power-of-two scale (one
+  // bf16 rounding of dO measured up to 3e-2 of the RMS).  Shapes: bf16,
+  // C = 64, q / k per head, the register-state sweep's (contraction dv in
+  // (64, 128], dk a multiple of 64, at most 256 chunks).
   FwdPlan pd{};
   bool dq_rs = dtype == LL_BF16 && C == 64 && G == 1 && dv > 64 && dv <= 128 && dk % 64 == 0 &&
-               p.nslot <= ll::rs_max_slots() && 2 * (dk / 64) <= dk / 16;
+               p.nslot <= 8;
   if (dq_rs) dq_rs = plan_fwd(B, H, T, dv, dk, C, -1, &pd) == LL_OK &&
                      ll::rs_dlam_lds_bytes(pd.L, pd.nslot) <= ll::kMaxLds;
-  const size_t dob = dq_rs ? align256((size_t)p.BH * T * dv * 2) : 0;
   const size_t fws = dq_rs ? pd.ws_total : 0;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, part + dcb + 2 * per_head + 2 * dob + fws, stream) != hipSuccess) return LL_ERR_HIP;
+  if (hipMallocAsync(&ws, part + dcb + 2 * per_head + fws, stream) != hipSuccess) return LL_ERR_HIP;
   char* wsb = static_cast<char*>(ws);
   float* dq_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb) : dq;
   float* dk_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb + per_head) : dk_out;
@@ -388,16 +386,12 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
                 reinterpret_cast<float*>(wsb), reinterpret_cast<double*>(wsb + part),
                 p.BH, T, dk, dv, p.L, p.nslot, G};
   if (dq_rs) {
-    char* dw = wsb + part + dcb + 2 * per_head;
-    void* do_hi = dw;
-    void* do_lo = dw + dob;
-    char* fw = dw + 2 * dob;
-    st = ll::launch_split_bf16(dout, do_hi, do_lo, (long long)p.BH * T * dv, stream);
+    char* fw = wsb + part + dcb + 2 * per_head;
     float* blk_state = reinterpret_cast<float*>(fw);
     float* nodes = pd.ws_total ? reinterpret_cast<float*>(fw + pd.ws_state) : nullptr;
     float* seg_decay = pd.ws_total ? reinterpret_cast<float*>(fw + pd.ws_state + pd.ws_nodes) : nullptr;
     float* blk_decay = pd.ws_total ? reinterpret_cast<float*>(fw + pd.ws_state + pd.ws_nodes + pd.ws_decay) : nullptr;
-    if (st == LL_OK && pd.nseg > 1) {
+    if (pd.nseg > 1) {
       // segment states of the swapped problem: keys v, values k
       ll::SegArgs sa{v, k, log_a, blk_state, blk_decay, pd.BH, T, dv, dk, C, pd.blk_log2, pd.nblk1, 1};
       st = ll::launch_seg_state_rs(sa, pd.BH, stream);
@@ -410,17 +404,15 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
     const long long pairs = (long long)pd.BH * pd.nseg;
     const long long nblocks = ((pairs + 7) / 8) * 8 * (dk / 64);
     if (nblocks > 0x7fffffffLL) st = LL_ERR_UNSUPPORTED;
-    const size_t pstride = (size_t)(dk / 64) * p.BH * T * (p.nslot > 0 ? p.nslot : 1);
-    for (int pass = 0; pass < 2 && st == LL_OK; ++pass) {
-      ll::FwdArgs fa{pass ? do_lo : do_hi, v, k, log_a, lambda, dq_h, nodes, seg_decay, pd.BH, T, dv, dk, pd.L,
+    if (st == LL_OK) {
+      ll::FwdArgs fa{dout, v, k, log_a, lambda, dq_h, nodes, seg_decay, pd.BH, T, dv, dk, pd.L,
                      pd.seg_log2, pd.nseg, pd.nslot, nullptr, 0, 1};
       fa.qo = q;
-      fa.dlam_part = a.dlam_part + pass * pstride;
-      fa.accum = pass;
+      fa.dlam_part = a.dlam_part;
       st = ll::launch_sweep_rs_dlam(fa, static_cast<int>(nblocks), stream);
     }
     a.dq_done = 1;
-    a.dlam_parts = 2 * (dk / 64);
+    a.dlam_parts = dk / 64;
   }
   if (st == LL_OK) st = ll::launch_bwd(dtype, C, a, stream);
   if (st == LL_OK && G > 1) {

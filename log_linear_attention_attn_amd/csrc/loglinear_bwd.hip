@@ -757,39 +757,6 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
-// fp32 -> bf16 hi + lo, eight elements (two 16-byte loads, two 16-byte
-// stores) per thread
-__global__ void __launch_bounds__(256) split_bf16_kernel(const float* __restrict__ in, bf16* __restrict__ hi,
-                                                         bf16* __restrict__ lo, long long n8) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 x0 = reinterpret_cast<const f32x4*>(in)[2 * i];
-  const f32x4 x1 = reinterpret_cast<const f32x4*>(in)[2 * i + 1];
-  bf16x8 h, l;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bf16 a, b;
-    split_bf16(e < 4 ? x0[e] : x1[e - 4], a, b);
-    h[e] = a;
-    l[e] = b;
-  }
-  reinterpret_cast<bf16x8*>(hi)[i] = h;
-  reinterpret_cast<bf16x8*>(lo)[i] = l;
-}
-
-int launch_split_bf16(const float* in, void* hi, void* lo, long long n, hipStream_t s) {
-  if (n % 8 != 0 ||
-      ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(hi) | reinterpret_cast<uintptr_t>(lo)) & 15))
-    return LL_ERR_SHAPE;
-  const long long n8 = n / 8;
-  if (n8 == 0) return LL_OK;
-  const long long blocks = (n8 + 255) / 256;
-  if (blocks > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(split_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, in,
-                     static_cast<bf16*>(hi), static_cast<bf16*>(lo), n8);
-  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
-}
-
 int launch_bwd(int dtype, int C, const BwdArgs& a, hipStream_t s) {
   if (dtype == LL_BF16) {
     switch (C) {

@@ -70,7 +70,7 @@ __host__ __device__ inline int lds_bytes(int L, int nslot) { return lam_off(nsl_
 // weight region holds the per-wave dlambda partials [8][64 rows][slots].
 constexpr int LDQO = 64 + 8;
 __host__ __device__ inline int qo_off(int L, int nslot) { return (lds_bytes(L, nslot) + 15) & ~15; }
-__host__ __device__ inline int lds_bytes_dlam(int L, int nslot) { return qo_off(L, nslot) + C * LDQO * 2; }
+__host__ __device__ inline int lds_bytes_dlam(int L, int nslot) { return qo_off(L, nslot) + C * LDQO * 2 + C * 4; }
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
 typedef _Float16 __attribute__((ext_vector_type(4))) f16x4;
@@ -180,9 +180,6 @@ __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ f32x4 load_f4(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 // four consecutive fp32 outputs as one 16-byte store (dropped past the range)
 __device__ __forceinline__ void store_row(rsrc_t r, f32x4 x, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
@@ -196,8 +193,8 @@ __device__ __forceinline__ void store_row(rsrc_t r, f32x4 x, uint32_t off) {
 // through LDS; each wave finishes the output of two row tiles.
 // EMIT: also write the prefill decode states (a separate instantiation, so the
 // plain forward does not carry the extra live registers).
-// DLAM: the backward's dQ sweep.  The kernel then runs on (q, k, v) = (dO as
-// bf16, v, k) of the forward, so `out` is dQ, and it also forms the
+// DLAM: the backward's dQ sweep.  The kernel then runs on (q, k, v) = (dO in
+// fp32, v, k) of the forward, so `out` is dQ, and it also forms the
 // chunk-level dlambda: dlambda[t, log2C+1+b] = q_t . (level-b read of row t),
 // the read being exactly the per-level product this sweep computes for dQ
 // before its lambda weight.  Its products are taken transposed (lane = row,
@@ -218,6 +215,7 @@ fwd_rs_kernel(FwdArgs a) {
   float* qmax_s = reinterpret_cast<float*>(smem + QM_OFF);
   float* lam_s = reinterpret_cast<float*>(smem + lam_off(NSLOT));
   _Float16* Qo = reinterpret_cast<_Float16*>(smem + ((lam_off(NSLOT) + (C * a.L + 16) * 4 + 15) & ~15));  // DLAM only
+  int* er_s = reinterpret_cast<int*>(Qo + C * LDQO);  // DLAM: per-row fp16 scale exponent of q
 
   const int D = a.dv >> 6;  // 64-column groups
   const int id = blockIdx.x;
@@ -239,7 +237,9 @@ fwd_rs_kernel(FwdArgs a) {
   const size_t bhT = (size_t)bh * T;
   // per-(b,h) slices; every slice is < 2^31 bytes (checked by the launcher)
   const size_t qkT = (size_t)(bh / a.G) * T;
-  const rsrc_t qr = make_rsrc(static_cast<const bf16*>(a.q) + qkT * dk, T * dk * 2);
+  // DLAM: "q" is dO in fp32
+  const rsrc_t qr = DLAM ? make_rsrc(static_cast<const float*>(a.q) + qkT * dk, T * dk * 4)
+                         : make_rsrc(static_cast<const bf16*>(a.q) + qkT * dk, T * dk * 2);
   const rsrc_t kr = make_rsrc(static_cast<const bf16*>(a.k) + qkT * dk, T * dk * 2);
   const rsrc_t vr = make_rsrc(static_cast<const bf16*>(a.v) + bhT * dv, T * dv * 2);
   const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
@@ -300,6 +300,7 @@ fwd_rs_kernel(FwdArgs a) {
 
   // ---- register prefetch of one chunk ----------------------------------
   bf16x8 pq[2], pk[2], pv, pqo;
+  f32x4 pqf[2][2];  // DLAM: the fp32 q values of pq
   float plam[3];  // lambda words 2*tid, 2*tid+1 and, for L > 16, 1024+tid of the chunk
   float pla;
   // per-thread parts of the chunk loads' offsets; columns past dk (padded
@@ -326,7 +327,14 @@ fwd_rs_kernel(FwdArgs a) {
     const uint32_t cq = tok0 * dk * 2;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      pq[i] = load_b128(qr, off_qk[i] + cq);
+      if constexpr (DLAM) {
+        const uint32_t o = off_qk[i] & kOutOfRange ? kOutOfRange : 2 * (off_qk[i] + cq);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          pqf[i][h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, o + 16 * h, 0, 0));
+      } else {
+        pq[i] = load_b128(qr, off_qk[i] + cq);
+      }
       pk[i] = load_b128(kr, off_qk[i] + cq);
     }
     pv = load_b128(vr, off_v + tok0 * dv * 2);
@@ -371,19 +379,49 @@ fwd_rs_kernel(FwdArgs a) {
     float* cl_s = reinterpret_cast<float*>(smem + CL_OFF) + par * (2 * C);
     float* esf_s = cl_s + C;
     // ---------------- stage: registers -> LDS ------------------------------
-    u16x2 qm = {0, 0};  // max |q| of this thread's values, as bf16 magnitude bits
+    if constexpr (DLAM) {
+      // the score tiles run in fp16: K goes to the bf16 Q tile's place as
+      // fp16 (exact for bf16 values in range); q (fp32 dO) is scaled per row
+      // by a power of two so the row's max |q| sits at 2^14..2^15 (the 16
+      // lanes of a DPP row hold one row) and its exponent goes to er_s
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
-      *reinterpret_cast<bf16x8*>(Qs + row * LDQ + col) = pq[i];
-      *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
-      const uint4 bits = __builtin_bit_cast(uint4, pq[i]);
-      qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.x & 0x7fff7fffu));
-      qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.y & 0x7fff7fffu));
-      qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.z & 0x7fff7fffu));
-      qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.w & 0x7fff7fffu));
-    }
-    {
+      for (int i = 0; i < 2; ++i) {
+        const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
+        *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
+        f16x8 hk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hk[e] = static_cast<_Float16>(static_cast<float>(pk[i][e]));
+        *reinterpret_cast<f16x8*>(Qs + row * LDQ + col) = hk;
+        float qf = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qf = fmaxf(qf, fabsf(pqf[i][h][e]));
+        qf = dpp_max<0x121>(qf);  // row_ror:1, 2, 4, 8: the row's max in all 16 lanes
+        qf = dpp_max<0x122>(qf);
+        qf = dpp_max<0x124>(qf);
+        qf = dpp_max<0x128>(qf);
+        const int e2 = scale_exp(qf);
+        const float sc = exp2_int(-e2);
+        f16x8 hq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hq[e] = static_cast<_Float16>(pqf[i][e >> 2][e & 3] * sc);
+        *reinterpret_cast<f16x8*>(Qh + row * LDQ + col) = hq;
+        if ((tid & 15) == 0) er_s[row] = e2;
+      }
+    } else {
+      u16x2 qm = {0, 0};  // max |q| of this thread's values, as bf16 magnitude bits
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int v = tid + NTH * i, row = v >> 4, col = (v & 15) * 8;
+        *reinterpret_cast<bf16x8*>(Qs + row * LDQ + col) = pq[i];
+        *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = pk[i];
+        const uint4 bits = __builtin_bit_cast(uint4, pq[i]);
+        qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.x & 0x7fff7fffu));
+        qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.y & 0x7fff7fffu));
+        qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.z & 0x7fff7fffu));
+        qm = __builtin_elementwise_max(qm, __builtin_bit_cast(u16x2, bits.w & 0x7fff7fffu));
+      }
       const unsigned m16 = max(static_cast<unsigned>(qm[0]), static_cast<unsigned>(qm[1]));
       const float qmw = wave_max(__uint_as_float(m16 << 16));
       if (lane == 0) qmax_s[w] = qmw;
@@ -418,15 +456,8 @@ fwd_rs_kernel(FwdArgs a) {
       const int tp = tok0 - C;
       if constexpr (DLAM) {
         // transposed tiles: row li, columns c0 + 4 g4 .. + 3
-        const uint32_t o0 = ((tp + 16 * own0 + li) * dv + dv0 + c0 + 4 * g4) * 4;
-        const uint32_t o1 = ((tp + 16 * own1 + li) * dv + dv0 + c0 + 4 * g4) * 4;
-        f32x4 y0 = O0 + x0, y1 = O1 + x1;
-        if (a.accum) {
-          y0 += load_f4(outr, o0);
-          y1 += load_f4(outr, o1);
-        }
-        store_row(outr, y0, o0);
-        store_row(outr, y1, o1);
+        store_row(outr, O0 + x0, ((tp + 16 * own0 + li) * dv + dv0 + c0 + 4 * g4) * 4);
+        store_row(outr, O1 + x1, ((tp + 16 * own1 + li) * dv + dv0 + c0 + 4 * g4) * 4);
         dlam_flush(n - 1);
       } else {
 #pragma unroll
@@ -442,8 +473,8 @@ fwd_rs_kernel(FwdArgs a) {
 
     // fp16 copy of Q for the Q.G products, scaled by a power of two so the
     // chunk's max |q| sits at 2^14..2^15 (exact for bf16 values in range)
-    int eq;
-    {
+    int eq = 0;
+    if constexpr (!DLAM) {
       float qmx = qmax_s[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) qmx = fmaxf(qmx, qmax_s[i]);
@@ -484,11 +515,18 @@ fwd_rs_kernel(FwdArgs a) {
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
           if (it < ntile) {
-            const bf16x8 ka =
-                *reinterpret_cast<const bf16x8*>(Ks + (16 * kbt[it] + li) * LDQ + 32 * ks + 8 * g4);
-            const bf16x8 qb8 =
-                *reinterpret_cast<const bf16x8*>(Qs + (16 * qbt[it] + li) * LDQ + 32 * ks + 8 * g4);
-            acc[it] = mma(ka, qb8, acc[it]);
+            if constexpr (DLAM) {  // fp16 K copy (in the Q tile's place) and scaled fp16 q
+              const f16x8 kh = *reinterpret_cast<const f16x8*>(reinterpret_cast<const _Float16*>(Qs) +
+                                                               (16 * kbt[it] + li) * LDQ + 32 * ks + 8 * g4);
+              const f16x8 qh = *reinterpret_cast<const f16x8*>(Qh + (16 * qbt[it] + li) * LDQ + 32 * ks + 8 * g4);
+              acc[it] = mma16(kh, qh, acc[it]);
+            } else {
+              const bf16x8 ka =
+                  *reinterpret_cast<const bf16x8*>(Ks + (16 * kbt[it] + li) * LDQ + 32 * ks + 8 * g4);
+              const bf16x8 qb8 =
+                  *reinterpret_cast<const bf16x8*>(Qs + (16 * qbt[it] + li) * LDQ + 32 * ks + 8 * g4);
+              acc[it] = mma(ka, qb8, acc[it]);
+            }
           }
         }
       }
@@ -498,7 +536,8 @@ fwd_rs_kernel(FwdArgs a) {
           const int qb = qbt[it], kb = kbt[it];
           // acc[r] = score(query 16qb+li, key 16kb+4g4+r)
           const int qi = 16 * qb + li;
-          const float clq = cl_s[qi];
+          // DLAM: undo the row's fp16 scale through the decay exponent (base 2)
+          const float clq = DLAM ? cl_s[qi] + static_cast<float>(er_s[qi]) : cl_s[qi];
           const f32x4 clk = *reinterpret_cast<const f32x4*>(cl_s + 16 * kb + 4 * g4);
           f32x4 pv4;
           if (kb < qb) {
@@ -566,7 +605,7 @@ fwd_rs_kernel(FwdArgs a) {
         f16x4 qof[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-          ecr[mi] = exp2f_fast(cl_s[16 * mi + li]) * exp2_int(eq);
+          ecr[mi] = exp2f_fast(cl_s[16 * mi + li]) * exp2_int(er_s[16 * mi + li]);
           qof[mi] = *reinterpret_cast<const f16x4*>(Qo + (16 * mi + li) * LDQO + c0 + 4 * g4);
         }
         float* dlw = reinterpret_cast<float*>(smem + LW_OFF) + w * (C * NSLOT);
@@ -759,15 +798,8 @@ fwd_rs_kernel(FwdArgs a) {
     const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
     const int tp = (n1 - 1) * C;
     if constexpr (DLAM) {
-      const uint32_t o0 = ((tp + 16 * own0 + li) * dv + dv0 + c0 + 4 * g4) * 4;
-      const uint32_t o1 = ((tp + 16 * own1 + li) * dv + dv0 + c0 + 4 * g4) * 4;
-      f32x4 y0 = O0 + x0, y1 = O1 + x1;
-      if (a.accum) {
-        y0 += load_f4(outr, o0);
-        y1 += load_f4(outr, o1);
-      }
-      store_row(outr, y0, o0);
-      store_row(outr, y1, o1);
+      store_row(outr, O0 + x0, ((tp + 16 * own0 + li) * dv + dv0 + c0 + 4 * g4) * 4);
+      store_row(outr, O1 + x1, ((tp + 16 * own1 + li) * dv + dv0 + c0 + 4 * g4) * 4);
       dlam_flush(n1 - 1);
     } else {
 #pragma unroll
@@ -975,18 +1007,13 @@ int rs_dlam_lds_bytes(int L, int nslot) { return rs::lds_bytes_dlam(L, nslot); }
 
 int launch_sweep_rs_dlam(const FwdArgs& a, int nblocks, hipStream_t stream) {
   const int bytes = rs::lds_bytes_dlam(a.L, a.nslot);
-  if (a.nslot > 10 || a.L > 24 || bytes > kMaxLds || !a.qo || !a.dlam_part || a.G != 1 || a.st_out)
+  if (a.nslot > 8 || a.L > 24 || bytes > kMaxLds || !a.qo || !a.dlam_part || a.G != 1 || a.st_out)
     return LL_ERR_UNSUPPORTED;
   const size_t row_bytes = std::max({(size_t)a.dk * 2, (size_t)a.dv * 4, (size_t)a.L * 4});
   if ((size_t)(a.T + 2 * rs::C) * row_bytes >= (size_t)1 << 31) return LL_ERR_UNSUPPORTED;
-  static std::atomic<uint64_t> raised8{0}, raised10{0};
-  if (a.nslot > 8) {
-    if (!raise_lds_limit(reinterpret_cast<const void*>(&fwd_rs_kernel<10, false, true>), raised10)) return LL_ERR_HIP;
-    hipLaunchKernelGGL((fwd_rs_kernel<10, false, true>), dim3(nblocks), dim3(512), bytes, stream, a);
-  } else {
-    if (!raise_lds_limit(reinterpret_cast<const void*>(&fwd_rs_kernel<8, false, true>), raised8)) return LL_ERR_HIP;
-    hipLaunchKernelGGL((fwd_rs_kernel<8, false, true>), dim3(nblocks), dim3(512), bytes, stream, a);
-  }
+  static std::atomic<uint64_t> raised{0};
+  if (!raise_lds_limit(reinterpret_cast<const void*>(&fwd_rs_kernel<8, false, true>), raised)) return LL_ERR_HIP;
+  hipLaunchKernelGGL((fwd_rs_kernel<8, false, true>), dim3(nblocks), dim3(512), bytes, stream, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
