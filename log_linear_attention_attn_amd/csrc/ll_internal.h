@@ -89,7 +89,35 @@ struct BwdArgs {
   // own dQ sweep and sums dlam_parts partials per (t, level)
   int dq_done = 0;
   int dlam_parts = 0;
+  // dK and dV already formed by the reverse register-state sweep
+  // (launch_bwd_rev): the backward skips its own
+  int kv_done = 0;
 };
+
+// Reverse register-state sweep for dV and dK (bf16, C = 64, dk = dv = 128,
+// q / k per head): chunks of 2^seg_log2 per segment; the pre-pass writes the
+// per-(segment, level) states seg_part [BH][nseg][nj][128][128] fp32 and the
+// segments' log2 decay totals seg_tot2 [BH][nseg] (workspace, nseg > 1 only).
+struct BwdRevArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* dout;
+  const float* log_a;
+  const float* lam;
+  float* dk_out;  // [BH][T][128]
+  float* dv_out;  // [BH][T][128]
+  float* seg_part;
+  float* seg_tot2;
+  int BH, T, L, seg_log2, nseg, nj;
+};
+struct BwdRevPlan {
+  int seg_log2, nseg, nj;
+};
+void bwd_rev_plan(int T, BwdRevPlan* p);
+bool bwd_rev_ok(int C, int dk, int dv, int G, int T, int L);
+size_t bwd_rev_workspace(int BH, int T);
+int launch_bwd_rev(const BwdRevArgs& a, hipStream_t s);
 
 struct SegArgs {
   const void* k;

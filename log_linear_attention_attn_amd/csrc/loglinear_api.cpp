@@ -377,8 +377,13 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   if (dq_rs) dq_rs = plan_fwd(B, H, T, dv, dk, C, -1, &pd) == LL_OK &&
                      ll::rs_dlam_lds_bytes(pd.L, pd.nslot) <= ll::kMaxLds;
   const size_t fws = dq_rs ? pd.ws_total : 0;
+  // dV and dK through the reverse register-state sweep (bf16, C = 64,
+  // dk = dv = 128, q / k per head); its pre-pass states follow the rest of
+  // the workspace
+  const bool kv_rev = dtype == LL_BF16 && ll::bwd_rev_ok(C, dk, dv, G, T, p.L);
+  const size_t rws = kv_rev ? align256(ll::bwd_rev_workspace(p.BH, T)) : 0;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, part + dcb + 2 * per_head + fws, stream) != hipSuccess) return LL_ERR_HIP;
+  if (hipMallocAsync(&ws, part + dcb + 2 * per_head + fws + rws, stream) != hipSuccess) return LL_ERR_HIP;
   char* wsb = static_cast<char*>(ws);
   float* dq_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb) : dq;
   float* dk_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb + per_head) : dk_out;
@@ -413,6 +418,18 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
     }
     a.dq_done = 1;
     a.dlam_parts = dk / 64;
+  }
+  if (st == LL_OK && kv_rev) {
+    ll::BwdRevPlan rp;
+    ll::bwd_rev_plan(T, &rp);
+    char* rw = wsb + part + dcb + 2 * per_head + fws;
+    float* seg_part = rws ? reinterpret_cast<float*>(rw) : nullptr;
+    float* seg_tot2 =
+        rws ? reinterpret_cast<float*>(rw + (size_t)p.BH * rp.nseg * rp.nj * dk * dv * sizeof(float)) : nullptr;
+    ll::BwdRevArgs ra{q, k, v, dout, log_a, lambda, dk_h, dv_out, seg_part, seg_tot2,
+                      p.BH, T, p.L, rp.seg_log2, rp.nseg, rp.nj};
+    st = ll::launch_bwd_rev(ra, stream);
+    a.kv_done = 1;
   }
   if (st == LL_OK) st = ll::launch_bwd(dtype, C, a, stream);
   if (st == LL_OK && G > 1) {

@@ -698,8 +698,9 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
       return LL_ERR_HIP;
     hipLaunchKernelGGL((bwd_dq_kernel<IT, C>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
   }
-  // dV and dK
-  if (sizeof(IT) == 2 && C == 64 && bwd_kv16_ok(a)) {
+  // dV and dK (unless the reverse register-state sweep formed them already)
+  if (a.kv_done) {
+  } else if (sizeof(IT) == 2 && C == 64 && bwd_kv16_ok(a)) {
     const int st = launch_bwd_kv16(a, s);
     if (st != LL_OK) return st;
   } else {
