@@ -23,7 +23,8 @@
 // suffix state (every t after the segment sees it at the level fixed by the
 // highest differing segment bit), summed at the start of the sweep from
 // per-(segment, level) states that the pre-pass (PREP) forms with the same
-// accumulation.
+// accumulation.  Those states are sum_t w_t q_t dO_t^T for dV and their
+// transposes for dK, so one pre-pass serves both.
 //
 // Every product runs on fp16 matrix cores.  c, x and a are staged as fp16
 // rows scaled by a power of two each (their row maximum in [2^14, 2^15)),
@@ -56,8 +57,8 @@ constexpr int PS_OFF = AL_OFF + 2 * C * LDA * 2;      // score tiles fp16 [hi, l
 constexpr int XC_OFF = PS_OFF + 2 * 16 * 64 * 8;      // partner partial sums [8][2][64] f32x4
 constexpr int ROW_OFF = XC_OFF + 8 * 2 * 64 * 16;     // [2] x {cl (log2), ec, ex, ea} [64]
 constexpr int RF_OFF = ROW_OFF + 2 * 4 * C * 4;       // left-read row factors [64]
-constexpr int WT_OFF = RF_OFF + C * 4;                // level-update token weights [NLEV][64]
-constexpr int KE_OFF = WT_OFF + NLEV * C * 4;         // their exponents [NLEV], tile exponents [16]
+constexpr int WT_OFF = RF_OFF + C * 4;                // level-update token weights fp16 [NLEV][64]
+constexpr int KE_OFF = WT_OFF + NLEV * C * 2;         // the states' new exponents [NLEV], tile exponents [16]
 constexpr int LAM_OFF = KE_OFF + 32 * 4;              // lambda rows of the chunk [64][L]
 constexpr int LDS_BYTES = LAM_OFF + C * LMAX * 4;
 
@@ -82,33 +83,37 @@ __device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mma16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
+// Maxima of non-negative floats compare as unsigned integers.
 template <int CTRL>
-__device__ __forceinline__ float dpp_max(float x) {
-  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false)));
+__device__ __forceinline__ unsigned dpp_umax(unsigned x) {
+  return max(x, static_cast<unsigned>(
+                    __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xf, 0xf, false)));
 }
 // max over the 64 lanes of a non-negative value, wave-uniform
-__device__ __forceinline__ float wave_max(float x) {
-  x = dpp_max<0xb1>(x);   // quad_perm [1,0,3,2]
-  x = dpp_max<0x4e>(x);   // quad_perm [2,3,0,1]
-  x = dpp_max<0x124>(x);  // row_ror 4
-  x = dpp_max<0x128>(x);  // row_ror 8
-  const int xi = __float_as_int(x);
-  const unsigned a0 = __builtin_amdgcn_readlane(xi, 0), a1 = __builtin_amdgcn_readlane(xi, 16);
-  const unsigned a2 = __builtin_amdgcn_readlane(xi, 32), a3 = __builtin_amdgcn_readlane(xi, 48);
+__device__ __forceinline__ float wave_max(float v) {
+  unsigned x = __float_as_uint(v);
+  x = dpp_umax<0xb1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_umax<0x4e>(x);   // quad_perm [2,3,0,1]
+  x = dpp_umax<0x124>(x);  // row_ror 4
+  x = dpp_umax<0x128>(x);  // row_ror 8
+  const unsigned a0 = __builtin_amdgcn_readlane(x, 0), a1 = __builtin_amdgcn_readlane(x, 16);
+  const unsigned a2 = __builtin_amdgcn_readlane(x, 32), a3 = __builtin_amdgcn_readlane(x, 48);
   return __uint_as_float(max(max(a0, a1), max(a2, a3)));
 }
-// max over each aligned group of 16 lanes (one DPP row)
-__device__ __forceinline__ float row16_max(float m) {
-  m = dpp_max<0x121>(m);
-  m = dpp_max<0x122>(m);
-  m = dpp_max<0x124>(m);
-  return dpp_max<0x128>(m);
+// max over each aligned group of 16 lanes (one DPP row), non-negative values
+__device__ __forceinline__ float row16_max(float v) {
+  unsigned m = __float_as_uint(v);
+  m = dpp_umax<0x121>(m);
+  m = dpp_umax<0x122>(m);
+  m = dpp_umax<0x124>(m);
+  return __uint_as_float(dpp_umax<0x128>(m));
 }
-// max over each aligned group of 8 lanes
-__device__ __forceinline__ float row8_max(float m) {
-  m = dpp_max<0xb1>(m);
-  m = dpp_max<0x4e>(m);
-  return dpp_max<0x141>(m);  // row_half_mirror
+// max over each aligned group of 8 lanes, non-negative values
+__device__ __forceinline__ float row8_max(float v) {
+  unsigned m = __float_as_uint(v);
+  m = dpp_umax<0xb1>(m);
+  m = dpp_umax<0x4e>(m);
+  return __uint_as_float(dpp_umax<0x141>(m));  // row_half_mirror
 }
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_add(float x) {
@@ -182,8 +187,9 @@ struct Row8 {
 
 }  // namespace rv
 
-// MODE 0: dV; MODE 1: dK.  PREP: the per-(segment, level) states of the
-// segments after the first (see the file comment).
+// MODE 0: dV; MODE 1: dK.  PREP (MODE 0 only): the per-(segment, level)
+// states of the segments after the first (see the file comment); the dK sweep
+// reads their transposes.
 template <int MODE, bool PREP>
 __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
   using namespace rv;
@@ -191,7 +197,7 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
   f16x4* Ps = reinterpret_cast<f16x4*>(smem + PS_OFF);  // [hi, lo][sb][tb][lane]
   f32x4* Xc = reinterpret_cast<f32x4*>(smem + XC_OFF);  // [wave][2][lane]
   float* rf_s = reinterpret_cast<float*>(smem + RF_OFF);
-  float* WT = reinterpret_cast<float*>(smem + WT_OFF);
+  _Float16* WT = reinterpret_cast<_Float16*>(smem + WT_OFF);
   int* ke_s = reinterpret_cast<int*>(smem + KE_OFF);  // [0, NLEV): level updates; [16, 32): score tiles
   float* lam_s = reinterpret_cast<float*>(smem + LAM_OFF);
 
@@ -294,16 +300,25 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
     for (int gq = seg + 1; gq < a.nseg; ++gq) {
       const int j = 31 - __clz(seg ^ gq);
       const float wgt = __builtin_amdgcn_exp2f(d2);
-      const float* __restrict__ src = a.seg_part + (((size_t)(bh * a.nseg + gq) * a.nj + j) * DC + col0 + c0 + li) * DC +
-                                      64 * hh + 8 * g4;
+      const float* __restrict__ st = a.seg_part + ((size_t)(bh * a.nseg + gq) * a.nj + j) * DC * DC;
+      if constexpr (MODE == 0) {
+        const float* __restrict__ src = st + (col0 + c0 + li) * DC + 64 * hh + 8 * g4;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4 y = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4 * h);
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 y = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4 * h);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[2 * ks + h][e] += wgt * y[e];
-        }
+            for (int e = 0; e < 4; ++e) x[2 * ks + h][e] += wgt * y[e];
+          }
+      } else {
+        // the dK state is the transpose of the dV one: sum w dO_t q_t^T
+        const float* __restrict__ src = st + (64 * hh + 8 * g4) * DC + col0 + c0 + li;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[2 * ks + (e >> 2)][e & 3] += wgt * src[(32 * ks + e) * DC];
+      }
       d2 += a.seg_tot2[bh * a.nseg + gq];
     }
     float mx = 0.f;
@@ -369,7 +384,7 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
       const int e2 = scale_exp(row8_max(av.amax()));
       const f16x8 h = av.scaled(e2);
       *reinterpret_cast<f16x8*>(Ah + row * LDA + col) = h;
-      if constexpr (MODE == 0) *reinterpret_cast<f16x8*>(Al + row * LDA + col) = av.residual(e2, h);
+      if constexpr (MODE == 0 && !PREP) *reinterpret_cast<f16x8*>(Al + row * LDA + col) = av.residual(e2, h);
       if ((tid & 7) == 0) ea_s[row] = e2;
     }
     if (tid * 2 < C * L) {
@@ -460,8 +475,10 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
       if (w == 7) rf_s[lane] = __builtin_amdgcn_exp2f(A2 - cl2 + static_cast<float>(ex_s[lane]));
     }
     // level-update token weights (lane = t): wave b forms level b's
-    //   lambda[t, lvl] exp(cum_t - cum at the end of chunk n - 1) 2^(ec_t + ea_t),
-    // scaled by 2^-k with k the chunk's exponent (maximum in [1/2, 1))
+    //   lambda[t, lvl] exp(cum_t - cum at the end of chunk n - 1) 2^(ec_t + ea_t)
+    // in units of the state's new exponent kn (fp16, below 1): kn is the
+    // chunk's own exponent k (maximum in [1/2, 1)) or, if larger, that of the
+    // decayed state, so the state never grows by more than a factor 2 per chunk
     {
       const bool act = w < nlev && (PREP ? ((seg >> w) & 1) : ((n >> w) & 1));
       if (act) {
@@ -469,8 +486,15 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
         const float raw = lam_s[lane * L + lvl] *
                           __builtin_amdgcn_exp2f(cl2 + static_cast<float>(ec_s[lane] + ea_s[lane]));
         const int kc = scale_exp(wave_max(fabsf(raw))) + 15;
-        WT[w * C + lane] = ldexp_(raw, -kc);
-        if (lane == 0) ke_s[w] = kc;
+        int krw = kr[0];
+#pragma unroll
+        for (int b = 1; b < NLEV; ++b)
+          if (w == b) krw = kr[b];
+        const int base = (n >> (w + 1)) << (w + 1);
+        const bool first = PREP ? n == n1 - 1 : n == min(n1, base + (2 << w)) - 1;
+        const int kn = first ? kc : max(kc, krw + static_cast<int>(floorf(fmaxf(A2, -1.0e4f))));
+        WT[w * C + lane] = static_cast<_Float16>(ldexp_(raw, -kn));
+        if (lane == 0) ke_s[w] = kn;
       }
     }
     __syncthreads();
@@ -552,32 +576,21 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
       if (upd) {
         const int base = (n >> (b + 1)) << (b + 1);
         const bool first = PREP ? n == n1 - 1 : n == min(n1, base + (2 << b)) - 1;
-        const int kc = ke_s[b];
-        int kn = kc;
-        if (first) {
+        const int kn = uniform_i(ke_s[b]);
+        // the first chunk of the right half starts the state: the register
+        // contents are finite (fp32 or packed finite fp16), so a factor 0 clears them
+        const float f = first ? 0.f : __builtin_amdgcn_exp2f(A2 + static_cast<float>(kr[b] - kn));
 #pragma unroll
-          for (int t = 0; t < 4; ++t) R[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        } else {
-          const float dl = fmaxf(A2, -1.0e4f);
-          kn = max(kc, kr[b] + static_cast<int>(floorf(dl)));
-          const float f = __builtin_amdgcn_exp2f(A2 + static_cast<float>(kr[b] - kn));
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) R[b][t][r] *= f;
-        }
-        kr[b] = uniform_i(kn);
-        const int sh = kc - kn;  // <= 0
+          for (int r = 0; r < 4; ++r) R[b][t][r] *= f;
+        kr[b] = kn;
         f16x8 va[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const _Float16* a0 = Ah + (32 * ks + 8 * g4 + (li >> 2)) * LDA + c0 + 4 * (li & 3);
-          const f16x8 x = cat(tr_read(a0), tr_read(a0 + 4 * LDA));
-          const f32x4 w0 = *reinterpret_cast<const f32x4*>(WT + b * C + 32 * ks + 8 * g4);
-          const f32x4 w1 = *reinterpret_cast<const f32x4*>(WT + b * C + 32 * ks + 8 * g4 + 4);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            va[ks][e] = static_cast<_Float16>(ldexp_(static_cast<float>(x[e]) * (e < 4 ? w0[e] : w1[e - 4]), sh));
+          va[ks] = cat(tr_read(a0), tr_read(a0 + 4 * LDA)) *
+                   *reinterpret_cast<const f16x8*>(WT + b * C + 32 * ks + 8 * g4);
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -687,11 +700,9 @@ static int launch_one(const BwdRevArgs& a, hipStream_t stream) {
 int launch_bwd_rev(const BwdRevArgs& a, hipStream_t stream) {
   if (a.L > rv::LMAX || a.seg_log2 < 0 || a.seg_log2 > rv::NLEV || a.nj > rv::NLEV) return LL_ERR_UNSUPPORTED;
   if (a.nseg > 1 && (!a.seg_part || !a.seg_tot2)) return LL_ERR_UNSUPPORTED;
-  const bool prep = a.nseg > 1;
   int st = LL_OK;
-  if (prep) st = launch_one<0, true>(a, stream);
+  if (a.nseg > 1) st = launch_one<0, true>(a, stream);
   if (st == LL_OK) st = launch_one<0, false>(a, stream);
-  if (st == LL_OK && prep) st = launch_one<1, true>(a, stream);
   if (st == LL_OK) st = launch_one<1, false>(a, stream);
   return st;
 }
