@@ -99,14 +99,16 @@ __device__ __forceinline__ f32x4 mma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Maxima of NON-NEGATIVE floats: their bit patterns order like the values,
+// so unsigned max (which folds into the DPP form of v_max_u32) serves.
 template <int CTRL>
 __device__ __forceinline__ float dpp_max(float x) {
-  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false)));
+  const unsigned u = __float_as_uint(x);
+  return __uint_as_float(max(u, static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xf, 0xf, false))));
 }
 // Max over the 64 lanes of a NON-NEGATIVE value, returned wave-uniform: DPP
 // swaps within quads and rotations within 16-lane rows, then the four row
-// maxima compared as integers (the bit patterns of non-negative floats order
-// like the values).
+// maxima compared as integers.
 __device__ __forceinline__ float wave_max(float x) {
   x = dpp_max<0xb1>(x);   // quad_perm [1,0,3,2]
   x = dpp_max<0x4e>(x);   // quad_perm [2,3,0,1]
@@ -116,6 +118,15 @@ __device__ __forceinline__ float wave_max(float x) {
   const unsigned a0 = __builtin_amdgcn_readlane(xi, 0), a1 = __builtin_amdgcn_readlane(xi, 16);
   const unsigned a2 = __builtin_amdgcn_readlane(xi, 32), a3 = __builtin_amdgcn_readlane(xi, 48);
   return __uint_as_float(max(max(a0, a1), max(a2, a3)));
+}
+
+// Two-term bf16 split with a truncated high part: hi = the top 16 bits of x,
+// lo = x - hi rounded to bf16.  |x - hi| < 2^-7 |x|, so |x - hi - lo| <=
+// 2^-16 |x|, the bound of the round-to-nearest split, at fewer instructions.
+__device__ __forceinline__ void split_bf16_t(float x, bf16& hi, bf16& lo) {
+  const unsigned u = __float_as_uint(x);
+  hi = __builtin_bit_cast(bf16, static_cast<unsigned short>(u >> 16));
+  lo = static_cast<bf16>(x - __uint_as_float(u & 0xffff0000u));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within each
@@ -555,7 +566,7 @@ fwd_rs_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             bf16 x1, x2;
-            split_bf16(pv4[r], x1, x2);
+            split_bf16_t(pv4[r], x1, x2);
             h[r] = x1;
             l[r] = x2;
           }
@@ -716,7 +727,7 @@ fwd_rs_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           bf16 x1, x2;
-          split_bf16(static_cast<float>(x[e]) * (e < 4 ? e0[e] : e1[e - 4]), x1, x2);
+          split_bf16_t(static_cast<float>(x[e]) * (e < 4 ? e0[e] : e1[e - 4]), x1, x2);
           vh[ks][e] = x1;
           vl[ks][e] = x2;
         }
@@ -767,23 +778,18 @@ fwd_rs_kernel(FwdArgs a) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) gn[t >> 1][4 * (t & 1) + r] = static_cast<_Float16>(Sh[t][r] * sc);
-      if (m == 0) {  // every other chunk: the new state is level 0, nothing merged
-        G[0][0] = gn[0];
-        G[0][1] = gn[1];
-        eg[0] = em;
-        dec[0] = 0.f;
+      // the new state becomes level m; the levels above it age by this
+      // chunk's decay, those below it were merged and are not read again
+      // before they are rewritten (one uniform loop keeps every level state
+      // in fixed registers)
 #pragma unroll
-        for (int b = 1; b < NSLOT; ++b) dec[b] = uniform(dec[b] + Atot);
-      } else {
-#pragma unroll
-        for (int b = 1; b < NSLOT; ++b) {
-          if (b == m) {
-            G[b][0] = gn[0];
-            G[b][1] = gn[1];
-            eg[b] = em;
-          }
-          dec[b] = uniform(b == m ? 0.f : (b > m ? dec[b] + Atot : dec[b]));
+      for (int b = 0; b < NSLOT; ++b) {
+        if (b == m) {
+          G[b][0] = gn[0];
+          G[b][1] = gn[1];
+          eg[b] = em;
         }
+        dec[b] = uniform(b == m ? 0.f : (b > m ? dec[b] + Atot : dec[b]));
       }
     }
     __builtin_amdgcn_s_setprio(0);
