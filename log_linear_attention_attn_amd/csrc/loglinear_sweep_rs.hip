@@ -603,46 +603,36 @@ fwd_rs_kernel(FwdArgs a) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) Op[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      f16x8 qa[4][2];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 * ks + 8 * g4);
       if constexpr (DLAM) {
         // lane li is row 16 mi + li, element r column c0 + 4 g4 + r.  Row
         // factor exp(cl_row) 2^eq; the forward's q of the row and columns.
-        float ecr[4];
-        f16x4 qof[4];
+        // Row tiles outer, levels inner: one tile's Q fragments are live at
+        // a time.
+        float* dlw = reinterpret_cast<float*>(smem + LW_OFF) + w * (C * NSLOT);
+        float fb[NSLOT];
+#pragma unroll
+        for (int b = 0; b < NSLOT; ++b) fb[b] = uniform(__expf(dec[b]) * exp2_int(eg[b]));
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-          ecr[mi] = exp2f_fast(cl_s[16 * mi + li]) * exp2_int(er_s[16 * mi + li]);
-          qof[mi] = *reinterpret_cast<const f16x4*>(Qo + (16 * mi + li) * LDQO + c0 + 4 * g4);
-        }
-        float* dlw = reinterpret_cast<float*>(smem + LW_OFF) + w * (C * NSLOT);
+          const f16x8 qa0 = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 8 * g4);
+          const f16x8 qa1 = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 + 8 * g4);
+          const float ecr = exp2f_fast(cl_s[16 * mi + li]) * exp2_int(er_s[16 * mi + li]);
+          const f16x4 qof = *reinterpret_cast<const f16x4*>(Qo + (16 * mi + li) * LDQO + c0 + 4 * g4);
 #pragma unroll
-        for (int b = 0; b < NSLOT; ++b) {
-          if ((n >> b) & 1) {
-            f32x4 acc[4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-              for (int mi = 0; mi < 4; ++mi) acc[mi] = mma16(G[b][ks], qa[mi][ks], acc[mi]);
-            const float fb = __expf(dec[b]) * exp2_int(eg[b]);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-              const float wd = ecr[mi] * fb;  // the level's read of this row: wd * acc
+          for (int b = 0; b < NSLOT; ++b) {
+            if ((n >> b) & 1) {
+              f32x4 acc = mma16(G[b][0], qa0, f32x4{0.f, 0.f, 0.f, 0.f});
+              acc = mma16(G[b][1], qa1, acc);
+              const float wd = ecr * fb[b];  // the level's read of this row: wd * acc
               const float wq = lam_s[(16 * mi + li) * L + LOGC + 1 + b] * wd;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) Op[mi][r] += wq * acc[mi][r];
+              for (int r = 0; r < 4; ++r) Op[mi][r] += wq * acc[r];
               // dot of the row's read with the forward's q over this wave's
               // 16 columns: four products here, the other twelve in the
               // lanes li + 16, + 32, + 48 (same row, next column groups)
               float pd = 0.f;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) pd += static_cast<float>(qof[mi][r]) * acc[mi][r];
+              for (int r = 0; r < 4; ++r) pd += static_cast<float>(qof[r]) * acc[r];
               pd = xor16_sum(pd);
               pd = xor32_sum(pd);
               if (g4 == 0) dlw[(16 * mi + li) * NSLOT + b] = pd * wd;
@@ -650,6 +640,12 @@ fwd_rs_kernel(FwdArgs a) {
           }
         }
       } else {
+        f16x8 qa[4][2];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            qa[mi][ks] = *reinterpret_cast<const f16x8*>(Qh + (16 * mi + li) * LDQ + 64 * hh + 32 * ks + 8 * g4);
 #pragma unroll
         for (int b = 0; b < NSLOT; ++b) {
           if ((n >> b) & 1) {
