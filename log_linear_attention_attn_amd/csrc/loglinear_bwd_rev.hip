@@ -46,21 +46,41 @@ namespace rv {
 constexpr int C = 64, DC = 128, LOGC = 6, NLEV = 5, NTH = 512, LMAX = 16;
 constexpr int LDC = DC + 8;  // fp16 rows of the c and x tiles
 constexpr int LDA = 64 + 8;  // fp16 rows of the a tile (the group's 64 columns)
-// LDS layout.  The tiles and row data read in phase 2 are double-buffered by
-// chunk parity; everything else is written after the chunk's first barrier
-// and read before the next chunk's first barrier.
-constexpr int CH_OFF = 0;                             // c fp16 [2][64][LDC]
-constexpr int XH_OFF = CH_OFF + 2 * C * LDC * 2;      // x fp16 [2][64][LDC]
-constexpr int AH_OFF = XH_OFF + 2 * C * LDC * 2;      // a fp16 [2][64][LDA]
-constexpr int AL_OFF = AH_OFF + 2 * C * LDA * 2;      // fp16 residual of a (fp32 a only) [2][64][LDA]
-constexpr int PS_OFF = AL_OFF + 2 * C * LDA * 2;      // score tiles fp16 [hi, lo][4 sb][4 tb][64 lanes] x 8 B
-constexpr int XC_OFF = PS_OFF + 2 * 16 * 64 * 8;      // partner partial sums [8][2][64] f32x4
-constexpr int ROW_OFF = XC_OFF + 8 * 2 * 64 * 16;     // [2] x {cl (log2), ec, ex, ea} [64]
-constexpr int RF_OFF = ROW_OFF + 2 * 4 * C * 4;       // left-read row factors [64]
-constexpr int WT_OFF = RF_OFF + C * 4;                // level-update token weights fp16 [NLEV][64]
-constexpr int KE_OFF = WT_OFF + NLEV * C * 2;         // the states' new exponents [NLEV], tile exponents [16]
-constexpr int LAM_OFF = KE_OFF + 32 * 4;              // lambda rows of the chunk [64][L]
-constexpr int LDS_BYTES = LAM_OFF + C * LMAX * 4;
+// LDS layouts.  The tiles and row data read in phase 2 are double-buffered
+// by chunk parity; everything else is written after the chunk's first
+// barrier and read before the next chunk's first barrier.  The pre-pass keeps
+// only c, a, the row data, the weights and lambda, so two of its workgroups
+// share a CU.
+template <bool PREP>
+struct Lay;
+template <>
+struct Lay<false> {
+  static constexpr int CH = 0;                         // c fp16 [2][64][LDC]
+  static constexpr int XH = CH + 2 * C * LDC * 2;      // x fp16 [2][64][LDC]
+  static constexpr int AH = XH + 2 * C * LDC * 2;      // a fp16 [2][64][LDA]
+  static constexpr int AL = AH + 2 * C * LDA * 2;      // fp16 residual of a (fp32 a only) [2][64][LDA]
+  static constexpr int PS = AL + 2 * C * LDA * 2;      // score tiles fp16 [hi, lo][4 sb][4 tb][64 lanes] x 8 B
+  static constexpr int XC = PS + 2 * 16 * 64 * 8;      // partner partial sums [8][2][64] f32x4
+  static constexpr int ROW = XC + 8 * 2 * 64 * 16;     // [2] x {cl (log2), ec, ex, ea} [64]
+  static constexpr int RF = ROW + 2 * 4 * C * 4;       // left-read row factors [64]
+  static constexpr int WT = RF + C * 4;                // level-update token weights fp16 [NLEV][64]
+  static constexpr int KE = WT + NLEV * C * 2;         // the states' new exponents [NLEV], tile exponents [16]
+  static constexpr int LAM = KE + 32 * 4;              // lambda rows of the chunk [64][L]
+  static constexpr int BYTES = LAM + C * LMAX * 4;
+};
+template <>
+struct Lay<true> {
+  static constexpr int CH = 0;
+  static constexpr int AH = CH + 2 * C * LDC * 2;
+  static constexpr int ROW = AH + 2 * C * LDA * 2;
+  static constexpr int WT = ROW + 2 * 4 * C * 4;
+  static constexpr int KE = WT + NLEV * C * 2;
+  static constexpr int LAM = KE + 32 * 4;
+  static constexpr int BYTES = LAM + C * LMAX * 4;
+  static constexpr int XH = 0, AL = 0, PS = 0, XC = 0, RF = 0;  // not used by the pre-pass
+};
+// register levels of the pre-pass variant that shares a CU with another
+constexpr int NL_SMALL = 3;
 
 typedef short __attribute__((ext_vector_type(4))) s16x4;
 typedef _Float16 __attribute__((ext_vector_type(4))) f16x4;
@@ -189,17 +209,17 @@ struct Row8 {
 
 // MODE 0: dV; MODE 1: dK.  PREP (MODE 0 only): the per-(segment, level)
 // states of the segments after the first (see the file comment); the dK sweep
-// reads their transposes.
-template <int MODE, bool PREP>
-__global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
+// reads their transposes.  NL: levels held in registers.
+template <int MODE, bool PREP, int NL>
+__device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* smem) {
   using namespace rv;
-  extern __shared__ __align__(16) unsigned char smem[];
-  f16x4* Ps = reinterpret_cast<f16x4*>(smem + PS_OFF);  // [hi, lo][sb][tb][lane]
-  f32x4* Xc = reinterpret_cast<f32x4*>(smem + XC_OFF);  // [wave][2][lane]
-  float* rf_s = reinterpret_cast<float*>(smem + RF_OFF);
-  _Float16* WT = reinterpret_cast<_Float16*>(smem + WT_OFF);
-  int* ke_s = reinterpret_cast<int*>(smem + KE_OFF);  // [0, NLEV): level updates; [16, 32): score tiles
-  float* lam_s = reinterpret_cast<float*>(smem + LAM_OFF);
+  using LY = Lay<PREP>;
+  f16x4* Ps = reinterpret_cast<f16x4*>(smem + LY::PS);  // [hi, lo][sb][tb][lane]
+  f32x4* Xc = reinterpret_cast<f32x4*>(smem + LY::XC);  // [wave][2][lane]
+  float* rf_s = reinterpret_cast<float*>(smem + LY::RF);
+  _Float16* WT = reinterpret_cast<_Float16*>(smem + LY::WT);
+  int* ke_s = reinterpret_cast<int*>(smem + LY::KE);  // [0, NLEV): level updates; [16, 32): score tiles
+  float* lam_s = reinterpret_cast<float*>(smem + LY::LAM);
 
   const int id = blockIdx.x;
   const int px = id & 7, rest = id >> 3;
@@ -241,11 +261,11 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
   // group; true value R * 2^kr[b].  Once the right half is complete, R[b][0]
   // and R[b][1] hold the fp16 read operand (element e of R[b][kl]:
   // contraction 64 hh + 32 kl + 8 g4 + e), true value * 2^er[b].
-  f32x4 R[NLEV][4];
-  int kr[NLEV], er[NLEV];
-  float g2[NLEV];  // log2 decay from the end of the current chunk to the end of the left half
+  f32x4 R[NL][4];
+  int kr[NL], er[NL];
+  float g2[NL];  // log2 decay from the end of the current chunk to the end of the left half
 #pragma unroll
-  for (int b = 0; b < NLEV; ++b) {
+  for (int b = 0; b < NL; ++b) {
     kr[b] = 0;
     er[b] = 0;
     g2[b] = 0.f;
@@ -350,11 +370,11 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
   f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int n = n1 - 1; n >= n0; --n) {
     const int tok0 = n * C, par = n & 1;
-    _Float16* Ch = reinterpret_cast<_Float16*>(smem + CH_OFF) + par * (C * LDC);
-    _Float16* Xh = reinterpret_cast<_Float16*>(smem + XH_OFF) + par * (C * LDC);
-    _Float16* Ah = reinterpret_cast<_Float16*>(smem + AH_OFF) + par * (C * LDA);
-    _Float16* Al = reinterpret_cast<_Float16*>(smem + AL_OFF) + par * (C * LDA);
-    float* cl_s = reinterpret_cast<float*>(smem + ROW_OFF) + par * (4 * C);
+    _Float16* Ch = reinterpret_cast<_Float16*>(smem + LY::CH) + par * (C * LDC);
+    _Float16* Xh = reinterpret_cast<_Float16*>(smem + LY::XH) + par * (C * LDC);
+    _Float16* Ah = reinterpret_cast<_Float16*>(smem + LY::AH) + par * (C * LDA);
+    _Float16* Al = reinterpret_cast<_Float16*>(smem + LY::AL) + par * (C * LDA);
+    float* cl_s = reinterpret_cast<float*>(smem + LY::ROW) + par * (4 * C);
     int* ec_s = reinterpret_cast<int*>(cl_s + C);
     int* ex_s = ec_s + C;
     int* ea_s = ex_s + C;
@@ -488,7 +508,7 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
         const int kc = scale_exp(wave_max(fabsf(raw))) + 15;
         int krw = kr[0];
 #pragma unroll
-        for (int b = 1; b < NLEV; ++b)
+        for (int b = 1; b < NL; ++b)
           if (w == b) krw = kr[b];
         const int base = (n >> (w + 1)) << (w + 1);
         const bool first = PREP ? n == n1 - 1 : n == min(n1, base + (2 << w)) - 1;
@@ -503,16 +523,16 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
     if constexpr (!PREP) {
       // left reads over this wave's contraction half, all four row tiles:
       // Op[mi] = sum_b u_b x_h . R_b, times the row factor
-      float ub[NLEV + 1];
-      bool live[NLEV + 1];
+      float ub[NL + 1];
+      bool live[NL + 1];
 #pragma unroll
-      for (int b = 0; b < NLEV; ++b) {
+      for (int b = 0; b < NL; ++b) {
         const int base = (n >> (b + 1)) << (b + 1);
         live[b] = b < S && !((n >> b) & 1) && base + (1 << b) < n1;
         ub[b] = __builtin_amdgcn_exp2f(g2[b] + static_cast<float>(er[b]));
       }
-      live[NLEV] = has_suffix;
-      ub[NLEV] = __builtin_amdgcn_exp2f(dn2 + static_cast<float>(eh));
+      live[NL] = has_suffix;
+      ub[NL] = __builtin_amdgcn_exp2f(dn2 + static_cast<float>(eh));
       f32x4 Op[4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
@@ -520,10 +540,10 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
         const f16x8 xa0 = *reinterpret_cast<const f16x8*>(Xh + (16 * mi + li) * LDC + 64 * hh + 8 * g4);
         const f16x8 xa1 = *reinterpret_cast<const f16x8*>(Xh + (16 * mi + li) * LDC + 64 * hh + 32 + 8 * g4);
 #pragma unroll
-        for (int b = 0; b <= NLEV; ++b) {
+        for (int b = 0; b <= NL; ++b) {
           if (live[b]) {
-            const f16x8 gr0 = b < NLEV ? __builtin_bit_cast(f16x8, R[b][0]) : Rh[0];
-            const f16x8 gr1 = b < NLEV ? __builtin_bit_cast(f16x8, R[b][1]) : Rh[1];
+            const f16x8 gr0 = b < NL ? __builtin_bit_cast(f16x8, R[b][0]) : Rh[0];
+            const f16x8 gr1 = b < NL ? __builtin_bit_cast(f16x8, R[b][1]) : Rh[1];
             f32x4 acc = mma32(xa0, gr0, f32x4{0.f, 0.f, 0.f, 0.f});
             acc = mma32(xa1, gr1, acc);
 #pragma unroll
@@ -571,7 +591,7 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
     // fold's layout; the state's exponent follows the larger of the decayed
     // state and the chunk
 #pragma unroll
-    for (int b = 0; b < NLEV; ++b) {
+    for (int b = 0; b < NL; ++b) {
       const bool upd = b < nlev && (PREP ? ((seg >> b) & 1) : ((n >> b) & 1));
       if (upd) {
         const int base = (n >> (b + 1)) << (b + 1);
@@ -631,7 +651,7 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
   if constexpr (PREP) {
     // P[seg, j][column][contraction] = R_j 2^kr_j
 #pragma unroll
-    for (int b = 0; b < NLEV; ++b) {
+    for (int b = 0; b < NL; ++b) {
       if (b < nlev && ((seg >> b) & 1)) {
         float* dst = a.seg_part + (((size_t)(bh * a.nseg + seg) * a.nj + b) * DC + col0 + c0 + li) * DC + 64 * hh +
                      8 * g4;
@@ -662,6 +682,19 @@ __global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
   }
 }
 
+template <int MODE>
+__global__ void __launch_bounds__(512) bwd_rev_kernel(BwdRevArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  rev_body<MODE, false, rv::NLEV>(a, smem);
+}
+// the pre-pass; with NL = NL_SMALL register levels it fits two workgroups per CU
+template <int NL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NL <= rv::NL_SMALL ? 4 : 2)))
+bwd_rev_prep_kernel(BwdRevArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  rev_body<0, true, NL>(a, smem);
+}
+
 void bwd_rev_plan(int T, BwdRevPlan* p) {
   const int N = (T + rv::C - 1) / rv::C;
   const int nslot = N > 1 ? 32 - __builtin_clz(static_cast<unsigned>(N - 1)) : 0;
@@ -684,26 +717,30 @@ size_t bwd_rev_workspace(int BH, int T) {
   return (size_t)BH * p.nseg * p.nj * rv::DC * rv::DC * 4 + (size_t)BH * p.nseg * 4;
 }
 
-template <int MODE, bool PREP>
-static int launch_one(const BwdRevArgs& a, hipStream_t stream) {
-  static std::atomic<uint64_t> raised{0};
-  if (!raise_lds_limit(reinterpret_cast<const void*>(&bwd_rev_kernel<MODE, PREP>), raised)) return LL_ERR_HIP;
+template <typename K>
+static int launch_grid(K kernel, std::atomic<uint64_t>& raised, int bytes, const BwdRevArgs& a, hipStream_t stream) {
+  if (!raise_lds_limit(reinterpret_cast<const void*>(kernel), raised)) return LL_ERR_HIP;
   const long long pairs = (long long)a.BH * a.nseg;
   const long long nblocks = (pairs + 7) / 8 * 8 * 2;
   if (nblocks <= 0) return LL_OK;
   if (nblocks > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((bwd_rev_kernel<MODE, PREP>), dim3(static_cast<unsigned>(nblocks)), dim3(rv::NTH),
-                     rv::LDS_BYTES, stream, a);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(nblocks)), dim3(rv::NTH), bytes, stream, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
 int launch_bwd_rev(const BwdRevArgs& a, hipStream_t stream) {
   if (a.L > rv::LMAX || a.seg_log2 < 0 || a.seg_log2 > rv::NLEV || a.nj > rv::NLEV) return LL_ERR_UNSUPPORTED;
   if (a.nseg > 1 && (!a.seg_part || !a.seg_tot2)) return LL_ERR_UNSUPPORTED;
+  static std::atomic<uint64_t> r0{0}, r1{0}, r2{0}, r3{0};
   int st = LL_OK;
-  if (a.nseg > 1) st = launch_one<0, true>(a, stream);
-  if (st == LL_OK) st = launch_one<0, false>(a, stream);
-  if (st == LL_OK) st = launch_one<1, false>(a, stream);
+  if (a.nseg > 1) {
+    if (a.nj <= rv::NL_SMALL)
+      st = launch_grid(&bwd_rev_prep_kernel<rv::NL_SMALL>, r0, rv::Lay<true>::BYTES, a, stream);
+    else
+      st = launch_grid(&bwd_rev_prep_kernel<rv::NLEV>, r1, rv::Lay<true>::BYTES, a, stream);
+  }
+  if (st == LL_OK) st = launch_grid(&bwd_rev_kernel<0>, r2, rv::Lay<false>::BYTES, a, stream);
+  if (st == LL_OK) st = launch_grid(&bwd_rev_kernel<1>, r3, rv::Lay<false>::BYTES, a, stream);
   return st;
 }
 
