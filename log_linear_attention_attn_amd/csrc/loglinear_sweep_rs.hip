@@ -774,18 +774,36 @@ fwd_rs_kernel(FwdArgs a) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) gn[t >> 1][4 * (t & 1) + r] = static_cast<_Float16>(Sh[t][r] * sc);
-      // the new state becomes level m; the levels above it age by this
-      // chunk's decay, those below it were merged and are not read again
-      // before they are rewritten (one uniform loop keeps every level state
-      // in fixed registers)
+      if constexpr (DLAM) {
+        // the same merge as one uniform per-level loop: the register
+        // allocation of this variant spills less with it (the forward
+        // instantiations spill more with it)
 #pragma unroll
-      for (int b = 0; b < NSLOT; ++b) {
-        if (b == m) {
-          G[b][0] = gn[0];
-          G[b][1] = gn[1];
-          eg[b] = em;
+        for (int b = 0; b < NSLOT; ++b) {
+          if (b == m) {
+            G[b][0] = gn[0];
+            G[b][1] = gn[1];
+            eg[b] = em;
+          }
+          dec[b] = uniform(b == m ? 0.f : (b > m ? dec[b] + Atot : dec[b]));
         }
-        dec[b] = uniform(b == m ? 0.f : (b > m ? dec[b] + Atot : dec[b]));
+      } else if (m == 0) {  // every other chunk: the new state is level 0, nothing merged
+        G[0][0] = gn[0];
+        G[0][1] = gn[1];
+        eg[0] = em;
+        dec[0] = 0.f;
+#pragma unroll
+        for (int b = 1; b < NSLOT; ++b) dec[b] = uniform(dec[b] + Atot);
+      } else {
+#pragma unroll
+        for (int b = 1; b < NSLOT; ++b) {
+          if (b == m) {
+            G[b][0] = gn[0];
+            G[b][1] = gn[1];
+            eg[b] = em;
+          }
+          dec[b] = uniform(b == m ? 0.f : (b > m ? dec[b] + Atot : dec[b]));
+        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
