@@ -808,6 +808,10 @@ fwd_rs_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
     Aprev = Atot;
+    // DLAM stages the scaled dO (Qh), the forward's q (Qo) and their row
+    // exponents before the chunk's first barrier, and phase 2 reads them:
+    // every wave finishes this chunk before any wave stages the next one
+    if constexpr (DLAM) __syncthreads();
   }
 
   // ---------------- last chunk: add the partner's partial sums, store -------

@@ -118,3 +118,34 @@ def test_bwd_256_chunks_sampled(decay):
         assert_parity(grads[4][bh][idx], dlam, BF16_TOL, f"dlam rows {decay} {bh}")
         assert_parity(grads[1][bh][idx], dk_, BF16_TOL, f"dk cols {decay} {bh}")
         assert_parity(grads[2][bh][idx], dv_, BF16_TOL, f"dv cols {decay} {bh}")
+
+
+def test_bwd_ten_segments_sampled():
+    """T=20000, C=64: 313 chunks, so the reverse register-state sweeps for dK
+    and dV run ten 32-chunk segments (four segment-level bits, the pre-pass
+    with five register levels) and a ragged last segment of 25 chunks whose
+    last chunk is partial.  Sampled rows of dq, dlambda and columns of dk, dv
+    at every segment boundary, weak decay so the segment-level states carry
+    weight."""
+    B, H, T = 1, 1, 20000
+    w = W.FwdWorkload("bwd313", B, H, T, 128, 128, 64, "bf16", decay="weak", seed=11)
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    dout = torch.from_numpy(np.random.default_rng(12).standard_normal((B, H, T, 128)).astype(np.float32))
+    announce("bwd ten segments sampled")
+    dev = to_dev(q, k, v, la, lam)
+    out = ll.fwd(*dev, C=64)
+    grads = [g.cpu().numpy() for g in ll.bwd(*dev, out, dout.cuda(), C=64)]
+    torch.cuda.synchronize()
+    seg = 32 * 64
+    fixed = [0, T - 1, T - 2, 288 * 64, 312 * 64, 312 * 64 - 1]
+    for g in range(1, 10):
+        fixed += [g * seg - 1, g * seg]
+    rng = np.random.default_rng(13)
+    idx = sorted(set(fixed) | set(rng.integers(0, T, 16).tolist()))
+    bh = (0, 0)
+    dq, dlam = oracle.backward_rows(q, k, v, la, lam, dout, bh, idx)
+    dk_, dv_ = oracle.backward_cols(q, k, v, la, lam, dout, bh, idx)
+    assert_parity(grads[0][bh][idx], dq, BF16_TOL, "dq rows T=20000")
+    assert_parity(grads[4][bh][idx], dlam, BF16_TOL, "dlam rows T=20000")
+    assert_parity(grads[1][bh][idx], dk_, BF16_TOL, "dk cols T=20000")
+    assert_parity(grads[2][bh][idx], dv_, BF16_TOL, "dv cols T=20000")
