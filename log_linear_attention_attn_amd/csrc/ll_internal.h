@@ -92,6 +92,10 @@ struct BwdArgs {
   // dK and dV already formed by the reverse register-state sweep
   // (launch_bwd_rev): the backward skips its own
   int kv_done = 0;
+  // the in-chunk dlambda as partial sums of the dV sweep
+  // ([intra_parts][BH][T][8]): the backward sums them instead of its own pass
+  const float* dlam_intra_part = nullptr;
+  int intra_parts = 0;
 };
 
 // Reverse register-state sweep for dV and dK (bf16, C = 64, dk = dv = 128,
@@ -110,6 +114,9 @@ struct BwdRevArgs {
   float* seg_part;
   float* seg_tot2;
   int BH, T, L, seg_log2, nseg, nj;
+  // the dV sweep's in-chunk dlambda partials [2 column groups][BH][T][8]
+  // (levels 0 .. log2C in the first seven words), or null
+  float* intra_part = nullptr;
 };
 struct BwdRevPlan {
   int seg_log2, nseg, nj;

@@ -382,8 +382,10 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   // the workspace
   const bool kv_rev = dtype == LL_BF16 && ll::bwd_rev_ok(C, dk, dv, G, T, p.L);
   const size_t rws = kv_rev ? align256(ll::bwd_rev_workspace(p.BH, T)) : 0;
+  // the dV sweep's in-chunk dlambda partials, one per 64-column group of dv
+  const size_t iws = kv_rev ? align256((size_t)(dv / 64) * p.BH * T * 8 * sizeof(float)) : 0;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, part + dcb + 2 * per_head + fws + rws, stream) != hipSuccess) return LL_ERR_HIP;
+  if (hipMallocAsync(&ws, part + dcb + 2 * per_head + fws + rws + iws, stream) != hipSuccess) return LL_ERR_HIP;
   char* wsb = static_cast<char*>(ws);
   float* dq_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb) : dq;
   float* dk_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb + per_head) : dk_out;
@@ -428,8 +430,11 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
         rws ? reinterpret_cast<float*>(rw + (size_t)p.BH * rp.nseg * rp.nj * dk * dv * sizeof(float)) : nullptr;
     ll::BwdRevArgs ra{q, k, v, dout, log_a, lambda, dk_h, dv_out, seg_part, seg_tot2,
                       p.BH, T, p.L, rp.seg_log2, rp.nseg, rp.nj};
+    ra.intra_part = reinterpret_cast<float*>(wsb + part + dcb + 2 * per_head + fws + rws);
     st = ll::launch_bwd_rev(ra, stream);
     a.kv_done = 1;
+    a.dlam_intra_part = ra.intra_part;
+    a.intra_parts = dv / 64;
   }
   if (st == LL_OK) st = ll::launch_bwd(dtype, C, a, stream);
   if (st == LL_OK && G > 1) {

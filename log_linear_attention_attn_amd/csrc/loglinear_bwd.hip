@@ -528,6 +528,24 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dlam_intra_kernel(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// bwd_dlam_intra_sum_kernel: dlam of the in-chunk levels 0 .. logc as the
+// in-order sum of the reverse dV sweep's per-column-group partials
+// ([nparts][BH][T][8]).  One thread per (b,h, t, level).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_dlam_intra_sum_kernel(BwdArgs a, int logc, int nparts) {
+  const int nl = logc + 1;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // (bh * T + t) * nl + l
+  if (e >= (long long)a.BH * a.T * nl) return;
+  const long long row = e / nl;
+  const int l = static_cast<int>(e - row * nl);
+  if (l >= a.L) return;
+  const size_t pstride = (size_t)a.BH * a.T * 8;
+  float x = 0.f;
+  for (int p = 0; p < nparts; ++p) x += a.dlam_intra_part[p * pstride + (size_t)row * 8 + l];
+  a.dlam[(size_t)row * a.L + l] = x;
+}
+
+// ---------------------------------------------------------------------------
 // bwd_dlam_inter_kernel: dlam of the chunk levels, the sum of the per-slice
 // partials in slice order (0 past the levels a row reaches).  One thread per
 // (b,h, t, level b < nslot): the partials of one slice and (b,h) are one
@@ -721,7 +739,11 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_kv_kernel<IT, C, 1>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
   }
   }
-  if (sizeof(IT) == 2 && C == 64 && bwd_dlam_intra16_ok(a)) {
+  if (a.intra_parts > 0) {
+    const long long elems = (long long)a.BH * a.T * (Lg<C>::v + 1);
+    hipLaunchKernelGGL(bwd_dlam_intra_sum_kernel, dim3(static_cast<unsigned>((elems + 255) / 256)), dim3(256), 0, s,
+                       a, Lg<C>::v, a.intra_parts);
+  } else if (sizeof(IT) == 2 && C == 64 && bwd_dlam_intra16_ok(a)) {
     const int st = launch_bwd_dlam_intra16(a, s);
     if (st != LL_OK) return st;
   } else {

@@ -66,7 +66,12 @@ struct Lay<false> {
   static constexpr int WT = RF + C * 4;                // level-update token weights fp16 [NLEV][64]
   static constexpr int KE = WT + NLEV * C * 2;         // the states' new exponents [NLEV], tile exponents [16]
   static constexpr int LAM = KE + 32 * 4;              // lambda rows of the chunk [64][L]
-  static constexpr int BYTES = LAM + C * LMAX * 4;
+  // dV sweep only: v of the group's columns, fp16 [64][LDA], its row
+  // exponents [64], and the in-chunk dlambda row sums [2][64][8]
+  static constexpr int VH = LAM + C * LMAX * 4;
+  static constexpr int EV = VH + C * LDA * 2;
+  static constexpr int ISL = EV + C * 4;
+  static constexpr int BYTES = ISL + 2 * C * 8 * 4;
 };
 template <>
 struct Lay<true> {
@@ -77,7 +82,7 @@ struct Lay<true> {
   static constexpr int KE = WT + NLEV * C * 2;
   static constexpr int LAM = KE + 32 * 4;
   static constexpr int BYTES = LAM + C * LMAX * 4;
-  static constexpr int XH = 0, AL = 0, PS = 0, XC = 0, RF = 0;  // not used by the pre-pass
+  static constexpr int XH = 0, AL = 0, PS = 0, XC = 0, RF = 0, VH = 0, EV = 0, ISL = 0;  // not used by the pre-pass
 };
 // register levels of the pre-pass variant that shares a CU with another
 constexpr int NL_SMALL = 3;
@@ -134,6 +139,35 @@ __device__ __forceinline__ float row8_max(float v) {
   m = dpp_umax<0xb1>(m);
   m = dpp_umax<0x4e>(m);
   return __uint_as_float(dpp_umax<0x141>(m));  // row_half_mirror
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Sums over the 16 lanes of a 16-lane group of x[0..3]; lane li returns the
+// total of x[li >> 2]: a reduce-scatter over lane bits 3 and 2 (each lane
+// keeps half of its values and adds its partner's copy of them), then a sum
+// over the four lanes of a quad.
+__device__ __forceinline__ float rowsum16(const float x[4], int li) {
+  const bool h8 = li & 8, h4 = li & 4;
+  const float k0 = h8 ? x[2] : x[0], k1 = h8 ? x[3] : x[1];
+  // the values a lane sends depend on its own lane bits: each is made opaque
+  // (an empty asm) before the DPP read, so the compiler cannot substitute the
+  // receiving lane's select into the sending lane's value
+  float s0 = h8 ? x[0] : x[2], s1 = h8 ? x[1] : x[3];
+  asm volatile("" : "+v"(s0), "+v"(s1));
+  const float y0 = k0 + dpp_mov<0x128>(s0);  // row_ror 8: lane li ^ 8
+  const float y1 = k1 + dpp_mov<0x128>(s1);
+  float send = h4 ? y0 : y1;
+  asm volatile("" : "+v"(send));
+  // lane li ^ 4 in one exchange for every lane (ds_swizzle, bit mode: xor 4):
+  // a per-lane choice between two DPP rotations can be compiled as a branch,
+  // and a DPP read of a lane outside EXEC returns 0
+  const float from = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(send), 0x101F));
+  float z = (h4 ? y1 : y0) + from;
+  z += dpp_mov<0xb1>(z);  // quad_perm [1,0,3,2]
+  z += dpp_mov<0x4e>(z);  // quad_perm [2,3,0,1]
+  return z;
 }
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_add(float x) {
@@ -249,6 +283,13 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
   const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
   const rsrc_t lamr = make_rsrc(a.lam + bhT * L, T * L * 4);
   const rsrc_t yr = make_rsrc((MODE == 0 ? a.dv_out : a.dk_out) + bhT * DC, T * DC * 4);
+  // dV sweep: v of the group's columns, for the in-chunk dlambda
+  constexpr bool INTRA = MODE == 0 && !PREP;
+  const bool intra = INTRA && a.intra_part != nullptr;
+  const rsrc_t vr = make_rsrc(static_cast<const bf16*>(a.v) + bhT * DC, T * DC * 2);
+  _Float16* Vh = reinterpret_cast<_Float16*>(smem + LY::VH);
+  int* ev_s = reinterpret_cast<int*>(smem + LY::EV);
+  float* isl = reinterpret_cast<float*>(smem + LY::ISL);
   const int own0 = hh ? 1 : 0, own1 = hh ? 2 : 3;
   const int oth0 = hh ? 0 : 1, oth1 = hh ? 3 : 2;
   // levels held in registers: the chunk-level bits below S; in the pre-pass
@@ -274,7 +315,7 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
   }
 
   // ---- register prefetch of one chunk ----------------------------------------
-  u32x4 pc[2][2], px8[2], pa[2];
+  u32x4 pc[2][2], px8[2], pa[2], pv8;
   float plam[2], pla;
   const uint32_t off_a = static_cast<uint32_t>((tid >> 3) * DC + col0 + (tid & 7) * 8);
   auto prefetch = [&](int n) {
@@ -301,6 +342,7 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
     if constexpr (MODE == 0) {
       pa[0] = load_u4(ar, (ce + off_a) * 4);
       pa[1] = load_u4(ar, (ce + off_a) * 4 + 16);
+      if constexpr (INTRA) pv8 = load_u4(vr, (ce + off_a) * 2);
     } else {
       pa[0] = load_u4(ar, (ce + off_a) * 2);
     }
@@ -367,6 +409,21 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
     dlev[r] = level_of(li, 4 * g4 + r);
     dmask |= (4 * g4 + r >= li ? 1u : 0u) << r;
   }
+  // chunk nc's in-chunk dlambda: one thread per (row, level); level 5 is the
+  // key block next to the row's (odd row blocks), level 6 key blocks 0 and 1
+  // (row blocks 2 and 3)
+  auto flush_intra = [&](int nc) {
+    if (tid < C * (LOGC + 1)) {
+      const float* sl = isl + (nc & 1) * (C * 8);
+      const int row = tid / (LOGC + 1), lv = tid - row * (LOGC + 1);
+      const int tb = row >> 4, t = nc * C + row;
+      float x;
+      if (lv <= 4) x = sl[row * 8 + lv];
+      else if (lv == 5) x = (tb & 1) ? sl[row * 8 + 5 + tb - 1] : 0.f;
+      else x = tb >= 2 ? sl[row * 8 + 5] + sl[row * 8 + 6] : 0.f;
+      if (t < T) a.intra_part[(((size_t)dg * a.BH + bh) * T + t) * 8 + lv] = x;
+    }
+  };
   f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int n = n1 - 1; n >= n0; --n) {
     const int tok0 = n * C, par = n & 1;
@@ -406,6 +463,13 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
       *reinterpret_cast<f16x8*>(Ah + row * LDA + col) = h;
       if constexpr (MODE == 0 && !PREP) *reinterpret_cast<f16x8*>(Al + row * LDA + col) = av.residual(e2, h);
       if ((tid & 7) == 0) ea_s[row] = e2;
+      if constexpr (INTRA) {
+        Row8 vv;
+        vv.from_bf16(pv8);
+        const int e4 = scale_exp(row8_max(vv.amax()));
+        *reinterpret_cast<f16x8*>(Vh + row * LDA + col) = vv.scaled(e4);
+        if ((tid & 7) == 0) ev_s[row] = e4;
+      }
     }
     if (tid * 2 < C * L) {
       lam_s[tid * 2] = plam[0];
@@ -428,6 +492,9 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
         const int t1 = tp + 16 * own1 + 4 * g4 + r;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), yr, (t0 * DC + col0 + c0 + li) * 4, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), yr, (t1 * DC + col0 + c0 + li) * 4, 0, 0);
+      }
+      if constexpr (INTRA) {
+        if (intra) flush_intra(n + 1);
       }
     }
     if (n > n0) prefetch(n - 1);
@@ -465,16 +532,54 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
           const f32x4 clt = *reinterpret_cast<const f32x4*>(cl_s + 16 * tb + 4 * g4);
           const i32x4 ect = *reinterpret_cast<const i32x4*>(ec_s + 16 * tb + 4 * g4);
           const i32x4 eat = *reinterpret_cast<const i32x4*>(ea_s + 16 * tb + 4 * g4);
-          float pv[4];
+          float pv[4], ev[4];
           float mx = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int ti = 16 * tb + 4 * g4 + r;
             const float ex = clt[r] + sfac + static_cast<float>(ect[r] + eat[r]);
             const float lam = tb > sb ? lam_s[ti * L + 4 + (32 - __clz(sb ^ tb))] : lam_s[ti * L + dlev[r]];
-            const float x = acc[it][r] * lam * __builtin_amdgcn_exp2f(ex);
+            ev[r] = acc[it][r] * __builtin_amdgcn_exp2f(ex);  // the pair's weight before lambda, times 2^ea_t
+            const float x = ev[r] * lam;
             pv[r] = (tb > sb || ((dmask >> r) & 1)) ? x : 0.f;
             mx = fmaxf(mx, fabsf(pv[r]));
+          }
+          if constexpr (INTRA) {
+            if (intra) {
+              // in-chunk dlambda over this group's columns:
+              //   D[t,s] = (dO_t . v_s)(q_t . k_s) exp(cum_t - cum_s)
+              // dO_t . v_s from the fp16 hi + lo dO rows and the scaled v rows
+              // (the diagonal terms cancel in the decay gradient, so they
+              // keep ~2^-20); rows summed over s per level
+              f32x4 s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int ks = 0; ks < 2; ++ks) {
+                const f16x8 vb = *reinterpret_cast<const f16x8*>(Vh + (16 * sb + li) * LDA + 32 * ks + 8 * g4);
+                const f16x8 ah = *reinterpret_cast<const f16x8*>(Ah + (16 * tb + li) * LDA + 32 * ks + 8 * g4);
+                const f16x8 al = *reinterpret_cast<const f16x8*>(Al + (16 * tb + li) * LDA + 32 * ks + 8 * g4);
+                s1 = mma32(ah, vb, s1);
+                s1 = mma32(al, vb, s1);
+              }
+              const float evs = ldexp_(1.f, ev_s[si]);
+              float d[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) d[r] = (tb > sb || ((dmask >> r) & 1)) ? (s1[r] * evs) * ev[r] : 0.f;
+              float* slot = isl + par * (C * 8) + (16 * tb + 4 * g4 + (li >> 2)) * 8;
+              const bool writer = (li & 3) == 0;
+              if (tb > sb) {
+                const float z = rowsum16(d, li);
+                if (writer) slot[5 + sb] = z;
+              } else {
+#pragma unroll
+                for (int lv = 0; lv <= 4; ++lv) {
+                  float x[4];
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) x[r] = dlev[r] == lv ? d[r] : 0.f;
+                  const float z = rowsum16(x, li);
+                  if (writer) slot[lv] = z;
+                }
+              }
+            }
           }
           // fp16 hi + lo: the in-chunk terms carry the diagonal ones, which
           // cancel in the decay gradient (dO_t . O_t - v_t . dV_t)
@@ -678,6 +783,9 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
       const int t1 = tp + 16 * own1 + 4 * g4 + r;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), yr, (t0 * DC + col0 + c0 + li) * 4, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), yr, (t1 * DC + col0 + c0 + li) * 4, 0, 0);
+    }
+    if constexpr (INTRA) {
+      if (intra) flush_intra(n0);
     }
   }
 }
