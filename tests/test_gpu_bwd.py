@@ -149,3 +149,27 @@ def test_bwd_ten_segments_sampled():
     assert_parity(grads[4][bh][idx], dlam, BF16_TOL, "dlam rows T=20000")
     assert_parity(grads[1][bh][idx], dk_, BF16_TOL, "dk cols T=20000")
     assert_parity(grads[2][bh][idx], dv_, BF16_TOL, "dv cols T=20000")
+
+
+@pytest.mark.parametrize("scale", [(8.0, 1e-6), (0.05, 1e3)], ids=["big_qk_tiny_dout", "small_qk_big_dout"])
+def test_bwd_input_scales(scale):
+    """The fp16 register-state sweeps (dQ, dK, dV and the in-chunk dlambda)
+    carry power-of-two scales per row, per score tile and per level state so
+    that no fp16 operand leaves fp16's normal range: q and k scaled by 8 with
+    dO by 1e-6, and q, k by 0.05 with dO by 1e3, against the oracle on the
+    same (bf16-rounded) inputs.  T=4200: three 32-chunk segments, weak decay."""
+    sq, sd = scale
+    case = (1, 1, 4200, 128, 128, 64, "bf16", "weak")
+    w, inp, dout = _inputs(case, seed=21)
+    q, k, v, la, lam = inp
+    q = (q.float() * sq).to(q.dtype)
+    k = (k.float() * sq).to(k.dtype)
+    dout = dout * sd
+    inp = (q, k, v, la, lam)
+    out = torch.from_numpy(oracle.forward(*inp).astype(np.float32))
+    announce(f"bwd input scales {scale}")
+    grads = ll.bwd(*to_dev(*inp), out.cuda(), dout.cuda(), C=64)
+    torch.cuda.synchronize()
+    want = oracle.backward(*inp, dout)
+    for name, g, ref in zip(NAMES, grads, want):
+        assert_parity(g.cpu().numpy(), ref, BF16_TOL, f"{name} scales {scale}")

@@ -219,6 +219,24 @@ def test_register_state_kernel_parity(case):
     assert_parity(lds.cpu().numpy(), want, BF16_TOL, f"lds-state {case}")
 
 
+@pytest.mark.parametrize("scale", [(8.0, 1e-4), (0.05, 1e3)], ids=["big_qk_small_v", "small_qk_big_v"])
+def test_register_state_input_scales(scale):
+    """The register-state sweep's fp16 operands (Q per chunk, the level states
+    per wave) carry power-of-two scales chosen from their maxima, so extreme
+    input magnitudes stay inside fp16's normal range: q, k scaled by 8 with v
+    by 1e-4, and q, k by 0.05 with v by 1e3, weak decay, 16-chunk segments."""
+    sq, sv = scale
+    w = W.FwdWorkload("rs_scale", 1, 1, 4096, 128, 128, 64, "bf16", decay="weak", seed=31)
+    q, k, v, la, lam = W.make_fwd_inputs(w)
+    q = (q.float() * sq).to(q.dtype)
+    k = (k.float() * sq).to(k.dtype)
+    v = (v.float() * sv).to(v.dtype)
+    announce(f"register-state input scales {scale}")
+    out = ll.fwd_ex(*to_dev(q, k, v, la, lam), C=64, seg_log2=4, kernel=ll.KERNEL_REGISTER_STATE)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), oracle.forward(q, k, v, la, lam), BF16_TOL, f"register-state scales {scale}")
+
+
 def test_register_state_kernel_rejects_other_shapes():
     w = W.FwdWorkload("rs_no", 1, 1, 128, 128, 48, 64, "bf16")
     dq, dk_, dv_, dla, dlam = to_dev(*W.make_fwd_inputs(w))
