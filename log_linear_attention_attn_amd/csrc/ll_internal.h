@@ -92,10 +92,13 @@ struct BwdArgs {
   // dK and dV already formed by the reverse register-state sweep
   // (launch_bwd_rev): the backward skips its own
   int kv_done = 0;
-  // the in-chunk dlambda as partial sums of the dV sweep
-  // ([intra_parts][BH][T][8]): the backward sums them instead of its own pass
+  // the reverse sweeps' per-row records ([intra_parts][BH][T][8]: the
+  // in-chunk dlambda in words 0..6, v . dV in word 7): the backward forms
+  // dlam and dc from them in one pass, and then needs dc_blk, the totals of
+  // dc over each 64-row block of a (b,h) ([BH][ceil(T / 64)])
   const float* dlam_intra_part = nullptr;
   int intra_parts = 0;
+  double* dc_blk = nullptr;
 };
 
 // Reverse register-state sweep for dV and dK (bf16, C = 64, dk = dv = 128,

@@ -382,10 +382,13 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   // the workspace
   const bool kv_rev = dtype == LL_BF16 && ll::bwd_rev_ok(C, dk, dv, G, T, p.L);
   const size_t rws = kv_rev ? align256(ll::bwd_rev_workspace(p.BH, T)) : 0;
-  // the dV sweep's in-chunk dlambda partials, one per 64-column group of dv
+  // the dV sweep's row records (in-chunk dlambda and v . dV), one per
+  // 64-column group of dv, and the 64-row block totals of dc
   const size_t iws = kv_rev ? align256((size_t)(dv / 64) * p.BH * T * 8 * sizeof(float)) : 0;
+  const size_t bws = kv_rev ? align256((size_t)p.BH * ((T + 63) / 64) * sizeof(double)) : 0;
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, part + dcb + 2 * per_head + fws + rws + iws, stream) != hipSuccess) return LL_ERR_HIP;
+  if (hipMallocAsync(&ws, part + dcb + 2 * per_head + fws + rws + iws + bws, stream) != hipSuccess)
+    return LL_ERR_HIP;
   char* wsb = static_cast<char*>(ws);
   float* dq_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb) : dq;
   float* dk_h = G > 1 ? reinterpret_cast<float*>(wsb + part + dcb + per_head) : dk_out;
@@ -435,6 +438,7 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
     a.kv_done = 1;
     a.dlam_intra_part = ra.intra_part;
     a.intra_parts = dv / 64;
+    a.dc_blk = reinterpret_cast<double*>(wsb + part + dcb + 2 * per_head + fws + rws + iws);
   }
   if (st == LL_OK) st = ll::launch_bwd(dtype, C, a, stream);
   if (st == LL_OK && G > 1) {

@@ -29,6 +29,11 @@
 //   bwd_dlam_intra_kernel  dlam of the in-chunk levels.
 //   bwd_dlam_inter_kernel  dlam of the chunk levels from the partials.
 //   bwd_dcum_kernel, bwd_dlog_a_kernel  dlog_a.
+//   bwd_dlam_rows_kernel, bwd_dlog_a_blk_kernel  with the reverse
+//                   register-state sweeps (whose dV sweep writes per-row
+//                   records of the in-chunk dlam and of v . dV): all of
+//                   dlam and dc in one pass, then dlog_a as a scan over
+//                   (b,h, 1024-row) workgroups.
 // Each output row slice of 16 columns belongs to one workgroup (no atomics).
 // All products run as fp32 matrix-core instructions (v_mfma_f32_16x16x4f32);
 // bf16 inputs are widened when staged.
@@ -528,21 +533,138 @@ __global__ void __launch_bounds__(C / 16 * 64) bwd_dlam_intra_kernel(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// bwd_dlam_intra_sum_kernel: dlam of the in-chunk levels 0 .. logc as the
-// in-order sum of the reverse dV sweep's per-column-group partials
-// ([nparts][BH][T][8]).  One thread per (b,h, t, level).
+// bwd_dlam_rows_kernel: everything per (b,h, t) row that follows the sweeps
+// when the reverse register-state sweeps wrote their per-column-group row
+// records ([nin][BH][T][8]: words 0..logc the in-chunk dlambda, word 7
+// v_t . dV_t over the group's columns): dlam of the in-chunk levels (the
+// records summed in group order), of the chunk levels (the dQ sweep's
+// per-slice partials summed in slice order, 0 past the levels the row
+// reaches), and
+//   dc_t = dO_t . O_t - v_t . dV_t = sum_l lambda[t,l] dlambda[t,l] - sum_g (v . dV)_g
+// in fp64, with the total of dc over the block for the decay gradient's scan.
+// A workgroup takes 64 consecutive rows of one (b,h): one thread per (row,
+// level) forms and writes dlam (consecutive threads on consecutive words),
+// then four threads per row sum its products from LDS.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) bwd_dlam_intra_sum_kernel(BwdArgs a, int logc, int nparts) {
-  const int nl = logc + 1;
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // (bh * T + t) * nl + l
-  if (e >= (long long)a.BH * a.T * nl) return;
-  const long long row = e / nl;
-  const int l = static_cast<int>(e - row * nl);
-  if (l >= a.L) return;
-  const size_t pstride = (size_t)a.BH * a.T * 8;
-  float x = 0.f;
-  for (int p = 0; p < nparts; ++p) x += a.dlam_intra_part[p * pstride + (size_t)row * 8 + l];
-  a.dlam[(size_t)row * a.L + l] = x;
+constexpr int kRowBlk = 64;     // rows per workgroup of bwd_dlam_rows_kernel
+constexpr int kScanRows = 1024; // rows per workgroup of bwd_dlog_a_blk_kernel
+
+template <int NP>
+__global__ void __launch_bounds__(256) bwd_dlam_rows_kernel(BwdArgs a, int logc, int nin, int nout) {
+  constexpr int R = kRowBlk;
+  __shared__ float s_lam[R * 32], s_dl[R * 32];  // L <= 32
+  __shared__ double s_w[4];
+  const int ntb = (a.T + R - 1) / R;
+  const int bh = blockIdx.x / ntb, tb = blockIdx.x - bh * ntb;
+  const long long rows = (long long)a.BH * a.T;
+  const long long r0 = (long long)bh * a.T + (long long)tb * R;
+  const int nr = min(R, a.T - tb * R);
+  const int L = a.L, nl = logc + 1, nslot = a.nslot, tid = threadIdx.x;
+  const size_t istride = (size_t)rows * 8, pstride = (size_t)rows * nslot;
+  const float* __restrict__ in = a.dlam_intra_part;
+  const float inv_l = 1.f / static_cast<float>(L);
+  // (row, level) elements e = tid + 256 i: every element's loads are issued
+  // before any sum (at most NP group and NP slice partials)
+  constexpr int EPT = (R * 32) / 256;
+  float part_v[EPT][NP], lam_v[EPT];
+  bool is_in[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + 256 * i;
+    // e / L: e < 2^11, so the rounded quotient of e + 1/2 is exact
+    const int rr = __float2int_rz((static_cast<float>(e) + 0.5f) * inv_l), l = e - rr * L;
+    const size_t row = r0 + rr;
+    const bool ok = e < nr * L;
+    is_in[i] = l < nl;
+    const bool sl_ok = !is_in[i] && l - nl < nslot;
+    const float* __restrict__ src = is_in[i] ? in + row * 8 + l : a.dlam_part + row * nslot + (l - nl);
+    const size_t stride = is_in[i] ? istride : pstride;
+    const int np = is_in[i] ? nin : (sl_ok ? nout : 0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) part_v[i][p] = ok && p < np ? src[p * stride] : 0.f;
+    lam_v[i] = ok ? a.lam[r0 * L + e] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + 256 * i;
+    float y = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) y += part_v[i][p];  // partials past np are +0: the in-order sum
+    if (e < nr * L) {
+      a.dlam[r0 * L + e] = y;
+      s_lam[e] = lam_v[i];
+      s_dl[e] = y;
+    }
+  }
+  __syncthreads();
+  // row rr = tid / 4: its quarter q of the levels, then the row's sum
+  const int rr = tid >> 2, q = tid & 3;
+  double x = 0.0;
+  if (rr < nr)
+    for (int l = q; l < L; l += 4) x += (double)s_lam[rr * L + l] * s_dl[rr * L + l];
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  if (rr < nr && q == 0) {
+    const size_t row = r0 + rr;
+    for (int p = 0; p < nin; ++p) x -= (double)in[p * istride + row * 8 + 7];
+    a.dc[row] = x;
+  } else {
+    x = 0.0;
+  }
+  // block total: the 16 rows of each wave, then the four waves in order
+#pragma unroll
+  for (int off = 4; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  if ((tid & 63) == 0) s_w[tid >> 6] = x;
+  __syncthreads();
+  if (tid == 0) a.dc_blk[(size_t)bh * ntb + tb] = ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+}
+
+// bwd_dlog_a_blk_kernel: dlog_a = reverse prefix sum of dc over T (fp64),
+// one workgroup per (b,h, 1024 rows): the later rows' total from the 64-row
+// block totals, then a reverse scan of the workgroup's rows (four per thread).
+__global__ void __launch_bounds__(256) bwd_dlog_a_blk_kernel(BwdArgs a) {
+  constexpr int S = kScanRows, PER = S / 256;
+  __shared__ double part[256];
+  const int T = a.T, tid = threadIdx.x;
+  const int nsb = (T + S - 1) / S, ntb = (T + kRowBlk - 1) / kRowBlk;
+  const int bh = blockIdx.x / nsb, sb = blockIdx.x - bh * nsb;
+  // total of the blocks after this workgroup's rows
+  const int tb0 = (sb + 1) * (S / kRowBlk);
+  double s = 0.0;
+  for (int tb = tb0 + tid; tb < ntb; tb += 256) s += a.dc_blk[(size_t)bh * ntb + tb];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) part[tid] += part[tid + off];
+    __syncthreads();
+  }
+  const double later = part[0];
+  __syncthreads();
+  // this thread's rows t0 .. t0 + PER - 1
+  const double* __restrict__ d = a.dc + (size_t)bh * T;
+  float* __restrict__ out = a.dlog_a + (size_t)bh * T;
+  const int t0 = sb * S + tid * PER;
+  double v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = t0 + i < T ? d[t0 + i] : 0.0;
+  double own = 0.0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) own += v[i];
+  part[tid] = own;
+  __syncthreads();
+  // inclusive suffix sums of the thread totals (log-step scan)
+  for (int off = 1; off < 256; off <<= 1) {
+    const double u = tid + off < 256 ? part[tid + off] : 0.0;
+    __syncthreads();
+    part[tid] += u;
+    __syncthreads();
+  }
+  double run = later + (tid + 1 < 256 ? part[tid + 1] : 0.0);
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    run += v[i];
+    if (t0 + i < T) out[t0 + i] = static_cast<float>(run);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -740,10 +862,21 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   }
   }
   if (a.intra_parts > 0) {
-    const long long elems = (long long)a.BH * a.T * (Lg<C>::v + 1);
-    hipLaunchKernelGGL(bwd_dlam_intra_sum_kernel, dim3(static_cast<unsigned>((elems + 255) / 256)), dim3(256), 0, s,
-                       a, Lg<C>::v, a.intra_parts);
-  } else if (sizeof(IT) == 2 && C == 64 && bwd_dlam_intra16_ok(a)) {
+    // the reverse dV sweep's row records: one pass forms dlam and dc
+    const long long nb = (long long)a.BH * ((a.T + kRowBlk - 1) / kRowBlk);
+    const long long ns = (long long)a.BH * ((a.T + kScanRows - 1) / kScanRows);
+    const int nout = a.dq_done ? a.dlam_parts : a.dk / 16;
+    if (nb > 0x7fffffffLL || !a.dc_blk || a.L > 32 || a.intra_parts > 8 || nout > 8) return LL_ERR_UNSUPPORTED;
+    if (a.intra_parts <= 2 && nout <= 2)
+      hipLaunchKernelGGL(bwd_dlam_rows_kernel<2>, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a, Lg<C>::v,
+                         a.intra_parts, nout);
+    else
+      hipLaunchKernelGGL(bwd_dlam_rows_kernel<8>, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a, Lg<C>::v,
+                         a.intra_parts, nout);
+    hipLaunchKernelGGL(bwd_dlog_a_blk_kernel, dim3(static_cast<unsigned>(ns)), dim3(256), 0, s, a);
+    return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
+  }
+  if (sizeof(IT) == 2 && C == 64 && bwd_dlam_intra16_ok(a)) {
     const int st = launch_bwd_dlam_intra16(a, s);
     if (st != LL_OK) return st;
   } else {

@@ -67,11 +67,13 @@ struct Lay<false> {
   static constexpr int KE = WT + NLEV * C * 2;         // the states' new exponents [NLEV], tile exponents [16]
   static constexpr int LAM = KE + 32 * 4;              // lambda rows of the chunk [64][L]
   // dV sweep only: v of the group's columns, fp16 [64][LDA], its row
-  // exponents [64], and the in-chunk dlambda row sums [2][64][8]
+  // exponents [64], the in-chunk dlambda row sums [2][64][8] and the v . dV
+  // row sums of the four 16-column slices [2][64][4]
   static constexpr int VH = LAM + C * LMAX * 4;
   static constexpr int EV = VH + C * LDA * 2;
   static constexpr int ISL = EV + C * 4;
-  static constexpr int BYTES = ISL + 2 * C * 8 * 4;
+  static constexpr int VSL = ISL + 2 * C * 8 * 4;
+  static constexpr int BYTES = VSL + 2 * C * 4 * 4;
 };
 template <>
 struct Lay<true> {
@@ -82,7 +84,7 @@ struct Lay<true> {
   static constexpr int KE = WT + NLEV * C * 2;
   static constexpr int LAM = KE + 32 * 4;
   static constexpr int BYTES = LAM + C * LMAX * 4;
-  static constexpr int XH = 0, AL = 0, PS = 0, XC = 0, RF = 0, VH = 0, EV = 0, ISL = 0;  // not used by the pre-pass
+  static constexpr int XH = 0, AL = 0, PS = 0, XC = 0, RF = 0, VH = 0, EV = 0, ISL = 0, VSL = 0;  // not used by the pre-pass
 };
 // register levels of the pre-pass variant that shares a CU with another
 constexpr int NL_SMALL = 3;
@@ -168,6 +170,31 @@ __device__ __forceinline__ float rowsum16(const float x[4], int li) {
   z += dpp_mov<0xb1>(z);  // quad_perm [1,0,3,2]
   z += dpp_mov<0x4e>(z);  // quad_perm [2,3,0,1]
   return z;
+}
+// Sums over the 16 lanes of a 16-lane group of x[0..7]; lanes li and li ^ 1
+// return the total of x[(li >> 1) & 7]: a reduce-scatter over lane bits 3,
+// 2 and 1 as above, then a sum over lane bit 0.
+__device__ __forceinline__ float rowsum16x8(const float x[8], int li) {
+  const bool h8 = li & 8, h4 = li & 4, h2 = li & 2;
+  float y[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float sd = h8 ? x[m] : x[4 + m];
+    asm volatile("" : "+v"(sd));
+    y[m] = (h8 ? x[4 + m] : x[m]) + dpp_mov<0x128>(sd);  // row_ror 8: lane li ^ 8
+  }
+  float z[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    float sd = h4 ? y[m] : y[2 + m];
+    asm volatile("" : "+v"(sd));
+    z[m] = (h4 ? y[2 + m] : y[m]) + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sd), 0x101F));
+  }
+  float sd = h2 ? z[0] : z[1];
+  asm volatile("" : "+v"(sd));
+  float u = (h2 ? z[1] : z[0]) + dpp_mov<0x4e>(sd);  // quad_perm [2,3,0,1]: lane li ^ 2
+  u += dpp_mov<0xb1>(u);                              // quad_perm [1,0,3,2]: lane li ^ 1
+  return u;
 }
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_add(float x) {
@@ -290,6 +317,7 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
   _Float16* Vh = reinterpret_cast<_Float16*>(smem + LY::VH);
   int* ev_s = reinterpret_cast<int*>(smem + LY::EV);
   float* isl = reinterpret_cast<float*>(smem + LY::ISL);
+  float* vsl = reinterpret_cast<float*>(smem + LY::VSL);
   const int own0 = hh ? 1 : 0, own1 = hh ? 2 : 3;
   const int oth0 = hh ? 0 : 1, oth1 = hh ? 3 : 2;
   // levels held in registers: the chunk-level bits below S; in the pre-pass
@@ -412,16 +440,67 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
   // chunk nc's in-chunk dlambda: one thread per (row, level); level 5 is the
   // key block next to the row's (odd row blocks), level 6 key blocks 0 and 1
   // (row blocks 2 and 3)
+  // the helpers below derive their lane indices from an opaque copy of the
+  // thread index, so the compiler recomputes them per chunk instead of
+  // keeping them (and what it derives from them) live across the loop
+  auto opaque = [](int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
   auto flush_intra = [&](int nc) {
-    if (tid < C * (LOGC + 1)) {
+    const int tid_ = opaque(tid);
+    if (tid_ < C * (LOGC + 1)) {
       const float* sl = isl + (nc & 1) * (C * 8);
-      const int row = tid / (LOGC + 1), lv = tid - row * (LOGC + 1);
+      const int row = tid_ / (LOGC + 1), lv = tid_ - row * (LOGC + 1);
       const int tb = row >> 4, t = nc * C + row;
       float x;
       if (lv <= 4) x = sl[row * 8 + lv];
       else if (lv == 5) x = (tb & 1) ? sl[row * 8 + 5 + tb - 1] : 0.f;
       else x = tb >= 2 ? sl[row * 8 + 5] + sl[row * 8 + 6] : 0.f;
       if (t < T) a.intra_part[(((size_t)dg * a.BH + bh) * T + t) * 8 + lv] = x;
+    }
+  };
+  // v_t . dV_t over the group's columns, the term the decay gradient
+  // subtracts (the in-chunk products of this sweep are exact enough for the
+  // cancellation of its diagonal terms against dO_t . O_t).  The wave's own
+  // rows of chunk nv take v from global memory (read two chunks earlier, so
+  // mostly from L2) at the chunk's store, where dV is final, loaded and used
+  // within the store so that no register is held across the sweep's phases;
+  // the reduction over the wave's 16 columns goes to word cs of the row in
+  // the chunk's parity buffer, and the four slices' words are added (in
+  // slice order) into word 7 of the row record one chunk later, after a
+  // barrier
+  constexpr bool VDV = INTRA;
+  const bool vdv = intra;
+  unsigned short vq[2][4];
+  auto load_vdv = [&](int nv) {
+    const int ln = opaque(lane);
+    const int off = ((nv * C + 4 * (ln >> 4)) * DC + col0 + c0 + (ln & 15)) * 2;
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vq[o][r] = __builtin_amdgcn_raw_buffer_load_b16(
+            vr, static_cast<uint32_t>(off + ((16 * (o ? own1 : own0) + r) * DC) * 2), 0, 0);
+  };
+  auto vdv_rows = [&](int nv, const float f0[4], const float f1[4]) {
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = __uint_as_float(static_cast<uint32_t>(vq[0][r]) << 16) * f0[r];
+      x[4 + r] = __uint_as_float(static_cast<uint32_t>(vq[1][r]) << 16) * f1[r];
+    }
+    const int ln = opaque(lane), lj = ln & 15;
+    const float sum = rowsum16x8(x, lj);
+    const int j = (lj >> 1) & 7;
+    if (!(lj & 1)) vsl[((nv & 1) * C + 16 * ((j >> 2) ? own1 : own0) + 4 * (ln >> 4) + (j & 3)) * 4 + cs] = sum;
+  };
+  auto flush_vdv = [&](int nv) {
+    const int tid_ = opaque(tid);
+    if (tid_ < C) {
+      const float* sl = vsl + ((nv & 1) * C + tid_) * 4;
+      const int t = nv * C + tid_;
+      if (t < T) a.intra_part[(((size_t)dg * a.BH + bh) * T + t) * 8 + 7] = ((sl[0] + sl[1]) + sl[2]) + sl[3];
     }
   };
   f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -478,6 +557,9 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
     const float cl2 = wave_prefix_sum(pla) * kLog2e;  // lane = token
     const float A2 = uniform(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl2), 63)));
     if (w == 0) cl_s[lane] = cl2;
+    if constexpr (VDV) {
+      if (vdv && n + 1 < n1) load_vdv(n + 1);
+    }
     __syncthreads();
 
     // ---------------- chunk n + 1: add the partner's partial sums, store ---------
@@ -486,15 +568,24 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
       const f32x4 x0 = Xc[(partner * 2 + 0) * 64 + lane];
       const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
       const int tp = tok0 + C;
+      float f0[4], f1[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t0 = tp + 16 * own0 + 4 * g4 + r;
         const int t1 = tp + 16 * own1 + 4 * g4 + r;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), yr, (t0 * DC + col0 + c0 + li) * 4, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), yr, (t1 * DC + col0 + c0 + li) * 4, 0, 0);
+        f0[r] = O0[r] + x0[r];
+        f1[r] = O1[r] + x1[r];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f0[r]), yr, (t0 * DC + col0 + c0 + li) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f1[r]), yr, (t1 * DC + col0 + c0 + li) * 4, 0, 0);
       }
       if constexpr (INTRA) {
         if (intra) flush_intra(n + 1);
+      }
+      if constexpr (VDV) {
+        if (vdv) {
+          vdv_rows(n + 1, f0, f1);
+          if (n + 2 < n1) flush_vdv(n + 2);
+        }
       }
     }
     if (n > n0) prefetch(n - 1);
@@ -772,20 +863,34 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
     if (tid == 0 && dg == 0) a.seg_tot2[bh * a.nseg + seg] = tot2;
   } else {
     // ---------------- first chunk of the segment: partner sums, store -------------
+    if constexpr (VDV) {
+      if (vdv) load_vdv(n0);
+    }
     __syncthreads();
     const int partner = w ^ 4;
     const f32x4 x0 = Xc[(partner * 2 + 0) * 64 + lane];
     const f32x4 x1 = Xc[(partner * 2 + 1) * 64 + lane];
     const int tp = n0 * C;
+    float f0[4], f1[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t0 = tp + 16 * own0 + 4 * g4 + r;
       const int t1 = tp + 16 * own1 + 4 * g4 + r;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O0[r] + x0[r]), yr, (t0 * DC + col0 + c0 + li) * 4, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O1[r] + x1[r]), yr, (t1 * DC + col0 + c0 + li) * 4, 0, 0);
+      f0[r] = O0[r] + x0[r];
+      f1[r] = O1[r] + x1[r];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f0[r]), yr, (t0 * DC + col0 + c0 + li) * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f1[r]), yr, (t1 * DC + col0 + c0 + li) * 4, 0, 0);
     }
     if constexpr (INTRA) {
       if (intra) flush_intra(n0);
+    }
+    if constexpr (VDV) {
+      if (vdv) {
+        vdv_rows(n0, f0, f1);
+        if (n0 + 1 < n1) flush_vdv(n0 + 1);
+        __syncthreads();
+        flush_vdv(n0);
+      }
     }
   }
 }
