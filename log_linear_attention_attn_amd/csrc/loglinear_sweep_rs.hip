@@ -870,13 +870,18 @@ fwd_rs_kernel(FwdArgs a) {
 // T_g = sum over segment g of exp(cum[end] - cum[s]) k_s v_s^T, written as
 // [dv][128] fp32, plus the segment's total log decay.  One 512-thread
 // workgroup per (b,h, segment, 64 dv columns); the segment is walked in
-// 64-token tiles.  Each tile's V is scaled by the decay to the tile's end and
-// split bf16 hi/lo once, at staging; K and V stay row-major in LDS (double
-// buffered, one barrier per tile, loads issued two tiles ahead) and are read
-// transposed.  Wave w keeps the
-// 64 x 16 block (dk half w>>2, columns 16(w&3)) of the running sum, which is
-// rescaled by each tile's total decay.  Workgroups of the same (b,h, segment)
-// sit on the same XCD so the second column group finds K in L2.
+// 64-token tiles from its end to its start, so each token's weight, the decay
+// from it to the segment's end, is the tile's in-tile suffix plus the running
+// total of the tiles already walked, and the running sum never needs a
+// rescale.  Each tile's V is scaled by those weights and split bf16 hi/lo
+// once, at staging; K and V stay row-major in LDS (double buffered, one
+// barrier per tile, loads issued two tiles ahead) and are read transposed.
+// Every tile's loads go through buffer resources over just that tile's rows
+// inside the segment (scalar work), so the per-lane offsets are constants and
+// rows past the segment's end, or tiles before its start, read zero.  Wave w
+// keeps the 64 x 16 block (dk half w>>2, columns 16(w&3)) of the running sum.
+// Workgroups of the same (b,h, segment) sit on the same XCD so the second
+// column group finds K in L2.
 namespace ss {
 constexpr int NTH = 512;
 constexpr int KS_OFF = 0;
@@ -905,34 +910,41 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
   const int s0 = g * segtok, s1 = min(T, s0 + segtok);
   const int dv0 = dg * 64;
   const size_t bhT = (size_t)bh * T;
-  const rsrc_t kr = make_rsrc(static_cast<const bf16*>(a.k) + (size_t)(bh / a.G) * T * dk, T * dk * 2);
-  const rsrc_t vr = make_rsrc(static_cast<const bf16*>(a.v) + bhT * dv, T * dv * 2);
-  const rsrc_t lar = make_rsrc(a.log_a + bhT, T * 4);
+  const bf16* kb = static_cast<const bf16*>(a.k) + (size_t)(bh / a.G) * T * dk;
+  const bf16* vb = static_cast<const bf16*>(a.v) + bhT * dv;
+  const float* lb = a.log_a + bhT;
+  // this lane's byte offsets inside a tile: K rows v >> 4 (16-byte pieces
+  // past dk fall outside every resource), V row tid >> 3, log_a token lane
+  uint32_t ko[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int v = tid + ss::NTH * i, row = v >> 4, col = (v & 15) * 8;
+    ko[i] = col < dk ? static_cast<uint32_t>((row * dk + col) * 2) : kOutOfRange;
+  }
+  const uint32_t vo = static_cast<uint32_t>(((tid >> 3) * dv + dv0 + (tid & 7) * 8) * 2);
 
   // Register prefetch two tiles ahead: tiles alternate between two register
-  // sets (and the two LDS buffers); tokens at or past s1 read zero (offsets
-  // out of the resource's range).
+  // sets (and the two LDS buffers).
   struct Regs {
     bf16x8 k[2], v;
     float la;
   };
   auto prefetch = [&](Regs& r, int b0) {
-    r.la = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-        lar, b0 + lane < s1 ? (b0 + lane) * 4 : kOutOfRange, 0, 0));
+    const int nrow = b0 >= s0 ? min(C, s1 - b0) : 0;  // rows of the tile inside the segment
+    const int t0 = max(b0, 0);
+    const rsrc_t kr = make_rsrc(kb + (size_t)t0 * dk, static_cast<uint32_t>(nrow * dk * 2));
+    const rsrc_t vr = make_rsrc(vb + (size_t)t0 * dv, static_cast<uint32_t>(nrow * dv * 2));
+    const rsrc_t lar = make_rsrc(lb + t0, static_cast<uint32_t>(nrow * 4));
+    r.la = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lar, lane * 4, 0, 0));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int v = tid + ss::NTH * i, row = v >> 4, col = (v & 15) * 8;
-      const bool ok = b0 + row < s1 && col < dk;
-      r.k[i] = load_b128(kr, ok ? ((b0 + row) * dk + col) * 2 : kOutOfRange);
-    }
-    const int row = tid >> 3;
-    r.v = load_b128(vr, b0 + row < s1 ? ((b0 + row) * dv + dv0 + (tid & 7) * 8) * 2 : kOutOfRange);
+    for (int i = 0; i < 2; ++i) r.k[i] = load_b128(kr, ko[i]);
+    r.v = load_b128(vr, vo);
   };
 
   f32x4 S[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float Aseg = 0.f;
+  float later = 0.f;  // total log decay of the tiles after the current one
   // one 64-token tile from register set r into LDS buffer buf, then its MFMAs
   auto tile = [&](Regs& r, int buf, int b0) {
     // keep the scheduler from hoisting this tile's register work above the
@@ -942,10 +954,10 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
     bf16* Ks = reinterpret_cast<bf16*>(base + ss::KS_OFF);
     bf16* Vh = reinterpret_cast<bf16*>(base + ss::VH_OFF);
     bf16* Vl = reinterpret_cast<bf16*>(base + ss::VL_OFF);
-    // decay of each token to the tile's last token, every wave redundantly
+    // decay of each token to the segment's last token, every wave redundantly
     const float cl = wave_prefix_sum(r.la);
     const float Ab = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63));
-    const float esf = __expf(Ab - cl);
+    const float esf = __expf(Ab - cl + later);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + ss::NTH * i, row = v >> 4, col = (v & 15) * 8;
@@ -965,14 +977,10 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
       *reinterpret_cast<bf16x8*>(Vh + row * LDV + col) = h;
       *reinterpret_cast<bf16x8*>(Vl + row * LDV + col) = l;
     }
-    prefetch(r, b0 + 2 * C);
+    later += Ab;
+    prefetch(r, b0 - 2 * C);
     __syncthreads();
 
-    const float fa = __expf(Ab);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) S[t][q] *= fa;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int vrow = (32 * ks + 8 * g4 + (li >> 2)) * LDV + c0 + 4 * (li & 3);
@@ -987,18 +995,19 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
         S[t] = mma(ka, vl, S[t]);
       }
     }
-    Aseg += Ab;
   };
-  // Every prefetch and tile is unconditional: tiles past s1 read zeros (k, v
-  // and log_a alike, so they add nothing and decay by exp(0)).  With a fixed
-  // count of loads per tile the wait for a tile's registers leaves the
+  // Tiles from the segment's last down to its first, two per iteration (an
+  // odd count ends with a tile before the segment: zeros, exp(0)); with a
+  // fixed count of loads per tile the wait for a tile's registers leaves the
   // following tile's loads in flight.
+  const int ntile = (s1 - s0 + C - 1) / C;
   Regs ra, rb;
-  prefetch(ra, s0);
-  prefetch(rb, s0 + C);
-  for (int b0 = s0; b0 < s1; b0 += 2 * C) {
+  int b0 = s0 + (ntile - 1) * C;
+  prefetch(ra, b0);
+  prefetch(rb, b0 - C);
+  for (int k = 0; k < ntile; k += 2, b0 -= 2 * C) {
     tile(ra, 0, b0);
-    tile(rb, 1, b0 + C);
+    tile(rb, 1, b0 - C);
   }
   // element r of S[t] is dk 64hh + 32(t>>1) + 8g4 + 4(t&1) + r, column c0 + li
   float* __restrict__ Tout =
@@ -1008,7 +1017,7 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
     *reinterpret_cast<f32x4*>(Tout + 32 * kl) = S[2 * kl];
     *reinterpret_cast<f32x4*>(Tout + 32 * kl + 4) = S[2 * kl + 1];
   }
-  if (tid == 0 && dg == 0) a.seg_decay[bh * a.nseg + g] = Aseg;
+  if (tid == 0 && dg == 0) a.seg_decay[bh * a.nseg + g] = later;
 }
 
 int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t stream) {
