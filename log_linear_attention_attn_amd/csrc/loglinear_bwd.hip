@@ -833,9 +833,8 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   } else {
     const int bytes = DqCfg<IT, C>::bytes(a.dv, a.L, a.nslot);
     if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<IT, C>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-      return LL_ERR_HIP;
+    static std::atomic<uint64_t> raised{0};  // once per device: to the maximum, any size fits
+    if (!raise_lds_limit(reinterpret_cast<const void*>(&bwd_dq_kernel<IT, C>), raised)) return LL_ERR_HIP;
     hipLaunchKernelGGL((bwd_dq_kernel<IT, C>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
   }
   // dV and dK (unless the reverse register-state sweep formed them already)
@@ -847,17 +846,15 @@ static int launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   {
     const int bytes = KvCfg<IT, C, 0>::bytes(a.dk, a.L, N, a.nslot);
     if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv_kernel<IT, C, 0>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-      return LL_ERR_HIP;
+    static std::atomic<uint64_t> raised{0};  // once per device: to the maximum, any size fits
+    if (!raise_lds_limit(reinterpret_cast<const void*>(&bwd_kv_kernel<IT, C, 0>), raised)) return LL_ERR_HIP;
     hipLaunchKernelGGL((bwd_kv_kernel<IT, C, 0>), dim3(a.BH * (a.dv / 16)), dim3(NT), bytes, s, a);
   }
   {
     const int bytes = KvCfg<IT, C, 1>::bytes(a.dv, a.L, N, a.nslot);
     if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv_kernel<IT, C, 1>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-      return LL_ERR_HIP;
+    static std::atomic<uint64_t> raised{0};  // once per device: to the maximum, any size fits
+    if (!raise_lds_limit(reinterpret_cast<const void*>(&bwd_kv_kernel<IT, C, 1>), raised)) return LL_ERR_HIP;
     hipLaunchKernelGGL((bwd_kv_kernel<IT, C, 1>), dim3(a.BH * (a.dk / 16)), dim3(NT), bytes, s, a);
   }
   }

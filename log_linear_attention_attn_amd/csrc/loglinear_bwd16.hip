@@ -852,9 +852,8 @@ bool bwd_dq16_ok(const BwdArgs& a) {
 
 int launch_bwd_dq16(const BwdArgs& a, hipStream_t s) {
   const int bytes = b16::DqLay::bytes(a.L);
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq16_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          bytes) != hipSuccess)
-    return LL_ERR_HIP;
+  static std::atomic<uint64_t> raised{0};  // once per device: to the maximum, any size fits
+  if (!raise_lds_limit(reinterpret_cast<const void*>(&bwd_dq16_kernel), raised)) return LL_ERR_HIP;
   hipLaunchKernelGGL(bwd_dq16_kernel, dim3(a.BH * (a.dk / 16)), dim3(b16::NT), bytes, s, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
@@ -981,16 +980,14 @@ int launch_bwd_kv16(const BwdArgs& a, hipStream_t s) {
   const int N = (a.T + b16::C - 1) / b16::C;
   {
     const int bytes = b16::KvLay<0>::bytes(a.L, N);
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv16_kernel<0>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-      return LL_ERR_HIP;
+    static std::atomic<uint64_t> raised{0};  // once per device: to the maximum, any size fits
+    if (!raise_lds_limit(reinterpret_cast<const void*>(&bwd_kv16_kernel<0>), raised)) return LL_ERR_HIP;
     hipLaunchKernelGGL(bwd_kv16_kernel<0>, dim3(a.BH * (a.dv / 16)), dim3(b16::NT), bytes, s, a);
   }
   {
     const int bytes = b16::KvLay<1>::bytes(a.L, N);
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv16_kernel<1>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-      return LL_ERR_HIP;
+    static std::atomic<uint64_t> raised{0};  // once per device: to the maximum, any size fits
+    if (!raise_lds_limit(reinterpret_cast<const void*>(&bwd_kv16_kernel<1>), raised)) return LL_ERR_HIP;
     hipLaunchKernelGGL(bwd_kv16_kernel<1>, dim3(a.BH * (a.dk / 16)), dim3(b16::NT), bytes, s, a);
   }
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;

@@ -729,9 +729,8 @@ static int launch_sweep_t(const FwdArgs& a, int nblocks, hipStream_t stream) {
   using Cfg = SweepCfg<IT, C, DKP>;
   const int bytes = Cfg::bytes(a.L, a.nslot);
   if (bytes > kMaxLds) return LL_ERR_UNSUPPORTED;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_sweep_kernel<IT, C, DKP>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-    return LL_ERR_HIP;
+  static std::atomic<uint64_t> raised{0};  // once per device: to the maximum, any size fits
+  if (!raise_lds_limit(reinterpret_cast<const void*>(&fwd_sweep_kernel<IT, C, DKP>), raised)) return LL_ERR_HIP;
   hipLaunchKernelGGL((fwd_sweep_kernel<IT, C, DKP>), dim3(nblocks), dim3(Cfg::NT), bytes, stream, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
@@ -739,9 +738,8 @@ static int launch_sweep_t(const FwdArgs& a, int nblocks, hipStream_t stream) {
 template <typename IT, int DKP>
 static int launch_seg_t(const SegArgs& a, int nblocks, hipStream_t stream) {
   using Cfg = SegCfg<IT, DKP>;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_state_kernel<IT, DKP>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::BYTES) != hipSuccess)
-    return LL_ERR_HIP;
+  static std::atomic<uint64_t> raised{0};  // once per device: to the maximum, any size fits
+  if (!raise_lds_limit(reinterpret_cast<const void*>(&seg_state_kernel<IT, DKP>), raised)) return LL_ERR_HIP;
   hipLaunchKernelGGL((seg_state_kernel<IT, DKP>), dim3(nblocks), dim3(Cfg::NT), Cfg::BYTES, stream, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }

@@ -1026,9 +1026,8 @@ int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t stream) {
   if (nblocks > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
   const size_t row_bytes = std::max((size_t)a.dk * 2, (size_t)a.dv * 2);
   if ((size_t)(a.T + 2 * rs::C) * row_bytes >= (size_t)1 << 31) return LL_ERR_UNSUPPORTED;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&seg_state_rs_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, ss::LDS_BYTES) != hipSuccess)
-    return LL_ERR_HIP;
+  static std::atomic<uint64_t> raised{0};
+  if (!raise_lds_limit(reinterpret_cast<const void*>(&seg_state_rs_kernel), raised, ss::LDS_BYTES)) return LL_ERR_HIP;
   hipLaunchKernelGGL(seg_state_rs_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(ss::NTH), ss::LDS_BYTES,
                      stream, a);
   return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
@@ -1066,8 +1065,9 @@ int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t stream) {
                                     : reinterpret_cast<const void*>(&fwd_rs_kernel<10, false>))
                         : (a.st_out ? reinterpret_cast<const void*>(&fwd_rs_kernel<8, true>)
                                     : reinterpret_cast<const void*>(&fwd_rs_kernel<8, false>));
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
-    return LL_ERR_HIP;
+  // each instantiation's limit is raised to the maximum once per device
+  static std::atomic<uint64_t> raised[4] = {};
+  if (!raise_lds_limit(fn, raised[(wide ? 2 : 0) + (a.st_out ? 1 : 0)])) return LL_ERR_HIP;
   if (wide && a.st_out)
     hipLaunchKernelGGL((fwd_rs_kernel<10, true>), dim3(nblocks), dim3(512), bytes, stream, a);
   else if (wide)
