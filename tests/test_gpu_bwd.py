@@ -37,6 +37,9 @@ CASES = [
     (1, 1, 3000, 128, 64, 64, "bf16", "weak"),   # 47 chunks, six chunk-level bits, ragged
     (1, 2, 500, 32, 96, 64, "bf16", "strong"),   # contraction widths 32 and 96 on the bf16 kernels
     (1, 1, 4200, 128, 128, 64, "bf16", "weak"),  # 66 chunks: chunk-level bits 0-6, ragged
+    # reverse sweeps' row records over two (b,h): 64-row blocks that end inside
+    # a chunk, three 1024-row decay-gradient scan blocks per (b,h), the last ragged
+    (2, 1, 2500, 128, 128, 64, "bf16", "none"),
 ]
 
 
