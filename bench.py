@@ -354,8 +354,9 @@ def bwd_record(w, dev, K: int, Wm: int, base=None):
         "steps": K, "warmup": Wm, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
         "tflops": tflops, "algorithmic_flops": flops, "algorithmic_bytes": abytes,
         "hbm_gbs_algorithmic": abytes / (ms * 1e-3) / 1e9,
-        "roofline": {"kernel": ("whole backward (fp16 / bf16 matrix cores: dQ and dK, dV register-state "
-                                "sweeps on power-of-two scaled fp16 operands, the in-chunk dlambda on bf16 hi/lo)"
+        "roofline": {"kernel": ("whole backward (fp16 matrix cores: the dQ, dV and dK register-state sweeps "
+                                "on power-of-two scaled fp16 operands, the in-chunk dlambda and v . dV inside "
+                                "the dV sweep, one row pass for dlambda and dc)"
                                 if bf16 else "whole backward (fp32 matrix-core arithmetic)"),
                      "bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": tflops / peak, "traffic": None},
