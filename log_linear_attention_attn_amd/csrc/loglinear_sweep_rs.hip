@@ -884,8 +884,12 @@ fwd_rs_kernel(FwdArgs a) {
 // column group finds K in L2.
 namespace ss {
 constexpr int NTH = 512;
+// K row stride (bf16): 80 banks, 16 modulo 64, so the four rows and four
+// 16-byte pieces a 16-lane group reads in a transposed read fall on disjoint
+// banks (K is only read transposed here)
+constexpr int LDK = 160;
 constexpr int KS_OFF = 0;
-constexpr int VH_OFF = KS_OFF + rs::C * rs::LDQ * 2;
+constexpr int VH_OFF = KS_OFF + rs::C * LDK * 2;
 constexpr int VL_OFF = VH_OFF + rs::C * rs::LDV * 2;
 constexpr int BUF = VL_OFF + rs::C * rs::LDV * 2;
 constexpr int LDS_BYTES = 2 * BUF;
@@ -961,7 +965,7 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int v = tid + ss::NTH * i, row = v >> 4, col = (v & 15) * 8;
-      *reinterpret_cast<bf16x8*>(Ks + row * LDQ + col) = r.k[i];
+      *reinterpret_cast<bf16x8*>(Ks + row * ss::LDK + col) = r.k[i];
     }
     {
       const int row = tid >> 3, col = (tid & 7) * 8;
@@ -989,8 +993,8 @@ __global__ void __launch_bounds__(512) seg_state_rs_kernel(SegArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kq = 2 * hh + (t >> 1), half = t & 1;
-        const bf16* k0 = Ks + (32 * ks + 8 * g4 + (li >> 2)) * LDQ + 32 * kq + 8 * (li & 3) + 4 * half;
-        const bf16x8 ka = cat(tr_read(k0), tr_read(k0 + 4 * LDQ));
+        const bf16* k0 = Ks + (32 * ks + 8 * g4 + (li >> 2)) * ss::LDK + 32 * kq + 8 * (li & 3) + 4 * half;
+        const bf16x8 ka = cat(tr_read(k0), tr_read(k0 + 4 * ss::LDK));
         S[t] = mma(ka, vh, S[t]);
         S[t] = mma(ka, vl, S[t]);
       }
