@@ -45,6 +45,11 @@ namespace rv {
 
 constexpr int C = 64, DC = 128, LOGC = 6, NLEV = 5, NTH = 512, LMAX = 16;
 constexpr int LDC = DC + 8;  // fp16 rows of the c and x tiles
+// the pre-pass reads its c tile only transposed (level updates): rows of 80
+// banks, 16 modulo 64, put the four rows and four 16-byte pieces a 16-lane
+// group reads on disjoint banks (the sweeps also read c by rows, for which
+// LDC's 68 banks are the conflict-free stride)
+constexpr int LDC_PREP = DC + 32;
 constexpr int LDA = 64 + 8;  // fp16 rows of the a tile (the group's 64 columns)
 // LDS layouts.  The tiles and row data read in phase 2 are double-buffered
 // by chunk parity; everything else is written after the chunk's first
@@ -78,7 +83,7 @@ struct Lay<false> {
 template <>
 struct Lay<true> {
   static constexpr int CH = 0;
-  static constexpr int AH = CH + 2 * C * LDC * 2;
+  static constexpr int AH = CH + 2 * C * LDC_PREP * 2;
   static constexpr int ROW = AH + 2 * C * LDA * 2;
   static constexpr int WT = ROW + 2 * 4 * C * 4;
   static constexpr int KE = WT + NLEV * C * 2;
@@ -506,7 +511,8 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
   f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int n = n1 - 1; n >= n0; --n) {
     const int tok0 = n * C, par = n & 1;
-    _Float16* Ch = reinterpret_cast<_Float16*>(smem + LY::CH) + par * (C * LDC);
+    constexpr int LDCH = PREP ? LDC_PREP : LDC;  // row stride of the c tile
+    _Float16* Ch = reinterpret_cast<_Float16*>(smem + LY::CH) + par * (C * LDCH);
     _Float16* Xh = reinterpret_cast<_Float16*>(smem + LY::XH) + par * (C * LDC);
     _Float16* Ah = reinterpret_cast<_Float16*>(smem + LY::AH) + par * (C * LDA);
     _Float16* Al = reinterpret_cast<_Float16*>(smem + LY::AL) + par * (C * LDA);
@@ -522,7 +528,7 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
       if constexpr (MODE == 0) c.from_bf16(pc[i][0]);
       else c.from_f32(pc[i][0], pc[i][1]);
       const int e2 = scale_exp(row16_max(c.amax()));
-      *reinterpret_cast<f16x8*>(Ch + row * LDC + col) = c.scaled(e2);
+      *reinterpret_cast<f16x8*>(Ch + row * LDCH + col) = c.scaled(e2);
       if ((tid & 15) == 0) ec_s[row] = e2;
       if constexpr (!PREP) {
         Row8 x;
@@ -609,7 +615,7 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
 #pragma unroll
         for (int it = 0; it < 2; ++it)
           if (it < ntile) {
-            const f16x8 ca = *reinterpret_cast<const f16x8*>(Ch + (16 * tbt[it] + li) * LDC + 32 * ks + 8 * g4);
+            const f16x8 ca = *reinterpret_cast<const f16x8*>(Ch + (16 * tbt[it] + li) * LDCH + 32 * ks + 8 * g4);
             const f16x8 xb = *reinterpret_cast<const f16x8*>(Xh + (16 * sbt[it] + li) * LDC + 32 * ks + 8 * g4);
             acc[it] = mma32(ca, xb, acc[it]);  // acc[r] = c_t . x_s, s = 16 sb + li, t = 16 tb + 4 g4 + r (scaled)
           }
@@ -813,8 +819,8 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int kq = 2 * hh + (t >> 1), half = t & 1;
-            const _Float16* k0 = Ch + (32 * ks + 8 * g4 + (li >> 2)) * LDC + 32 * kq + 8 * (li & 3) + 4 * half;
-            const f16x8 ca = cat(tr_read(k0), tr_read(k0 + 4 * LDC));
+            const _Float16* k0 = Ch + (32 * ks + 8 * g4 + (li >> 2)) * LDCH + 32 * kq + 8 * (li & 3) + 4 * half;
+            const f16x8 ca = cat(tr_read(k0), tr_read(k0 + 4 * LDCH));
             R[b][t] = mma32(ca, va[ks], R[b][t]);
           }
         // the right half's lowest chunk: from the next chunk on, the left
