@@ -512,6 +512,12 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
   for (int n = n1 - 1; n >= n0; --n) {
     const int tok0 = n * C, par = n & 1;
     constexpr int LDCH = PREP ? LDC_PREP : LDC;  // row stride of the c tile
+    // dK sweep: its c tile is read by rows (score tiles) and transposed (level
+    // updates); 16-byte piece p of row r sits at p ^ ((r & 3) << 2), which
+    // puts both a row read's 16 rows and a transposed read's four rows and
+    // four pieces on disjoint banks at the 68-bank stride.  (The dV sweep has
+    // no registers left for the swizzle's terms: 5 to 12 spilled.)
+    constexpr bool CSWZ = MODE == 1 && !PREP;
     _Float16* Ch = reinterpret_cast<_Float16*>(smem + LY::CH) + par * (C * LDCH);
     _Float16* Xh = reinterpret_cast<_Float16*>(smem + LY::XH) + par * (C * LDC);
     _Float16* Ah = reinterpret_cast<_Float16*>(smem + LY::AH) + par * (C * LDA);
@@ -528,7 +534,7 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
       if constexpr (MODE == 0) c.from_bf16(pc[i][0]);
       else c.from_f32(pc[i][0], pc[i][1]);
       const int e2 = scale_exp(row16_max(c.amax()));
-      *reinterpret_cast<f16x8*>(Ch + row * LDCH + col) = c.scaled(e2);
+      *reinterpret_cast<f16x8*>(Ch + row * LDCH + (CSWZ ? (((col >> 3) ^ ((row & 3) << 2)) << 3) : col)) = c.scaled(e2);
       if ((tid & 15) == 0) ec_s[row] = e2;
       if constexpr (!PREP) {
         Row8 x;
@@ -615,7 +621,9 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
 #pragma unroll
         for (int it = 0; it < 2; ++it)
           if (it < ntile) {
-            const f16x8 ca = *reinterpret_cast<const f16x8*>(Ch + (16 * tbt[it] + li) * LDCH + 32 * ks + 8 * g4);
+            const int swr = CSWZ ? (li & 3) << 2 : 0;  // (row & 3) << 2
+            const f16x8 ca = *reinterpret_cast<const f16x8*>(
+                Ch + (16 * tbt[it] + li) * LDCH + (CSWZ ? ((4 * ks + g4) ^ swr) << 3 : 32 * ks + 8 * g4));
             const f16x8 xb = *reinterpret_cast<const f16x8*>(Xh + (16 * sbt[it] + li) * LDC + 32 * ks + 8 * g4);
             acc[it] = mma32(ca, xb, acc[it]);  // acc[r] = c_t . x_s, s = 16 sb + li, t = 16 tb + 4 g4 + r (scaled)
           }
@@ -819,7 +827,9 @@ __device__ __forceinline__ void rev_body(const BwdRevArgs& a, unsigned char* sme
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int kq = 2 * hh + (t >> 1), half = t & 1;
-            const _Float16* k0 = Ch + (32 * ks + 8 * g4 + (li >> 2)) * LDCH + 32 * kq + 8 * (li & 3) + 4 * half;
+            const int cpc = 4 * kq + (li & 3);  // 16-byte piece of the row
+            const int swt = CSWZ ? ((li >> 2) & 3) << 2 : 0;  // (row & 3) << 2
+            const _Float16* k0 = Ch + (32 * ks + 8 * g4 + (li >> 2)) * LDCH + ((cpc ^ swt) << 3) + 4 * half;
             const f16x8 ca = cat(tr_read(k0), tr_read(k0 + 4 * LDCH));
             R[b][t] = mma32(ca, va[ks], R[b][t]);
           }
