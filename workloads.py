@@ -212,3 +212,59 @@ def make_lambda_proj_inputs(w: LambdaProjWorkload):
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     return (torch.from_numpy(x).to(tdt), torch.from_numpy(W).to(tdt),
             torch.from_numpy(bias) if w.bias else None)
+
+
+@dataclasses.dataclass(frozen=True)
+class GdnWorkload:
+    """Log-linear Gated DeltaNet forward inputs."""
+    name: str
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    dtype: str = "bf16"  # q, k, v storage: "bf16" or "f32"
+    decay: str = "weak"  # log_alpha: "strong", "weak" or "none", as for the forward
+    seed: int = 0
+
+    @property
+    def L(self) -> int:
+        return num_levels(self.T)
+
+
+# The language-model shape of the forward bench, as a Gated DeltaNet layer.
+GDN_LM_T16K = GdnWorkload("gdn_B2H16_T16384_dk128_dv128", 2, 16, 16384, 128, 128, seed=3)
+
+
+def make_gdn_inputs(w: GdnWorkload):
+    """Draw (q, k, v, log_alpha, beta, lam) as CPU tensors, in this order:
+
+    q, v ~ N(0, 1) / sqrt(dk); k ~ N(0, 1) L2-normalised over dk (the delta
+    rule's keys are unit vectors); log_alpha as log_a of the forward recipe;
+    beta = sigmoid(N(0, 1)) in (0, 1); lam[b, h, t, l] = softplus(N(0, 1)).
+    q, k, v: [B, H, T, dk|dv] bf16 or f32 (bf16 rounded once, both sides get
+    the rounded values); log_alpha, beta: [B, H, T] f32; lam: [B, H, T, L] f32.
+    """
+    rng = np.random.default_rng(w.seed)
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    scale = np.float32(1.0 / math.sqrt(dk))
+    q = rng.standard_normal((B, H, T, dk), dtype=np.float32) * scale
+    k = rng.standard_normal((B, H, T, dk), dtype=np.float32)
+    k = (k / np.maximum(np.sqrt(np.sum(k.astype(np.float64) ** 2, axis=-1, keepdims=True)),
+                        1e-12)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, dv), dtype=np.float32) * scale
+    g = rng.standard_normal((B, H, T), dtype=np.float32)
+    if w.decay == "none":
+        log_alpha = np.zeros((B, H, T), dtype=np.float32)
+    elif w.decay == "strong":
+        log_alpha = -_softplus(g + 2.0)
+    elif w.decay == "weak":
+        log_alpha = (-_softplus(g + 2.0) / np.float32(1024.0)).astype(np.float32)
+    else:
+        raise ValueError(w.decay)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, T)).astype(np.float64)))).astype(np.float32)
+    lam = _softplus(rng.standard_normal((B, H, T, w.L), dtype=np.float32))
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return (torch.from_numpy(q).to(tdt), torch.from_numpy(k).to(tdt), torch.from_numpy(v).to(tdt),
+            torch.from_numpy(np.ascontiguousarray(log_alpha)), torch.from_numpy(beta),
+            torch.from_numpy(lam))
