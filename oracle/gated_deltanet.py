@@ -137,3 +137,27 @@ def loglinear_recurrent(q, k, v, log_alpha, beta, lam) -> np.ndarray:
                 out[b, h, t] = np.einsum("l,d,lde->e", lam[b, h, t], q[b, h, t], S)
     return out
 
+
+
+def loglinear_rows(q, k, v, log_alpha, beta, lam, bh: tuple[int, int], rows) -> np.ndarray:
+    """Selected output rows of one (b, h), same definition as ``loglinear_forward``.
+
+    For each row t, r = q_t^T Phi(t,s) is carried from s = t down to 0 by
+    r <- r A_s, giving c(t,s) = beta_s r . k_s on the way; O(t dk) per row, so
+    rows of long sequences can be checked one at a time.
+    """
+    b, h = bh
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+    la, be, lm = _f64(log_alpha[b, h]), _f64(beta[b, h]), _f64(lam[b, h])
+    res = []
+    for t in rows:
+        t = int(t)
+        r = qh[t].copy()
+        coef = np.empty(t + 1)
+        for s in range(t, -1, -1):
+            rk = r @ kh[s]
+            coef[s] = be[s] * rk
+            r = np.exp(la[s]) * (r - be[s] * rk * kh[s])
+        lev = level_rows(t, t + 1, t + 1)[0]
+        res.append((coef * lm[t, lev]) @ vh[: t + 1])
+    return np.stack(res) if res else np.zeros((0, vh.shape[-1]))

@@ -124,3 +124,14 @@ def test_zero_beta_writes_nothing_and_one_token_closed_form():
     want = lam1[0, 0, 0, 0] * b1[0, 0, 0] * (q1[0, 0, 0] @ k1[0, 0, 0]) * v1[0, 0, 0]
     np.testing.assert_allclose(G.loglinear_forward(q1, k1, v1, la1, b1, lam1[..., :1])[0, 0, 0], want,
                                rtol=1e-13)
+
+
+def test_rows_match_dense():
+    """The one-row evaluation used for long sequences equals the dense form."""
+    rng = np.random.default_rng(6)
+    q, k, v, la, beta, lam = _inputs(rng, 2, 2, 150, 8, 3)
+    dense = G.loglinear_forward(q, k, v, la, beta, lam)
+    rows = [0, 1, 63, 64, 65, 127, 128, 149]
+    for bh in [(0, 1), (1, 0)]:
+        np.testing.assert_allclose(G.loglinear_rows(q, k, v, la, beta, lam, bh, rows), dense[bh][rows],
+                                   rtol=1e-11, atol=1e-12)
