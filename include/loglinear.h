@@ -340,6 +340,39 @@ int loglinear_decode_step_ex(const loglinear_states* states, const void* q, cons
                              const int* t, float* out, int dtype, int qk_heads, void* stream);
 
 /*
+ * Log-linear Gated DeltaNet forward.  The pages lift Gated DeltaNet with the
+ * same Fenwick hierarchy as Mamba-2 (page "论文阅读：Log-Linear Attention — 基于
+ * Fenwick 树与层次矩阵的对数线性复杂度注意力机制", section 与已有模型的组合; page
+ * "算力终结者来了！华人天团「降维打击」注意力瓶颈，AI狂飙进对数时代", section
+ * 对Mamba-2和门控DeltaNet的对数线性推广) but print no delta rule; this call
+ * takes the published gated delta rule, with k-major states,
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ * and weights each pair of its unrolled form by the level weight:
+ *     o_t = sum_{s<=t} lambda[t, level(t,s)] beta_s q_t^T A_t...A_{s+1} k_s v_s,
+ *     A_r = alpha_r (I - beta_r k_r k_r^T),  alpha_r = exp(log_alpha[r]).
+ * With lambda = 1 on every level this is Gated DeltaNet itself.
+ *   q, k      : [B, H, T, dk]  bf16 (dtype LL_BF16) or fp32 (LL_F32); the
+ *               delta rule expects unit-norm keys (not checked)
+ *   v         : [B, H, T, dv]  same dtype as q
+ *   log_alpha : [B, H, T] fp32 (<= 0),  beta : [B, H, T] fp32 (in [0, 1])
+ *   lambda    : [B, H, T, L] fp32,  out : [B, H, T, dv] fp32, written completely
+ * Chunks of 64 tokens; arithmetic in fp32 (matrix cores).  dk in {64, 128},
+ * dv a multiple of 16, ceil(T / 64) <= 8192 chunks at dk = 128 (else
+ * LL_ERR_UNSUPPORTED; the bucket states of a 16-column slice live in LDS).
+ * workspace: NULL (the call allocates and frees it on `stream`) or at least
+ * loglinear_gdn_workspace_size() bytes of device memory, 256-byte aligned,
+ * else LL_ERR_WORKSPACE; its contents on entry do not matter.  It holds
+ * 4 (3 dk + 128) * 64 bytes per chunk (~128 KiB at dk = 128).
+ */
+int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                      const float* beta, const float* lambda, float* out, int B, int H, int T, int dk,
+                      int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of loglinear_gdn_fwd for these sizes; (size_t)-1 if the
+ * sizes are invalid or unsupported. */
+size_t loglinear_gdn_workspace_size(int B, int H, int T, int dk, int dv);
+
+/*
  * Test export: lev[t*T + s] = level(t, s) for s <= t and -1 for s > t (int8,
  * DEVICE buffer of T*T bytes), computed on the GPU with the same device
  * helper the kernels use (section 层级判定算法).  1 <= T <= 8192.

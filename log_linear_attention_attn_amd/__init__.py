@@ -11,6 +11,8 @@ Entry points (same names as the C ABI in include/loglinear.h):
     prefill(q, k, v, log_a, lam, C=64, L=None)          forward + decode states at T-1
     bwd(q, k, v, log_a, lam, out, dout, C=64)           gradients of sum(out * dout)
     fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1)
+    gdn_fwd(q, k, v, log_alpha, beta, lam, out=None, workspace=None)   log-linear Gated DeltaNet
+    gdn_workspace_size(B, H, T, dk, dv)
     decode_step(states, q, k, v, log_a, lam, t, out=None)
     level_table(T, device=None)                          int8 [T, T]
     num_levels(T)
@@ -24,7 +26,7 @@ import torch
 
 __all__ = [
     "LogLinearError", "lib", "library_path", "num_levels", "fwd", "fwd_ex", "prefill", "bwd",
-    "fwd_workspace_size", "decode_step", "level_table", "strerror",
+    "fwd_workspace_size", "decode_step", "level_table", "strerror", "gdn_fwd", "gdn_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "loglinear_bwd_ex", "loglinear_fwd_workspace_size",
     "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_decode_step_ex",
     "loglinear_level_table", "loglinear_lambda_proj", "loglinear_lambda_proj_bwd",
-    "loglinear_strerror", "loglinear_fwd_noalloc",
+    "loglinear_strerror", "loglinear_fwd_noalloc", "loglinear_gdn_fwd", "loglinear_gdn_workspace_size",
 )
 
 # bytes of the static scratch behind loglinear_fwd_noalloc (the header's
@@ -117,6 +119,10 @@ def lib():
     L.loglinear_lambda_proj_bwd.restype = i
     L.loglinear_level_table.argtypes = [vp, i, vp]
     L.loglinear_level_table.restype = i
+    L.loglinear_gdn_fwd.argtypes = [vp] * 7 + [i] * 6 + [vp, sz, vp]
+    L.loglinear_gdn_fwd.restype = i
+    L.loglinear_gdn_workspace_size.argtypes = [i] * 5
+    L.loglinear_gdn_workspace_size.restype = sz
     L.loglinear_strerror.argtypes = [i]
     L.loglinear_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -471,3 +477,44 @@ def level_table(T: int, device=None):
     lev = torch.empty((T, T), dtype=torch.int8, device=dev)
     _raise(lib().loglinear_level_table(_ptr(lev), int(T), _stream(dev)), "loglinear_level_table")
     return lev
+
+
+def gdn_workspace_size(B, H, T, dk, dv) -> int:
+    n = lib().loglinear_gdn_workspace_size(B, H, T, dk, dv)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid or unsupported sizes")
+    return int(n)
+
+
+def gdn_fwd(q, k, v, log_alpha, beta, lam, out=None, workspace=None):
+    """Log-linear Gated DeltaNet forward through loglinear_gdn_fwd.
+
+    q, k: [B, H, T, dk]; v: [B, H, T, dv] (all bf16 or all fp32);
+    log_alpha, beta: [B, H, T] fp32; lam: [B, H, T, L] fp32, L = num_levels(T).
+    workspace: None (the library allocates) or a uint8 device tensor of at
+    least gdn_workspace_size(...) bytes.  Returns out [B, H, T, dv] fp32.
+    """
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T) if T > 0 else 0
+    _check_dev("q", q, q.dtype, (B, H, T, dk), dev)
+    _check_dev("k", k, q.dtype, (B, H, T, dk), dev)
+    _check_dev("v", v, q.dtype, (B, H, T, dv), dev)
+    _check_dev("log_alpha", log_alpha, torch.float32, (B, H, T), dev)
+    _check_dev("beta", beta, torch.float32, (B, H, T), dev)
+    _check_dev("lam", lam, torch.float32, (B, H, T, L), dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (B, H, T, dv), dev)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().loglinear_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(lam),
+                                 _ptr(out), B, H, T, dk, dv,
+                                 LL_BF16 if q.dtype == torch.bfloat16 else LL_F32,
+                                 _ptr(workspace), nbytes, _stream(dev))
+    _raise(st, "loglinear_gdn_fwd")
+    return out

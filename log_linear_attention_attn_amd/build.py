@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libloglinear.so")
 SOURCES = ["loglinear_fwd.hip", "loglinear_sweep_rs.hip", "loglinear_sweep_wide.hip", "loglinear_decode.hip", "loglinear_bwd.hip", "loglinear_bwd16.hip", "loglinear_bwd_rev.hip", "loglinear_lambda.hip",
-           "loglinear_lambda_bwd.hip", "loglinear_noalloc.hip", "loglinear_api.cpp"]
+           "loglinear_lambda_bwd.hip", "loglinear_noalloc.hip", "loglinear_gdn.hip",
+           "loglinear_api.cpp"]
 ARCH = "gfx950"
 
 

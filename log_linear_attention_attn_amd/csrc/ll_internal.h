@@ -234,6 +234,23 @@ int rs_lds_bytes(int L, int nslot);
 int launch_sweep_rs(const FwdArgs& a, int nblocks, hipStream_t s);
 int launch_seg_state_rs(const SegArgs& a, int BH, hipStream_t s);
 int launch_level_table(signed char* lev, int T, hipStream_t s);
+// Log-linear Gated DeltaNet forward: chunk records, then the level sweep.
+struct GdnArgs {
+  const void* q;          // [BH][T][dk]
+  const void* k;          // [BH][T][dk]
+  const void* v;          // [BH][T][dv]
+  const float* log_alpha; // [BH][T]
+  const float* beta;      // [BH][T]
+  const float* lam;       // [BH][T][L]
+  float* out;             // [BH][T][dv]
+  float* ws;              // per-chunk records [BH][N] x gdn chunk record
+  float* gchunk;          // [BH][N] decay of each whole chunk
+  int BH, T, dk, dv, L, N;
+  int nslot;              // chunk-level Fenwick bits = bit_length(N - 1)
+};
+size_t gdn_workspace_bytes(long long BH, int N, int dk);
+int gdn_sweep_lds_bytes(int nslot, int dk);
+int launch_gdn(int dtype, const GdnArgs& a, hipStream_t s);
 int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot);

@@ -450,6 +450,46 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   return st;
 }
 
+int gdn_plan(int B, int H, int T, int dk, int dv, int* N, int* nslot, size_t* ws) {
+  if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return LL_ERR_SHAPE;
+  if (dk != 64 && dk != 128) return LL_ERR_UNSUPPORTED;
+  if (dv % 16 != 0) return LL_ERR_UNSUPPORTED;
+  *N = (T + 63) / 64;
+  *nslot = *N > 1 ? bit_length(*N - 1) : 0;
+  if (ll::gdn_sweep_lds_bytes(*nslot, dk) > ll::kMaxLds) return LL_ERR_UNSUPPORTED;
+  *ws = ll::gdn_workspace_bytes((long long)B * H, *N, dk);
+  return LL_OK;
+}
+
+int run_gdn(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+            const float* beta, const float* lambda, float* out, int B, int H, int T, int dk, int dv,
+            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int N = 0, nslot = 0;
+  size_t need = 0;
+  if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
+  int st = gdn_plan(B, H, T, dk, dv, &N, &nslot, &need);
+  if (st != LL_OK) return st;
+  if (B == 0 || H == 0 || T == 0) return LL_OK;
+  if (!q || !k || !v || !log_alpha || !beta || !lambda || !out) return LL_ERR_NULL;
+  if (!aligned16({q, k, v, lambda, out})) return LL_ERR_SHAPE;
+  if (workspace && workspace_bytes < need) return LL_ERR_WORKSPACE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255)) return LL_ERR_WORKSPACE;
+  void* ws = workspace;
+  bool owned = false;
+  if (!ws) {
+    if (hipMallocAsync(&ws, need, stream) != hipSuccess) return LL_ERR_HIP;
+    owned = true;
+  }
+  const long long BH = (long long)B * H;
+  const size_t rec_bytes = need - align256(size_t(BH) * N * 4);
+  ll::GdnArgs a{q, k, v, log_alpha, beta, lambda, out, static_cast<float*>(ws),
+                reinterpret_cast<float*>(static_cast<char*>(ws) + rec_bytes),
+                static_cast<int>(BH), T, dk, dv, bit_length(T - 1) + 1, N, nslot};
+  st = ll::launch_gdn(dtype, a, stream);
+  if (owned && hipFreeAsync(ws, stream) != hipSuccess && st == LL_OK) st = LL_ERR_HIP;
+  return st;
+}
+
 }  // namespace
 
 namespace ll {
@@ -566,6 +606,20 @@ int loglinear_decode_step_ex(const loglinear_states* states, const void* q, cons
                              float* out, int dtype, int qk_heads, void* stream) {
   return run_decode(dtype, states, q, k, v, log_a, lambda, t, out, qk_heads,
                     static_cast<hipStream_t>(stream));
+}
+
+int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                      const float* beta, const float* lambda, float* out, int B, int H, int T, int dk,
+                      int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_gdn(dtype, q, k, v, log_alpha, beta, lambda, out, B, H, T, dk, dv, workspace,
+                 workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t loglinear_gdn_workspace_size(int B, int H, int T, int dk, int dv) {
+  int N = 0, nslot = 0;
+  size_t ws = 0;
+  if (gdn_plan(B, H, T, dk, dv, &N, &nslot, &ws) != LL_OK) return static_cast<size_t>(-1);
+  return ws;
 }
 
 int loglinear_level_table(signed char* lev, int T, void* stream) {

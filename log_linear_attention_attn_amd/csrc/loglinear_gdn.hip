@@ -1,0 +1,464 @@
+// Log-linear Gated DeltaNet forward (gfx950).
+//
+// The operator ([P1] 与已有模型的组合 and [P2] 对Mamba-2和门控DeltaNet的对数线性推广
+// lift Gated DeltaNet with the Fenwick hierarchy; the delta rule itself is the
+// published gated delta rule, S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} +
+// beta_t k_t v_t^T, states k-major):
+//
+//     o_t = sum_{s<=t} lambda[t, level(t,s)] beta_s q_t^T Phi(t,s) k_s v_s,
+//     Phi(t,s) = A_t ... A_{s+1},  A_r = alpha_r (I - beta_r k_r k_r^T).
+//
+// Chunkwise form (C = 64).  Inside a chunk with in-chunk cumulative log decay
+// g_i and Gamma[i][j] = exp(g_i - g_j) (j <= i), the unit lower-triangular
+// system (I + N) X = diag(beta), N[i][j] = beta_i (k_i . k_j) Gamma[i][j]
+// (j < i), gives Tb = X and, with the products of the chunk's transitions
+// written as gamma_t I - sum_i Gamma[t][i] k_i w_i^T (w = rows of Tb diag(gamma) K):
+//   in-chunk pairs:  c(t,s) = [(Q K^T ⊙ Gamma ⊙ tril) Tb][t][s]   (Ceff)
+//   a bucket state S seen from row t:  o_t += lambda q~_t^T S,
+//       q~_t = gamma_t q_t - sum_{i<=t} Gamma[t][i] (q_t . k_i) w_i  (Q~)
+//   a bucket state carried over the chunk:  S <- gamma_C S - K^^T (W S),
+//       K^_i = exp(g_last - g_i) k_i
+//   the chunk's own state:  K^^T (Tb V).
+// Every bucket state follows the same transitions, so the lssb merge of
+// [P1] 解码：基于 lssb 的状态更新 stays a plain sum, applied over chunk
+// indices; the chunk-level bucket of bit b carries level log2(C) + 1 + b.
+//
+// Two kernels:
+//   gdn_prep_kernel  — one workgroup per chunk: Q~, W, K^, Tb, Ceff ⊙ lambda
+//                       (in-chunk levels) and gamma_C, written to the workspace
+//                       in the matrix-core fragment order the sweep consumes.
+//   gdn_sweep_kernel — one workgroup per (b, h, 16 value columns): walks the
+//                       chunks in order with the bucket states in LDS.
+// All arithmetic is fp32 (v_mfma_f32_16x16x4f32).
+//
+// Page abbreviations:
+//   [P1] "论文阅读：Log-Linear Attention — 基于 Fenwick 树与层次矩阵的对数线性复杂度注意力机制"
+//   [P2] "算力终结者来了！华人天团「降维打击」注意力瓶颈，AI狂飙进对数时代"
+#include "ll_device.h"
+#include "ll_internal.h"
+
+namespace ll {
+namespace {
+
+constexpr int GC = 64;       // chunk length
+constexpr int GLOGC = 6;
+constexpr int GTHR = 256;    // four waves
+constexpr int LDM = GC + 4;  // row stride (floats) of the C x C LDS matrices
+
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Four consecutive input elements as fp32 (row-major input, 8-byte aligned
+// for bf16, 16-byte aligned for fp32).
+template <typename IT>
+__device__ __forceinline__ f32x4 load4(const IT* p);
+template <>
+__device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <typename IT>
+__device__ __forceinline__ float load1(const IT* p);
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f(*p); }
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+
+// Per-chunk workspace record, in floats (KT = dk / 16).  Every matrix is
+// stored as 16x16 fragments [tile][64 lanes][4]; lane l of fragment (i, j)
+// of a matrix M holds M[16 i + l % 16][16 j + 4 (l / 16) + r], r = 0..3, the
+// A-operand order of v_mfma_f32_16x16x4f32 over four reduction steps.
+//   Q~  [4 row tiles][KT]      W  [4][KT]       (C x dk)
+//   K^T [KT][4]  (K^ transposed: dk x C)
+//   Ceff ⊙ lambda [4][4],  Tb [4][4]            (C x C, tiles above the
+//                                                 diagonal not written)
+__host__ __device__ constexpr size_t gdn_off_qt(int) { return 0; }
+__host__ __device__ constexpr size_t gdn_off_wt(int KT) { return size_t(1024) * KT; }
+__host__ __device__ constexpr size_t gdn_off_kh(int KT) { return size_t(2048) * KT; }
+__host__ __device__ constexpr size_t gdn_off_al(int KT) { return size_t(3072) * KT; }
+__host__ __device__ constexpr size_t gdn_off_tb(int KT) { return size_t(3072) * KT + 4096; }
+__host__ __device__ constexpr size_t gdn_chunk_floats(int KT) { return size_t(3072) * KT + 8192; }
+
+// ---------------------------------------------------------------------------
+// Chunk preparation.  LDS: K and Q (later W) as fp32 rows of DK + 4, the C x C
+// matrices N (later Tb) and Q K^T ⊙ Gamma ⊙ tril, and g, gamma, beta.
+// ---------------------------------------------------------------------------
+template <typename IT, int DK>
+__global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
+  constexpr int KT = DK / 16;
+  constexpr int KTW = KT / 4;  // dk tiles per wave
+  constexpr int LDK = DK + 4;
+  extern __shared__ __align__(16) float sm[];
+  float* Ks = sm;
+  float* Qs = Ks + GC * LDK;  // Q, then W (row-major, C x dk)
+  float* Nm = Qs + GC * LDK;  // N, then Tb
+  float* QG = Nm + GC * LDM;
+  float* gs = QG + GC * LDM;
+  float* gam = gs + GC;
+  float* bs = gam + GC;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int cid = blockIdx.x;
+  const int bh = cid / a.N, n = cid - bh * a.N;
+  const int p0 = n * GC;
+  const int nrow = min(GC, a.T - p0);
+  const IT* q = static_cast<const IT*>(a.q) + (size_t(bh) * a.T + p0) * DK;
+  const IT* k = static_cast<const IT*>(a.k) + (size_t(bh) * a.T + p0) * DK;
+  float* rec = a.ws + size_t(cid) * gdn_chunk_floats(KT);
+
+  // Phase 0: K, Q rows to LDS (zero past T), beta, and the in-chunk prefix of log alpha.
+  for (int idx = tid; idx < GC * DK / 4; idx += GTHR) {
+    const int r = idx / (DK / 4), c = (idx - r * (DK / 4)) * 4;
+    f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv;
+    if (r < nrow) {
+      kv = load4<IT>(k + r * DK + c);
+      qv = load4<IT>(q + r * DK + c);
+    }
+    *reinterpret_cast<f32x4*>(Ks + r * LDK + c) = kv;
+    *reinterpret_cast<f32x4*>(Qs + r * LDK + c) = qv;
+  }
+  if (w == 0) {
+    const bool in = lane < nrow;
+    float x = in ? a.log_alpha[size_t(bh) * a.T + p0 + lane] : 0.f;
+    const float b = in ? a.beta[size_t(bh) * a.T + p0 + lane] : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    gs[lane] = x;
+    gam[lane] = __expf(x);
+    bs[lane] = b;
+  }
+  __syncthreads();
+
+  // Phase 1: K K^T and Q K^T, row tile w, column tiles <= w.
+  //   N[i][j]  = beta_i (k_i . k_j) Gamma[i][j]   j < i,  else 0
+  //   QG[i][j] = (q_i . k_j) Gamma[i][j]          j <= i, else 0
+  for (int ct = 0; ct < 4; ++ct) {
+    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+    if (ct <= w) {
+#pragma unroll 8
+      for (int k0 = 0; k0 < DK; k0 += 4) {
+        const float bk = Ks[(16 * ct + l16) * LDK + k0 + g4];
+        kk = mma4(Ks[(16 * w + l16) * LDK + k0 + g4], bk, kk);
+        qk = mma4(Qs[(16 * w + l16) * LDK + k0 + g4], bk, qk);
+      }
+    }
+    const int j = 16 * ct + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * g4 + r;
+      const float G = j <= i ? __expf(gs[i] - gs[j]) : 0.f;
+      Nm[i * LDM + j] = j < i ? bs[i] * kk[r] * G : 0.f;
+      QG[i * LDM + j] = qk[r] * G;
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: (I + N) X = diag(beta) by forward substitution.  Wave w solves
+  // columns 16w..16w+15; lane (col, p) keeps X[4m + p][col] in x[m] and sums
+  // the j = p (mod 4) part of each row, the quad adds the four parts.
+  {
+    const int col = 16 * w + (lane >> 2), p = lane & 3;
+    float x[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) x[m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < GC; ++i) {
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m <= (i >> 2); ++m) part += Nm[i * LDM + 4 * m + p] * x[m];
+      part += dppf<0xB1>(part);
+      part += dppf<0x4E>(part);
+      const float xi = (i == col ? bs[i] : 0.f) - part;
+      if (p == (i & 3)) x[i >> 2] = xi;
+    }
+    __syncthreads();  // every wave has read N: overwrite it with Tb
+#pragma unroll
+    for (int m = 0; m < 16; ++m) Nm[(4 * m + p) * LDM + col] = x[m];
+  }
+  __syncthreads();
+  const float* Tb = Nm;
+
+  // Phase 3a: W^T = (gamma K)^T Tb^T, tiles (kt, rt); reduction index c runs
+  // over the rows of K with Tb[t][c] != 0, c <= t.  The accumulator of tile
+  // (kt, rt) is W's fragment (rt, kt); it also goes to LDS (row-major) for Q~.
+  float* Ws = Qs;
+#pragma unroll
+  for (int ktl = 0; ktl < KTW; ++ktl) {
+    const int kt = w * KTW + ktl;
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < 16 * rt + 16; c0 += 4) {
+        const int c = c0 + g4;
+        acc = mma4(Ks[c * LDK + 16 * kt + l16] * gam[c], Tb[(16 * rt + l16) * LDM + c], acc);
+      }
+      *reinterpret_cast<f32x4*>(rec + gdn_off_wt(KT) + ((rt * KT + kt) * 64 + lane) * 4) = acc;
+      *reinterpret_cast<f32x4*>(Ws + (16 * rt + l16) * LDK + 16 * kt + 4 * g4) = acc;
+    }
+  }
+  // Phase 3b: Ceff^T = Tb^T QG^T, tiles (ct, rt) with ct <= rt = w: the
+  // accumulator is Ceff's fragment (rt, ct); times the in-chunk level weight.
+  {
+    const int rt = w;
+    const int t = 16 * rt + l16;
+    const bool trow = t < nrow;
+    const float* lam_t = a.lam + (size_t(bh) * a.T + p0 + (trow ? t : 0)) * a.L;
+    for (int ct = 0; ct <= rt; ++ct) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 16 * ct; c0 < 16 * rt + 16; c0 += 4) {
+        const int c = c0 + g4;
+        acc = mma4(Tb[c * LDM + 16 * ct + l16], QG[t * LDM + c], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * ct + 4 * g4 + r;
+        acc[r] = (trow && s <= t) ? acc[r] * lam_t[level_of(uint32_t(t), uint32_t(s))] : 0.f;
+      }
+      *reinterpret_cast<f32x4*>(rec + gdn_off_al(KT) + ((rt * 4 + ct) * 64 + lane) * 4) = acc;
+      // Tb's fragment (rt, ct)
+      *reinterpret_cast<f32x4*>(rec + gdn_off_tb(KT) + ((rt * 4 + ct) * 64 + lane) * 4) =
+          *reinterpret_cast<const f32x4*>(Tb + t * LDM + 16 * ct + 4 * g4);
+    }
+  }
+  // Phase 3c: K^ transposed, fragments (dt, ct): K^[c][d] = exp(g_last - g_c) k_c[d].
+  {
+    const float glast = gs[GC - 1];
+#pragma unroll
+    for (int dtl = 0; dtl < KTW; ++dtl) {
+      const int dt = w * KTW + dtl;
+      for (int ct = 0; ct < 4; ++ct) {
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * ct + 4 * g4 + r;
+          v[r] = __expf(glast - gs[c]) * Ks[c * LDK + 16 * dt + l16];
+        }
+        *reinterpret_cast<f32x4*>(rec + gdn_off_kh(KT) + ((dt * 4 + ct) * 64 + lane) * 4) = v;
+      }
+    }
+    if (tid == 0) a.gchunk[cid] = __expf(glast);
+  }
+  __syncthreads();
+
+  // Phase 4: Q~^T = (gamma Q)^T - W^T QG^T, tiles (kt, rt): the accumulator is
+  // Q~'s fragment (rt, kt).  gamma Q comes from global memory (Q's LDS rows
+  // now hold W).
+#pragma unroll
+  for (int ktl = 0; ktl < KTW; ++ktl) {
+    const int kt = w * KTW + ktl;
+    for (int rt = 0; rt < 4; ++rt) {
+      const int t = 16 * rt + l16;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < 16 * rt + 16; c0 += 4) {
+        const int c = c0 + g4;
+        acc = mma4(Ws[c * LDK + 16 * kt + l16], QG[t * LDM + c], acc);
+      }
+      f32x4 qv = {0.f, 0.f, 0.f, 0.f};
+      if (t < nrow) qv = load4<IT>(q + t * DK + 16 * kt + 4 * g4);
+      const float gt = gam[t];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = gt * qv[r] - acc[r];
+      *reinterpret_cast<f32x4*>(rec + gdn_off_qt(KT) + ((rt * KT + kt) * 64 + lane) * 4) = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Level sweep.  Wave w owns row tile w of the chunk (outputs, W S, Tb V) and
+// dk tiles w*KTW .. of every bucket state (the state updates).  LDS: the
+// bucket states [slot][KT][64][4] (accumulator order: lane l holds
+// S[16 kt + 4 (l/16) + r][l % 16], which is also the B-operand order over
+// the reduction index d), the products W S per slot [slot][4][64][4], and
+// Tb V [4][64][4].
+// ---------------------------------------------------------------------------
+template <typename IT, int DK>
+__global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
+  constexpr int KT = DK / 16;
+  constexpr int KTW = KT / 4;
+  extern __shared__ __align__(16) float sm[];
+  const int NB = a.nslot;
+  f32x4* st = reinterpret_cast<f32x4*>(sm);  // [NB][KT][64]
+  f32x4* yb = st + NB * KT * 64;              // [NB][4][64]
+  f32x4* ub = yb + NB * 4 * 64;               // [4][64]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int nsl = a.dv / 16;
+  // all column slices of one (b,h) on one XCD (workgroups are dealt to the
+  // eight XCDs round-robin), so they share its L2 copy of the chunk records
+  const int nwg = gridDim.x;
+  const int id = (nwg & 7) ? blockIdx.x : (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int bh = id / nsl, n0 = (id - bh * nsl) * 16;
+  const IT* v = static_cast<const IT*>(a.v) + size_t(bh) * a.T * a.dv + n0 + l16;
+  float* out = a.out + size_t(bh) * a.T * a.dv + n0 + l16;
+  const float* lam = a.lam + size_t(bh) * a.T * a.L;
+
+  for (int n = 0; n < a.N; ++n) {
+    const int p0 = n * GC;
+    const float* rec = a.ws + (size_t(bh) * a.N + n) * gdn_chunk_floats(KT);
+    f32x4 qt[KT], wt[KT], kh[KTW][4], al[4], tb[4];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      qt[kt] = *reinterpret_cast<const f32x4*>(rec + gdn_off_qt(KT) + ((w * KT + kt) * 64 + lane) * 4);
+      wt[kt] = *reinterpret_cast<const f32x4*>(rec + gdn_off_wt(KT) + ((w * KT + kt) * 64 + lane) * 4);
+    }
+#pragma unroll
+    for (int dtl = 0; dtl < KTW; ++dtl)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        kh[dtl][ct] = *reinterpret_cast<const f32x4*>(
+            rec + gdn_off_kh(KT) + (((w * KTW + dtl) * 4 + ct) * 64 + lane) * 4);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      al[ct] = tb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ct <= w) {
+        al[ct] = *reinterpret_cast<const f32x4*>(rec + gdn_off_al(KT) + ((w * 4 + ct) * 64 + lane) * 4);
+        tb[ct] = *reinterpret_cast<const f32x4*>(rec + gdn_off_tb(KT) + ((w * 4 + ct) * 64 + lane) * 4);
+      }
+    }
+    // V as B operand: lane holds V[16 ct + 4 (l/16) + r][n0 + l % 16]
+    f32x4 vb[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = p0 + 16 * ct + 4 * g4 + r;
+        vb[ct][r] = row < a.T ? load1<IT>(v + size_t(row) * a.dv) : 0.f;
+      }
+
+    // in-chunk pairs and the chunk's own Tb V (rows of tile w)
+    f32x4 o = {0.f, 0.f, 0.f, 0.f}, u = o;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      if (ct <= w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          o = mma4(al[ct][r], vb[ct][r], o);
+          u = mma4(tb[ct][r], vb[ct][r], u);
+        }
+      }
+    // bucket states of the chunk prefix: one per set bit b of n
+    for (int b = 0; b < NB; ++b) {
+      if (!((n >> b) & 1)) continue;
+      f32x4 oq = {0.f, 0.f, 0.f, 0.f}, y = oq;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const f32x4 s = st[(b * KT + kt) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          oq = mma4(qt[kt][r], s[r], oq);
+          y = mma4(wt[kt][r], s[r], y);
+        }
+      }
+      const int lev = GLOGC + 1 + b;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = p0 + 16 * w + 4 * g4 + r;
+        if (t < a.T) o[r] += lam[size_t(t) * a.L + lev] * oq[r];
+      }
+      yb[(b * 4 + w) * 64 + lane] = y;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = p0 + 16 * w + 4 * g4 + r;
+      if (t < a.T) out[size_t(t) * a.dv] = o[r];
+    }
+    ub[w * 64 + lane] = u;
+    __syncthreads();
+    if (n + 1 < a.N) {
+      // carry the states over the chunk, add the chunk's own state, merge by lssb(n + 1)
+      const int m = __ffs(n + 1) - 1;
+      const float gC = a.gchunk[size_t(bh) * a.N + n];
+      f32x4 own[KTW];
+#pragma unroll
+      for (int dtl = 0; dtl < KTW; ++dtl) {
+        own[dtl] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const f32x4 uu = ub[ct * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) own[dtl] = mma4(kh[dtl][ct][r], uu[r], own[dtl]);
+        }
+      }
+      for (int b = 0; b < NB; ++b) {
+        if (!((n >> b) & 1)) continue;
+#pragma unroll
+        for (int dtl = 0; dtl < KTW; ++dtl) {
+          const int dt = w * KTW + dtl;
+          f32x4 ky = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const f32x4 yy = yb[(b * 4 + ct) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ky = mma4(kh[dtl][ct][r], yy[r], ky);
+          }
+          const f32x4 s = st[(b * KT + dt) * 64 + lane];
+          f32x4 ns;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ns[r] = gC * s[r] - ky[r];
+          if (b < m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) own[dtl][r] += ns[r];
+          } else {
+            st[(b * KT + dt) * 64 + lane] = ns;
+          }
+        }
+      }
+#pragma unroll
+      for (int dtl = 0; dtl < KTW; ++dtl) st[(m * KT + w * KTW + dtl) * 64 + lane] = own[dtl];
+      __syncthreads();
+    }
+  }
+}
+
+template <typename IT, int DK>
+int launch_gdn_t(const GdnArgs& a, hipStream_t s) {
+  constexpr int KT = DK / 16;
+  const int prep_lds = (2 * GC * (DK + 4) + 2 * GC * LDM + 3 * GC) * 4;
+  const int sweep_lds = (a.nslot * KT * 64 + a.nslot * 4 * 64 + 4 * 64) * 16;
+  if (sweep_lds > kMaxLds) return LL_ERR_UNSUPPORTED;
+  static std::atomic<uint64_t> raised[2];
+  if (!raise_lds_limit(reinterpret_cast<const void*>(&gdn_prep_kernel<IT, DK>), raised[0])) return LL_ERR_HIP;
+  if (!raise_lds_limit(reinterpret_cast<const void*>(&gdn_sweep_kernel<IT, DK>), raised[1])) return LL_ERR_HIP;
+  const long long nchunks = (long long)a.BH * a.N;
+  if (nchunks > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((gdn_prep_kernel<IT, DK>), dim3(static_cast<unsigned>(nchunks)), dim3(GTHR), prep_lds, s, a);
+  if (hipGetLastError() != hipSuccess) return LL_ERR_HIP;
+  const long long nwg = (long long)a.BH * (a.dv / 16);
+  hipLaunchKernelGGL((gdn_sweep_kernel<IT, DK>), dim3(static_cast<unsigned>(nwg)), dim3(GTHR), sweep_lds, s, a);
+  if (hipGetLastError() != hipSuccess) return LL_ERR_HIP;
+  return LL_OK;
+}
+
+}  // namespace
+
+size_t gdn_workspace_bytes(long long BH, int N, int dk) {
+  const size_t rec = gdn_chunk_floats(dk / 16) * 4;
+  return ((size_t(BH) * N * rec + 255) & ~size_t(255)) + ((size_t(BH) * N * 4 + 255) & ~size_t(255));
+}
+
+int gdn_sweep_lds_bytes(int nslot, int dk) { return (nslot * (dk / 16) * 64 + nslot * 4 * 64 + 4 * 64) * 16; }
+
+int launch_gdn(int dtype, const GdnArgs& a, hipStream_t s) {
+  if (a.dk == 128) return dtype == LL_BF16 ? launch_gdn_t<uint16_t, 128>(a, s) : launch_gdn_t<float, 128>(a, s);
+  if (a.dk == 64) return dtype == LL_BF16 ? launch_gdn_t<uint16_t, 64>(a, s) : launch_gdn_t<float, 64>(a, s);
+  return LL_ERR_UNSUPPORTED;
+}
+
+}  // namespace ll

@@ -279,3 +279,32 @@ def test_fwd_noalloc_rejects_sizes_beyond_its_scratch():
     assert fn(p, p, p, p, p, p, 1, 1, 64, 16, 16, 48, None) == LL_ERR_SHAPE
     assert fn(None, p, p, p, p, p, 1, 1, 64, 16, 16, 16, None) == LL_ERR_NULL
     assert fn(p, p, p, p, p, p, 0, 1, 64, 16, 16, 16, None) == LL_OK
+
+
+def test_gdn_argument_errors():
+    """loglinear_gdn_fwd rejects bad sizes, pointers and workspaces on the host."""
+    L = ll.lib()
+    p = ctypes.c_void_p(1 << 20)   # 16-byte aligned, never dereferenced
+
+    def call(B=1, H=1, T=64, dk=64, dv=16, dtype=0, ws=None, nbytes=0, ptr=p):
+        return L.loglinear_gdn_fwd(ptr, p, p, p, p, p, p, B, H, T, dk, dv, dtype, ws, nbytes, None)
+
+    assert call(dk=32) == LL_ERR_UNSUPPORTED
+    assert call(dk=256) == LL_ERR_UNSUPPORTED
+    assert call(dv=24) == LL_ERR_UNSUPPORTED
+    assert call(dv=0) == LL_ERR_SHAPE
+    assert call(B=-1) == LL_ERR_SHAPE
+    assert call(dtype=7) == LL_ERR_SHAPE
+    assert call(T=64 * 8193, dk=128) == LL_ERR_UNSUPPORTED   # 14 chunk-level bits: states exceed LDS
+    assert call(ptr=None) == LL_ERR_NULL
+    assert call(B=0, ptr=None) == LL_OK
+    assert call(ptr=ctypes.c_void_p((1 << 20) + 8)) == LL_ERR_SHAPE
+    need = L.loglinear_gdn_workspace_size(1, 1, 64, 64, 16)
+    assert call(ws=p, nbytes=need - 1) == LL_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16), nbytes=need) == LL_ERR_WORKSPACE
+    # 4 (3 dk + 128) * 64 bytes per chunk, plus one float per chunk (each part 256-byte aligned)
+    for B, H, T, dk in [(1, 1, 64, 64), (2, 16, 16384, 128), (1, 2, 4200, 128)]:
+        n = B * H * ((T + 63) // 64)
+        want = ((n * 4 * (3 * dk + 128) * 64 + 255) // 256 + (n * 4 + 255) // 256) * 256
+        assert L.loglinear_gdn_workspace_size(B, H, T, dk, 16) == want
+    assert L.loglinear_gdn_workspace_size(1, 1, 64, 48, 16) == ctypes.c_size_t(-1).value

@@ -1,0 +1,97 @@
+"""GPU parity of the log-linear Gated DeltaNet forward (loglinear_gdn_fwd)
+against the fp64 oracle (oracle/gated_deltanet.py; parity unpinned by the
+pages, pinned by the mathematics in tests/test_oracle_gdn.py).
+
+Tolerance: max |gpu - oracle| <= GDN_TOL * RMS(oracle).  The kernels run
+fp32 end to end (fp32 matrix cores); bf16 inputs are rounded once and the
+oracle gets the same rounded values, so the bound is the same for both input
+types.  Error sources: fp32 products of length <= 128 (~1e-6 relative), the
+in-chunk triangular solve (unit-diagonal, entries |beta (k.k) Gamma| < 1 for
+unit keys) and the exponent of fp32 in-chunk prefix sums of log alpha
+(|g| up to ~150 under strong decay: ~1e-5 relative in exp); GDN_TOL = 1e-4
+leaves room for the chunk-to-chunk carries of the bucket states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import log_linear_attention_attn_amd as ll
+import workloads as W
+from oracle import gated_deltanet as G
+from gpu_util import announce, assert_parity, have_gpu, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+GDN_TOL = 1e-4
+
+CASES = [
+    # (B, H, T, dk, dv, dtype, decay)
+    (1, 1, 1, 64, 16, "f32", "weak"),        # one token
+    (1, 2, 64, 64, 16, "f32", "none"),       # one full chunk
+    (1, 1, 200, 64, 32, "f32", "strong"),    # ragged, four chunks
+    (2, 1, 300, 128, 64, "bf16", "weak"),
+    (1, 1, 1000, 128, 128, "bf16", "none"),  # 16 chunks, chunk-level bits 0-3
+    (1, 2, 700, 128, 48, "f32", "weak"),     # three column slices (grid not a multiple of 8)
+    (1, 1, 4200, 128, 32, "f32", "weak"),    # 66 chunks: chunk-level bits 0-6, ragged
+    (1, 1, 2500, 64, 64, "bf16", "none"),    # dk = 64, 40 chunks
+]
+
+
+def _run(case, seed):
+    B, H, T, dk, dv, dtype, decay = case
+    w = W.GdnWorkload("gdn", B, H, T, dk, dv, dtype, decay, seed=seed)
+    inp = W.make_gdn_inputs(w)
+    announce(f"gdn {case}")
+    got = ll.gdn_fwd(*to_dev(*inp))
+    torch.cuda.synchronize()
+    return inp, got.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}_{}_{}".format(*c))
+def test_gdn_matches_oracle(case):
+    inp, got = _run(case, seed=case[2] + case[4])
+    want = G.loglinear_forward(*inp)
+    assert_parity(got, want, GDN_TOL, f"gdn {case}")
+
+
+def test_gdn_unit_lambda_is_gated_deltanet():
+    """lambda = 1 on every level: the GPU result is Gated DeltaNet's own
+    one-token recurrence (oracle.gated_delta_recurrent)."""
+    w = W.GdnWorkload("gdn", 1, 2, 300, 64, 32, "f32", "weak", seed=4)
+    q, k, v, la, beta, lam = W.make_gdn_inputs(w)
+    lam = torch.ones_like(lam)
+    announce("gdn unit lambda")
+    got = ll.gdn_fwd(*to_dev(q, k, v, la, beta, lam)).cpu().numpy()
+    assert_parity(got, G.gated_delta_recurrent(q, k, v, la, beta), GDN_TOL, "gdn unit lambda")
+
+
+def test_gdn_headline_shape_sampled_rows():
+    """B=2 H=16 T=16384 dk=dv=128 (256 chunks, chunk-level bits 0-7, 256
+    workgroups), weak decay so every level carries weight: sampled rows of
+    two heads against the one-row oracle, at chunk and Fenwick boundaries."""
+    w = W.GDN_LM_T16K
+    inp = W.make_gdn_inputs(w)
+    announce("gdn B2H16 T16384 sampled")
+    dev = to_dev(*inp)
+    ws = torch.empty(ll.gdn_workspace_size(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+    got = ll.gdn_fwd(*dev, workspace=ws)
+    again = ll.gdn_fwd(*dev)
+    torch.cuda.synchronize()
+    assert torch.equal(got, again), "workspace and allocating calls differ"
+    got = got.cpu().numpy()
+    rng = np.random.default_rng(5)
+    fixed = [0, 63, 64, 127, 128, 1023, 1024, 4095, 4096, 8191, 8192, 12287, 16320, 16383]
+    rows = sorted(set(fixed) | set(rng.integers(0, w.T, 6).tolist()))
+    for bh in [(0, 0), (1, 15)]:
+        want = G.loglinear_rows(*inp, bh, rows)
+        assert_parity(got[bh][rows], want, GDN_TOL, f"gdn T16384 rows {bh}")
+
+
+def test_gdn_deterministic():
+    w = W.GdnWorkload("gdn", 1, 2, 900, 128, 32, "bf16", "weak", seed=6)
+    dev = to_dev(*W.make_gdn_inputs(w))
+    announce("gdn determinism")
+    a = ll.gdn_fwd(*dev)
+    b = ll.gdn_fwd(*dev)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
