@@ -1,7 +1,7 @@
 """Benchmark of the log-linear attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 300] [--workload NAME] [--no-cpu-baseline]
-                    [--headline-only] [--pass fwd|bwd|decode|lambda]
+                    [--headline-only] [--pass fwd|bwd|decode|lambda|gdn]
 
 A step is one loglinear_fwd_ex call (segment-state, node and sweep kernels,
 caller-owned workspace) over one batch of synthetic inputs already resident in
@@ -15,10 +15,11 @@ each timed the same way:
   "decode"      one decode step of 64 sequences x 16 heads, L = 17;
   "lambda_proj" the level-weight projection at the same B, T, H, L with hidden
                 width 2048, and its gradient;
+  "gdn"         the log-linear Gated DeltaNet forward at the same B, H, T, dk, dv;
   "pages_context" the pages' own speed statements (context, not a target).
 The backward and the configs run before the headline forward is timed.
---pass bwd / decode / lambda time only the backward, the decode step or the
-projection.
+--pass bwd / decode / lambda / gdn time only the backward, the decode step, the
+projection or the Gated DeltaNet forward.
 Default workload: log-linear Mamba-2 forward, B=2, H=16, T=16384, dk=dv=128,
 bf16 q/k/v, fp32 log_a / lambda / out, L=15, C=64.
 """
@@ -372,6 +373,54 @@ def bwd_record(w, dev, K: int, Wm: int, base=None):
     }
 
 
+def gdn_algorithmic_flops(B, H, T, dk, dv, C=64):
+    """Matrix-product flops of the chunkwise log-linear Gated DeltaNet forward,
+    counted as dense products (no credit for the triangular shapes): per chunk
+    K K^T and Q K^T (2 C^2 dk each), the WY rows and the transformed queries
+    (2 C^2 dk each), the in-chunk coefficients (2 C^3) and the triangular solve
+    (C^3 / 3); per chunk and 16-column slice summed over dv, the in-chunk
+    output and Tb V (2 C^2 dv each), the chunk's own state (2 C dk dv) and, per
+    live bucket level, its output, W S and carried state (3 x 2 C dk dv)."""
+    N = (T + C - 1) // C
+    live = sum(bin(n).count("1") for n in range(N))
+    per_chunk = 8 * C * C * dk + 2 * C ** 3 + C ** 3 / 3 + 4 * C * C * dv + 2 * C * dk * dv
+    return B * H * (N * per_chunk + live * 6 * C * dk * dv)
+
+
+def gdn_record(dev, K: int, Wm: int):
+    """Log-linear Gated DeltaNet forward (loglinear_gdn_fwd: the chunk
+    preparation and level sweep kernels, caller-owned workspace) at
+    B=2 H=16 T=16384 dk=dv=128, timed over K calls after Wm untimed ones."""
+    import torch
+    import log_linear_attention_attn_amd as ll
+    import workloads as W
+    w = W.GDN_LM_T16K
+    q, k, v, la, beta, lam = [t.to(dev) for t in W.make_gdn_inputs(w)]
+    out = torch.empty(w.B, w.H, w.T, w.dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(ll.gdn_workspace_size(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    for _ in range(Wm):
+        ll.gdn_fwd(q, k, v, la, beta, lam, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(K):
+        ll.gdn_fwd(q, k, v, la, beta, lam, out=out, workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+    flops = gdn_algorithmic_flops(w.B, w.H, w.T, w.dk, w.dv)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "C": 64,
+                   "L": w.L, "inputs": f"{w.dtype} q/k/v, fp32 log_alpha/beta/lambda/out", "decay": w.decay},
+        "steps": K, "warmup": Wm, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+        "tflops": tflops, "algorithmic_flops": flops, "workspace_bytes": ws.numel(),
+        "roofline": {"kernel": "whole call: chunk preparation + level sweep (fp32 matrix cores)",
+                     "bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_FP32_TFLOPS, "traffic": None},
+    }
+
+
 def bench_prefill(sets, w, steps: int, warmup: int):
     """Forward plus the decode states at T-1 (loglinear_prefill) on the same
     inputs: the extra cost over the forward is the state emit of the last
@@ -484,7 +533,7 @@ def main():
                     help="time only the headline forward (no other configs, backward, prefill, "
                          "decode or projection objects)")
     ap.add_argument("--seg-log2", type=int, default=-1)
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode", "lambda"], default="fwd",
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode", "lambda", "gdn"], default="fwd",
                     help="time the forward (default, the headline; its line also carries one "
                          "decode and one lambda-projection measurement), the backward, or only the "
                          "decode step or the lambda projection")
@@ -518,6 +567,16 @@ def main():
             "vs_baseline": None, "dtype": rec["dtype"], "data": "synthetic",
             "config": {k: rec[k] for k in ("workload", "B", "T", "D", "H", "L")},
             "roofline": rec["roofline"], "tflops": rec["tflops"], "bwd": rec["bwd"]}))
+        return
+    if args.which == "gdn":
+        rec = gdn_record(dev, args.steps, args.warmup)
+        print(json.dumps({
+            "metric": "log-linear Gated DeltaNet fwd tokens/sec", "value": rec["tokens_per_s"],
+            "unit": "tokens/s", "n_gpus": 1, "steps": rec["steps"], "warmup": rec["warmup"],
+            "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": rec["config"],
+            "roofline": rec["roofline"], "tflops": rec["tflops"],
+            "algorithmic_flops": rec["algorithmic_flops"]}))
         return
     if args.which == "decode":
         rec = bench_decode(dev, args.steps, args.warmup)
@@ -571,6 +630,7 @@ def main():
         rec["prefill"] = bench_prefill(sets, w, K, Wm)
         rec["decode"] = bench_decode(dev, K, Wm)
         rec["lambda_proj"] = bench_lambda(dev, K, Wm)
+        rec["gdn"] = gdn_record(dev, max(3, K // 4), 3)
         # the same shapes with log_a = 0 (no decay), timed last so its launches
         # do not sit among the headline's in a trace: the instruction stream is
         # the same, only the data (and with it the power draw) differs

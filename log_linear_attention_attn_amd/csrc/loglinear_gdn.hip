@@ -284,8 +284,8 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
 // dk tiles w*KTW .. of every bucket state (the state updates).  LDS: the
 // bucket states [slot][KT][64][4] (accumulator order: lane l holds
 // S[16 kt + 4 (l/16) + r][l % 16], which is also the B-operand order over
-// the reduction index d), the products W S per slot [slot][4][64][4], and
-// Tb V [4][64][4].
+// the reduction index d), the products W S per slot [slot][4][64][4], Tb V
+// [4][64][4] and the chunk's chunk-level weights lambda [64 rows][slot].
 // ---------------------------------------------------------------------------
 template <typename IT, int DK>
 __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
@@ -296,6 +296,7 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
   f32x4* st = reinterpret_cast<f32x4*>(sm);  // [NB][KT][64]
   f32x4* yb = st + NB * KT * 64;              // [NB][4][64]
   f32x4* ub = yb + NB * 4 * 64;               // [4][64]
+  float* ls = reinterpret_cast<float*>(ub + 4 * 64);  // [64][NB]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -309,38 +310,73 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
   float* out = a.out + size_t(bh) * a.T * a.dv + n0 + l16;
   const float* lam = a.lam + size_t(bh) * a.T * a.L;
 
-  for (int n = 0; n < a.N; ++n) {
-    const int p0 = n * GC;
+  // one chunk's record fragments and V (B operand: lane holds
+  // V[16 ct + 4 (l/16) + r][n0 + l % 16]) in registers; the next chunk's are
+  // loaded while the current chunk's states are carried
+  struct Rec {
+    f32x4 qt[KT], wt[KT], kh[KTW][4], al[4], tb[4], vb[4];
+  };
+  auto load_rec = [&](int n, Rec& R) {
     const float* rec = a.ws + (size_t(bh) * a.N + n) * gdn_chunk_floats(KT);
-    f32x4 qt[KT], wt[KT], kh[KTW][4], al[4], tb[4];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      qt[kt] = *reinterpret_cast<const f32x4*>(rec + gdn_off_qt(KT) + ((w * KT + kt) * 64 + lane) * 4);
-      wt[kt] = *reinterpret_cast<const f32x4*>(rec + gdn_off_wt(KT) + ((w * KT + kt) * 64 + lane) * 4);
+      R.qt[kt] = *reinterpret_cast<const f32x4*>(rec + gdn_off_qt(KT) + ((w * KT + kt) * 64 + lane) * 4);
+      R.wt[kt] = *reinterpret_cast<const f32x4*>(rec + gdn_off_wt(KT) + ((w * KT + kt) * 64 + lane) * 4);
     }
 #pragma unroll
     for (int dtl = 0; dtl < KTW; ++dtl)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
-        kh[dtl][ct] = *reinterpret_cast<const f32x4*>(
+        R.kh[dtl][ct] = *reinterpret_cast<const f32x4*>(
             rec + gdn_off_kh(KT) + (((w * KTW + dtl) * 4 + ct) * 64 + lane) * 4);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      al[ct] = tb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      R.al[ct] = R.tb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (ct <= w) {
-        al[ct] = *reinterpret_cast<const f32x4*>(rec + gdn_off_al(KT) + ((w * 4 + ct) * 64 + lane) * 4);
-        tb[ct] = *reinterpret_cast<const f32x4*>(rec + gdn_off_tb(KT) + ((w * 4 + ct) * 64 + lane) * 4);
+        R.al[ct] = *reinterpret_cast<const f32x4*>(rec + gdn_off_al(KT) + ((w * 4 + ct) * 64 + lane) * 4);
+        R.tb[ct] = *reinterpret_cast<const f32x4*>(rec + gdn_off_tb(KT) + ((w * 4 + ct) * 64 + lane) * 4);
       }
     }
-    // V as B operand: lane holds V[16 ct + 4 (l/16) + r][n0 + l % 16]
-    f32x4 vb[4];
+    const int p0 = n * GC;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = p0 + 16 * ct + 4 * g4 + r;
-        vb[ct][r] = row < a.T ? load1<IT>(v + size_t(row) * a.dv) : 0.f;
+        R.vb[ct][r] = row < a.T ? load1<IT>(v + size_t(row) * a.dv) : 0.f;
       }
+  };
+  // the chunk-level weights lambda[t, log2(C) + 1 + b] of a chunk's rows, [64][NB]
+  auto load_lam = [&](int n, float* x) {
+    const int p0 = n * GC;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + j * GTHR, row = idx / max(NB, 1), b = idx - row * max(NB, 1);
+      x[j] = (idx < GC * NB && p0 + row < a.T) ? lam[size_t(p0 + row) * a.L + GLOGC + 1 + b] : 0.f;
+    }
+  };
+  auto store_lam = [&](const float* x) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (tid + j * GTHR < GC * NB) ls[tid + j * GTHR] = x[j];
+  };
+
+  Rec cur;
+  load_rec(0, cur);
+  {
+    float x[4];
+    load_lam(0, x);
+    store_lam(x);
+  }
+  __syncthreads();
+  for (int n = 0; n < a.N; ++n) {
+    const int p0 = n * GC;
+    const f32x4 (&qt)[KT] = cur.qt;
+    const f32x4 (&wt)[KT] = cur.wt;
+    const f32x4 (&kh)[KTW][4] = cur.kh;
+    const f32x4 (&al)[4] = cur.al;
+    const f32x4 (&tb)[4] = cur.tb;
+    const f32x4 (&vb)[4] = cur.vb;
 
     // in-chunk pairs and the chunk's own Tb V (rows of tile w)
     f32x4 o = {0.f, 0.f, 0.f, 0.f}, u = o;
@@ -366,12 +402,8 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
           y = mma4(wt[kt][r], s[r], y);
         }
       }
-      const int lev = GLOGC + 1 + b;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = p0 + 16 * w + 4 * g4 + r;
-        if (t < a.T) o[r] += lam[size_t(t) * a.L + lev] * oq[r];
-      }
+      for (int r = 0; r < 4; ++r) o[r] += ls[(16 * w + 4 * g4 + r) * NB + b] * oq[r];
       yb[(b * 4 + w) * 64 + lane] = y;
     }
 #pragma unroll
@@ -382,6 +414,10 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
     ub[w * 64 + lane] = u;
     __syncthreads();
     if (n + 1 < a.N) {
+      Rec nxt;
+      load_rec(n + 1, nxt);
+      float lx[4];
+      load_lam(n + 1, lx);
       // carry the states over the chunk, add the chunk's own state, merge by lssb(n + 1)
       const int m = __ffs(n + 1) - 1;
       const float gC = a.gchunk[size_t(bh) * a.N + n];
@@ -422,7 +458,9 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
       }
 #pragma unroll
       for (int dtl = 0; dtl < KTW; ++dtl) st[(m * KT + w * KTW + dtl) * 64 + lane] = own[dtl];
+      store_lam(lx);
       __syncthreads();
+      cur = nxt;
     }
   }
 }
@@ -431,7 +469,7 @@ template <typename IT, int DK>
 int launch_gdn_t(const GdnArgs& a, hipStream_t s) {
   constexpr int KT = DK / 16;
   const int prep_lds = (2 * GC * (DK + 4) + 2 * GC * LDM + 3 * GC) * 4;
-  const int sweep_lds = (a.nslot * KT * 64 + a.nslot * 4 * 64 + 4 * 64) * 16;
+  const int sweep_lds = gdn_sweep_lds_bytes(a.nslot, DK);
   if (sweep_lds > kMaxLds) return LL_ERR_UNSUPPORTED;
   static std::atomic<uint64_t> raised[2];
   if (!raise_lds_limit(reinterpret_cast<const void*>(&gdn_prep_kernel<IT, DK>), raised[0])) return LL_ERR_HIP;
@@ -453,7 +491,9 @@ size_t gdn_workspace_bytes(long long BH, int N, int dk) {
   return ((size_t(BH) * N * rec + 255) & ~size_t(255)) + ((size_t(BH) * N * 4 + 255) & ~size_t(255));
 }
 
-int gdn_sweep_lds_bytes(int nslot, int dk) { return (nslot * (dk / 16) * 64 + nslot * 4 * 64 + 4 * 64) * 16; }
+int gdn_sweep_lds_bytes(int nslot, int dk) {
+  return (nslot * (dk / 16) * 64 + nslot * 4 * 64 + 4 * 64) * 16 + GC * nslot * 4;
+}
 
 int launch_gdn(int dtype, const GdnArgs& a, hipStream_t s) {
   if (a.dk == 128) return dtype == LL_BF16 ? launch_gdn_t<uint16_t, 128>(a, s) : launch_gdn_t<float, 128>(a, s);
