@@ -121,20 +121,23 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
   float* rec = a.ws + size_t(cid) * gdn_chunk_floats(KT);
 
   // Phase 0: K, Q rows to LDS (zero past T), beta, and the in-chunk prefix of log alpha.
+  // (loads from a clamped row, then a select: a load under a branch would
+  // make the compiler wait for it before the next one)
+#pragma unroll
   for (int idx = tid; idx < GC * DK / 4; idx += GTHR) {
     const int r = idx / (DK / 4), c = (idx - r * (DK / 4)) * 4;
-    f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv;
-    if (r < nrow) {
-      kv = load4<IT>(k + r * DK + c);
-      qv = load4<IT>(q + r * DK + c);
-    }
-    *reinterpret_cast<f32x4*>(Ks + r * LDK + c) = kv;
-    *reinterpret_cast<f32x4*>(Qs + r * LDK + c) = qv;
+    const int rr = min(r, nrow - 1);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 kv = load4<IT>(k + rr * DK + c), qv = load4<IT>(q + rr * DK + c);
+    *reinterpret_cast<f32x4*>(Ks + r * LDK + c) = r < nrow ? kv : z;
+    *reinterpret_cast<f32x4*>(Qs + r * LDK + c) = r < nrow ? qv : z;
   }
   if (w == 0) {
     const bool in = lane < nrow;
-    float x = in ? a.log_alpha[size_t(bh) * a.T + p0 + lane] : 0.f;
-    const float b = in ? a.beta[size_t(bh) * a.T + p0 + lane] : 0.f;
+    const int ll_ = min(lane, nrow - 1);
+    const float xa = a.log_alpha[size_t(bh) * a.T + p0 + ll_], xb = a.beta[size_t(bh) * a.T + p0 + ll_];
+    float x = in ? xa : 0.f;
+    const float b = in ? xb : 0.f;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const float y = __shfl_up(x, d);
@@ -199,6 +202,13 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
   // over the rows of K with Tb[t][c] != 0, c <= t.  The accumulator of tile
   // (kt, rt) is W's fragment (rt, kt); it also goes to LDS (row-major) for Q~.
   float* Ws = Qs;
+  // the rows of Q that phase 4 needs, loaded now so they arrive during phase 3
+  f32x4 qpre[KTW][4];
+#pragma unroll
+  for (int ktl = 0; ktl < KTW; ++ktl)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      qpre[ktl][rt] = load4<IT>(q + min(16 * rt + l16, nrow - 1) * DK + 16 * (w * KTW + ktl) + 4 * g4);
 #pragma unroll
   for (int ktl = 0; ktl < KTW; ++ktl) {
     const int kt = w * KTW + ktl;
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
     const int rt = w;
     const int t = 16 * rt + l16;
     const bool trow = t < nrow;
-    const float* lam_t = a.lam + (size_t(bh) * a.T + p0 + (trow ? t : 0)) * a.L;
+    const float* lam_t = a.lam + (size_t(bh) * a.T + p0 + min(t, nrow - 1)) * a.L;
     for (int ct = 0; ct <= rt; ++ct) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int c0 = 16 * ct; c0 < 16 * rt + 16; c0 += 4) {
@@ -228,7 +238,8 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * ct + 4 * g4 + r;
-        acc[r] = (trow && s <= t) ? acc[r] * lam_t[level_of(uint32_t(t), uint32_t(s))] : 0.f;
+        const float lw = lam_t[min(level_of(uint32_t(t), uint32_t(s)), a.L - 1)];
+        acc[r] = (trow && s <= t) ? acc[r] * lw : 0.f;
       }
       *reinterpret_cast<f32x4*>(rec + gdn_off_al(KT) + ((rt * 4 + ct) * 64 + lane) * 4) = acc;
       // Tb's fragment (rt, ct)
@@ -262,6 +273,7 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
   for (int ktl = 0; ktl < KTW; ++ktl) {
     const int kt = w * KTW + ktl;
+#pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int t = 16 * rt + l16;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -269,9 +281,8 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
         const int c = c0 + g4;
         acc = mma4(Ws[c * LDK + 16 * kt + l16], QG[t * LDM + c], acc);
       }
-      f32x4 qv = {0.f, 0.f, 0.f, 0.f};
-      if (t < nrow) qv = load4<IT>(q + t * DK + 16 * kt + 4 * g4);
-      const float gt = gam[t];
+      const f32x4 qv = qpre[ktl][rt];
+      const float gt = t < nrow ? gam[t] : 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = gt * qv[r] - acc[r];
       *reinterpret_cast<f32x4*>(rec + gdn_off_qt(KT) + ((rt * KT + kt) * 64 + lane) * 4) = acc;
@@ -343,7 +354,8 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = p0 + 16 * ct + 4 * g4 + r;
-        R.vb[ct][r] = row < a.T ? load1<IT>(v + size_t(row) * a.dv) : 0.f;
+        const float x = load1<IT>(v + size_t(min(row, a.T - 1)) * a.dv);
+        R.vb[ct][r] = row < a.T ? x : 0.f;
       }
   };
   // the chunk-level weights lambda[t, log2(C) + 1 + b] of a chunk's rows, [64][NB]
@@ -352,7 +364,9 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = tid + j * GTHR, row = idx / max(NB, 1), b = idx - row * max(NB, 1);
-      x[j] = (idx < GC * NB && p0 + row < a.T) ? lam[size_t(p0 + row) * a.L + GLOGC + 1 + b] : 0.f;
+      const bool in = idx < GC * NB && p0 + row < a.T;
+      const float y = lam[size_t(min(p0 + row, a.T - 1)) * a.L + min(GLOGC + 1 + b, a.L - 1)];
+      x[j] = in ? y : 0.f;
     }
   };
   auto store_lam = [&](const float* x) {
