@@ -93,8 +93,9 @@ __host__ __device__ constexpr size_t gdn_off_tb(int KT) { return size_t(3072) * 
 __host__ __device__ constexpr size_t gdn_chunk_floats(int KT) { return size_t(3072) * KT + 8192; }
 
 // ---------------------------------------------------------------------------
-// Chunk preparation.  LDS: K and Q (later W) as fp32 rows of DK + 4, the C x C
-// matrices N (later Tb) and Q K^T ⊙ Gamma ⊙ tril, and g, gamma, beta.
+// Chunk preparation.  LDS (~68 KiB at dk = 128, two workgroups per CU): K as
+// fp32 rows of DK + 4, the C x C matrices N (later Tb) and Q K^T ⊙ Gamma ⊙
+// tril (later Ceff), and g, gamma, beta.  Q is read from global memory.
 // ---------------------------------------------------------------------------
 template <typename IT, int DK>
 __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
@@ -103,9 +104,8 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
   constexpr int LDK = DK + 4;
   extern __shared__ __align__(16) float sm[];
   float* Ks = sm;
-  float* Qs = Ks + GC * LDK;  // Q, then W (row-major, C x dk)
-  float* Nm = Qs + GC * LDK;  // N, then Tb
-  float* QG = Nm + GC * LDM;
+  float* Nm = Ks + GC * LDK;  // N, then Tb
+  float* QG = Nm + GC * LDM;  // Q K^T ⊙ Gamma ⊙ tril, then Ceff
   float* gs = QG + GC * LDM;
   float* gam = gs + GC;
   float* bs = gam + GC;
@@ -120,17 +120,22 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
   const IT* k = static_cast<const IT*>(a.k) + (size_t(bh) * a.T + p0) * DK;
   float* rec = a.ws + size_t(cid) * gdn_chunk_floats(KT);
 
-  // Phase 0: K, Q rows to LDS (zero past T), beta, and the in-chunk prefix of log alpha.
+  // Phase 0: K rows to LDS (zero past T), beta, and the in-chunk prefix of
+  // log alpha; this wave's Q rows (row tile w) to registers for phase 1.
   // (loads from a clamped row, then a select: a load under a branch would
   // make the compiler wait for it before the next one)
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 qa[KT];
+#pragma unroll
+  for (int kq = 0; kq < KT; ++kq) {
+    const f32x4 x = load4<IT>(q + min(16 * w + l16, nrow - 1) * DK + 16 * kq + 4 * g4);
+    qa[kq] = 16 * w + l16 < nrow ? x : z4;
+  }
 #pragma unroll
   for (int idx = tid; idx < GC * DK / 4; idx += GTHR) {
     const int r = idx / (DK / 4), c = (idx - r * (DK / 4)) * 4;
-    const int rr = min(r, nrow - 1);
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 kv = load4<IT>(k + rr * DK + c), qv = load4<IT>(q + rr * DK + c);
-    *reinterpret_cast<f32x4*>(Ks + r * LDK + c) = r < nrow ? kv : z;
-    *reinterpret_cast<f32x4*>(Qs + r * LDK + c) = r < nrow ? qv : z;
+    const f32x4 kv = load4<IT>(k + min(r, nrow - 1) * DK + c);
+    *reinterpret_cast<f32x4*>(Ks + r * LDK + c) = r < nrow ? kv : z4;
   }
   if (w == 0) {
     const bool in = lane < nrow;
@@ -152,14 +157,19 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
   // Phase 1: K K^T and Q K^T, row tile w, column tiles <= w.
   //   N[i][j]  = beta_i (k_i . k_j) Gamma[i][j]   j < i,  else 0
   //   QG[i][j] = (q_i . k_j) Gamma[i][j]          j <= i, else 0
+  // (reduction index of fragment step r of block kq: 16 kq + 4 (l/16) + r)
   for (int ct = 0; ct < 4; ++ct) {
     f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
     if (ct <= w) {
-#pragma unroll 8
-      for (int k0 = 0; k0 < DK; k0 += 4) {
-        const float bk = Ks[(16 * ct + l16) * LDK + k0 + g4];
-        kk = mma4(Ks[(16 * w + l16) * LDK + k0 + g4], bk, kk);
-        qk = mma4(Qs[(16 * w + l16) * LDK + k0 + g4], bk, qk);
+#pragma unroll
+      for (int kq = 0; kq < KT; ++kq) {
+        const f32x4 bk = *reinterpret_cast<const f32x4*>(Ks + (16 * ct + l16) * LDK + 16 * kq + 4 * g4);
+        const f32x4 ak = *reinterpret_cast<const f32x4*>(Ks + (16 * w + l16) * LDK + 16 * kq + 4 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          kk = mma4(ak[r], bk[r], kk);
+          qk = mma4(qa[kq][r], bk[r], qk);
+        }
       }
     }
     const int j = 16 * ct + l16;
@@ -200,8 +210,7 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
 
   // Phase 3a: W^T = (gamma K)^T Tb^T, tiles (kt, rt); reduction index c runs
   // over the rows of K with Tb[t][c] != 0, c <= t.  The accumulator of tile
-  // (kt, rt) is W's fragment (rt, kt); it also goes to LDS (row-major) for Q~.
-  float* Ws = Qs;
+  // (kt, rt) is W's fragment (rt, kt).
   // the rows of Q that phase 4 needs, loaded now so they arrive during phase 3
   f32x4 qpre[KTW][4];
 #pragma unroll
@@ -219,22 +228,32 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
         acc = mma4(Ks[c * LDK + 16 * kt + l16] * gam[c], Tb[(16 * rt + l16) * LDM + c], acc);
       }
       *reinterpret_cast<f32x4*>(rec + gdn_off_wt(KT) + ((rt * KT + kt) * 64 + lane) * 4) = acc;
-      *reinterpret_cast<f32x4*>(Ws + (16 * rt + l16) * LDK + 16 * kt + 4 * g4) = acc;
     }
   }
   // Phase 3b: Ceff^T = Tb^T QG^T, tiles (ct, rt) with ct <= rt = w: the
   // accumulator is Ceff's fragment (rt, ct); times the in-chunk level weight.
+  // Ceff itself replaces this wave's rows of QG (each wave reads and writes
+  // only its own rows t, so no other wave is affected) for phase 4.
   {
     const int rt = w;
     const int t = 16 * rt + l16;
     const bool trow = t < nrow;
     const float* lam_t = a.lam + (size_t(bh) * a.T + p0 + min(t, nrow - 1)) * a.L;
-    for (int ct = 0; ct <= rt; ++ct) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 16 * ct; c0 < 16 * rt + 16; c0 += 4) {
-        const int c = c0 + g4;
-        acc = mma4(Tb[c * LDM + 16 * ct + l16], QG[t * LDM + c], acc);
-      }
+    f32x4 ce[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      ce[ct] = z4;
+      if (ct <= rt)
+        for (int c0 = 16 * ct; c0 < 16 * rt + 16; c0 += 4) {
+          const int c = c0 + g4;
+          ce[ct] = mma4(Tb[c * LDM + 16 * ct + l16], QG[t * LDM + c], ce[ct]);
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct > rt) continue;
+      *reinterpret_cast<f32x4*>(QG + t * LDM + 16 * ct + 4 * g4) = ce[ct];
+      f32x4 acc = ce[ct];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * ct + 4 * g4 + r;
@@ -267,9 +286,10 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
   }
   __syncthreads();
 
-  // Phase 4: Q~^T = (gamma Q)^T - W^T QG^T, tiles (kt, rt): the accumulator is
-  // Q~'s fragment (rt, kt).  gamma Q comes from global memory (Q's LDS rows
-  // now hold W).
+  // Phase 4: Q~ = gamma Q - QG W = gamma Q - Ceff (gamma K) (W = Tb gamma K),
+  // as Q~^T = (gamma Q)^T - (gamma K)^T Ceff^T, tiles (kt, rt): the
+  // accumulator is Q~'s fragment (rt, kt).
+  const float* CE = QG;
 #pragma unroll
   for (int ktl = 0; ktl < KTW; ++ktl) {
     const int kt = w * KTW + ktl;
@@ -279,7 +299,7 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int c0 = 0; c0 < 16 * rt + 16; c0 += 4) {
         const int c = c0 + g4;
-        acc = mma4(Ws[c * LDK + 16 * kt + l16], QG[t * LDM + c], acc);
+        acc = mma4(Ks[c * LDK + 16 * kt + l16] * gam[c], CE[t * LDM + c], acc);
       }
       const f32x4 qv = qpre[ktl][rt];
       const float gt = t < nrow ? gam[t] : 0.f;
@@ -482,7 +502,7 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
 template <typename IT, int DK>
 int launch_gdn_t(const GdnArgs& a, hipStream_t s) {
   constexpr int KT = DK / 16;
-  const int prep_lds = (2 * GC * (DK + 4) + 2 * GC * LDM + 3 * GC) * 4;
+  const int prep_lds = (GC * (DK + 4) + 2 * GC * LDM + 3 * GC) * 4;
   const int sweep_lds = gdn_sweep_lds_bytes(a.nslot, DK);
   if (sweep_lds > kMaxLds) return LL_ERR_UNSUPPORTED;
   static std::atomic<uint64_t> raised[2];
