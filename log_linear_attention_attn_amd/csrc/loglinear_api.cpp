@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 
 #include "ll_internal.h"
 #include "loglinear.h"
@@ -340,6 +341,42 @@ int run_lambda_proj_bwd(int dtype, const void* x, const void* W, const float* la
   return st;
 }
 
+// A second stream per device for the part of the backward that does not
+// depend on the rest (the dQ chain runs beside the dK / dV chain, joined by an
+// event before the kernels that need both).  Default priority; created on
+// first use and kept until the process ends.  `mu` makes one call's
+// fork/join sequence atomic with respect to other host threads, since the two
+// events are shared.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+SideStream* side_stream() {
+  static SideStream ss[64];
+  static std::mutex init_mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(init_mu);
+  SideStream& x = ss[dev];
+  if (!x.s) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f) hipEventDestroy(f);
+      hipStreamDestroy(s);
+      return nullptr;
+    }
+    x.fork = f;
+    x.join = j;
+    x.s = s;
+  }
+  return &x;
+}
+
 int run_bwd(int dtype, const void* q, const void* k, const void* v, const float* log_a,
             const float* lambda, const float* out, const float* dout, float* dq, float* dk_out,
             float* dv_out, float* dlog_a, float* dlambda, int B, int H, int T, int dk, int dv, int C,
@@ -395,6 +432,15 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
   ll::BwdArgs a{q, k, v, log_a, lambda, out, dout, dq_h, dk_h, dv_out, dlog_a, dlambda,
                 reinterpret_cast<float*>(wsb), reinterpret_cast<double*>(wsb + part),
                 p.BH, T, dk, dv, p.L, p.nslot, G};
+  // the dQ chain on the side stream when the dK / dV chain runs too
+  SideStream* side = dq_rs && kv_rev ? side_stream() : nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  hipStream_t qs = stream;
+  if (side) {
+    side_lock = std::unique_lock<std::mutex>(side->mu);
+    if (hipEventRecord(side->fork, stream) == hipSuccess && hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess)
+      qs = side->s;
+  }
   if (dq_rs) {
     char* fw = wsb + part + dcb + 2 * per_head;
     float* blk_state = reinterpret_cast<float*>(fw);
@@ -404,11 +450,11 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
     if (pd.nseg > 1) {
       // segment states of the swapped problem: keys v, values k
       ll::SegArgs sa{v, k, log_a, blk_state, blk_decay, pd.BH, T, dv, dk, C, pd.blk_log2, pd.nblk1, 1};
-      st = ll::launch_seg_state_rs(sa, pd.BH, stream);
+      st = ll::launch_seg_state_rs(sa, pd.BH, qs);
       if (st == LL_OK) {
         ll::NodeArgs na{blk_state, blk_decay, nodes, seg_decay, pd.nseg, pd.nblk1, pd.seg_log2 - pd.blk_log2,
                         dk * pd.DKP};
-        st = ll::launch_seg_nodes(na, pd.BH, stream);
+        st = ll::launch_seg_nodes(na, pd.BH, qs);
       }
     }
     const long long pairs = (long long)pd.BH * pd.nseg;
@@ -419,7 +465,7 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
                      pd.seg_log2, pd.nseg, pd.nslot, nullptr, 0, 1};
       fa.qo = q;
       fa.dlam_part = a.dlam_part;
-      st = ll::launch_sweep_rs_dlam(fa, static_cast<int>(nblocks), stream);
+      st = ll::launch_sweep_rs_dlam(fa, static_cast<int>(nblocks), qs);
     }
     a.dq_done = 1;
     a.dlam_parts = dk / 64;
@@ -439,6 +485,13 @@ int run_bwd(int dtype, const void* q, const void* k, const void* v, const float*
     a.dlam_intra_part = ra.intra_part;
     a.intra_parts = dv / 64;
     a.dc_blk = reinterpret_cast<double*>(wsb + part + dcb + 2 * per_head + fws + rws + iws);
+  }
+  // join: whatever was enqueued on the side stream finishes before the main
+  // stream goes on (also after an error, before the workspace is freed)
+  if (qs != stream && (hipEventRecord(side->join, qs) != hipSuccess ||
+                       hipStreamWaitEvent(stream, side->join, 0) != hipSuccess)) {
+    if (st == LL_OK) st = LL_ERR_HIP;
+    hipStreamSynchronize(qs);
   }
   if (st == LL_OK) st = ll::launch_bwd(dtype, C, a, stream);
   if (st == LL_OK && G > 1) {
