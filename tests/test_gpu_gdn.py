@@ -95,3 +95,19 @@ def test_gdn_deterministic():
     b = ll.gdn_fwd(*dev)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T,decay", [(65536, "weak"), (8192, "none")], ids=["T65536_weak", "T8192_none"])
+def test_gdn_long_sampled_rows(T, decay):
+    """One (b,h), one 16-column slice: T = 65536 walks 1024 chunks with ten
+    chunk-level bits (the sweep's LDS at 124 KiB); T = 8192 ends exactly on a
+    chunk boundary with 128 chunks.  Sampled rows at chunk, Fenwick and
+    end-of-sequence boundaries against the one-row oracle."""
+    w = W.GdnWorkload("gdn_long", 1, 1, T, 128, 16, "bf16", decay, seed=T % 97)
+    inp = W.make_gdn_inputs(w)
+    announce(f"gdn long T={T} {decay}")
+    got = ll.gdn_fwd(*to_dev(*inp)).cpu().numpy()
+    fixed = [0, 63, 64, 4095, 4096, T // 2 - 1, T // 2, T - 65, T - 64, T - 1]
+    rows = sorted(set(r for r in fixed if r < T) | set(np.random.default_rng(3).integers(0, T, 4).tolist()))
+    want = G.loglinear_rows(*inp, (0, 0), rows)
+    assert_parity(got[0, 0][rows], want, GDN_TOL, f"gdn T={T} rows")
