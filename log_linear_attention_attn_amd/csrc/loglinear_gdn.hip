@@ -423,23 +423,41 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
           u = mma4(tb[ct][r], vb[ct][r], u);
         }
       }
-    // bucket states of the chunk prefix: one per set bit b of n
+    // bucket states of the chunk prefix: one per set bit b of n.  The levels
+    // b < m = lssb(n + 1) are merged into one bucket after this chunk; the
+    // carry is linear, so only the sum of their W S is kept (slot m, unused
+    // by the live bits of n)
+    const int m = n + 1 < a.N ? __ffs(n + 1) - 1 : 0;
+    f32x4 ysum = {0.f, 0.f, 0.f, 0.f};
     for (int b = 0; b < NB; ++b) {
       if (!((n >> b) & 1)) continue;
       f32x4 oq = {0.f, 0.f, 0.f, 0.f}, y = oq;
+      if (b < m) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const f32x4 s = st[(b * KT + kt) * 64 + lane];
+        for (int kt = 0; kt < KT; ++kt) {
+          const f32x4 s = st[(b * KT + kt) * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          oq = mma4(qt[kt][r], s[r], oq);
-          y = mma4(wt[kt][r], s[r], y);
+          for (int r = 0; r < 4; ++r) {
+            oq = mma4(qt[kt][r], s[r], oq);
+            ysum = mma4(wt[kt][r], s[r], ysum);
+          }
         }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const f32x4 s = st[(b * KT + kt) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            oq = mma4(qt[kt][r], s[r], oq);
+            y = mma4(wt[kt][r], s[r], y);
+          }
+        }
+        yb[(b * 4 + w) * 64 + lane] = y;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] += ls[(16 * w + 4 * g4 + r) * NB + b] * oq[r];
-      yb[(b * 4 + w) * 64 + lane] = y;
     }
+    if (m > 0) yb[(m * 4 + w) * 64 + lane] = ysum;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = p0 + 16 * w + 4 * g4 + r;
@@ -452,8 +470,9 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
       load_rec(n + 1, nxt);
       float lx[4];
       load_lam(n + 1, lx);
-      // carry the states over the chunk, add the chunk's own state, merge by lssb(n + 1)
-      const int m = __ffs(n + 1) - 1;
+      // carry the states over the chunk, add the chunk's own state, merge by
+      // lssb(n + 1): the merged bucket is K^T (Tb V) + sum_{b<m} (gamma_C S^b -
+      // K^T W S^b) = gamma_C sum_{b<m} S^b + K^T (Tb V - sum_{b<m} W S^b)
       const float gC = a.gchunk[size_t(bh) * a.N + n];
       f32x4 own[KTW];
 #pragma unroll
@@ -461,12 +480,25 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
         own[dtl] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const f32x4 uu = ub[ct * 64 + lane];
+          f32x4 uu = ub[ct * 64 + lane];
+          if (m > 0) {
+            const f32x4 ys = yb[(m * 4 + ct) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) uu[r] -= ys[r];
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) own[dtl] = mma4(kh[dtl][ct][r], uu[r], own[dtl]);
         }
       }
-      for (int b = 0; b < NB; ++b) {
+      for (int b = 0; b < m; ++b) {
+#pragma unroll
+        for (int dtl = 0; dtl < KTW; ++dtl) {
+          const f32x4 s = st[(b * KT + w * KTW + dtl) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) own[dtl][r] += gC * s[r];
+        }
+      }
+      for (int b = m; b < NB; ++b) {
         if (!((n >> b) & 1)) continue;
 #pragma unroll
         for (int dtl = 0; dtl < KTW; ++dtl) {
@@ -482,12 +514,7 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
           f32x4 ns;
 #pragma unroll
           for (int r = 0; r < 4; ++r) ns[r] = gC * s[r] - ky[r];
-          if (b < m) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) own[dtl][r] += ns[r];
-          } else {
-            st[(b * KT + dt) * 64 + lane] = ns;
-          }
+          st[(b * KT + dt) * 64 + lane] = ns;
         }
       }
 #pragma unroll
