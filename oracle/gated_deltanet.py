@@ -161,3 +161,43 @@ def loglinear_rows(q, k, v, log_alpha, beta, lam, bh: tuple[int, int], rows) -> 
         lev = level_rows(t, t + 1, t + 1)[0]
         res.append((coef * lm[t, lev]) @ vh[: t + 1])
     return np.stack(res) if res else np.zeros((0, vh.shape[-1]))
+
+
+def decode_step(states, q, k, v, log_alpha, beta, lam, t):
+    """One decode step of log-linear Gated DeltaNet for every (sequence, head).
+
+    states: [N, H, L, dk, dv] holding the bucket states after t-1 (k-major;
+    levels dead at t-1 are 0); q, k: [N, H, dk]; v: [N, H, dv];
+    log_alpha, beta: [N, H]; lam: [N, H, L]; t: [N] positions of the tokens.
+    Returns (out [N, H, dv], new_states) and leaves ``states`` untouched.
+
+    With m = lssb(t) ([P1] 解码：基于 lssb 的状态更新): level m+1 takes the sum
+    of levels 0..m, levels 0..m are emptied, then every level passes through
+    A_t = alpha_t (I - beta_t k_t k_t^T), and level 0 receives beta_t k_t v_t^T
+    (at t = 0 every level starts empty).  o_t = sum_l lam[l] (S^l)^T q_t.
+    Positions outside [0, 2^(L-1)) give a NaN output row and unchanged states.
+    """
+    S = _f64(states).copy()
+    q, k, v, log_alpha, beta, lam = (_f64(x) for x in (q, k, v, log_alpha, beta, lam))
+    t = np.asarray(t.detach().cpu().numpy() if hasattr(t, "detach") else t, dtype=np.int64)
+    N, H, L, dk, dv = S.shape
+    out = np.zeros((N, H, dv))
+    for i in range(N):
+        ti = int(t[i])
+        if ti < 0 or ti >= (1 << (L - 1)):
+            out[i] = np.nan
+            continue
+        for h in range(H):
+            lev = S[i, h]
+            kk, bt = k[i, h], beta[i, h]
+            if ti == 0:
+                lev[:] = 0.0
+            else:
+                m = lssb(ti)
+                lev[m + 1] = lev[: m + 1].sum(axis=0)
+                lev[: m + 1] = 0.0
+                for level in range(L):
+                    lev[level] = np.exp(log_alpha[i, h]) * (lev[level] - bt * np.outer(kk, kk @ lev[level]))
+            lev[0] = bt * np.outer(kk, v[i, h])
+            out[i, h] = np.einsum("l,d,lde->e", lam[i, h], q[i, h], lev)
+    return out, S

@@ -135,3 +135,33 @@ def test_rows_match_dense():
     for bh in [(0, 1), (1, 0)]:
         np.testing.assert_allclose(G.loglinear_rows(q, k, v, la, beta, lam, bh, rows), dense[bh][rows],
                                    rtol=1e-11, atol=1e-12)
+
+
+def test_decode_chain_equals_dense():
+    """Decode steps from empty states over t = 0..T-1 reproduce the dense
+    definition row by row (the step of [P1] 解码：基于 lssb 的状态更新 with the
+    transition A_t on every level), and levels dead at t hold exactly 0."""
+    rng = np.random.default_rng(7)
+    B, H, T, dk, dv = 2, 1, 40, 5, 3
+    q, k, v, la, beta, lam = _inputs(rng, B, H, T, dk, dv)
+    L = lam.shape[-1]
+    want = G.loglinear_forward(q, k, v, la, beta, lam)
+    S = np.zeros((B, H, L, dk, dv))
+    for t in range(T):
+        o, S = G.decode_step(S, q[:, :, t], k[:, :, t], v[:, :, t], la[:, :, t], beta[:, :, t],
+                             lam[:, :, t], np.full(B, t))
+        np.testing.assert_allclose(o, want[:, :, t], rtol=1e-10, atol=1e-12)
+        live = {0} | {b + 1 for b in range(L - 1) if (t >> b) & 1}
+        for level in range(L):
+            assert np.any(S[:, :, level]) == (level in live), (t, level)
+
+
+def test_decode_out_of_range_position():
+    rng = np.random.default_rng(8)
+    S = rng.standard_normal((2, 1, 4, 3, 2))
+    q, k = rng.standard_normal((2, 1, 3)), rng.standard_normal((2, 1, 3))
+    v, la, beta = rng.standard_normal((2, 1, 2)), -rng.random((2, 1)), rng.random((2, 1))
+    lam = rng.random((2, 1, 4))
+    o, S2 = G.decode_step(S, q, k, v, la, beta, lam, np.array([8, 3]))
+    assert np.all(np.isnan(o[0])) and np.array_equal(S2[0], S[0])
+    assert np.all(np.isfinite(o[1]))

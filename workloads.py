@@ -268,3 +268,36 @@ def make_gdn_inputs(w: GdnWorkload):
     return (torch.from_numpy(q).to(tdt), torch.from_numpy(k).to(tdt), torch.from_numpy(v).to(tdt),
             torch.from_numpy(np.ascontiguousarray(log_alpha)), torch.from_numpy(beta),
             torch.from_numpy(lam))
+
+
+GDN_DECODE_64x16 = DecodeWorkload("gdn_decode_N64_H16_dk128_dv128_L17", 64, 16, 128, 128, 17, 65535, seed=5)
+
+
+def make_gdn_decode_inputs(w: DecodeWorkload, t: np.ndarray | None = None):
+    """Draw (states, q, k, v, log_alpha, beta, lam, t) for one log-linear Gated
+    DeltaNet decode step, in this order: states as make_decode_inputs (levels
+    live at t-1 ~ N(0,1)/dk, dead levels exactly 0), q, v ~ N(0,1)/sqrt(dk),
+    k ~ N(0,1) L2-normalised, log_alpha = -softplus(N(0,1)+2), beta =
+    sigmoid(N(0,1)), lam = softplus(N(0,1)), t ~ U{1..t_max} unless given."""
+    rng = np.random.default_rng(w.seed)
+    N, H, dk, dv, L = w.N, w.H, w.dk, w.dv, w.L
+    if t is None:
+        t = rng.integers(1, w.t_max + 1, N).astype(np.int32)
+    t = np.asarray(t, dtype=np.int32)
+    S = np.zeros((N, H, L, dk, dv), dtype=np.float32)
+    for i in range(N):
+        if t[i] >= 1:
+            for level in live_levels(int(t[i]) - 1, L):
+                S[i, :, level] = rng.standard_normal((H, dk, dv), dtype=np.float32) / np.float32(dk)
+    scale = np.float32(1.0 / math.sqrt(dk))
+    q = rng.standard_normal((N, H, dk), dtype=np.float32) * scale
+    k = rng.standard_normal((N, H, dk), dtype=np.float32)
+    k = (k / np.maximum(np.sqrt(np.sum(k.astype(np.float64) ** 2, axis=-1, keepdims=True)), 1e-12)).astype(np.float32)
+    v = rng.standard_normal((N, H, dv), dtype=np.float32) * scale
+    log_alpha = -_softplus(rng.standard_normal((N, H), dtype=np.float32) + 2.0)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((N, H)).astype(np.float64)))).astype(np.float32)
+    lam = _softplus(rng.standard_normal((N, H, L), dtype=np.float32))
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return (torch.from_numpy(S), torch.from_numpy(q).to(tdt), torch.from_numpy(k).to(tdt),
+            torch.from_numpy(v).to(tdt), torch.from_numpy(np.ascontiguousarray(log_alpha)),
+            torch.from_numpy(beta), torch.from_numpy(lam), torch.from_numpy(t))
