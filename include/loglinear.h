@@ -368,6 +368,30 @@ int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const float* 
                       const float* beta, const float* lambda, float* out, int B, int H, int T, int dk,
                       int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One O(log T) decode step of log-linear Gated DeltaNet (the delta rule as in
+ * loglinear_gdn_fwd; the decode rule of the page above, section 解码：基于
+ * lssb 的状态更新, with the transition in place of the scalar decay) for N
+ * sequences x H heads.
+ *   states : as loglinear_decode_step (k-major [N, H, L, dk, dv] fp32, levels
+ *            dead at t-1 equal to 0), updated in place: with m = lssb(t),
+ *            level m+1 <- A_t sum_{l<=m} S^l, live levels above m+1 <- A_t S^l,
+ *            levels 1..m <- 0, level 0 <- beta k v^T, where A_t = alpha
+ *            (I - beta k k^T), alpha = exp(log_alpha).  At t = 0 every level
+ *            is cleared before level 0 is written.  Levels above m+1 that are
+ *            dead at t are neither read nor written.
+ *   q, k   : [N, H, dk], v : [N, H, dv]  (dtype LL_BF16 or LL_F32)
+ *   log_alpha, beta : [N, H] fp32;  lambda : [N, H, L] fp32
+ *   t      : [N] int32 DEVICE array, position of the incoming token
+ *   out    : [N, H, dv] fp32, o = sum_l lambda[l] q^T S_t^l
+ * Valid t: 0 <= t < 2^(L-1); other t give NaN output rows and leave that
+ * sequence's states unchanged.  Sizes: dk in {64, 128}, dv a multiple of 4 in
+ * [4, 1024] (else LL_ERR_UNSUPPORTED / LL_ERR_SHAPE); 1 <= L <= 31.
+ */
+int loglinear_gdn_decode_step(const loglinear_states* states, const void* q, const void* k,
+                              const void* v, const float* log_alpha, const float* beta,
+                              const float* lambda, const int* t, float* out, int dtype, void* stream);
+
 /* Workspace bytes of loglinear_gdn_fwd for these sizes; (size_t)-1 if the
  * sizes are invalid or unsupported. */
 size_t loglinear_gdn_workspace_size(int B, int H, int T, int dk, int dv);

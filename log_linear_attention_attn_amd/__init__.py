@@ -13,6 +13,7 @@ Entry points (same names as the C ABI in include/loglinear.h):
     fwd_workspace_size(B, H, T, dk, dv, C, seg_log2=-1)
     gdn_fwd(q, k, v, log_alpha, beta, lam, out=None, workspace=None)   log-linear Gated DeltaNet
     gdn_workspace_size(B, H, T, dk, dv)
+    gdn_decode_step(states, q, k, v, log_alpha, beta, lam, t, out=None)   its decode step
     decode_step(states, q, k, v, log_a, lam, t, out=None)
     level_table(T, device=None)                          int8 [T, T]
     num_levels(T)
@@ -27,6 +28,7 @@ import torch
 __all__ = [
     "LogLinearError", "lib", "library_path", "num_levels", "fwd", "fwd_ex", "prefill", "bwd",
     "fwd_workspace_size", "decode_step", "level_table", "strerror", "gdn_fwd", "gdn_workspace_size",
+    "gdn_decode_step",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_decode_step_ex",
     "loglinear_level_table", "loglinear_lambda_proj", "loglinear_lambda_proj_bwd",
     "loglinear_strerror", "loglinear_fwd_noalloc", "loglinear_gdn_fwd", "loglinear_gdn_workspace_size",
+    "loglinear_gdn_decode_step",
 )
 
 # bytes of the static scratch behind loglinear_fwd_noalloc (the header's
@@ -122,6 +125,8 @@ def lib():
     L.loglinear_gdn_fwd.argtypes = [vp] * 7 + [i] * 6 + [vp, sz, vp]
     L.loglinear_gdn_fwd.restype = i
     L.loglinear_gdn_workspace_size.argtypes = [i] * 5
+    L.loglinear_gdn_decode_step.argtypes = [ctypes.POINTER(_States)] + [vp] * 8 + [i, vp]
+    L.loglinear_gdn_decode_step.restype = i
     L.loglinear_gdn_workspace_size.restype = sz
     L.loglinear_strerror.argtypes = [i]
     L.loglinear_strerror.restype = ctypes.c_char_p
@@ -517,4 +522,36 @@ def gdn_fwd(q, k, v, log_alpha, beta, lam, out=None, workspace=None):
                                  LL_BF16 if q.dtype == torch.bfloat16 else LL_F32,
                                  _ptr(workspace), nbytes, _stream(dev))
     _raise(st, "loglinear_gdn_fwd")
+    return out
+
+
+def gdn_decode_step(states, q, k, v, log_alpha, beta, lam, t, out=None):
+    """One log-linear Gated DeltaNet decode step (loglinear_gdn_decode_step);
+    updates ``states`` [N, H, L, dk, dv] fp32 in place.
+
+    q, k: [N, H, dk]; v: [N, H, dv] (bf16 or fp32); log_alpha, beta: [N, H]
+    fp32; lam: [N, H, L] fp32; t: [N] int32.  Returns out [N, H, dv] fp32.
+    """
+    dev = states.device
+    if dev.type != "cuda":
+        raise ValueError("states must be on a GPU device")
+    N, H, L, dk, dv = states.shape
+    _check_dev("states", states, torch.float32, (N, H, L, dk, dv), dev)
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    _check_dev("q", q, q.dtype, (N, H, dk), dev)
+    _check_dev("k", k, q.dtype, (N, H, dk), dev)
+    _check_dev("v", v, q.dtype, (N, H, dv), dev)
+    _check_dev("log_alpha", log_alpha, torch.float32, (N, H), dev)
+    _check_dev("beta", beta, torch.float32, (N, H), dev)
+    _check_dev("lam", lam, torch.float32, (N, H, L), dev)
+    _check_dev("t", t, torch.int32, (N,), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.float32, (N, H, dv), dev)
+    desc = _States(states.data_ptr(), N, H, L, dk, dv)
+    st = lib().loglinear_gdn_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                         _ptr(beta), _ptr(lam), _ptr(t), _ptr(out),
+                                         LL_BF16 if q.dtype == torch.bfloat16 else LL_F32, _stream(dev))
+    _raise(st, "loglinear_gdn_decode_step")
     return out

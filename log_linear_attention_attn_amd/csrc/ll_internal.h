@@ -251,6 +251,20 @@ struct GdnArgs {
 size_t gdn_workspace_bytes(long long BH, int N, int dk);
 int gdn_sweep_lds_bytes(int nslot, int dk);
 int launch_gdn(int dtype, const GdnArgs& a, hipStream_t s);
+// Log-linear Gated DeltaNet decode step (states updated in place).
+struct GdnDecArgs {
+  float* S;               // [N][H][L][dk][dv]
+  const void* q;          // [N][H][dk]
+  const void* k;          // [N][H][dk]
+  const void* v;          // [N][H][dv]
+  const float* log_alpha; // [N][H]
+  const float* beta;      // [N][H]
+  const float* lam;       // [N][H][L]
+  const int* t;           // [N]
+  float* out;             // [N][H][dv]
+  int N, H, L, dk, dv;
+};
+int launch_gdn_decode(int dtype, const GdnDecArgs& a, hipStream_t s);
 int launch_handoff_intra(int dtype, const HandoffArgs& a, hipStream_t s);
 int launch_decode(int dtype, const DecArgs& a, hipStream_t s);
 int bwd_lds_bytes(int dtype, int C, int dk, int dv, int L, int N, int nslot);

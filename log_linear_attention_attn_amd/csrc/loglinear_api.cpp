@@ -289,6 +289,24 @@ int run_decode(int dtype, const loglinear_states* s, const void* q, const void* 
   return ll::launch_decode(dtype, a, stream);
 }
 
+int run_gdn_decode(int dtype, const loglinear_states* s, const void* q, const void* k, const void* v,
+                   const float* log_alpha, const float* beta, const float* lambda, const int* t,
+                   float* out, hipStream_t stream) {
+  if (!s) return LL_ERR_NULL;
+  if (s->N < 0 || s->H < 0) return LL_ERR_SHAPE;
+  if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
+  if (s->L < 1 || s->L > 31) return LL_ERR_SHAPE;
+  if (s->dk < 4 || s->dk % 4 != 0 || s->dv < 4 || s->dv % 4 != 0) return LL_ERR_SHAPE;
+  if ((s->dk != 64 && s->dk != 128) || s->dv > 1024) return LL_ERR_UNSUPPORTED;
+  if ((long long)s->N * s->H > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
+  if (s->N == 0 || s->H == 0) return LL_OK;
+  if (!s->data || !q || !k || !v || !log_alpha || !beta || !lambda || !t || !out) return LL_ERR_NULL;
+  // states and out move as 16-byte vectors; q, k, v are read one element at a time
+  if (!aligned16({s->data, out})) return LL_ERR_SHAPE;
+  ll::GdnDecArgs a{s->data, q, k, v, log_alpha, beta, lambda, t, out, s->N, s->H, s->L, s->dk, s->dv};
+  return ll::launch_gdn_decode(dtype, a, stream);
+}
+
 int run_lambda_proj(int dtype, const void* x, const void* W, const float* bias, float* lam, int B, int T,
                     int D, int H, int L, hipStream_t stream) {
   if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
@@ -666,6 +684,13 @@ int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const float* 
                       int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return run_gdn(dtype, q, k, v, log_alpha, beta, lambda, out, B, H, T, dk, dv, workspace,
                  workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_gdn_decode_step(const loglinear_states* states, const void* q, const void* k,
+                              const void* v, const float* log_alpha, const float* beta,
+                              const float* lambda, const int* t, float* out, int dtype, void* stream) {
+  return run_gdn_decode(dtype, states, q, k, v, log_alpha, beta, lambda, t, out,
+                        static_cast<hipStream_t>(stream));
 }
 
 size_t loglinear_gdn_workspace_size(int B, int H, int T, int dk, int dv) {

@@ -526,6 +526,165 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode step.  Per (sequence, head) with m = lssb(t): level m+1 takes the sum
+// of levels 0..m, every level then passes through A_t = alpha (I - beta k k^T),
+// levels 1..m are emptied and level 0 receives beta k v^T; the output is
+// sum_l lambda_l q^T S_t^l.  A_t needs k^T S of each level (a reduction over
+// dk) before the level can be written, and q^T A_t S = alpha (q^T S - beta
+// (q . k) k^T S) comes out of the same reduction, so each level is read once
+// and written once.  One workgroup per (sequence*head, 64 value columns):
+// 16 column lanes of float4 x 16 row groups (256-byte row segments); the
+// levels are walked one after another, the next one's rows loaded while the
+// current one is reduced (16 lanes of a row group in a wave, then the four
+// waves through LDS).
+// ---------------------------------------------------------------------------
+template <typename IT, int RPT>
+__global__ __launch_bounds__(256) void gdn_decode_kernel(GdnDecArgs a) {
+  __shared__ f32x4 red[2][4][16][2];
+  __shared__ float qkred[4];
+  const int nh = blockIdx.x, seq = nh / a.H;
+  const int tid = threadIdx.x, c = tid & 15, rg = tid >> 4, wv = tid >> 6;
+  const int col = blockIdx.y * 64 + 4 * c;
+  const bool colok = col < a.dv;  // dv is a multiple of 4
+  const int L = a.L, dk = a.dk, dv = a.dv;
+  const int t = a.t[seq];
+  float* outp = a.out + size_t(nh) * dv + col;
+  if (t < 0 || t >= (1 << (L - 1))) {
+    if (rg == 0 && colok) {
+      const float nan = __builtin_nanf("");
+      *reinterpret_cast<f32x4*>(outp) = f32x4{nan, nan, nan, nan};
+    }
+    return;
+  }
+  const float al = __expf(a.log_alpha[nh]), be = a.beta[nh];
+  const float* lam = a.lam + size_t(nh) * L;
+  const IT* q = static_cast<const IT*>(a.q) + size_t(nh) * dk;
+  const IT* k = static_cast<const IT*>(a.k) + size_t(nh) * dk;
+  const IT* v = static_cast<const IT*>(a.v) + size_t(nh) * dv;
+  float* S = a.S + size_t(nh) * L * dk * dv + col;
+  const size_t lvl = size_t(dk) * dv;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+  // this thread's rows rg + 16 i
+  float kr[RPT], qr[RPT];
+  float qk = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    kr[i] = load1<IT>(k + rg + 16 * i);
+    qr[i] = load1<IT>(q + rg + 16 * i);
+    qk += qr[i] * kr[i];
+  }
+  f32x4 vv = z4;
+  if (colok) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv[j] = load1<IT>(v + col + j);
+  }
+  // q . k over the 16 row groups: the four in a wave, then the four waves
+  qk += __shfl_xor(qk, 16);
+  qk += __shfl_xor(qk, 32);
+  if ((tid & 63) == 0) qkred[wv] = qk;
+  __syncthreads();
+  qk = (qkred[0] + qkred[1]) + (qkred[2] + qkred[3]);
+
+  auto row = [&](int level, int i) { return S + level * lvl + size_t(rg + 16 * i) * dv; };
+  // level 0's new state beta k v^T
+  f32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = lam[0] * be * qk * vv[j];
+
+  if (t > 0) {
+    const int m = lssb(static_cast<uint32_t>(t));
+    // the merged bucket: levels 0..m, all live at t - 1
+    f32x4 x[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) x[i] = z4;
+    if (colok)
+      for (int l = 0; l <= m; ++l)
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const f32x4 y = *reinterpret_cast<const f32x4*>(row(l, i));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[i][j] += y[j];
+        }
+    // then the live levels above m + 1: level b + 1 for each set bit b > m of t
+    unsigned rest = static_cast<unsigned>(t) >> (m + 1);
+    int cur = m + 1, buf = 0;
+    while (true) {
+      int next = -1;
+      if (rest) {
+        next = m + 1 + __ffs(rest);
+        rest &= rest - 1;
+      }
+      f32x4 y[RPT];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) y[i] = (colok && next >= 0) ? *reinterpret_cast<const f32x4*>(row(max(next, 0), i)) : z4;
+      f32x4 ks = z4, qs = z4;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ks[j] += kr[i] * x[i][j];
+          qs[j] += qr[i] * x[i][j];
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ks[j] += __shfl_xor(ks[j], 16);
+        ks[j] += __shfl_xor(ks[j], 32);
+        qs[j] += __shfl_xor(qs[j], 16);
+        qs[j] += __shfl_xor(qs[j], 32);
+      }
+      if ((rg & 3) == 0) {
+        red[buf][wv][c][0] = ks;
+        red[buf][wv][c][1] = qs;
+      }
+      __syncthreads();
+      f32x4 u = z4, sq = z4;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const f32x4 a0 = red[buf][w2][c][0], a1 = red[buf][w2][c][1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u[j] += a0[j];
+          sq[j] += a1[j];
+        }
+      }
+      // S <- alpha (S - beta k u^T); q^T S_t = alpha (q^T S - beta (q . k) u)
+      if (colok)
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          f32x4 xn;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xn[j] = al * (x[i][j] - be * kr[i] * u[j]);
+          *reinterpret_cast<f32x4*>(row(cur, i)) = xn;
+        }
+      const float lw = lam[cur];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] += lw * al * (sq[j] - be * qk * u[j]);
+      if (next < 0) break;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) x[i] = y[i];
+      cur = next;
+      buf ^= 1;
+    }
+  }
+  // levels 1..m emptied (at t = 0: every level above 0), level 0 = beta k v^T
+  if (colok) {
+    const int top = t > 0 ? lssb(static_cast<uint32_t>(t)) : L - 1;
+    for (int l = 1; l <= top; ++l)
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) *reinterpret_cast<f32x4*>(row(l, i)) = z4;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      f32x4 n0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) n0[j] = be * kr[i] * vv[j];
+      *reinterpret_cast<f32x4*>(row(0, i)) = n0;
+    }
+    if (rg == 0) *reinterpret_cast<f32x4*>(outp) = o;
+  }
+}
+
 template <typename IT, int DK>
 int launch_gdn_t(const GdnArgs& a, hipStream_t s) {
   constexpr int KT = DK / 16;
@@ -554,6 +713,24 @@ size_t gdn_workspace_bytes(long long BH, int N, int dk) {
 
 int gdn_sweep_lds_bytes(int nslot, int dk) {
   return (nslot * (dk / 16) * 64 + nslot * 4 * 64 + 4 * 64) * 16 + GC * nslot * 4;
+}
+
+int launch_gdn_decode(int dtype, const GdnDecArgs& a, hipStream_t s) {
+  const long long nh = (long long)a.N * a.H;
+  if (nh == 0) return LL_OK;
+  if (nh > 0x7fffffffLL) return LL_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(nh), static_cast<unsigned>((a.dv + 63) / 64));
+  const bool bf = dtype == LL_BF16;
+  if (a.dk == 128) {
+    if (bf) hipLaunchKernelGGL((gdn_decode_kernel<uint16_t, 8>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gdn_decode_kernel<float, 8>), grid, dim3(256), 0, s, a);
+  } else if (a.dk == 64) {
+    if (bf) hipLaunchKernelGGL((gdn_decode_kernel<uint16_t, 4>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gdn_decode_kernel<float, 4>), grid, dim3(256), 0, s, a);
+  } else {
+    return LL_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? LL_OK : LL_ERR_HIP;
 }
 
 int launch_gdn(int dtype, const GdnArgs& a, hipStream_t s) {

@@ -308,3 +308,25 @@ def test_gdn_argument_errors():
         want = ((n * 4 * (3 * dk + 128) * 64 + 255) // 256 + (n * 4 + 255) // 256) * 256
         assert L.loglinear_gdn_workspace_size(B, H, T, dk, 16) == want
     assert L.loglinear_gdn_workspace_size(1, 1, 64, 48, 16) == ctypes.c_size_t(-1).value
+
+
+def test_gdn_decode_argument_errors():
+    L = ll.lib()
+    p = ctypes.c_void_p(1 << 20)
+
+    def call(N=1, H=1, Lv=5, dk=64, dv=16, dtype=0, data=1 << 20, ptr=p):
+        st = ll._States(data, N, H, Lv, dk, dv)
+        return L.loglinear_gdn_decode_step(ctypes.byref(st), ptr, p, p, p, p, p, p, p, dtype, None)
+
+    assert L.loglinear_gdn_decode_step(None, p, p, p, p, p, p, p, p, 0, None) == LL_ERR_NULL
+    assert call(dk=32) == LL_ERR_UNSUPPORTED
+    assert call(dk=6) == LL_ERR_SHAPE
+    assert call(dv=2) == LL_ERR_SHAPE
+    assert call(dv=2048) == LL_ERR_UNSUPPORTED
+    assert call(Lv=0) == LL_ERR_SHAPE
+    assert call(Lv=32) == LL_ERR_SHAPE
+    assert call(N=-1) == LL_ERR_SHAPE
+    assert call(dtype=3) == LL_ERR_SHAPE
+    assert call(N=0, ptr=None) == LL_OK
+    assert call(ptr=None) == LL_ERR_NULL
+    assert call(data=(1 << 20) + 4) == LL_ERR_SHAPE

@@ -111,3 +111,60 @@ def test_gdn_long_sampled_rows(T, decay):
     rows = sorted(set(r for r in fixed if r < T) | set(np.random.default_rng(3).integers(0, T, 4).tolist()))
     want = G.loglinear_rows(*inp, (0, 0), rows)
     assert_parity(got[0, 0][rows], want, GDN_TOL, f"gdn T={T} rows")
+
+
+def _decode_case(w, t=None):
+    S, q, k, v, la, beta, lam, tt = W.make_gdn_decode_inputs(w, t)
+    dS = S.cuda()
+    o = ll.gdn_decode_step(dS, *to_dev(q, k, v, la, beta, lam, tt))
+    torch.cuda.synchronize()
+    want_o, want_S = G.decode_step(S, q, k, v, la, beta, lam, tt)
+    return o.cpu().numpy(), dS.cpu().numpy(), want_o, want_S, S.numpy()
+
+
+def test_gdn_decode_full_workload():
+    """64 sequences x 16 heads, dk = dv = 128, L = 17, random t: outputs and
+    every updated state against the oracle step; levels dead at t are 0."""
+    w = W.GDN_DECODE_64x16
+    announce("gdn decode 64x16")
+    o, S, want_o, want_S, _ = _decode_case(w)
+    assert_parity(o, want_o, GDN_TOL, "gdn decode out")
+    assert_parity(S, want_S, 1e-5, "gdn decode states")
+    assert np.array_equal(S == 0, want_S == 0)
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("f32", 64, 20), ("bf16", 128, 200)])
+def test_gdn_decode_special_positions(dtype, dk, dv):
+    """t = 0 (every level cleared), powers of two (one merged bucket), odd t,
+    the last valid position 2^(L-1) - 1, and out-of-range positions (NaN
+    output, states untouched); dv not a multiple of 64."""
+    Lv = 9
+    t = np.array([0, 1, 2, 64, 127, 128, 255, 256, 300, -1], dtype=np.int32)
+    w = W.DecodeWorkload("gdn_dec_special", len(t), 3, dk, dv, Lv, 255, dtype=dtype, seed=dk + dv)
+    announce(f"gdn decode special {dtype} {dk} {dv}")
+    o, S, want_o, want_S, S0 = _decode_case(w, t)
+    ok = (t >= 0) & (t < 256)
+    assert_parity(o[ok], want_o[ok], GDN_TOL, "gdn decode special out")
+    assert_parity(S[ok], want_S[ok], 1e-5, "gdn decode special states")
+    assert np.all(np.isnan(o[~ok]))
+    assert np.array_equal(S[~ok], S0[~ok])
+
+
+def test_gdn_decode_chain_matches_forward():
+    """Decode steps on the GPU from empty states over t = 0..T-1 give the GPU
+    forward's rows (two GPU kernels that share no code path)."""
+    B, H, T, dk, dv = 2, 2, 130, 64, 32
+    wf = W.GdnWorkload("gdn_chain", B, H, T, dk, dv, "f32", "weak", seed=9)
+    q, k, v, la, beta, lam = to_dev(*W.make_gdn_inputs(wf))
+    announce("gdn decode chain")
+    fwd = ll.gdn_fwd(q, k, v, la, beta, lam)
+    S = torch.zeros((B, H, lam.shape[-1], dk, dv), dtype=torch.float32, device="cuda")
+    outs = []
+    for t in range(T):
+        tt = torch.full((B,), t, dtype=torch.int32, device="cuda")
+        outs.append(ll.gdn_decode_step(S, q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                       v[:, :, t].contiguous(), la[:, :, t].contiguous(),
+                                       beta[:, :, t].contiguous(), lam[:, :, t].contiguous(), tt))
+    dec = torch.stack(outs, dim=2)
+    torch.cuda.synchronize()
+    assert_parity(dec.cpu().numpy(), fwd.cpu().numpy(), GDN_TOL, "gdn decode chain vs forward")
