@@ -15,7 +15,8 @@ each timed the same way:
   "decode"      one decode step of 64 sequences x 16 heads, L = 17;
   "lambda_proj" the level-weight projection at the same B, T, H, L with hidden
                 width 2048, and its gradient;
-  "gdn"         the log-linear Gated DeltaNet forward at the same B, H, T, dk, dv;
+  "gdn"         the log-linear Gated DeltaNet forward at the same B, H, T, dk, dv,
+                and its decode step at the decode step's shapes;
   "pages_context" the pages' own speed statements (context, not a target).
 The backward and the configs run before the headline forward is timed.
 --pass bwd / decode / lambda / gdn time only the backward, the decode step, the
@@ -140,6 +141,41 @@ def bench_decode(dev, steps: int, warmup: int):
         "t": "U{1..65535} per sequence, seed 0", "steps": steps, "ms_per_step": ms,
         "tokens_per_s": w.N / (ms * 1e-3), "algorithmic_bytes": nbytes,
         "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
+    }
+
+
+def bench_gdn_decode(dev, steps: int, warmup: int):
+    """One log-linear Gated DeltaNet decode step (loglinear_gdn_decode_step) for
+    64 sequences x 16 heads, dk = dv = 128, L = 17, t ~ U{1..65535}, timed like
+    bench_decode.  It moves the Mamba-2 step's bytes plus beta: each live level
+    is read once and written once."""
+    import torch
+    import log_linear_attention_attn_amd as ll
+    import workloads as W
+    w = W.GDN_DECODE_64x16
+    S, q, k, v, la, beta, lam, t = W.make_gdn_decode_inputs(w)
+    t_host = t.numpy().copy()
+    S, q, k, v, la, beta, lam, t = (x.to(dev) for x in (S, q, k, v, la, beta, lam, t))
+    out = torch.empty(w.N, w.H, w.dv, dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        ll.gdn_decode_step(S, q, k, v, la, beta, lam, t, out=out)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        ll.gdn_decode_step(S, q, k, v, la, beta, lam, t, out=out)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    nbytes = decode_bytes(t_host, w.H, w.L, w.dk, w.dv, 2 if w.dtype == "bf16" else 4) + w.N * w.H * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del S
+    return {
+        "workload": w.name, "N": w.N, "H": w.H, "dk": w.dk, "dv": w.dv, "L": w.L,
+        "t": f"U{{1..65535}} per sequence, seed {w.seed}", "steps": steps, "ms_per_step": ms,
+        "tokens_per_s": w.N / (ms * 1e-3), "algorithmic_bytes": nbytes,
+        "roofline": {"kernel": "gdn_decode_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
     }
 
@@ -576,7 +612,8 @@ def main():
             "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": rec["config"],
             "roofline": rec["roofline"], "tflops": rec["tflops"],
-            "algorithmic_flops": rec["algorithmic_flops"]}))
+            "algorithmic_flops": rec["algorithmic_flops"],
+            "decode": bench_gdn_decode(dev, args.steps, args.warmup)}))
         return
     if args.which == "decode":
         rec = bench_decode(dev, args.steps, args.warmup)
@@ -631,6 +668,7 @@ def main():
         rec["decode"] = bench_decode(dev, K, Wm)
         rec["lambda_proj"] = bench_lambda(dev, K, Wm)
         rec["gdn"] = gdn_record(dev, max(3, K // 4), 3)
+        rec["gdn"]["decode"] = bench_gdn_decode(dev, K, Wm)
         # the same shapes with log_a = 0 (no decay), timed last so its launches
         # do not sit among the headline's in a trace: the instruction stream is
         # the same, only the data (and with it the power draw) differs
