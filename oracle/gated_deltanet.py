@@ -201,3 +201,33 @@ def decode_step(states, q, k, v, log_alpha, beta, lam, t):
             lev[0] = bt * np.outer(kk, v[i, h])
             out[i, h] = np.einsum("l,d,lde->e", lam[i, h], q[i, h], lev)
     return out, S
+
+
+def states_after(k, v, log_alpha, beta, t: int, L: int) -> np.ndarray:
+    """Per-level decode states after the tokens 0..t, for every (b, h).
+
+    By definition the level-l state is the sum over the level-l Fenwick bucket
+    of t of Phi(t,s) beta_s k_s v_s^T (k-major, dk x dv); levels with no
+    bucket at t are 0.  These are the states a decode step at t+1 starts
+    from.  Evaluated by the per-level recurrence of ``loglinear_recurrent``
+    (lssb merges, the transition on every level).
+    k: [B, H, T, dk], v: [B, H, T, dv], log_alpha, beta: [B, H, T], T > t.
+    Returns [B, H, L, dk, dv] fp64.
+    """
+    k, v, log_alpha, beta = (_f64(x) for x in (k, v, log_alpha, beta))
+    B, H, _, dk = k.shape
+    dv = v.shape[-1]
+    out = np.zeros((B, H, L, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((L, dk, dv))
+            for s in range(t + 1):
+                ks, bs = k[b, h, s], beta[b, h, s]
+                if s > 0:
+                    m = lssb(s)
+                    S[m + 1] = S[: m + 1].sum(axis=0)
+                    S[: m + 1] = 0.0
+                    S = np.exp(log_alpha[b, h, s]) * (S - bs * np.einsum("d,le->lde", ks, np.einsum("d,lde->le", ks, S)))
+                S[0] = bs * np.outer(ks, v[b, h, s])
+            out[b, h] = S
+    return out

@@ -165,3 +165,29 @@ def test_decode_out_of_range_position():
     o, S2 = G.decode_step(S, q, k, v, la, beta, lam, np.array([8, 3]))
     assert np.all(np.isnan(o[0])) and np.array_equal(S2[0], S[0])
     assert np.all(np.isfinite(o[1]))
+
+
+def test_states_after_brute_force():
+    """The level states after t equal the bucket sums of Phi(t,s) beta_s k_s v_s^T
+    built from explicit transition matrices over the Fenwick buckets of t
+    ([P1] 前缀的层次化分解), and a decode step from them gives row t+1 of
+    the dense definition."""
+    rng = np.random.default_rng(9)
+    T, dk, dv = 14, 3, 2
+    q, k, v, la, beta, lam = _inputs(rng, 1, 1, T, dk, dv)
+    L = lam.shape[-1]
+    A = [np.exp(la[0, 0, r]) * (np.eye(dk) - beta[0, 0, r] * np.outer(k[0, 0, r], k[0, 0, r])) for r in range(T)]
+    dense = G.loglinear_forward(q, k, v, la, beta, lam)
+    for t in (0, 5, 7, 12):
+        got = G.states_after(k, v, la, beta, t, L)[0, 0]
+        want = np.zeros_like(got)
+        for level, lo, hi in oracle.fenwick_buckets(t):
+            for s in range(lo, hi):
+                phi = np.eye(dk)
+                for r in range(s + 1, t + 1):
+                    phi = A[r] @ phi
+                want[level] += beta[0, 0, s] * np.outer(phi @ k[0, 0, s], v[0, 0, s])
+        np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13)
+        o, _ = G.decode_step(got[None, None], q[:, :, t + 1], k[:, :, t + 1], v[:, :, t + 1], la[:, :, t + 1],
+                             beta[:, :, t + 1], lam[:, :, t + 1], np.array([t + 1]))
+        np.testing.assert_allclose(o[0, 0], dense[0, 0, t + 1], rtol=1e-10, atol=1e-12)
