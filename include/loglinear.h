@@ -392,6 +392,23 @@ int loglinear_gdn_decode_step(const loglinear_states* states, const void* q, con
                               const void* v, const float* log_alpha, const float* beta,
                               const float* lambda, const int* t, float* out, int dtype, void* stream);
 
+/*
+ * loglinear_gdn_fwd plus the decode states at position T-1 (prefill ->
+ * decode hand-off, page above, section 解码：基于 lssb 的状态更新):
+ *   states   : [B, H, states_L, dk, dv] fp32 DEVICE, 16-byte aligned, written
+ *              completely: level l holds sum over the level-l Fenwick bucket of
+ *              T-1 of A_{T-1}...A_{s+1} beta_s k_s v_s^T (k-major); levels with
+ *              no bucket at T-1 hold 0.  These are exactly the states a
+ *              loglinear_gdn_decode_step at t = T continues from.
+ *   states_L : levels of the states tensor, L <= states_L <= 31 (else
+ *              LL_ERR_SHAPE); NULL states with non-empty sizes: LL_ERR_NULL.
+ * Other arguments, sizes and errors as loglinear_gdn_fwd.
+ */
+int loglinear_gdn_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const float* lambda, float* out, float* states,
+                          int states_L, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Workspace bytes of loglinear_gdn_fwd for these sizes; (size_t)-1 if the
  * sizes are invalid or unsupported. */
 size_t loglinear_gdn_workspace_size(int B, int H, int T, int dk, int dv);

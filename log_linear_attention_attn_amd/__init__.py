@@ -14,6 +14,7 @@ Entry points (same names as the C ABI in include/loglinear.h):
     gdn_fwd(q, k, v, log_alpha, beta, lam, out=None, workspace=None)   log-linear Gated DeltaNet
     gdn_workspace_size(B, H, T, dk, dv)
     gdn_decode_step(states, q, k, v, log_alpha, beta, lam, t, out=None)   its decode step
+    gdn_prefill(q, k, v, log_alpha, beta, lam, L=None, workspace=None)     forward + states at T-1
     decode_step(states, q, k, v, log_a, lam, t, out=None)
     level_table(T, device=None)                          int8 [T, T]
     num_levels(T)
@@ -28,7 +29,7 @@ import torch
 __all__ = [
     "LogLinearError", "lib", "library_path", "num_levels", "fwd", "fwd_ex", "prefill", "bwd",
     "fwd_workspace_size", "decode_step", "level_table", "strerror", "gdn_fwd", "gdn_workspace_size",
-    "gdn_decode_step",
+    "gdn_decode_step", "gdn_prefill",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "loglinear_decode_step", "loglinear_decode_step_f32", "loglinear_decode_step_ex",
     "loglinear_level_table", "loglinear_lambda_proj", "loglinear_lambda_proj_bwd",
     "loglinear_strerror", "loglinear_fwd_noalloc", "loglinear_gdn_fwd", "loglinear_gdn_workspace_size",
-    "loglinear_gdn_decode_step",
+    "loglinear_gdn_decode_step", "loglinear_gdn_prefill",
 )
 
 # bytes of the static scratch behind loglinear_fwd_noalloc (the header's
@@ -127,6 +128,8 @@ def lib():
     L.loglinear_gdn_workspace_size.argtypes = [i] * 5
     L.loglinear_gdn_decode_step.argtypes = [ctypes.POINTER(_States)] + [vp] * 8 + [i, vp]
     L.loglinear_gdn_decode_step.restype = i
+    L.loglinear_gdn_prefill.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
+    L.loglinear_gdn_prefill.restype = i
     L.loglinear_gdn_workspace_size.restype = sz
     L.loglinear_strerror.argtypes = [i]
     L.loglinear_strerror.restype = ctypes.c_char_p
@@ -499,6 +502,25 @@ def gdn_fwd(q, k, v, log_alpha, beta, lam, out=None, workspace=None):
     workspace: None (the library allocates) or a uint8 device tensor of at
     least gdn_workspace_size(...) bytes.  Returns out [B, H, T, dv] fp32.
     """
+    out = _gdn_check(q, k, v, log_alpha, beta, lam, out)
+    return _gdn_call(q, k, v, log_alpha, beta, lam, out, workspace, None)
+
+
+def gdn_prefill(q, k, v, log_alpha, beta, lam, L=None, workspace=None, out=None):
+    """loglinear_gdn_prefill: the Gated DeltaNet forward plus the decode
+    states at T-1, [B, H, L, dk, dv] fp32 with L = num_levels(T) unless given
+    (more levels are written as 0).  Returns (out, states)."""
+    out = _gdn_check(q, k, v, log_alpha, beta, lam, out)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    Ls = int(L) if L is not None else num_levels(T)
+    states = torch.empty((B, H, Ls, dk, dv), dtype=torch.float32, device=q.device)
+    _gdn_call(q, k, v, log_alpha, beta, lam, out, workspace, states)
+    return out, states
+
+
+def _gdn_check(q, k, v, log_alpha, beta, lam, out):
+    """Metadata checks of the Gated DeltaNet calls; returns out (allocated unless given)."""
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q, k, v must be bfloat16 or float32")
     dev = q.device
@@ -516,7 +538,21 @@ def gdn_fwd(q, k, v, log_alpha, beta, lam, out=None, workspace=None):
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
     _check_dev("out", out, torch.float32, (B, H, T, dv), dev)
+    return out
+
+
+def _gdn_call(q, k, v, log_alpha, beta, lam, out, workspace, states):
+    dev = q.device
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    dtype = LL_BF16 if q.dtype == torch.bfloat16 else LL_F32
+    if states is not None:
+        st = lib().loglinear_gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(lam),
+                                         _ptr(out), _ptr(states), states.shape[2], B, H, T, dk, dv, dtype,
+                                         _ptr(workspace), nbytes, _stream(dev))
+        _raise(st, "loglinear_gdn_prefill")
+        return out
     st = lib().loglinear_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(lam),
                                  _ptr(out), B, H, T, dk, dv,
                                  LL_BF16 if q.dtype == torch.bfloat16 else LL_F32,

@@ -247,6 +247,9 @@ struct GdnArgs {
   float* gchunk;          // [BH][N] decay of each whole chunk
   int BH, T, dk, dv, L, N;
   int nslot;              // chunk-level Fenwick bits = bit_length(N - 1)
+  // decode states at position T-1 (prefill), or null: [BH][st_L][dk][dv] fp32
+  float* st_out = nullptr;
+  int st_L = 0;
 };
 size_t gdn_workspace_bytes(long long BH, int N, int dk);
 int gdn_sweep_lds_bytes(int nslot, int dk);

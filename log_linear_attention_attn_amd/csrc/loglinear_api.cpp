@@ -534,15 +534,18 @@ int gdn_plan(int B, int H, int T, int dk, int dv, int* N, int* nslot, size_t* ws
 
 int run_gdn(int dtype, const void* q, const void* k, const void* v, const float* log_alpha,
             const float* beta, const float* lambda, float* out, int B, int H, int T, int dk, int dv,
-            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+            void* workspace, size_t workspace_bytes, hipStream_t stream, float* st_out = nullptr,
+            int st_L = 0) {
   int N = 0, nslot = 0;
   size_t need = 0;
   if (dtype != LL_BF16 && dtype != LL_F32) return LL_ERR_SHAPE;
   int st = gdn_plan(B, H, T, dk, dv, &N, &nslot, &need);
   if (st != LL_OK) return st;
+  const int L = T > 0 ? bit_length(T - 1) + 1 : 0;
+  if (st_out && (st_L < std::max(L, 1) || st_L > 31)) return LL_ERR_SHAPE;
   if (B == 0 || H == 0 || T == 0) return LL_OK;
   if (!q || !k || !v || !log_alpha || !beta || !lambda || !out) return LL_ERR_NULL;
-  if (!aligned16({q, k, v, lambda, out})) return LL_ERR_SHAPE;
+  if (!aligned16({q, k, v, lambda, out, st_out})) return LL_ERR_SHAPE;
   if (workspace && workspace_bytes < need) return LL_ERR_WORKSPACE;
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255)) return LL_ERR_WORKSPACE;
   void* ws = workspace;
@@ -555,7 +558,9 @@ int run_gdn(int dtype, const void* q, const void* k, const void* v, const float*
   const size_t rec_bytes = need - align256(size_t(BH) * N * 4);
   ll::GdnArgs a{q, k, v, log_alpha, beta, lambda, out, static_cast<float*>(ws),
                 reinterpret_cast<float*>(static_cast<char*>(ws) + rec_bytes),
-                static_cast<int>(BH), T, dk, dv, bit_length(T - 1) + 1, N, nslot};
+                static_cast<int>(BH), T, dk, dv, L, N, nslot};
+  a.st_out = st_out;
+  a.st_L = st_L;
   st = ll::launch_gdn(dtype, a, stream);
   if (owned && hipFreeAsync(ws, stream) != hipSuccess && st == LL_OK) st = LL_ERR_HIP;
   return st;
@@ -684,6 +689,15 @@ int loglinear_gdn_fwd(const void* q, const void* k, const void* v, const float* 
                       int dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return run_gdn(dtype, q, k, v, log_alpha, beta, lambda, out, B, H, T, dk, dv, workspace,
                  workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int loglinear_gdn_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const float* lambda, float* out, float* states,
+                          int states_L, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!states && B > 0 && H > 0 && T > 0) return LL_ERR_NULL;
+  return run_gdn(dtype, q, k, v, log_alpha, beta, lambda, out, B, H, T, dk, dv, workspace,
+                 workspace_bytes, static_cast<hipStream_t>(stream), states, states ? states_L : 0);
 }
 
 int loglinear_gdn_decode_step(const loglinear_states* states, const void* q, const void* k,

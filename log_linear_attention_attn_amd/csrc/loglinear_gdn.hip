@@ -524,6 +524,85 @@ __global__ __launch_bounds__(GTHR) void gdn_sweep_kernel(GdnArgs a) {
       cur = nxt;
     }
   }
+
+  // Prefill: the decode states at T - 1 ([BH][st_L][dk][dv], this slice's 16
+  // columns, dk tiles of wave w).  The bucket states of the last chunk's
+  // prefix are carried through that chunk (positions past T have beta = 0
+  // and alpha = 1, so the chunk's transition is the one up to T - 1); a bucket
+  // [lo, hi) inside the chunk holds sum_s Phi(T-1, s) beta_s k_s v_s^T =
+  // K^T Tb (V restricted to rows lo..hi-1), by linearity in V.  Levels with
+  // no bucket at T - 1 are written as 0.
+  if (a.st_out) {
+    const int n = a.N - 1, p = a.T - 1 - n * GC;
+    const float gC = a.gchunk[size_t(bh) * a.N + n];
+    auto put = [&](int level, int dt, const f32x4& x) {
+      float* dst = a.st_out + ((size_t(bh) * a.st_L + level) * DK + 16 * dt + 4 * g4) * a.dv + n0 + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[size_t(r) * a.dv] = x[r];
+    };
+    for (int b = 0; b < NB; ++b) {
+      if (!((n >> b) & 1)) continue;
+#pragma unroll
+      for (int dtl = 0; dtl < KTW; ++dtl) {
+        const int dt = w * KTW + dtl;
+        f32x4 ky = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const f32x4 yy = yb[(b * 4 + ct) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ky = mma4(cur.kh[dtl][ct][r], yy[r], ky);
+        }
+        const f32x4 sv = st[(b * KT + dt) * 64 + lane];
+        f32x4 ns;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ns[r] = gC * sv[r] - ky[r];
+        put(GLOGC + 1 + b, dt, ns);
+      }
+    }
+    // in-chunk buckets of p: level 0 is {p}; set bit j of p (lowest first)
+    // cuts [e - 2^j, e) at level j + 1, with e starting at p
+    int e = p;
+    for (int lev = 0; lev <= GLOGC; ++lev) {
+      int lo = p, hi = p + 1;
+      if (lev > 0) {
+        if (!((p >> (lev - 1)) & 1)) continue;
+        hi = e;
+        lo = e - (1 << (lev - 1));
+        e = lo;
+      }
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (ct <= w) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * ct + 4 * g4 + r;
+            u = mma4(cur.tb[ct][r], (row >= lo && row < hi) ? cur.vb[ct][r] : 0.f, u);
+          }
+        }
+      __syncthreads();  // the previous level's reads of ub are done
+      ub[w * 64 + lane] = u;
+      __syncthreads();
+#pragma unroll
+      for (int dtl = 0; dtl < KTW; ++dtl) {
+        f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const f32x4 uu = ub[ct * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sv = mma4(cur.kh[dtl][ct][r], uu[r], sv);
+        }
+        put(lev, w * KTW + dtl, sv);
+      }
+    }
+    for (int lev = 0; lev < a.st_L; ++lev) {
+      const bool live = lev == 0 || (lev <= GLOGC && ((p >> (lev - 1)) & 1)) ||
+                        (lev > GLOGC && lev - GLOGC - 1 < 31 && ((n >> (lev - GLOGC - 1)) & 1));
+      if (live) continue;
+#pragma unroll
+      for (int dtl = 0; dtl < KTW; ++dtl) put(lev, w * KTW + dtl, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -330,3 +330,17 @@ def test_gdn_decode_argument_errors():
     assert call(N=0, ptr=None) == LL_OK
     assert call(ptr=None) == LL_ERR_NULL
     assert call(data=(1 << 20) + 4) == LL_ERR_SHAPE
+
+
+def test_gdn_prefill_argument_errors():
+    L = ll.lib()
+    p = ctypes.c_void_p(1 << 20)
+
+    def call(states=p, Ls=7, T=64, B=1):
+        return L.loglinear_gdn_prefill(p, p, p, p, p, p, p, states, Ls, B, 1, T, 64, 16, 0, None, 0, None)
+
+    assert call(states=None) == LL_ERR_NULL
+    assert call(Ls=6) == LL_ERR_SHAPE              # T = 64 has L = 7 levels
+    assert call(Ls=32) == LL_ERR_SHAPE
+    assert call(states=ctypes.c_void_p((1 << 20) + 4)) == LL_ERR_SHAPE
+    assert call(states=None, B=0) == LL_OK

@@ -168,3 +168,42 @@ def test_gdn_decode_chain_matches_forward():
     dec = torch.stack(outs, dim=2)
     torch.cuda.synchronize()
     assert_parity(dec.cpu().numpy(), fwd.cpu().numpy(), GDN_TOL, "gdn decode chain vs forward")
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200, 4200, 8192])
+def test_gdn_prefill_states(T):
+    """The prefill's decode states at T-1 against the oracle's level states
+    (one ragged or full last chunk, in-chunk buckets of every size, chunk-level
+    buckets up to bit 6), with two extra levels that must be 0."""
+    w = W.GdnWorkload("gdn_prefill", 1, 2, T, 128 if T > 100 else 64, 32, "f32", "weak", seed=T)
+    inp = W.make_gdn_inputs(w)
+    announce(f"gdn prefill T={T}")
+    out, st = ll.gdn_prefill(*to_dev(*inp), L=w.L + 2)
+    torch.cuda.synchronize()
+    want = G.states_after(inp[1], inp[2], inp[3], inp[4], T - 1, w.L + 2)
+    assert_parity(st.cpu().numpy(), want, GDN_TOL, f"gdn prefill states T={T}")
+    assert not st[:, :, w.L:].any()
+    assert torch.equal(out, ll.gdn_fwd(*to_dev(*inp)))
+
+
+def test_gdn_prefill_then_decode_matches_forward():
+    """Prefill over the first 300 tokens, then decode steps 300..339 from its
+    states: the rows equal the GPU forward over all 340 tokens."""
+    B, H, T0, T, dk, dv = 2, 2, 300, 340, 128, 64
+    wf = W.GdnWorkload("gdn_handoff", B, H, T, dk, dv, "bf16", "none", seed=13)
+    q, k, v, la, beta, lam = to_dev(*W.make_gdn_inputs(wf))
+    announce("gdn prefill then decode")
+    full = ll.gdn_fwd(q, k, v, la, beta, lam)
+    L = lam.shape[-1]
+    _, S = ll.gdn_prefill(q[:, :, :T0].contiguous(), k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(),
+                          la[:, :, :T0].contiguous(), beta[:, :, :T0].contiguous(),
+                          lam[:, :, :T0, :W.num_levels(T0)].contiguous(), L=L)
+    rows = []
+    for t in range(T0, T):
+        tt = torch.full((B,), t, dtype=torch.int32, device="cuda")
+        rows.append(ll.gdn_decode_step(S, q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                       v[:, :, t].contiguous(), la[:, :, t].contiguous(),
+                                       beta[:, :, t].contiguous(), lam[:, :, t].contiguous(), tt))
+    dec = torch.stack(rows, dim=2)
+    torch.cuda.synchronize()
+    assert_parity(dec.cpu().numpy(), full[:, :, T0:].cpu().numpy(), GDN_TOL, "gdn prefill -> decode")
