@@ -218,14 +218,22 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
       qpre[ktl][rt] = load4<IT>(q + min(16 * rt + l16, nrow - 1) * DK + 16 * (w * KTW + ktl) + 4 * g4);
+  // (in phases 3 and 4 step r of 16-block cb reduces over c = 16 cb + 4 (l/16) + r,
+  // so the operand read along c is one 16-byte LDS read per four products)
 #pragma unroll
   for (int ktl = 0; ktl < KTW; ++ktl) {
     const int kt = w * KTW + ktl;
+#pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < 16 * rt + 16; c0 += 4) {
-        const int c = c0 + g4;
-        acc = mma4(Ks[c * LDK + 16 * kt + l16] * gam[c], Tb[(16 * rt + l16) * LDM + c], acc);
+#pragma unroll
+      for (int cb = 0; cb <= rt; ++cb) {
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(Tb + (16 * rt + l16) * LDM + 16 * cb + 4 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * cb + 4 * g4 + r;
+          acc = mma4(Ks[c * LDK + 16 * kt + l16] * gam[c], bt[r], acc);
+        }
       }
       *reinterpret_cast<f32x4*>(rec + gdn_off_wt(KT) + ((rt * KT + kt) * 64 + lane) * 4) = acc;
     }
@@ -244,9 +252,15 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
     for (int ct = 0; ct < 4; ++ct) {
       ce[ct] = z4;
       if (ct <= rt)
-        for (int c0 = 16 * ct; c0 < 16 * rt + 16; c0 += 4) {
-          const int c = c0 + g4;
-          ce[ct] = mma4(Tb[c * LDM + 16 * ct + l16], QG[t * LDM + c], ce[ct]);
+#pragma unroll
+        for (int cb = ct; cb < 4; ++cb) {
+          if (cb > rt) continue;
+          const f32x4 bq = *reinterpret_cast<const f32x4*>(QG + t * LDM + 16 * cb + 4 * g4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 16 * cb + 4 * g4 + r;
+            ce[ct] = mma4(Tb[c * LDM + 16 * ct + l16], bq[r], ce[ct]);
+          }
         }
     }
 #pragma unroll
@@ -297,9 +311,14 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
     for (int rt = 0; rt < 4; ++rt) {
       const int t = 16 * rt + l16;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < 16 * rt + 16; c0 += 4) {
-        const int c = c0 + g4;
-        acc = mma4(Ks[c * LDK + 16 * kt + l16] * gam[c], CE[t * LDM + c], acc);
+#pragma unroll
+      for (int cb = 0; cb <= rt; ++cb) {
+        const f32x4 bc = *reinterpret_cast<const f32x4*>(CE + t * LDM + 16 * cb + 4 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * cb + 4 * g4 + r;
+          acc = mma4(Ks[c * LDK + 16 * kt + l16] * gam[c], bc[r], acc);
+        }
       }
       const f32x4 qv = qpre[ktl][rt];
       const float gt = t < nrow ? gam[t] : 0.f;
