@@ -24,7 +24,7 @@ Sources (the web pages this follows; cited by title and section):
 * [P5] "論文紹介：Log Linear Attention" (journal-club slides), slides 19-21
   (t=7 walk-through, decode update rule).
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 
 * M^S is the Mamba-2 scalar-decay mask M^S[t,s] = exp(cum[t] - cum[s]) with
   cum the inclusive prefix sum of log_a ([P1] 与已有模型的组合 names "the
