@@ -56,3 +56,25 @@ def test_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, o_eager)
         assert torch.equal(S_graph, S_eager)
+
+
+def test_gdn_forward_graph_replays_match_eager():
+    """The Gated DeltaNet forward with a caller workspace (preparation and
+    level sweep) captured once and replayed."""
+    w = W.GdnWorkload("graph_gdn", 1, 2, 700, 128, 32, "bf16", "weak", seed=12)
+    q, k, v, la, beta, lam = to_dev(*W.make_gdn_inputs(w))
+    ws = torch.empty(ll.gdn_workspace_size(w.B, w.H, w.T, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+    announce("gdn forward graph capture")
+    eager = ll.gdn_fwd(q, k, v, la, beta, lam, workspace=ws).clone()
+    out = torch.empty_like(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ll.gdn_fwd(q, k, v, la, beta, lam, out=out, workspace=ws)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(7)                        # the workspace's contents on entry must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
