@@ -95,7 +95,11 @@ __host__ __device__ constexpr size_t gdn_chunk_floats(int KT) { return size_t(30
 // ---------------------------------------------------------------------------
 // Chunk preparation.  LDS (~68 KiB at dk = 128, two workgroups per CU): K as
 // fp32 rows of DK + 4, the C x C matrices N (later Tb) and Q K^T ⊙ Gamma ⊙
-// tril (later Ceff), and g, gamma, beta.  Q is read from global memory.
+// tril (later Ceff), and g (two words), gamma, beta.  Q is read from global
+// memory.  The in-chunk prefix g of log alpha is a compensated sum (g = gs +
+// gl, the rounding error of every addition kept in gl), so the decay factors
+// exp(g_i - g_j) = exp((gs_i - gs_j) + (gl_i - gl_j)) do not carry the
+// rounding of the running sum, which reaches |g| ~ 10^2 under strong decay.
 // ---------------------------------------------------------------------------
 template <typename IT, int DK>
 __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
@@ -109,6 +113,7 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
   float* gs = QG + GC * LDM;
   float* gam = gs + GC;
   float* bs = gam + GC;
+  float* gl = bs + GC;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -141,15 +146,21 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
     const bool in = lane < nrow;
     const int ll_ = min(lane, nrow - 1);
     const float xa = a.log_alpha[size_t(bh) * a.T + p0 + ll_], xb = a.beta[size_t(bh) * a.T + p0 + ll_];
-    float x = in ? xa : 0.f;
+    float x = in ? xa : 0.f, xl = 0.f;
     const float b = in ? xb : 0.f;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(x, d);
-      if (lane >= d) x += y;
+      const float y = __shfl_up(x, d), yl = __shfl_up(xl, d);
+      if (lane >= d) {
+        // two-sum: s + e == x + y exactly
+        const float s = x + y, bp = s - x, e = (x - (s - bp)) + (y - bp);
+        x = s;
+        xl += yl + e;
+      }
     }
     gs[lane] = x;
-    gam[lane] = __expf(x);
+    gl[lane] = xl;
+    gam[lane] = __expf(x + xl);
     bs[lane] = b;
   }
   __syncthreads();
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * w + 4 * g4 + r;
-      const float G = j <= i ? __expf(gs[i] - gs[j]) : 0.f;
+      const float G = j <= i ? __expf((gs[i] - gs[j]) + (gl[i] - gl[j])) : 0.f;
       Nm[i * LDM + j] = j < i ? bs[i] * kk[r] * G : 0.f;
       QG[i * LDM + j] = qk[r] * G;
     }
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
   }
   // Phase 3c: K^ transposed, fragments (dt, ct): K^[c][d] = exp(g_last - g_c) k_c[d].
   {
-    const float glast = gs[GC - 1];
+    const float glast = gs[GC - 1], glast_l = gl[GC - 1];
 #pragma unroll
     for (int dtl = 0; dtl < KTW; ++dtl) {
       const int dt = w * KTW + dtl;
@@ -291,12 +302,12 @@ __global__ __launch_bounds__(GTHR) void gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * g4 + r;
-          v[r] = __expf(glast - gs[c]) * Ks[c * LDK + 16 * dt + l16];
+          v[r] = __expf((glast - gs[c]) + (glast_l - gl[c])) * Ks[c * LDK + 16 * dt + l16];
         }
         *reinterpret_cast<f32x4*>(rec + gdn_off_kh(KT) + ((dt * 4 + ct) * 64 + lane) * 4) = v;
       }
     }
-    if (tid == 0) a.gchunk[cid] = __expf(glast);
+    if (tid == 0) a.gchunk[cid] = __expf(glast + glast_l);
   }
   __syncthreads();
 
@@ -786,7 +797,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(GdnDecArgs a) {
 template <typename IT, int DK>
 int launch_gdn_t(const GdnArgs& a, hipStream_t s) {
   constexpr int KT = DK / 16;
-  const int prep_lds = (GC * (DK + 4) + 2 * GC * LDM + 3 * GC) * 4;
+  const int prep_lds = (GC * (DK + 4) + 2 * GC * LDM + 4 * GC) * 4;
   const int sweep_lds = gdn_sweep_lds_bytes(a.nslot, DK);
   if (sweep_lds > kMaxLds) return LL_ERR_UNSUPPORTED;
   static std::atomic<uint64_t> raised[2];
